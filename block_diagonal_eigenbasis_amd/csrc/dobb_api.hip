@@ -1,0 +1,350 @@
+// C ABI of libdobb: host-side validation, workspace sizing, grouping of matrix sets by shape, and
+// the optional kernel timer.  Every computation is done by the kernels in k_*.hip.
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "dobb_internal.h"
+
+namespace dobb {
+
+// ---- kernel timer ----------------------------------------------------------------------------
+namespace {
+struct Pending {
+    const char *name;
+    hipEvent_t a, b;
+};
+struct ProfState {
+    bool on = false;
+    const char *cur_name = nullptr;
+    hipEvent_t cur = nullptr;
+    std::vector<Pending> pending;
+    std::vector<std::tuple<const char *, int64_t, double>> totals;  // name, launches, ms
+};
+ProfState &prof() {
+    static ProfState p;
+    return p;
+}
+void prof_collect() {
+    ProfState &p = prof();
+    for (Pending &e : p.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(e.b) == hipSuccess && hipEventElapsedTime(&ms, e.a, e.b) == hipSuccess) {
+            bool found = false;
+            for (auto &t : p.totals)
+                if (std::string(std::get<0>(t)) == e.name) { std::get<1>(t) += 1; std::get<2>(t) += ms; found = true; break; }
+            if (!found) p.totals.emplace_back(e.name, 1, (double)ms);
+        }
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
+    }
+    p.pending.clear();
+}
+}  // namespace
+
+void prof_before(const char *name, hipStream_t s) {
+    ProfState &p = prof();
+    if (!p.on) return;
+    if (hipEventCreate(&p.cur) != hipSuccess) { p.cur = nullptr; return; }
+    p.cur_name = name;
+    (void)hipEventRecord(p.cur, s);
+}
+
+void prof_after(hipStream_t s) {
+    ProfState &p = prof();
+    if (!p.on || !p.cur) return;
+    hipEvent_t b;
+    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(p.cur); p.cur = nullptr; return; }
+    (void)hipEventRecord(b, s);
+    p.pending.push_back({p.cur_name, p.cur, b});
+    p.cur = nullptr;
+    if (p.pending.size() > 4096) prof_collect();  // bound the number of live events
+}
+
+int max_lds_bytes() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+namespace {
+
+constexpr int64_t kMaxNb = 1024;
+constexpr int64_t kMaxRows = (int64_t)65535 * kBM;
+
+inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+dobb_status check_shape(const dobb_shape *s) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    if (s->m < 1 || s->n < 1 || s->nb < 1 || s->nb > kMaxNb || s->n % s->nb != 0 || s->m > kMaxRows)
+        return DOBB_ERR_SHAPE;
+    return DOBB_OK;
+}
+
+bool same_shape(const dobb_shape &a, const dobb_shape &b) { return a.m == b.m && a.n == b.n && a.nb == b.nb; }
+
+// indices of matrices grouped by identical shape, first-seen order
+std::vector<std::vector<int>> group_by_shape(int count, const dobb_shape *shapes) {
+    std::vector<std::vector<int>> groups;
+    for (int i = 0; i < count; ++i) {
+        bool placed = false;
+        for (auto &g : groups)
+            if (same_shape(shapes[g[0]], shapes[i])) { g.push_back(i); placed = true; break; }
+        if (!placed) groups.push_back({i});
+    }
+    return groups;
+}
+
+size_t step_ws_one(const dobb_shape &sh, int norm) {
+    const size_t mn = (size_t)sh.m * (size_t)sh.n;
+    if (norm == DOBB_NORM_SIGN) return al256(mn);                 // int8 sign codes
+    return al256(mn * 4) + al256((size_t)sh.n * 4);               // fp32 coefficients + column scales
+}
+
+size_t group_ws(dobb_op op, const dobb_shape &sh, int cnt, int64_t N, int variant) {
+    const int c = cnt < kMaxMats ? cnt : kMaxMats;
+    switch (op) {
+        case DOBB_OP_ACCUMULATE: return al256(accumulate_ws(sh, N, cnt));
+        case DOBB_OP_REFRESH: return al256(refresh_ws(sh, cnt));
+        case DOBB_OP_STEP: return step_ws_one(sh, variant) * c;
+    }
+    return 0;
+}
+
+dobb_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return DOBB_OK;
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < need) return DOBB_ERR_WORKSPACE;
+    return DOBB_OK;
+}
+
+dobb_status hip_status(hipError_t e) { return e == hipSuccess ? DOBB_OK : DOBB_ERR_HIP; }
+
+}  // namespace
+}  // namespace dobb
+
+using namespace dobb;
+
+extern "C" {
+
+int dobb_abi_version(void) { return DOBB_ABI_VERSION; }
+
+const char *dobb_status_string(dobb_status st) {
+    switch (st) {
+        case DOBB_OK: return "ok";
+        case DOBB_ERR_INVALID_ARG: return "invalid argument";
+        case DOBB_ERR_SHAPE: return "invalid shape (need m, n, nb >= 1, n % nb == 0, nb <= 1024, ldx >= n)";
+        case DOBB_ERR_DTYPE: return "unsupported dtype";
+        case DOBB_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or too small";
+        case DOBB_ERR_HIP: return "HIP launch failed";
+        case DOBB_ERR_NOT_CONVERGED: return "eigensolver did not converge";
+    }
+    return "unknown status";
+}
+
+size_t dobb_workspace_size(dobb_op op, int count, const dobb_shape *shapes, int64_t N, int32_t variant) {
+    if (count < 1 || !shapes) return 0;
+    if (op != DOBB_OP_ACCUMULATE && op != DOBB_OP_REFRESH && op != DOBB_OP_STEP) return 0;
+    if (op == DOBB_OP_ACCUMULATE && N < 1) return 0;
+    if (op == DOBB_OP_STEP && (variant < 0 || variant > 2)) return 0;
+    for (int i = 0; i < count; ++i)
+        if (check_shape(&shapes[i]) != DOBB_OK) return 0;
+    size_t need = 0;
+    for (const auto &g : group_by_shape(count, shapes)) {
+        size_t w = group_ws(op, shapes[g[0]], (int)g.size(), N, variant);
+        if (w > need) need = w;
+    }
+    return need;
+}
+
+dobb_status dobb_accumulate_moment_grouped(int count, const dobb_shape *shapes, const void *const *X, dobb_dtype x_dtype,
+                                           int64_t N, const int64_t *ldx, float beta, float *const *A, void *ws,
+                                           size_t ws_bytes, dobb_stream_t stream) {
+    if (count < 1 || !shapes || !X || !A) return DOBB_ERR_INVALID_ARG;
+    if (x_dtype != DOBB_F32 && x_dtype != DOBB_BF16) return DOBB_ERR_DTYPE;
+    if (N < 1 || !(beta >= 0.f && beta < 1.f)) return DOBB_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        dobb_status st = check_shape(&shapes[i]);
+        if (st != DOBB_OK) return st;
+        if (!X[i] || !A[i]) return DOBB_ERR_INVALID_ARG;
+        if (ldx && ldx[i] < shapes[i].n) return DOBB_ERR_SHAPE;
+    }
+    const auto groups = group_by_shape(count, shapes);
+    size_t need = 0;
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_ACCUMULATE, shapes[g[0]], (int)g.size(), N, 0); if (w > need) need = w; }
+    dobb_status st = check_ws(ws, ws_bytes, need);
+    if (st != DOBB_OK) return st;
+    for (const auto &g : groups) {
+        std::vector<const void *> xs;
+        std::vector<float *> as;
+        std::vector<int64_t> lds;
+        for (int i : g) { xs.push_back(X[i]); as.push_back(A[i]); lds.push_back(ldx ? ldx[i] : shapes[i].n); }
+        AccumulateArgs a{};
+        a.count = (int)g.size();
+        a.sh = shapes[g[0]];
+        a.x_dtype = x_dtype;
+        a.N = N;
+        a.ldx = lds.data();
+        a.X = xs.data();
+        a.A = as.data();
+        a.beta = beta;
+        a.nsplit = accumulate_splits(a.sh, N, a.count);
+        a.partial = (double *)ws;
+        st = hip_status(launch_accumulate(a, (hipStream_t)stream));
+        if (st != DOBB_OK) return st;
+    }
+    return DOBB_OK;
+}
+
+dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtype x_dtype, int64_t N, int64_t ldx,
+                                   float beta, float *A, void *ws, size_t ws_bytes, dobb_stream_t stream) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    return dobb_accumulate_moment_grouped(1, s, &X, x_dtype, N, &ldx, beta, &A, ws, ws_bytes, stream);
+}
+
+dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, const float *const *A, float *const *Q,
+                                       float *const *lambda, dobb_refresh_mode mode, int iters, int warm_start, float tol,
+                                       int32_t *const *info, void *ws, size_t ws_bytes, dobb_stream_t stream) {
+    if (count < 1 || !shapes || !A || !Q) return DOBB_ERR_INVALID_ARG;
+    if (mode != DOBB_REFRESH_EXACT && mode != DOBB_REFRESH_ORTH_ITER) return DOBB_ERR_INVALID_ARG;
+    if (mode == DOBB_REFRESH_ORTH_ITER && iters < 1) return DOBB_ERR_INVALID_ARG;
+    if (iters < 0 || iters > 1000) return DOBB_ERR_INVALID_ARG;
+    if (!(tol >= 0.f) || tol >= 1.f) return DOBB_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        dobb_status st = check_shape(&shapes[i]);
+        if (st != DOBB_OK) return st;
+        if (!A[i] || !Q[i]) return DOBB_ERR_INVALID_ARG;
+    }
+    const auto groups = group_by_shape(count, shapes);
+    size_t need = 0;
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_REFRESH, shapes[g[0]], (int)g.size(), 0, 0); if (w > need) need = w; }
+    dobb_status st = check_ws(ws, ws_bytes, need);
+    if (st != DOBB_OK) return st;
+    for (const auto &g : groups) {
+        std::vector<const float *> as;
+        std::vector<float *> qs, ls;
+        std::vector<int32_t *> is;
+        for (int i : g) {
+            as.push_back(A[i]); qs.push_back(Q[i]);
+            ls.push_back(lambda ? lambda[i] : nullptr);
+            is.push_back(info ? info[i] : nullptr);
+        }
+        RefreshArgs a{};
+        a.count = (int)g.size();
+        a.sh = shapes[g[0]];
+        a.A = as.data();
+        a.Q = qs.data();
+        a.lambda = ls.data();
+        a.info = is.data();
+        a.mode = mode;
+        a.iters = mode == DOBB_REFRESH_EXACT ? (iters > 0 ? iters : 30) : iters;
+        a.warm = warm_start ? 1 : 0;
+        a.tol = tol > 0.f ? tol : 1e-7f;
+        a.ws = ws;
+        st = hip_status(launch_refresh(a, (hipStream_t)stream));
+        if (st != DOBB_OK) return st;
+    }
+    return DOBB_OK;
+}
+
+dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, float *Q, float *lambda, dobb_refresh_mode mode,
+                               int iters, int warm_start, float tol, int32_t *info, void *ws, size_t ws_bytes,
+                               dobb_stream_t stream) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    return dobb_refresh_basis_grouped(1, s, &A, &Q, &lambda, mode, iters, warm_start, tol, &info, ws, ws_bytes, stream);
+}
+
+dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype, const void *const *G,
+                              dobb_dtype g_dtype, float *const *M, const float *const *Q, const dobb_hparams *hp,
+                              float *const *U_out, void *ws, size_t ws_bytes, dobb_stream_t stream) {
+    if (count < 1 || !shapes || !W || !G || !M || !Q || !hp) return DOBB_ERR_INVALID_ARG;
+    if ((w_dtype != DOBB_F32 && w_dtype != DOBB_BF16) || (g_dtype != DOBB_F32 && g_dtype != DOBB_BF16))
+        return DOBB_ERR_DTYPE;
+    for (int i = 0; i < count; ++i) {
+        dobb_status st = check_shape(&shapes[i]);
+        if (st != DOBB_OK) return st;
+        if (!W[i] || !G[i] || !M[i] || !Q[i]) return DOBB_ERR_INVALID_ARG;
+        if (hp[i].norm < 0 || hp[i].norm > 2) return DOBB_ERR_INVALID_ARG;
+        if (hp[i].norm != hp[0].norm || (hp[i].nesterov != 0) != (hp[0].nesterov != 0)) return DOBB_ERR_INVALID_ARG;
+    }
+    const int norm = hp[0].norm;
+    const auto groups = group_by_shape(count, shapes);
+    size_t need = 0;
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_STEP, shapes[g[0]], (int)g.size(), 0, norm); if (w > need) need = w; }
+    dobb_status st = check_ws(ws, ws_bytes, need);
+    if (st != DOBB_OK) return st;
+    for (const auto &g : groups) {
+        const dobb_shape sh = shapes[g[0]];
+        const size_t per = step_ws_one(sh, norm);
+        std::vector<const void *> gs;
+        std::vector<float *> ms, us, cs, ps;
+        std::vector<void *> ws_;
+        std::vector<const float *> qs;
+        std::vector<int8_t *> ss;
+        std::vector<dobb_hparams> hs;
+        for (size_t k = 0; k < g.size(); ++k) {
+            const int i = g[k];
+            gs.push_back(G[i]); ms.push_back(M[i]); ws_.push_back(W[i]); qs.push_back(Q[i]);
+            us.push_back(U_out ? U_out[i] : nullptr);
+            hs.push_back(hp[i]);
+            char *reg = (char *)ws + per * (k % kMaxMats);  // a chunk of kMaxMats shares the workspace
+            ss.push_back((int8_t *)reg);
+            cs.push_back((float *)reg);
+            ps.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + al256((size_t)sh.m * sh.n * 4)));
+        }
+        StepArgs a{};
+        a.count = (int)g.size();
+        a.sh = sh;
+        a.w_dtype = w_dtype;
+        a.g_dtype = g_dtype;
+        a.hp = hs.data();
+        a.G = gs.data();
+        a.M = ms.data();
+        a.W = ws_.data();
+        a.U = us.data();
+        a.Q = qs.data();
+        a.S = ss.data();
+        a.C = cs.data();
+        a.colscale = ps.data();
+        st = hip_status(launch_step(a, (hipStream_t)stream));
+        if (st != DOBB_OK) return st;
+    }
+    return DOBB_OK;
+}
+
+dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype, float *M,
+                      const float *Q, const dobb_hparams *hp, float *U_out, void *ws, size_t ws_bytes,
+                      dobb_stream_t stream) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, hp, &U_out, ws, ws_bytes, stream);
+}
+
+void dobb_profile_enable(int on) {
+    if (!on) prof_collect();
+    prof().on = on != 0;
+}
+
+int dobb_profile_read(const char **names, int64_t *launches, double *total_ms, int cap) {
+    prof_collect();
+    const auto &t = prof().totals;
+    const int n = (int)t.size();
+    for (int i = 0; i < n && i < cap; ++i) {
+        if (names) names[i] = std::get<0>(t[i]);
+        if (launches) launches[i] = std::get<1>(t[i]);
+        if (total_ms) total_ms[i] = std::get<2>(t[i]);
+    }
+    return n;
+}
+
+void dobb_profile_reset(void) {
+    prof_collect();
+    prof().totals.clear();
+}
+
+}  // extern "C"

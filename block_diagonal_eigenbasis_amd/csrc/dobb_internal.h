@@ -1,0 +1,175 @@
+// Internal definitions shared by the libdobb kernels and the C-ABI layer (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dobb.h"
+
+namespace dobb {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Matrices handled by one launch.  Kernels receive a table of per-matrix device pointers by value
+// (kernel arguments are copied at launch, so nothing is staged in device memory); the matrices of
+// one table share a shape.  Launchers split longer lists into chunks of kMaxMats.
+constexpr int kMaxMats = 16;
+
+// ---- bf16 helpers (round-to-nearest-even on store; NaN kept quiet) ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// sign with sign(0) = 0 and NaN kept; encoded in int8 as -1, 0, 1 and 0x7f for NaN
+__device__ __forceinline__ int8_t sign_code(float c) {
+    return c > 0.f ? (int8_t)1 : c < 0.f ? (int8_t)-1 : c == 0.f ? (int8_t)0 : (int8_t)127;
+}
+__device__ __forceinline__ float sign_decode(int8_t s) { return s == 127 ? __builtin_nanf("") : (float)s; }
+
+// ---- tiled fp32 MFMA GEMM core -------------------------------------------------------------
+// One 256-thread workgroup computes a 64 x 64 output tile; wave w owns the 32 x 32 sub-tile at rows
+// 32*(w/2), cols 32*(w%2) with v_mfma_f32_32x32x2_f32.  Operands are staged through LDS one
+// 16-deep K-chunk at a time, both k-major: a[k][i] (output row i) and b[k][j] (output column j), so
+// every MFMA operand read is 32 consecutive floats.  Lane layout of the 32x32 accumulator (checked
+// on gfx950): register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+constexpr int kBM = 64, kBN = 64, kBK = 16, kPad = 4;
+
+struct GemmSmem {
+    float a[kBK][kBM + kPad];
+    float b[kBK][kBN + kPad];
+};
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
+
+template <typename LoadA, typename LoadB>
+__device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB &lb, GemmSmem &sm) {
+    f32x16 acc = {};
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wr = 32 * (w >> 1), wc = 32 * (w & 1);
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+        la(k0, sm.a);
+        lb(k0, sm.b);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 2) {
+            float a = sm.a[kk + (lane >> 5)][wr + (lane & 31)];
+            float b = sm.b[kk + (lane >> 5)][wc + (lane & 31)];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    return acc;
+}
+
+// Loader: a[k][i] = src[(r0 + i) * ld + k0 + k] (row-major operand that must be transposed into the
+// k-major LDS layout).  Zero outside rows < rows, k < K.  Thread t loads row t/4, k = 4*(t%4)..+3.
+template <bool VEC>
+struct LoadRowsT {
+    const float *src; int64_t ld; int rows; int K;
+    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBM + kPad]) const {
+        const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (i < rows) {
+            const float *p = src + (int64_t)i * ld + k;
+            if (VEC) {
+                if (k < K) { f32x4 q = *(const f32x4 *)p; v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3]; }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) if (k + c < K) v[c] = p[c];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
+    }
+};
+
+// Loader: b[k][j] = src[(k0 + k) * ld + j] (already k-major).  Zero outside k < K, j < cols.
+// Thread t loads k = t/16, j = 4*(t%16)..+3.
+template <bool VEC>
+struct LoadColsK {
+    const float *src; int64_t ld; int cols; int K;
+    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBN + kPad]) const {
+        const int t = threadIdx.x, kk = t >> 4, j = 4 * (t & 15), k = k0 + kk;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (k < K) {
+            const float *p = src + (int64_t)k * ld + j;
+            if (VEC) {
+                if (j < cols) { f32x4 q = *(const f32x4 *)p; v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3]; }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) if (j + c < cols) v[c] = p[c];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[kk][j + c] = v[c];
+    }
+};
+
+// ---- kernel launchers (one translation unit each); arrays are host arrays of length count ----
+void prof_before(const char *name, hipStream_t s);  // event pair around each launch when profiling
+void prof_after(hipStream_t s);
+int max_lds_bytes();
+
+struct StepArgs {
+    int count;
+    dobb_shape sh;
+    dobb_dtype w_dtype, g_dtype;
+    const dobb_hparams *hp;           // per matrix
+    const void *const *G;
+    float *const *M;
+    void *const *W;
+    float *const *U;                  // entries may be NULL
+    const float *const *Q;
+    // workspace regions per matrix
+    int8_t *const *S;                 // sign codes m x n
+    float *const *C;                  // fp32 coefficients m x n (identity / column-l2 norms)
+    float *const *colscale;           // n column scales (column-l2)
+};
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
+struct AccumulateArgs {
+    int count;
+    dobb_shape sh;
+    dobb_dtype x_dtype;
+    int64_t N;
+    const int64_t *ldx;               // per matrix
+    const void *const *X;
+    float *const *A;
+    float beta;
+    double *partial;                  // split-K partial sums (whole group), may be NULL if nsplit == 1
+    int nsplit;
+};
+int accumulate_splits(const dobb_shape &sh, int64_t N, int count);
+size_t accumulate_ws(const dobb_shape &sh, int64_t N, int count);
+hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s);
+
+struct RefreshArgs {
+    int count;
+    dobb_shape sh;
+    const float *const *A;
+    float *const *Q;
+    float *const *lambda;             // entries may be NULL
+    int32_t *const *info;             // entries may be NULL
+    dobb_refresh_mode mode;
+    int iters;
+    int warm;
+    float tol;
+    void *ws;                         // scratch for the whole group
+};
+size_t refresh_ws(const dobb_shape &sh, int count);
+hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s);
+
+}  // namespace dobb
+
+#define DOBB_LAUNCH(name, stream, kernel, grid, block, shmem, ...)                          \
+    do {                                                                                    \
+        ::dobb::prof_before(name, stream);                                                  \
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
+        ::dobb::prof_after(stream);                                                         \
+    } while (0)

@@ -1,0 +1,174 @@
+/*
+ * dobb.h -- C ABI of libdobb.so, the MI355X (gfx950) implementation of the Dobb optimizer step
+ * described in "Dobb: Shard-Local Preconditioning in Block-Diagonal Eigenbases" (arXiv 2610.39412).
+ *
+ * For each weight W (m x n, y = W x) the step keeps, per contiguous block b of nb input columns:
+ *   A_b  the nb x nb block of the input-activation second moment, as an EMA   (abstract)
+ *   Q_b  a complete orthonormal eigenbasis of A_b, refreshed periodically      (abstract; Tables 14-16)
+ * and applies  U_b = sign(M_b Q_b) Q_b^T,  W <- W - lr (s U + wd W)              (abstract; Table 9)
+ * with M the heavy-ball momentum of the gradient.
+ *
+ * Conventions shared by every call
+ *   Layout    torch layout.  W, G, M, U are m x n row-major (leading dimension n).  Activations X are
+ *             N x n row-major with leading dimension ldx >= n (token t is row t).  Block b covers
+ *             columns [b*nb, (b+1)*nb); B = n / nb.  A, Q are B consecutive nb x nb row-major
+ *             matrices; Q_b holds eigenvectors as COLUMNS (Q_b[p*nb + j] = entry p of vector j).
+ *             lambda is B x nb.
+ *   Memory    Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor's storage),
+ *             owned by the caller.  The library never allocates, frees or keeps any of it.  Scratch
+ *             memory is the caller's workspace `ws` of at least dobb_workspace_size(...) bytes,
+ *             256-byte aligned; its contents are undefined after a call.
+ *   Streams   All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null
+ *             stream).  No call synchronizes the device.  Results are bitwise reproducible for fixed
+ *             inputs, shapes and device (no floating-point atomics).
+ *   Errors    Arguments are validated on the host BEFORE anything is enqueued; on any error nothing is
+ *             launched and the status says why.  DOBB_ERR_HIP reports a failed launch.  Convergence of
+ *             the eigensolver is reported per block in the device array `info`, never as a status.
+ *             NaN/Inf inputs are not checked; they propagate (sign(NaN) = NaN).
+ *   Threads   The library keeps no mutable global state except the optional kernel timer
+ *             (dobb_profile_*), which is not thread-safe.  Calls that share a workspace or outputs
+ *             must be ordered by the caller.
+ */
+#ifndef DOBB_H
+#define DOBB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DOBB_ABI_VERSION 1
+
+struct ihipStream_t;
+typedef struct ihipStream_t *dobb_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    DOBB_OK = 0,
+    DOBB_ERR_INVALID_ARG = -1,   /* NULL pointer, bad enum, beta outside [0,1), N < 1, ... */
+    DOBB_ERR_SHAPE = -2,         /* m, n or nb < 1, n % nb != 0, ldx < n, nb too large */
+    DOBB_ERR_DTYPE = -3,         /* dtype not supported for that argument */
+    DOBB_ERR_WORKSPACE = -4,     /* ws is NULL, misaligned or smaller than dobb_workspace_size */
+    DOBB_ERR_HIP = -5,           /* a HIP launch or query failed (no device, bad pointer, ...) */
+    DOBB_ERR_NOT_CONVERGED = -6  /* reserved for host-side checks; device results go to info[] */
+} dobb_status;
+
+typedef enum { DOBB_F32 = 0, DOBB_BF16 = 1 } dobb_dtype;
+
+typedef enum {
+    DOBB_REFRESH_EXACT = 0,      /* Table 15 "Exact eigendecomposition": cyclic Jacobi to tolerance */
+    DOBB_REFRESH_ORTH_ITER = 1   /* Table 15 "k=1 (principal)": k steps Q <- qr(A_b Q).Q, Householder */
+} dobb_refresh_mode;
+
+typedef enum {
+    DOBB_NORM_SIGN = 0,          /* abstract / Table 13: sign normalization of the coefficients */
+    DOBB_NORM_IDENTITY = 1,      /* no normalization: U = M Q Q^T (= M); a round-trip test mode */
+    DOBB_NORM_COL_L2 = 2         /* Tables 11-12 "Dobb-l2": unit l2 norm per column of C_b */
+} dobb_norm;
+
+typedef enum { DOBB_OP_ACCUMULATE = 0, DOBB_OP_REFRESH = 1, DOBB_OP_STEP = 2 } dobb_op;
+
+typedef struct {
+    int64_t m;   /* output dimension (rows of W) */
+    int64_t n;   /* input dimension (columns of W); n % nb == 0 */
+    int64_t nb;  /* block width; B = n / nb blocks (1 <= nb <= 1024) */
+} dobb_shape;
+
+typedef struct {
+    float lr;            /* gamma: W <- W - lr (update_scale * U + weight_decay * W) */
+    float weight_decay;  /* lambda (decoupled; uses the weights before the update) */
+    float momentum;      /* mu: M <- mu M + G */
+    float update_scale;  /* applied scale s_eff on U; tau sqrt(max(m,n)/m) reproduces Table 9's
+                            RMS for sign (tau = 0.2 for GPT-2); for COL_L2 Table 9's s = tau sqrt(max(m,n)) */
+    int32_t nesterov;    /* 0: project M;  1: project G + mu M (Table 19 ablation) */
+    int32_t norm;        /* a dobb_norm */
+} dobb_hparams;
+
+/* Bytes of workspace the op needs for `count` matrices of the given shapes.  N (tokens per capture)
+ * is used by DOBB_OP_ACCUMULATE only; variant is the dobb_norm for DOBB_OP_STEP (sign needs 1 byte
+ * per weight entry, the other norms 4) and is ignored otherwise.  The refresh figure covers both
+ * modes.  Returns 0 for bad arguments and for an op that needs no scratch. */
+size_t dobb_workspace_size(dobb_op op, int count, const dobb_shape *shapes, int64_t N, int32_t variant);
+
+/* ------------------------------------------------------------------------------------------------
+ * Second-moment capture (abstract: input-activation second moment approximated by diagonal blocks;
+ * Figure 2 caption: averaged over accumulated mini-batches; Table 17: capture policy is the caller's).
+ *   A_b <- beta * A_b + (1 - beta) * (1/N) * sum_t x_{t,b} x_{t,b}^T,   for every block b.
+ * X: device, N x n (ldx >= n), fp32 or bf16.  A: device fp32 B x nb x nb, read (when beta > 0) and
+ * written in place; the result is exactly symmetric.  0 <= beta < 1 (beta = 0: pure capture, A need
+ * not be initialised).  Products are formed in fp32 (exact for bf16), summed in fp32 over at most 64
+ * tokens and across those chunks in fp64, so A is close to correctly rounded.
+ * -------------------------------------------------------------------------------------------------*/
+dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtype x_dtype, int64_t N,
+                                   int64_t ldx, float beta, float *A, void *ws, size_t ws_bytes,
+                                   dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Basis refresh (abstract: a complete basis is tracked within each block; Tables 14-16).
+ *   EXACT:     Q_b, lambda_b = eig(A_b) by parallel-order cyclic Jacobi in fp32.  warm_start = 0
+ *              starts from the identity; warm_start = 1 diagonalises Q_prev^T A_b Q_prev and
+ *              accumulates the rotations onto Q_prev.  iters = maximum sweeps (<= 0: 30).  tol is
+ *              the relative threshold: a pair (p,q) is rotated while |a_pq| > tol sqrt(|a_pp a_qq|)
+ *              (<= 0: 1e-7); the block has converged after a sweep with no rotation.  Output is
+ *              sorted by descending eigenvalue, each eigenvector with its largest entry positive.
+ *   ORTH_ITER: iters = k >= 1 steps of  Q_b <- qr(A_b Q_b).Q  (Householder, diag(R) > 0) from the
+ *              Q passed in (which must hold a basis); lambda_b receives the Rayleigh quotients
+ *              q_j^T A_b q_j.  warm_start and tol are ignored.
+ * A: device fp32 B x nb x nb (symmetric; only read).  Q: device fp32 B x nb x nb, in/out.
+ * lambda: device fp32 B x nb or NULL.  info: device int32 [B] or NULL; receives the sweeps used
+ * (EXACT, -1 if iters sweeps did not converge) or k (ORTH_ITER).
+ * -------------------------------------------------------------------------------------------------*/
+dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, float *Q, float *lambda,
+                               dobb_refresh_mode mode, int iters, int warm_start, float tol,
+                               int32_t *info, void *ws, size_t ws_bytes, dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * The Dobb step (abstract: project momentum into the block bases, sign-normalise the coefficients,
+ * reconstruct; Table 9: update scale; Table 21 note: decoupled weight decay; Table 19: Nesterov).
+ *   M <- mu M + G;   P = M (or G + mu M with nesterov);   C_b = P_b Q_b;
+ *   U_b = sign(C_b) Q_b^T   (sign(0) = 0);   W <- W - lr (update_scale U + weight_decay W).
+ * W: device m x n, fp32 or bf16 (bf16 is updated in fp32 and rounded to nearest even).
+ * G: device m x n, fp32 or bf16.  M: device fp32 m x n, in/out.  Q: device fp32 B x nb x nb.
+ * hp: host pointer.  U_out: device fp32 m x n or NULL (receives U before scaling).
+ * -------------------------------------------------------------------------------------------------*/
+dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,
+                      float *M, const float *Q, const dobb_hparams *hp, float *U_out, void *ws,
+                      size_t ws_bytes, dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Grouped forms over a matrix set: the same semantics for `count` matrices, enqueued together.
+ * shapes, the pointer arrays and hp are HOST arrays of length count whose entries are device
+ * pointers (U_out may be NULL, or an array with NULL entries; ldx may be NULL for ldx = n).  The
+ * workspace is sized by dobb_workspace_size(op, count, shapes, N, variant) and shared by the whole
+ * group.  All hp entries of one dobb_step_grouped call must share norm and nesterov.
+ * -------------------------------------------------------------------------------------------------*/
+dobb_status dobb_accumulate_moment_grouped(int count, const dobb_shape *shapes, const void *const *X,
+                                           dobb_dtype x_dtype, int64_t N, const int64_t *ldx, float beta,
+                                           float *const *A, void *ws, size_t ws_bytes, dobb_stream_t stream);
+dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, const float *const *A,
+                                       float *const *Q, float *const *lambda, dobb_refresh_mode mode,
+                                       int iters, int warm_start, float tol, int32_t *const *info,
+                                       void *ws, size_t ws_bytes, dobb_stream_t stream);
+dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype,
+                              const void *const *G, dobb_dtype g_dtype, float *const *M,
+                              const float *const *Q, const dobb_hparams *hp, float *const *U_out,
+                              void *ws, size_t ws_bytes, dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Kernel timer (tracing).  While enabled, every kernel the library enqueues is bracketed by a pair
+ * of HIP events on its stream; dobb_profile_read synchronizes those events and returns, per kernel
+ * name, the launch count and the summed duration in milliseconds.  Names are static strings.
+ * Returns the number of distinct kernels (at most cap entries are written).  Not thread-safe.
+ * -------------------------------------------------------------------------------------------------*/
+void dobb_profile_enable(int on);
+int dobb_profile_read(const char **names, int64_t *launches, double *total_ms, int cap);
+void dobb_profile_reset(void);
+
+const char *dobb_status_string(dobb_status st);
+int dobb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DOBB_H */

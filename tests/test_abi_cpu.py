@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: libdobb.so loads, exports every entry point include/dobb.h declares, and
+rejects bad arguments on the host before anything is enqueued.
+
+Every call below is invalid in at least one argument, so validation returns before any launch; the
+non-null "device pointers" are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diagonal_eigenbasis_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: each call fails validation first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dobb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dobb_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    names = declared_functions()
+    assert len(names) == 12
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert _abi.dobb_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert _abi.status_string(st)
+    assert "unknown" in _abi.status_string(42)
+
+
+def _shape(m, n, nb):
+    return _abi.Shape(m, n, nb)
+
+
+@pytest.mark.parametrize("m,n,nb,status", [
+    (0, 8, 4, _abi.DOBB_ERR_SHAPE), (4, 0, 4, _abi.DOBB_ERR_SHAPE), (4, 8, 0, _abi.DOBB_ERR_SHAPE),
+    (4, 10, 4, _abi.DOBB_ERR_SHAPE), (4, 4096, 2048, _abi.DOBB_ERR_SHAPE)])
+def test_step_shape_errors(m, n, nb, status):
+    s = _shape(m, n, nb)
+    hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
+    st = _abi.lib().dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None)
+    assert st == status
+
+
+def test_step_argument_errors():
+    L = _abi.lib()
+    s = _shape(64, 64, 16)
+    hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
+    assert L.dobb_step(None, FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), None, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), FAKE, 7, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -3
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 5, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -3
+    bad = _abi.make_hparams(0.1, 0.0, 0.9, 0.2, norm=9)
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(bad), None, FAKE, 1 << 30, None) == -1
+    # workspace: missing, too small, misaligned
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, None, 0, None) == -4
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 16, None) == -4
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None,
+                       ctypes.c_void_p(0x10010), 1 << 30, None) == -4
+
+
+def test_accumulate_argument_errors():
+    L = _abi.lib()
+    s = _shape(1, 64, 16)
+    ok = dict(X=FAKE, dt=0, N=128, ldx=64, beta=0.5, A=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.dobb_accumulate_moment(ctypes.byref(s), a["X"], a["dt"], a["N"], a["ldx"], a["beta"], a["A"],
+                                        None, 0, None)
+    assert call(X=None) == -1
+    assert call(A=None) == -1
+    assert call(dt=3) == -3
+    assert call(N=0) == -1
+    assert call(ldx=32) == -2
+    assert call(beta=1.0) == -1
+    assert call(beta=-0.1) == -1
+    assert call(beta=float("nan")) == -1
+    # token split needs a workspace for this small shape: missing workspace is reported
+    assert _abi.dobb_workspace_size(_abi.DOBB_OP_ACCUMULATE, [(1, 64, 16)], 4096) > 0
+    assert call(N=4096) == -4
+
+
+def test_refresh_argument_errors():
+    L = _abi.lib()
+    s = _shape(1, 64, 16)
+
+    def call(A=FAKE, Q=FAKE, mode=0, iters=0, tol=0.0, ws=None, wsb=0):
+        return L.dobb_refresh_basis(ctypes.byref(s), A, Q, None, mode, iters, 0, tol, None, ws, wsb, None)
+    assert call(A=None) == -1
+    assert call(Q=None) == -1
+    assert call(mode=4) == -1
+    assert call(mode=1, iters=0) == -1      # orthogonal iteration needs k >= 1
+    assert call(iters=-2) == -1
+    assert call(tol=-1.0) == -1
+    assert call() == -4                     # the refresh always needs a workspace
+
+
+def test_workspace_sizes():
+    ws = _abi.dobb_workspace_size
+    assert ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, _abi.DOBB_NORM_SIGN) >= 768 * 768
+    assert ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, _abi.DOBB_NORM_COL_L2) >= 4 * 768 * 768 + 4 * 768
+    assert ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, 7) == 0
+    r = ws(_abi.DOBB_OP_REFRESH, [(1, 768, 192)])
+    assert r >= 4 * (192 * 192 * (4 + 8 + 4))
+    assert ws(_abi.DOBB_OP_REFRESH, [(1, 770, 192)]) == 0         # n % nb != 0
+    assert ws(_abi.DOBB_OP_ACCUMULATE, [(1, 768, 192)], 0) == 0   # N < 1
+    # a group larger than one launch chunk reuses the chunk's workspace
+    big = ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 40, 0, 0)
+    assert big == ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 16, 0, 0)
+
+
+def test_grouped_rejects_mixed_norms():
+    L = _abi.lib()
+    shapes = (_abi.Shape * 2)(_shape(64, 64, 16), _shape(64, 64, 16))
+    hps = (_abi.HParams * 2)(_abi.make_hparams(0.1, 0, 0.9, 0.2), _abi.make_hparams(0.1, 0, 0.9, 0.2, norm=2))
+    P = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    st = L.dobb_step_grouped(2, shapes, P, 0, P, 0, P, P, hps, None, FAKE, 1 << 30, None)
+    assert st == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        _abi.dobb_step(torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(1, 4, 4), 4,
+                       _abi.make_hparams(0.1, 0, 0.9, 0.2))

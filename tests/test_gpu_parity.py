@@ -1,0 +1,411 @@
+"""GPU parity: every entry point of libdobb.so against the fp64 CPU oracle (MI355X only).
+
+Tolerances (fp32 arithmetic on the GPU, fp64 in the oracle):
+* accumulate: products are exact or fp32-rounded, sums run in fp32 over <= 64 tokens and in fp64
+  beyond, then one rounding to fp32 -> |A_gpu - A_ref| <= 4e-7 max|A_b| (a few units of fp32 rounding).
+* exact refresh, from the Dobb problem statement: eigenvalue error (normwise, relative to max|lambda|)
+  <= 1e-5, eigen-residual ||A Q - Q L||_F / ||A||_F <= 1e-5, max|Q^T Q - I| <= 1e-5.  Eigenvectors are
+  compared column by column against the oracle with the first-order bound 8 u ||A|| / gap_j + 1e-6.
+* step fed the oracle's Q: ||C_gpu - C_ref||_F / ||C_ref||_F <= 1e-5; no sign mismatch where
+  |C_ref| > 1e-5 max|C_ref|; ||U_gpu - sign(C_gpu) Q^T||_F / ||.||_F <= 1e-5 (isolates the
+  reconstruction GEMM); W_new within 2 fp32 ulps of W - lr (s U_gpu + wd W).
+* end to end (accumulate -> exact refresh -> step): <= 0.1 % of U's entries differ by more than
+  1e-3 RMS(U).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+
+dobb = pytest.importorskip("block_diagonal_eigenbasis_amd")
+
+DEV = "cuda"
+RNG = np.random.default_rng
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    _gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def t32(x):
+    return torch.as_tensor(np.ascontiguousarray(x), dtype=torch.float32, device=DEV)
+
+
+def host(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def random_basis(B, nb, rng):
+    return np.stack([workload.haar(nb, rng) for _ in range(B)])
+
+
+# ------------------------------------------------------------------------------------------------
+# accumulate
+
+@pytest.mark.parametrize("N,n,nb,dtype", [
+    (4096, 768, 192, torch.float32),     # the 768 x 768, B = 4 workload
+    (2048, 768, 48, torch.bfloat16),     # GPT-2 Small attention shapes, B = 16
+    (1000, 90, 30, torch.float32),       # ragged: N % 64 != 0, nb % 4 != 0
+    (777, 400, 100, torch.bfloat16),     # GPT-2 XL block width, ragged token count
+    (300, 800, 400, torch.float32),      # several 64-wide tiles per block with a tail
+])
+def test_accumulate_matches_oracle(N, n, nb, dtype):
+    print(f"accumulate N={N} n={n} nb={nb} {dtype}", flush=True)
+    rng = RNG(N + n + nb)
+    X = t32(workload.activations(N, n, 0.15, rng)).to(dtype)
+    B = n // nb
+    A = torch.empty(B, nb, nb, device=DEV)
+    dobb.dobb_accumulate_moment(X, A, nb, beta=0.0)
+    ref = oracle.accumulate(X.cpu(), nb)
+    got = host(A)
+    for b in range(B):
+        assert np.max(np.abs(got[b] - ref[b])) <= 4e-7 * np.max(np.abs(ref[b]))
+    np.testing.assert_array_equal(got, np.transpose(got, (0, 2, 1)))
+    # second capture with EMA
+    X2 = t32(workload.activations(N, n, 0.15, rng)).to(dtype)
+    dobb.dobb_accumulate_moment(X2, A, nb, beta=0.9)
+    ref2 = oracle.accumulate(X2.cpu(), nb, A=got, beta=0.9)
+    got2 = host(A)
+    for b in range(B):
+        assert np.max(np.abs(got2[b] - ref2[b])) <= 4e-7 * np.max(np.abs(ref2[b]))
+
+
+# ------------------------------------------------------------------------------------------------
+# exact refresh
+
+def _check_eig(A32, lam, Q, lam_ref, Q_ref):
+    """A32: (B, nb, nb) the fp32 input widened; lam, Q: GPU results; *_ref: oracle."""
+    B, nb, _ = A32.shape
+    for b in range(B):
+        A = A32[b]
+        nA = np.linalg.norm(A)
+        scale = np.max(np.abs(lam_ref[b]))
+        assert np.max(np.abs(lam[b] - lam_ref[b])) <= 1e-5 * scale, "eigenvalues"
+        assert np.linalg.norm(A @ Q[b] - Q[b] * lam[b]) <= 1e-5 * nA, "residual"
+        assert np.max(np.abs(Q[b].T @ Q[b] - np.eye(nb))) <= 1e-5, "orthonormality"
+        lr = lam_ref[b]
+        gap = np.full(nb, np.inf)
+        gap[:-1] = np.minimum(gap[:-1], lr[:-1] - lr[1:])
+        gap[1:] = np.minimum(gap[1:], lr[:-1] - lr[1:])
+        err = np.linalg.norm(Q[b] - Q_ref[b], axis=0)
+        bound = 8 * 6e-8 * nA / np.maximum(gap, 1e-300) + 1e-6
+        bad = np.nonzero(err > bound)[0]
+        assert bad.size == 0, f"eigenvectors {bad[:5]} err {err[bad[:5]]} bound {bound[bad[:5]]}"
+
+
+@pytest.mark.parametrize("N,n,nb", [(4096, 768, 192), (2048, 96, 48), (2048, 75, 25), (4096, 200, 100),
+                                    (4096, 400, 400)])
+def test_refresh_exact_matches_oracle(N, n, nb):
+    print(f"refresh exact n={n} nb={nb}", flush=True)
+    rng = RNG(7 * n + nb)
+    X = workload.activations(N, n, 0.15, rng)
+    A64 = oracle.accumulate(X, nb)
+    A = t32(A64)
+    A32 = host(A)
+    B = n // nb
+    Q = torch.empty(B, nb, nb, device=DEV)
+    lam = torch.empty(B, nb, device=DEV)
+    info = torch.empty(B, dtype=torch.int32, device=DEV)
+    dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT, iters=30, lam=lam, info=info)
+    lam_ref, Q_ref, _ = oracle.eig(A32)
+    assert np.all(info.cpu().numpy() > 0)
+    _check_eig(A32, host(lam), host(Q), lam_ref, Q_ref)
+
+
+def test_refresh_exact_warm_start():
+    rng = RNG(11)
+    n, nb = 384, 96
+    A1 = t32(oracle.accumulate(workload.activations(4096, n, 0.15, rng), nb))
+    Q = torch.empty(n // nb, nb, nb, device=DEV)
+    dobb.dobb_refresh_basis(A1, Q, dobb.DOBB_REFRESH_EXACT)
+    # a nearby moment: EMA with a new capture; warm start from the previous basis
+    A2 = A1.clone()
+    X2 = t32(workload.activations(4096, n, 0.15, rng))
+    dobb.dobb_accumulate_moment(X2, A2, nb, beta=0.9)
+    lam = torch.empty(n // nb, nb, device=DEV)
+    info = torch.empty(n // nb, dtype=torch.int32, device=DEV)
+    dobb.dobb_refresh_basis(A2, Q, dobb.DOBB_REFRESH_EXACT, warm_start=True, lam=lam, info=info)
+    A32 = host(A2)
+    lam_ref, Q_ref, _ = oracle.eig(A32)
+    _check_eig(A32, host(lam), host(Q), lam_ref, Q_ref)
+    assert np.all(info.cpu().numpy() >= 0)
+
+
+def test_refresh_exact_reports_non_convergence():
+    rng = RNG(12)
+    A = t32(oracle.accumulate(workload.activations(2048, 64, 0.15, rng), 64))
+    Q = torch.empty(1, 64, 64, device=DEV)
+    info = torch.empty(1, dtype=torch.int32, device=DEV)
+    dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT, iters=1, info=info)
+    assert int(info.item()) == -1
+
+
+# ------------------------------------------------------------------------------------------------
+# orthogonal-iteration refresh
+
+@pytest.mark.parametrize("n,nb,k", [(768, 192, 1), (200, 100, 2), (75, 25, 1), (400, 400, 1)])
+def test_refresh_orth_iter_matches_oracle(n, nb, k):
+    print(f"refresh orth_iter n={n} nb={nb} k={k}", flush=True)
+    rng = RNG(13 * n + k)
+    A64 = oracle.accumulate(workload.activations(4096, n, 0.15, rng), nb)
+    A = t32(A64)
+    A32 = host(A)
+    B = n // nb
+    Qp = random_basis(B, nb, rng).astype(np.float32)
+    Q = t32(Qp)
+    lam = torch.empty(B, nb, device=DEV)
+    info = torch.empty(B, dtype=torch.int32, device=DEV)
+    dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_ORTH_ITER, iters=k, lam=lam, info=info)
+    Q_ref, lam_ref = oracle.orth_iter(A32, Qp.astype(np.float64), k=k)
+    got = host(Q)
+    assert np.all(info.cpu().numpy() == k)
+    for b in range(B):
+        assert np.max(np.abs(got[b].T @ got[b] - np.eye(nb))) <= 1e-5
+        # QR of Z = A Q amplifies rounding by about cond(Z); the bound is 4 u cond(Z) per entry
+        Z = A32[b] @ Qp[b].astype(np.float64)
+        for _ in range(k - 1):
+            Z = A32[b] @ np.linalg.qr(Z)[0]
+        cond = np.linalg.cond(Z)
+        assert np.max(np.abs(got[b] - Q_ref[b])) <= 4 * 6e-8 * cond + 1e-6
+        np.testing.assert_allclose(host(lam)[b], lam_ref[b], rtol=0, atol=1e-5 * np.max(np.abs(lam_ref[b])))
+
+
+# ------------------------------------------------------------------------------------------------
+# the step, fed the oracle's basis
+
+def _step_case(m, n, nb, seed, w_dtype=torch.float32, g_dtype=torch.float32, mu=0.9, wd=0.1, nesterov=False):
+    rng = RNG(seed)
+    Q64 = random_basis(n // nb, nb, rng)
+    Q = t32(Q64)
+    Qh = host(Q)                       # the fp32 basis both sides use
+    W = t32(0.02 * rng.standard_normal((m, n))).to(w_dtype)
+    G = t32(rng.standard_normal((m, n))).to(g_dtype)
+    M = t32(rng.standard_normal((m, n)))
+    s = oracle.default_update_scale(m, n)
+    f32 = lambda v: float(np.float32(v))  # the ABI carries fp32 hyperparameters; the oracle gets the same values
+    hp = dict(lr=f32(2.5e-3), weight_decay=f32(wd), momentum=f32(mu), update_scale=f32(s), nesterov=nesterov)
+    return Q, Qh, W, G, M, hp
+
+
+def check_w(W_gpu, W0, U, hp, bf16=False):
+    """W_new = w - lr (s u + wd w) evaluated in fp32 from the GPU's own U: four roundings, each relative
+    to |result| or |lr (s u + wd w)|; a bf16 store adds half a bf16 ulp of the result."""
+    lr, s, wd = hp["lr"], hp["update_scale"], hp["weight_decay"]
+    want = W0 - lr * (s * U + wd * W0)
+    bound = 1.2e-7 * (np.abs(want) + 3 * lr * (s * np.abs(U) + wd * np.abs(W0))) + 1e-30
+    if bf16:
+        bound = bound + 2.0 ** -8 * np.abs(want)
+    assert np.all(np.abs(W_gpu - want) <= bound)
+
+
+def _check_momentum(M_gpu, M0, G, mu, M_ref):
+    """fmaf(mu, M, G) is one fp32 rounding of the exact value: |err| <= 2^-24 |M_ref| (+ tiny slack)."""
+    err = np.abs(host(M_gpu) - M_ref)
+    assert np.all(err <= 6e-8 * np.abs(M_ref) + 1e-30)
+
+
+def _run_step(W, G, M, Q, nb, hp, norm):
+    W, M = W.clone(), M.clone()
+    U = torch.empty(W.shape, device=DEV)
+    dobb.dobb_step(W, G, M, Q, nb, dobb.make_hparams(norm=norm, **hp), U_out=U)
+    return W, M, U
+
+
+@pytest.mark.parametrize("m,n,nb", [(768, 768, 192), (130, 96, 48), (70, 75, 25), (200, 800, 400), (64, 256, 128)])
+def test_step_matches_oracle(m, n, nb):
+    print(f"step m={m} n={n} nb={nb}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=m + n + nb)
+    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    _, _, U_id = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_IDENTITY)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"])
+    _check_momentum(M_s, M, G, hp["momentum"], M_r)
+    B = n // nb
+    U_sh, U_idh, W_sh, W0 = host(U_s), host(U_id), host(W_s), host(W)
+    for b in range(B):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = M_r[:, sl] @ Qh[b]
+        C_gpu = U_idh[:, sl] @ Qh[b]                        # identity mode: U = C Q^T
+        assert np.linalg.norm(C_gpu - C_ref) <= 1e-5 * np.linalg.norm(C_ref)
+        S_gpu = np.rint(U_sh[:, sl] @ Qh[b])                # recover the sign codes
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref))
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the dead zone"
+        R = S_gpu @ Qh[b].T
+        assert np.linalg.norm(U_sh[:, sl] - R) <= 1e-5 * np.linalg.norm(R)
+    frac = np.mean(np.abs(U_sh - U_r) > 1e-3)
+    assert frac <= 1e-3
+    check_w(W_sh, W0, U_sh, hp)
+
+
+def test_step_identity_round_trip():
+    Q, Qh, W, G, M, hp = _step_case(100, 192, 64, seed=5, mu=1.0)
+    G.zero_()
+    _, M1, U = _run_step(W, G, M, Q, 64, hp, dobb.DOBB_NORM_IDENTITY)
+    np.testing.assert_allclose(host(U), host(M), atol=2e-6 * float(M.abs().max()))
+
+
+def test_step_bf16_weights_and_gradients():
+    m, n, nb = 256, 512, 128
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=9, w_dtype=torch.bfloat16, g_dtype=torch.bfloat16)
+    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"])
+    _check_momentum(M_s, M, G, hp["momentum"], M_r)
+    assert np.mean(np.abs(host(U_s) - U_r) > 1e-3) <= 1e-3
+    # bf16 store: within one bf16 rounding of the fp64 update computed from the GPU's U
+    check_w(host(W_s), host(W), host(U_s), hp, bf16=True)
+
+
+def test_step_nesterov_and_column_l2():
+    m, n, nb = 96, 128, 64
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=21, nesterov=True)
+    _, _, U_id = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_IDENTITY)
+    _, _, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                            hp["update_scale"], nesterov=True, norm=oracle.NORM_IDENTITY)
+    np.testing.assert_allclose(host(U_id), U_r, atol=1e-5 * np.abs(U_r).max())
+    hp["nesterov"] = False
+    W_l, _, U_l = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_COL_L2)
+    W_r, _, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                              hp["update_scale"], norm=oracle.NORM_COL_L2)
+    assert np.linalg.norm(host(U_l) - U_r) <= 1e-5 * np.linalg.norm(U_r)
+    np.testing.assert_allclose(host(W_l), W_r, rtol=1e-6, atol=1e-9)
+
+
+def test_step_sign_flip_invariance_is_bitwise():
+    m, n, nb = 128, 256, 64
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=31)
+    flips = torch.tensor(RNG(3).choice([-1.0, 1.0], size=(n // nb, 1, nb)), dtype=torch.float32, device=DEV)
+    _, _, U1 = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    _, _, U2 = _run_step(W, G, M, (Q * flips).contiguous(), nb, hp, dobb.DOBB_NORM_SIGN)
+    assert torch.equal(U1, U2)
+
+
+def test_step_nan_propagates_to_its_row_block():
+    m, n, nb = 64, 128, 64
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=41)
+    M[3, 70] = float("nan")
+    hp["momentum"] = 1.0
+    G.zero_()
+    _, _, U = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    U = host(U)
+    assert np.all(np.isnan(U[3, 64:])) and np.all(np.isfinite(U[3, :64]))
+    assert np.all(np.isfinite(np.delete(U, 3, 0)))
+
+
+def test_determinism_bitwise():
+    rng = RNG(51)
+    n, nb, m = 384, 96, 200
+    X = t32(workload.activations(1024, n, 0.15, rng))
+    outs = []
+    for _ in range(2):
+        A = torch.empty(n // nb, nb, nb, device=DEV)
+        dobb.dobb_accumulate_moment(X, A, nb)
+        Q = torch.empty_like(A)
+        dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT)
+        Q2 = Q.clone()
+        dobb.dobb_refresh_basis(A, Q2, dobb.DOBB_REFRESH_ORTH_ITER, iters=1)
+        W = t32(0.02 * RNG(1).standard_normal((m, n)))
+        G = t32(RNG(2).standard_normal((m, n)))
+        M = torch.zeros(m, n, device=DEV)
+        dobb.dobb_step(W, G, M, Q2, nb, dobb.make_hparams(2.5e-3, 0.1, 0.9, 0.2))
+        outs.append((A, Q, Q2, W, M))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------------
+# grouped forms equal single calls
+
+def test_grouped_equals_single_calls():
+    rng = RNG(61)
+    shapes = [(64, 96, 48)] * 18 + [(96, 128, 64)] * 3      # > one launch chunk of one shape
+    Ws, Gs, Ms, Qs, nbs, hps = [], [], [], [], [], []
+    for m, n, nb in shapes:
+        Ws.append(t32(0.02 * rng.standard_normal((m, n))))
+        Gs.append(t32(rng.standard_normal((m, n))))
+        Ms.append(t32(rng.standard_normal((m, n))))
+        Qs.append(t32(random_basis(n // nb, nb, rng)))
+        nbs.append(nb)
+        hps.append(dobb.make_hparams(2.5e-3, 0.1, 0.9, oracle.default_update_scale(m, n)))
+    Ws1, Ms1 = [w.clone() for w in Ws], [x.clone() for x in Ms]
+    for W, G, M, Q, nb, hp in zip(Ws1, Gs, Ms1, Qs, nbs, hps):
+        dobb.dobb_step(W, G, M, Q, nb, hp)
+    dobb.dobb_step_grouped(Ws, Gs, Ms, Qs, nbs, hps)
+    for a, b in zip(Ws, Ws1):
+        assert torch.equal(a, b)
+    for a, b in zip(Ms, Ms1):
+        assert torch.equal(a, b)
+    # accumulate + refresh, grouped
+    Xs = [t32(workload.activations(512, n, 0.15, rng)) for _, n, _ in shapes[:4]]
+    As = [torch.empty(n // nb, nb, nb, device=DEV) for _, n, nb in shapes[:4]]
+    As1 = [a.clone() for a in As]
+    dobb.dobb_accumulate_moment_grouped(Xs, As, nbs[:4])
+    for X, A, nb in zip(Xs, As1, nbs[:4]):
+        dobb.dobb_accumulate_moment(X, A, nb)
+    for a, b in zip(As, As1):
+        assert torch.equal(a, b)
+    Qg = [torch.empty_like(a) for a in As]
+    Q1 = [torch.empty_like(a) for a in As]
+    dobb.dobb_refresh_basis_grouped(As, Qg, dobb.DOBB_REFRESH_EXACT, 30)
+    for A, Q in zip(As, Q1):
+        dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT, iters=30)
+    for a, b in zip(Qg, Q1):
+        assert torch.equal(a, b)
+
+
+def test_profiler_reports_kernels():
+    dobb.dobb_profile_reset()
+    dobb.dobb_profile_enable(True)
+    Q, Qh, W, G, M, hp = _step_case(128, 256, 64, seed=71)
+    _run_step(W, G, M, Q, 64, hp, dobb.DOBB_NORM_SIGN)
+    torch.cuda.synchronize()
+    dobb.dobb_profile_enable(False)
+    rep = dobb.dobb_profile_read()
+    for k in ("momentum", "project", "reconstruct"):
+        assert k in rep and rep[k][0] >= 1 and rep[k][1] > 0
+    dobb.dobb_profile_reset()
+
+
+# ------------------------------------------------------------------------------------------------
+# end to end on the single 768 x 768 weight, B = 4 (nb = 192): X is 4096 x 768 with a 15 % effective
+# rank spectrum, M = G ~ N(0, 1) (mu = 0); one accumulate, one exact refresh, one step.
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_end_to_end_768_B4(seed):
+    print(f"end-to-end seed={seed}", flush=True)
+    rng = RNG(seed)
+    N, m, n, nb = 4096, 768, 768, 192
+    X = t32(workload.activations(N, n, 0.15, rng))
+    G = t32(rng.standard_normal((m, n)))
+    W = t32(0.02 * rng.standard_normal((m, n)))
+    hp = dict(lr=float(np.float32(2.5e-3)), weight_decay=float(np.float32(0.1)), momentum=0.0,
+              update_scale=float(np.float32(oracle.default_update_scale(m, n))))
+    A = torch.empty(n // nb, nb, nb, device=DEV)
+    dobb.dobb_accumulate_moment(X, A, nb)
+    Q = torch.empty_like(A)
+    dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT)
+    M = torch.zeros(m, n, device=DEV)
+    W1, U = W.clone(), torch.empty(m, n, device=DEV)
+    dobb.dobb_step(W1, G, M, Q, nb, dobb.make_hparams(**hp), U_out=U)
+    A_ref = oracle.accumulate(X.cpu(), nb)
+    lam_ref, Q_ref, _ = oracle.eig(A_ref)
+    W_ref, _, U_ref = oracle.step(W.cpu(), G.cpu(), np.zeros((m, n)), Q_ref, nb, hp["lr"], hp["weight_decay"],
+                                  hp["momentum"], hp["update_scale"])
+    Ug = host(U)
+    rms = np.sqrt(np.mean(U_ref ** 2))
+    frac = np.mean(np.abs(Ug - U_ref) > 1e-3 * rms)
+    gaps = np.min(np.diff(-lam_ref, axis=1) / lam_ref[:, :1], axis=1)
+    print(f"  differing U entries {frac:.2e}  min relative gap per block {gaps}", flush=True)
+    assert frac <= 1e-3
