@@ -20,11 +20,23 @@ struct ProfState {
     const char *cur_name = nullptr;
     hipEvent_t cur = nullptr;
     std::vector<Pending> pending;
+    std::vector<hipEvent_t> pool;                                   // recycled events
     std::vector<std::tuple<const char *, int64_t, double>> totals;  // name, launches, ms
 };
 ProfState &prof() {
     static ProfState p;
     return p;
+}
+hipEvent_t prof_event() {
+    ProfState &p = prof();
+    if (!p.pool.empty()) {
+        hipEvent_t e = p.pool.back();
+        p.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
 }
 void prof_collect() {
     ProfState &p = prof();
@@ -36,8 +48,8 @@ void prof_collect() {
                 if (std::string(std::get<0>(t)) == e.name) { std::get<1>(t) += 1; std::get<2>(t) += ms; found = true; break; }
             if (!found) p.totals.emplace_back(e.name, 1, (double)ms);
         }
-        (void)hipEventDestroy(e.a);
-        (void)hipEventDestroy(e.b);
+        p.pool.push_back(e.a);
+        p.pool.push_back(e.b);
     }
     p.pending.clear();
 }
@@ -46,7 +58,8 @@ void prof_collect() {
 void prof_before(const char *name, hipStream_t s) {
     ProfState &p = prof();
     if (!p.on) return;
-    if (hipEventCreate(&p.cur) != hipSuccess) { p.cur = nullptr; return; }
+    p.cur = prof_event();
+    if (!p.cur) return;
     p.cur_name = name;
     (void)hipEventRecord(p.cur, s);
 }
@@ -54,8 +67,8 @@ void prof_before(const char *name, hipStream_t s) {
 void prof_after(hipStream_t s) {
     ProfState &p = prof();
     if (!p.on || !p.cur) return;
-    hipEvent_t b;
-    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(p.cur); p.cur = nullptr; return; }
+    hipEvent_t b = prof_event();
+    if (!b) { p.pool.push_back(p.cur); p.cur = nullptr; return; }
     (void)hipEventRecord(b, s);
     p.pending.push_back({p.cur_name, p.cur, b});
     p.cur = nullptr;
