@@ -116,6 +116,7 @@ std::vector<std::vector<int>> group_by_shape(int count, const dobb_shape *shapes
 }
 
 size_t step_ws_one(const dobb_shape &sh, int norm) {
+    if (step_bf16_eligible(sh, norm)) return step_bf16_ws_one(sh);
     const size_t mn = (size_t)sh.m * (size_t)sh.n;
     if (norm == DOBB_NORM_SIGN) return al256(mn);                 // int8 sign codes
     return al256(mn * 4) + al256((size_t)sh.n * 4);               // fp32 coefficients + column scales
@@ -207,7 +208,7 @@ dobb_status dobb_accumulate_moment_grouped(int count, const dobb_shape *shapes, 
         a.X = xs.data();
         a.A = as.data();
         a.beta = beta;
-        a.nsplit = accumulate_splits(a.sh, N, a.count);
+        a.nsplit = accumulate_splits(a.sh, N, a.count, x_dtype == DOBB_BF16);
         a.partial = (double *)ws;
         st = hip_status(launch_accumulate(a, (hipStream_t)stream));
         if (st != DOBB_OK) return st;
@@ -300,7 +301,10 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
         std::vector<void *> ws_;
         std::vector<const float *> qs;
         std::vector<int8_t *> ss;
+        std::vector<uint16_t *> pls;
         std::vector<dobb_hparams> hs;
+        const bool bf16 = step_bf16_eligible(sh, norm);
+        bool aligned = true;
         for (size_t k = 0; k < g.size(); ++k) {
             const int i = g[k];
             gs.push_back(G[i]); ms.push_back(M[i]); ws_.push_back(W[i]); qs.push_back(Q[i]);
@@ -310,6 +314,10 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
             ss.push_back((int8_t *)reg);
             cs.push_back((float *)reg);
             ps.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + al256((size_t)sh.m * sh.n * 4)));
+            const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
+            pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
+            aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
+                      ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0;
         }
         StepArgs a{};
         a.count = (int)g.size();
@@ -325,6 +333,12 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
         a.S = ss.data();
         a.C = cs.data();
         a.colscale = ps.data();
+        a.planes = pls.data();
+        if (bf16 && aligned) {
+            st = hip_status(launch_step_bf16(a, (hipStream_t)stream));
+            if (st != DOBB_OK) return st;
+            continue;
+        }
         st = hip_status(launch_step(a, (hipStream_t)stream));
         if (st != DOBB_OK) return st;
     }

@@ -14,15 +14,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Matrices handled by one launch.  Kernels receive a table of per-matrix device pointers by value
 // (kernel arguments are copied at launch, so nothing is staged in device memory); the matrices of
 // one table share a shape.  Launchers split longer lists into chunks of kMaxMats.
-constexpr int kMaxMats = 16;
+constexpr int kMaxMats = 48;
 
 // ---- bf16 helpers (round-to-nearest-even on store; NaN kept quiet) ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : rne);  // NaN stays NaN
 }
 
 // sign with sign(0) = 0 and NaN kept; encoded in int8 as -1, 0, 1 and 0x7f for NaN
@@ -130,8 +129,14 @@ struct StepArgs {
     int8_t *const *S;                 // sign codes m x n
     float *const *C;                  // fp32 coefficients m x n (identity / column-l2 norms)
     float *const *colscale;           // n column scales (column-l2)
+    uint16_t *const *planes;          // bf16 planes of Q (bf16 path)
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+// fp32-accurate bf16-split path for the sign norm (nb <= 512, nb % 4 == 0)
+bool step_bf16_eligible(const dobb_shape &sh, int norm);
+size_t step_bf16_ws_one(const dobb_shape &sh);
+int step_bf16_ldp(int64_t nb);
+hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s);
 
 struct AccumulateArgs {
     int count;
@@ -145,7 +150,7 @@ struct AccumulateArgs {
     double *partial;                  // split-K partial sums (whole group), may be NULL if nsplit == 1
     int nsplit;
 };
-int accumulate_splits(const dobb_shape &sh, int64_t N, int count);
+int accumulate_splits(const dobb_shape &sh, int64_t N, int count, bool bf16);
 size_t accumulate_ws(const dobb_shape &sh, int64_t N, int count);
 hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s);
 

@@ -133,6 +133,159 @@ __global__ void __launch_bounds__(256) k_syrk(int64_t N, int nb, int T, int npai
     }
 }
 
+// ---- bf16 inputs: v_mfma_f32_32x32x16_bf16 --------------------------------------------------
+// Output tile 128 x 128 per workgroup of 8 waves (wave w owns the 32 x 64 piece at rows 32*(w/2),
+// cols 64*(w%2), as 1 x 2 MFMA tiles).  Both MFMA operands want 8 consecutive tokens of one column per
+// lane, so each 128-token chunk is transposed on the way into LDS: each thread loads 8 tokens x 8
+// columns, transposes the 8 x 8 block in registers and writes one 16-byte row per column into
+// xs[strip][col][token].  The products of bf16 values are exact in fp32; the fp32 sums of every 256
+// tokens are folded into fp64 registers.  Diagonal tile pairs load one strip and skip the quarter below the
+// diagonal.  Workgroups are renumbered so the tile pairs of one block run on the same XCD (the
+// dispatcher deals workgroup ids round-robin over the 8 XCDs) and share its L2.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kST = 128, kSK = 128, kSLd = kSK + 8;
+constexpr int kSFold = 2;  // fold fp32 sums into fp64 every 2 chunks (256 tokens)
+
+__device__ __forceinline__ int xcd_remap(int x, int G) {
+    if (G % 8) return x;
+    return (x % 8) * (G / 8) + x / 8;
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_row8(const uint16_t *p, int valid, uint32_t d[4]) {
+    if (valid >= 8 && VEC == 8) {
+        const uint4 v = *(const uint4 *)p;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else if (valid >= 8 && VEC == 4) {
+        const uint2 v0 = *(const uint2 *)p, v1 = *(const uint2 *)(p + 4);
+        d[0] = v0.x; d[1] = v0.y; d[2] = v1.x; d[3] = v1.y;
+    } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) h[c] = c < valid ? p[c] : (uint16_t)0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
+    }
+}
+
+// grid.x = npairs * nblk * count (renumbered per XCD), grid.y = token splits
+template <int VEC>
+__global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int npairs, int nblk, int64_t tok_per_split,
+                                                      int nsplit, float beta, AccTable t, double *partial) {
+    __shared__ __align__(16) uint16_t xs[2][kST][kSLd];
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int pair = x % npairs;
+    const int rest = x / npairs;
+    const int b = rest % nblk, mat = rest / nblk;
+    int ti, tj;
+    tile_pair(pair, T, ti, tj);
+    const bool diag = ti == tj;
+    const int i0 = ti * kST, j0 = tj * kST;
+    const int wi = min(kST, nb - i0), wj = min(kST, nb - j0);
+    const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t te = min<int64_t>(N, tb + tok_per_split);
+    const int64_t ld = t.ldx[mat];
+    const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // loader role: strip ls, columns 8*cg.., tokens 8*tg.. of the chunk (16 x 16 blocks per strip)
+    const int ls = tid >> 8, cg = (tid & 255) >> 4, tg = tid & 15;
+    const bool loader = !(diag && ls == 1);
+    const int lcol0 = (ls ? j0 : i0) + 8 * cg;
+    const int lvalid = (ls ? wj : wi) - 8 * cg;
+    // compute role
+    const int wr = 32 * (w >> 1), wc = 64 * (w & 1);
+    const bool skip = diag && wr >= wc + 64;  // strictly below the diagonal: mirrored from above
+    const int sj = diag ? 0 : 1;
+
+    f32x16 acc[2];
+    double accd[2][16];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        acc[c] = (f32x16){};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accd[c][r] = 0.0;
+    }
+
+    uint32_t d[8][4];
+    auto gload = [&](int64_t t0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t row = t0 + 8 * tg + r;
+            if (loader && row < te && lvalid > 0) load_row8<VEC>(Xb + row * ld + lcol0, lvalid, d[r]);
+            else { d[r][0] = d[r][1] = d[r][2] = d[r][3] = 0u; }
+        }
+    };
+    // software pipeline: the global loads of chunk c+1 are issued before the MFMAs of chunk c
+    if (tb < te) gload(tb);
+    int nchunk = 0;
+    for (int64_t t0 = tb; t0 < te; t0 += kSK) {
+        __syncthreads();  // previous chunk's MFMA reads are done
+        if (loader) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                uint4 o;
+                uint32_t e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = d[2 * q][c >> 1], hi = d[2 * q + 1][c >> 1];
+                    e[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+                }
+                o.x = e[0]; o.y = e[1]; o.z = e[2]; o.w = e[3];
+                *(uint4 *)&xs[ls][8 * cg + c][8 * tg] = o;
+            }
+        }
+        __syncthreads();
+        if (t0 + kSK < te) gload(t0 + kSK);
+        if (!skip) {
+#pragma unroll
+            for (int kk = 0; kk < kSK; kk += 16) {
+                const int kofs = kk + 8 * (lane >> 5);
+                bf16x8 a0 = *(const bf16x8 *)&xs[0][wr + (lane & 31)][kofs];
+                bf16x8 b0 = *(const bf16x8 *)&xs[sj][wc + (lane & 31)][kofs];
+                bf16x8 b1 = *(const bf16x8 *)&xs[sj][wc + 32 + (lane & 31)][kofs];
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[1], 0, 0, 0);
+            }
+            if (++nchunk == kSFold) {
+                nchunk = 0;
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) { accd[c][r] += (double)acc[c][r]; acc[c][r] = 0.f; }
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accd[c][r] += (double)acc[c][r];
+    if (skip) return;
+
+    const double invN = 1.0 / (double)N;
+    const double bd = (double)beta;
+    float *Ab = t.A[mat] + (int64_t)b * nb * nb;
+    const int64_t tot_blocks = gridDim.x / npairs;
+    double *Pb = partial ? partial + ((int64_t)blockIdx.y * tot_blocks + rest) * nb * nb : nullptr;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int gj = j0 + wc + 32 * c + acc_col(lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int gi = i0 + wr + acc_row(r, lane);
+            if (gi >= nb || gj >= nb || gi > gj) continue;
+            if (nsplit == 1) {
+                const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
+                const float v = (float)(bd * old + (1.0 - bd) * (accd[c][r] * invN));
+                Ab[(int64_t)gi * nb + gj] = v;
+                Ab[(int64_t)gj * nb + gi] = v;
+            } else {
+                Pb[(int64_t)gi * nb + gj] = accd[c][r];
+            }
+        }
+    }
+}
+
 // Sum the token-split partials in split order, apply the EMA, write both triangles.
 // grid.x over nb*nb entries of a block, grid.y = block index within the launch (nblk * count).
 __global__ void __launch_bounds__(256) k_syrk_reduce(int64_t N, int nb, int nblk, int nsplit, int64_t tot_blocks,
@@ -157,9 +310,10 @@ __global__ void __launch_bounds__(256) k_syrk_reduce(int64_t N, int nb, int nblk
 
 // Token split plan: enough workgroups for >= 4 per CU, >= 256 tokens per split, split length a
 // multiple of 64 tokens (the fp64 fold period).  Returns the number of splits; *tps its length.
-int accumulate_plan(const dobb_shape &sh, int64_t N, int count, int64_t *tps) {
+int accumulate_plan(const dobb_shape &sh, int64_t N, int count, int64_t *tps, bool bf16) {
     const int nb = (int)sh.nb;
-    const int T = (nb + kBM - 1) / kBM;
+    const int tile = bf16 ? kST : kBM;
+    const int T = (nb + tile - 1) / tile;
     const int64_t tiles = (int64_t)T * (T + 1) / 2 * (sh.n / nb) * (count < kMaxMats ? count : kMaxMats);
     int64_t nsplit = (1024 + tiles - 1) / tiles;
     const int64_t cap = N / 256;
@@ -171,10 +325,13 @@ int accumulate_plan(const dobb_shape &sh, int64_t N, int count, int64_t *tps) {
     return (int)((N + len - 1) / len);
 }
 
-int accumulate_splits(const dobb_shape &sh, int64_t N, int count) { return accumulate_plan(sh, N, count, nullptr); }
+int accumulate_splits(const dobb_shape &sh, int64_t N, int count, bool bf16) {
+    return accumulate_plan(sh, N, count, nullptr, bf16);
+}
 
 size_t accumulate_ws(const dobb_shape &sh, int64_t N, int count) {
-    const int nsplit = accumulate_splits(sh, N, count);
+    const int nsplit = accumulate_splits(sh, N, count, false) > accumulate_splits(sh, N, count, true)
+                           ? accumulate_splits(sh, N, count, false) : accumulate_splits(sh, N, count, true);
     if (nsplit <= 1) return 0;
     const int cnt = count < kMaxMats ? count : kMaxMats;
     return (size_t)nsplit * cnt * (size_t)(sh.n / sh.nb) * sh.nb * sh.nb * sizeof(double);
@@ -183,26 +340,34 @@ size_t accumulate_ws(const dobb_shape &sh, int64_t N, int count) {
 hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
     const int nb = (int)a.sh.nb;
     const int nblk = (int)(a.sh.n / nb);
-    const int T = (nb + kBM - 1) / kBM;
+    const bool xbf = a.x_dtype == DOBB_BF16;
+    const int tile = xbf ? kST : kBM;
+    const int T = (nb + tile - 1) / tile;
     const int npairs = T * (T + 1) / 2;
     int64_t tps = a.N;
-    const int nsplit = accumulate_plan(a.sh, a.N, a.count, &tps);
+    const int nsplit = accumulate_plan(a.sh, a.N, a.count, &tps, xbf);
     if (nsplit <= 1) tps = a.N;
-    const bool xbf = a.x_dtype == DOBB_BF16;
     for (int c0 = 0; c0 < a.count;) {
         const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
         AccTable t{};
-        bool vec = nb % 4 == 0;
+        bool vec4 = nb % 4 == 0, vec8 = nb % 8 == 0;
         for (int i = 0; i < cnt; ++i) {
             t.X[i] = a.X[c0 + i]; t.A[i] = a.A[c0 + i]; t.ldx[i] = a.ldx[c0 + i];
-            vec = vec && (t.ldx[i] % 4 == 0) && (((uintptr_t)t.X[i] & (xbf ? 7u : 15u)) == 0);
+            const uintptr_t p = (uintptr_t)t.X[i];
+            vec4 = vec4 && (t.ldx[i] % 4 == 0) && ((p & (xbf ? 7u : 15u)) == 0);
+            vec8 = vec8 && (t.ldx[i] % 8 == 0) && ((p & 15u) == 0);
         }
         dim3 grid((unsigned)(npairs * nblk * cnt), (unsigned)nsplit);
         double *part = nsplit > 1 ? a.partial : nullptr;
-#define DOBB_SYRK(XB, V) DOBB_LAUNCH("accumulate_syrk", s, (k_syrk<XB, V>), grid, dim3(256), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
-        if (xbf) { if (vec) DOBB_SYRK(true, true); else DOBB_SYRK(true, false); }
-        else { if (vec) DOBB_SYRK(false, true); else DOBB_SYRK(false, false); }
+        if (xbf) {
+#define DOBB_SYRKB(V) DOBB_LAUNCH("accumulate_syrk_bf16", s, (k_syrk_bf16<V>), grid, dim3(512), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
+            if (vec8) DOBB_SYRKB(8); else if (vec4) DOBB_SYRKB(4); else DOBB_SYRKB(1);
+#undef DOBB_SYRKB
+        } else {
+#define DOBB_SYRK(V) DOBB_LAUNCH("accumulate_syrk", s, (k_syrk<false, V>), grid, dim3(256), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
+            if (vec4) DOBB_SYRK(true); else DOBB_SYRK(false);
 #undef DOBB_SYRK
+        }
         if (nsplit > 1) {
             const int64_t tot = (int64_t)nblk * cnt;
             dim3 g2((unsigned)(((int64_t)nb * nb + 255) / 256), (unsigned)tot);

@@ -329,93 +329,461 @@ __global__ void __launch_bounds__(256) k_jacobi_finalize(int nb, int nbp, int nb
     }
 }
 
-// ---- Householder QR --------------------------------------------------------------------------
+// ---- Householder QR, blocked (WY form) ------------------------------------------------------
 // Z (nb x nb, the workspace copy of A_b Q_b) -> Q with diag(R) > 0, written to the Q table.
-// Reflector j: H = I - tau v v^T with v_j = 1, v_i = x_i / (x_j + sgn(x_j) ||x||) (i > j) stored
-// below the diagonal, tau = 1 + |x_j| / ||x||, R_jj = -sgn(x_j) ||x||.  Q = H_0 ... H_{nb-1} is then
-// formed in place from the last reflector to the first, and columns with R_jj < 0 are negated.
-// Dot products and updates are computed in fp64 from fp32 storage.  grid.x = blocks, block 256.
-template <bool LDS>
-__global__ void __launch_bounds__(256) k_householder(int nb, int nblk, float *Z_all, OutTable t) {
+// Panels of kQP = 32 columns.  Each panel is factored column by column in LDS: reflector c is
+// H = I - tau v v^T with v_c = 1, v_r = x_r / (x_c + sgn(x_c) ||x||) below, tau = 1 + |x_c| / ||x||,
+// R_cc = -sgn(x_c) ||x||.  The panel's reflectors are combined as H_1..H_w = I - V T V^T, with T
+// upper triangular from V^T V and the taus; the trailing columns are updated as
+// Z <- Z - V T^T (V^T Z) with three fp32 MFMA 32x32x2 products per 32-column tile (one tile per
+// wave).  V and T of every panel are kept (V in Z's panel columns, T in the workspace); Q is then
+// formed from the identity by applying the block reflectors last to first, Q <- Q - V T (V^T Q), and
+// the columns with R_cc < 0 are negated.  Z lives in LDS when it fits, in the workspace otherwise.
+constexpr int kQP = 32;
+constexpr int kQrLdsMaxNb = 64;  // blocks up to this width use the single-workgroup LDS kernel
+
+struct QrLayout {
+    size_t red, tau, gsh, tsd, part, wk, ts, wsh, neg, vs, zs, total;
+};
+__host__ __device__ inline size_t al16(size_t x) { return (x + 15) / 16 * 16; }
+__host__ __device__ inline QrLayout qr_layout(int nb, bool zlds) {
+    QrLayout L;
+    size_t o = 0;
+    L.red = o;  o += al16(8 * 8);
+    L.tau = o;  o += al16(kQP * 8);
+    L.gsh = o;  o += al16(kQP * kQP * 8);
+    L.tsd = o;  o += al16(kQP * kQP * 8);
+    L.part = o; o += al16(8 * kQP * 8);
+    L.wk = o;   o += al16(kQP * 8);
+    L.ts = o;   o += al16(kQP * (kQP + 1) * 4);
+    L.wsh = o;  o += al16(4 * 32 * 33 * 4);
+    L.neg = o;  o += al16((size_t)nb);
+    L.vs = o;   o += al16((size_t)nb * (kQP + 1) * 4);
+    L.zs = o;   o += zlds ? al16((size_t)nb * (nb + 1) * 4) : 0;
+    L.total = o;
+    return L;
+}
+
+// acc (32x32, MFMA layout) -> S[32][33]
+__device__ __forceinline__ void acc_to_lds(const f32x16 &acc, float (*S)[33], int lane) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[acc_row(r, lane)][acc_col(lane)] = acc[r];
+}
+
+// One 32-column tile update, run by one wave:  X[rows, c0:c0+32] -= V op(T) (V^T X[rows, c0:c0+32])
+// X rows are offset by j0 (row r of the tile is X row j0 + r).  op(T) = T^T (factorisation) or T.
+template <bool TRANS_T>
+__device__ __forceinline__ void wy_tile(float *X, int ldx, int ncols_total, int j0, int rows, int c0,
+                                        const float (*Vs)[kQP + 1], const float (*Ts)[kQP + 1], float (*W)[33],
+                                        int lane, bool active) {
+    f32x16 acc = {};
+    if (active) {
+        const int kr = lane >> 5, cc = lane & 31;
+        const bool colok = c0 + cc < ncols_total;
+#pragma unroll 8
+        for (int k = 0; k < rows; k += 2) {
+            const int r = k + kr;
+            const float a = r < rows ? Vs[r][cc] : 0.f;
+            const float bz = (r < rows && colok) ? X[(int64_t)(j0 + r) * ldx + c0 + cc] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bz, acc, 0, 0, 0);
+        }
+        acc_to_lds(acc, W, lane);
+    }
+    __syncthreads();
+    f32x16 y = {};
+    if (active) {
+#pragma unroll
+        for (int kk = 0; kk < kQP; kk += 2) {
+            const int k = kk + (lane >> 5), i = lane & 31;
+            const float a = TRANS_T ? Ts[k][i] : Ts[i][k];
+            y = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][i], y, 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    if (active) acc_to_lds(y, W, lane);
+    __syncthreads();
+    if (active) {
+        for (int r0 = 0; r0 < rows; r0 += 32) {
+            f32x16 u = {};
+#pragma unroll
+            for (int kk = 0; kk < kQP; kk += 2) {
+                const int k = kk + (lane >> 5), rr = r0 + (lane & 31);
+                const float a = rr < rows ? Vs[rr][k] : 0.f;
+                u = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][lane & 31], u, 0, 0, 0);
+            }
+            const int col = c0 + acc_col(lane);
+            if (col < ncols_total) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + acc_row(r, lane);
+                    if (row < rows) X[(int64_t)(j0 + row) * ldx + col] -= u[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// grid.x = blocks, block 256 (4 waves)
+template <bool ZLDS>
+__global__ void __launch_bounds__(256) k_householder(int nb, int nblk, float *Z_all, float *Tq_all, OutTable t,
+                                                     int info_value) {
     extern __shared__ __align__(16) unsigned char dsm[];
+    const QrLayout L = qr_layout(nb, ZLDS);
+    double *red = (double *)(dsm + L.red);
+    double *tau = (double *)(dsm + L.tau);
+    double *gsh = (double *)(dsm + L.gsh);
+    double *tsd = (double *)(dsm + L.tsd);
+    double *part = (double *)(dsm + L.part);
+    double *wk = (double *)(dsm + L.wk);
+    float(*Ts)[kQP + 1] = (float(*)[kQP + 1])(dsm + L.ts);
+    float(*Wsh)[32][33] = (float(*)[32][33])(dsm + L.wsh);
+    int8_t *neg = (int8_t *)(dsm + L.neg);
+    float(*Vs)[kQP + 1] = (float(*)[kQP + 1])(dsm + L.vs);
+
     const int g = blockIdx.x;
     const int b = g % nblk, mat = g / nblk;
-    const int tid = threadIdx.x;
-    double *tau = (double *)dsm;      // nb
-    double *wv = tau + nb;            // nb
-    double *red = wv + nb;            // 4 wave partials + 3 scalars
-    int8_t *neg = (int8_t *)(red + 8);  // nb
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int npanel = (nb + kQP - 1) / kQP;
     float *Zg = Z_all + (int64_t)g * nb * nb;
-    const int ld = LDS ? nb + 1 : nb;
-    float *Z = LDS ? (float *)(dsm + ((size_t)(2 * nb + 8) * 8 + nb + 15) / 16 * 16) : Zg;
-    if (LDS) for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) Z[(e / nb) * ld + e % nb] = Zg[e];
+    float *Tq = Tq_all + (int64_t)g * npanel * kQP * kQP;
+    const int ldz = ZLDS ? nb + 1 : nb;
+    float *Z = ZLDS ? (float *)(dsm + L.zs) : Zg;
+    if (ZLDS) for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) Z[(e / nb) * ldz + e % nb] = Zg[e];
     __syncthreads();
 
-    for (int j = 0; j < nb; ++j) {
-        double part = 0.0;
-        for (int i = j + tid; i < nb; i += 256) { const double x = Z[(int64_t)i * ld + j]; part += x * x; }
-        for (int o = 32; o > 0; o >>= 1) part += __shfl_down(part, o, 64);
-        if ((tid & 63) == 0) red[tid >> 6] = part;
+    for (int p = 0; p < npanel; ++p) {
+        const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
+        for (int e = tid; e < rows * kQP; e += 256) {
+            const int r = e / kQP, c = e % kQP;
+            Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
+        }
+        __syncthreads();
+        // factor the panel
+        for (int c = 0; c < w; ++c) {
+            double ps = 0.0;
+            for (int r = c + tid; r < rows; r += 256) { const double x = Vs[r][c]; ps += x * x; }
+            for (int o = 32; o > 0; o >>= 1) ps += __shfl_down(ps, o, 64);
+            if (lane == 0) red[wv] = ps;
+            __syncthreads();
+            if (tid == 0) {
+                const double alpha = sqrt(red[0] + red[1] + red[2] + red[3]);
+                const double x0 = Vs[c][c];
+                const double sg = x0 >= 0.0 ? 1.0 : -1.0;
+                if (alpha == 0.0) { tau[c] = 0.0; red[4] = 1.0; red[5] = 0.0; }
+                else { tau[c] = 1.0 + fabs(x0) / alpha; red[4] = x0 + sg * alpha; red[5] = -sg * alpha; }
+                neg[j0 + c] = red[5] < 0.0;
+            }
+            __syncthreads();
+            const double u0 = red[4], tc = tau[c];
+            for (int r = c + 1 + tid; r < rows; r += 256) Vs[r][c] = (float)((double)Vs[r][c] / u0);
+            __syncthreads();
+            {   // s_k = v^T panel[:, k] for k in (c, w): 8 row groups x 32 columns
+                const int k = tid & 31, grp = tid >> 5;
+                double sk = 0.0;
+                if (k > c && k < w) {
+                    for (int r = c + grp; r < rows; r += 8) {
+                        const double v = r == c ? 1.0 : (double)Vs[r][c];
+                        sk += v * (double)Vs[r][k];
+                    }
+                }
+                part[grp * kQP + k] = sk;
+            }
+            __syncthreads();
+            if (tid < kQP) {
+                double sk = 0.0;
+                for (int q = 0; q < 8; ++q) sk += part[q * kQP + tid];
+                wk[tid] = tc * sk;
+            }
+            __syncthreads();
+            for (int e = tid; e < (rows - c) * kQP; e += 256) {
+                const int r = c + e / kQP, k = e % kQP;
+                if (k > c && k < w) {
+                    const double v = r == c ? 1.0 : (double)Vs[r][c];
+                    Vs[r][k] = (float)((double)Vs[r][k] - v * wk[k]);
+                }
+            }
+            __syncthreads();
+        }
+        // explicit V: unit diagonal, zeros above
+        for (int e = tid; e < rows * kQP; e += 256) {
+            const int r = e / kQP, c = e % kQP;
+            if (c < w) { if (r == c) Vs[r][c] = 1.f; else if (r < c) Vs[r][c] = 0.f; }
+        }
+        __syncthreads();
+        // G = V^T V (upper part) in fp64
+        for (int e = tid; e < kQP * kQP; e += 256) {
+            const int i = e / kQP, j = e % kQP;
+            double sgv = 0.0;
+            if (i < j && j < w)
+                for (int r = i; r < rows; ++r) sgv += (double)Vs[r][i] * (double)Vs[r][j];
+            gsh[e] = sgv;
+            tsd[e] = 0.0;
+        }
+        __syncthreads();
+        // T: T_jj = tau_j, T[0:j, j] = -tau_j T[0:j, 0:j] G[0:j, j]
+        for (int j = 0; j < w; ++j) {
+            if (tid < j) {
+                double sum = 0.0;
+                for (int k = tid; k < j; ++k) sum += tsd[tid * kQP + k] * gsh[k * kQP + j];
+                tsd[tid * kQP + j] = -tau[j] * sum;
+            }
+            if (tid == j) tsd[j * kQP + j] = tau[j];
+            __syncthreads();
+        }
+        for (int e = tid; e < kQP * kQP; e += 256) {
+            const int i = e / kQP, j = e % kQP;
+            Ts[i][j] = (float)tsd[e];
+            Tq[(int64_t)p * kQP * kQP + e] = (float)tsd[e];
+        }
+        // keep V in Z's panel columns for the formation of Q
+        for (int e = tid; e < rows * w; e += 256) {
+            const int r = e / w, c = e % w;
+            Z[(int64_t)(j0 + r) * ldz + j0 + c] = Vs[r][c];
+        }
+        __syncthreads();
+        // trailing update, one 32-column tile per wave per round
+        const int first = j0 + w;
+        const int ntiles = (nb - first + 31) / 32;
+        for (int it = 0; it < (ntiles + 3) / 4; ++it) {
+            const int tile = it * 4 + wv;
+            wy_tile<true>(Z, ldz, nb, j0, rows, first + tile * 32, Vs, Ts, Wsh[wv], lane, tile < ntiles);
+        }
+    }
+
+    // form Q = H_1 ... H_nb from the identity, block reflectors applied last to first
+    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+    for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+    __syncthreads();
+    for (int p = npanel - 1; p >= 0; --p) {
+        const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
+        for (int e = tid; e < rows * kQP; e += 256) {
+            const int r = e / kQP, c = e % kQP;
+            Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
+        }
+        for (int e = tid; e < kQP * kQP; e += 256) Ts[e / kQP][e % kQP] = Tq[(int64_t)p * kQP * kQP + e];
+        __syncthreads();
+        const int ntiles = (nb - j0 + 31) / 32;
+        for (int it = 0; it < (ntiles + 3) / 4; ++it) {
+            const int tile = it * 4 + wv;
+            wy_tile<false>(Q, nb, nb, j0, rows, j0 + tile * 32, Vs, Ts, Wsh[wv], lane, tile < ntiles);
+        }
+    }
+    for (int64_t e = tid; e < (int64_t)nb * nb; e += 256)
+        if (neg[e % nb]) Q[e] = -Q[e];
+    if (tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
+}
+
+// ---- Householder QR, blocked, one launch per panel step (large blocks) ------------------------
+// The same algorithm as k_householder, split so the trailing updates spread over the whole GPU:
+//   k_qr_panel   one workgroup per block factors panel p (32 columns) in LDS, writes V into Z's
+//                panel columns, T into the workspace and the signs of R's diagonal;
+//   k_qr_update  one workgroup per (block, 64-column tile) applies the panel's block reflector:
+//                X <- X - V op(T) (V^T X), with op(T) = T^T while factoring Z and op(T) = T while
+//                forming Q from the identity (panels last to first);
+//   k_qr_finish  negates the columns of Q with R_cc < 0 and writes info.
+struct QrPanelLayout {
+    size_t red, tau, gsh, tsd, part, wk, vs, total;
+};
+__host__ __device__ inline QrPanelLayout qr_panel_layout(int nb) {
+    QrPanelLayout L;
+    size_t o = 0;
+    L.red = o;  o += al16(8 * 8);
+    L.tau = o;  o += al16(kQP * 8);
+    L.gsh = o;  o += al16(kQP * kQP * 8);
+    L.tsd = o;  o += al16(kQP * kQP * 8);
+    L.part = o; o += al16(8 * kQP * 8);
+    L.wk = o;   o += al16(kQP * 8);
+    L.vs = o;   o += al16((size_t)nb * (kQP + 1) * 4);
+    L.total = o;
+    return L;
+}
+
+// grid.x = blocks, block 256
+__global__ void __launch_bounds__(256) k_qr_panel(int nb, int p, float *Z_all, float *Tq_all, int8_t *neg_all) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    const QrPanelLayout L = qr_panel_layout(nb);
+    double *red = (double *)(dsm + L.red);
+    double *tau = (double *)(dsm + L.tau);
+    double *gsh = (double *)(dsm + L.gsh);
+    double *tsd = (double *)(dsm + L.tsd);
+    double *part = (double *)(dsm + L.part);
+    double *wk = (double *)(dsm + L.wk);
+    float(*Vs)[kQP + 1] = (float(*)[kQP + 1])(dsm + L.vs);
+    const int g = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int npanel = (nb + kQP - 1) / kQP;
+    float *Z = Z_all + (int64_t)g * nb * nb;
+    float *Tq = Tq_all + ((int64_t)g * npanel + p) * kQP * kQP;
+    int8_t *neg = neg_all + (int64_t)g * nb;
+    const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
+    for (int e = tid; e < rows * kQP; e += 256) {
+        const int r = e / kQP, c = e % kQP;
+        Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * nb + j0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < w; ++c) {
+        double ps = 0.0;
+        for (int r = c + tid; r < rows; r += 256) { const double x = Vs[r][c]; ps += x * x; }
+        for (int o = 32; o > 0; o >>= 1) ps += __shfl_down(ps, o, 64);
+        if (lane == 0) red[wv] = ps;
         __syncthreads();
         if (tid == 0) {
-            const double norm2 = red[0] + red[1] + red[2] + red[3];
-            const double alpha = sqrt(norm2);
-            const double x0 = Z[(int64_t)j * ld + j];
+            const double alpha = sqrt(red[0] + red[1] + red[2] + red[3]);
+            const double x0 = Vs[c][c];
             const double sg = x0 >= 0.0 ? 1.0 : -1.0;
-            if (alpha == 0.0) { tau[j] = 0.0; red[4] = 1.0; red[5] = 0.0; }
-            else { tau[j] = 1.0 + fabs(x0) / alpha; red[4] = x0 + sg * alpha; red[5] = -sg * alpha; }
+            if (alpha == 0.0) { tau[c] = 0.0; red[4] = 1.0; red[5] = 0.0; }
+            else { tau[c] = 1.0 + fabs(x0) / alpha; red[4] = x0 + sg * alpha; red[5] = -sg * alpha; }
+            neg[j0 + c] = red[5] < 0.0;
         }
         __syncthreads();
-        const double tj = tau[j];
-        const double u0 = red[4];
-        for (int i = j + 1 + tid; i < nb; i += 256) Z[(int64_t)i * ld + j] = (float)((double)Z[(int64_t)i * ld + j] / u0);
+        const double u0 = red[4], tc = tau[c];
+        for (int r = c + 1 + tid; r < rows; r += 256) Vs[r][c] = (float)((double)Vs[r][c] / u0);
         __syncthreads();
-        for (int k = j + 1 + tid; k < nb; k += 256) {
-            double s = Z[(int64_t)j * ld + k];
-            for (int i = j + 1; i < nb; ++i) s += (double)Z[(int64_t)i * ld + j] * (double)Z[(int64_t)i * ld + k];
-            wv[k] = tj * s;
-        }
-        __syncthreads();
-        const int w = nb - j - 1;
-        for (int64_t e = tid; e < (int64_t)(nb - j) * w; e += 256) {
-            const int i = j + (int)(e / w), k = j + 1 + (int)(e % w);
-            const double vi = i == j ? 1.0 : (double)Z[(int64_t)i * ld + j];
-            Z[(int64_t)i * ld + k] = (float)((double)Z[(int64_t)i * ld + k] - vi * wv[k]);
-        }
-        if (tid == 0) { neg[j] = red[5] < 0.0; Z[(int64_t)j * ld + j] = (float)red[5]; }
-        __syncthreads();
-    }
-    // form Q in place: for j = nb-1 .. 0, apply H_j to the already formed trailing columns
-    for (int j = nb - 1; j >= 0; --j) {
-        const double tj = tau[j];
-        if (j < nb - 1) {
-            for (int k = j + 1 + tid; k < nb; k += 256) {
-                double s = Z[(int64_t)j * ld + k];  // row j of a formed column is zero; kept for clarity
-                for (int i = j + 1; i < nb; ++i) s += (double)Z[(int64_t)i * ld + j] * (double)Z[(int64_t)i * ld + k];
-                wv[k] = tj * s;
+        {
+            const int k = tid & 31, grp = tid >> 5;
+            double sk = 0.0;
+            if (k > c && k < w) {
+                for (int r = c + grp; r < rows; r += 8) {
+                    const double v = r == c ? 1.0 : (double)Vs[r][c];
+                    sk += v * (double)Vs[r][k];
+                }
             }
-            __syncthreads();
-            const int w = nb - j - 1;
-            for (int64_t e = tid; e < (int64_t)(nb - j) * w; e += 256) {
-                const int i = j + (int)(e / w), k = j + 1 + (int)(e % w);
-                const double vi = i == j ? 1.0 : (double)Z[(int64_t)i * ld + j];
-                Z[(int64_t)i * ld + k] = (float)((double)Z[(int64_t)i * ld + k] - vi * wv[k]);
-            }
-            __syncthreads();
+            part[grp * kQP + k] = sk;
         }
-        for (int i = tid; i < nb; i += 256) {
-            if (i > j) Z[(int64_t)i * ld + j] = (float)(-tj * (double)Z[(int64_t)i * ld + j]);
-            else if (i == j) Z[(int64_t)i * ld + j] = (float)(1.0 - tj);
-            else Z[(int64_t)i * ld + j] = 0.f;
+        __syncthreads();
+        if (tid < kQP) {
+            double sk = 0.0;
+            for (int q = 0; q < 8; ++q) sk += part[q * kQP + tid];
+            wk[tid] = tc * sk;
+        }
+        __syncthreads();
+        for (int e = tid; e < (rows - c) * kQP; e += 256) {
+            const int r = c + e / kQP, k = e % kQP;
+            if (k > c && k < w) {
+                const double v = r == c ? 1.0 : (double)Vs[r][c];
+                Vs[r][k] = (float)((double)Vs[r][k] - v * wk[k]);
+            }
         }
         __syncthreads();
     }
+    for (int e = tid; e < rows * kQP; e += 256) {
+        const int r = e / kQP, c = e % kQP;
+        if (c < w) { if (r == c) Vs[r][c] = 1.f; else if (r < c) Vs[r][c] = 0.f; }
+    }
+    __syncthreads();
+    for (int e = tid; e < kQP * kQP; e += 256) {
+        const int i = e / kQP, j = e % kQP;
+        double sgv = 0.0;
+        if (i < j && j < w)
+            for (int r = i; r < rows; ++r) sgv += (double)Vs[r][i] * (double)Vs[r][j];
+        gsh[e] = sgv;
+        tsd[e] = 0.0;
+    }
+    __syncthreads();
+    for (int j = 0; j < w; ++j) {
+        if (tid < j) {
+            double sum = 0.0;
+            for (int k = tid; k < j; ++k) sum += tsd[tid * kQP + k] * gsh[k * kQP + j];
+            tsd[tid * kQP + j] = -tau[j] * sum;
+        }
+        if (tid == j) tsd[j * kQP + j] = tau[j];
+        __syncthreads();
+    }
+    for (int e = tid; e < kQP * kQP; e += 256) Tq[e] = (float)tsd[e];
+    for (int e = tid; e < rows * w; e += 256) {
+        const int r = e / w, c = e % w;
+        Z[(int64_t)(j0 + r) * nb + j0 + c] = Vs[r][c];
+    }
+}
+
+// grid = (64-column tiles, blocks), block 256: wave w works on column half h = w & 1 of the tile;
+// for V^T X the two waves of a half split the rows, for X -= V Y they split 32-row chunks.
+template <bool FACTOR>
+__global__ void __launch_bounds__(256) k_qr_update(int nb, int nblk, int p, const float *Z_all, const float *Tq_all,
+                                                   OutTable t) {
+    __shared__ float Ts[kQP][kQP + 1];
+    __shared__ float Wp[2][2][32][33];   // [row half][column half]
+    __shared__ float Ysh[2][32][33];
+    const int g = blockIdx.y;
+    const int b = g % nblk, mat = g / nblk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int h = wv & 1, kp = wv >> 1;
+    const int npanel = (nb + kQP - 1) / kQP;
+    const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
+    const float *Z = Z_all + (int64_t)g * nb * nb;       // V of panel p in columns j0..j0+w
+    float *X = FACTOR ? (float *)Z_all + (int64_t)g * nb * nb : t.Q[mat] + (int64_t)b * nb * nb;
+    const int first = FACTOR ? j0 + w : j0;
+    const int c0 = first + blockIdx.x * 64 + 32 * h;
+    const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kQP * kQP;
+    for (int e = tid; e < kQP * kQP; e += 256) Ts[e / kQP][e % kQP] = Tq[e];
+    const int cc = lane & 31, kr = lane >> 5;
+    const bool colok = c0 + cc < nb;
+    const bool vok = cc < w;
+    // W partial = V[rows of this half]^T X
+    {
+        const int half = (rows + 1) / 2;
+        const int rbeg = kp ? half : 0, rend = kp ? rows : half;
+        f32x16 acc = {};
+#pragma unroll 8
+        for (int k = rbeg; k < rend; k += 2) {
+            const int r = k + kr;
+            const bool rok = r < rend;
+            const float a = (rok && vok) ? Z[(int64_t)(j0 + r) * nb + j0 + cc] : 0.f;
+            const float bx = (rok && colok) ? X[(int64_t)(j0 + r) * nb + c0 + cc] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bx, acc, 0, 0, 0);
+        }
+        acc_to_lds(acc, Wp[kp][h], lane);
+    }
+    __syncthreads();
+    if (kp == 0) {   // Y = op(T) W for this column half
+        f32x16 y = {};
+#pragma unroll
+        for (int kk = 0; kk < kQP; kk += 2) {
+            const int k = kk + kr;
+            const float a = FACTOR ? Ts[k][cc] : Ts[cc][k];
+            const float wkj = Wp[0][h][k][cc] + Wp[1][h][k][cc];
+            y = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wkj, y, 0, 0, 0);
+        }
+        acc_to_lds(y, Ysh[h], lane);
+    }
+    __syncthreads();
+    // X -= V Y: chunks of 32 rows, alternating between the two waves of this half
+    for (int r0 = 32 * kp; r0 < rows; r0 += 64) {
+        f32x16 u = {};
+        const int rr = r0 + cc;
+#pragma unroll
+        for (int kk = 0; kk < kQP; kk += 2) {
+            const int k = kk + kr;
+            const float a = (rr < rows && k < w) ? Z[(int64_t)(j0 + rr) * nb + j0 + k] : 0.f;
+            u = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Ysh[h][k][cc], u, 0, 0, 0);
+        }
+        const int col = c0 + acc_col(lane);
+        if (col < nb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0 + acc_row(r, lane);
+                if (row < rows) X[(int64_t)(j0 + row) * nb + col] -= u[r];
+            }
+        }
+    }
+}
+
+// Q := I before the formation sweep.  grid = blocks.
+__global__ void __launch_bounds__(256) k_qr_identity(int nb, int nblk, OutTable t) {
+    const int g = blockIdx.x;
+    float *Q = t.Q[g / nblk] + (int64_t)(g % nblk) * nb * nb;
+    for (int64_t e = threadIdx.x; e < (int64_t)nb * nb; e += 256) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+}
+
+__global__ void __launch_bounds__(256) k_qr_finish(int nb, int nblk, const int8_t *neg_all, OutTable t, int info_value) {
+    const int g = blockIdx.x;
+    const int b = g % nblk, mat = g / nblk;
     float *Q = t.Q[mat] + (int64_t)b * nb * nb;
-    for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) {
-        const int i = (int)(e / nb), j = (int)(e % nb);
-        const float v = Z[(int64_t)i * ld + j];
-        Q[e] = neg[j] ? -v : v;
-    }
+    const int8_t *neg = neg_all + (int64_t)g * nb;
+    for (int64_t e = threadIdx.x; e < (int64_t)nb * nb; e += 256)
+        if (neg[e % nb]) Q[e] = -Q[e];
+    if (threadIdx.x == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
 }
 
 // lambda_j = q_j^T (A q_j), with T = A Q in the workspace.  grid.x = blocks.
@@ -435,7 +803,7 @@ __global__ void __launch_bounds__(256) k_rayleigh(int nb, int nblk, const float 
 // ---- workspace layout: five regions, each an array of dense per-block records ----------------
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 struct Regions {
-    size_t aw, v, t, tlog, state, total;
+    size_t aw, v, t, tlog, state, tq, neg, total;
 };
 Regions regions(int64_t nb, int64_t nblocks) {
     const int64_t nbp = (nb + 1) / 2 * 2;
@@ -445,7 +813,9 @@ Regions regions(int64_t nb, int64_t nblocks) {
     R.t = al256((size_t)nb * nb * 8 * nblocks);     // T: nb x nb, fp32 (A Q products) or fp64 (refinement)
     R.tlog = al256((size_t)(nbp - 1) * (nbp / 2) * 8 * nblocks);   // tangents of one sweep
     R.state = al256((size_t)16 * nblocks);                         // 4 ints
-    R.total = R.aw + R.v + R.t + R.tlog + R.state;
+    R.tq = al256((size_t)((nb + kQP - 1) / kQP) * kQP * kQP * 4 * nblocks);  // QR panel T factors
+    R.neg = al256((size_t)nb * nblocks);                                      // signs of diag(R)
+    R.total = R.aw + R.v + R.t + R.tlog + R.state + R.tq + R.neg;
     return R;
 }
 
@@ -460,10 +830,6 @@ constexpr int kMaxFp64Sweeps = 8;
 __global__ void k_stage_flag(int32_t *state_all) {
     const int g = blockIdx.x;
     if (threadIdx.x == 0) state_all[4 * g + 3] = state_all[4 * g + 1];
-}
-size_t householder_lds_bytes(int nb, bool lds) {
-    size_t head = ((size_t)(2 * nb + 8) * 8 + nb + 15) / 16 * 16;
-    return head + (lds ? (size_t)nb * (nb + 1) * 4 : 0);
 }
 
 }  // namespace
@@ -489,6 +855,8 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
         float *Tm = (float *)(base + R.aw + R.v);
         double *tlog = (double *)(base + R.aw + R.v + R.t);
         int32_t *state = (int32_t *)(base + R.aw + R.v + R.t + R.tlog);
+        float *tq = (float *)(base + R.aw + R.v + R.t + R.tlog + R.state);
+        int8_t *negs = (int8_t *)(base + R.aw + R.v + R.t + R.tlog + R.state + R.tq);
         const int64_t aw_stride = (int64_t)nbp * nbp, t_stride = (int64_t)nb * nb;
 
         OutTable ot{};
@@ -572,23 +940,45 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
                             nbp, nblk, (const double *)Aw64, (const double *)V, (const int32_t *)state, ot);
             }
         } else {
-            const size_t hl = householder_lds_bytes(nb, true);
-            const bool lds = (int64_t)hl <= lds_max;
-            const size_t hsh = householder_lds_bytes(nb, lds);
+            // small blocks: one workgroup per block with Z in LDS; larger ones: one launch per panel step
+            const size_t hl = qr_layout(nb, true).total;
+            const bool lds = nb <= kQrLdsMaxNb && (int64_t)hl <= lds_max;
+            const size_t pl = qr_panel_layout(nb).total;
             if (lds) (void)hipFuncSetAttribute((const void *)k_householder<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hl);
+            else (void)hipFuncSetAttribute((const void *)k_qr_panel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl);
+            const int npanel = (nb + kQP - 1) / kQP;
             for (int it = 0; it < a.iters; ++it) {
                 DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
-                if (lds) DOBB_LAUNCH("householder_qr", s, k_householder<true>, dim3((unsigned)nblocks), dim3(256), hsh, nb, nblk,
-                                     Tm, ot);
-                else DOBB_LAUNCH("householder_qr", s, k_householder<false>, dim3((unsigned)nblocks), dim3(256), hsh, nb, nblk,
-                                 Tm, ot);
+                const int infov = it == a.iters - 1 ? a.iters : 0;
+                if (lds) {
+                    DOBB_LAUNCH("householder_qr_lds", s, k_householder<true>, dim3((unsigned)nblocks), dim3(256), hl, nb, nblk,
+                                Tm, tq, ot, infov);
+                    continue;
+                }
+                for (int p = 0; p < npanel; ++p) {
+                    DOBB_LAUNCH("qr_panel", s, k_qr_panel, dim3((unsigned)nblocks), dim3(256), pl, nb, p, Tm, tq, negs);
+                    const int first = p * kQP + (nb - p * kQP < kQP ? nb - p * kQP : kQP);
+                    const int ntiles = (nb - first + 63) / 64;
+                    if (ntiles > 0)
+                        DOBB_LAUNCH("qr_update", s, k_qr_update<true>, dim3((unsigned)ntiles, (unsigned)nblocks), dim3(256), 0, nb,
+                                    nblk, p, (const float *)Tm, (const float *)tq, ot);
+                }
+                DOBB_LAUNCH("qr_identity", s, k_qr_identity, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, ot);
+                for (int p = npanel - 1; p >= 0; --p) {
+                    const int ntiles = (nb - p * kQP + 63) / 64;
+                    DOBB_LAUNCH("qr_form", s, k_qr_update<false>, dim3((unsigned)ntiles, (unsigned)nblocks), dim3(256), 0, nb,
+                                nblk, p, (const float *)Tm, (const float *)tq, ot);
+                }
+                DOBB_LAUNCH("qr_finish", s, k_qr_finish, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, (const int8_t *)negs,
+                            ot, infov);
             }
-            bool want_lam = false, want_info = false;
-            for (int i = 0; i < cnt; ++i) { want_lam |= ot.lam[i] != nullptr; want_info |= ot.info[i] != nullptr; }
-            if (want_lam) DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
-            if (want_lam || want_info)
+            bool want_lam = false;
+            for (int i = 0; i < cnt; ++i) want_lam |= ot.lam[i] != nullptr;
+            if (want_lam) {
+                DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
                 DOBB_LAUNCH("rayleigh", s, k_rayleigh, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, (const float *)Tm, ot,
                             a.iters);
+            }
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

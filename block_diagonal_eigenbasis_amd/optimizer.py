@@ -88,9 +88,13 @@ class DobbGroup:
             self.count, self._ash, xp, _abi._dtype_code(xs[0]), N, self._ldx, float(beta), self._A,
             self.ws.data_ptr(), self.ws.numel(), self._stream(stream)), "dobb_accumulate_moment_grouped")
 
-    def refresh(self, mode: int, iters: int, warm_start: bool = True, tol: float = 0.0, stream=None) -> None:
+    def refresh(self, mode: int, iters: int, warm_start: bool = True, tol: float = 0.0, want_lambda: bool = False,
+                stream=None) -> None:
+        """Refresh every basis; lambda is filled for the exact mode, and for orthogonal iteration only
+        when want_lambda (Rayleigh quotients cost an extra product per block)."""
+        lam = self._lam if (want_lambda or mode == _abi.DOBB_REFRESH_EXACT) else None
         _abi._check(_abi.lib().dobb_refresh_basis_grouped(
-            self.count, self._ash, self._A, self._Q, self._lam, int(mode), int(iters), int(bool(warm_start)),
+            self.count, self._ash, self._A, self._Q, lam, int(mode), int(iters), int(bool(warm_start)),
             float(tol), self._info, self.ws.data_ptr(), self.ws.numel(), self._stream(stream)),
             "dobb_refresh_basis_grouped")
         self.refreshes += 1

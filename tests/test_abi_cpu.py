@@ -115,9 +115,10 @@ def test_workspace_sizes():
     assert r >= 4 * (192 * 192 * (4 + 8 + 4))
     assert ws(_abi.DOBB_OP_REFRESH, [(1, 770, 192)]) == 0         # n % nb != 0
     assert ws(_abi.DOBB_OP_ACCUMULATE, [(1, 768, 192)], 0) == 0   # N < 1
-    # a group larger than one launch chunk reuses the chunk's workspace
-    big = ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 40, 0, 0)
-    assert big == ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 16, 0, 0)
+    # a group larger than one launch chunk (48 matrices) reuses the chunk's workspace
+    big = ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 60, 0, 0)
+    assert big == ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 48, 0, 0)
+    assert big > ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 16, 0, 0)
 
 
 def test_grouped_rejects_mixed_norms():

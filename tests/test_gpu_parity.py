@@ -373,8 +373,9 @@ def test_profiler_reports_kernels():
     torch.cuda.synchronize()
     dobb.dobb_profile_enable(False)
     rep = dobb.dobb_profile_read()
-    for k in ("momentum", "project", "reconstruct"):
-        assert k in rep and rep[k][0] >= 1 and rep[k][1] > 0
+    assert any(k.startswith("project") for k in rep) and any(k.startswith("reconstruct") for k in rep)
+    for k, (launches, ms) in rep.items():
+        assert launches >= 1 and ms > 0
     dobb.dobb_profile_reset()
 
 

@@ -78,10 +78,11 @@ def activations_torch(N: int, n: int, target: float, seed: int, device, dtype, b
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     lam = torch.from_numpy(power_law(n, target)).to(device=device, dtype=torch.float32)
-    if basis is None:
-        gq = torch.randn(n, n, generator=g, device=device, dtype=torch.float32)
-        q, r = torch.linalg.qr(gq)
-        basis = q * torch.sign(torch.diagonal(r))
+    if basis is None:  # Haar basis from a CPU QR (keeps GPU solver libraries out of the picture)
+        gc = torch.Generator()
+        gc.manual_seed(int(seed))
+        q, r = torch.linalg.qr(torch.randn(n, n, generator=gc, dtype=torch.float64))
+        basis = (q * torch.sign(torch.diagonal(r))).to(device=device, dtype=torch.float32)
     Z = torch.randn(N, n, generator=g, device=device, dtype=torch.float32)
     X = (Z * lam.sqrt()) @ basis.T
     return X.to(dtype), basis
