@@ -16,6 +16,8 @@
 //   k_proj_bf16    M <- mu M + G fused; C = P Q (P = M or G + mu M); S = sign(C) as int8 codes
 //   k_recon_bf16   U = S Q^T;  W <- W - lr (s U + wd W)
 // A workgroup owns 128 rows x the whole block width, so it writes its rows of M exactly once.
+// Signs travel from the projection to the reconstruction as one byte each: the high byte of the
+// fp16 value (+1 -> 0x3c, -1 -> 0xbc, 0 -> 0x00, NaN -> 0x7e), so a byte permute rebuilds fp16.
 // Workgroup ids are renumbered so the row tiles of one block run on one XCD and share Q_b in L2.
 #include "dobb_internal.h"
 
@@ -53,6 +55,10 @@ __device__ __forceinline__ void split2h(float v, uint16_t &h, uint16_t &l) {
     const _Float16 a = (_Float16)v;
     h = __builtin_bit_cast(uint16_t, a);
     l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)a));
+}
+
+__device__ __forceinline__ uint8_t sign_f16_hi(float c) {
+    return c > 0.f ? (uint8_t)0x3c : c < 0.f ? (uint8_t)0xbc : c == 0.f ? (uint8_t)0 : (uint8_t)0x7e;
 }
 
 // grid = (tiles^2 over nb x ldp, blocks * matrices), block 256 (32 x 8)
@@ -150,7 +156,7 @@ struct ProjTable16 {
     float *M[kMaxMats];
     const void *G[kMaxMats];
     const uint16_t *planes[kMaxMats];
-    int8_t *S[kMaxMats];
+    uint8_t *S[kMaxMats];
     float mu[kMaxMats];
 };
 
@@ -172,7 +178,8 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
     const int rg = w / CW, cg = w % CW;
     const int kh = 8 * (lane >> 5);
     const int64_t r0 = (int64_t)rt * kRows;
-    float *M = t.M[mat] + (int64_t)b * nb;
+    float *const __restrict__ M = t.M[mat] + (int64_t)b * nb;
+    const void *const __restrict__ Gv = t.G[mat];
     const float mu = t.mu[mat];
     const int64_t plane = (int64_t)nblk * nb * ldp;
     const uint16_t *QT = t.planes[mat] + 2 * plane + (int64_t)b * nb * ldp;  // transposed planes
@@ -181,35 +188,34 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
     const int ar = tid >> 2, ak = 4 * (tid & 3);
     const int64_t arow = r0 + ar;
     const bool arok = arow < m;
-    f32x4 mv[2], gv[2];   // operands of the next two k-steps (slot = step parity)
-    auto fetch_a = [&](int k0, int slot) {
+    f32x4 mv, gv;   // operands of the next k-step to be staged
+    auto fetch_a = [&](int k0) {
         const int kq = k0 + ak;
-        mv[slot] = f32x4{0.f, 0.f, 0.f, 0.f};
-        gv[slot] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mv = f32x4{0.f, 0.f, 0.f, 0.f};
+        gv = f32x4{0.f, 0.f, 0.f, 0.f};
         if (arok && kq < nb) {
             const int64_t e = arow * n + kq;
-            mv[slot] = *(const f32x4 *)(M + e);
+            mv = *(const f32x4 *)(M + e);
             if (GBF16) {
-                const uint2 hb = *(const uint2 *)((const uint16_t *)t.G[mat] + (int64_t)b * nb + e);
-                gv[slot][0] = bf16_to_f32((uint16_t)(hb.x & 0xffff)); gv[slot][1] = bf16_to_f32((uint16_t)(hb.x >> 16));
-                gv[slot][2] = bf16_to_f32((uint16_t)(hb.y & 0xffff)); gv[slot][3] = bf16_to_f32((uint16_t)(hb.y >> 16));
+                const uint2 hb = *(const uint2 *)((const uint16_t *)Gv + (int64_t)b * nb + e);
+                gv[0] = bf16_to_f32((uint16_t)(hb.x & 0xffff)); gv[1] = bf16_to_f32((uint16_t)(hb.x >> 16));
+                gv[2] = bf16_to_f32((uint16_t)(hb.y & 0xffff)); gv[3] = bf16_to_f32((uint16_t)(hb.y >> 16));
             } else {
-                gv[slot] = *(const f32x4 *)((const float *)t.G[mat] + (int64_t)b * nb + e);
+                gv = *(const f32x4 *)((const float *)Gv + (int64_t)b * nb + e);
             }
         }
     };
     // momentum update of the fetched values, written back once; their split goes to LDS
-    auto store_a = [&](int k0, uint16_t *A, int slot) {
+    auto store_a = [&](int k0, uint16_t *A) {
         const int kq = k0 + ak;
-        const f32x4 mvs = mv[slot], gvs = gv[slot];
         f32x4 mn;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) mn[c] = __builtin_fmaf(mu, mvs[c], gvs[c]);
+        for (int c = 0; c < 4; ++c) mn[c] = __builtin_fmaf(mu, mv[c], gv[c]);
         if (arok && kq < nb) *(f32x4 *)(M + arow * n + kq) = mn;
         uint16_t h[4], md[4], l[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float pv = NEST ? __builtin_fmaf(mu, mn[c], gvs[c]) : mn[c];
+            const float pv = NEST ? __builtin_fmaf(mu, mn[c], gv[c]) : mn[c];
             split3(pv, h[c], md[c], l[c]);
         }
         uint2 vh = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
@@ -228,10 +234,10 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
 
     BStage<3, C::kCols> bs;
     bs.fetch(QT, plane, nb, ldp, 0, ncols);
-    fetch_a(0, 0);
-    fetch_a(kKS, 1);
+    fetch_a(0);
     bs.store(BBUF(0), ncols);
-    store_a(0, ABUF(0), 0);
+    store_a(0, ABUF(0));
+    fetch_a(kKS);
     __syncthreads();
     int cur = 0;
     for (int k0 = 0; k0 < nb; k0 += kKS) {
@@ -264,16 +270,16 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
         }
         if (more) {
             bs.store(BBUF(cur ^ 1), ncols);
-            store_a(k0 + kKS, ABUF(cur ^ 1), cur ^ 1);   // slot of step k0 + 16
-            fetch_a(k0 + 2 * kKS, cur);                  // refill the slot just consumed
+            store_a(k0 + kKS, ABUF(cur ^ 1));
+            fetch_a(k0 + 2 * kKS);   // lands during the next step's products
         }
         __syncthreads();
         cur ^= 1;
     }
 #undef ABUF
 #undef BBUF
-    // sign codes, stored with row stride nblk * ldp (block b at column offset b * ldp)
-    int8_t *S = t.S[mat] + (int64_t)b * ldp;
+    // sign bytes, stored with row stride nblk * ldp (block b at column offset b * ldp)
+    uint8_t *const __restrict__ S = t.S[mat] + (int64_t)b * ldp;
     const int64_t lds_ = (int64_t)nblk * ldp;
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
@@ -284,13 +290,13 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t rr = r0 + (rg * C::RT + i) * 32 + acc_row(r, lane);
-                if (rr < m) S[rr * lds_ + col] = sign_code(acc[i][c][r]);
+                if (rr < m) S[rr * lds_ + col] = sign_f16_hi(acc[i][c][r]);
             }
     }
 }
 
 struct ReconTable16 {
-    const int8_t *S[kMaxMats];
+    const uint8_t *S[kMaxMats];
     const uint16_t *planes[kMaxMats];
     void *W[kMaxMats];
     float *U[kMaxMats];
@@ -299,8 +305,50 @@ struct ReconTable16 {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint16_t sign_f16(int8_t s) {
-    return s == 1 ? (uint16_t)0x3c00 : s == -1 ? (uint16_t)0xbc00 : s == 0 ? (uint16_t)0 : (uint16_t)0x7e00;
+// two consecutive sign bytes (bytes 2j, 2j+1 of x) -> two fp16 values
+template <int J>
+__device__ __forceinline__ uint32_t signs_f16x2(uint32_t x) {
+    return __builtin_amdgcn_perm(0u, x, J == 0 ? 0x010c000cu : 0x030c020cu);
+}
+
+// W <- W - lr (s U + wd W) for the accumulator tiles of one wave.  Lane l of a 32 x 32 tile holds
+// column l % 32 and rows 4 (l / 32) + 8 (r / 4) + r % 4, so each lane walks one column with
+// compile-time row offsets from its own row pointer.  FULL: every row of the workgroup is < m.
+template <bool FULL, int RT, int NCW, int CW, bool WBF16>
+__device__ __forceinline__ void recon_epilogue(const f32x16 (&acc)[RT][NCW], void *Wv, float *U, int64_t m,
+                                               int64_t n, int nb, int b, int64_t r0, int rg, int cg, int lane,
+                                               float lr, float wd, float sc) {
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+        const int col = 32 * (cg + CW * c) + acc_col(lane);
+        if (col >= nb) continue;
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const int64_t rl = r0 + (rg * RT + i) * 32 + 4 * (lane >> 5);   // this lane's first row
+            const int64_t base = rl * n + (int64_t)b * nb + col;
+            const int64_t vr = m - rl;                                     // rows left from rl on
+            // loads of rows past m read a valid row instead: rl if rl < m, else row 0
+            const int64_t lbase = FULL || vr > 0 ? base : (int64_t)b * nb + col;
+            float wv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ro = 8 * (r >> 2) + (r & 3);
+                const int64_t e = lbase + (FULL || ro < vr ? (int64_t)ro * n : 0);
+                wv[r] = WBF16 ? bf16_to_f32(((const uint16_t *)Wv)[e]) : ((const float *)Wv)[e];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ro = 8 * (r >> 2) + (r & 3);
+                if (!FULL && ro >= vr) continue;
+                const int64_t e = base + (int64_t)ro * n;
+                const float u = acc[i][c][r];
+                if (U) U[e] = u;
+                const float nw = wv[r] - lr * __builtin_fmaf(sc, u, wd * wv[r]);
+                if (WBF16) ((uint16_t *)Wv)[e] = f32_to_bf16(nw);
+                else ((float *)Wv)[e] = nw;
+            }
+        }
+    }
 }
 
 // U = S Q^T with Q = Qh + Ql (fp16 parts) and S in {-1, 0, +1, NaN}: two f16 MFMAs per tile and k-step.
@@ -321,20 +369,24 @@ __global__ void __launch_bounds__(512) k_recon_bf16(int64_t m, int64_t n, int nb
     const int kh = 8 * (lane >> 5);
     const int64_t r0 = (int64_t)rt * kRows;
     const int64_t lds_ = (int64_t)nblk * ldp;
-    const int8_t *S = t.S[mat] + (int64_t)b * ldp;
+    const uint8_t *S = t.S[mat] + (int64_t)b * ldp;
     const int64_t plane = (int64_t)nblk * nb * ldp;
     const uint16_t *Qn = t.planes[mat] + (int64_t)b * nb * ldp;  // natural fp16 planes: row p, entries c
     const int nct = (nb + 31) / 32, ncols = 32 * nct;
     const int belems = 2 * ncols * kRowLd;
 
-    uint2 sq[2][RT];  // sign codes of the next two k-steps (slot = step parity)
-    auto fetch_s = [&](int k0, int slot) {
-        const int k = k0 + kh;
+    // sign bytes of the current and the next k-step (rows past m and k past nb read as 0)
+    uint2 sa[RT], sb[RT];
+    auto fetch_s = [&](int k0, uint2 *sq) {
+        const int k = k0 + kh;   // multiple of 8; nb is a multiple of 4, so k < nb means k + 4 <= nb
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             const int64_t row = r0 + (rg * RT + i) * 32 + (lane & 31);
-            sq[slot][i] = uint2{0u, 0u};
-            if (row < m && k < nb) sq[slot][i] = *(const uint2 *)(S + row * lds_ + k);  // codes past nb masked
+            sq[i] = uint2{0u, 0u};
+            if (row < m && k < nb) {
+                sq[i] = *(const uint2 *)(S + row * lds_ + k);
+                if (k + 4 >= nb) sq[i].y = 0u;
+            }
         }
     };
 
@@ -346,8 +398,8 @@ __global__ void __launch_bounds__(512) k_recon_bf16(int64_t m, int64_t n, int nb
 
     BStage<2, kColsMax> bs;
     bs.fetch(Qn, plane, nb, ldp, 0, ncols);
-    fetch_s(0, 0);
-    fetch_s(kKS, 1);
+    fetch_s(0, sa);
+    fetch_s(kKS, sb);
     bs.store(lds, ncols);
     __syncthreads();
     int cur = 0;
@@ -355,17 +407,11 @@ __global__ void __launch_bounds__(512) k_recon_bf16(int64_t m, int64_t n, int nb
         const bool more = k0 + kKS < nb;
         if (more) bs.fetch(Qn, plane, nb, ldp, k0 + kKS, ncols);
         const uint16_t *B = lds + cur * belems;
-        const int k = k0 + kh;
         f16x8 as[RT];
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            const int64_t row = r0 + (rg * RT + i) * 32 + (lane & 31);
-            u16x8 v;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int8_t code = (int8_t)(((c < 4 ? sq[cur][i].x : sq[cur][i].y) >> (8 * (c & 3))) & 0xff);
-                v[c] = (row < m && k + c < nb) ? sign_f16(code) : (uint16_t)0;
-            }
+            const uint4 v = {signs_f16x2<0>(sa[i].x), signs_f16x2<1>(sa[i].x), signs_f16x2<0>(sa[i].y),
+                             signs_f16x2<1>(sa[i].y)};
             as[i] = __builtin_bit_cast(f16x8, v);
         }
 #pragma unroll
@@ -383,37 +429,19 @@ __global__ void __launch_bounds__(512) k_recon_bf16(int64_t m, int64_t n, int nb
         }
         if (more) {
             bs.store(lds + (cur ^ 1) * belems, ncols);
-            fetch_s(k0 + 2 * kKS, cur);
+#pragma unroll
+            for (int i = 0; i < RT; ++i) sa[i] = sb[i];
+            fetch_s(k0 + 2 * kKS, sb);
         }
         __syncthreads();
         cur ^= 1;
     }
+    // epilogue: per 32-row tile, all 16 loads of W are issued before any store
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
-    float *U = t.U[mat];
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) {
-        const int col = 32 * (cg + CW * c) + acc_col(lane);
-        if (col >= nb) continue;
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t rr = r0 + (rg * RT + i) * 32 + acc_row(r, lane);
-                if (rr >= m) continue;
-                const int64_t e = rr * n + (int64_t)b * nb + col;
-                const float u = acc[i][c][r];
-                if (U) U[e] = u;
-                if (WBF16) {
-                    uint16_t *W = (uint16_t *)t.W[mat];
-                    const float wv = bf16_to_f32(W[e]);
-                    W[e] = f32_to_bf16(wv - lr * __builtin_fmaf(sc, u, wd * wv));
-                } else {
-                    float *W = (float *)t.W[mat];
-                    const float wv = W[e];
-                    W[e] = wv - lr * __builtin_fmaf(sc, u, wd * wv);
-                }
-            }
-    }
+    if (r0 + kRows <= m)
+        recon_epilogue<true, RT, NCW, CW, WBF16>(acc, t.W[mat], t.U[mat], m, n, nb, b, r0, rg, cg, lane, lr, wd, sc);
+    else
+        recon_epilogue<false, RT, NCW, CW, WBF16>(acc, t.W[mat], t.U[mat], m, n, nb, b, r0, rg, cg, lane, lr, wd, sc);
 }
 
 template <int CW, int NCW>
@@ -434,7 +462,7 @@ hipError_t launch_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s
         ProjTable16 t{};
         for (int i = 0; i < cnt; ++i) {
             t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i];
-            t.S[i] = a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+            t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
         }
         const bool gbf = a.g_dtype == DOBB_BF16;
         const bool nest = a.hp[c0].nesterov != 0;
@@ -461,7 +489,7 @@ hipError_t launch_recon(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t
     ReconTable16 t{};
     for (int i = 0; i < cnt; ++i) {
         const dobb_hparams &h = a.hp[c0 + i];
-        t.S[i] = a.S[c0 + i]; t.planes[i] = a.planes[c0 + i]; t.W[i] = a.W[c0 + i];
+        t.S[i] = (const uint8_t *)a.S[c0 + i]; t.planes[i] = a.planes[c0 + i]; t.W[i] = a.W[c0 + i];
         t.U[i] = a.U ? a.U[c0 + i] : nullptr;
         t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
     }
