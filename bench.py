@@ -10,7 +10,7 @@ Householder) -> the Dobb step (momentum, projection, sign, reconstruction, weigh
 first refresh (setup, untimed) is exact.  Times come from events around the timed steps; the
 library's kernel timer attributes them to kernels.  The CPU oracle is timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--layers L] [--copy-mib C]
 """
 from __future__ import annotations
 
@@ -26,11 +26,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "Dobb optimizer-step ms for GPT-2-XL-shaped matrix set; MFMA %peak, HBM %peak"
-PEAK_FP32_MFMA = 157.3e12
-PEAK_FP64_VALU = 78.6e12
-PEAK_HBM = 8.0e12
+# MI355X published peaks (dense)
+PEAK_HBM = 8.0e12            # B/s
+PEAK_BF16_MFMA = 2.5e15      # flop/s, bf16 and fp16
+PEAK_FP32_MFMA = 157.3e12    # flop/s
+PEAK_FP32_VALU = 157.3e12    # flop/s
 N_TOKENS = 16384
 BLOCKS = 16
+QR_PANEL = 32                # Householder panel width of the refresh
 
 
 def parse():
@@ -40,42 +43,160 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=48, help="GPT-2 XL has 48 layers")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the per-kernel HBM traffic table from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (a known-size kernel "
+                         "for calibrating hardware byte counters)")
     return ap.parse_args()
 
 
-def algorithmic_work(specs, n_tokens):
-    """Per-step algorithmic work of each kernel family (flops or bytes)."""
-    w = dict(momentum_bytes=0, project_flops=0, reconstruct_flops=0, accumulate_flops=0,
-             refresh_gemm_flops=0, householder_flops=0, xbytes=0)
+def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
+    """Per-step work of each kernel of the path, summed over the matrix set.
+
+    Per kernel: algorithmic HBM bytes (each operand read or written once), algorithmic flops with the
+    peak of the precision they stand for, and the matrix-core flops the kernel actually issues with
+    that dtype's peak.  Units (per weight m x n with B = n / nb blocks):
+      accumulate_syrk_bf16  X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b)
+      accumulate_reduce     A read + written: 8 nb^2 B bytes
+      refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
+      qr_update / qr_form   Householder factor / formation: 4/3 nb^3 B flops each (fp32)
+      qr_panel              panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
+      split_q               Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
+      project_bf16x6        M read + written, G read, sign bytes written: (9 + g) m n bytes;
+                            2 m n nb flops (fp32 contraction), issued as six bf16 products
+      reconstruct_f16x2     sign bytes read, W read + written: (1 + 2 w) m n bytes;
+                            2 m n nb flops (fp32 contraction), issued as two fp16 products
+    """
+    w = {}
+
+    def add(name, nbytes=0.0, flops=0.0, flops_peak=PEAK_FP32_MFMA, issued=0.0, issued_peak=PEAK_BF16_MFMA,
+            compute="mfma"):
+        e = w.setdefault(name, dict(bytes=0.0, flops=0.0, flops_peak=flops_peak, issued=0.0,
+                                    issued_peak=issued_peak, compute=compute))
+        e["bytes"] += nbytes; e["flops"] += flops; e["issued"] += issued
+
     for s in specs:
-        B = s.n // s.nb
-        w["momentum_bytes"] += 12 * s.m * s.n                 # read G, M; write M (fp32)
-        w["project_flops"] += 2 * s.m * s.n * s.nb
-        w["reconstruct_flops"] += 2 * s.m * s.n * s.nb
-        w["accumulate_flops"] += n_tokens * s.nb * (s.nb + 1) * B   # unique entries of X_b^T X_b
-        w["refresh_gemm_flops"] += 2 * s.nb ** 3 * B
-        w["householder_flops"] += (8 * s.nb ** 3 // 3) * B
-        w["xbytes"] += 2 * n_tokens * s.n
+        B, nb, mn = s.n // s.nb, s.nb, s.m * s.n
+        add("accumulate_syrk_bf16", 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
+        add("accumulate_reduce", 8.0 * nb * nb * B)
+        add("refresh_gemm", 12.0 * nb * nb * B, 2.0 * nb ** 3 * B)
+        add("qr_update", 0.0, 4.0 / 3.0 * nb ** 3 * B)
+        add("qr_form", 0.0, 4.0 / 3.0 * nb ** 3 * B)
+        add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
+        add("split_q", 14.0 * nb * nb * B)
+        add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
+        add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
     return w
 
 
-ROOFLINE = {  # kernel name -> (work key, bound, peak, unit)
-    "momentum": ("momentum_bytes", "hbm", PEAK_HBM, "GB/s"),
-    "project": ("project_flops", "mfma", PEAK_FP32_MFMA, "TFLOP/s"),
-    "reconstruct": ("reconstruct_flops", "mfma", PEAK_FP32_MFMA, "TFLOP/s"),
-    "accumulate_syrk": ("accumulate_flops", "mfma", PEAK_FP32_MFMA, "TFLOP/s"),
-    "refresh_gemm": ("refresh_gemm_flops", "mfma", PEAK_FP32_MFMA, "TFLOP/s"),
-    "householder_qr": ("householder_flops", "alu", PEAK_FP64_VALU, "TFLOP/s"),
+def roofline_entry(work, seconds):
+    """The binding resource of the kernel as built, and the fraction of its peak reached.
+
+    Time at peak: HBM bytes / 8 TB/s against matrix-core time, which is the issued products at
+    their dtype's peak for the split-precision kernels and the algorithmic flops at the fp32 peak
+    otherwise.  "achieved" is algorithmic bytes per second when HBM binds, else the flops rate
+    (issued products for the split kernels, with the algorithmic fp32-equivalent rate beside it)."""
+    t_hbm = work["bytes"] / PEAK_HBM
+    if work["issued"]:
+        t_cmp, rate, peak = work["issued"] / work["issued_peak"], work["issued"] / seconds, work["issued_peak"]
+    else:
+        t_cmp, rate, peak = work["flops"] / work["flops_peak"], work["flops"] / seconds, work["flops_peak"]
+    if t_hbm >= t_cmp:
+        ent = {"bound": "hbm", "achieved": work["bytes"] / seconds / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        ent = {"bound": work["compute"], "achieved": rate / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s"}
+    ent["frac"] = ent["achieved"] / ent["peak"]
+    ent["hbm_frac"] = work["bytes"] / seconds / PEAK_HBM
+    if work["issued"]:
+        ent["mfma_issued_frac"] = work["issued"] / seconds / work["issued_peak"]
+        ent["fp32_equiv_tflops"] = work["flops"] / seconds / 1e12
+    return ent
+
+
+# ---- measured HBM traffic (rocprofv3 counters), tied to the kernel sources they were taken on ----
+CSRC = os.path.join(ROOT, "block_diagonal_eigenbasis_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_step.md")
+# library kernel name -> (substring of the device symbol, source file)
+KERNEL_SYMBOLS = {
+    "accumulate_syrk_bf16": ("k_syrk_bf16<", "k_accumulate.hip"),
+    "accumulate_reduce": ("k_syrk_reduce", "k_accumulate.hip"),
+    "refresh_gemm": ("k_bgemm<", "k_refresh.hip"),
+    "qr_panel": ("k_qr_panel", "k_refresh.hip"),
+    "qr_update": ("k_qr_update<true>", "k_refresh.hip"),
+    "qr_form": ("k_qr_update<false>", "k_refresh.hip"),
+    "qr_identity": ("k_qr_identity", "k_refresh.hip"),
+    "qr_finish": ("k_qr_finish", "k_refresh.hip"),
+    "split_q": ("k_split_q", "k_step_bf16.hip"),
+    "project_bf16x6": ("k_proj_bf16<", "k_step_bf16.hip"),
+    "reconstruct_f16x2": ("k_recon_bf16<", "k_step_bf16.hip"),
 }
 
 
+def source_digest(kernel):
+    """Digest of the source file that defines a kernel plus the shared internal header."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SYMBOLS[kernel][1], "dobb_internal.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (fetched + written) from the committed counter summary, or None when the
+    kernel's source has changed since the counters were taken."""
+    if kernel not in KERNEL_SYMBOLS or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            f = line.strip().strip("|").split("|")
+            f = [x.strip() for x in f]
+            if len(f) >= 5 and f[0] == kernel:
+                if f[1].strip("`") != source_digest(kernel):
+                    return None
+                return float(f[3]) + float(f[4])
+    return None
+
+
+def pmc_summary(fetch_csv, write_csv, copy_mib):
+    """Per-kernel HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, in
+    KiB per dispatch).  Each counter is scaled so that the largest device copy (the calibration copy of
+    copy_mib MiB run by --copy-mib) reads and writes exactly its size."""
+    import csv
+    import collections
+
+    def per_kernel(fn):
+        rows = list(csv.DictReader(open(fn)))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        ref = max(copies)
+        scale = copy_mib * 1024.0 / ref
+        acc = collections.defaultdict(list)
+        for r in rows:
+            for name, (sym, _) in KERNEL_SYMBOLS.items():
+                if sym in r["Kernel_Name"]:
+                    acc[name].append(float(r["Counter_Value"]) * scale * 1024.0)
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}, scale, ref
+
+    fetch, fscale, fref = per_kernel(fetch_csv)
+    write, wscale, wref = per_kernel(write_csv)
+    print(f"calibration: {copy_mib} MiB copy read {fref:.0f} KiB (FETCH_SIZE), wrote {wref:.0f} KiB (WRITE_SIZE); "
+          f"scale factors {fscale:.3f} and {wscale:.3f}")
+    print()
+    print("| kernel | source digest | launches | fetched bytes/launch | written bytes/launch |")
+    print("|---|---|---|---|---|")
+    for name in KERNEL_SYMBOLS:
+        if name in fetch and name in write:
+            print(f"| {name} | `{source_digest(name)}` | {fetch[name][1]} | {fetch[name][0]:.0f} | {write[name][0]:.0f} |")
+
+
 def cpu_baseline(group, xs, specs, layers):
-    """Time the oracle on layer 0's four weights: the step on 1/8 of the rows, the capture on 2048
-    tokens, the orthogonal-iteration refresh on 2 blocks per weight; scale linearly to the full
-    set (every term is linear in rows, tokens and blocks)."""
+    """Time the oracle (one thread) on layer 0's four weights: the step on all rows, the capture on
+    8192 of the tokens, the orthogonal-iteration refresh on 8 of the 16 blocks of each weight; scale
+    linearly to the full set (every term is linear in rows, tokens, blocks and layers)."""
     import torch
     import oracle
-    rows_frac, tok, nblk_s = 8, 2048, 2
+    rows_frac, tok, nblk_s = 1, 8192, 8
     t_step = t_acc = t_ref = 0.0
     s_step = s_acc = s_ref = 0.0
     for i in range(4):
@@ -108,6 +229,9 @@ def cpu_baseline(group, xs, specs, layers):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_mib or 1024)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the Dobb step here is the single-GPU kernel path "
               "(no collectives); run with --gpus 1", file=sys.stderr)
@@ -119,6 +243,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {args.copy_mib} MiB read, {args.copy_mib} MiB written", file=sys.stderr,
+              flush=True)
+        del src, dst
     specs = workload.gpt2_xl_set(BLOCKS)[: 4 * args.layers]
     print(f"[bench] {len(specs)} weights, {workload.param_count(specs) / 1e9:.4f} B params", file=sys.stderr, flush=True)
 
@@ -196,26 +329,27 @@ def main():
     acc_ms = timed(lambda: group.accumulate(xs, beta), reps)
     ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, 1), reps)
 
-    # ---- roofline of the dominant kernel ---------------------------------------------------------
-    work = algorithmic_work(specs, N_TOKENS)
+    # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
+    g_bytes = Gs[0].element_size()
+    w_bytes = Ws[0].element_size()
+    work = kernel_work(specs, N_TOKENS, g_bytes, w_bytes)
     per_kernel = {}
     for name, (launches, total_ms) in kernels.items():
         ent = {"launches_per_step": launches / args.steps, "ms_per_step": round(total_ms / args.steps, 4),
                "avg_launch_ms": round(total_ms / launches, 5)}
-        if name in ROOFLINE:
-            key, bound, peak, unit = ROOFLINE[name]
-            rate = work[key] / (total_ms / args.steps / 1e3)
-            ent.update({"bound": bound, "achieved": rate, "frac": rate / peak})
+        if name in work:
+            ent.update({k: (round(v, 4) if isinstance(v, float) else v)
+                        for k, v in roofline_entry(work[name], total_ms / args.steps / 1e3).items()})
         per_kernel[name] = ent
-    dom = max((k for k in per_kernel if k in ROOFLINE), key=lambda k: per_kernel[k]["ms_per_step"])
-    key, bound, peak, unit = ROOFLINE[dom]
-    scale = 1e9 if unit == "GB/s" else 1e12
-    ach = per_kernel[dom]["achieved"]
-    launches = kernels[dom][0] / args.steps
-    roofline = {"kernel": dom, "bound": bound, "achieved": round(ach / scale, 3), "peak": peak / scale,
-                "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
-                "work_per_launch": work[key] / launches, "work_unit": "bytes" if unit == "GB/s" else "flop",
-                "avg_launch_ms": per_kernel[dom]["avg_launch_ms"]}
+    dom = max((k for k in per_kernel if k in work), key=lambda k: per_kernel[k]["ms_per_step"])
+    d = per_kernel[dom]
+    launches = d["launches_per_step"]
+    unit_work = work[dom]["bytes"] if d["bound"] == "hbm" else work[dom]["flops"]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
+                "frac": d["frac"], "traffic": measured_traffic(dom),
+                "work_per_launch": unit_work / launches,
+                "work_unit": "bytes" if d["bound"] == "hbm" else "flop",
+                "avg_launch_ms": d["avg_launch_ms"], "launches_per_step": launches}
 
     cpu = None
     if not args.no_cpu_baseline:

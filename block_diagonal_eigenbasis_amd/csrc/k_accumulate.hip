@@ -143,7 +143,11 @@ __global__ void __launch_bounds__(256) k_syrk(int64_t N, int nb, int T, int npai
 // diagonal.  Workgroups are renumbered so the tile pairs of one block run on the same XCD (the
 // dispatcher deals workgroup ids round-robin over the 8 XCDs) and share its L2.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-constexpr int kST = 128, kSK = 128, kSLd = kSK + 8;
+constexpr int kST = 128, kSK = 128;
+// LDS row j (one column of X) holds the chunk's 128 tokens as 16 groups of 8; group g sits in slot
+// g ^ swz(j).  The transposed writes (16 lanes: rows 8*cg + c, same g) and the MFMA reads (16
+// consecutive rows, same g) then each touch 16 distinct 16-byte slots of the 256-byte bank window.
+__device__ __forceinline__ int swz(int j) { return (j ^ (j >> 3)) & 15; }
 constexpr int kSFold = 2;  // fold fp32 sums into fp64 every 2 chunks (256 tokens)
 
 __device__ __forceinline__ int xcd_remap(int x, int G) {
@@ -151,13 +155,16 @@ __device__ __forceinline__ int xcd_remap(int x, int G) {
     return (x % 8) * (G / 8) + x / 8;
 }
 
+// 8 consecutive bf16 of one row (valid > 0 of them in range).  VEC = 8: nb % 8 == 0 and 16-byte
+// alignment, so valid >= 8; VEC = 4: nb % 4 == 0 and 8-byte alignment, so valid is a multiple of 4.
 template <int VEC>
 __device__ __forceinline__ void load_row8(const uint16_t *p, int valid, uint32_t d[4]) {
-    if (valid >= 8 && VEC == 8) {
+    if (VEC == 8) {
         const uint4 v = *(const uint4 *)p;
         d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    } else if (valid >= 8 && VEC == 4) {
-        const uint2 v0 = *(const uint2 *)p, v1 = *(const uint2 *)(p + 4);
+    } else if (VEC == 4) {
+        const uint2 v0 = *(const uint2 *)p;
+        const uint2 v1 = valid >= 8 ? *(const uint2 *)(p + 4) : uint2{0u, 0u};
         d[0] = v0.x; d[1] = v0.y; d[2] = v1.x; d[3] = v1.y;
     } else {
         uint16_t h[8];
@@ -168,11 +175,10 @@ __device__ __forceinline__ void load_row8(const uint16_t *p, int valid, uint32_t
     }
 }
 
-// grid.x = npairs * nblk * count (renumbered per XCD), grid.y = token splits
 template <int VEC>
 __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int npairs, int nblk, int64_t tok_per_split,
                                                       int nsplit, float beta, AccTable t, double *partial) {
-    __shared__ __align__(16) uint16_t xs[2][kST][kSLd];
+    __shared__ __align__(16) uint16_t xs[2][kST][kSK];
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int pair = x % npairs;
     const int rest = x / npairs;
@@ -188,8 +194,9 @@ __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int
     const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // loader role: strip ls, columns 8*cg.., tokens 8*tg.. of the chunk (16 x 16 blocks per strip)
-    const int ls = tid >> 8, cg = (tid & 255) >> 4, tg = tid & 15;
+    // loader role: strip ls, columns 8*cg.., tokens 8*tg.. of the chunk (16 x 16 blocks per strip);
+    // cg varies fastest, so each load instruction of a wave reads 4 rows x 256 contiguous bytes
+    const int ls = tid >> 8, cg = tid & 15, tg = (tid & 255) >> 4;
     const bool loader = !(diag && ls == 1);
     const int lcol0 = (ls ? j0 : i0) + 8 * cg;
     const int lvalid = (ls ? wj : wi) - 8 * cg;
@@ -232,7 +239,8 @@ __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int
                     e[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
                 }
                 o.x = e[0]; o.y = e[1]; o.z = e[2]; o.w = e[3];
-                *(uint4 *)&xs[ls][8 * cg + c][8 * tg] = o;
+                const int j = 8 * cg + c;
+                *(uint4 *)&xs[ls][j][8 * (tg ^ swz(j))] = o;
             }
         }
         __syncthreads();
@@ -240,10 +248,11 @@ __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int
         if (!skip) {
 #pragma unroll
             for (int kk = 0; kk < kSK; kk += 16) {
-                const int kofs = kk + 8 * (lane >> 5);
-                bf16x8 a0 = *(const bf16x8 *)&xs[0][wr + (lane & 31)][kofs];
-                bf16x8 b0 = *(const bf16x8 *)&xs[sj][wc + (lane & 31)][kofs];
-                bf16x8 b1 = *(const bf16x8 *)&xs[sj][wc + 32 + (lane & 31)][kofs];
+                const int g = (kk >> 3) + (lane >> 5);
+                const int ja = wr + (lane & 31), jb0 = wc + (lane & 31), jb1 = jb0 + 32;
+                bf16x8 a0 = *(const bf16x8 *)&xs[0][ja][8 * (g ^ swz(ja))];
+                bf16x8 b0 = *(const bf16x8 *)&xs[sj][jb0][8 * (g ^ swz(jb0))];
+                bf16x8 b1 = *(const bf16x8 *)&xs[sj][jb1][8 * (g ^ swz(jb1))];
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[1], 0, 0, 0);
             }
