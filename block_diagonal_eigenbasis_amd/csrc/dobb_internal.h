@@ -169,6 +169,11 @@ struct RefreshArgs {
 };
 size_t refresh_ws(const dobb_shape &sh, int count);
 hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s);
+// Householder QR of every block of a launch, nb <= 512.  Z: the blocks of the launch, dense nb x nb
+// each (overwritten); tq: npanel x 32 x 32 fp32 per block; negs: nb bytes per block.
+bool qr_block_supported(int64_t nb);
+hipError_t launch_qr_block(int nb, int nblk, int cnt, float *Z, float *tq, int8_t *negs, float *const *Q,
+                           int32_t *const *info, int info_value, hipStream_t s);
 
 }  // namespace dobb
 

@@ -1,0 +1,601 @@
+// Householder QR of every block of a launch: Q_b <- qr(Z_b).Q with diag(R) > 0.
+//
+// Dobb paper (arXiv 2610.39412), Tables 15-16: the orthogonal-iteration refresh orthonormalises
+// Z = A_b Q_b with a QR routine, Householder being the principal one.
+//
+// Blocked Householder with 32-column panels.  Reflector c of a panel is H = I - tau v v^T with
+// v_c = 1, v_r = x_r / (x_c + sgn(x_c) ||x||), tau = 1 + |x_c| / ||x||, R_cc = -sgn(x_c) ||x||; the
+// panel's reflectors combine as H_1 ... H_w = I - V T V^T (compact WY).  Factoring applies
+// I - V T^T V^T to the trailing columns; Q is formed from the identity by applying I - V T V^T for
+// the panels last to first on rows and columns >= the panel start, the last application also
+// negating the columns whose R_cc < 0.
+//
+// Panel factorisation (factor_panel): the panel lives in registers, thread (k, g) holding column k
+// at rows g, g + 8, ...; each column costs two workgroup barriers.  Norms, the cross-thread sums
+// and T are kept in fp64, the per-element work is fp32.  The dot products v_c^T x_k of a column
+// step also give v_k^T v_c for the earlier columns k, from which T is built one column behind.
+//
+// nb <= 128 (k_qr_block): one workgroup per block with Z in LDS does every panel, trailing update
+// and formation step in one launch.
+// nb > 128: per panel one k_qr_panel launch (one workgroup per block) and one k_qr_apply launch
+// (one workgroup per 64-column tile per block); formation is one k_qr_apply launch per panel.  A
+// k_qr_apply wave keeps its 32 x (rows/2) share of the tile in registers from load to store, in the
+// MFMA accumulator layout (rows are fed to the V^T X products in that order), so the tile is read
+// and written once; V is staged in LDS.
+#include "dobb_internal.h"
+
+#include <math.h>
+
+namespace dobb {
+namespace {
+
+constexpr int kPW = 32;             // panel width
+constexpr int kQT = 256;            // threads per workgroup
+constexpr int kGroups = kQT / kPW;  // row groups of a panel
+
+struct QrBlockOut {
+    float *Q[kMaxMats];
+    int32_t *info[kMaxMats];
+};
+
+__host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+
+// ---- panel factorisation ------------------------------------------------------------------------
+struct PanelLds {
+    size_t gs, td, vcol, red, part, tau, total;
+};
+__host__ __device__ inline PanelLds panel_lds(int nb, size_t o) {
+    PanelLds L;
+    L.gs = o;   o += a16((size_t)kPW * kPW * 8);      // v_k^T v_c (k < c)
+    L.td = o;   o += a16((size_t)kPW * kPW * 8);      // T, fp64
+    L.vcol = o; o += a16((size_t)2 * nb * 4);         // column c, double buffered by c parity
+    L.red = o;  o += a16((size_t)2 * kGroups * 8);
+    L.part = o; o += a16((size_t)kGroups * kPW * 8);
+    L.tau = o;  o += a16((size_t)kPW * 8);
+    L.total = o;
+    return L;
+}
+
+struct PanelPtrs {
+    double (*Gs)[kPW];
+    double (*Td)[kPW];
+    float *vcol;
+    double *red;
+    double (*part)[kPW];
+    double *tau;
+};
+__device__ inline PanelPtrs panel_ptrs(unsigned char *dsm, const PanelLds &L) {
+    return PanelPtrs{(double(*)[kPW])(dsm + L.gs), (double(*)[kPW])(dsm + L.td), (float *)(dsm + L.vcol),
+                     (double *)(dsm + L.red), (double(*)[kPW])(dsm + L.part), (double *)(dsm + L.tau)};
+}
+
+// Factor the panel held in P (thread (k, grp): column k, rows grp + 8 i of the rows x w panel).
+// On return P holds column k of V (1 at row k, 0 above), negf[c] = 1 where R_cc < 0, and S.Td
+// (fp64, upper triangle of the leading w x w) holds T once the caller has passed a barrier.
+template <int RPT>
+__device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, int k, int grp, const PanelPtrs &S,
+                                             int8_t *negf) {
+    // column c's owners publish its entries at rows >= c and their partial sum of squares; for
+    // c >= 1 this happens right after they applied reflector c-1 to it
+    auto publish = [&](int c) {
+        float *vc = S.vcol + (c & 1) * rows;
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = grp + kGroups * i;
+            if (r >= c && r < rows) { ss += (double)P[i] * (double)P[i]; vc[r] = P[i]; }
+        }
+        S.red[(c & 1) * kGroups + grp] = ss;
+    };
+    if (k == 0) publish(0);
+    for (int c = 0; c < w; ++c) {
+        const int buf = c & 1;
+        const float *vc = S.vcol + buf * rows;
+        __syncthreads();
+        double a2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) a2 += S.red[buf * kGroups + q];
+        const double alpha = sqrt(a2);
+        const double x0 = (double)vc[c];
+        const double sg = x0 >= 0.0 ? 1.0 : -1.0;
+        const double tc = alpha == 0.0 ? 0.0 : 1.0 + fabs(x0) / alpha;
+        const float inv = alpha == 0.0 ? 1.f : (float)(1.0 / (x0 + sg * alpha));
+        // column c-1 of T: its Gram entries and tau became visible at the barrier above
+        if (c >= 1 && grp == ((c - 1) & (kGroups - 1)) && k < c - 1) {
+            double sum = 0.0;
+            for (int l = k; l < c - 1; ++l) sum += S.Td[k][l] * S.Gs[l][c - 1];
+            S.Td[k][c - 1] = -S.tau[c - 1] * sum;
+        }
+        // v on this thread's rows and the partial dot product with this thread's column
+        float vt[RPT];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = grp + kGroups * i;
+            const float v = (r >= c && r < rows) ? (r == c ? 1.f : vc[r] * inv) : 0.f;
+            vt[i] = v;
+            if (i & 1) s1 = __builtin_fmaf(v, P[i], s1);
+            else s0 = __builtin_fmaf(v, P[i], s0);
+        }
+        S.part[grp][k] = (k != c && k < w) ? (double)s0 + (double)s1 : 0.0;
+        __syncthreads();
+        double tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) tot += S.part[q][k];
+        if (k > c && k < w) {
+            const float wk = (float)(tc * tot);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) P[i] = __builtin_fmaf(-vt[i], wk, P[i]);   // vt = 0 above row c
+            if (k == c + 1) publish(c + 1);
+        } else if (k == c) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) P[i] = vt[i];
+            if (grp == 0) {
+                S.tau[c] = tc;
+                S.Td[c][c] = tc;
+                negf[c] = (alpha != 0.0 && sg > 0.0) ? 1 : 0;   // R_cc = -sg alpha < 0
+            }
+        } else if (k < c && grp == 0) {
+            S.Gs[k][c] = tot;
+        }
+    }
+    __syncthreads();
+    if (w >= 2 && grp == ((w - 1) & (kGroups - 1)) && k < w - 1) {
+        double sum = 0.0;
+        for (int l = k; l < w - 1; ++l) sum += S.Td[k][l] * S.Gs[l][w - 1];
+        S.Td[k][w - 1] = -S.tau[w - 1] * sum;
+    }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- one wave applies a block reflector to a 32-column tile held in LDS ----------------------------
+//   X[j0 + r, c0 + j] -= (V op(T) V^T X)[r, j],  r < rows, j < 32 (columns >= ncols are skipped)
+// op(T) = T^T while factoring, T while forming Q.  W: this wave's 32 x 33 LDS scratch.  FLIP negates
+// the stored column col where neg[col] is set.
+template <bool TRANS_T, bool FLIP>
+__device__ void wy_wave(float *X, int ldx, int ncols, int j0, int rows, int c0, const float (*Vs)[kPW + 1],
+                        const float (*Ts)[kPW + 1], float (*W)[33], const int8_t *neg, int lane) {
+    const int kr = lane >> 5, cc = lane & 31;
+    const bool colok = c0 + cc < ncols;
+    const int ccl = colok ? c0 + cc : 0;
+    f32x16 acc = {};
+    for (int kb = 0; kb < rows; kb += 16) {
+        float a[8], bx[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = kb + 2 * u + kr;
+            const bool ok = r < rows;
+            const int rs = ok ? r : 0;
+            const float av = Vs[rs][cc];
+            const float xv = X[(int64_t)(j0 + rs) * ldx + ccl];
+            a[u] = ok ? av : 0.f;
+            bx[u] = (ok && colok) ? xv : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], bx[u], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) W[acc_row(r, lane)][acc_col(lane)] = acc[r];
+    wave_sync_lds();
+    f32x16 y = {};
+#pragma unroll
+    for (int kk = 0; kk < kPW; kk += 2) {
+        const int k = kk + kr;
+        const float a = TRANS_T ? Ts[k][cc] : Ts[cc][k];
+        y = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][cc], y, 0, 0, 0);
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) W[acc_row(r, lane)][acc_col(lane)] = y[r];
+    wave_sync_lds();
+    const int col = c0 + acc_col(lane);
+    const float sgn = (FLIP && colok && neg[col]) ? -1.f : 1.f;
+    for (int r0 = 0; r0 < rows; r0 += 32) {
+        f32x16 u = {};
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2) {
+            const int k = kk + kr, rr = r0 + cc;
+            const float a = rr < rows ? Vs[rr < rows ? rr : 0][k] : 0.f;
+            u = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][cc], u, 0, 0, 0);
+        }
+        if (!colok) continue;
+        float *xc = X + (int64_t)(j0 + r0) * ldx + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = r0 + acc_row(r, lane);
+            if (row < rows) {
+                const float v = xc[(int64_t)acc_row(r, lane) * ldx] - u[r];
+                xc[(int64_t)acc_row(r, lane) * ldx] = FLIP ? sgn * v : v;
+            }
+        }
+    }
+}
+
+// ---- nb <= 128: one workgroup per block, Z in LDS ----------------------------------------------------
+struct BlockLds {
+    size_t vs, ts, wsc, neg, zs, total;
+    PanelLds pn;
+};
+__host__ __device__ inline BlockLds block_lds(int nb) {
+    BlockLds L;
+    size_t o = 0;
+    L.vs = o; o += a16((size_t)nb * (kPW + 1) * 4);
+    L.ts = o; o += a16((size_t)kPW * (kPW + 1) * 4);
+    L.pn = panel_lds(nb, o);                    // panel scratch, reused as the waves' update scratch
+    L.wsc = o;
+    const size_t wend = o + a16((size_t)4 * 32 * 33 * 4);
+    o = L.pn.total > wend ? L.pn.total : wend;
+    L.neg = o; o += a16((size_t)nb);
+    L.zs = o;  o += a16((size_t)nb * (nb + 1) * 4);
+    L.total = o;
+    return L;
+}
+
+// grid.x = blocks of the launch, block 256; RPT >= ceil(nb / 8).  T of panel p goes to Tq (workspace).
+template <int RPT>
+__global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float *Z_all, float *Tq_all, QrBlockOut t,
+                                                  int info_value) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    const BlockLds L = block_lds(nb);
+    float(*Vs)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.vs);
+    float(*Ts)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.ts);
+    float(*Wsc)[32][33] = (float(*)[32][33])(dsm + L.wsc);
+    int8_t *neg = (int8_t *)(dsm + L.neg);
+    const PanelPtrs S = panel_ptrs(dsm, L.pn);
+    const int ldz = nb + 1;
+    float *Z = (float *)(dsm + L.zs);
+
+    const int g = blockIdx.x;
+    const int b = g % nblk, mat = g / nblk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int k = tid & (kPW - 1), grp = tid / kPW;
+    const int npanel = (nb + kPW - 1) / kPW;
+    const float *Zg = Z_all + (int64_t)g * nb * nb;
+    float *Tq = Tq_all + (int64_t)g * npanel * kPW * kPW;
+    for (int64_t e = tid; e < (int64_t)nb * nb; e += kQT) Z[(e / nb) * ldz + e % nb] = Zg[e];
+    __syncthreads();
+
+    for (int p = 0; p < npanel; ++p) {
+        const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+        float P[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = grp + kGroups * i;
+            P[i] = (k < w && r < rows) ? Z[(int64_t)(j0 + r) * ldz + j0 + k] : 0.f;
+        }
+        factor_panel<RPT>(P, w, rows, k, grp, S, neg + j0);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = grp + kGroups * i;
+            if (r < rows) {
+                Vs[r][k] = k < w ? P[i] : 0.f;
+                if (k < w) Z[(int64_t)(j0 + r) * ldz + j0 + k] = P[i];
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < kPW * kPW; e += kQT) {
+            const int i = e / kPW, j = e % kPW;
+            const float tv = (i <= j && j < w) ? (float)S.Td[i][j] : 0.f;
+            Ts[i][j] = tv;
+            Tq[(int64_t)p * kPW * kPW + e] = tv;
+        }
+        __syncthreads();
+        const int first = j0 + w;
+        const int ntiles = (nb - first + 31) / 32;
+        for (int tile = wv; tile < ntiles; tile += 4)
+            wy_wave<true, false>(Z, ldz, nb, j0, rows, first + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
+        __syncthreads();
+    }
+
+    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+    for (int64_t e = tid; e < (int64_t)nb * nb; e += kQT) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+    for (int p = npanel - 1; p >= 0; --p) {
+        const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+        for (int e = tid; e < rows * kPW; e += kQT) {
+            const int r = e / kPW, c = e % kPW;
+            Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
+        }
+        for (int e = tid; e < kPW * kPW; e += kQT) Ts[e / kPW][e % kPW] = Tq[(int64_t)p * kPW * kPW + e];
+        __syncthreads();
+        const int ntiles = (nb - j0 + 31) / 32;
+        for (int tile = wv; tile < ntiles; tile += 4) {
+            if (p == 0) wy_wave<false, true>(Q, nb, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
+            else wy_wave<false, false>(Q, nb, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
+        }
+        __syncthreads();
+    }
+    if (tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
+}
+
+// ---- nb > 128: panel launch ------------------------------------------------------------------------
+// grid.x = blocks, block 256.  Writes V into Z's panel columns, T (fp32) to Tq, diag(R) signs to negs.
+template <int RPT>
+__global__ void __launch_bounds__(256) k_qr_panel(int nb, int p, float *Z_all, float *Tq_all, int8_t *neg_all) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    const PanelLds L = panel_lds(nb, 0);
+    const PanelPtrs S = panel_ptrs(dsm, L);
+    const int g = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int k = tid & (kPW - 1), grp = tid / kPW;
+    const int npanel = (nb + kPW - 1) / kPW;
+    const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+    float *Z = Z_all + (int64_t)g * nb * nb;
+    float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
+    float P[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = grp + kGroups * i;
+        P[i] = (k < w && r < rows) ? Z[(int64_t)(j0 + r) * nb + j0 + k] : 0.f;
+    }
+    factor_panel<RPT>(P, w, rows, k, grp, S, neg_all + (int64_t)g * nb + j0);
+    if (k < w) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = grp + kGroups * i;
+            if (r < rows) Z[(int64_t)(j0 + r) * nb + j0 + k] = P[i];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < kPW * kPW; e += kQT) {
+        const int i = e / kPW, j = e % kPW;
+        Tq[e] = (i <= j && j < w) ? (float)S.Td[i][j] : 0.f;
+    }
+}
+
+// ---- nb > 128: apply a panel's block reflector -------------------------------------------------------
+// grid = (64-column tiles, blocks), block 256.  Wave (kp, h): column half h of the tile, row half kp.
+// A wave's rows are processed in 32-row chunks; chunk rows are fed to the V^T X products in the
+// order of the MFMA accumulator layout (k-step s of half-wave q uses row 8 (s/4) + 4 q + s % 4), so
+// the chunk loaded for those products is already laid out as the X - V Y result.
+// FACTOR: X = Z (columns after the panel), op(T) = T^T.  Otherwise X = Q (columns from the panel
+// start), op(T) = T, and with FLIP (first panel) the columns whose R_cc < 0 are negated.
+// Vs[r][c] = V[r][c] for r < rows, c < 32 (zero for c >= w) from Z's panel columns, and zero rows
+// from rows up to the next multiple of 32.  8 threads per row, eight rows per thread in flight.
+template <int CH>
+__device__ __forceinline__ void stage_v(float (*Vs)[kPW + 1], const float *Z, int nb, int j0, int w, int rows, int tid) {
+    constexpr int kPasses = 2 * CH;   // 32 rows per pass
+    const int c4 = 4 * (tid & 7), r0 = tid >> 3;
+    const int rpad = (rows + 31) & ~31;
+    const bool vec = (nb & 3) == 0 && c4 + 4 <= w;
+    const float *Zp = Z + (int64_t)j0 * nb + j0;
+#pragma unroll
+    for (int b0 = 0; b0 < kPasses; b0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = r0 + 32 * (b0 + i);
+            const bool ok = b0 + i < kPasses && r < rows;
+            const float *src = Zp + (ok ? r : 0) * nb + c4;
+            if (vec) {
+                v[i] = *(const f32x4 *)src;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[i][q] = c4 + q < w ? src[q] : 0.f;
+            }
+            if (!ok) v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = r0 + 32 * (b0 + i);
+            if (b0 + i < kPasses && r < rpad) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Vs[r][c4 + q] = v[i][q];
+            }
+        }
+    }
+}
+
+struct ApplyLds {
+    size_t vs, ts, wp, total;
+};
+__host__ __device__ inline ApplyLds apply_lds(int nb) {
+    ApplyLds L;
+    size_t o = 0;
+    L.vs = o; o += a16((size_t)((nb + 31) & ~31) * (kPW + 1) * 4);
+    L.ts = o; o += a16((size_t)kPW * (kPW + 1) * 4);
+    L.wp = o; o += a16((size_t)2 * 2 * 32 * 33 * 4);   // [row half][column half]
+    L.total = o;
+    return L;
+}
+
+template <int CH, bool FACTOR, bool FLIP>
+__global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const float *Z_all, const float *Tq_all,
+                                                  const int8_t *neg_all, QrBlockOut t, int info_value) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    const ApplyLds L = apply_lds(nb);
+    float(*Vs)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.vs);
+    float(*Ts)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.ts);
+    float(*Wp)[2][32][33] = (float(*)[2][32][33])(dsm + L.wp);
+    const int g = blockIdx.y;
+    const int b = g % nblk, mat = g / nblk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int h = wv & 1, kp = wv >> 1;
+    const int kr = lane >> 5, cc = lane & 31;
+    const int npanel = (nb + kPW - 1) / kPW;
+    const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+    const float *Z = Z_all + (int64_t)g * nb * nb;
+    float *X = FACTOR ? (float *)Z_all + (int64_t)g * nb * nb : t.Q[mat] + (int64_t)b * nb * nb;
+    const int first = FACTOR ? j0 + w : j0;
+    const int c0 = first + blockIdx.x * 64 + 32 * h;
+    const bool colok = c0 + cc < nb;
+    const int ccl = colok ? c0 + cc : 0;
+    // rows of this wave: [rb, re), at most CH chunks of 32
+    const int half = ((rows + 63) / 64) * 32;
+    const int rb = kp ? half : 0, re = kp ? rows : (half < rows ? half : rows);
+    // element (row, col) of the tile lives at Xr[row * nb + col]; this lane's rows within a chunk are
+    // 4 kr + {0, 1, 2, 3, 8, ..., 27}: offsets from one 32-bit lane offset
+    float *Xr = X + (int64_t)j0 * nb;
+    const unsigned lo = (unsigned)((rb + 4 * kr) * nb + ccl);
+    const unsigned unb = (unsigned)nb;
+    // this wave's share of the tile, accumulator layout; rows >= re and columns >= nb read as 0
+    f32x16 x[CH];
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+        const int r0 = rb + 32 * ch;
+        if (r0 + 32 <= re && colok) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[ch][r] = Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0 + acc_row(r, lane);
+                const bool ok = row < re && colok;
+                const float v = Xr[ok ? lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb : 0u];
+                x[ch][r] = ok ? v : 0.f;
+            }
+        }
+    }
+    // V (zero rows up to a multiple of 32) and T
+    stage_v<CH>(Vs, Z, nb, j0, w, rows, tid);
+    const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
+    {
+        float tv[kPW * kPW / kQT];
+#pragma unroll
+        for (int i = 0; i < kPW * kPW / kQT; ++i) tv[i] = Tq[tid + kQT * i];
+#pragma unroll
+        for (int i = 0; i < kPW * kPW / kQT; ++i) Ts[(tid + kQT * i) / kPW][(tid + kQT * i) % kPW] = tv[i];
+    }
+    __syncthreads();
+    // W partial = V[this wave's rows]^T X (rows past `rows` have V = 0)
+    f32x16 acc = {};
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+        const int r0 = rb + 32 * ch;
+        if (r0 >= re) break;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const float a = Vs[r0 + 8 * (s >> 2) + 4 * kr + (s & 3)][cc];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x[ch][s], acc, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = acc[r];
+    __syncthreads();
+    // Y = op(T) (W_0 + W_1), computed by both waves of the column half
+    f32x16 y = {};
+#pragma unroll
+    for (int kk = 0; kk < kPW; kk += 2) {
+        const int kx = kk + kr;
+        const float a = FACTOR ? Ts[kx][cc] : Ts[cc][kx];
+        y = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Wp[0][h][kx][cc] + Wp[1][h][kx][cc], y, 0, 0, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = y[r];
+    wave_sync_lds();
+    float yb[kPW / 2];   // B operands of the V Y products, the same for every chunk
+#pragma unroll
+    for (int kk = 0; kk < kPW; kk += 2) yb[kk / 2] = Wp[kp][h][kk + kr][cc];
+    // X -= V Y on this wave's rows
+    const float sgn = (FLIP && colok && neg_all[(int64_t)g * nb + ccl]) ? -1.f : 1.f;
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+        const int r0 = rb + 32 * ch;
+        if (r0 >= re) break;
+        f32x16 u = {};
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2)
+            u = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[r0 + cc][kk + kr], yb[kk / 2], u, 0, 0, 0);
+        if (!colok) continue;
+        if (r0 + 32 <= re) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float v = x[ch][r] - u[r];
+                Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = FLIP ? sgn * v : v;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (r0 + acc_row(r, lane) < re) {
+                    const float v = x[ch][r] - u[r];
+                    Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = FLIP ? sgn * v : v;
+                }
+            }
+        }
+    }
+    if (FLIP && blockIdx.x == 0 && tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
+}
+
+// Q := I before the formation sweep.  grid = blocks.
+__global__ void __launch_bounds__(256) k_qr_identity(int nb, int nblk, QrBlockOut t) {
+    const int g = blockIdx.x;
+    float *Q = t.Q[g / nblk] + (int64_t)(g % nblk) * nb * nb;
+    for (int64_t e = threadIdx.x; e < (int64_t)nb * nb; e += 256) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+}
+
+template <int RPT>
+hipError_t launch_block(int nb, int nblk, int nblocks, const float *Z, float *tq, const QrBlockOut &o, int infov,
+                        hipStream_t s) {
+    const size_t sh = block_lds(nb).total;
+    (void)hipFuncSetAttribute((const void *)k_qr_block<RPT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    DOBB_LAUNCH("qr_block", s, (k_qr_block<RPT>), dim3((unsigned)nblocks), dim3(kQT), sh, nb, nblk, Z, tq, o, infov);
+    return hipGetLastError();
+}
+
+template <int RPT, int CH>
+hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int8_t *negs, const QrBlockOut &o,
+                         int infov, hipStream_t s) {
+    const size_t ps = panel_lds(nb, 0).total;
+    const size_t as = apply_lds(nb).total;
+    (void)hipFuncSetAttribute((const void *)k_qr_panel<RPT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
+    (void)hipFuncSetAttribute((const void *)k_qr_panel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
+    (void)hipFuncSetAttribute((const void *)k_qr_panel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
+    (void)hipFuncSetAttribute((const void *)k_qr_panel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
+    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
+    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
+    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
+    const int npanel = (nb + kPW - 1) / kPW;
+    for (int p = 0; p < npanel; ++p) {
+        const int rows = nb - p * kPW;   // rows per thread: ceil(rows / 8), rounded up to a template size
+        if (rows <= 64 && RPT > 8)
+            DOBB_LAUNCH("qr_panel", s, (k_qr_panel<8>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
+        else if (rows <= 128 && RPT > 16)
+            DOBB_LAUNCH("qr_panel", s, (k_qr_panel<16>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
+        else if (rows <= 256 && RPT > 32)
+            DOBB_LAUNCH("qr_panel", s, (k_qr_panel<32>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
+        else
+            DOBB_LAUNCH("qr_panel", s, (k_qr_panel<RPT>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
+        const int first = p * kPW + (nb - p * kPW < kPW ? nb - p * kPW : kPW);
+        const int ntiles = (nb - first + 63) / 64;
+        if (ntiles > 0)
+            DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
+                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
+    }
+    DOBB_LAUNCH("qr_identity", s, k_qr_identity, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, o);
+    for (int p = npanel - 1; p >= 0; --p) {
+        const int ntiles = (nb - p * kPW + 63) / 64;
+        if (p > 0)
+            DOBB_LAUNCH("qr_form", s, (k_qr_apply<CH, false, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
+                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
+        else
+            DOBB_LAUNCH("qr_form", s, (k_qr_apply<CH, false, true>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
+                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, infov);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool qr_block_supported(int64_t nb) { return nb >= 1 && nb <= 512; }
+
+hipError_t launch_qr_block(int nb, int nblk, int cnt, float *Z, float *tq, int8_t *negs, float *const *Q,
+                           int32_t *const *info, int info_value, hipStream_t s) {
+    QrBlockOut o{};
+    for (int i = 0; i < cnt; ++i) { o.Q[i] = Q[i]; o.info[i] = info ? info[i] : nullptr; }
+    const int nblocks = nblk * cnt;
+    if (nb <= 128 && (int64_t)block_lds(nb).total <= max_lds_bytes()) {
+        if (nb <= 64) return launch_block<8>(nb, nblk, nblocks, Z, tq, o, info_value, s);
+        return launch_block<16>(nb, nblk, nblocks, Z, tq, o, info_value, s);
+    }
+    // panel rows per thread: ceil(nb / 8); 32-row chunks per apply wave: ceil(nb / 64)
+    if (nb <= 128) return launch_panels<16, 2>(nb, nblk, nblocks, Z, tq, negs, o, info_value, s);
+    if (nb <= 256) return launch_panels<32, 4>(nb, nblk, nblocks, Z, tq, negs, o, info_value, s);
+    return launch_panels<64, 8>(nb, nblk, nblocks, Z, tq, negs, o, info_value, s);
+}
+
+}  // namespace dobb

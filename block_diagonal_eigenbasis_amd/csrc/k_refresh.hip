@@ -950,6 +950,11 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
             for (int it = 0; it < a.iters; ++it) {
                 DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
                 const int infov = it == a.iters - 1 ? a.iters : 0;
+                if (qr_block_supported(nb)) {
+                    const hipError_t e = launch_qr_block(nb, nblk, cnt, Tm, tq, negs, ot.Q, ot.info, infov, s);
+                    if (e != hipSuccess) return e;
+                    continue;
+                }
                 if (lds) {
                     DOBB_LAUNCH("householder_qr_lds", s, k_householder<true>, dim3((unsigned)nblocks), dim3(256), hl, nb, nblk,
                                 Tm, tq, ot, infov);
