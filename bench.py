@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +35,7 @@ PEAK_FP32_VALU = 157.3e12    # flop/s
 N_TOKENS = 16384
 BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
+QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
 
 
 def parse():
@@ -60,8 +62,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
       accumulate_syrk_bf16  X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b)
       accumulate_reduce     A read + written: 8 nb^2 B bytes
       refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
-      qr_update / qr_form   Householder factor / formation: 4/3 nb^3 B flops each (fp32)
-      qr_panel              panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
+      qr_block              nb <= 128, the whole Householder QR in one launch: 8/3 nb^3 B flops
+      qr_update / qr_form   nb > 128, factor / formation updates: 4/3 nb^3 B flops each (fp32)
+      qr_panel              nb > 128, panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
       split_q               Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
       project_bf16x6        M read + written, G read, sign bytes written: (9 + g) m n bytes;
                             2 m n nb flops (fp32 contraction), issued as six bf16 products
@@ -81,9 +84,12 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
         add("accumulate_syrk_bf16", 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
         add("accumulate_reduce", 8.0 * nb * nb * B)
         add("refresh_gemm", 12.0 * nb * nb * B, 2.0 * nb ** 3 * B)
-        add("qr_update", 0.0, 4.0 / 3.0 * nb ** 3 * B)
-        add("qr_form", 0.0, 4.0 / 3.0 * nb ** 3 * B)
-        add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
+        if nb <= QR_SINGLE_LAUNCH_MAX_NB:
+            add("qr_block", 0.0, 8.0 / 3.0 * nb ** 3 * B)
+        else:
+            add("qr_update", 0.0, 4.0 / 3.0 * nb ** 3 * B)
+            add("qr_form", 0.0, 4.0 / 3.0 * nb ** 3 * B)
+            add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
         add("split_q", 14.0 * nb * nb * B)
         add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
         add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
@@ -117,19 +123,19 @@ def roofline_entry(work, seconds):
 # ---- measured HBM traffic (rocprofv3 counters), tied to the kernel sources they were taken on ----
 CSRC = os.path.join(ROOT, "block_diagonal_eigenbasis_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_step.md")
-# library kernel name -> (substring of the device symbol, source file)
+# library kernel name -> (regular expression on the device symbol, source file)
 KERNEL_SYMBOLS = {
-    "accumulate_syrk_bf16": ("k_syrk_bf16<", "k_accumulate.hip"),
-    "accumulate_reduce": ("k_syrk_reduce", "k_accumulate.hip"),
-    "refresh_gemm": ("k_bgemm<", "k_refresh.hip"),
-    "qr_panel": ("k_qr_panel", "k_refresh.hip"),
-    "qr_update": ("k_qr_update<true>", "k_refresh.hip"),
-    "qr_form": ("k_qr_update<false>", "k_refresh.hip"),
-    "qr_identity": ("k_qr_identity", "k_refresh.hip"),
-    "qr_finish": ("k_qr_finish", "k_refresh.hip"),
-    "split_q": ("k_split_q", "k_step_bf16.hip"),
-    "project_bf16x6": ("k_proj_bf16<", "k_step_bf16.hip"),
-    "reconstruct_f16x2": ("k_recon_bf16<", "k_step_bf16.hip"),
+    "accumulate_syrk_bf16": (r"k_syrk_bf16<", "k_accumulate.hip"),
+    "accumulate_reduce": (r"k_syrk_reduce", "k_accumulate.hip"),
+    "refresh_gemm": (r"k_bgemm<", "k_refresh.hip"),
+    "qr_block": (r"k_qr_block<", "k_qr.hip"),
+    "qr_panel": (r"k_qr_panel<", "k_qr.hip"),
+    "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),
+    "qr_form": (r"k_qr_apply<\d+, false,", "k_qr.hip"),
+    "qr_identity": (r"k_qr_identity", "k_qr.hip"),
+    "split_q": (r"k_split_q", "k_step_bf16.hip"),
+    "project_bf16x6": (r"k_proj_bf16<", "k_step_bf16.hip"),
+    "reconstruct_f16x2": (r"k_recon_bf16<", "k_step_bf16.hip"),
 }
 
 
@@ -174,7 +180,7 @@ def pmc_summary(fetch_csv, write_csv, copy_mib):
         acc = collections.defaultdict(list)
         for r in rows:
             for name, (sym, _) in KERNEL_SYMBOLS.items():
-                if sym in r["Kernel_Name"]:
+                if re.search(sym, r["Kernel_Name"]):
                     acc[name].append(float(r["Counter_Value"]) * scale * 1024.0)
         return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}, scale, ref
 
