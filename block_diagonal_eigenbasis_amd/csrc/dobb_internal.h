@@ -137,9 +137,10 @@ bool step_bf16_eligible(const dobb_shape &sh, int norm);
 size_t step_bf16_ws_one(const dobb_shape &sh);
 int step_bf16_ldp(int64_t nb);
 hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s);
-// nb <= 128: the same arithmetic with each block's basis resident in LDS (k_step_res.hip)
-bool step_res_eligible(const dobb_shape &sh);
-hipError_t launch_step_res(const StepArgs &a, int ldp, hipStream_t s);
+// nb <= 128: the same arithmetic with each block's basis resident in LDS and row tiles staged
+// through LDS (k_step_rows.hip)
+bool step_rows_eligible(const dobb_shape &sh);
+hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s);
 
 struct AccumulateArgs {
     int count;

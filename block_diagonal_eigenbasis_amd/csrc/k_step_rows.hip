@@ -1,0 +1,540 @@
+// The Dobb step (sign normalisation) for block widths nb <= 128: row tiles staged through LDS.
+//
+// Dobb paper (arXiv 2610.39412): abstract (project momentum into the block bases, sign-normalise,
+// reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
+// (Nesterov).
+//
+// Same arithmetic as k_step_bf16.hip: C = P Q with both operands split into three bf16 parts (the
+// six products of order <= 2); U = S Q^T with Q split into two fp16 parts (S is exact in fp16).
+// Signs travel as the high byte of their fp16 value (+1 -> 0x3c, -1 -> 0xbc, 0 -> 0x00, NaN -> 0x7e).
+//
+// Layout of the work: a workgroup (8 waves) owns one block b; it splits Q_b into LDS once and then
+// streams tiles of TR rows.  Every global access walks along rows (consecutive lanes take
+// consecutive 16- or 8-byte pieces of a row's nb-wide slice): an access pattern where each lane
+// takes a different row, as the MFMA operand layout would, reaches well under half of the HBM
+// bandwidth.  The MFMA operands are read from LDS tiles:
+//   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32);
+//                 waves take (32-row tile, column chunks): C^T = Q^T P^T; sign bytes -> LDS -> rows
+//   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
+//                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
+// The next tile's rows are loaded while the current tile's products run.
+#include "dobb_internal.h"
+
+#include <type_traits>
+
+namespace dobb {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRT = 512;    // threads per workgroup (8 waves)
+constexpr int kKS = 16;     // k per MFMA step
+constexpr int kPadK = 8;    // Q plane row padding (2-byte elements)
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ void split3(float v, uint16_t &h, uint16_t &m, uint16_t &l) {
+    h = bf16_bits(v);
+    const float r1 = v - bf16_to_f32(h);
+    m = bf16_bits(r1);
+    l = bf16_bits(r1 - bf16_to_f32(m));
+}
+__device__ __forceinline__ void split2h(float v, uint16_t &h, uint16_t &l) {
+    const _Float16 a = (_Float16)v;
+    h = __builtin_bit_cast(uint16_t, a);
+    l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)a));
+}
+// high byte of the fp16 value of sign(c), from the bits of c without branches
+__device__ __forceinline__ uint32_t sign_byte(float c) {
+    const uint32_t u = __float_as_uint(c);
+    const uint32_t mag = u & 0x7fffffffu;
+    const uint32_t sb = 0x3cu | ((u >> 24) & 0x80u);
+    const uint32_t nz = mag > 0x7f800000u ? 0x7eu : sb;
+    return mag == 0u ? 0u : nz;
+}
+template <int J>
+__device__ __forceinline__ uint32_t signs_f16x2(uint32_t x) {
+    return __builtin_amdgcn_perm(0u, x, J == 0 ? 0x010c000cu : 0x030c020cu);
+}
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+__device__ __forceinline__ int xcd_remap(int x, int G) {
+    if (G % 8) return x;
+    return (x % 8) * (G / 8) + x / 8;
+}
+
+// LDS geometry shared by host and device
+struct RowsGeo {
+    int KS, kpad, qld, pld, uld, NCH;
+};
+__host__ __device__ inline RowsGeo rows_geo(int nb) {
+    RowsGeo g;
+    g.KS = (nb + kKS - 1) / kKS;
+    g.kpad = g.KS * kKS;
+    g.qld = g.kpad + kPadK;     // Q planes: 2-byte elements per row
+    g.pld = g.kpad + 4;         // P tile: fp32 per row; (pld / 4) odd keeps 16 rows on distinct banks
+    g.uld = nb + 4 + ((nb / 4) % 2 == 0 ? 0 : 4);   // U tile: fp32 per row, (uld / 4) odd
+    g.NCH = (nb + 31) / 32;
+    return g;
+}
+__host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+
+// ---- projection ----------------------------------------------------------------------------------
+struct ProjRowsTable {
+    float *M[kMaxMats];
+    const void *G[kMaxMats];
+    const float *Q[kMaxMats];
+    uint8_t *S[kMaxMats];
+    float mu[kMaxMats];
+};
+__host__ __device__ inline size_t proj_rows_lds(int nb, int TR, int ldp) {
+    const RowsGeo g = rows_geo(nb);
+    return a16((size_t)3 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp);
+}
+
+// grid.x = tile groups x blocks x matrices (block fastest, renumbered per XCD), block 512.
+// TR = 128 or 64 rows per tile; the 8 waves take (32-row tile rt, group cg of column chunks).
+template <int NCH, int TR, int NEST, bool GBF16>
+__global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
+                                                   int ldp, ProjRowsTable t) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const RowsGeo geo = rows_geo(nb);
+    const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, pld = geo.pld;
+    uint16_t *qs = (uint16_t *)lds;                                          // [3][nb][qld]
+    float *ps = (float *)(lds + a16((size_t)3 * nb * qld * 2));              // [TR][pld]
+    uint8_t *ss = lds + a16((size_t)3 * nb * qld * 2) + a16((size_t)TR * pld * 4);   // [TR][ldp]
+
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = x % nblk, rest = x / nblk;
+    const int tg = rest % ngroups, mat = rest / ngroups;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t ntile = (m + TR - 1) / TR;
+    const int64_t t_begin = (int64_t)tg * tpg;
+    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
+
+    // Q_b^T split into three bf16 planes (element (p, j) of Q at plane[j][p]); zero for p in [nb, kpad)
+    {
+        const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+        const int total = kpad * nb;
+        for (int e0 = 0; e0 < total; e0 += kRT * 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + tid + kRT * i;
+                v[i] = (e < total && e < nb * nb) ? Q[e] : 0.f;   // e = p * nb + j
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + tid + kRT * i;
+                if (e < total) {
+                    const int p = e / nb, j = e - p * nb;
+                    uint16_t h, md, l;
+                    split3(v[i], h, md, l);
+                    qs[(0 * nb + j) * qld + p] = h;
+                    qs[(1 * nb + j) * qld + p] = md;
+                    qs[(2 * nb + j) * qld + p] = l;
+                }
+            }
+        }
+        // the P tiles' columns [nb, kpad) stay zero
+        for (int e = tid; e < TR * (kpad - nb); e += kRT) {
+            const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
+            ps[r * pld + c] = 0.f;
+        }
+    }
+
+    // row pieces: piece e -> row e / q, columns 4 (e % q) .. + 3 of the block slice
+    const int q = nb / 4;
+    constexpr int kIPT = (TR * 32 + kRT - 1) / kRT;   // pieces per thread for q <= 32
+    float *M = t.M[mat] + (int64_t)b * nb;
+    const void *Gv = t.G[mat];
+    const float mu = t.mu[mat];
+    f32x4 mr[kIPT], gr[kIPT];
+    auto load_tile = [&](int64_t tile) {
+#pragma unroll
+        for (int i = 0; i < kIPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q, c = 4 * (e - r * q);
+            const int64_t row = tile * TR + r;
+            mr[i] = gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tile < t_end && e < TR * q && row < m) {
+                const int64_t off = row * n + c;
+                mr[i] = *(const f32x4 *)(M + off);
+                if (GBF16) {
+                    const uint2 hb = *(const uint2 *)((const uint16_t *)Gv + (int64_t)b * nb + off);
+                    gr[i] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
+                                  bf16_to_f32((uint16_t)hb.y), bf16_to_f32((uint16_t)(hb.y >> 16))};
+                } else {
+                    gr[i] = *(const f32x4 *)((const float *)Gv + (int64_t)b * nb + off);
+                }
+            }
+        }
+    };
+
+    constexpr int kRTiles = TR / 32;              // 32-row tiles per tile
+    constexpr int kGroups = 8 / kRTiles;          // column-chunk groups
+    constexpr int kCPG = (NCH + kGroups - 1) / kGroups;
+    const int rt = wv % kRTiles, cg = wv / kRTiles;
+    const int kh = 8 * (lane >> 5);
+    uint8_t *S = t.S[mat] + (int64_t)b * ldp;
+    const int64_t sld = (int64_t)nblk * ldp;
+
+    load_tile(t_begin);
+    for (int64_t tile = t_begin; tile < t_end; ++tile) {
+        // momentum (written back along the rows) and P into the LDS tile (its last readers passed the
+        // previous tile's second barrier)
+        float *pc = ps;
+#pragma unroll
+        for (int i = 0; i < kIPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q, c = 4 * (e - r * q);
+            const int64_t row = tile * TR + r;
+            f32x4 mn, pv;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
+                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
+            }
+            if (e < TR * q) {
+                if (row < m) *(f32x4 *)(M + row * n + c) = mn;
+                *(f32x4 *)(pc + r * pld + c) = pv;   // rows past m hold zeros (their loads read zero)
+            }
+        }
+        load_tile(tile + 1);
+        __syncthreads();
+        // C^T = Q^T P^T for 32-row tile rt and this wave's column chunks
+        f32x16 acc[kCPG];
+#pragma unroll
+        for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
+        for (int ks = 0; ks < KS; ++ks) {
+            const float *pr = pc + (32 * rt + (lane & 31)) * pld + ks * kKS + kh;
+            const f32x4 p0 = *(const f32x4 *)pr, p1 = *(const f32x4 *)(pr + 4);
+            uint16_t hh[8], hm[8], hl[8];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                split3(p0[cc], hh[cc], hm[cc], hl[cc]);
+                split3(p1[cc], hh[cc + 4], hm[cc + 4], hl[cc + 4]);
+            }
+            const uint4 uh = {pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])};
+            const uint4 um = {pack2(hm[0], hm[1]), pack2(hm[2], hm[3]), pack2(hm[4], hm[5]), pack2(hm[6], hm[7])};
+            const uint4 ul = {pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])};
+            const bf16x8 ah = __builtin_bit_cast(bf16x8, uh), am = __builtin_bit_cast(bf16x8, um),
+                         al = __builtin_bit_cast(bf16x8, ul);
+            bf16x8 Qh[kCPG], Qm[kCPG], Ql[kCPG];
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) {
+                const int ch = cg * kCPG + j;
+                const int col = 32 * ch + (lane & 31);
+                const bool ok = ch < NCH && col < nb;
+                const int cs = ok ? col : 0;
+                uint4 bh = *(const uint4 *)&qs[(0 * nb + cs) * qld + ks * kKS + kh];
+                uint4 bm = *(const uint4 *)&qs[(1 * nb + cs) * qld + ks * kKS + kh];
+                uint4 bl = *(const uint4 *)&qs[(2 * nb + cs) * qld + ks * kKS + kh];
+                if (!ok) bh = bm = bl = uint4{0u, 0u, 0u, 0u};
+                Qh[j] = __builtin_bit_cast(bf16x8, bh);
+                Qm[j] = __builtin_bit_cast(bf16x8, bm);
+                Ql[j] = __builtin_bit_cast(bf16x8, bl);
+            }
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], ah, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm[j], ah, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], am, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql[j], ah, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm[j], am, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], al, acc[j], 0, 0, 0);
+        }
+        // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t -> LDS
+#pragma unroll
+        for (int j = 0; j < kCPG; ++j) {
+            const int ch = cg * kCPG + j;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;   // nb % 4 == 0: all 4 valid or none
+                const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
+                                    (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
+                if (ch < NCH && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
+            }
+        }
+        __syncthreads();
+        // sign rows out in 8-byte pieces (bytes [nb, ldp) of a row are padding, never read as signs)
+        {
+            const int q8 = ldp / 8;
+            for (int e = tid; e < TR * q8; e += kRT) {
+                const int r = e / q8, c = 8 * (e - r * q8);
+                const int64_t row = tile * TR + r;
+                if (row < m) *(uint2 *)(S + row * sld + c) = *(const uint2 *)(ss + r * ldp + c);
+            }
+        }
+    }
+}
+
+// ---- reconstruction ------------------------------------------------------------------------------
+struct ReconRowsTable {
+    const uint8_t *S[kMaxMats];
+    const float *Q[kMaxMats];
+    void *W[kMaxMats];
+    float *U[kMaxMats];
+    float lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
+};
+__host__ __device__ inline size_t recon_rows_lds(int nb, int TR, int ldp) {
+    const RowsGeo g = rows_geo(nb);
+    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * ldp) + a16((size_t)TR * g.uld * 4);
+}
+
+template <int NCH, int TR, bool WBF16>
+__global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
+                                                    int ldp, ReconRowsTable t) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const RowsGeo geo = rows_geo(nb);
+    const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, uld = geo.uld;
+    uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
+    uint8_t *ssb = lds + a16((size_t)2 * nb * qld * 2);                      // [TR][ldp]
+    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * ldp));   // [TR][uld]
+
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = x % nblk, rest = x / nblk;
+    const int tg = rest % ngroups, mat = rest / ngroups;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t ntile = (m + TR - 1) / TR;
+    const int64_t t_begin = (int64_t)tg * tpg;
+    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
+
+    // Q_b split into two fp16 planes in its natural layout (element (p, c) at plane[p][c]); zero for c >= nb
+    {
+        const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+        const int total = nb * kpad;
+        for (int e0 = 0; e0 < total; e0 += kRT * 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + tid + kRT * i;
+                const int p = e / kpad, c = e - p * kpad;
+                v[i] = (e < total && c < nb) ? Q[p * nb + c] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + tid + kRT * i;
+                if (e < total) {
+                    const int p = e / kpad, c = e - p * kpad;
+                    uint16_t h, l;
+                    split2h(v[i], h, l);
+                    qs[(0 * nb + p) * qld + c] = h;
+                    qs[(1 * nb + p) * qld + c] = l;
+                }
+            }
+        }
+    }
+
+    const uint8_t *S = t.S[mat] + (int64_t)b * ldp;
+    const int64_t sld = (int64_t)nblk * ldp;
+    const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
+    void *const Wv = t.W[mat];
+    float *const U = t.U[mat];
+    // sign rows: 8-byte pieces, ldp / 8 per row; W rows: 4-element pieces, nb / 4 per row
+    const int q8 = ldp / 8, q = nb / 4;
+    constexpr int kSPT = (TR * 16 + kRT - 1) / kRT;   // sign pieces per thread (ldp <= 128)
+    constexpr int kWPT = (TR * 32 + kRT - 1) / kRT;   // W pieces per thread (nb <= 128)
+    using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
+    uint2 sr[kSPT];
+    WVec wr[kWPT];
+    auto load_tile = [&](int64_t tile) {
+#pragma unroll
+        for (int i = 0; i < kSPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q8, c = 8 * (e - r * q8);
+            const int64_t row = tile * TR + r;
+            sr[i] = uint2{0u, 0u};
+            if (tile < t_end && e < TR * q8 && row < m) {
+                sr[i] = *(const uint2 *)(S + row * sld + c);
+                // bytes at or past nb are padding: zero them (c is a multiple of 8, nb of 4)
+                if (c + 4 >= nb) sr[i].y = 0u;
+                if (c >= nb) sr[i].x = 0u;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kWPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q, c = 4 * (e - r * q);
+            const int64_t row = tile * TR + r;
+            if (tile < t_end && e < TR * q && row < m)
+                wr[i] = *(const WVec *)((const char *)Wv + ((row * n + (int64_t)b * nb + c) * (WBF16 ? 2 : 4)));
+        }
+    };
+
+    constexpr int kRTiles = TR / 32;
+    constexpr int kGroups = 8 / kRTiles;
+    constexpr int kCPG = (NCH + kGroups - 1) / kGroups;
+    const int rt = wv % kRTiles, cg = wv / kRTiles;
+    const int kh = 8 * (lane >> 5);
+
+    load_tile(t_begin);
+    for (int64_t tile = t_begin; tile < t_end; ++tile) {
+        uint8_t *sc_ = ssb;
+#pragma unroll
+        for (int i = 0; i < kSPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q8, c = 8 * (e - r * q8);
+            if (e < TR * q8) *(uint2 *)(sc_ + r * ldp + c) = sr[i];
+        }
+        WVec wcur[kWPT];
+#pragma unroll
+        for (int i = 0; i < kWPT; ++i) wcur[i] = wr[i];
+        __syncthreads();
+        // U^T = Q S^T for 32-row tile rt and this wave's column chunks
+        f32x16 acc[kCPG];
+#pragma unroll
+        for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * ldp + ks * kKS + kh);
+            const uint4 av = {signs_f16x2<0>(sv.x), signs_f16x2<1>(sv.x), signs_f16x2<0>(sv.y), signs_f16x2<1>(sv.y)};
+            const f16x8 as = __builtin_bit_cast(f16x8, av);
+            f16x8 Bh[kCPG], Bl[kCPG];
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) {
+                const int ch = cg * kCPG + j;
+                const int p = 32 * ch + (lane & 31);
+                const bool ok = ch < NCH && p < nb;
+                const int ps = ok ? p : 0;
+                uint4 bh = *(const uint4 *)&qs[(0 * nb + ps) * qld + ks * kKS + kh];
+                uint4 bl = *(const uint4 *)&qs[(1 * nb + ps) * qld + ks * kKS + kh];
+                if (!ok) bh = bl = uint4{0u, 0u, 0u, 0u};
+                Bh[j] = __builtin_bit_cast(f16x8, bh);
+                Bl[j] = __builtin_bit_cast(f16x8, bl);
+            }
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], as, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bl[j], as, acc[j], 0, 0, 0);
+        }
+        // U tile -> LDS: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t
+#pragma unroll
+        for (int j = 0; j < kCPG; ++j) {
+            const int ch = cg * kCPG + j;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;
+                if (ch < NCH && col < nb)
+                    *(f32x4 *)(us + (32 * rt + (lane & 31)) * uld + col) =
+                        f32x4{acc[j][4 * qq], acc[j][4 * qq + 1], acc[j][4 * qq + 2], acc[j][4 * qq + 3]};
+            }
+        }
+        load_tile(tile + 1);
+        __syncthreads();
+        // W <- W - lr (s U + wd W) along the rows
+#pragma unroll
+        for (int i = 0; i < kWPT; ++i) {
+            const int e = tid + kRT * i;
+            const int r = e / q, c = 4 * (e - r * q);
+            const int64_t row = tile * TR + r;
+            if (e < TR * q && row < m) {
+                const f32x4 u = *(const f32x4 *)(us + r * uld + c);
+                const int64_t off = row * n + (int64_t)b * nb + c;
+                float w0[4];
+                if constexpr (WBF16) {
+                    const uint2 hb = wcur[i];
+                    w0[0] = bf16_to_f32((uint16_t)hb.x); w0[1] = bf16_to_f32((uint16_t)(hb.x >> 16));
+                    w0[2] = bf16_to_f32((uint16_t)hb.y); w0[3] = bf16_to_f32((uint16_t)(hb.y >> 16));
+                } else {
+                    w0[0] = wcur[i][0]; w0[1] = wcur[i][1]; w0[2] = wcur[i][2]; w0[3] = wcur[i][3];
+                }
+                float nw[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) nw[cc] = w0[cc] - lr * __builtin_fmaf(sc, u[cc], wd * w0[cc]);
+                if (U) *(f32x4 *)(U + off) = u;
+                if constexpr (WBF16) {
+                    *(uint2 *)((uint16_t *)Wv + off) =
+                        uint2{(uint32_t)f32_to_bf16(nw[0]) | ((uint32_t)f32_to_bf16(nw[1]) << 16),
+                              (uint32_t)f32_to_bf16(nw[2]) | ((uint32_t)f32_to_bf16(nw[3]) << 16)};
+                } else {
+                    *(f32x4 *)((float *)Wv + off) = f32x4{nw[0], nw[1], nw[2], nw[3]};
+                }
+            }
+        }
+    }
+}
+
+template <int NCH, int TR>
+hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const int64_t ntile = (m + TR - 1) / TR;
+    const int64_t blocks = (int64_t)nblk * cnt;
+    // about four workgroups per CU over the launch, at least 4 tiles each
+    int64_t tpg = (ntile * blocks + 1023) / 1024;
+    if (tpg < 4) tpg = 4;
+    if (tpg > ntile) tpg = ntile;
+    const int ngroups = (int)((ntile + tpg - 1) / tpg);
+    const dim3 grid((unsigned)(ngroups * blocks));
+    {
+        ProjRowsTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
+            t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+        }
+        const size_t sh = proj_rows_lds(nb, TR, ldp);
+        const bool gbf = a.g_dtype == DOBB_BF16;
+        const bool nest = a.hp[c0].nesterov != 0;
+#define DOBB_PROWS(NE, GB)                                                                                       \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_bf16x6", s, (k_proj_rows<NCH, TR, NE, GB>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups,  \
+                    (int)tpg, ldp, t);                                                                           \
+    } while (0)
+        if (!nest) { if (gbf) DOBB_PROWS(0, true); else DOBB_PROWS(0, false); }
+        else { if (gbf) DOBB_PROWS(1, true); else DOBB_PROWS(1, false); }
+#undef DOBB_PROWS
+    }
+    {
+        ReconRowsTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            const dobb_hparams &h = a.hp[c0 + i];
+            t.S[i] = (const uint8_t *)a.S[c0 + i]; t.Q[i] = a.Q[c0 + i]; t.W[i] = a.W[c0 + i];
+            t.U[i] = a.U ? a.U[c0 + i] : nullptr;
+            t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
+        }
+        const size_t sh = recon_rows_lds(nb, TR, ldp);
+#define DOBB_RROWS(WB)                                                                                           \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_recon_rows<NCH, TR, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("reconstruct_f16x2", s, (k_recon_rows<NCH, TR, WB>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups, \
+                    (int)tpg, ldp, t);                                                                           \
+    } while (0)
+        if (a.w_dtype == DOBB_BF16) DOBB_RROWS(true); else DOBB_RROWS(false);
+#undef DOBB_RROWS
+    }
+    return hipGetLastError();
+}
+
+template <int NCH>
+hipError_t launch_rows(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
+    const int nb = (int)a.sh.nb;
+    if ((int64_t)proj_rows_lds(nb, 128, ldp) <= max_lds_bytes() && (int64_t)recon_rows_lds(nb, 128, ldp) <= max_lds_bytes())
+        return launch_rows_tr<NCH, 128>(a, c0, cnt, ldp, s);
+    return launch_rows_tr<NCH, 64>(a, c0, cnt, ldp, s);
+}
+
+}  // namespace
+
+bool step_rows_eligible(const dobb_shape &sh) { return sh.nb <= 128; }
+
+hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s) {
+    const int nct = (int)((a.sh.nb + 31) / 32);
+    for (int c0 = 0; c0 < a.count;) {
+        const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
+        hipError_t e;
+        if (nct <= 1) e = launch_rows<1>(a, c0, cnt, ldp, s);
+        else if (nct <= 2) e = launch_rows<2>(a, c0, cnt, ldp, s);
+        else if (nct <= 3) e = launch_rows<3>(a, c0, cnt, ldp, s);
+        else e = launch_rows<4>(a, c0, cnt, ldp, s);
+        if (e != hipSuccess) return e;
+        c0 += cnt;
+    }
+    return hipSuccess;
+}
+
+}  // namespace dobb
