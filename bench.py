@@ -36,6 +36,7 @@ N_TOKENS = 16384
 BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
+STEP_ROWS_MAX_NB = 128        # blocks up to this width keep Q resident in LDS in the step kernels (no split_q)
 
 
 def parse():
@@ -59,13 +60,14 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
     Per kernel: algorithmic HBM bytes (each operand read or written once), algorithmic flops with the
     peak of the precision they stand for, and the matrix-core flops the kernel actually issues with
     that dtype's peak.  Units (per weight m x n with B = n / nb blocks):
-      accumulate_syrk_bf16  X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b)
+      accumulate_syrk_*     X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b);
+                            "wide" for bf16 blocks 128 < nb <= 512, nb % 8 == 0
       accumulate_reduce     A read + written: 8 nb^2 B bytes
       refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
       qr_block              nb <= 128, the whole Householder QR in one launch: 8/3 nb^3 B flops
       qr_update / qr_form   nb > 128, factor / formation updates: 4/3 nb^3 B flops each (fp32)
       qr_panel              nb > 128, panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
-      split_q               Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
+      split_q               nb > 128 only, Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
       project_bf16x6        M read + written, G read, sign bytes written: (9 + g) m n bytes;
                             2 m n nb flops (fp32 contraction), issued as six bf16 products
       reconstruct_f16x2     sign bytes read, W read + written: (1 + 2 w) m n bytes;
@@ -81,7 +83,8 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
 
     for s in specs:
         B, nb, mn = s.n // s.nb, s.nb, s.m * s.n
-        add("accumulate_syrk_bf16", 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
+        syrk = "accumulate_syrk_wide" if 128 < nb <= 512 and nb % 8 == 0 else "accumulate_syrk_bf16"
+        add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
         add("accumulate_reduce", 8.0 * nb * nb * B)
         add("refresh_gemm", 12.0 * nb * nb * B, 2.0 * nb ** 3 * B)
         if nb <= QR_SINGLE_LAUNCH_MAX_NB:
@@ -90,7 +93,8 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
             add("qr_update", 0.0, 4.0 / 3.0 * nb ** 3 * B)
             add("qr_form", 0.0, 4.0 / 3.0 * nb ** 3 * B)
             add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
-        add("split_q", 14.0 * nb * nb * B)
+        if nb > STEP_ROWS_MAX_NB:
+            add("split_q", 14.0 * nb * nb * B)
         add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
         add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
     return w
@@ -126,6 +130,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_step.md")
 # library kernel name -> (regular expression on the device symbol, source file)
 KERNEL_SYMBOLS = {
     "accumulate_syrk_bf16": (r"k_syrk_bf16<", "k_accumulate.hip"),
+    "accumulate_syrk_wide": (r"k_syrk_wide", "k_accumulate.hip"),
     "accumulate_reduce": (r"k_syrk_reduce", "k_accumulate.hip"),
     "refresh_gemm": (r"k_bgemm<", "k_refresh.hip"),
     "qr_block": (r"k_qr_block<", "k_qr.hip"),
@@ -134,8 +139,8 @@ KERNEL_SYMBOLS = {
     "qr_form": (r"k_qr_apply<\d+, false,", "k_qr.hip"),
     "qr_identity": (r"k_qr_identity", "k_qr.hip"),
     "split_q": (r"k_split_q", "k_step_bf16.hip"),
-    "project_bf16x6": (r"k_proj_bf16<", "k_step_bf16.hip"),
-    "reconstruct_f16x2": (r"k_recon_bf16<", "k_step_bf16.hip"),
+    "project_bf16x6": (r"k_proj_(bf16|rows)<", ("k_step_bf16.hip", "k_step_rows.hip")),
+    "reconstruct_f16x2": (r"k_recon_(bf16|rows)<", ("k_step_bf16.hip", "k_step_rows.hip")),
 }
 
 
@@ -143,7 +148,8 @@ def source_digest(kernel):
     """Digest of the source file that defines a kernel plus the shared internal header."""
     import hashlib
     h = hashlib.sha256()
-    for f in (KERNEL_SYMBOLS[kernel][1], "dobb_internal.h"):
+    src = KERNEL_SYMBOLS[kernel][1]
+    for f in (*(src if isinstance(src, tuple) else (src,)), "dobb_internal.h"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -10,6 +10,8 @@
 // Without a token split the EMA is fused into the epilogue; with one, fp64 partials go to the
 // workspace and k_syrk_reduce adds them in split order (deterministic, no atomics).  Each result is
 // written at (i, j) and (j, i) from the same value, so A is exactly symmetric.
+// k_syrk_bf16 takes bf16 activations in 128 x 128 tile pairs; k_syrk_wide takes bf16 blocks wider
+// than 128 whole, so that their activations are read from HBM once (both described below).
 #include "dobb_internal.h"
 
 namespace dobb {
@@ -295,27 +297,224 @@ __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int
     }
 }
 
-// Sum the token-split partials in split order, apply the EMA, write both triangles.
-// grid.x over nb*nb entries of a block, grid.y = block index within the launch (nblk * count).
+// ---- wide blocks (bf16 X, 128 < nb <= 512) ------------------------------------------------------
+// One workgroup stages a 64-token chunk of ALL nb columns of block b in LDS, so X is read from HBM
+// once.  The upper triangle of X_b^T X_b is covered by groups of 2 x 4 tiles of 32 x 32 (row tiles
+// 2p, 2p+1; column tiles from 2p on, four at a time); each wave owns one group and keeps its eight
+// accumulators in registers for the whole token split (8 MFMAs per 6 LDS operand reads).  The
+// groups of a block are spread over ceil(groups / 8) adjacent workgroups, which read the same chunks
+// close together in time, so the repeated reads are served by L2.
+// A chunk is loaded into registers (8 tokens x 8 columns per thread), transposed 8 x 8 on the way
+// into LDS ([column][token], 16-byte slots swizzled against bank conflicts), double buffered.
+// The sums stay fp32 over a split of at most 4096 tokens (256 MFMA steps); splits are added in fp64
+// by k_syrk_reduce<float> in split order.
+constexpr int kWK = 64;          // tokens per LDS chunk
+constexpr int kWMaxGroups = 32;  // 2 x 4 tile groups for up to 16 tile rows (20 needed)
+constexpr int64_t kWSplitMax = 4096;
+constexpr unsigned kWOff = 0xffffffffu;   // buffer offset past the end: the load returns zeros
+
+struct WideGroups {
+    uint8_t r0[kWMaxGroups], c0[kWMaxGroups];
+};
+
+// 16-byte slot of 8 tokens within a 128-byte column row: conflict-free for 8- and 16-lane phases
+__device__ __forceinline__ int wswz(int c) { return (c ^ (c >> 3)) & 7; }
+
+// grid.x = wgs (fastest) x blocks x matrices, renumbered per XCD; grid.y = token splits; block 512
+__global__ void __launch_bounds__(512) k_syrk_wide(int64_t N, int nb, int T32, int ngroups, int wgs, int nblk,
+                                                   int64_t tok_per_split, int nsplit, float beta, AccTable t,
+                                                   WideGroups grp, float *partial) {
+    extern __shared__ __align__(16) uint16_t xw[];   // [2][32 T32][kWK]
+    const int nbp = 32 * T32;
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int wg = x % wgs, rest = x / wgs;
+    const int b = rest % nblk, mat = rest / nblk;
+    const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t te = min<int64_t>(N, tb + tok_per_split);
+    const int64_t ld = t.ldx[mat];
+    const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // columns [nb, nbp) of both buffers stay zero (they only feed discarded entries)
+    for (int e = tid; e < 2 * (nbp - nb) * (kWK / 8); e += 512) {
+        const int bb = e / ((nbp - nb) * (kWK / 8)), r = e % ((nbp - nb) * (kWK / 8));
+        const int c = nb + r / (kWK / 8), sl = r % (kWK / 8);
+        *(uint4 *)&xw[((size_t)bb * nbp + c) * kWK + 8 * sl] = uint4{0u, 0u, 0u, 0u};
+    }
+
+    // loader role: token group tg (8 tokens), column group cg (8 columns); cg fastest.  Buffer loads
+    // with an offset past the end for idle lanes and tokens >= te read zeros without a branch.
+    const int ncg = nb / 8;
+    const int tg = tid / ncg, cg = tid - tg * ncg;
+    const bool loader = tid < ncg * (kWK / 8);
+    const __amdgpu_buffer_rsrc_t rX =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Xb), (short)0, (int)((N * ld - (int64_t)b * nb) * 2), 0x00020000);
+    uint32_t d[8][4];
+    auto gload = [&](int64_t t0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int64_t row = t0 + 8 * tg + r;
+            const unsigned off = (loader && row < te) ? (unsigned)((row * ld + 8 * cg) * 2) : kWOff;
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
+            d[r][0] = v.x; d[r][1] = v.y; d[r][2] = v.z; d[r][3] = v.w;
+        }
+    };
+
+    // compute role: group g -> row tiles R0, R0 + 1 and column tiles C0 .. C0 + 3 (wave-uniform).
+    // All eight products are issued; tiles past the grid (operand strip 0) or below the diagonal
+    // are discarded in the epilogue.
+    const int g = wg * 8 + w;
+    const bool active = g < ngroups;
+    const int R0 = active ? grp.r0[g] : 0, C0 = active ? grp.c0[g] : 0;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    int acol[2], bcol[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acol[i] = 32 * (R0 + i < T32 ? R0 + i : 0) + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bcol[j] = 32 * (C0 + j < T32 ? C0 + j : 0) + (lane & 31);
+
+    if (tb < te) gload(tb);
+    int cur = 0;
+    for (int64_t t0 = tb; t0 < te; t0 += kWK) {
+        uint16_t *xs = xw + (size_t)cur * nbp * kWK;
+        if (loader) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                uint32_t e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = d[2 * q][c >> 1], hi = d[2 * q + 1][c >> 1];
+                    e[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+                }
+                const int col = 8 * cg + c;
+                *(uint4 *)&xs[(size_t)col * kWK + 8 * (tg ^ wswz(col))] = uint4{e[0], e[1], e[2], e[3]};
+            }
+        }
+        __syncthreads();   // this chunk is staged; the other buffer's readers finished last trip
+        if (t0 + kWK < te) gload(t0 + kWK);
+        if (active) {
+#pragma unroll
+            for (int kk = 0; kk < kWK; kk += 16) {
+                const int gq = (kk >> 3) + (lane >> 5);
+                bf16x8 a[2], bv[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8 *)&xs[(size_t)acol[i] * kWK + 8 * (gq ^ wswz(acol[i]))];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8 *)&xs[(size_t)bcol[j] * kWK + 8 * (gq ^ wswz(bcol[j]))];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        cur ^= 1;
+    }
+    if (!active) return;
+
+    const int64_t tot_blocks = (int64_t)nblk * (gridDim.x / (wgs * nblk));
+    float *Ab = t.A[mat] + (int64_t)b * nb * nb;
+    float *Pb = partial ? partial + ((int64_t)blockIdx.y * tot_blocks + rest) * nb * nb : nullptr;
+    const double invN = 1.0 / (double)N, bd = (double)beta;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (R0 + i >= T32 || C0 + j >= T32 || C0 + j < R0 + i) continue;
+            const int gj = 32 * (C0 + j) + acc_col(lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gi = 32 * (R0 + i) + acc_row(r, lane);
+                if (gi >= nb || gj >= nb || gi > gj) continue;
+                if (Pb) {
+                    Pb[(int64_t)gi * nb + gj] = acc[i][j][r];
+                } else {
+                    const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
+                    const float v = (float)(bd * old + (1.0 - bd) * ((double)acc[i][j][r] * invN));
+                    Ab[(int64_t)gi * nb + gj] = v;
+                    Ab[(int64_t)gj * nb + gi] = v;
+                }
+            }
+        }
+}
+
+// Sum the token-split partials in split order, apply the EMA, write both triangles.  One
+// workgroup per 32 x 32 tile (I, J), I <= J, of a block: the partials of the upper triangle are
+// read along rows, and the mirrored tile (J, I) goes out through LDS, also along rows.
+// grid.x = T32 (T32 + 1) / 2 tile pairs, grid.y = block index within the launch (nblk * count).
+template <typename PT>
 __global__ void __launch_bounds__(256) k_syrk_reduce(int64_t N, int nb, int nblk, int nsplit, int64_t tot_blocks,
-                                                     float beta, AccTable t, const double *partial) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)nb * nb) return;
-    const int i = (int)(e / nb), j = (int)(e % nb);
-    if (i > j) return;
+                                                     float beta, AccTable t, const PT *partial) {
+    __shared__ float tile[32][33];
+    const int T32 = (nb + 31) / 32;
+    int I, J;
+    tile_pair(blockIdx.x, T32, I, J);
     const int g = blockIdx.y;
     const int b = g % nblk, mat = g / nblk;
-    double s = 0.0;
-    for (int sp = 0; sp < nsplit; ++sp) s += partial[((int64_t)sp * tot_blocks + g) * nb * nb + e];
     float *Ab = t.A[mat] + (int64_t)b * nb * nb;
-    const double bd = (double)beta;
-    const double old = beta > 0.f ? (double)Ab[e] : 0.0;
-    const float v = (float)(bd * old + (1.0 - bd) * (s / (double)N));
-    Ab[(int64_t)i * nb + j] = v;
-    Ab[(int64_t)j * nb + i] = v;
+    const double bd = (double)beta, invN = 1.0 / (double)N;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = tid + 256 * k, r = e >> 5, c = e & 31;
+        const int i = 32 * I + r, j = 32 * J + c;
+        float v = 0.f;
+        if (i < nb && j < nb && i <= j) {
+            const int64_t off = (int64_t)i * nb + j;
+            double s = 0.0;
+            for (int sp = 0; sp < nsplit; ++sp) s += (double)partial[((int64_t)sp * tot_blocks + g) * nb * nb + off];
+            const double old = beta > 0.f ? (double)Ab[off] : 0.0;
+            v = (float)(bd * old + (1.0 - bd) * (s * invN));
+            Ab[off] = v;
+        }
+        tile[r][c] = v;
+    }
+    __syncthreads();
+    // mirror: A[32 J + r][32 I + c] = tile[c][r] for entries strictly below the diagonal
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = tid + 256 * k, r = e >> 5, c = e & 31;
+        const int i = 32 * J + r, j = 32 * I + c;
+        if (i < nb && j < nb && j < i) Ab[(int64_t)i * nb + j] = tile[c][r];
+    }
 }
 
 }  // namespace
+
+// 2 x 4 tile groups over the upper triangle of a T32 x T32 grid of 32 x 32 tiles
+static int wide_groups(int T32, WideGroups *g) {
+    int n = 0;
+    for (int r = 0; r < T32; r += 2)
+        for (int c = r; c < T32; c += 4) {
+            if (g && n < kWMaxGroups) { g->r0[n] = (uint8_t)r; g->c0[n] = (uint8_t)c; }
+            ++n;
+        }
+    return n;
+}
+
+static bool wide_shape(int64_t nb) { return nb > 128 && nb <= 512 && nb % 8 == 0; }
+
+
+// Split plan of the wide kernel: at most kWSplitMax tokens per split (the fp32 sum length), enough
+// workgroups for about four per CU, at least 256 tokens per split, lengths a multiple of kWK.
+static int wide_plan(const dobb_shape &sh, int64_t N, int count, int64_t *tps) {
+    const int nb = (int)sh.nb, T32 = (nb + 31) / 32;
+    const int wgs = (wide_groups(T32, nullptr) + 7) / 8;
+    const int64_t wgtot = (int64_t)wgs * (sh.n / nb) * (count < kMaxMats ? count : kMaxMats);
+    int64_t nsplit = (1024 + wgtot - 1) / wgtot;
+    if (nsplit > N / 256) nsplit = N / 256;
+    const int64_t need = (N + kWSplitMax - 1) / kWSplitMax;
+    if (nsplit < need) nsplit = need;
+    if (nsplit < 1) nsplit = 1;
+    const int64_t len = ((N + nsplit - 1) / nsplit + kWK - 1) / kWK * kWK;
+    if (tps) *tps = len;
+    return (int)((N + len - 1) / len);
+}
 
 // Token split plan: enough workgroups for >= 4 per CU, >= 256 tokens per split, split length a
 // multiple of 64 tokens (the fp64 fold period).  Returns the number of splits; *tps its length.
@@ -341,9 +540,14 @@ int accumulate_splits(const dobb_shape &sh, int64_t N, int count, bool bf16) {
 size_t accumulate_ws(const dobb_shape &sh, int64_t N, int count) {
     const int nsplit = accumulate_splits(sh, N, count, false) > accumulate_splits(sh, N, count, true)
                            ? accumulate_splits(sh, N, count, false) : accumulate_splits(sh, N, count, true);
-    if (nsplit <= 1) return 0;
     const int cnt = count < kMaxMats ? count : kMaxMats;
-    return (size_t)nsplit * cnt * (size_t)(sh.n / sh.nb) * sh.nb * sh.nb * sizeof(double);
+    const size_t per = (size_t)cnt * (size_t)(sh.n / sh.nb) * sh.nb * sh.nb;
+    size_t bytes = nsplit > 1 ? (size_t)nsplit * per * sizeof(double) : 0;
+    if (wide_shape(sh.nb)) {   // fp32 partials of the wide kernel
+        const int ws = wide_plan(sh, N, count, nullptr);
+        if (ws > 1 && (size_t)ws * per * sizeof(float) > bytes) bytes = (size_t)ws * per * sizeof(float);
+    }
+    return bytes;
 }
 
 hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
@@ -359,12 +563,37 @@ hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
     for (int c0 = 0; c0 < a.count;) {
         const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
         AccTable t{};
-        bool vec4 = nb % 4 == 0, vec8 = nb % 8 == 0;
+        bool vec4 = nb % 4 == 0, vec8 = nb % 8 == 0, wide_ok = true;
         for (int i = 0; i < cnt; ++i) {
             t.X[i] = a.X[c0 + i]; t.A[i] = a.A[c0 + i]; t.ldx[i] = a.ldx[c0 + i];
             const uintptr_t p = (uintptr_t)t.X[i];
             vec4 = vec4 && (t.ldx[i] % 4 == 0) && ((p & (xbf ? 7u : 15u)) == 0);
             vec8 = vec8 && (t.ldx[i] % 8 == 0) && ((p & 15u) == 0);
+            wide_ok = wide_ok && a.N * t.ldx[i] * 2 < ((int64_t)1 << 31);   // 32-bit buffer offsets
+        }
+        if (xbf && vec8 && wide_ok && wide_shape(nb)) {
+            const int T32 = (nb + 31) / 32;
+            WideGroups grp{};
+            const int ngroups = wide_groups(T32, &grp);
+            const int wgs = (ngroups + 7) / 8;
+            int64_t wtps = a.N;
+            const int wsplit = wide_plan(a.sh, a.N, a.count, &wtps);
+            const size_t lds = (size_t)2 * 32 * T32 * kWK * sizeof(uint16_t);
+            (void)hipFuncSetAttribute((const void *)k_syrk_wide, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            float *wpart = wsplit > 1 ? (float *)a.partial : nullptr;
+            dim3 grid((unsigned)(wgs * nblk * cnt), (unsigned)wsplit);
+            DOBB_LAUNCH("accumulate_syrk_wide", s, k_syrk_wide, grid, dim3(512), lds, a.N, nb, T32, ngroups, wgs, nblk,
+                        wtps, wsplit, a.beta, t, grp, wpart);
+            if (wsplit > 1) {
+                const int64_t tot = (int64_t)nblk * cnt;
+                dim3 g2((unsigned)(T32 * (T32 + 1) / 2), (unsigned)tot);
+                DOBB_LAUNCH("accumulate_reduce", s, k_syrk_reduce<float>, g2, dim3(256), 0, a.N, nb, nblk, wsplit, tot,
+                            a.beta, t, (const float *)wpart);
+            }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            c0 += cnt;
+            continue;
         }
         dim3 grid((unsigned)(npairs * nblk * cnt), (unsigned)nsplit);
         double *part = nsplit > 1 ? a.partial : nullptr;
@@ -379,8 +608,9 @@ hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
         }
         if (nsplit > 1) {
             const int64_t tot = (int64_t)nblk * cnt;
-            dim3 g2((unsigned)(((int64_t)nb * nb + 255) / 256), (unsigned)tot);
-            DOBB_LAUNCH("accumulate_reduce", s, k_syrk_reduce, g2, dim3(256), 0, a.N, nb, nblk, nsplit, tot, a.beta, t,
+            const int T32 = (nb + 31) / 32;
+            dim3 g2((unsigned)(T32 * (T32 + 1) / 2), (unsigned)tot);
+            DOBB_LAUNCH("accumulate_reduce", s, k_syrk_reduce<double>, g2, dim3(256), 0, a.N, nb, nblk, nsplit, tot, a.beta, t,
                         (const double *)part);
         }
         hipError_t e = hipGetLastError();
