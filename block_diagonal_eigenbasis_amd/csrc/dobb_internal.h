@@ -140,6 +140,10 @@ hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s);
 // nb <= 128: the same arithmetic with each block's basis resident in LDS and row tiles staged
 // through LDS (k_step_rows.hip)
 bool step_rows_eligible(const dobb_shape &sh);
+// 128 < nb <= 512: basis streamed in k-slices from slice-major planes, row tiles staged in LDS
+bool step_wide_eligible(const dobb_shape &sh);
+size_t step_wide_planes_bytes(const dobb_shape &sh);
+hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s);
 hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s);
 
 struct AccumulateArgs {

@@ -518,7 +518,8 @@ bool step_bf16_eligible(const dobb_shape &sh, int norm) {
 size_t step_bf16_ws_one(const dobb_shape &sh) {
     const int64_t ldp = step_bf16_ldp(sh.nb), nblk = sh.n / sh.nb;
     const size_t s_bytes = (size_t)sh.m * nblk * ldp;
-    const size_t p_bytes = (size_t)5 * nblk * sh.nb * ldp * 2;
+    size_t p_bytes = (size_t)5 * nblk * sh.nb * ldp * 2;
+    if (step_wide_planes_bytes(sh) > p_bytes) p_bytes = step_wide_planes_bytes(sh);
     return (s_bytes + 255) / 256 * 256 + (p_bytes + 255) / 256 * 256;
 }
 
@@ -526,6 +527,7 @@ hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s) {
     const int nb = (int)a.sh.nb;
     const int ldp = step_bf16_ldp(nb);
     if (step_rows_eligible(a.sh)) return launch_step_rows(a, ldp, s);
+    if (step_wide_eligible(a.sh)) return launch_step_wide(a, ldp, s);
     const int nct = (nb + 31) / 32;   // 32-column chunks of a block
     for (int c0 = 0; c0 < a.count;) {
         const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;

@@ -1,0 +1,560 @@
+// The Dobb step (sign normalisation) for block widths 128 < nb <= 512: row tiles staged through LDS.
+//
+// Dobb paper (arXiv 2610.39412): abstract (project momentum into the block bases, sign-normalise,
+// reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
+// (Nesterov).
+//
+// Same arithmetic as the narrow-block kernels: C = P Q with both operands split into three bf16
+// parts (the six products of order <= 2); U = S Q^T with Q split into two fp16 parts (S is exact in
+// fp16).  A block's basis is too large to stay in LDS, so it is streamed one 16-deep k-slice at a
+// time from planes that k_split_wide lays out slice by slice (each slice one contiguous copy, with
+// the LDS swizzle already applied).  All row data moves along rows:
+//   k_proj_wide   M, G rows (80-column chunks) -> M <- mu M + G (written back), P -> LDS (fp32);
+//                 waves take (32-row tile, every second 32-column chunk): C^T = Q^T P^T;
+//                 sign bytes -> LDS -> rows
+//   k_recon_wide  sign-byte rows of the tile -> LDS once; waves take (64 rows, every fourth chunk):
+//                 U = S Q^T; W <- W - lr (s U + wd W) from the accumulators, 128-byte row pieces
+// The workgroups of one block are adjacent in launch order, so they run together on one XCD and
+// read the basis slices from its L2.
+#include "step_common.h"
+
+namespace dobb {
+namespace {
+using namespace stepk;
+
+constexpr int kWT = 512;        // threads per workgroup (8 waves)
+constexpr int kTR = 128;        // rows per tile
+constexpr int kKSD = 16;        // k per MFMA step
+constexpr int kKC = 80;         // projection: fp32 columns of P per LDS chunk (5 k-steps)
+constexpr int kPLD = kKC + 4;   // P chunk pitch in floats (84 / 4 odd: 16 rows on distinct banks)
+
+struct WideGeo {
+    int KS, nct, R;   // k-steps, 32-column chunks, staged rows (32 nct)
+};
+__host__ __device__ inline WideGeo wide_geo(int nb) {
+    WideGeo g;
+    g.KS = (nb + kKSD - 1) / kKSD;
+    g.nct = (nb + 31) / 32;
+    g.R = 32 * g.nct;
+    return g;
+}
+// 2-byte elements of one plane of one block: KS slices of R rows x 16 k
+__host__ __device__ inline int64_t wide_plane_elems(int nb) {
+    const WideGeo g = wide_geo(nb);
+    return (int64_t)g.KS * g.R * kKSD;
+}
+// physical 16-byte half of logical half h of row j of a slice (32 bytes per row): rows 4 apart
+// alternate, so 8 or 16 consecutive rows read the same logical half from distinct banks
+__host__ __device__ inline int qswz(int j) { return ((j >> 2) ^ (j >> 3)) & 1; }
+__host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+
+// ---- basis planes --------------------------------------------------------------------------------
+// planes (5 per matrix, each nblk x KS x R x 16 two-byte elements, slice-major):
+//   0, 1  fp16 hi / lo of Q_b:    slice ks, row p, k: Q_b[p][16 ks + k]
+//   2-4   bf16 h / m / l of Q_b^T: slice ks, row j, k: Q_b[16 ks + k][j]
+// zero where a row or k index is >= nb.
+struct SplitWideTable {
+    const float *Q[kMaxMats];
+    uint16_t *planes[kMaxMats];
+};
+
+// grid = (KS, blocks x matrices), block 256
+__global__ void __launch_bounds__(256) k_split_wide(int nb, int nblk, SplitWideTable t) {
+    __shared__ float tile[512 * 17];   // [16][R + 1] for Q^T, then [R][17] for Q (R <= 512)
+    const WideGeo geo = wide_geo(nb);
+    const int R = geo.R, KS = geo.KS;
+    const int ks = blockIdx.x, g = blockIdx.y;
+    const int b = g % nblk, mat = g / nblk;
+    const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+    const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
+    uint16_t *P = t.planes[mat] + (int64_t)b * PE + (int64_t)ks * R * kKSD;
+    const int tid = threadIdx.x, k0 = kKSD * ks;
+    (void)KS;
+    // Q^T slice: rows k0 .. k0 + 15 of Q, every column j (along rows of Q)
+    for (int e = tid; e < kKSD * R; e += 256) {
+        const int kk = e / R, j = e - kk * R;
+        tile[kk * (R + 1) + j] = (k0 + kk < nb && j < nb) ? Q[(int64_t)(k0 + kk) * nb + j] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < 2 * R; e += 256) {
+        const int j = e >> 1, hs = e & 1, h = hs ^ qswz(j);
+        uint16_t ph[8], pm[8], pl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) split3(tile[(8 * h + i) * (R + 1) + j], ph[i], pm[i], pl[i]);
+        const int64_t o = (int64_t)j * kKSD + 8 * hs;
+        *(uint4 *)(P + 2 * plane + o) = uint4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
+        *(uint4 *)(P + 3 * plane + o) = uint4{pack2(pm[0], pm[1]), pack2(pm[2], pm[3]), pack2(pm[4], pm[5]), pack2(pm[6], pm[7])};
+        *(uint4 *)(P + 4 * plane + o) = uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
+    }
+    __syncthreads();
+    // Q slice: columns k0 .. k0 + 15 of every row p
+    for (int e = tid; e < kKSD * R; e += 256) {
+        const int p = e / kKSD, kk = e - p * kKSD;
+        tile[p * 17 + kk] = (p < nb && k0 + kk < nb) ? Q[(int64_t)p * nb + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < 2 * R; e += 256) {
+        const int p = e >> 1, hs = e & 1, h = hs ^ qswz(p);
+        uint16_t qh[8], ql[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) split2h(tile[p * 17 + 8 * h + i], qh[i], ql[i]);
+        const int64_t o = (int64_t)p * kKSD + 8 * hs;
+        *(uint4 *)(P + o) = uint4{pack2(qh[0], qh[1]), pack2(qh[2], qh[3]), pack2(qh[4], qh[5]), pack2(qh[6], qh[7])};
+        *(uint4 *)(P + plane + o) = uint4{pack2(ql[0], ql[1]), pack2(ql[2], ql[3]), pack2(ql[4], ql[5]), pack2(ql[6], ql[7])};
+    }
+}
+
+// ---- projection ----------------------------------------------------------------------------------
+struct ProjWideTable {
+    float *M[kMaxMats];
+    const void *G[kMaxMats];
+    const uint16_t *planes[kMaxMats];
+    uint8_t *S[kMaxMats];
+    float mu[kMaxMats];
+};
+// LDS: two Q^T slices (3 planes each; the sign tile overlays them after the products), P chunk
+__host__ __device__ inline size_t proj_wide_qregion(int nb, int ldp) {
+    const WideGeo g = wide_geo(nb);
+    const size_t q = (size_t)2 * 3 * g.R * kKSD * 2, s = (size_t)kTR * ldp;
+    return a16(q > s ? q : s);
+}
+__host__ __device__ inline size_t proj_wide_lds(int nb, int ldp) {
+    return proj_wide_qregion(nb, ldp) + (size_t)kTR * kPLD * 4;
+}
+
+// grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
+// NCT = ceil(nb / 32).  Wave w: 32-row tile rt = w % 4, column chunks cg + 2 j (cg = w / 4).
+template <int NCT, int NEST, bool GBF16>
+__global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
+                                                   int ldp, ProjWideTable t) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int NCW = (NCT + 1) / 2, R = 32 * NCT, nct = NCT;
+    const int KS = (nb + kKSD - 1) / kKSD;
+    uint16_t *qs = (uint16_t *)lds;                                   // [2][3][R][16]
+    uint8_t *ss = lds;                                                // [kTR][ldp], after the products
+    float *ps = (float *)(lds + proj_wide_qregion(nb, ldp));          // [kTR][kPLD]
+
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int tg = x % ngroups, rest = x / ngroups;
+    const int b = rest % nblk, mat = rest / nblk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rt = w & 3, cg = w >> 2;
+    const int64_t ntile = (m + kTR - 1) / kTR;
+    const int64_t t_begin = (int64_t)tg * tpg;
+    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
+
+    constexpr int kGS = GBF16 ? 2 : 4;
+    const int64_t mn_el = m * n - (int64_t)b * nb;
+    const __amdgpu_buffer_rsrc_t rM = make_rsrc(t.M[mat] + (int64_t)b * nb, mn_el * 4);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc((const char *)t.G[mat] + (int64_t)b * nb * kGS, mn_el * kGS);
+    const int64_t sld = (int64_t)nblk * ldp;
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(t.S[mat] + (int64_t)b * ldp, m * sld - (int64_t)b * ldp);
+    const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
+    const uint16_t *QT = t.planes[mat] + 2 * plane + (int64_t)b * PE;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QT, (2 * plane + PE) * 2);
+    const float mu = t.mu[mat];
+
+    // M / G chunk pieces: kTR rows x 20 four-column pieces, 5 per thread
+    constexpr int kMP = kTR * (kKC / 4) / kWT;
+    f32x4 mr[kMP], gr[kMP];
+    auto mg_off = [&](int i, int64_t tile, int kc0) -> unsigned {
+        const int e = tid + kWT * i;
+        const int r = e / (kKC / 4), c = kc0 + 4 * (e - r * (kKC / 4));
+        const int64_t row = tile * kTR + r;
+        return (tile < t_end && row < m && c < nb) ? (unsigned)(row * n + c) : kOff;
+    };
+    auto load_mg = [&](int64_t tile, int kc0) {
+#pragma unroll
+        for (int i = 0; i < kMP; ++i) {
+            const unsigned o = mg_off(i, tile, kc0);
+            mr[i] = bload4(rM, boff(o, 4));
+            if constexpr (GBF16) {
+                const uint2 hb = bload2u(rG, boff(o, 2));
+                gr[i] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
+                              bf16_to_f32((uint16_t)hb.y), bf16_to_f32((uint16_t)(hb.y >> 16))};
+            } else {
+                gr[i] = bload4(rG, boff(o, 4));
+            }
+        }
+    };
+    // momentum written back along the rows; P into the LDS chunk (zeros past m and nb)
+    auto stage_p = [&](int64_t tile, int kc0) {
+#pragma unroll
+        for (int i = 0; i < kMP; ++i) {
+            const int e = tid + kWT * i;
+            const int r = e / (kKC / 4), c = 4 * (e - r * (kKC / 4));
+            f32x4 mn, pv;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
+                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
+            }
+            bstore4(mn, rM, boff(mg_off(i, tile, kc0), 4));
+            *(f32x4 *)(ps + r * kPLD + c) = pv;
+        }
+    };
+    // Q^T slice pieces: 3 planes x R rows x 2 halves of 16 bytes
+    constexpr int kQP = (6 * R + kWT - 1) / kWT;
+    uint4 qr[kQP];
+    auto load_q = [&](int ks) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            const int pl = e / (2 * R), rem = e - pl * 2 * R;
+            const unsigned o = e < 6 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
+            qr[i] = bload4u(rQ, boff(o, 2));
+        }
+    };
+    auto store_q = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            if (e < 6 * R) *(uint4 *)(qs + (size_t)buf * 3 * R * kKSD + 8 * e) = qr[i];
+        }
+    };
+
+    const int kh = 8 * (lane >> 5);
+    const int nchunk = (KS + 4) / 5;
+    int par = 0;
+    load_mg(t_begin, 0);
+    load_q(0);
+    for (int64_t tile = t_begin; tile < t_end; ++tile) {
+        f32x16 acc[NCW];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+        for (int c = 0; c < nchunk; ++c) {
+            const int kc0 = c * kKC;
+            __syncthreads();   // the last chunk's products are done with ps, the sign drain with qs
+            stage_p(tile, kc0);
+            if (c + 1 < nchunk) load_mg(tile, kc0 + kKC);
+            else load_mg(tile + 1, 0);
+            const int s_end = KS - 5 * c < 5 ? KS - 5 * c : 5;
+            for (int s = 0; s < s_end; ++s) {
+                const int ks = 5 * c + s;
+                store_q(par);
+                load_q(ks + 1 < KS ? ks + 1 : 0);   // the next tile starts over at slice 0
+                __syncthreads();
+                const float *pr = ps + (32 * rt + (lane & 31)) * kPLD + kKSD * s + kh;
+                bf16x8 ah, am, al;
+                split3x8(*(const f32x4 *)pr, *(const f32x4 *)(pr + 4), ah, am, al);
+                const uint16_t *qb = qs + (size_t)par * 3 * R * kKSD;
+#pragma unroll
+                for (int j = 0; j < NCW; ++j) {
+                    const int ch = cg + 2 * j;
+                    if (ch < nct) {
+                        const int jr = 32 * ch + (lane & 31);
+                        const int o = jr * kKSD + 8 * ((lane >> 5) ^ qswz(jr));
+                        const bf16x8 Qh = *(const bf16x8 *)(qb + o);
+                        const bf16x8 Qm = *(const bf16x8 *)(qb + R * kKSD + o);
+                        const bf16x8 Ql = *(const bf16x8 *)(qb + 2 * R * kKSD + o);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, ah, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm, ah, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, am, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql, ah, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm, am, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, al, acc[j], 0, 0, 0);
+                    }
+                }
+                par ^= 1;
+            }
+        }
+        // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 8 qq + 4 (l / 32) + 0..3 -> LDS
+        __syncthreads();   // every wave is done with the Q slices that the sign tile overlays
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int ch = cg + 2 * j;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int col = 32 * ch + 8 * qq + 4 * (lane >> 5);   // nb % 4 == 0: all 4 valid or none
+                const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
+                                    (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
+                if (ch < nct && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
+            }
+        }
+        __syncthreads();
+        // sign rows out in 8-byte pieces (bytes [nb, ldp) of a row are padding, never read as signs)
+        const int q8 = ldp / 8;
+        for (int e = tid; e < kTR * q8; e += kWT) {
+            const int r = e / q8, c = 8 * (e - r * q8);
+            const int64_t row = tile * kTR + r;
+            bstore2u(*(const uint2 *)(ss + r * ldp + c), rS, row < m ? (unsigned)(row * sld + c) : kOff);
+        }
+    }
+}
+
+// ---- reconstruction ------------------------------------------------------------------------------
+struct ReconWideTable {
+    const uint8_t *S[kMaxMats];
+    const uint16_t *planes[kMaxMats];
+    void *W[kMaxMats];
+    float *U[kMaxMats];
+    float lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
+};
+// sign tile pitch: >= ldp, a multiple of 8 with an odd number of 8-byte units (rows on distinct banks)
+__host__ __device__ inline int wide_spitch(int ldp) { return (ldp / 8) % 2 ? ldp : ldp + 8; }
+// LDS: two Q slices (2 planes each), two sign tiles (this tile's and the next one's)
+__host__ __device__ inline size_t recon_wide_lds(int nb, int ldp) {
+    const WideGeo g = wide_geo(nb);
+    return a16((size_t)2 * 2 * g.R * kKSD * 2) + 2 * a16((size_t)kTR * wide_spitch(ldp));
+}
+
+// grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
+// NCT = ceil(nb / 32).  Wave w: rows 64 rg .. + 63 (rg = w / 4, two 32-row tiles), column chunks
+// cg + 4 j (cg = w % 4).
+template <int NCT, bool WBF16>
+__global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
+                                                    int ldp, ReconWideTable t) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int NCW = (NCT + 3) / 4, R = 32 * NCT, nct = NCT;
+    const int KS = (nb + kKSD - 1) / kKSD;
+    const int spitch = wide_spitch(ldp);
+    uint16_t *qs = (uint16_t *)lds;                                              // [2][2][R][16]
+    uint8_t *ss0 = lds + a16((size_t)2 * 2 * R * kKSD * 2);                      // [2][kTR][spitch]
+    const size_t sbuf = a16((size_t)kTR * spitch);
+
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int tg = x % ngroups, rest = x / ngroups;
+    const int b = rest % nblk, mat = rest / nblk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = w >> 2, cg = w & 3;
+    const int64_t ntile = (m + kTR - 1) / kTR;
+    const int64_t t_begin = (int64_t)tg * tpg;
+    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
+
+    constexpr int kWS = WBF16 ? 2 : 4;
+    const int64_t mn_el = m * n - (int64_t)b * nb;
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc((const char *)t.W[mat] + (int64_t)b * nb * kWS, mn_el * kWS);
+    float *const U = t.U[mat];
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(U ? (const void *)(U + (int64_t)b * nb) : t.W[mat], U ? mn_el * 4 : 0);
+    const int64_t sld = (int64_t)nblk * ldp;
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(t.S[mat] + (int64_t)b * ldp, m * sld - (int64_t)b * ldp);
+    const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
+    const uint16_t *QN = t.planes[mat] + (int64_t)b * PE;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QN, (plane + PE) * 2);
+    const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
+
+    // sign tile pieces: kTR rows x ldp / 8 eight-byte pieces (ldp <= R); piece i of a thread is
+    // e = tid + kWT i, row e / q8, bytes 8 (e % q8) .. + 7
+    constexpr int kSP = (kTR * (R / 8) + kWT - 1) / kWT;
+    const int q8 = ldp / 8;
+    auto load_piece = [&](int64_t tile, int i) -> uint2 {
+        const int e = tid + kWT * i;
+        const int r = e / q8, c = 8 * (e - r * q8);
+        const int64_t row = tile * kTR + r;
+        const unsigned o = (tile < t_end && e < kTR * q8 && row < m) ? (unsigned)(row * sld + c) : kOff;
+        uint2 v = bload2u(rS, o);
+        // bytes at or past nb are padding: zero them (c is a multiple of 8, nb of 4)
+        if (c + 4 >= nb) v.y = 0u;
+        if (c >= nb) v.x = 0u;
+        return v;
+    };
+    auto store_piece = [&](uint8_t *ss, int i, uint2 v) {
+        const int e = tid + kWT * i;
+        const int r = e / q8, c = 8 * (e - r * q8);
+        if (e < kTR * q8) *(uint2 *)(ss + r * spitch + c) = v;
+    };
+    // Q slice pieces: 2 planes x R rows x 2 halves
+    constexpr int kQP = (4 * R + kWT - 1) / kWT;
+    uint4 qr[kQP];
+    auto load_q = [&](int ks) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            const int pl = e / (2 * R), rem = e - pl * 2 * R;
+            const unsigned o = e < 4 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
+            qr[i] = bload4u(rQ, boff(o, 2));
+        }
+    };
+    auto store_q = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            if (e < 4 * R) *(uint4 *)(qs + (size_t)buf * 2 * R * kKSD + 8 * e) = qr[i];
+        }
+    };
+
+    const int kh = 8 * (lane >> 5);
+    int par = 0, sp = 0;
+    load_q(0);
+#pragma unroll
+    for (int i = 0; i < kSP; ++i) store_piece(ss0, i, load_piece(t_begin, i));
+    for (int64_t tile = t_begin; tile < t_end; ++tile) {
+        const uint8_t *ss = ss0 + sp * sbuf;      // this tile's sign rows
+        uint8_t *sn = ss0 + (sp ^ 1) * sbuf;      // the next tile's, one piece per k-step
+        f32x16 acc[2][NCW];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) acc[i][j] = (f32x16){};
+        uint2 snext = uint2{0u, 0u};
+        for (int ks = 0; ks < KS; ++ks) {
+            store_q(par);
+            load_q(ks + 1 < KS ? ks + 1 : 0);
+            if (ks >= 1 && ks <= kSP) store_piece(sn, ks - 1, snext);
+            if (ks < kSP) snext = load_piece(tile + 1, ks);
+            __syncthreads();
+            f16x8 as[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                as[i] = signs_f16x8(*(const uint2 *)(ss + (64 * rg + 32 * i + (lane & 31)) * spitch + kKSD * ks + kh));
+            const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                const int ch = cg + 4 * j;
+                if (ch < nct) {
+                    const int p = 32 * ch + (lane & 31);
+                    const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
+                    const f16x8 Bh = *(const f16x8 *)(qb + o);
+                    const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bh, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bl, acc[i][j], 0, 0, 0);
+                    }
+                }
+            }
+            par ^= 1;
+        }
+        // pieces that did not fit in the k-steps (kSP >= KS cannot happen for nb > 128, kept for safety)
+        if (KS <= kSP) store_piece(sn, KS - 1, snext);
+        for (int i = KS; i < kSP; ++i) store_piece(sn, i, load_piece(tile + 1, i));
+        sp ^= 1;
+        // W <- W - lr (s U + wd W): lane holds column 32 ch + l % 32 of rows 8 (r / 4) + 4 (l / 32) + r % 4
+        // of each 32-row tile; each load / store instruction covers 128 contiguous bytes of two rows.
+        // Eight rows at a time: their loads are all issued before the first store.
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int ch = cg + 4 * j;
+            if (ch >= nct) continue;
+            const int col = 32 * ch + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t rl = tile * kTR + 64 * rg + 32 * i + 4 * (lane >> 5);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    unsigned off[8];
+                    float wv[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int r = 8 * h + q;
+                        const int64_t row = rl + 8 * (r >> 2) + (r & 3);
+                        off[q] = (row < m && col < nb) ? (unsigned)(row * n + col) : kOff;
+                        wv[q] = WBF16 ? bf16_to_f32(bload1h(rW, boff(off[q], 2))) : bload1(rW, boff(off[q], 4));
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float u = acc[i][j][8 * h + q];
+                        const float nw = wv[q] - lr * __builtin_fmaf(sc, u, wd * wv[q]);
+                        if (U) bstore1(u, rU, boff(off[q], 4));
+                        if constexpr (WBF16) bstore1h(f32_to_bf16(nw), rW, boff(off[q], 2));
+                        else bstore1(nw, rW, boff(off[q], 4));
+                    }
+                }
+            }
+        }
+    }
+}
+
+// One 128-row tile per workgroup: the workgroups of a block are then as many as its tiles and run
+// together on one XCD, sharing its basis slices in L2.
+int64_t wide_tpg(int64_t, int64_t) { return 1; }
+
+template <int NCT>
+hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const WideGeo geo = wide_geo(nb);
+    {
+        SplitWideTable t{};
+        for (int i = 0; i < cnt; ++i) { t.Q[i] = a.Q[c0 + i]; t.planes[i] = a.planes[c0 + i]; }
+        DOBB_LAUNCH("split_q", s, k_split_wide, dim3((unsigned)geo.KS, (unsigned)(nblk * cnt)), dim3(256), 0, nb, nblk, t);
+    }
+    const int64_t ntile = (m + kTR - 1) / kTR;
+    const int64_t tpg = wide_tpg(ntile, (int64_t)nblk * cnt);
+    const int ngroups = (int)((ntile + tpg - 1) / tpg);
+    const dim3 grid((unsigned)((int64_t)ngroups * nblk * cnt));
+    {
+        ProjWideTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i];
+            t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+        }
+        const size_t sh = proj_wide_lds(nb, ldp);
+        const bool gbf = a.g_dtype == DOBB_BF16;
+        const bool nest = a.hp[c0].nesterov != 0;
+#define DOBB_PWIDE(NE, GB)                                                                                       \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_proj_wide<NCT, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_bf16x6", s, (k_proj_wide<NCT, NE, GB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups,  \
+                    (int)tpg, ldp, t);                                                                           \
+    } while (0)
+        if (!nest) { if (gbf) DOBB_PWIDE(0, true); else DOBB_PWIDE(0, false); }
+        else { if (gbf) DOBB_PWIDE(1, true); else DOBB_PWIDE(1, false); }
+#undef DOBB_PWIDE
+    }
+    {
+        ReconWideTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            const dobb_hparams &h = a.hp[c0 + i];
+            t.S[i] = (const uint8_t *)a.S[c0 + i]; t.planes[i] = a.planes[c0 + i]; t.W[i] = a.W[c0 + i];
+            t.U[i] = a.U ? a.U[c0 + i] : nullptr;
+            t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
+        }
+        const size_t sh = recon_wide_lds(nb, ldp);
+#define DOBB_RWIDE(WB)                                                                                           \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_recon_wide<NCT, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("reconstruct_f16x2", s, (k_recon_wide<NCT, WB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups, \
+                    (int)tpg, ldp, t);                                                                           \
+    } while (0)
+        if (a.w_dtype == DOBB_BF16) DOBB_RWIDE(true); else DOBB_RWIDE(false);
+#undef DOBB_RWIDE
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool step_wide_eligible(const dobb_shape &sh) {
+    if (sh.nb <= 128 || sh.nb > 512 || sh.nb % 4 != 0) return false;
+    const int ldp = step_bf16_ldp(sh.nb);
+    // 32-bit buffer offsets: the largest byte offset into M, G, W, U or the sign codes
+    const int64_t big = sh.m * sh.n * 4 > sh.m * (sh.n / sh.nb) * ldp ? sh.m * sh.n * 4 : sh.m * (sh.n / sh.nb) * ldp;
+    if (big >= ((int64_t)1 << 31)) return false;
+    return (int64_t)proj_wide_lds((int)sh.nb, ldp) <= max_lds_bytes() &&
+           (int64_t)recon_wide_lds((int)sh.nb, ldp) <= max_lds_bytes();
+}
+
+size_t step_wide_planes_bytes(const dobb_shape &sh) {
+    return (size_t)5 * (size_t)(sh.n / sh.nb) * (size_t)wide_plane_elems((int)sh.nb) * 2;
+}
+
+hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {
+    const int nct = (int)((a.sh.nb + 31) / 32);
+    for (int c0 = 0; c0 < a.count;) {
+        const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
+        hipError_t e;
+        switch (nct) {
+            case 5: e = launch_wide_cfg<5>(a, c0, cnt, ldp, s); break;
+            case 6: e = launch_wide_cfg<6>(a, c0, cnt, ldp, s); break;
+            case 7: e = launch_wide_cfg<7>(a, c0, cnt, ldp, s); break;
+            case 8: e = launch_wide_cfg<8>(a, c0, cnt, ldp, s); break;
+            case 9: e = launch_wide_cfg<9>(a, c0, cnt, ldp, s); break;
+            case 10: e = launch_wide_cfg<10>(a, c0, cnt, ldp, s); break;
+            case 11: e = launch_wide_cfg<11>(a, c0, cnt, ldp, s); break;
+            case 12: e = launch_wide_cfg<12>(a, c0, cnt, ldp, s); break;
+            case 13: e = launch_wide_cfg<13>(a, c0, cnt, ldp, s); break;
+            case 14: e = launch_wide_cfg<14>(a, c0, cnt, ldp, s); break;
+            case 15: e = launch_wide_cfg<15>(a, c0, cnt, ldp, s); break;
+            default: e = launch_wide_cfg<16>(a, c0, cnt, ldp, s); break;
+        }
+        if (e != hipSuccess) return e;
+        c0 += cnt;
+    }
+    return hipSuccess;
+}
+
+}  // namespace dobb

@@ -228,7 +228,8 @@ def _run_step(W, G, M, Q, nb, hp, norm):
     return W, M, U
 
 
-@pytest.mark.parametrize("m,n,nb", [(768, 768, 192), (130, 96, 48), (70, 75, 25), (200, 800, 400), (64, 256, 128)])
+@pytest.mark.parametrize("m,n,nb", [(768, 768, 192), (130, 96, 48), (70, 75, 25), (200, 800, 400), (64, 256, 128),
+                                    (130, 272, 136)])   # nb = 136: a partial last k-step, ragged rows
 def test_step_matches_oracle(m, n, nb):
     print(f"step m={m} n={n} nb={nb}", flush=True)
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=m + n + nb)
@@ -261,8 +262,9 @@ def test_step_identity_round_trip():
     np.testing.assert_allclose(host(U), host(M), atol=2e-6 * float(M.abs().max()))
 
 
-def test_step_bf16_weights_and_gradients():
-    m, n, nb = 256, 512, 128
+@pytest.mark.parametrize("m,n,nb", [(256, 512, 128), (150, 400, 200)])
+def test_step_bf16_weights_and_gradients(m, n, nb):
+    print(f"step bf16 m={m} n={n} nb={nb}", flush=True)
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=9, w_dtype=torch.bfloat16, g_dtype=torch.bfloat16)
     W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
     W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
@@ -286,6 +288,27 @@ def test_step_nesterov_and_column_l2():
                               hp["update_scale"], norm=oracle.NORM_COL_L2)
     assert np.linalg.norm(host(U_l) - U_r) <= 1e-5 * np.linalg.norm(U_r)
     np.testing.assert_allclose(host(W_l), W_r, rtol=1e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("m,n,nb", [(96, 128, 64), (140, 400, 200)])
+def test_step_sign_nesterov(m, n, nb):
+    """Nesterov (Table 19) through the sign path: P = G + mu (mu M + G) is what gets projected."""
+    print(f"step nesterov m={m} n={n} nb={nb}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=41 + nb, nesterov=True)
+    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"], nesterov=True)
+    _check_momentum(M_s, M, G, hp["momentum"], M_r)
+    P_r = G.cpu().double().numpy() + hp["momentum"] * M_r
+    U_sh = host(U_s)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = P_r[:, sl] @ Qh[b]
+        S_gpu = np.rint(U_sh[:, sl] @ Qh[b])
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref))
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the dead zone"
+    assert np.mean(np.abs(U_sh - U_r) > 1e-3) <= 1e-3
+    check_w(host(W_s), host(W), U_sh, hp)
 
 
 def test_step_sign_flip_invariance_is_bitwise():
