@@ -1,4 +1,4 @@
-// The Dobb step (sign normalisation) for block widths 128 < nb <= 512: row tiles staged through LDS.
+// The Dobb step (sign normalisation) for block widths 128 < nb <= 416: row tiles staged through LDS.
 //
 // Dobb paper (arXiv 2610.39412): abstract (project momentum into the block bases, sign-normalise,
 // reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
@@ -9,7 +9,8 @@
 // fp16).  A block's basis is too large to stay in LDS, so it is streamed one 16-deep k-slice at a
 // time from planes that k_split_wide lays out slice by slice (each slice one contiguous copy, with
 // the LDS swizzle already applied).  All row data moves along rows:
-//   k_proj_wide   M, G rows (80-column chunks) -> M <- mu M + G (written back), P -> LDS (fp32);
+//   k_proj_wide   M, G rows (64-column chunks) -> M <- mu M + G (written back), P -> LDS (split into
+//                 three bf16 planes once);
 //                 waves take (32-row tile, every second 32-column chunk): C^T = Q^T P^T;
 //                 sign bytes -> LDS -> rows
 //   k_recon_wide  sign-byte rows of the tile -> LDS once; waves take (64 rows, every fourth chunk):
@@ -25,8 +26,9 @@ using namespace stepk;
 constexpr int kWT = 512;        // threads per workgroup (8 waves)
 constexpr int kTR = 128;        // rows per tile
 constexpr int kKSD = 16;        // k per MFMA step
-constexpr int kKC = 80;         // projection: fp32 columns of P per LDS chunk (5 k-steps)
-constexpr int kPLD = kKC + 4;   // P chunk pitch in floats (84 / 4 odd: 16 rows on distinct banks)
+constexpr int kKC = 64;         // projection: columns of P per LDS chunk (4 k-steps)
+constexpr int kPLD = kKC + 8;   // P plane pitch in bf16 (144 bytes: 16 rows on distinct 16-byte slots)
+constexpr int kSPC = kKC / 16;  // k-steps per P chunk
 
 struct WideGeo {
     int KS, nct, R;   // k-steps, 32-column chunks, staged rows (32 nct)
@@ -112,14 +114,15 @@ struct ProjWideTable {
     uint8_t *S[kMaxMats];
     float mu[kMaxMats];
 };
-// LDS: two Q^T slices (3 planes each; the sign tile overlays them after the products), P chunk
+// LDS: two Q^T slices (3 planes each; the sign tile overlays them after the products), the P chunk
+// split into three bf16 planes
 __host__ __device__ inline size_t proj_wide_qregion(int nb, int ldp) {
     const WideGeo g = wide_geo(nb);
     const size_t q = (size_t)2 * 3 * g.R * kKSD * 2, s = (size_t)kTR * ldp;
     return a16(q > s ? q : s);
 }
 __host__ __device__ inline size_t proj_wide_lds(int nb, int ldp) {
-    return proj_wide_qregion(nb, ldp) + (size_t)kTR * kPLD * 4;
+    return proj_wide_qregion(nb, ldp) + (size_t)3 * kTR * kPLD * 2;
 }
 
 // grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
@@ -132,7 +135,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
     const int KS = (nb + kKSD - 1) / kKSD;
     uint16_t *qs = (uint16_t *)lds;                                   // [2][3][R][16]
     uint8_t *ss = lds;                                                // [kTR][ldp], after the products
-    float *ps = (float *)(lds + proj_wide_qregion(nb, ldp));          // [kTR][kPLD]
+    uint16_t *ps = (uint16_t *)(lds + proj_wide_qregion(nb, ldp));    // [3][kTR][kPLD]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int tg = x % ngroups, rest = x / ngroups;
@@ -162,7 +165,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
         const int e = tid + kWT * i;
         const int r = e / (kKC / 4), c = kc0 + 4 * (e - r * (kKC / 4));
         const int64_t row = tile * kTR + r;
-        return (tile < t_end && row < m && c < nb) ? (unsigned)(row * n + c) : kOff;
+        return (tile < t_end && row < m && c < nb) ? (unsigned)row * (unsigned)n + (unsigned)c : kOff;
     };
     auto load_mg = [&](int64_t tile, int kc0) {
 #pragma unroll
@@ -178,20 +181,25 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
             }
         }
     };
-    // momentum written back along the rows; P into the LDS chunk (zeros past m and nb)
+    // momentum written back along the rows; P split once into three bf16 planes of the LDS chunk
+    // (zeros past m and nb)
     auto stage_p = [&](int64_t tile, int kc0) {
 #pragma unroll
         for (int i = 0; i < kMP; ++i) {
             const int e = tid + kWT * i;
             const int r = e / (kKC / 4), c = 4 * (e - r * (kKC / 4));
-            f32x4 mn, pv;
+            f32x4 mn;
+            uint16_t h[4], md[4], l[4];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
-                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
+                split3(NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc], h[cc], md[cc], l[cc]);
             }
             bstore4(mn, rM, boff(mg_off(i, tile, kc0), 4));
-            *(f32x4 *)(ps + r * kPLD + c) = pv;
+            uint16_t *pp = ps + r * kPLD + c;
+            *(uint2 *)pp = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+            *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(md[0], md[1]), pack2(md[2], md[3])};
+            *(uint2 *)(pp + 2 * kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
         }
     };
     // Q^T slice pieces: 3 planes x R rows x 2 halves of 16 bytes
@@ -215,7 +223,11 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
     };
 
     const int kh = 8 * (lane >> 5);
-    const int nchunk = (KS + 4) / 5;
+    // this lane's Q^T slice offset for chunk cg; chunk cg + 2 j is 64 j rows further (qswz depends on
+    // row bits 2 and 3 only, so the swizzle is the same)
+    const int qrow = 32 * cg + (lane & 31);
+    const int qoff = qrow * kKSD + 8 * ((lane >> 5) ^ qswz(qrow));
+    const int nchunk = (KS + kSPC - 1) / kSPC;
     int par = 0;
     load_mg(t_begin, 0);
     load_q(0);
@@ -229,31 +241,50 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
             stage_p(tile, kc0);
             if (c + 1 < nchunk) load_mg(tile, kc0 + kKC);
             else load_mg(tile + 1, 0);
-            const int s_end = KS - 5 * c < 5 ? KS - 5 * c : 5;
+            const int s_end = KS - kSPC * c < kSPC ? KS - kSPC * c : kSPC;
             for (int s = 0; s < s_end; ++s) {
-                const int ks = 5 * c + s;
+                const int ks = kSPC * c + s;
                 store_q(par);
                 load_q(ks + 1 < KS ? ks + 1 : 0);   // the next tile starts over at slice 0
                 __syncthreads();
-                const float *pr = ps + (32 * rt + (lane & 31)) * kPLD + kKSD * s + kh;
-                bf16x8 ah, am, al;
-                split3x8(*(const f32x4 *)pr, *(const f32x4 *)(pr + 4), ah, am, al);
-                const uint16_t *qb = qs + (size_t)par * 3 * R * kKSD;
+                const uint16_t *pr = ps + (32 * rt + (lane & 31)) * kPLD + kKSD * s + kh;
+                const bf16x8 ah = *(const bf16x8 *)pr;
+                const bf16x8 am = *(const bf16x8 *)(pr + kTR * kPLD);
+                const bf16x8 al = *(const bf16x8 *)(pr + 2 * kTR * kPLD);
+                const uint16_t *qb = qs + (size_t)par * 3 * R * kKSD + qoff;
+                // chunks two at a time, their products interleaved so that consecutive MFMAs are
+                // independent
 #pragma unroll
-                for (int j = 0; j < NCW; ++j) {
-                    const int ch = cg + 2 * j;
-                    if (ch < nct) {
-                        const int jr = 32 * ch + (lane & 31);
-                        const int o = jr * kKSD + 8 * ((lane >> 5) ^ qswz(jr));
-                        const bf16x8 Qh = *(const bf16x8 *)(qb + o);
-                        const bf16x8 Qm = *(const bf16x8 *)(qb + R * kKSD + o);
-                        const bf16x8 Ql = *(const bf16x8 *)(qb + 2 * R * kKSD + o);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, ah, acc[j], 0, 0, 0);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm, ah, acc[j], 0, 0, 0);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, am, acc[j], 0, 0, 0);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql, ah, acc[j], 0, 0, 0);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm, am, acc[j], 0, 0, 0);
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh, al, acc[j], 0, 0, 0);
+                for (int j = 0; j < NCW; j += 2) {
+                    const bool two = j + 1 < NCW && cg + 2 * (j + 1) < nct;
+                    if (cg + 2 * j < nct) {
+                        const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
+                        const uint16_t *q1 = q0 + 2 * 32 * kKSD;
+                        const bf16x8 Qh0 = *(const bf16x8 *)q0, Qm0 = *(const bf16x8 *)(q0 + R * kKSD),
+                                     Ql0 = *(const bf16x8 *)(q0 + 2 * R * kKSD);
+                        if (two) {
+                            const bf16x8 Qh1 = *(const bf16x8 *)q1, Qm1 = *(const bf16x8 *)(q1 + R * kKSD),
+                                         Ql1 = *(const bf16x8 *)(q1 + 2 * R * kKSD);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, am, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, am, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, am, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm1, am, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, al, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, al, acc[j + 1], 0, 0, 0);
+                        } else {
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, am, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, am, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, al, acc[j], 0, 0, 0);
+                        }
                     }
                 }
                 par ^= 1;
@@ -339,9 +370,17 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
     // e = tid + kWT i, row e / q8, bytes 8 (e % q8) .. + 7
     constexpr int kSP = (kTR * (R / 8) + kWT - 1) / kWT;
     const int q8 = ldp / 8;
+    const float inv_q8 = 1.0f / (float)q8;
+    // e / q8 for e < 2^16: the float quotient is within one of the exact one; fix it up
+    auto divq8 = [&](int e) -> int {
+        int r = (int)((float)e * inv_q8);
+        r -= r * q8 > e;
+        r += (r + 1) * q8 <= e;
+        return r;
+    };
     auto load_piece = [&](int64_t tile, int i) -> uint2 {
         const int e = tid + kWT * i;
-        const int r = e / q8, c = 8 * (e - r * q8);
+        const int r = divq8(e), c = 8 * (e - r * q8);
         const int64_t row = tile * kTR + r;
         const unsigned o = (tile < t_end && e < kTR * q8 && row < m) ? (unsigned)(row * sld + c) : kOff;
         uint2 v = bload2u(rS, o);
@@ -352,7 +391,7 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
     };
     auto store_piece = [&](uint8_t *ss, int i, uint2 v) {
         const int e = tid + kWT * i;
-        const int r = e / q8, c = 8 * (e - r * q8);
+        const int r = divq8(e), c = 8 * (e - r * q8);
         if (e < kTR * q8) *(uint2 *)(ss + r * spitch + c) = v;
     };
     // Q slice pieces: 2 planes x R rows x 2 halves
@@ -409,10 +448,9 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
                     const f16x8 Bh = *(const f16x8 *)(qb + o);
                     const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bh, acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bl, acc[i][j], 0, 0, 0);
-                    }
+                    for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bh, acc[i][j], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bl, acc[i][j], 0, 0, 0);
                 }
             }
             par ^= 1;
@@ -432,15 +470,16 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t rl = tile * kTR + 64 * rg + 32 * i + 4 * (lane >> 5);
+                const unsigned base = (unsigned)rl * (unsigned)n + (unsigned)col;   // < 2^31 (checked on the host)
+                const int vr = col < nb ? (int)(m - rl < 32 ? m - rl : 32) : 0;  // valid rows from rl on
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     unsigned off[8];
                     float wv[8];
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
-                        const int r = 8 * h + q;
-                        const int64_t row = rl + 8 * (r >> 2) + (r & 3);
-                        off[q] = (row < m && col < nb) ? (unsigned)(row * n + col) : kOff;
+                        const int r = 8 * h + q, ro = 8 * (r >> 2) + (r & 3);
+                        off[q] = ro < vr ? base + (unsigned)ro * (unsigned)n : kOff;
                         wv[q] = WBF16 ? bf16_to_f32(bload1h(rW, boff(off[q], 2))) : bload1(rW, boff(off[q], 4));
                     }
 #pragma unroll
@@ -547,9 +586,7 @@ hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {
             case 11: e = launch_wide_cfg<11>(a, c0, cnt, ldp, s); break;
             case 12: e = launch_wide_cfg<12>(a, c0, cnt, ldp, s); break;
             case 13: e = launch_wide_cfg<13>(a, c0, cnt, ldp, s); break;
-            case 14: e = launch_wide_cfg<14>(a, c0, cnt, ldp, s); break;
-            case 15: e = launch_wide_cfg<15>(a, c0, cnt, ldp, s); break;
-            default: e = launch_wide_cfg<16>(a, c0, cnt, ldp, s); break;
+            default: return hipErrorInvalidValue;   // nb > 416 does not fit the LDS (see step_wide_eligible)
         }
         if (e != hipSuccess) return e;
         c0 += cnt;
