@@ -138,9 +138,9 @@ KERNEL_SYMBOLS = {
     "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),
     "qr_form": (r"k_qr_apply<\d+, false,", "k_qr.hip"),
     "qr_identity": (r"k_qr_identity", "k_qr.hip"),
-    "split_q": (r"k_split_q", "k_step_bf16.hip"),
-    "project_bf16x6": (r"k_proj_(bf16|rows)<", ("k_step_bf16.hip", "k_step_rows.hip")),
-    "reconstruct_f16x2": (r"k_recon_(bf16|rows)<", ("k_step_bf16.hip", "k_step_rows.hip")),
+    "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
+    "project_bf16x6": (r"k_proj_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
+    "reconstruct_f16x2": (r"k_recon_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
 }
 
 

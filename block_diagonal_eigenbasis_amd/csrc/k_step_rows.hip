@@ -18,49 +18,17 @@
 //   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
 //                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
 // The next tile's rows are loaded while the current tile's products run.
-#include "dobb_internal.h"
+#include "step_common.h"
 
 #include <type_traits>
 
 namespace dobb {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+using namespace stepk;
 
 constexpr int kRT = 512;    // threads per workgroup (8 waves)
 constexpr int kKS = 16;     // k per MFMA step
 constexpr int kPadK = 8;    // Q plane row padding (2-byte elements)
-
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-__device__ __forceinline__ void split3(float v, uint16_t &h, uint16_t &m, uint16_t &l) {
-    h = bf16_bits(v);
-    const float r1 = v - bf16_to_f32(h);
-    m = bf16_bits(r1);
-    l = bf16_bits(r1 - bf16_to_f32(m));
-}
-__device__ __forceinline__ void split2h(float v, uint16_t &h, uint16_t &l) {
-    const _Float16 a = (_Float16)v;
-    h = __builtin_bit_cast(uint16_t, a);
-    l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)a));
-}
-// high byte of the fp16 value of sign(c), from the bits of c without branches
-__device__ __forceinline__ uint32_t sign_byte(float c) {
-    const uint32_t u = __float_as_uint(c);
-    const uint32_t mag = u & 0x7fffffffu;
-    const uint32_t sb = 0x3cu | ((u >> 24) & 0x80u);
-    const uint32_t nz = mag > 0x7f800000u ? 0x7eu : sb;
-    return mag == 0u ? 0u : nz;
-}
-template <int J>
-__device__ __forceinline__ uint32_t signs_f16x2(uint32_t x) {
-    return __builtin_amdgcn_perm(0u, x, J == 0 ? 0x010c000cu : 0x030c020cu);
-}
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
-__device__ __forceinline__ int xcd_remap(int x, int G) {
-    if (G % 8) return x;
-    return (x % 8) * (G / 8) + x / 8;
-}
 
 // LDS geometry shared by host and device
 struct RowsGeo {
