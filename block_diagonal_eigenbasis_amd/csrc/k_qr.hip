@@ -11,9 +11,10 @@
 // negating the columns whose R_cc < 0.
 //
 // Panel factorisation (factor_panel): the panel lives in registers, thread (k, g) holding column k
-// at rows g, g + 8, ...; each column costs two workgroup barriers.  Norms, the cross-thread sums
-// and T are kept in fp64, the per-element work is fp32.  The dot products v_c^T x_k of a column
-// step also give v_k^T v_c for the earlier columns k, from which T is built one column behind.
+// at rows g RPT .. g RPT + RPT - 1; each column costs two workgroup barriers.  Norms, the
+// cross-thread sums and T are kept in fp64, the per-element work is fp32.  The dot products
+// v_c^T x_k of a column step also give v_k^T v_c for the earlier columns k, from which T is built
+// one column behind.
 //
 // nb <= 128 (k_qr_block): one workgroup per block with Z in LDS does every panel, trailing update
 // and formation step in one launch.
@@ -32,6 +33,7 @@ namespace {
 constexpr int kPW = 32;             // panel width
 constexpr int kQT = 256;            // threads per workgroup
 constexpr int kGroups = kQT / kPW;  // row groups of a panel
+constexpr int kVRows = 512;         // rows of a published column buffer (kGroups x the largest RPT)
 
 struct QrBlockOut {
     float *Q[kMaxMats];
@@ -48,7 +50,7 @@ __host__ __device__ inline PanelLds panel_lds(int nb, size_t o) {
     PanelLds L;
     L.gs = o;   o += a16((size_t)kPW * kPW * 8);      // v_k^T v_c (k < c)
     L.td = o;   o += a16((size_t)kPW * kPW * 8);      // T, fp64
-    L.vcol = o; o += a16((size_t)2 * nb * 4);         // column c, double buffered by c parity
+    L.vcol = o; o += a16((size_t)2 * kVRows * 4);     // column c, double buffered by c parity
     L.red = o;  o += a16((size_t)2 * kGroups * 8);
     L.part = o; o += a16((size_t)kGroups * kPW * 8);
     L.tau = o;  o += a16((size_t)kPW * 8);
@@ -69,28 +71,34 @@ __device__ inline PanelPtrs panel_ptrs(unsigned char *dsm, const PanelLds &L) {
                      (double *)(dsm + L.red), (double(*)[kPW])(dsm + L.part), (double *)(dsm + L.tau)};
 }
 
-// Factor the panel held in P (thread (k, grp): column k, rows grp + 8 i of the rows x w panel).
-// On return P holds column k of V (1 at row k, 0 above), negf[c] = 1 where R_cc < 0, and S.Td
-// (fp64, upper triangle of the leading w x w) holds T once the caller has passed a barrier.
+// Factor the panel held in P (thread (k, grp): column k, rows grp RPT + i of the rows x w panel,
+// zero at rows >= rows).  On return P holds column k of V (1 at row k, 0 above), negf[c] = 1 where
+// R_cc < 0, and S.Td (fp64, upper triangle of the leading w x w) holds T once the caller has passed
+// a barrier.  Every LDS access is unconditional (the column buffers have kVRows rows, zero past
+// `rows`) and row masks are selects, so a column step issues its reads back to back.
 template <int RPT>
 __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, int k, int grp, const PanelPtrs &S,
                                              int8_t *negf) {
-    // column c's owners publish its entries at rows >= c and their partial sum of squares; for
-    // c >= 1 this happens right after they applied reflector c-1 to it
+    static_assert(RPT % 4 == 0 && kGroups * RPT <= kVRows, "panel rows");
+    const int rbase = grp * RPT;
+    // column c's owners publish all their rows (entries above row c are never used) and their partial
+    // sum of squares over rows >= c; for c >= 1 this happens right after they applied reflector c-1
     auto publish = [&](int c) {
-        float *vc = S.vcol + (c & 1) * rows;
-        double ss = 0.0;
+        float *vc = S.vcol + (c & 1) * kVRows + rbase;
+        double ss[4] = {0.0, 0.0, 0.0, 0.0};   // four independent chains
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = grp + kGroups * i;
-            if (r >= c && r < rows) { ss += (double)P[i] * (double)P[i]; vc[r] = P[i]; }
+            const double d = rbase + i >= c ? (double)P[i] : 0.0;
+            ss[i & 3] = __builtin_fma(d, d, ss[i & 3]);
         }
-        S.red[(c & 1) * kGroups + grp] = ss;
+#pragma unroll
+        for (int i = 0; i < RPT; i += 4) *(f32x4 *)(vc + i) = f32x4{P[i], P[i + 1], P[i + 2], P[i + 3]};
+        S.red[(c & 1) * kGroups + grp] = (ss[0] + ss[1]) + (ss[2] + ss[3]);
     };
     if (k == 0) publish(0);
     for (int c = 0; c < w; ++c) {
         const int buf = c & 1;
-        const float *vc = S.vcol + buf * rows;
+        const float *vc = S.vcol + buf * kVRows;
         __syncthreads();
         double a2 = 0.0;
 #pragma unroll
@@ -106,18 +114,22 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
             for (int l = k; l < c - 1; ++l) sum += S.Td[k][l] * S.Gs[l][c - 1];
             S.Td[k][c - 1] = -S.tau[c - 1] * sum;
         }
-        // v on this thread's rows and the partial dot product with this thread's column
+        // v on this thread's rows (0 above row c, 1 at row c; the buffer is 0 past `rows`) and the
+        // partial dot product with this thread's column
         float vt[RPT];
-        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = grp + kGroups * i;
-            const float v = (r >= c && r < rows) ? (r == c ? 1.f : vc[r] * inv) : 0.f;
-            vt[i] = v;
-            if (i & 1) s1 = __builtin_fmaf(v, P[i], s1);
-            else s0 = __builtin_fmaf(v, P[i], s0);
+        for (int i = 0; i < RPT; i += 4) {
+            const f32x4 x = *(const f32x4 *)(vc + rbase + i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = rbase + i + q;
+                vt[i + q] = r < c ? 0.f : (r == c ? 1.f : x[q] * inv);
+            }
         }
-        S.part[grp][k] = (k != c && k < w) ? (double)s0 + (double)s1 : 0.0;
+        float sd[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) sd[i & 3] = __builtin_fmaf(vt[i], P[i], sd[i & 3]);
+        S.part[grp][k] = (k != c && k < w) ? ((double)sd[0] + (double)sd[1]) + ((double)sd[2] + (double)sd[3]) : 0.0;
         __syncthreads();
         double tot = 0.0;
 #pragma unroll
@@ -136,7 +148,7 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
                 negf[c] = (alpha != 0.0 && sg > 0.0) ? 1 : 0;   // R_cc = -sg alpha < 0
             }
         } else if (k < c && grp == 0) {
-            S.Gs[k][c] = tot;
+            S.Gs[k][c] = tot;   // v_k^T v_c
         }
     }
     __syncthreads();
@@ -265,13 +277,13 @@ __global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float 
         float P[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = grp + kGroups * i;
+            const int r = grp * RPT + i;
             P[i] = (k < w && r < rows) ? Z[(int64_t)(j0 + r) * ldz + j0 + k] : 0.f;
         }
         factor_panel<RPT>(P, w, rows, k, grp, S, neg + j0);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = grp + kGroups * i;
+            const int r = grp * RPT + i;
             if (r < rows) {
                 Vs[r][k] = k < w ? P[i] : 0.f;
                 if (k < w) Z[(int64_t)(j0 + r) * ldz + j0 + k] = P[i];
@@ -329,14 +341,14 @@ __global__ void __launch_bounds__(256) k_qr_panel(int nb, int p, float *Z_all, f
     float P[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int r = grp + kGroups * i;
+        const int r = grp * RPT + i;
         P[i] = (k < w && r < rows) ? Z[(int64_t)(j0 + r) * nb + j0 + k] : 0.f;
     }
     factor_panel<RPT>(P, w, rows, k, grp, S, neg_all + (int64_t)g * nb + j0);
     if (k < w) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = grp + kGroups * i;
+            const int r = grp * RPT + i;
             if (r < rows) Z[(int64_t)(j0 + r) * nb + j0 + k] = P[i];
         }
     }
