@@ -65,7 +65,8 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
       accumulate_reduce     A read + written: 8 nb^2 B bytes
       refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
       qr_block              nb <= 128, the whole Householder QR in one launch: 8/3 nb^3 B flops
-      qr_update / qr_form   nb > 128, factor / formation updates: 4/3 nb^3 B flops each (fp32)
+      qr_update / qr_form   nb > 128, factor updates (a launch per panel) / formation (one launch for
+                            all panels): 4/3 nb^3 B flops each (fp32)
       qr_panel              nb > 128, panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
       split_q               nb > 128 only, Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
       project_bf16x6        M read + written, G read, sign bytes written: (9 + g) m n bytes;
@@ -136,8 +137,7 @@ KERNEL_SYMBOLS = {
     "qr_block": (r"k_qr_block<", "k_qr.hip"),
     "qr_panel": (r"k_qr_panel<", "k_qr.hip"),
     "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),
-    "qr_form": (r"k_qr_apply<\d+, false,", "k_qr.hip"),
-    "qr_identity": (r"k_qr_identity", "k_qr.hip"),
+    "qr_form": (r"k_qr_form<", "k_qr.hip"),
     "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
     "project_bf16x6": (r"k_proj_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
     "reconstruct_f16x2": (r"k_recon_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),

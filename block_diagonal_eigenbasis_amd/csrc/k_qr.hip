@@ -19,10 +19,10 @@
 // nb <= 128 (k_qr_block): one workgroup per block with Z in LDS does every panel, trailing update
 // and formation step in one launch.
 // nb > 128: per panel one k_qr_panel launch (one workgroup per block) and one k_qr_apply launch
-// (one workgroup per 64-column tile per block); formation is one k_qr_apply launch per panel.  A
-// k_qr_apply wave keeps its 32 x (rows/2) share of the tile in registers from load to store, in the
-// MFMA accumulator layout (rows are fed to the V^T X products in that order), so the tile is read
-// and written once; V is staged in LDS.
+// (one workgroup per 64-column tile per block); formation is a single k_qr_form launch that carries
+// each 64-column tile of Q through all panels.  A wave keeps its 32 x (rows/2) share of a tile in
+// registers from load to store, in the MFMA accumulator layout (rows are fed to the V^T X products
+// in that order), so the tile is read and written once; V is staged in LDS.
 #include "dobb_internal.h"
 
 #include <math.h>
@@ -533,12 +533,124 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
     if (FLIP && blockIdx.x == 0 && tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
 }
 
-// Q := I before the formation sweep.  grid = blocks.
-__global__ void __launch_bounds__(256) k_qr_identity(int nb, int nblk, QrBlockOut t) {
-    const int g = blockIdx.x;
-    float *Q = t.Q[g / nblk] + (int64_t)(g % nblk) * nb * nb;
-    for (int64_t e = threadIdx.x; e < (int64_t)nb * nb; e += 256) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+// ---- nb > 128: formation of Q in one launch ---------------------------------------------------------
+// A workgroup owns a 64-column tile of Q_b over all nb rows and keeps it in registers (accumulator
+// layout, as in k_qr_apply) from the identity to the final store.  It applies the block reflectors
+// I - V_p T_p V_p^T for p = min(npanel - 1, last column / 32) down to 0 (panels starting past the
+// tile's last column leave its identity columns unchanged), each with V_p and T_p staged in LDS, and
+// stores the tile once with the columns whose R_cc < 0 negated.  Wave (kp, h): column half h, rows
+// [0, half) or [half, nb); 32-row chunks lying wholly above a panel's first row are skipped (V = 0).
+// grid = (ceil(nb / 64) tiles, blocks), block 256.
+template <int CH>
+__global__ void __launch_bounds__(256) k_qr_form(int nb, int nblk, const float *Z_all, const float *Tq_all,
+                                                 const int8_t *neg_all, QrBlockOut t, int info_value) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    const ApplyLds L = apply_lds(nb);
+    float(*Vs)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.vs);
+    float(*Ts)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.ts);
+    float(*Wp)[2][32][33] = (float(*)[2][32][33])(dsm + L.wp);
+    const int g = blockIdx.y;
+    const int b = g % nblk, mat = g / nblk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int h = wv & 1, kp = wv >> 1;
+    const int kr = lane >> 5, cc = lane & 31;
+    const int npanel = (nb + kPW - 1) / kPW;
+    const float *Z = Z_all + (int64_t)g * nb * nb;
+    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+    const int c0 = blockIdx.x * 64 + 32 * h;
+    const bool colok = c0 + cc < nb;
+    const int ccl = colok ? c0 + cc : 0;
+    const int half = ((nb + 63) / 64) * 32;
+    const int rb = kp ? half : 0, re = kp ? nb : (half < nb ? half : nb);
+    const unsigned lo = (unsigned)((rb + 4 * kr) * nb + ccl);
+    const unsigned unb = (unsigned)nb;
+    // the identity columns of the tile
+    f32x16 x[CH];
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rb + 32 * ch + acc_row(r, lane);
+            x[ch][r] = (colok && row < re && row == ccl) ? 1.f : 0.f;
+        }
+    const int plast = (blockIdx.x * 64 + 63) / kPW < npanel - 1 ? (blockIdx.x * 64 + 63) / kPW : npanel - 1;
+    for (int p = plast; p >= 0; --p) {
+        const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+        __syncthreads();   // the last panel's readers of Vs, Ts and Wp are done
+        stage_v<CH>(Vs, Z, nb, j0, w, rows, tid);
+        {
+            const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
+            float tv[kPW * kPW / kQT];
+#pragma unroll
+            for (int i = 0; i < kPW * kPW / kQT; ++i) tv[i] = Tq[tid + kQT * i];
+#pragma unroll
+            for (int i = 0; i < kPW * kPW / kQT; ++i) Ts[(tid + kQT * i) / kPW][(tid + kQT * i) % kPW] = tv[i];
+        }
+        __syncthreads();
+        // W partial = V^T X over this wave's chunks at rows >= j0 (chunks are 32-aligned, as is j0)
+        f32x16 acc = {};
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 < j0) continue;
+#pragma unroll
+            for (int s2 = 0; s2 < 16; ++s2) {
+                const float a = Vs[r0 - j0 + 8 * (s2 >> 2) + 4 * kr + (s2 & 3)][cc];
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x[ch][s2], acc, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = acc[r];
+        __syncthreads();
+        // Y = T (W_0 + W_1)
+        f32x16 y = {};
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2) {
+            const int kx = kk + kr;
+            y = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[cc][kx], Wp[0][h][kx][cc] + Wp[1][h][kx][cc], y, 0, 0, 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = y[r];
+        wave_sync_lds();
+        float yb[kPW / 2];
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2) yb[kk / 2] = Wp[kp][h][kk + kr][cc];
+        // X -= V Y on this wave's chunks at rows >= j0
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 < j0) continue;
+            f32x16 u = {};
+#pragma unroll
+            for (int kk = 0; kk < kPW; kk += 2)
+                u = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[r0 - j0 + cc][kk + kr], yb[kk / 2], u, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[ch][r] -= u[r];
+        }
+    }
+    // store, negating the columns whose R_cc < 0
+    if (colok) {
+        const float sgn = neg_all[(int64_t)g * nb + ccl] ? -1.f : 1.f;
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 + 32 <= re) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Q[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (r0 + acc_row(r, lane) < re) Q[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
+            }
+        }
+    }
+    if (blockIdx.x == 0 && tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
 }
+
 
 template <int RPT>
 hipError_t launch_block(int nb, int nblk, int nblocks, const float *Z, float *tq, const QrBlockOut &o, int infov,
@@ -559,8 +671,6 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
     (void)hipFuncSetAttribute((const void *)k_qr_panel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
     (void)hipFuncSetAttribute((const void *)k_qr_panel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
     (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
-    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
-    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
     const int npanel = (nb + kPW - 1) / kPW;
     for (int p = 0; p < npanel; ++p) {
         const int rows = nb - p * kPW;   // rows per thread: ceil(rows / 8), rounded up to a template size
@@ -578,16 +688,9 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
             DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
                         as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
     }
-    DOBB_LAUNCH("qr_identity", s, k_qr_identity, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, o);
-    for (int p = npanel - 1; p >= 0; --p) {
-        const int ntiles = (nb - p * kPW + 63) / 64;
-        if (p > 0)
-            DOBB_LAUNCH("qr_form", s, (k_qr_apply<CH, false, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
-                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
-        else
-            DOBB_LAUNCH("qr_form", s, (k_qr_apply<CH, false, true>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
-                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, infov);
-    }
+    (void)hipFuncSetAttribute((const void *)k_qr_form<CH>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
+    DOBB_LAUNCH("qr_form", s, (k_qr_form<CH>), dim3((unsigned)((nb + 63) / 64), (unsigned)nblocks), dim3(kQT), as, nb,
+                nblk, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, infov);
     return hipGetLastError();
 }
 
