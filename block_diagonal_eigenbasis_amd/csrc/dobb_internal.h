@@ -44,6 +44,12 @@ struct GemmSmem {
 };
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+// Workgroup ids renumbered so that each XCD (ids are dealt round-robin over the 8 XCDs) runs a
+// contiguous range of logical ids: neighbours in logical order then share one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int x, int G) {
+    if (G % 8) return x;
+    return (x % 8) * (G / 8) + x / 8;
+}
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
 template <typename LoadA, typename LoadB>

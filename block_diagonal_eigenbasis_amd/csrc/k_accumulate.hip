@@ -152,10 +152,6 @@ constexpr int kST = 128, kSK = 128;
 __device__ __forceinline__ int swz(int j) { return (j ^ (j >> 3)) & 15; }
 constexpr int kSFold = 2;  // fold fp32 sums into fp64 every 2 chunks (256 tokens)
 
-__device__ __forceinline__ int xcd_remap(int x, int G) {
-    if (G % 8) return x;
-    return (x % 8) * (G / 8) + x / 8;
-}
 
 // 8 consecutive bf16 of one row (valid > 0 of them in range).  VEC = 8: nb % 8 == 0 and 16-byte
 // alignment, so valid >= 8; VEC = 4: nb % 4 == 0 and 8-byte alignment, so valid is a multiple of 4.

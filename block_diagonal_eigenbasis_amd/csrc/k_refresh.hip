@@ -12,8 +12,9 @@
 //           accumulator by k_jacobi_rotate_v, spread over many workgroups (rows of V are
 //           independent).  k_jacobi_finalize sorts by descending eigenvalue, makes the largest entry
 //           of every eigenvector positive and writes fp32 Q, lambda and info.
-// ORTH_ITER k times: Z = A_b Q_b (MFMA), Q_b <- qr(Z).Q by Householder (k_householder, Z in LDS
-//           when it fits), diag(R) > 0.  Rayleigh quotients go to lambda when requested.
+// ORTH_ITER k times: Z = A_b Q_b (MFMA), Q_b <- qr(Z).Q by Householder (k_qr.hip: one launch with
+//           Z in LDS for nb <= 128, panel / update / formation launches above), diag(R) > 0.
+//           Rayleigh quotients go to lambda when requested.
 #include "dobb_internal.h"
 
 #include <math.h>
@@ -37,8 +38,9 @@ struct OutOpnd {
 template <bool TRANS_A>
 __global__ void __launch_bounds__(256) k_bgemm(int nb, int T, int nblk, Opnd A, Opnd B, OutOpnd C) {
     __shared__ GemmSmem sm;
-    const int tile = blockIdx.x % (T * T);
-    const int rest = blockIdx.x / (T * T);
+    const int x = xcd_remap(blockIdx.x, gridDim.x);   // the tiles of a block share one XCD's L2
+    const int tile = x % (T * T);
+    const int rest = x / (T * T);
     const int b = rest % nblk, mat = rest / nblk;
     const int i0 = (tile / T) * kBM, j0 = (tile % T) * kBN;
     const float *Ab = A.p[mat] + (int64_t)b * A.blk_stride;

@@ -40,11 +40,6 @@ __device__ __forceinline__ void split3(float v, uint16_t &h, uint16_t &m, uint16
     l = bf16_bits(r2);
 }
 
-__device__ __forceinline__ int xcd_remap(int x, int G) {
-    if (G % 8) return x;
-    return (x % 8) * (G / 8) + x / 8;
-}
-
 struct SplitTable {
     const float *Q[kMaxMats];
     uint16_t *planes[kMaxMats];  // 5 planes of B x nb x ldp: natural fp16 hi, lo; transposed bf16 h, m, l

@@ -56,11 +56,6 @@ __device__ __forceinline__ void split3x8(f32x4 p0, f32x4 p1, bf16x8 &ah, bf16x8 
     am = __builtin_bit_cast(bf16x8, uint4{pack2(hm[0], hm[1]), pack2(hm[2], hm[3]), pack2(hm[4], hm[5]), pack2(hm[6], hm[7])});
     al = __builtin_bit_cast(bf16x8, uint4{pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])});
 }
-// workgroup ids renumbered so that each XCD (ids dealt round-robin over 8) runs a contiguous range
-__device__ __forceinline__ int xcd_remap(int x, int G) {
-    if (G % 8) return x;
-    return (x % 8) * (G / 8) + x / 8;
-}
 
 // Buffer-descriptor access: a lane with nothing to do passes kOff, past the end of the buffer, so
 // its load returns zeros and its store is dropped, without a branch around the instruction.
