@@ -10,9 +10,10 @@
 // the panels last to first on rows and columns >= the panel start, the last application also
 // negating the columns whose R_cc < 0.
 //
-// Panel factorisation (factor_panel): the panel lives in registers, thread (k, g) holding column k
-// at rows g RPT .. g RPT + RPT - 1; each column costs two workgroup barriers.  Norms, the
-// cross-thread sums and T are kept in fp64, the per-element work is fp32.  The dot products
+// Panel factorisation (factor_panel): the panel lives in registers, thread 8 k + g holding column k
+// at rows g RPT .. g RPT + RPT - 1, so a column's threads share a wave; each column costs one
+// workgroup barrier.  Norms, the cross-thread sums and T are kept in fp64, the per-element work is
+// fp32.  The dot products
 // v_c^T x_k of a column step also give v_k^T v_c for the earlier columns k, from which T is built
 // one column behind.
 //
@@ -71,77 +72,82 @@ __device__ inline PanelPtrs panel_ptrs(unsigned char *dsm, const PanelLds &L) {
                      (double *)(dsm + L.red), (double(*)[kPW])(dsm + L.part), (double *)(dsm + L.tau)};
 }
 
-// Factor the panel held in P (thread (k, grp): column k, rows grp RPT + i of the rows x w panel,
-// zero at rows >= rows).  On return P holds column k of V (1 at row k, 0 above), negf[c] = 1 where
+// sum over the 8 lanes of a column (lanes 8 k .. 8 k + 7 of a wave)
+__device__ __forceinline__ double col_sum(double v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    return v;
+}
+
+// Factor the panel held in P (thread tid = 8 k + grp: column k, rows grp RPT + i of the rows x w
+// panel, zero at rows >= rows).  On return P holds column k of V (0 above row k), negf[c] = 1 where
 // R_cc < 0, and S.Td (fp64, upper triangle of the leading w x w) holds T once the caller has passed
-// a barrier.  Every LDS access is unconditional (the column buffers have kVRows rows, zero past
-// `rows`) and row masks are selects, so a column step issues its reads back to back.
+// a barrier.
+// A column's 8 threads share a wave, so its cross-thread sums are shuffles and a column step has
+// one workgroup barrier.  Column c is published by its own wave with its rows above c zeroed and
+// row c replaced by x_c + sgn(x_c) ||x||, so that v = x / (x_c + sgn(x_c) ||x||) is one scaling of
+// the published column on every row (v_c = 1 up to one fp32 rounding, and that same v is stored
+// and used everywhere); ||x|| and x_c go along in fp64 for tau = 1 + |x_c| / ||x|| and the sign.
 template <int RPT>
 __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, int k, int grp, const PanelPtrs &S,
                                              int8_t *negf) {
     static_assert(RPT % 4 == 0 && kGroups * RPT <= kVRows, "panel rows");
     const int rbase = grp * RPT;
-    // column c's owners publish all their rows (entries above row c are never used) and their partial
-    // sum of squares over rows >= c; for c >= 1 this happens right after they applied reflector c-1
     auto publish = [&](int c) {
-        float *vc = S.vcol + (c & 1) * kVRows + rbase;
-        double ss[4] = {0.0, 0.0, 0.0, 0.0};   // four independent chains
+        float *vc = S.vcol + (c & 1) * kVRows;
+        double ss[4] = {0.0, 0.0, 0.0, 0.0};   // exact squares, four chains
+        float x[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const double d = rbase + i >= c ? (double)P[i] : 0.0;
-            ss[i & 3] = __builtin_fma(d, d, ss[i & 3]);
+            x[i] = rbase + i >= c ? P[i] : 0.f;
+            ss[i & 3] = __builtin_fma((double)x[i], (double)x[i], ss[i & 3]);
         }
 #pragma unroll
-        for (int i = 0; i < RPT; i += 4) *(f32x4 *)(vc + i) = f32x4{P[i], P[i + 1], P[i + 2], P[i + 3]};
-        S.red[(c & 1) * kGroups + grp] = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+        for (int i = 0; i < RPT; i += 4) *(f32x4 *)(vc + rbase + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+        const double alpha = sqrt(col_sum((ss[0] + ss[1]) + (ss[2] + ss[3])));
+        if (grp == 0) {   // row c was stored by this wave: LDS operations of a wave are in order
+            const double x0 = (double)vc[c];
+            S.red[(c & 1) * 2] = alpha;
+            S.red[(c & 1) * 2 + 1] = x0;
+            vc[c] = (float)(x0 + (x0 >= 0.0 ? alpha : -alpha));
+        }
     };
     if (k == 0) publish(0);
     for (int c = 0; c < w; ++c) {
         const int buf = c & 1;
         const float *vc = S.vcol + buf * kVRows;
-        __syncthreads();
-        double a2 = 0.0;
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q) a2 += S.red[buf * kGroups + q];
-        const double alpha = sqrt(a2);
-        const double x0 = (double)vc[c];
+        __syncthreads();   // column c published; Gs, tau and T of earlier columns visible
+        const double alpha = S.red[buf * 2], x0 = S.red[buf * 2 + 1];
         const double sg = x0 >= 0.0 ? 1.0 : -1.0;
         const double tc = alpha == 0.0 ? 0.0 : 1.0 + fabs(x0) / alpha;
         const float inv = alpha == 0.0 ? 1.f : (float)(1.0 / (x0 + sg * alpha));
         // column c-1 of T: its Gram entries and tau became visible at the barrier above
-        if (c >= 1 && grp == ((c - 1) & (kGroups - 1)) && k < c - 1) {
+        if (c >= 1 && grp == 0 && k < c - 1) {
             double sum = 0.0;
             for (int l = k; l < c - 1; ++l) sum += S.Td[k][l] * S.Gs[l][c - 1];
             S.Td[k][c - 1] = -S.tau[c - 1] * sum;
         }
-        // v on this thread's rows (0 above row c, 1 at row c; the buffer is 0 past `rows`) and the
-        // partial dot product with this thread's column
-        float vt[RPT];
+        // v^T P_k = inv (x^T P_k) on this thread's rows, summed over the column's 8 threads
+        float x[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; i += 4) {
-            const f32x4 x = *(const f32x4 *)(vc + rbase + i);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = rbase + i + q;
-                vt[i + q] = r < c ? 0.f : (r == c ? 1.f : x[q] * inv);
-            }
+            const f32x4 q = *(const f32x4 *)(vc + rbase + i);
+            x[i] = q[0]; x[i + 1] = q[1]; x[i + 2] = q[2]; x[i + 3] = q[3];
         }
-        float sd[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains
+        float sd[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) sd[i & 3] = __builtin_fmaf(vt[i], P[i], sd[i & 3]);
-        S.part[grp][k] = (k != c && k < w) ? ((double)sd[0] + (double)sd[1]) + ((double)sd[2] + (double)sd[3]) : 0.0;
-        __syncthreads();
-        double tot = 0.0;
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q) tot += S.part[q][k];
+        for (int i = 0; i < RPT; ++i) sd[i & 3] = __builtin_fmaf(x[i], P[i], sd[i & 3]);
+        const double tot =
+            col_sum((double)inv * (((double)sd[0] + (double)sd[1]) + ((double)sd[2] + (double)sd[3])));
         if (k > c && k < w) {
-            const float wk = (float)(tc * tot);
+            const float a = (float)(tc * tot) * inv;   // P_k -= tc (v^T P_k) v
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) P[i] = __builtin_fmaf(-vt[i], wk, P[i]);   // vt = 0 above row c
+            for (int i = 0; i < RPT; ++i) P[i] = __builtin_fmaf(-a, x[i], P[i]);
             if (k == c + 1) publish(c + 1);
         } else if (k == c) {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) P[i] = vt[i];
+            for (int i = 0; i < RPT; ++i) P[i] = inv * x[i];   // v: 0 above row c
             if (grp == 0) {
                 S.tau[c] = tc;
                 S.Td[c][c] = tc;
@@ -152,7 +158,7 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
         }
     }
     __syncthreads();
-    if (w >= 2 && grp == ((w - 1) & (kGroups - 1)) && k < w - 1) {
+    if (w >= 2 && grp == 0 && k < w - 1) {
         double sum = 0.0;
         for (int l = k; l < w - 1; ++l) sum += S.Td[k][l] * S.Gs[l][w - 1];
         S.Td[k][w - 1] = -S.tau[w - 1] * sum;
@@ -265,7 +271,7 @@ __global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float 
     const int g = blockIdx.x;
     const int b = g % nblk, mat = g / nblk;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int k = tid & (kPW - 1), grp = tid / kPW;
+    const int k = tid >> 3, grp = tid & (kGroups - 1);   // tid = 8 k + grp
     const int npanel = (nb + kPW - 1) / kPW;
     const float *Zg = Z_all + (int64_t)g * nb * nb;
     float *Tq = Tq_all + (int64_t)g * npanel * kPW * kPW;
@@ -333,7 +339,7 @@ __global__ void __launch_bounds__(256) k_qr_panel(int nb, int p, float *Z_all, f
     const PanelPtrs S = panel_ptrs(dsm, L);
     const int g = blockIdx.x;
     const int tid = threadIdx.x;
-    const int k = tid & (kPW - 1), grp = tid / kPW;
+    const int k = tid >> 3, grp = tid & (kGroups - 1);   // tid = 8 k + grp
     const int npanel = (nb + kPW - 1) / kPW;
     const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
     float *Z = Z_all + (int64_t)g * nb * nb;
