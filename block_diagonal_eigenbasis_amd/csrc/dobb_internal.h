@@ -52,22 +52,43 @@ __device__ __forceinline__ int xcd_remap(int x, int G) {
 }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
+// Two LDS buffers for gemm_tile: the next K-chunk is fetched into registers before the products of
+// the current one and stored to the other buffer after them, so each chunk costs one barrier.
+struct GemmSmem2 {
+    float a[2][kBK][kBM + kPad];
+    float b[2][kBK][kBN + kPad];
+};
+
 template <typename LoadA, typename LoadB>
-__device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB &lb, GemmSmem &sm) {
+__device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB &lb, GemmSmem2 &sm) {
     f32x16 acc = {};
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wr = 32 * (w >> 1), wc = 32 * (w & 1);
+    float va[4], vb[4];
+    la.fetch(0, va);
+    lb.fetch(0, vb);
+    la.put(va, sm.a[0]);
+    lb.put(vb, sm.b[0]);
+    __syncthreads();
+    int cur = 0;
     for (int k0 = 0; k0 < K; k0 += kBK) {
-        la(k0, sm.a);
-        lb(k0, sm.b);
-        __syncthreads();
+        const bool more = k0 + kBK < K;
+        if (more) {
+            la.fetch(k0 + kBK, va);
+            lb.fetch(k0 + kBK, vb);
+        }
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 2) {
-            float a = sm.a[kk + (lane >> 5)][wr + (lane & 31)];
-            float b = sm.b[kk + (lane >> 5)][wc + (lane & 31)];
+            float a = sm.a[cur][kk + (lane >> 5)][wr + (lane & 31)];
+            float b = sm.b[cur][kk + (lane >> 5)][wc + (lane & 31)];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
+        if (more) {   // the other buffer's readers finished before the last barrier
+            la.put(va, sm.a[cur ^ 1]);
+            lb.put(vb, sm.b[cur ^ 1]);
+        }
         __syncthreads();
+        cur ^= 1;
     }
     return acc;
 }
@@ -77,9 +98,9 @@ __device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB 
 template <bool VEC>
 struct LoadRowsT {
     const float *src; int64_t ld; int rows; int K;
-    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        v[0] = v[1] = v[2] = v[3] = 0.f;
         if (i < rows) {
             const float *p = src + (int64_t)i * ld + k;
             if (VEC) {
@@ -89,6 +110,9 @@ struct LoadRowsT {
                 for (int c = 0; c < 4; ++c) if (k + c < K) v[c] = p[c];
             }
         }
+    }
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+        const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
         for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
     }
@@ -99,9 +123,9 @@ struct LoadRowsT {
 template <bool VEC>
 struct LoadColsK {
     const float *src; int64_t ld; int cols; int K;
-    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBN + kPad]) const {
+    __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, kk = t >> 4, j = 4 * (t & 15), k = k0 + kk;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        v[0] = v[1] = v[2] = v[3] = 0.f;
         if (k < K) {
             const float *p = src + (int64_t)k * ld + j;
             if (VEC) {
@@ -111,6 +135,9 @@ struct LoadColsK {
                 for (int c = 0; c < 4; ++c) if (j + c < cols) v[c] = p[c];
             }
         }
+    }
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBN + kPad]) const {
+        const int t = threadIdx.x, kk = t >> 4, j = 4 * (t & 15);
 #pragma unroll
         for (int c = 0; c < 4; ++c) dst[kk][j + c] = v[c];
     }

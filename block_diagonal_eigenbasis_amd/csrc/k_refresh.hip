@@ -37,7 +37,7 @@ struct OutOpnd {
 // grid.x = tiles * tiles * nblk * count
 template <bool TRANS_A>
 __global__ void __launch_bounds__(256) k_bgemm(int nb, int T, int nblk, Opnd A, Opnd B, OutOpnd C) {
-    __shared__ GemmSmem sm;
+    __shared__ GemmSmem2 sm;
     const int x = xcd_remap(blockIdx.x, gridDim.x);   // the tiles of a block share one XCD's L2
     const int tile = x % (T * T);
     const int rest = x / (T * T);

@@ -70,25 +70,29 @@ struct ProjTable {
 template <bool GBF16>
 struct LoadNesterovT {
     const float *M; const void *G; int64_t off; int64_t ld; int rows; int K; float mu;
-    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            float v = 0.f;
+            v[c] = 0.f;
             if (i < rows && k + c < K) {
                 int64_t e = off + (int64_t)i * ld + k + c;
                 float g = GBF16 ? bf16_to_f32(((const uint16_t *)G)[e]) : ((const float *)G)[e];
-                v = __builtin_fmaf(mu, M[e], g);
+                v[c] = __builtin_fmaf(mu, M[e], g);
             }
-            dst[4 * (t & 3) + c][i] = v;
         }
+    }
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+        const int t = threadIdx.x, i = t >> 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
     }
 };
 
 // grid.x = col_tiles * B * count (column tile fastest), grid.y = row tiles of 64
 template <bool VEC, int NEST /*0 none, 1 G fp32, 2 G bf16*/, bool SIGN>
 __global__ void __launch_bounds__(256) k_project(int64_t m, int64_t n, int nb, int col_tiles, int nblk, ProjTable t) {
-    __shared__ GemmSmem sm;
+    __shared__ GemmSmem2 sm;
     const int ct = blockIdx.x % col_tiles;
     const int rest = blockIdx.x / col_tiles;
     const int b = rest % nblk, mat = rest / nblk;
@@ -156,9 +160,9 @@ struct ReconTable {
 template <bool VEC>
 struct LoadSignT {
     const int8_t *src; int64_t ld; int rows; int K;
-    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        v[0] = v[1] = v[2] = v[3] = 0.f;
         if (i < rows) {
             const int8_t *p = src + (int64_t)i * ld + k;
             if (VEC) {
@@ -172,6 +176,9 @@ struct LoadSignT {
                 for (int c = 0; c < 4; ++c) if (k + c < K) v[c] = sign_decode(p[c]);
             }
         }
+    }
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+        const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
         for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
     }
@@ -181,23 +188,27 @@ struct LoadSignT {
 template <bool SCALED>
 struct LoadCoefT {
     const float *src; const float *cs; int64_t ld; int rows; int K;
-    __device__ __forceinline__ void operator()(int k0, float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            float v = 0.f;
+            v[c] = 0.f;
             if (i < rows && k + c < K) {
-                v = src[(int64_t)i * ld + k + c];
-                if (SCALED) v *= cs[k + c];
+                v[c] = src[(int64_t)i * ld + k + c];
+                if (SCALED) v[c] *= cs[k + c];
             }
-            dst[4 * (t & 3) + c][i] = v;
         }
+    }
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+        const int t = threadIdx.x, i = t >> 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
     }
 };
 
 template <bool VEC, int AMODE /*0 sign codes, 1 C, 2 C*colscale*/, bool WBF16>
 __global__ void __launch_bounds__(256) k_reconstruct(int64_t m, int64_t n, int nb, int col_tiles, int nblk, ReconTable t) {
-    __shared__ GemmSmem sm;
+    __shared__ GemmSmem2 sm;
     const int ct = blockIdx.x % col_tiles;
     const int rest = blockIdx.x / col_tiles;
     const int b = rest % nblk, mat = rest / nblk;
