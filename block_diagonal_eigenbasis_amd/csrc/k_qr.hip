@@ -34,7 +34,7 @@ namespace {
 constexpr int kPW = 32;             // panel width
 constexpr int kQT = 256;            // threads per workgroup
 constexpr int kGroups = kQT / kPW;  // row groups of a panel
-constexpr int kVRows = 512;         // rows of a published column buffer (kGroups x the largest RPT)
+constexpr int kVRows = 576;         // floats of a published column buffer (kGroups x (RPT + 4), RPT <= 64)
 
 struct QrBlockOut {
     float *Q[kMaxMats];
@@ -92,8 +92,12 @@ __device__ __forceinline__ double col_sum(double v) {
 template <int RPT>
 __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, int k, int grp, const PanelPtrs &S,
                                              int8_t *negf) {
-    static_assert(RPT % 4 == 0 && kGroups * RPT <= kVRows, "panel rows");
-    const int rbase = grp * RPT;
+    static_assert(RPT % 4 == 0 && kGroups * (RPT + 4) <= kVRows, "panel rows");
+    // a published column keeps group g's rows at [g (RPT + 4), + RPT): the 4-float gap between
+    // groups puts the 8 groups of a wave's reads on distinct banks
+    constexpr int kGS = RPT + 4;
+    const int rbase = grp * RPT, lbase = grp * kGS;
+    auto lds_row = [](int r) { return (r / RPT) * kGS + r % RPT; };
     auto publish = [&](int c) {
         float *vc = S.vcol + (c & 1) * kVRows;
         double ss[4] = {0.0, 0.0, 0.0, 0.0};   // exact squares, four chains
@@ -104,13 +108,13 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
             ss[i & 3] = __builtin_fma((double)x[i], (double)x[i], ss[i & 3]);
         }
 #pragma unroll
-        for (int i = 0; i < RPT; i += 4) *(f32x4 *)(vc + rbase + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+        for (int i = 0; i < RPT; i += 4) *(f32x4 *)(vc + lbase + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
         const double alpha = sqrt(col_sum((ss[0] + ss[1]) + (ss[2] + ss[3])));
         if (grp == 0) {   // row c was stored by this wave: LDS operations of a wave are in order
-            const double x0 = (double)vc[c];
+            const double x0 = (double)vc[lds_row(c)];
             S.red[(c & 1) * 2] = alpha;
             S.red[(c & 1) * 2 + 1] = x0;
-            vc[c] = (float)(x0 + (x0 >= 0.0 ? alpha : -alpha));
+            vc[lds_row(c)] = (float)(x0 + (x0 >= 0.0 ? alpha : -alpha));
         }
     };
     if (k == 0) publish(0);
@@ -132,7 +136,7 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
         float x[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; i += 4) {
-            const f32x4 q = *(const f32x4 *)(vc + rbase + i);
+            const f32x4 q = *(const f32x4 *)(vc + lbase + i);
             x[i] = q[0]; x[i + 1] = q[1]; x[i + 2] = q[2]; x[i + 3] = q[3];
         }
         float sd[4] = {0.f, 0.f, 0.f, 0.f};
