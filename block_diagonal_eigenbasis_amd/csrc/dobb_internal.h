@@ -54,10 +54,14 @@ __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
 // Two LDS buffers for gemm_tile: the next K-chunk is fetched into registers before the products of
 // the current one and stored to the other buffer after them, so each chunk costs one barrier.
+// Column index swizzled by row (gemm_swz): the two rows read by the half-waves of an MFMA operand
+// load fall in opposite bank halves, and the four rows a loader wave writes in one instruction
+// spread over all 64 banks.
 struct GemmSmem2 {
-    float a[2][kBK][kBM + kPad];
-    float b[2][kBK][kBN + kPad];
+    float a[2][kBK][kBM];
+    float b[2][kBK][kBN];
 };
+__device__ __forceinline__ int gemm_swz(int row) { return ((row & 1) << 5) ^ (((row >> 2) & 3) << 4); }
 
 template <typename LoadA, typename LoadB>
 __device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB &lb, GemmSmem2 &sm) {
@@ -79,8 +83,9 @@ __device__ __forceinline__ f32x16 gemm_tile(int K, const LoadA &la, const LoadB 
         }
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 2) {
-            float a = sm.a[cur][kk + (lane >> 5)][wr + (lane & 31)];
-            float b = sm.b[cur][kk + (lane >> 5)][wc + (lane & 31)];
+            const int kr = kk + (lane >> 5);
+            float a = sm.a[cur][kr][(wr + (lane & 31)) ^ gemm_swz(kr)];
+            float b = sm.b[cur][kr][(wc + (lane & 31)) ^ gemm_swz(kr)];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
         if (more) {   // the other buffer's readers finished before the last barrier
@@ -111,10 +116,10 @@ struct LoadRowsT {
             }
         }
     }
-    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM]) const {
         const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i ^ gemm_swz(4 * (t & 3) + c)] = v[c];
     }
 };
 
@@ -136,10 +141,10 @@ struct LoadColsK {
             }
         }
     }
-    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBN + kPad]) const {
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBN]) const {
         const int t = threadIdx.x, kk = t >> 4, j = 4 * (t & 15);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[kk][j + c] = v[c];
+        for (int c = 0; c < 4; ++c) dst[kk][(j + c) ^ gemm_swz(kk)] = v[c];
     }
 };
 

@@ -82,10 +82,10 @@ struct LoadNesterovT {
             }
         }
     }
-    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM]) const {
         const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i ^ gemm_swz(4 * (t & 3) + c)] = v[c];
     }
 };
 
@@ -177,10 +177,10 @@ struct LoadSignT {
             }
         }
     }
-    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM]) const {
         const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i ^ gemm_swz(4 * (t & 3) + c)] = v[c];
     }
 };
 
@@ -199,10 +199,10 @@ struct LoadCoefT {
             }
         }
     }
-    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM + kPad]) const {
+    __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBM]) const {
         const int t = threadIdx.x, i = t >> 2;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i] = v[c];
+        for (int c = 0; c < 4; ++c) dst[4 * (t & 3) + c][i ^ gemm_swz(4 * (t & 3) + c)] = v[c];
     }
 };
 
