@@ -60,24 +60,27 @@ struct SplitWideTable {
     uint16_t *planes[kMaxMats];
 };
 
-// grid = (KS, blocks x matrices), block 256
+// grid = (KS, blocks x matrices), block 256.  Workgroup ks reads rows 16 ks .. 16 ks + 15 of Q_b
+// once (along rows, into LDS) and writes from them Q^T slice ks (all rows j) and, for every slice
+// s, the 16 rows p = 16 ks .. of the Q slices; the last one also zeroes the Q slices' rows past
+// 16 KS (padding up to R).
 __global__ void __launch_bounds__(256) k_split_wide(int nb, int nblk, SplitWideTable t) {
-    __shared__ float tile[512 * 17];   // [16][R + 1] for Q^T, then [R][17] for Q (R <= 512)
+    __shared__ float tile[kKSD * 513];   // [16][R + 1], R <= 512
     const WideGeo geo = wide_geo(nb);
     const int R = geo.R, KS = geo.KS;
     const int ks = blockIdx.x, g = blockIdx.y;
     const int b = g % nblk, mat = g / nblk;
     const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
     const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
-    uint16_t *P = t.planes[mat] + (int64_t)b * PE + (int64_t)ks * R * kKSD;
+    uint16_t *Pb = t.planes[mat] + (int64_t)b * PE;
     const int tid = threadIdx.x, k0 = kKSD * ks;
-    (void)KS;
-    // Q^T slice: rows k0 .. k0 + 15 of Q, every column j (along rows of Q)
     for (int e = tid; e < kKSD * R; e += 256) {
         const int kk = e / R, j = e - kk * R;
         tile[kk * (R + 1) + j] = (k0 + kk < nb && j < nb) ? Q[(int64_t)(k0 + kk) * nb + j] : 0.f;
     }
     __syncthreads();
+    // Q^T slice ks: row j, k: Q[k0 + k][j]
+    uint16_t *P = Pb + (int64_t)ks * R * kKSD;
     for (int e = tid; e < 2 * R; e += 256) {
         const int j = e >> 1, hs = e & 1, h = hs ^ qswz(j);
         uint16_t ph[8], pm[8], pl[8];
@@ -88,21 +91,26 @@ __global__ void __launch_bounds__(256) k_split_wide(int nb, int nblk, SplitWideT
         *(uint4 *)(P + 3 * plane + o) = uint4{pack2(pm[0], pm[1]), pack2(pm[2], pm[3]), pack2(pm[4], pm[5]), pack2(pm[6], pm[7])};
         *(uint4 *)(P + 4 * plane + o) = uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
     }
-    __syncthreads();
-    // Q slice: columns k0 .. k0 + 15 of every row p
-    for (int e = tid; e < kKSD * R; e += 256) {
-        const int p = e / kKSD, kk = e - p * kKSD;
-        tile[p * 17 + kk] = (p < nb && k0 + kk < nb) ? Q[(int64_t)p * nb + k0 + kk] : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < 2 * R; e += 256) {
-        const int p = e >> 1, hs = e & 1, h = hs ^ qswz(p);
+    // Q slices s, rows p = k0 + kk: Q[p][16 s + k] (the tile holds those rows; zero past nb)
+    for (int e = tid; e < KS * kKSD * 2; e += 256) {
+        const int sl = e / (2 * kKSD), rem = e - sl * 2 * kKSD;
+        const int kk = rem >> 1, hs = rem & 1, p = k0 + kk, h = hs ^ qswz(p);
         uint16_t qh[8], ql[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) split2h(tile[p * 17 + 8 * h + i], qh[i], ql[i]);
-        const int64_t o = (int64_t)p * kKSD + 8 * hs;
-        *(uint4 *)(P + o) = uint4{pack2(qh[0], qh[1]), pack2(qh[2], qh[3]), pack2(qh[4], qh[5]), pack2(qh[6], qh[7])};
-        *(uint4 *)(P + plane + o) = uint4{pack2(ql[0], ql[1]), pack2(ql[2], ql[3]), pack2(ql[4], ql[5]), pack2(ql[6], ql[7])};
+        for (int i = 0; i < 8; ++i) split2h(tile[kk * (R + 1) + kKSD * sl + 8 * h + i], qh[i], ql[i]);
+        const int64_t o = ((int64_t)sl * R + p) * kKSD + 8 * hs;
+        *(uint4 *)(Pb + o) = uint4{pack2(qh[0], qh[1]), pack2(qh[2], qh[3]), pack2(qh[4], qh[5]), pack2(qh[6], qh[7])};
+        *(uint4 *)(Pb + plane + o) = uint4{pack2(ql[0], ql[1]), pack2(ql[2], ql[3]), pack2(ql[4], ql[5]), pack2(ql[6], ql[7])};
+    }
+    // padding rows [16 KS, R) of every Q slice
+    if (ks == KS - 1) {
+        const int pad = R - kKSD * KS;
+        for (int e = tid; e < KS * pad * 2; e += 256) {
+            const int sl = e / (2 * pad), rem = e - sl * 2 * pad;
+            const int64_t o = ((int64_t)sl * R + kKSD * KS + (rem >> 1)) * kKSD + 8 * (rem & 1);
+            *(uint4 *)(Pb + o) = uint4{0u, 0u, 0u, 0u};
+            *(uint4 *)(Pb + plane + o) = uint4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
