@@ -248,9 +248,14 @@ struct ReconRowsTable {
     float *U[kMaxMats];
     float lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
 };
+// sign tile pitch: the k extent kpad plus 8 bytes (an odd number of 8-byte units: rows on distinct
+// banks).  The tile holds every k the products read, zero past nb (zero times the basis' zero
+// padding: a stale byte there could decode to an infinite fp16 value and give NaN).
+__host__ __device__ inline int rows_spitch(int nb) { return rows_geo(nb).kpad + 8; }
 __host__ __device__ inline size_t recon_rows_lds(int nb, int TR, int ldp) {
     const RowsGeo g = rows_geo(nb);
-    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * ldp) + a16((size_t)TR * g.uld * 4);
+    (void)ldp;
+    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * rows_spitch(nb)) + a16((size_t)TR * g.uld * 4);
 }
 
 template <int NCH, int TR, bool WBF16>
@@ -260,8 +265,9 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     const RowsGeo geo = rows_geo(nb);
     const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, uld = geo.uld;
     uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
-    uint8_t *ssb = lds + a16((size_t)2 * nb * qld * 2);                      // [TR][ldp]
-    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * ldp));   // [TR][uld]
+    const int spitch = rows_spitch(nb);
+    uint8_t *ssb = lds + a16((size_t)2 * nb * qld * 2);                      // [TR][spitch]
+    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * spitch));   // [TR][uld]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -302,9 +308,9 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
     void *const Wv = t.W[mat];
     float *const U = t.U[mat];
-    // sign rows: 8-byte pieces, ldp / 8 per row; W rows: 4-element pieces, nb / 4 per row
-    const int q8 = ldp / 8, q = nb / 4;
-    constexpr int kSPT = (TR * 16 + kRT - 1) / kRT;   // sign pieces per thread (ldp <= 128)
+    // sign rows: 8-byte pieces, kpad / 8 per row; W rows: 4-element pieces, nb / 4 per row
+    const int q8 = kpad / 8, q = nb / 4;
+    constexpr int kSPT = (TR * 16 + kRT - 1) / kRT;   // sign pieces per thread (kpad <= 128)
     constexpr int kWPT = (TR * 32 + kRT - 1) / kRT;   // W pieces per thread (nb <= 128)
     using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
     uint2 sr[kSPT];
@@ -316,11 +322,11 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
             const int r = e / q8, c = 8 * (e - r * q8);
             const int64_t row = tile * TR + r;
             sr[i] = uint2{0u, 0u};
-            if (tile < t_end && e < TR * q8 && row < m) {
+            // c < nb <= ldp, multiples of 8 (c, ldp) and 4 (nb): the piece lies inside the row;
+            // bytes at or past nb are zero
+            if (tile < t_end && e < TR * q8 && row < m && c < nb) {
                 sr[i] = *(const uint2 *)(S + row * sld + c);
-                // bytes at or past nb are padding: zero them (c is a multiple of 8, nb of 4)
                 if (c + 4 >= nb) sr[i].y = 0u;
-                if (c >= nb) sr[i].x = 0u;
             }
         }
 #pragma unroll
@@ -346,7 +352,7 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
         for (int i = 0; i < kSPT; ++i) {
             const int e = tid + kRT * i;
             const int r = e / q8, c = 8 * (e - r * q8);
-            if (e < TR * q8) *(uint2 *)(sc_ + r * ldp + c) = sr[i];
+            if (e < TR * q8) *(uint2 *)(sc_ + r * spitch + c) = sr[i];
         }
         WVec wcur[kWPT];
 #pragma unroll
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
 #pragma unroll
         for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
         for (int ks = 0; ks < KS; ++ks) {
-            const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * ldp + ks * kKS + kh);
+            const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * spitch + ks * kKS + kh);
             const uint4 av = {signs_f16x2<0>(sv.x), signs_f16x2<1>(sv.x), signs_f16x2<0>(sv.y), signs_f16x2<1>(sv.y)};
             const f16x8 as = __builtin_bit_cast(f16x8, av);
             f16x8 Bh[kCPG], Bl[kCPG];

@@ -13,11 +13,14 @@
 //                 three bf16 planes once);
 //                 waves take (32-row tile, every second 32-column chunk): C^T = Q^T P^T;
 //                 sign bytes -> LDS -> rows
-//   k_recon_wide  sign-byte rows of the tile -> LDS once; waves take (64 rows, every fourth chunk):
-//                 U = S Q^T; W <- W - lr (s U + wd W) from the accumulators, 128-byte row pieces
+//   k_recon_wide  64-row tiles, two workgroups per CU: sign-byte rows -> LDS once; waves take
+//                 (32-row tile, every fourth chunk): U = S Q^T; U -> LDS (32 rows at a time) -> rows,
+//                 where W <- W - lr (s U + wd W) is applied
 // The workgroups of one block are adjacent in launch order, so they run together on one XCD and
 // read the basis slices from its L2.
 #include "step_common.h"
+
+#include <type_traits>
 
 namespace dobb {
 namespace {
@@ -330,37 +333,47 @@ struct ReconWideTable {
     float *U[kMaxMats];
     float lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
 };
-// sign tile pitch: >= ldp, a multiple of 8 with an odd number of 8-byte units (rows on distinct banks)
-__host__ __device__ inline int wide_spitch(int ldp) { return (ldp / 8) % 2 ? ldp : ldp + 8; }
-// LDS: two Q slices (2 planes each), two sign tiles (this tile's and the next one's)
+// sign tile pitch: the k extent 16 KS rounded up to an odd number of 8-byte units (rows on distinct
+// banks).  The tile holds every k the products read, zero past nb (zero times the basis' zero
+// padding: a stale byte there could decode to an infinite fp16 value and give NaN).
+__host__ __device__ inline int wide_spitch(int nb) { return kKSD * ((nb + kKSD - 1) / kKSD) + 8; }
+// U staging pitch in floats: R + 8 (R = 32 ceil(nb / 32)), 8 mod 16, so that the two rows written by
+// the half-waves of one accumulator register fall in opposite bank halves
+__host__ __device__ inline int wide_uld(int nb) { return wide_geo(nb).R + 8; }
+constexpr int kRTR = 64;   // reconstruction: rows per workgroup
+// LDS: region 0 holds two Q slices (2 planes each) during the products, then 32 rows of U at a time;
+// region 1 the tile's sign rows.  At most 81408 bytes (nb <= 416): two workgroups fit on a CU.
+__host__ __device__ inline size_t recon_wide_qregion(int nb) {
+    const size_t q = (size_t)2 * 2 * wide_geo(nb).R * kKSD * 2, u = (size_t)32 * wide_uld(nb) * 4;
+    return a16(q > u ? q : u);
+}
 __host__ __device__ inline size_t recon_wide_lds(int nb, int ldp) {
-    const WideGeo g = wide_geo(nb);
-    return a16((size_t)2 * 2 * g.R * kKSD * 2) + 2 * a16((size_t)kTR * wide_spitch(ldp));
+    (void)ldp;
+    return recon_wide_qregion(nb) + a16((size_t)kRTR * wide_spitch(nb));
 }
 
-// grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
-// NCT = ceil(nb / 32).  Wave w: rows 64 rg .. + 63 (rg = w / 4, two 32-row tiles), column chunks
-// cg + 4 j (cg = w % 4).
+// grid.x = tiles of kRTR rows (fastest) x blocks x matrices, renumbered per XCD; block 512, two
+// workgroups per CU (four waves per SIMD), so that one's products overlap the other's row traffic.
+// NCT = ceil(nb / 32).  Wave w: 32-row tile rt = w / 4, column chunks cg + 4 j (cg = w % 4).
 template <int NCT, bool WBF16>
-__global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
-                                                    int ldp, ReconWideTable t) {
+__global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int nb, int nblk, int ntile, int ldp,
+                                                       ReconWideTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int NCW = (NCT + 3) / 4, R = 32 * NCT, nct = NCT;
+    constexpr int uld = R + 8;   // wide_uld
     const int KS = (nb + kKSD - 1) / kKSD;
-    const int spitch = wide_spitch(ldp);
-    uint16_t *qs = (uint16_t *)lds;                                              // [2][2][R][16]
-    uint8_t *ss0 = lds + a16((size_t)2 * 2 * R * kKSD * 2);                      // [2][kTR][spitch]
-    const size_t sbuf = a16((size_t)kTR * spitch);
+    const int spitch = wide_spitch(nb);
+    uint16_t *qs = (uint16_t *)lds;                        // [2][2][R][16], then U rows [32][uld] fp32
+    float *us = (float *)lds;
+    uint8_t *ss = lds + recon_wide_qregion(nb);             // [kRTR][spitch]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
-    const int tg = x % ngroups, rest = x / ngroups;
+    const int tile = x % ntile, rest = x / ntile;
     const int b = rest % nblk, mat = rest / nblk;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = w >> 2, cg = w & 3;
-    const int64_t ntile = (m + kTR - 1) / kTR;
-    const int64_t t_begin = (int64_t)tg * tpg;
-    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
+    const int rt = w >> 2, cg = w & 3;
+    const int64_t row0 = (int64_t)tile * kRTR;
 
     constexpr int kWS = WBF16 ? 2 : 4;
     const int64_t mn_el = m * n - (int64_t)b * nb;
@@ -374,33 +387,12 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QN, (plane + PE) * 2);
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
 
-    // sign tile pieces: kTR rows x ldp / 8 eight-byte pieces (ldp <= R); piece i of a thread is
-    // e = tid + kWT i, row e / q8, bytes 8 (e % q8) .. + 7
-    constexpr int kSP = (kTR * (R / 8) + kWT - 1) / kWT;
-    const int q8 = ldp / 8;
-    const float inv_q8 = 1.0f / (float)q8;
-    // e / q8 for e < 2^16: the float quotient is within one of the exact one; fix it up
-    auto divq8 = [&](int e) -> int {
-        int r = (int)((float)e * inv_q8);
-        r -= r * q8 > e;
-        r += (r + 1) * q8 <= e;
+    // e / d for 0 <= e < 2^16, 0 < d < 2^10: the float quotient is within one of the exact one
+    auto divu = [](int e, int d, float inv) -> int {
+        int r = (int)((float)e * inv);
+        r -= r * d > e;
+        r += (r + 1) * d <= e;
         return r;
-    };
-    auto load_piece = [&](int64_t tile, int i) -> uint2 {
-        const int e = tid + kWT * i;
-        const int r = divq8(e), c = 8 * (e - r * q8);
-        const int64_t row = tile * kTR + r;
-        const unsigned o = (tile < t_end && e < kTR * q8 && row < m) ? (unsigned)(row * sld + c) : kOff;
-        uint2 v = bload2u(rS, o);
-        // bytes at or past nb are padding: zero them (c is a multiple of 8, nb of 4)
-        if (c + 4 >= nb) v.y = 0u;
-        if (c >= nb) v.x = 0u;
-        return v;
-    };
-    auto store_piece = [&](uint8_t *ss, int i, uint2 v) {
-        const int e = tid + kWT * i;
-        const int r = divq8(e), c = 8 * (e - r * q8);
-        if (e < kTR * q8) *(uint2 *)(ss + r * spitch + c) = v;
     };
     // Q slice pieces: 2 planes x R rows x 2 halves
     constexpr int kQP = (4 * R + kWT - 1) / kWT;
@@ -422,86 +414,130 @@ __global__ void __launch_bounds__(512) k_recon_wide(int64_t m, int64_t n, int nb
         }
     };
 
-    const int kh = 8 * (lane >> 5);
-    int par = 0, sp = 0;
     load_q(0);
+    // sign rows of the tile -> LDS in 8-byte pieces, k = 0 .. 16 KS - 1 (zero at and past nb)
+    {
+        constexpr int kSP = (kRTR * (R / 8) + kWT - 1) / kWT;
+        const int q8 = 2 * KS;
+        const float inv_q8 = 1.0f / (float)q8;
+        uint2 sv[kSP];
 #pragma unroll
-    for (int i = 0; i < kSP; ++i) store_piece(ss0, i, load_piece(t_begin, i));
-    for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        const uint8_t *ss = ss0 + sp * sbuf;      // this tile's sign rows
-        uint8_t *sn = ss0 + (sp ^ 1) * sbuf;      // the next tile's, one piece per k-step
-        f32x16 acc[2][NCW];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < NCW; ++j) acc[i][j] = (f32x16){};
-        uint2 snext = uint2{0u, 0u};
-        for (int ks = 0; ks < KS; ++ks) {
-            store_q(par);
-            load_q(ks + 1 < KS ? ks + 1 : 0);
-            if (ks >= 1 && ks <= kSP) store_piece(sn, ks - 1, snext);
-            if (ks < kSP) snext = load_piece(tile + 1, ks);
-            __syncthreads();
-            f16x8 as[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                as[i] = signs_f16x8(*(const uint2 *)(ss + (64 * rg + 32 * i + (lane & 31)) * spitch + kKSD * ks + kh));
-            const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
-#pragma unroll
-            for (int j = 0; j < NCW; ++j) {
-                const int ch = cg + 4 * j;
-                if (ch < nct) {
-                    const int p = 32 * ch + (lane & 31);
-                    const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
-                    const f16x8 Bh = *(const f16x8 *)(qb + o);
-                    const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bh, acc[i][j], 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as[i], Bl, acc[i][j], 0, 0, 0);
-                }
-            }
-            par ^= 1;
+        for (int i = 0; i < kSP; ++i) {
+            const int e = tid + kWT * i;
+            const int r = divu(e, q8, inv_q8), c = 8 * (e - r * q8);
+            const int64_t row = row0 + r;
+            // c < nb <= ldp and both multiples of 8 (ldp) or 4 (nb): the piece lies inside the row
+            sv[i] = bload2u(rS, (e < kRTR * q8 && row < m && c < nb) ? (unsigned)(row * sld + c) : kOff);
+            if (c + 4 >= nb) sv[i].y = 0u;
         }
-        // pieces that did not fit in the k-steps (kSP >= KS cannot happen for nb > 128, kept for safety)
-        if (KS <= kSP) store_piece(sn, KS - 1, snext);
-        for (int i = KS; i < kSP; ++i) store_piece(sn, i, load_piece(tile + 1, i));
-        sp ^= 1;
-        // W <- W - lr (s U + wd W): lane holds column 32 ch + l % 32 of rows 8 (r / 4) + 4 (l / 32) + r % 4
-        // of each 32-row tile; each load / store instruction covers 128 contiguous bytes of two rows.
-        // Eight rows at a time: their loads are all issued before the first store.
+#pragma unroll
+        for (int i = 0; i < kSP; ++i) {
+            const int e = tid + kWT * i;
+            const int r = divu(e, q8, inv_q8), c = 8 * (e - r * q8);
+            if (e < kRTR * q8) *(uint2 *)(ss + r * spitch + c) = sv[i];
+        }
+    }
+
+    // U = S Q^T for 32-row tile rt and this wave's column chunks
+    const int kh = 8 * (lane >> 5);
+    f32x16 acc[NCW];
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+    int par = 0;
+    for (int ks = 0; ks < KS; ++ks) {
+        store_q(par);
+        if (ks + 1 < KS) load_q(ks + 1);
+        __syncthreads();
+        const f16x8 as = signs_f16x8(*(const uint2 *)(ss + (32 * rt + (lane & 31)) * spitch + kKSD * ks + kh));
+        const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const int ch = cg + 4 * j;
-            if (ch >= nct) continue;
+            if (ch < nct) {
+                const int p = 32 * ch + (lane & 31);
+                const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
+                const f16x8 Bh = *(const f16x8 *)(qb + o);
+                const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
+            }
+            // one chunk's operands at a time (the other waves of the SIMD cover the LDS latency)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        par ^= 1;
+    }
+
+    // W <- W - lr (s U + wd W), one 32-row tile at a time: its waves write U to the LDS (lane: column
+    // 32 ch + l % 32 of rows 8 (r / 4) + 4 (l / 32) + r % 4), then every thread updates 16-byte
+    // pieces along the rows.  The W pieces of a half are loaded before its U is staged, and each
+    // register is refilled with the second half's piece as soon as it is used.
+    const int nq = nb >> 2;
+    const float inv_nq = 1.0f / (float)nq;
+    constexpr int kUP = (32 * (R / 4) + kWT - 1) / kWT;   // pieces per thread and half
+    using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
+    auto piece_off = [&](int h, int k) -> unsigned {       // element offset of piece k of half h
+        const int e = tid + kWT * k;
+        const int r = divu(e, nq, inv_nq), c = 4 * (e - r * nq);
+        const int64_t row = row0 + 32 * h + r;
+        return (e < 32 * nq && row < m) ? (unsigned)row * (unsigned)n + (unsigned)c : kOff;
+    };
+    auto load_piece_w = [&](int h, int k) -> WVec {
+        const unsigned o = piece_off(h, k);
+        if constexpr (WBF16) return bload2u(rW, boff(o, 2));
+        else return bload4(rW, boff(o, 4));
+    };
+    auto write_u = [&]() {
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int ch = cg + 4 * j;
             const int col = 32 * ch + (lane & 31);
+            if (ch < nct && col < nb) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int64_t rl = tile * kTR + 64 * rg + 32 * i + 4 * (lane >> 5);
-                const unsigned base = (unsigned)rl * (unsigned)n + (unsigned)col;   // < 2^31 (checked on the host)
-                const int vr = col < nb ? (int)(m - rl < 32 ? m - rl : 32) : 0;  // valid rows from rl on
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    unsigned off[8];
-                    float wv[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int r = 8 * h + q, ro = 8 * (r >> 2) + (r & 3);
-                        off[q] = ro < vr ? base + (unsigned)ro * (unsigned)n : kOff;
-                        wv[q] = WBF16 ? bf16_to_f32(bload1h(rW, boff(off[q], 2))) : bload1(rW, boff(off[q], 4));
-                    }
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float u = acc[i][j][8 * h + q];
-                        const float nw = wv[q] - lr * __builtin_fmaf(sc, u, wd * wv[q]);
-                        if (U) bstore1(u, rU, boff(off[q], 4));
-                        if constexpr (WBF16) bstore1h(f32_to_bf16(nw), rW, boff(off[q], 2));
-                        else bstore1(nw, rW, boff(off[q], 4));
-                    }
-                }
+                for (int r = 0; r < 16; ++r) us[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * uld + col] = acc[j][r];
             }
         }
-    }
+    };
+    WVec wv[kUP];
+    auto update = [&](int h) {
+#pragma unroll
+        for (int k = 0; k < kUP; ++k) {
+            const int e = tid + kWT * k;
+            const int r = divu(e, nq, inv_nq), c = 4 * (e - r * nq);
+            const unsigned o = piece_off(h, k);
+            if (e < 32 * nq) {
+                const f32x4 u = *(const f32x4 *)(us + r * uld + c);
+                float w0[4];
+                if constexpr (WBF16) {
+                    const uint2 hb = wv[k];
+                    w0[0] = bf16_to_f32((uint16_t)hb.x); w0[1] = bf16_to_f32((uint16_t)(hb.x >> 16));
+                    w0[2] = bf16_to_f32((uint16_t)hb.y); w0[3] = bf16_to_f32((uint16_t)(hb.y >> 16));
+                } else {
+                    w0[0] = wv[k][0]; w0[1] = wv[k][1]; w0[2] = wv[k][2]; w0[3] = wv[k][3];
+                }
+                float nw[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) nw[cc] = w0[cc] - lr * __builtin_fmaf(sc, u[cc], wd * w0[cc]);
+                if (U) bstore4(u, rU, boff(o, 4));
+                if constexpr (WBF16)
+                    bstore2u(uint2{(uint32_t)f32_to_bf16(nw[0]) | ((uint32_t)f32_to_bf16(nw[1]) << 16),
+                                   (uint32_t)f32_to_bf16(nw[2]) | ((uint32_t)f32_to_bf16(nw[3]) << 16)},
+                             rW, boff(o, 2));
+                else bstore4(f32x4{nw[0], nw[1], nw[2], nw[3]}, rW, boff(o, 4));
+            }
+            if (h == 0) wv[k] = load_piece_w(1, k);
+            __builtin_amdgcn_sched_barrier(0);   // one piece at a time (register pressure)
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kUP; ++k) wv[k] = load_piece_w(0, k);
+    __syncthreads();   // every wave is done with the Q slices
+    if (rt == 0) write_u();
+    __syncthreads();
+    update(0);
+    __syncthreads();   // every thread is done reading the first half
+    if (rt == 1) write_u();
+    __syncthreads();
+    update(1);
 }
 
 // One 128-row tile per workgroup: the workgroups of a block are then as many as its tiles and run
@@ -551,11 +587,13 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
             t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
         }
         const size_t sh = recon_wide_lds(nb, ldp);
+        const int rtiles = (int)((m + kRTR - 1) / kRTR);
+        const dim3 rgrid((unsigned)((int64_t)rtiles * nblk * cnt));
 #define DOBB_RWIDE(WB)                                                                                           \
     do {                                                                                                         \
         (void)hipFuncSetAttribute((const void *)k_recon_wide<NCT, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("reconstruct_f16x2", s, (k_recon_wide<NCT, WB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups, \
-                    (int)tpg, ldp, t);                                                                           \
+        DOBB_LAUNCH("reconstruct_f16x2", s, (k_recon_wide<NCT, WB>), rgrid, dim3(kWT), sh, m, n, nb, nblk, rtiles, \
+                    ldp, t);                                                                                     \
     } while (0)
         if (a.w_dtype == DOBB_BF16) DOBB_RWIDE(true); else DOBB_RWIDE(false);
 #undef DOBB_RWIDE

@@ -230,6 +230,7 @@ def _run_step(W, G, M, Q, nb, hp, norm):
 
 @pytest.mark.parametrize("m,n,nb", [(768, 768, 192), (130, 96, 48), (70, 75, 25), (200, 800, 400), (64, 256, 128),
                                     (130, 272, 136),    # nb = 136: a partial last k-step, ragged rows
+                                    (300, 400, 100),    # nb = 100: row kernels, a partial last k-step
                                     (100, 960, 480)])   # nb = 480: the staged kernels for the widest blocks
 def test_step_matches_oracle(m, n, nb):
     print(f"step m={m} n={n} nb={nb}", flush=True)
