@@ -10,7 +10,16 @@ Householder) -> the Dobb step (momentum, projection, sign, reconstruction, weigh
 first refresh (setup, untimed) is exact.  Times come from events around the timed steps; the
 library's kernel timer attributes them to kernels.  The CPU oracle is timed on a bounded sample.
 
+The default workload is the GPT-2 XL set.  ``--workload gpt2small`` runs the GPT-2 Small set (12 layers x
+{qkv 2304x768, proj 768x768, fc 3072x768, fc-proj 768x3072}, B = 16, fp32 state, bf16 activations of
+8192 tokens) and ``--workload llama7b`` the 7B-style stack (32 layers x {q, k, v, o 4096x4096, gate/up
+11008x4096, down 4096x11008}, nb = 128, bf16 W and G, fp32 M, A and Q; the pages give no token count
+for it, so a capture here is 4096 tokens).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--layers L] [--copy-mib C]
+                       [--workload gpt2xl|gpt2small|llama7b]
+       python bench.py --pmc-summary FETCH_CSV WRITE_CSV [--copy-mib C]
+       python bench.py --mfma-summary COUNTER_CSV
 """
 from __future__ import annotations
 
@@ -32,11 +41,27 @@ PEAK_HBM = 8.0e12            # B/s
 PEAK_BF16_MFMA = 2.5e15      # flop/s, bf16 and fp16
 PEAK_FP32_MFMA = 157.3e12    # flop/s
 PEAK_FP32_VALU = 157.3e12    # flop/s
-N_TOKENS = 16384
 BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
 STEP_ROWS_MAX_NB = 128        # blocks up to this width keep Q resident in LDS in the step kernels (no split_q)
+
+# Matrix sets.  per_layer: weights per layer; tokens: activations per capture; config: seed namespace;
+# cpu_rows / cpu_tokens: the oracle sample (1/cpu_rows of each weight's rows, cpu_tokens of the tokens).
+WORKLOADS = {
+    "gpt2xl": dict(specs="gpt2_xl_set", arg=BLOCKS, layers=48, per_layer=4, tokens=16384, w_dtype="float32",
+                   config=4, lr=2.5e-3, cpu_rows=1, cpu_tokens=8192,
+                   text="GPT-2 XL matrix set ({L} layers x qkv 4800x1600, proj 1600x1600, fc 6400x1600, "
+                        "fc-proj 1600x6400; B=16, nb=100/400), fp32 W/G/M/A/Q, bf16 activations {N} tokens"),
+    "gpt2small": dict(specs="gpt2_small_set", arg=BLOCKS, layers=12, per_layer=4, tokens=8192, w_dtype="float32",
+                      config=3, lr=3.54e-3, cpu_rows=1, cpu_tokens=8192,
+                      text="GPT-2 Small matrix set ({L} layers x qkv 2304x768, proj 768x768, fc 3072x768, "
+                           "fc-proj 768x3072; B=16, nb=48/192), fp32 W/G/M/A/Q, bf16 activations {N} tokens"),
+    "llama7b": dict(specs="llama7b_set", arg=128, layers=32, per_layer=7, tokens=4096, w_dtype="bfloat16",
+                    config=5, lr=2.5e-3, cpu_rows=16, cpu_tokens=512,
+                    text="Llama-7B-style stack ({L} layers x q,k,v,o 4096x4096, gate/up 11008x4096, down "
+                         "4096x11008; nb=128), bf16 W/G, fp32 M/A/Q, bf16 activations {N} tokens"),
+}
 
 
 def parse():
@@ -45,7 +70,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layers", type=int, default=48, help="GPT-2 XL has 48 layers")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2xl")
+    ap.add_argument("--layers", type=int, default=0, help="layers of the matrix set (default: all)")
+    ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
+                    help="per-kernel MFMA utilisation and issued MFMA flops from a rocprofv3 --pmc run of "
+                         "MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 MfmaFlopsF32")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-kernel HBM traffic table from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -202,16 +231,39 @@ def pmc_summary(fetch_csv, write_csv, copy_mib):
             print(f"| {name} | `{source_digest(name)}` | {fetch[name][1]} | {fetch[name][0]:.0f} | {write[name][0]:.0f} |")
 
 
-def cpu_baseline(group, xs, specs, layers):
-    """Time the oracle (one thread) on layer 0's four weights: the step on all rows, the capture on
-    8192 of the tokens, the orthogonal-iteration refresh on 8 of the 16 blocks of each weight; scale
-    linearly to the full set (every term is linear in rows, tokens, blocks and layers)."""
-    import torch
+def mfma_summary(counter_csv):
+    """Per-kernel matrix-core figures from one rocprofv3 --pmc run of the derived counters MfmaUtil
+    (MFMA-busy SIMD cycles over active cycles x SIMDs, percent) and MfmaFlops{BF16,F16,F32} (issued
+    MFMA operations x 512, per dispatch), averaged over each kernel's dispatches."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(counter_csv)):
+        for name, (sym, _) in KERNEL_SYMBOLS.items():
+            if re.search(sym, r["Kernel_Name"]):
+                acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    print("| kernel | source digest | launches | MFMA busy (% of SIMD cycles) | bf16 MFMA flop/launch | "
+          "fp16 MFMA flop/launch | fp32 MFMA flop/launch |")
+    print("|---|---|---|---|---|---|---|")
+    for name in KERNEL_SYMBOLS:
+        c = acc.get(name)
+        if not c:
+            continue
+        avg = lambda k: (sum(c[k]) / len(c[k])) if c.get(k) else float("nan")
+        print(f"| {name} | `{source_digest(name)}` | {len(c.get('MfmaUtil', []))} | {avg('MfmaUtil'):.1f} | "
+              f"{avg('MfmaFlopsBF16'):.4g} | {avg('MfmaFlopsF16'):.4g} | {avg('MfmaFlopsF32'):.4g} |")
+
+
+def cpu_baseline(group, xs, specs, wl, layers):
+    """Time the oracle (one thread) on layer 0's weights: the step on 1/cpu_rows of each weight's rows,
+    the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on 8 blocks of each
+    weight; scale linearly to the full set (every term is linear in rows, tokens, blocks and layers)."""
     import oracle
-    rows_frac, tok, nblk_s = 1, 8192, 8
+    rows_frac, tok, nblk_s = wl["cpu_rows"], wl["cpu_tokens"], 8
+    n_tokens = wl["tokens"]
     t_step = t_acc = t_ref = 0.0
     s_step = s_acc = s_ref = 0.0
-    for i in range(4):
+    for i in range(wl["per_layer"]):
         s = specs[i]
         B = s.n // s.nb
         r = s.m // rows_frac
@@ -228,14 +280,14 @@ def cpu_baseline(group, xs, specs, layers):
         oracle.orth_iter(A, Qp, k=1, cores=1)
         t3 = time.perf_counter()
         t_step += t1 - t0; t_acc += t2 - t1; t_ref += t3 - t2
-        s_step += (t1 - t0) * rows_frac
-        s_acc += (t2 - t1) * (N_TOKENS / tok)
-        s_ref += (t3 - t2) * (B / nblk_s)
+        s_step += (t1 - t0) * (s.m / r)
+        s_acc += (t2 - t1) * (n_tokens / tok)
+        s_ref += (t3 - t2) * (B / min(nblk_s, B))
     total_s = (s_step + s_acc + s_ref) * layers
     return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
             "sample": (f"layer 0 of {layers}: step on 1/{rows_frac} of each weight's rows, capture on {tok} of "
-                       f"{N_TOKENS} tokens, orthogonal-iteration refresh on {nblk_s} of 16 blocks; measured "
-                       f"{t_step + t_acc + t_ref:.1f} s, scaled linearly (rows, tokens, blocks, layers)"),
+                       f"{n_tokens} tokens, orthogonal-iteration refresh on {nblk_s} blocks of each weight; "
+                       f"measured {t_step + t_acc + t_ref:.1f} s, scaled linearly (rows, tokens, blocks, layers)"),
             "seconds_measured": round(t_step + t_acc + t_ref, 2)}
 
 
@@ -243,6 +295,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_mib or 1024)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the Dobb step here is the single-GPU kernel path "
@@ -264,7 +319,11 @@ def main():
         print(f"[bench] calibration copy: {args.copy_mib} MiB read, {args.copy_mib} MiB written", file=sys.stderr,
               flush=True)
         del src, dst
-    specs = workload.gpt2_xl_set(BLOCKS)[: 4 * args.layers]
+    wl = WORKLOADS[args.workload]
+    layers = args.layers or wl["layers"]
+    n_tokens = wl["tokens"]
+    specs = getattr(workload, wl["specs"])(wl["arg"])[: wl["per_layer"] * layers]
+    w_dtype = getattr(torch, wl["w_dtype"])
     print(f"[bench] {len(specs)} weights, {workload.param_count(specs) / 1e9:.4f} B params", file=sys.stderr, flush=True)
 
     # ---- inputs (seeded, synthetic) -------------------------------------------------------------
@@ -272,12 +331,14 @@ def main():
     gen.manual_seed(4)
     Ws, Gs = [], []
     for s in specs:
-        Ws.append((0.02 * torch.randn(s.m, s.n, device=dev, generator=gen)))
-        Gs.append(torch.randn(s.m, s.n, device=dev, generator=gen))
+        Ws.append((0.02 * torch.randn(s.m, s.n, device=dev, generator=gen)).to(w_dtype))
+        Gs.append(torch.randn(s.m, s.n, device=dev, generator=gen).to(w_dtype))
     bases = {}
     xs = []
     for li, s in enumerate(specs):
-        X, basis = workload.activations_torch(N_TOKENS, s.n, 0.15, seed=workload.seed_for(4, li // 4, li % 4),
+        X, basis = workload.activations_torch(n_tokens, s.n, 0.15,
+                                              seed=workload.seed_for(wl["config"], li // wl["per_layer"],
+                                                                     li % wl["per_layer"]),
                                               device=dev, dtype=torch.bfloat16, basis=bases.get(s.n))
         bases[s.n] = basis
         xs.append(X)
@@ -285,7 +346,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] inputs ready", file=sys.stderr, flush=True)
 
-    group = DobbGroup(Ws, [s.nb for s in specs], grads=Gs, n_tokens=N_TOKENS, lr=2.5e-3, weight_decay=0.1,
+    group = DobbGroup(Ws, [s.nb for s in specs], grads=Gs, n_tokens=n_tokens, lr=wl["lr"], weight_decay=0.1,
                       momentum=0.9)
     beta = 0.9
     # setup: first capture and the exact refresh (untimed, but measured once)
@@ -344,7 +405,7 @@ def main():
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
     w_bytes = Ws[0].element_size()
-    work = kernel_work(specs, N_TOKENS, g_bytes, w_bytes)
+    work = kernel_work(specs, n_tokens, g_bytes, w_bytes)
     per_kernel = {}
     for name, (launches, total_ms) in kernels.items():
         ent = {"launches_per_step": launches / args.steps, "ms_per_step": round(total_ms / args.steps, 4),
@@ -366,18 +427,16 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(group, xs, specs, args.layers)
+        cpu = cpu_baseline(group, xs, specs, wl, layers)
 
     amort = lambda T: (full_ms_untimed + (T - 1) * step_ms) / T
     out = {
         "metric": METRIC, "value": round(ms_per_step, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"GPT-2 XL matrix set ({args.layers} layers x qkv 4800x1600, proj 1600x1600, "
-                               f"fc 6400x1600, fc-proj 1600x6400; B=16, nb=100/400), fp32 W/G/M/A/Q, bf16 "
-                               f"activations {N_TOKENS} tokens; capture + orthogonal-iteration refresh (k=1) + "
-                               f"step every step",
-                   "matrices": len(specs), "params": workload.param_count(specs), "tokens": N_TOKENS,
+        "config": {"workload": wl["text"].format(L=layers, N=n_tokens) + "; capture + orthogonal-iteration "
+                               "refresh (k=1) + step every step",
+                   "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
                    "refresh_period": 1},
         "roofline": roofline,
         "cpu_baseline": cpu,
