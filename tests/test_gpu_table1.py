@@ -10,7 +10,12 @@ are missing from the listing, so the orthogonality figures are compared GPU agai
 
 Bars: the end-to-end bar (<= 0.1 % of U's entries differ by more than 1e-3 RMS(U)) and the
 orthogonality of the GPU's update within 1e-3 of the oracle's, for sign and for column-l2
-normalisation in the same eigenbasis.
+normalisation in the same eigenbasis.  The end-to-end bar holds for inputs with distinct eigenvalues;
+at B = 1 the 768 eigenvalues of this spectrum include pairs 1.6e-7 max(lambda) apart, and storing A in
+fp32 (as the library does) moves those eigenvectors by itself: the oracle's own basis of its A
+correctly rounded to fp32 already changes 2.6e-3 of U's entries.  So each case measures that floor
+with the oracle alone (its update from the fp32-rounded A against its update from the fp64 A) and the
+bars are max(0.1 %, 2 x floor) for sign and max(1e-4, 2 x floor) relative Frobenius for column-l2.
 
 The oracle's Jacobi eigensolver at nb = 768 is warm-started from LAPACK's eigenvectors (a library
 routine used as the starting basis only, to keep the case within seconds): the oracle checks that
@@ -64,10 +69,13 @@ def _gradient(rank):
     return _cache[key]
 
 
-def _oracle_basis(nb):
-    key = ("Q", nb)
+def _oracle_basis(nb, fp32_A=False):
+    """The oracle's eigenbasis of its own A blocks, or of those blocks correctly rounded to fp32."""
+    key = ("Q", nb, fp32_A)
     if key not in _cache:
         A = oracle.accumulate(_activations(), nb)
+        if fp32_A:
+            A = np.float64(np.float32(A))
         V0 = np.stack([np.linalg.eigh(a)[1] for a in A]) if nb > 256 else None
         lam, Q, info = oracle.eig(A, V0=V0)
         assert np.all(info >= 0)
@@ -89,7 +97,7 @@ def test_table1b_gradients(rank, B):
     info = torch.empty(B, dtype=torch.int32, device=DEV)
     dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT, info=info)
     assert bool((info > 0).all()), "eigensolver did not converge"
-    Q_ref = _oracle_basis(nb)
+    Q_ref, Q_ref32 = _oracle_basis(nb), _oracle_basis(nb, fp32_A=True)
     zeros = np.zeros((DIM, DIM))
     out = {}
     for name, norm, onorm in [("sign", dobb.DOBB_NORM_SIGN, oracle.NORM_SIGN),
@@ -99,13 +107,19 @@ def test_table1b_gradients(rank, B):
         U = torch.empty(DIM, DIM, device=DEV)
         dobb.dobb_step(W, G, M, Q, nb, dobb.make_hparams(0.0, 0.0, 0.0, 1.0, norm=norm), U_out=U)
         _, _, U_ref = oracle.step(zeros, Gh, zeros, Q_ref, nb, 0.0, 0.0, 0.0, 1.0, norm=onorm)
+        _, _, U_ref32 = oracle.step(zeros, Gh, zeros, Q_ref32, nb, 0.0, 0.0, 0.0, 1.0, norm=onorm)
         Ug = host(U)
         if name == "sign":
             rms = np.sqrt(np.mean(U_ref ** 2))
+            floor = np.mean(np.abs(U_ref32 - U_ref) > 1e-3 * rms)
             frac = np.mean(np.abs(Ug - U_ref) > 1e-3 * rms)
-            assert frac <= 1e-3, f"{frac:.2e} of U's entries differ"
+            print(f"  sign: {frac:.2e} of U's entries differ (fp32-storage floor {floor:.2e})", flush=True)
+            assert frac <= max(1e-3, 2 * floor), f"{frac:.2e} of U's entries differ"
         else:
-            assert np.linalg.norm(Ug - U_ref) <= 1e-4 * np.linalg.norm(U_ref)
+            floor = np.linalg.norm(U_ref32 - U_ref) / np.linalg.norm(U_ref)
+            err = np.linalg.norm(Ug - U_ref) / np.linalg.norm(U_ref)
+            print(f"  column-l2: relative error {err:.2e} (fp32-storage floor {floor:.2e})", flush=True)
+            assert err <= max(1e-4, 2 * floor)
         o_gpu, o_ref = metrics.orthogonality(Ug), metrics.orthogonality(U_ref)
         assert abs(o_gpu - o_ref) <= 1e-3
         out[name] = (o_gpu, o_ref)
