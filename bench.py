@@ -98,8 +98,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
                             all panels): 4/3 nb^3 B flops each (fp32)
       qr_panel              nb > 128, panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
       split_q               nb > 128 only, Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
-      project_bf16x6        M read + written, G read, sign bytes written: (9 + g) m n bytes;
-                            2 m n nb flops (fp32 contraction), issued as six bf16 products
+      project_f16x3         nb <= 416: M read + written, G read, sign bytes written: (9 + g) m n bytes;
+                            2 m n nb flops (fp32 contraction), issued as three fp16 products
+      project_bf16x6        nb > 416 (staged kernels): same bytes and flops, issued as six bf16 products
       reconstruct_f16x2     sign bytes read, W read + written: (1 + 2 w) m n bytes;
                             2 m n nb flops (fp32 contraction), issued as two fp16 products
     """
@@ -125,7 +126,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
             add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)
-        add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
+        if nb <= 416:
+            add("project_f16x3", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+        else:
+            add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
         add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
     return w
 
@@ -168,7 +172,8 @@ KERNEL_SYMBOLS = {
     "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),
     "qr_form": (r"k_qr_form<", "k_qr.hip"),
     "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
-    "project_bf16x6": (r"k_proj_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
+    "project_f16x3": (r"k_proj_(rows|wide)<", ("k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
+    "project_bf16x6": (r"k_proj_bf16<", ("k_step_bf16.hip", "step_common.h")),
     "reconstruct_f16x2": (r"k_recon_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
 }
 

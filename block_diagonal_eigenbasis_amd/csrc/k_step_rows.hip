@@ -4,8 +4,10 @@
 // reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
 // (Nesterov).
 //
-// Same arithmetic as k_step_bf16.hip: C = P Q with both operands split into three bf16 parts (the
-// six products of order <= 2); U = S Q^T with Q split into two fp16 parts (S is exact in fp16).
+// C = P Q with both operands split into two fp16 parts (three products: hi*hi, hi*lo, lo*hi).  The
+// rows of P are first scaled by a power of two (exact) that puts each row's largest magnitude in
+// [2^13, 2^14), so the fp16 parts neither overflow nor lose the row's scale; the sign of C does not
+// depend on that scale.  U = S Q^T with Q split into two fp16 parts (S is exact in fp16).
 // Signs travel as the high byte of their fp16 value (+1 -> 0x3c, -1 -> 0xbc, 0 -> 0x00, NaN -> 0x7e).
 //
 // Layout of the work: a workgroup (8 waves) owns one block b; it splits Q_b into LDS once and then
@@ -13,7 +15,7 @@
 // consecutive 16- or 8-byte pieces of a row's nb-wide slice): an access pattern where each lane
 // takes a different row, as the MFMA operand layout would, reaches well under half of the HBM
 // bandwidth.  The MFMA operands are read from LDS tiles:
-//   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32);
+//   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32), row maxima -> LDS;
 //                 waves take (32-row tile, column chunks): C^T = Q^T P^T; sign bytes -> LDS -> rows
 //   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
 //                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
@@ -54,9 +56,11 @@ struct ProjRowsTable {
     uint8_t *S[kMaxMats];
     float mu[kMaxMats];
 };
+// LDS: Q_b^T (two fp16 planes), the P tile (fp32), the sign tile, and two buffers of per-row maxima
+// of |P| (fp32 bits; the buffer of tile t is t % 2)
 __host__ __device__ inline size_t proj_rows_lds(int nb, int TR, int ldp) {
     const RowsGeo g = rows_geo(nb);
-    return a16((size_t)3 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp);
+    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp) + (size_t)2 * TR * 4;
 }
 
 // grid.x = tile groups x blocks x matrices (block fastest, renumbered per XCD), block 512.
@@ -67,9 +71,10 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
     extern __shared__ __align__(16) unsigned char lds[];
     const RowsGeo geo = rows_geo(nb);
     const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, pld = geo.pld;
-    uint16_t *qs = (uint16_t *)lds;                                          // [3][nb][qld]
-    float *ps = (float *)(lds + a16((size_t)3 * nb * qld * 2));              // [TR][pld]
-    uint8_t *ss = lds + a16((size_t)3 * nb * qld * 2) + a16((size_t)TR * pld * 4);   // [TR][ldp]
+    uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
+    float *ps = (float *)(lds + a16((size_t)2 * nb * qld * 2));              // [TR][pld]
+    uint8_t *ss = lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * pld * 4);   // [TR][ldp]
+    uint32_t *rmax = (uint32_t *)(ss + a16((size_t)TR * ldp));                // [2][TR]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -79,7 +84,7 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
     const int64_t t_begin = (int64_t)tg * tpg;
     const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
 
-    // Q_b^T split into three bf16 planes (element (p, j) of Q at plane[j][p]); zero for p in [nb, kpad)
+    // Q_b^T split into two fp16 planes (element (p, j) of Q at plane[j][p]); zero for p in [nb, kpad)
     {
         const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
         const int total = kpad * nb;
@@ -95,11 +100,10 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
                 const int e = e0 + tid + kRT * i;
                 if (e < total) {
                     const int p = e / nb, j = e - p * nb;
-                    uint16_t h, md, l;
-                    split3(v[i], h, md, l);
+                    uint16_t h, l;
+                    split2h(v[i], h, l);
                     qs[(0 * nb + j) * qld + p] = h;
-                    qs[(1 * nb + j) * qld + p] = md;
-                    qs[(2 * nb + j) * qld + p] = l;
+                    qs[(1 * nb + j) * qld + p] = l;
                 }
             }
         }
@@ -108,7 +112,9 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
             ps[r * pld + c] = 0.f;
         }
+        for (int e = tid; e < 2 * TR; e += kRT) rmax[e] = 0u;
     }
+    __syncthreads();   // the row maxima start at zero before the first tile's atomics
 
     // row pieces: piece e -> row e / q, columns 4 (e % q) .. + 3 of the block slice
     const int q = nb / 4;
@@ -148,9 +154,11 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
 
     load_tile(t_begin);
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        // momentum (written back along the rows) and P into the LDS tile (its last readers passed the
-        // previous tile's second barrier)
+        // momentum (written back along the rows), P into the LDS tile and its row maxima (their last
+        // readers passed the previous tile's second barrier)
         float *pc = ps;
+        const int rb = (int)((tile - t_begin) & 1);
+        uint32_t *rm = rmax + rb * TR;
 #pragma unroll
         for (int i = 0; i < kIPT; ++i) {
             const int e = tid + kRT * i;
@@ -165,10 +173,20 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             if (e < TR * q) {
                 if (row < m) *(f32x4 *)(M + row * n + c) = mn;
                 *(f32x4 *)(pc + r * pld + c) = pv;   // rows past m hold zeros (their loads read zero)
+                uint32_t mx = __float_as_uint(pv[0]) & 0x7fffffffu;
+#pragma unroll
+                for (int cc = 1; cc < 4; ++cc) {
+                    const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
+                    mx = u > mx ? u : mx;
+                }
+                atomicMax(rm + r, mx);
             }
         }
         load_tile(tile + 1);
         __syncthreads();
+        // the other buffer is free (read last in the previous tile): clear it for the next tile
+        for (int e = tid; e < TR; e += kRT) rmax[(rb ^ 1) * TR + e] = 0u;
+        const int sexp = row_scale_exp(rm[32 * rt + (lane & 31)]);
         // C^T = Q^T P^T for 32-row tile rt and this wave's column chunks
         f32x16 acc[kCPG];
 #pragma unroll
@@ -176,18 +194,16 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
         for (int ks = 0; ks < KS; ++ks) {
             const float *pr = pc + (32 * rt + (lane & 31)) * pld + ks * kKS + kh;
             const f32x4 p0 = *(const f32x4 *)pr, p1 = *(const f32x4 *)(pr + 4);
-            uint16_t hh[8], hm[8], hl[8];
+            uint16_t hh[8], hl[8];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-                split3(p0[cc], hh[cc], hm[cc], hl[cc]);
-                split3(p1[cc], hh[cc + 4], hm[cc + 4], hl[cc + 4]);
+                split2s(__builtin_amdgcn_ldexpf(p0[cc], sexp), hh[cc], hl[cc]);
+                split2s(__builtin_amdgcn_ldexpf(p1[cc], sexp), hh[cc + 4], hl[cc + 4]);
             }
             const uint4 uh = {pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])};
-            const uint4 um = {pack2(hm[0], hm[1]), pack2(hm[2], hm[3]), pack2(hm[4], hm[5]), pack2(hm[6], hm[7])};
             const uint4 ul = {pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])};
-            const bf16x8 ah = __builtin_bit_cast(bf16x8, uh), am = __builtin_bit_cast(bf16x8, um),
-                         al = __builtin_bit_cast(bf16x8, ul);
-            bf16x8 Qh[kCPG], Qm[kCPG], Ql[kCPG];
+            const f16x8 ah = __builtin_bit_cast(f16x8, uh), al = __builtin_bit_cast(f16x8, ul);
+            f16x8 Qh[kCPG], Ql[kCPG];
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) {
                 const int ch = cg * kCPG + j;
@@ -195,25 +211,17 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
                 const bool ok = ch < NCH && col < nb;
                 const int cs = ok ? col : 0;
                 uint4 bh = *(const uint4 *)&qs[(0 * nb + cs) * qld + ks * kKS + kh];
-                uint4 bm = *(const uint4 *)&qs[(1 * nb + cs) * qld + ks * kKS + kh];
-                uint4 bl = *(const uint4 *)&qs[(2 * nb + cs) * qld + ks * kKS + kh];
-                if (!ok) bh = bm = bl = uint4{0u, 0u, 0u, 0u};
-                Qh[j] = __builtin_bit_cast(bf16x8, bh);
-                Qm[j] = __builtin_bit_cast(bf16x8, bm);
-                Ql[j] = __builtin_bit_cast(bf16x8, bl);
+                uint4 bl = *(const uint4 *)&qs[(1 * nb + cs) * qld + ks * kKS + kh];
+                if (!ok) bh = bl = uint4{0u, 0u, 0u, 0u};
+                Qh[j] = __builtin_bit_cast(f16x8, bh);
+                Ql[j] = __builtin_bit_cast(f16x8, bl);
             }
 #pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], ah, acc[j], 0, 0, 0);
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], ah, acc[j], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm[j], ah, acc[j], 0, 0, 0);
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql[j], ah, acc[j], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], am, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql[j], ah, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm[j], am, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh[j], al, acc[j], 0, 0, 0);
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], al, acc[j], 0, 0, 0);
         }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t -> LDS
 #pragma unroll
@@ -456,7 +464,7 @@ hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream
 #define DOBB_PROWS(NE, GB)                                                                                       \
     do {                                                                                                         \
         (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("project_bf16x6", s, (k_proj_rows<NCH, TR, NE, GB>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups,  \
+        DOBB_LAUNCH("project_f16x3", s, (k_proj_rows<NCH, TR, NE, GB>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups,  \
                     (int)tpg, ldp, t);                                                                           \
     } while (0)
         if (!nest) { if (gbf) DOBB_PROWS(0, true); else DOBB_PROWS(0, false); }

@@ -4,13 +4,15 @@
 // reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
 // (Nesterov).
 //
-// Same arithmetic as the narrow-block kernels: C = P Q with both operands split into three bf16
-// parts (the six products of order <= 2); U = S Q^T with Q split into two fp16 parts (S is exact in
-// fp16).  A block's basis is too large to stay in LDS, so it is streamed one 16-deep k-slice at a
+// Same arithmetic as the narrow-block kernels: C = P Q with both operands split into two fp16 parts
+// (three products), each row of P scaled by a power of two that keeps its largest magnitude in
+// [2^13, 2^14); U = S Q^T with Q split into two fp16 parts (S is exact in fp16).  P streams through
+// in column chunks, so a row's scale is the one its largest entry so far asks for: when a later chunk
+// lowers it, the row's accumulators are rescaled by the (exact) power of two before its products.  A block's basis is too large to stay in LDS, so it is streamed one 16-deep k-slice at a
 // time from planes that k_split_wide lays out slice by slice (each slice one contiguous copy, with
 // the LDS swizzle already applied).  All row data moves along rows:
-//   k_proj_wide   M, G rows (64-column chunks) -> M <- mu M + G (written back), P -> LDS (split into
-//                 three bf16 planes once);
+//   k_proj_wide   M, G rows (64-column chunks) -> M <- mu M + G (written back), P -> LDS (scaled per
+//                 row, split into two fp16 planes once);
 //                 waves take (32-row tile, every second 32-column chunk): C^T = Q^T P^T;
 //                 sign bytes -> LDS -> rows
 //   k_recon_wide  64-row tiles, two workgroups per CU: sign-byte rows -> LDS once; waves take
@@ -54,9 +56,9 @@ __host__ __device__ inline int qswz(int j) { return ((j >> 2) ^ (j >> 3)) & 1; }
 __host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
 
 // ---- basis planes --------------------------------------------------------------------------------
-// planes (5 per matrix, each nblk x KS x R x 16 two-byte elements, slice-major):
+// planes (4 per matrix, each nblk x KS x R x 16 two-byte elements, slice-major):
 //   0, 1  fp16 hi / lo of Q_b:    slice ks, row p, k: Q_b[p][16 ks + k]
-//   2-4   bf16 h / m / l of Q_b^T: slice ks, row j, k: Q_b[16 ks + k][j]
+//   2, 3  fp16 hi / lo of Q_b^T:  slice ks, row j, k: Q_b[16 ks + k][j]
 // zero where a row or k index is >= nb.
 struct SplitWideTable {
     const float *Q[kMaxMats];
@@ -86,13 +88,12 @@ __global__ void __launch_bounds__(256) k_split_wide(int nb, int nblk, SplitWideT
     uint16_t *P = Pb + (int64_t)ks * R * kKSD;
     for (int e = tid; e < 2 * R; e += 256) {
         const int j = e >> 1, hs = e & 1, h = hs ^ qswz(j);
-        uint16_t ph[8], pm[8], pl[8];
+        uint16_t ph[8], pl[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) split3(tile[(8 * h + i) * (R + 1) + j], ph[i], pm[i], pl[i]);
+        for (int i = 0; i < 8; ++i) split2h(tile[(8 * h + i) * (R + 1) + j], ph[i], pl[i]);
         const int64_t o = (int64_t)j * kKSD + 8 * hs;
         *(uint4 *)(P + 2 * plane + o) = uint4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
-        *(uint4 *)(P + 3 * plane + o) = uint4{pack2(pm[0], pm[1]), pack2(pm[2], pm[3]), pack2(pm[4], pm[5]), pack2(pm[6], pm[7])};
-        *(uint4 *)(P + 4 * plane + o) = uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
+        *(uint4 *)(P + 3 * plane + o) = uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
     }
     // Q slices s, rows p = k0 + kk: Q[p][16 s + k] (the tile holds those rows; zero past nb)
     for (int e = tid; e < KS * kKSD * 2; e += 256) {
@@ -125,15 +126,15 @@ struct ProjWideTable {
     uint8_t *S[kMaxMats];
     float mu[kMaxMats];
 };
-// LDS: two Q^T slices (3 planes each; the sign tile overlays them after the products), the P chunk
-// split into three bf16 planes
+// LDS: two Q^T slices (2 planes each; the sign tile overlays them after the products), the P chunk
+// split into two fp16 planes, and the tile's per-row scale exponents
 __host__ __device__ inline size_t proj_wide_qregion(int nb, int ldp) {
     const WideGeo g = wide_geo(nb);
-    const size_t q = (size_t)2 * 3 * g.R * kKSD * 2, s = (size_t)kTR * ldp;
+    const size_t q = (size_t)2 * 2 * g.R * kKSD * 2, s = (size_t)kTR * ldp;
     return a16(q > s ? q : s);
 }
 __host__ __device__ inline size_t proj_wide_lds(int nb, int ldp) {
-    return proj_wide_qregion(nb, ldp) + (size_t)3 * kTR * kPLD * 2;
+    return proj_wide_qregion(nb, ldp) + (size_t)2 * kTR * kPLD * 2 + (size_t)kTR * 4;
 }
 
 // grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
@@ -144,9 +145,10 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int NCW = (NCT + 1) / 2, R = 32 * NCT, nct = NCT;
     const int KS = (nb + kKSD - 1) / kKSD;
-    uint16_t *qs = (uint16_t *)lds;                                   // [2][3][R][16]
+    uint16_t *qs = (uint16_t *)lds;                                   // [2][2][R][16]
     uint8_t *ss = lds;                                                // [kTR][ldp], after the products
-    uint16_t *ps = (uint16_t *)(lds + proj_wide_qregion(nb, ldp));    // [3][kTR][kPLD]
+    uint16_t *ps = (uint16_t *)(lds + proj_wide_qregion(nb, ldp));    // [2][kTR][kPLD]
+    int *rs = (int *)(ps + 2 * kTR * kPLD);                           // [kTR] row scale exponents
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int tg = x % ngroups, rest = x / ngroups;
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(t.S[mat] + (int64_t)b * ldp, m * sld - (int64_t)b * ldp);
     const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
     const uint16_t *QT = t.planes[mat] + 2 * plane + (int64_t)b * PE;
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QT, (2 * plane + PE) * 2);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QT, (plane + PE) * 2);
     const float mu = t.mu[mat];
 
     // M / G chunk pieces: kTR rows x 20 four-column pieces, 5 per thread
@@ -192,36 +194,56 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
             }
         }
     };
-    // momentum written back along the rows; P split once into three bf16 planes of the LDS chunk
-    // (zeros past m and nb)
-    auto stage_p = [&](int64_t tile, int kc0) {
+    // momentum written back along the rows; P scaled by its row's power of two and split once into
+    // two fp16 planes of the LDS chunk (zeros past m and nb).  The 16 lanes of a row are consecutive,
+    // so the chunk's row maximum is a 16-lane reduction; the row's exponent is the smaller of the
+    // chunk's and the one in rs (the first chunk of a tile starts afresh).
+    auto stage_p = [&](int64_t tile, int kc0, bool first) {
 #pragma unroll
         for (int i = 0; i < kMP; ++i) {
             const int e = tid + kWT * i;
             const int r = e / (kKC / 4), c = 4 * (e - r * (kKC / 4));
-            f32x4 mn;
-            uint16_t h[4], md[4], l[4];
+            f32x4 mn, pv;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
-                split3(NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc], h[cc], md[cc], l[cc]);
+                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
             }
             bstore4(mn, rM, boff(mg_off(i, tile, kc0), 4));
+            uint32_t mx = __float_as_uint(pv[0]) & 0x7fffffffu;
+#pragma unroll
+            for (int cc = 1; cc < 4; ++cc) {
+                const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
+                mx = u > mx ? u : mx;
+            }
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)mx, sh, 16);
+                mx = o > mx ? o : mx;
+            }
+            int se = row_scale_exp(mx);
+            if (!first) {
+                const int so = rs[r];
+                se = so < se ? so : se;
+            }
+            if ((tid & 15) == 0) rs[r] = se;
+            uint16_t h[4], l[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) split2s(__builtin_amdgcn_ldexpf(pv[cc], se), h[cc], l[cc]);
             uint16_t *pp = ps + r * kPLD + c;
             *(uint2 *)pp = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-            *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(md[0], md[1]), pack2(md[2], md[3])};
-            *(uint2 *)(pp + 2 * kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+            *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
         }
     };
-    // Q^T slice pieces: 3 planes x R rows x 2 halves of 16 bytes
-    constexpr int kQP = (6 * R + kWT - 1) / kWT;
+    // Q^T slice pieces: 2 planes x R rows x 2 halves of 16 bytes
+    constexpr int kQP = (4 * R + kWT - 1) / kWT;
     uint4 qr[kQP];
     auto load_q = [&](int ks) {
 #pragma unroll
         for (int i = 0; i < kQP; ++i) {
             const int e = tid + kWT * i;
             const int pl = e / (2 * R), rem = e - pl * 2 * R;
-            const unsigned o = e < 6 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
+            const unsigned o = e < 4 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
             qr[i] = bload4u(rQ, boff(o, 2));
         }
     };
@@ -229,7 +251,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
 #pragma unroll
         for (int i = 0; i < kQP; ++i) {
             const int e = tid + kWT * i;
-            if (e < 6 * R) *(uint4 *)(qs + (size_t)buf * 3 * R * kKSD + 8 * e) = qr[i];
+            if (e < 4 * R) *(uint4 *)(qs + (size_t)buf * 2 * R * kKSD + 8 * e) = qr[i];
         }
     };
 
@@ -242,14 +264,16 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
     int par = 0;
     load_mg(t_begin, 0);
     load_q(0);
+    const int prow = 32 * rt + (lane & 31);   // the P row (tile row) of this lane's accumulators
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
         f32x16 acc[NCW];
 #pragma unroll
         for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+        int sreg = 0;   // the scale exponent acc holds its row at
         for (int c = 0; c < nchunk; ++c) {
             const int kc0 = c * kKC;
             __syncthreads();   // the last chunk's products are done with ps, the sign drain with qs
-            stage_p(tile, kc0);
+            stage_p(tile, kc0, c == 0);
             if (c + 1 < nchunk) load_mg(tile, kc0 + kKC);
             else load_mg(tile + 1, 0);
             const int s_end = KS - kSPC * c < kSPC ? KS - kSPC * c : kSPC;
@@ -258,11 +282,22 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                 store_q(par);
                 load_q(ks + 1 < KS ? ks + 1 : 0);   // the next tile starts over at slice 0
                 __syncthreads();
-                const uint16_t *pr = ps + (32 * rt + (lane & 31)) * kPLD + kKSD * s + kh;
-                const bf16x8 ah = *(const bf16x8 *)pr;
-                const bf16x8 am = *(const bf16x8 *)(pr + kTR * kPLD);
-                const bf16x8 al = *(const bf16x8 *)(pr + 2 * kTR * kPLD);
-                const uint16_t *qb = qs + (size_t)par * 3 * R * kKSD + qoff;
+                if (s == 0) {
+                    // this chunk's scale of the lane's row: rescale what acc holds when it dropped
+                    const int se = rs[prow];
+                    const int d = c == 0 ? 0 : se - sreg;
+                    if (__any(d != 0)) {
+#pragma unroll
+                        for (int j = 0; j < NCW; ++j)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) acc[j][i] = __builtin_amdgcn_ldexpf(acc[j][i], d);
+                    }
+                    sreg = se;
+                }
+                const uint16_t *pr = ps + prow * kPLD + kKSD * s + kh;
+                const f16x8 ah = *(const f16x8 *)pr;
+                const f16x8 al = *(const f16x8 *)(pr + kTR * kPLD);
+                const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD + qoff;
                 // chunks two at a time, their products interleaved so that consecutive MFMAs are
                 // independent
 #pragma unroll
@@ -271,30 +306,19 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                     if (cg + 2 * j < nct) {
                         const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
                         const uint16_t *q1 = q0 + 2 * 32 * kKSD;
-                        const bf16x8 Qh0 = *(const bf16x8 *)q0, Qm0 = *(const bf16x8 *)(q0 + R * kKSD),
-                                     Ql0 = *(const bf16x8 *)(q0 + 2 * R * kKSD);
+                        const f16x8 Qh0 = *(const f16x8 *)q0, Ql0 = *(const f16x8 *)(q0 + R * kKSD);
                         if (two) {
-                            const bf16x8 Qh1 = *(const bf16x8 *)q1, Qm1 = *(const bf16x8 *)(q1 + R * kKSD),
-                                         Ql1 = *(const bf16x8 *)(q1 + 2 * R * kKSD);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, ah, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, ah, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, ah, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm1, ah, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, am, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, am, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql0, ah, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql1, ah, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, am, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm1, am, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, al, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh1, al, acc[j + 1], 0, 0, 0);
+                            const f16x8 Qh1 = *(const f16x8 *)q1, Ql1 = *(const f16x8 *)(q1 + R * kKSD);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, al, acc[j + 1], 0, 0, 0);
                         } else {
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, ah, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, ah, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, am, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ql0, ah, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qm0, am, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qh0, al, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
                         }
                     }
                 }
@@ -571,7 +595,7 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
 #define DOBB_PWIDE(NE, GB)                                                                                       \
     do {                                                                                                         \
         (void)hipFuncSetAttribute((const void *)k_proj_wide<NCT, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("project_bf16x6", s, (k_proj_wide<NCT, NE, GB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups,  \
+        DOBB_LAUNCH("project_f16x3", s, (k_proj_wide<NCT, NE, GB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups,  \
                     (int)tpg, ldp, t);                                                                           \
     } while (0)
         if (!nest) { if (gbf) DOBB_PWIDE(0, true); else DOBB_PWIDE(0, false); }
@@ -604,7 +628,8 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
 }  // namespace
 
 bool step_wide_eligible(const dobb_shape &sh) {
-    if (sh.nb <= 128 || sh.nb > 512 || sh.nb % 4 != 0) return false;
+    // the launcher instantiates 5 <= ceil(nb / 32) <= 13
+    if (sh.nb <= 128 || sh.nb > 416 || sh.nb % 4 != 0) return false;
     const int ldp = step_bf16_ldp(sh.nb);
     // 32-bit buffer offsets: the largest byte offset into M, G, W, U or the sign codes
     const int64_t big = sh.m * sh.n * 4 > sh.m * (sh.n / sh.nb) * ldp ? sh.m * sh.n * 4 : sh.m * (sh.n / sh.nb) * ldp;
@@ -614,7 +639,7 @@ bool step_wide_eligible(const dobb_shape &sh) {
 }
 
 size_t step_wide_planes_bytes(const dobb_shape &sh) {
-    return (size_t)5 * (size_t)(sh.n / sh.nb) * (size_t)wide_plane_elems((int)sh.nb) * 2;
+    return (size_t)4 * (size_t)(sh.n / sh.nb) * (size_t)wide_plane_elems((int)sh.nb) * 2;
 }
 
 hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {

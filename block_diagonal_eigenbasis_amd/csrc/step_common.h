@@ -24,6 +24,18 @@ __device__ __forceinline__ void split2h(float v, uint16_t &h, uint16_t &l) {
     h = __builtin_bit_cast(uint16_t, a);
     l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)a));
 }
+// power-of-two exponent that scales a row whose largest magnitude has fp32 bits `bits` into
+// [2^13, 2^14): 14 minus the frexp exponent (biased exponent - 126).  A zero row gets 140 (its
+// entries stay zero); an infinite or NaN maximum gets -115 (the row's coefficients become NaN, as
+// they would unscaled).
+__device__ __forceinline__ int row_scale_exp(uint32_t bits) { return 140 - (int)(bits >> 23); }
+// v (already scaled by its row's power of two, |v| < 2^14) = h + l in fp16; the residual v - h is
+// exact in fp32, and |v - h - l| <= 2^-22 |v| where l is normal
+__device__ __forceinline__ void split2s(float v, uint16_t &h, uint16_t &l) {
+    const _Float16 a = (_Float16)v;
+    h = __builtin_bit_cast(uint16_t, a);
+    l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)a));
+}
 // high byte of the fp16 value of sign(c), from the bits of c without branches:
 // +1 -> 0x3c, -1 -> 0xbc, 0 -> 0x00, NaN -> 0x7e
 __device__ __forceinline__ uint32_t sign_byte(float c) {

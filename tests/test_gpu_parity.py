@@ -257,6 +257,38 @@ def test_step_matches_oracle(m, n, nb):
     check_w(W_sh, W0, U_sh, hp)
 
 
+@pytest.mark.parametrize("m,n,nb", [(130, 96, 48), (300, 400, 100), (200, 800, 400), (150, 400, 200)])
+def test_step_rows_across_the_fp32_range(m, n, nb):
+    """Rows of P from 1e-30 to 1e30, and rows whose later columns are 1e6 times their first ones (in
+    the wide blocks a row's scale then drops between column chunks).  The projection scales each row
+    by a power of two before its fp16 split, so every row keeps fp32-level relative accuracy: no sign
+    mismatch where |C_ref| > 1e-5 of that row's largest |C_ref| in the block, and U equal to
+    sign(C) Q^T to 1e-5."""
+    print(f"step row scales m={m} n={n} nb={nb}", flush=True)
+    rng = RNG(61 + nb)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=61 + nb)
+    rs = np.float32(10.0 ** rng.uniform(-30, 30, size=(m, 1)))
+    ramp = np.ones((m, n), dtype=np.float32)
+    ramp[::3, :] = np.float32(10.0 ** (6.0 * (np.arange(n) % nb) / nb))   # within each block
+    M = t32(host(M) * rs * ramp)
+    G = t32(host(G) * rs * ramp)
+    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"])
+    _check_momentum(M_s, M, G, hp["momentum"], M_r)
+    U_sh = host(U_s)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = M_r[:, sl] @ Qh[b]
+        S_gpu = np.rint(U_sh[:, sl] @ Qh[b])
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref), axis=1, keepdims=True)
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the row's dead zone"
+        R = S_gpu @ Qh[b].T
+        assert np.linalg.norm(U_sh[:, sl] - R) <= 1e-5 * np.linalg.norm(R)
+    assert np.mean(np.abs(U_sh - U_r) > 1e-3) <= 1e-3
+    check_w(host(W_s), host(W), U_sh, hp)
+
+
 def test_step_identity_round_trip():
     Q, Qh, W, G, M, hp = _step_case(100, 192, 64, seed=5, mu=1.0)
     G.zero_()
