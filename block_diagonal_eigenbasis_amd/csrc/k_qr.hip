@@ -378,9 +378,9 @@ __global__ void __launch_bounds__(256) k_qr_panel(int nb, int p, float *Z_all, f
 // start), op(T) = T, and with FLIP (first panel) the columns whose R_cc < 0 are negated.
 // Vs[r][c] = V[r][c] for r < rows, c < 32 (zero for c >= w) from Z's panel columns, and zero rows
 // from rows up to the next multiple of 32.  8 threads per row, eight rows per thread in flight.
-template <int CH>
+template <int CH, int NT = kQT>
 __device__ __forceinline__ void stage_v(float (*Vs)[kPW + 1], const float *Z, int nb, int j0, int w, int rows, int tid) {
-    constexpr int kPasses = 2 * CH;   // 32 rows per pass
+    constexpr int kPasses = 2 * CH;   // NT / 8 rows per pass
     const int c4 = 4 * (tid & 7), r0 = tid >> 3;
     const int rpad = (rows + 31) & ~31;
     const bool vec = (nb & 3) == 0 && c4 + 4 <= w;
@@ -390,7 +390,7 @@ __device__ __forceinline__ void stage_v(float (*Vs)[kPW + 1], const float *Z, in
         f32x4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = r0 + 32 * (b0 + i);
+            const int r = r0 + (NT / 8) * (b0 + i);
             const bool ok = b0 + i < kPasses && r < rows;
             const float *src = Zp + (ok ? r : 0) * nb + c4;
             if (vec) {
@@ -403,7 +403,7 @@ __device__ __forceinline__ void stage_v(float (*Vs)[kPW + 1], const float *Z, in
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = r0 + 32 * (b0 + i);
+            const int r = r0 + (NT / 8) * (b0 + i);
             if (b0 + i < kPasses && r < rpad) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) Vs[r][c4 + q] = v[i][q];
@@ -545,17 +545,31 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
 
 // ---- nb > 128: formation of Q in one launch ---------------------------------------------------------
 // A workgroup owns a 64-column tile of Q_b over all nb rows and keeps it in registers (accumulator
-// layout, as in k_qr_apply) from the identity to the final store.  It applies the block reflectors
+// layout, as in k_qr_apply) from the identity to the final store.  Its 8 waves split the tile into
+// two column halves by four row parts, so a wave holds at most 4 x 32 rows and two waves share each
+// SIMD.  It applies the block reflectors
 // I - V_p T_p V_p^T for p = min(npanel - 1, last column / 32) down to 0 (panels starting past the
 // tile's last column leave its identity columns unchanged), each with V_p and T_p staged in LDS, and
 // stores the tile once with the columns whose R_cc < 0 negated.  Wave (kp, h): column half h, rows
-// [0, half) or [half, nb); 32-row chunks lying wholly above a panel's first row are skipped (V = 0).
-// grid = (ceil(nb / 64) tiles, blocks), block 256.
+// [kp part, (kp + 1) part) with part = 32 ceil(nb / 128); 32-row chunks lying wholly above a panel's
+// first row are skipped (V = 0).
+// grid = (ceil(nb / 64) tiles, blocks), block 512.  CH = part / 32.
+constexpr int kFP = 4;                 // formation: row parts
+constexpr int kFT = 2 * 64 * kFP;      // formation: threads per workgroup
+__host__ __device__ inline ApplyLds form_lds(int nb) {
+    ApplyLds L;
+    size_t o = 0;
+    L.vs = o; o += a16((size_t)((nb + 31) & ~31) * (kPW + 1) * 4);
+    L.ts = o; o += a16((size_t)kPW * (kPW + 1) * 4);
+    L.wp = o; o += a16((size_t)kFP * 2 * 32 * 33 * 4);   // [row part][column half]
+    L.total = o;
+    return L;
+}
 template <int CH>
-__global__ void __launch_bounds__(256) k_qr_form(int nb, int nblk, const float *Z_all, const float *Tq_all,
+__global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *Z_all, const float *Tq_all,
                                                  const int8_t *neg_all, QrBlockOut t, int info_value) {
     extern __shared__ __align__(16) unsigned char dsm[];
-    const ApplyLds L = apply_lds(nb);
+    const ApplyLds L = form_lds(nb);
     float(*Vs)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.vs);
     float(*Ts)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.ts);
     float(*Wp)[2][32][33] = (float(*)[2][32][33])(dsm + L.wp);
@@ -570,8 +584,8 @@ __global__ void __launch_bounds__(256) k_qr_form(int nb, int nblk, const float *
     const int c0 = blockIdx.x * 64 + 32 * h;
     const bool colok = c0 + cc < nb;
     const int ccl = colok ? c0 + cc : 0;
-    const int half = ((nb + 63) / 64) * 32;
-    const int rb = kp ? half : 0, re = kp ? nb : (half < nb ? half : nb);
+    const int part = ((nb + 32 * kFP - 1) / (32 * kFP)) * 32;
+    const int rb = kp * part, re = rb + part < nb ? rb + part : nb;
     const unsigned lo = (unsigned)((rb + 4 * kr) * nb + ccl);
     const unsigned unb = (unsigned)nb;
     // the identity columns of the tile
@@ -587,14 +601,14 @@ __global__ void __launch_bounds__(256) k_qr_form(int nb, int nblk, const float *
     for (int p = plast; p >= 0; --p) {
         const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
         __syncthreads();   // the last panel's readers of Vs, Ts and Wp are done
-        stage_v<CH>(Vs, Z, nb, j0, w, rows, tid);
+        stage_v<CH, kFT>(Vs, Z, nb, j0, w, rows, tid);
         {
             const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
-            float tv[kPW * kPW / kQT];
+            float tv[kPW * kPW / kFT];
 #pragma unroll
-            for (int i = 0; i < kPW * kPW / kQT; ++i) tv[i] = Tq[tid + kQT * i];
+            for (int i = 0; i < kPW * kPW / kFT; ++i) tv[i] = Tq[tid + kFT * i];
 #pragma unroll
-            for (int i = 0; i < kPW * kPW / kQT; ++i) Ts[(tid + kQT * i) / kPW][(tid + kQT * i) % kPW] = tv[i];
+            for (int i = 0; i < kPW * kPW / kFT; ++i) Ts[(tid + kFT * i) / kPW][(tid + kFT * i) % kPW] = tv[i];
         }
         __syncthreads();
         // W partial = V^T X over this wave's chunks at rows >= j0 (chunks are 32-aligned, as is j0)
@@ -613,12 +627,15 @@ __global__ void __launch_bounds__(256) k_qr_form(int nb, int nblk, const float *
 #pragma unroll
         for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = acc[r];
         __syncthreads();
-        // Y = T (W_0 + W_1)
+        // Y = T (W_0 + W_1 + W_2 + W_3)
         f32x16 y = {};
 #pragma unroll
         for (int kk = 0; kk < kPW; kk += 2) {
             const int kx = kk + kr;
-            y = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[cc][kx], Wp[0][h][kx][cc] + Wp[1][h][kx][cc], y, 0, 0, 0);
+            float wsum = Wp[0][h][kx][cc];
+#pragma unroll
+            for (int q = 1; q < kFP; ++q) wsum += Wp[q][h][kx][cc];
+            y = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[cc][kx], wsum, y, 0, 0, 0);
         }
         __syncthreads();
 #pragma unroll
@@ -698,9 +715,11 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
             DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
                         as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
     }
-    (void)hipFuncSetAttribute((const void *)k_qr_form<CH>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
-    DOBB_LAUNCH("qr_form", s, (k_qr_form<CH>), dim3((unsigned)((nb + 63) / 64), (unsigned)nblocks), dim3(kQT), as, nb,
-                nblk, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, infov);
+    // formation: four row parts of 32 ceil(nb / 128) rows, i.e. CH / 2 chunks
+    const size_t fs = form_lds(nb).total;
+    (void)hipFuncSetAttribute((const void *)k_qr_form<CH / 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fs);
+    DOBB_LAUNCH("qr_form", s, (k_qr_form<CH / 2>), dim3((unsigned)((nb + 63) / 64), (unsigned)nblocks), dim3(kFT), fs,
+                nb, nblk, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, infov);
     return hipGetLastError();
 }
 
