@@ -15,7 +15,7 @@
 // consecutive 16- or 8-byte pieces of a row's nb-wide slice): an access pattern where each lane
 // takes a different row, as the MFMA operand layout would, reaches well under half of the HBM
 // bandwidth.  The MFMA operands are read from LDS tiles:
-//   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32), row maxima -> LDS;
+//   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32);
 //                 waves take (32-row tile, column chunks): C^T = Q^T P^T; sign bytes -> LDS -> rows
 //   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
 //                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
@@ -56,11 +56,10 @@ struct ProjRowsTable {
     uint8_t *S[kMaxMats];
     float mu[kMaxMats];
 };
-// LDS: Q_b^T (two fp16 planes), the P tile (fp32), the sign tile, and two buffers of per-row maxima
-// of |P| (fp32 bits; the buffer of tile t is t % 2)
+// LDS: Q_b^T (two fp16 planes), the P tile (fp32) and the sign tile
 __host__ __device__ inline size_t proj_rows_lds(int nb, int TR, int ldp) {
     const RowsGeo g = rows_geo(nb);
-    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp) + (size_t)2 * TR * 4;
+    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp);
 }
 
 // grid.x = tile groups x blocks x matrices (block fastest, renumbered per XCD), block 512.
@@ -74,7 +73,6 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
     uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
     float *ps = (float *)(lds + a16((size_t)2 * nb * qld * 2));              // [TR][pld]
     uint8_t *ss = lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * pld * 4);   // [TR][ldp]
-    uint32_t *rmax = (uint32_t *)(ss + a16((size_t)TR * ldp));                // [2][TR]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -112,9 +110,7 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
             ps[r * pld + c] = 0.f;
         }
-        for (int e = tid; e < 2 * TR; e += kRT) rmax[e] = 0u;
     }
-    __syncthreads();   // the row maxima start at zero before the first tile's atomics
 
     // row pieces: piece e -> row e / q, columns 4 (e % q) .. + 3 of the block slice
     const int q = nb / 4;
@@ -154,11 +150,9 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
 
     load_tile(t_begin);
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        // momentum (written back along the rows), P into the LDS tile and its row maxima (their last
-        // readers passed the previous tile's second barrier)
+        // momentum (written back along the rows) and P into the LDS tile (its last readers passed the
+        // previous tile's second barrier)
         float *pc = ps;
-        const int rb = (int)((tile - t_begin) & 1);
-        uint32_t *rm = rmax + rb * TR;
 #pragma unroll
         for (int i = 0; i < kIPT; ++i) {
             const int e = tid + kRT * i;
@@ -173,20 +167,29 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             if (e < TR * q) {
                 if (row < m) *(f32x4 *)(M + row * n + c) = mn;
                 *(f32x4 *)(pc + r * pld + c) = pv;   // rows past m hold zeros (their loads read zero)
-                uint32_t mx = __float_as_uint(pv[0]) & 0x7fffffffu;
-#pragma unroll
-                for (int cc = 1; cc < 4; ++cc) {
-                    const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
-                    mx = u > mx ? u : mx;
-                }
-                atomicMax(rm + r, mx);
             }
         }
         load_tile(tile + 1);
         __syncthreads();
-        // the other buffer is free (read last in the previous tile): clear it for the next tile
-        for (int e = tid; e < TR; e += kRT) rmax[(rb ^ 1) * TR + e] = 0u;
-        const int sexp = row_scale_exp(rm[32 * rt + (lane & 31)]);
+        // the scale of this lane's row: its half of the row (k = 16 ks + kh ..), then the other half
+        // from lane ^ 32
+        int sexp;
+        {
+            const float *pr = pc + (32 * rt + (lane & 31)) * pld + kh;
+            uint32_t mx = 0u;
+            for (int ks = 0; ks < KS; ++ks) {
+                const f32x4 p0 = *(const f32x4 *)(pr + ks * kKS), p1 = *(const f32x4 *)(pr + ks * kKS + 4);
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const uint32_t u0 = __float_as_uint(p0[cc]) & 0x7fffffffu;
+                    const uint32_t u1 = __float_as_uint(p1[cc]) & 0x7fffffffu;
+                    mx = u0 > mx ? u0 : mx;
+                    mx = u1 > mx ? u1 : mx;
+                }
+            }
+            const uint32_t o = (uint32_t)__shfl_xor((int)mx, 32);
+            sexp = row_scale_exp(o > mx ? o : mx);
+        }
         // C^T = Q^T P^T for 32-row tile rt and this wave's column chunks
         f32x16 acc[kCPG];
 #pragma unroll
