@@ -34,8 +34,9 @@ struct OutOpnd {
     int64_t ld;
 };
 
-// grid.x = tiles * tiles * nblk * count
-template <bool TRANS_A>
+// grid.x = tiles * tiles * nblk * count.  VEC: 16-byte operand loads (nb % 4 == 0, so every row
+// and 4-column piece starts 16-byte aligned)
+template <bool TRANS_A, bool VEC>
 __global__ void __launch_bounds__(256) k_bgemm(int nb, int T, int nblk, Opnd A, Opnd B, OutOpnd C) {
     __shared__ GemmSmem2 sm;
     const int x = xcd_remap(blockIdx.x, gridDim.x);   // the tiles of a block share one XCD's L2
@@ -45,13 +46,13 @@ __global__ void __launch_bounds__(256) k_bgemm(int nb, int T, int nblk, Opnd A, 
     const int i0 = (tile / T) * kBM, j0 = (tile % T) * kBN;
     const float *Ab = A.p[mat] + (int64_t)b * A.blk_stride;
     const float *Bb = B.p[mat] + (int64_t)b * B.blk_stride;
-    LoadColsK<false> lb{Bb + j0, B.ld, nb - j0, nb};
+    LoadColsK<VEC> lb{Bb + j0, B.ld, nb - j0, nb};
     f32x16 acc;
     if (TRANS_A) {  // op(A)[i][k] = A[k][i]: already k-major
-        LoadColsK<false> la{Ab + i0, A.ld, nb - i0, nb};
+        LoadColsK<VEC> la{Ab + i0, A.ld, nb - i0, nb};
         acc = gemm_tile(nb, la, lb, sm);
     } else {
-        LoadRowsT<false> la{Ab + (int64_t)i0 * A.ld, A.ld, nb - i0, nb};
+        LoadRowsT<VEC> la{Ab + (int64_t)i0 * A.ld, A.ld, nb - i0, nb};
         acc = gemm_tile(nb, la, lb, sm);
     }
     float *Cb = C.p[mat] + (int64_t)b * C.blk_stride;
@@ -877,10 +878,15 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
         outT.blk_stride = t_stride;
         outT.ld = nb;
         const dim3 ggemm((unsigned)(T * T * nblocks));
+#define DOBB_BGEMM(TR, OA, OB, OC)                                                                               \
+    do {                                                                                                         \
+        if (nb % 4 == 0) DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, true>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC); \
+        else DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, false>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC);         \
+    } while (0)
 
         if (a.mode == DOBB_REFRESH_EXACT) {
             if (a.warm) {
-                DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
+                DOBB_BGEMM(false, opA, opQ, outT);
                 Opnd opT{};
                 OutOpnd outAw{};
                 for (int i = 0; i < cnt; ++i) {
@@ -889,7 +895,7 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
                 }
                 opT.blk_stride = t_stride; opT.ld = nb;
                 outAw.blk_stride = aw_stride; outAw.ld = nbp;
-                DOBB_LAUNCH("refresh_gemm", s, k_bgemm<true>, ggemm, dim3(256), 0, nb, T, nblk, opQ, opT, outAw);
+                DOBB_BGEMM(true, opQ, opT, outAw);
             }
             JacTable jt{};
             for (int i = 0; i < cnt; ++i) { jt.A[i] = a.A[c0 + i]; jt.Qp[i] = a.Q[c0 + i]; }
@@ -950,7 +956,7 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
             else (void)hipFuncSetAttribute((const void *)k_qr_panel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl);
             const int npanel = (nb + kQP - 1) / kQP;
             for (int it = 0; it < a.iters; ++it) {
-                DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
+                DOBB_BGEMM(false, opA, opQ, outT);
                 const int infov = it == a.iters - 1 ? a.iters : 0;
                 if (qr_block_supported(nb)) {
                     const hipError_t e = launch_qr_block(nb, nblk, cnt, Tm, tq, negs, ot.Q, ot.info, infov, s);
@@ -982,11 +988,12 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
             bool want_lam = false;
             for (int i = 0; i < cnt; ++i) want_lam |= ot.lam[i] != nullptr;
             if (want_lam) {
-                DOBB_LAUNCH("refresh_gemm", s, k_bgemm<false>, ggemm, dim3(256), 0, nb, T, nblk, opA, opQ, outT);
+                DOBB_BGEMM(false, opA, opQ, outT);
                 DOBB_LAUNCH("rayleigh", s, k_rayleigh, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, (const float *)Tm, ot,
                             a.iters);
             }
         }
+        #undef DOBB_BGEMM
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         c0 += cnt;
