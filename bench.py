@@ -426,7 +426,9 @@ def main():
     launches = d["launches_per_step"]
     unit_work = work[dom]["bytes"] if d["bound"] == "hbm" else work[dom]["flops"]
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
-                "frac": d["frac"], "traffic": measured_traffic(dom),
+                "frac": d["frac"],
+                # counters were taken on the full GPT-2 XL set only
+                "traffic": measured_traffic(dom) if args.workload == "gpt2xl" and layers == 48 else None,
                 "work_per_launch": unit_work / launches,
                 "work_unit": "bytes" if d["bound"] == "hbm" else "flop",
                 "avg_launch_ms": d["avg_launch_ms"], "launches_per_step": launches}
