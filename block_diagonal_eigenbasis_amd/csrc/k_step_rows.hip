@@ -19,7 +19,8 @@
 //                 waves take (32-row tile, column chunks): C^T = Q^T P^T; sign bytes -> LDS -> rows
 //   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
 //                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
-// The next tile's rows are loaded while the current tile's products run.
+// The next tile's rows are loaded while the current tile's products run (in the reconstruction,
+// from before its products to the end of its W update).
 #include "step_common.h"
 
 #include <type_traits>
@@ -368,6 +369,7 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
         WVec wcur[kWPT];
 #pragma unroll
         for (int i = 0; i < kWPT; ++i) wcur[i] = wr[i];
+        load_tile(tile + 1);
         __syncthreads();
         // U^T = Q S^T for 32-row tile rt and this wave's column chunks
         f32x16 acc[kCPG];
@@ -407,7 +409,6 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
                         f32x4{acc[j][4 * qq], acc[j][4 * qq + 1], acc[j][4 * qq + 2], acc[j][4 * qq + 3]};
             }
         }
-        load_tile(tile + 1);
         __syncthreads();
         // W <- W - lr (s U + wd W) along the rows
 #pragma unroll
