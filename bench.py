@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2xl")
     ap.add_argument("--layers", type=int, default=0, help="layers of the matrix set (default: all)")
+    ap.add_argument("--norm", choices=["sign", "col_l2"], default="sign",
+                    help="normalisation of the coefficients: sign (Dobb) or column-l2 (Dobb-l2, Tables 11-12)")
+    ap.add_argument("--orth-iters", type=int, default=1, help="orthogonal-iteration steps per refresh (Table 15)")
     ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
                     help="per-kernel MFMA utilisation and issued MFMA flops from a rocprofv3 --pmc run of "
                          "MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 MfmaFlopsF32")
@@ -83,7 +86,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
+def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1):
     """Per-step work of each kernel of the path, summed over the matrix set.
 
     Per kernel: algorithmic HBM bytes (each operand read or written once), algorithmic flops with the
@@ -103,6 +106,12 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
       project_bf16x6        nb > 416 (staged kernels): same bytes and flops, issued as six bf16 products
       reconstruct_f16x2     sign bytes read, W read + written: (1 + 2 w) m n bytes;
                             2 m n nb flops (fp32 contraction), issued as two fp16 products
+    Column-l2 normalisation (norm="col_l2") takes the plain fp32 kernels instead of the last four:
+      momentum              G read, M read + written: (8 + g) m n bytes
+      project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
+      colnorm               C read: 4 m n bytes
+      reconstruct           C read, W read + written: (4 + 2 w) m n bytes; 2 m n nb fp32 MFMA flops
+    The refresh kernels run orth_iters times per refresh.
     """
     w = {}
 
@@ -117,13 +126,20 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4):
         syrk = "accumulate_syrk_wide" if 128 < nb <= 512 and nb % 8 == 0 else "accumulate_syrk_bf16"
         add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
         add("accumulate_reduce", 8.0 * nb * nb * B)
-        add("refresh_gemm", 12.0 * nb * nb * B, 2.0 * nb ** 3 * B)
+        k = orth_iters
+        add("refresh_gemm", k * 12.0 * nb * nb * B, k * 2.0 * nb ** 3 * B)
         if nb <= QR_SINGLE_LAUNCH_MAX_NB:
-            add("qr_block", 0.0, 8.0 / 3.0 * nb ** 3 * B)
+            add("qr_block", 0.0, k * 8.0 / 3.0 * nb ** 3 * B)
         else:
-            add("qr_update", 0.0, 4.0 / 3.0 * nb ** 3 * B)
-            add("qr_form", 0.0, 4.0 / 3.0 * nb ** 3 * B)
-            add("qr_panel", 0.0, QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
+            add("qr_update", 0.0, k * 4.0 / 3.0 * nb ** 3 * B)
+            add("qr_form", 0.0, k * 4.0 / 3.0 * nb ** 3 * B)
+            add("qr_panel", 0.0, k * QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
+        if norm == "col_l2":
+            add("momentum", (8.0 + g_bytes) * mn)
+            add("project", 8.0 * mn, 2.0 * mn * nb)
+            add("colnorm", 4.0 * mn)
+            add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
+            continue
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)
         if nb <= 416:
@@ -259,7 +275,7 @@ def mfma_summary(counter_csv):
               f"{avg('MfmaFlopsBF16'):.4g} | {avg('MfmaFlopsF16'):.4g} | {avg('MfmaFlopsF32'):.4g} |")
 
 
-def cpu_baseline(group, xs, specs, wl, layers):
+def cpu_baseline(group, xs, specs, wl, layers, col_l2=False, k_orth=1):
     """Time the oracle (one thread) on layer 0's weights: the step on 1/cpu_rows of each weight's rows,
     the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on 8 blocks of each
     weight; scale linearly to the full set (every term is linear in rows, tokens, blocks and layers)."""
@@ -278,11 +294,11 @@ def cpu_baseline(group, xs, specs, wl, layers):
         A = group.A[i][:nblk_s].cpu()
         Qp = group.Q[i][:nblk_s].cpu()
         t0 = time.perf_counter()
-        oracle.step(W, G, M, Q, s.nb, 2.5e-3, 0.1, 0.9, 0.2)
+        oracle.step(W, G, M, Q, s.nb, 2.5e-3, 0.1, 0.9, 0.2, norm=oracle.NORM_COL_L2 if col_l2 else oracle.NORM_SIGN)
         t1 = time.perf_counter()
         oracle.accumulate(X, s.nb)
         t2 = time.perf_counter()
-        oracle.orth_iter(A, Qp, k=1, cores=1)
+        oracle.orth_iter(A, Qp, k=k_orth, cores=1)
         t3 = time.perf_counter()
         t_step += t1 - t0; t_acc += t2 - t1; t_ref += t3 - t2
         s_step += (t1 - t0) * (s.m / r)
@@ -351,8 +367,14 @@ def main():
     torch.cuda.synchronize()
     print("[bench] inputs ready", file=sys.stderr, flush=True)
 
+    col_l2 = args.norm == "col_l2"
+    # Table 9: the applied scale is tau sqrt(max(m, n)/m) on the sign update U, tau sqrt(max(m, n)) on
+    # the column-l2 one
+    scales = [0.2 * (max(s.m, s.n) / (1.0 if col_l2 else s.m)) ** 0.5 for s in specs]
     group = DobbGroup(Ws, [s.nb for s in specs], grads=Gs, n_tokens=n_tokens, lr=wl["lr"], weight_decay=0.1,
-                      momentum=0.9)
+                      momentum=0.9, norm=dobb.DOBB_NORM_COL_L2 if col_l2 else dobb.DOBB_NORM_SIGN,
+                      update_scales=scales)
+    K_ORTH = args.orth_iters
     beta = 0.9
     # setup: first capture and the exact refresh (untimed, but measured once)
     group.accumulate(xs, 0.0)
@@ -367,7 +389,7 @@ def main():
 
     def full_step():
         group.accumulate(xs, beta)
-        group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, 1)
+        group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH)
         group.step()
 
     for _ in range(args.warmup):
@@ -405,14 +427,14 @@ def main():
     full_ms_untimed = timed(full_step, reps)
     step_ms = timed(group.step, reps)
     acc_ms = timed(lambda: group.accumulate(xs, beta), reps)
-    ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, 1), reps)
+    ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH), reps)
     # the exact refresh warm-started from the current basis (the exact mode's steady state)
     warm_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=True), 1)
 
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
     w_bytes = Ws[0].element_size()
-    work = kernel_work(specs, n_tokens, g_bytes, w_bytes)
+    work = kernel_work(specs, n_tokens, g_bytes, w_bytes, args.norm, K_ORTH)
     per_kernel = {}
     for name, (launches, total_ms) in kernels.items():
         ent = {"launches_per_step": launches / args.steps, "ms_per_step": round(total_ms / args.steps, 4),
@@ -428,7 +450,8 @@ def main():
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"],
                 "frac": d["frac"],
                 # counters were taken on the full GPT-2 XL set only
-                "traffic": measured_traffic(dom) if args.workload == "gpt2xl" and layers == 48 else None,
+                "traffic": (measured_traffic(dom) if args.workload == "gpt2xl" and layers == 48
+                            and args.norm == "sign" and K_ORTH == 1 else None),
                 "work_per_launch": unit_work / launches,
                 "work_unit": "bytes" if d["bound"] == "hbm" else "flop",
                 "avg_launch_ms": d["avg_launch_ms"], "launches_per_step": launches}
@@ -436,21 +459,22 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(group, xs, specs, wl, layers)
+        cpu = cpu_baseline(group, xs, specs, wl, layers, col_l2, K_ORTH)
 
     amort = lambda T: (full_ms_untimed + (T - 1) * step_ms) / T
     out = {
         "metric": METRIC, "value": round(ms_per_step, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": wl["text"].format(L=layers, N=n_tokens) + "; capture + orthogonal-iteration "
-                               "refresh (k=1) + step every step",
+        "config": {"workload": wl["text"].format(L=layers, N=n_tokens) + f"; capture + orthogonal-iteration "
+                               f"refresh (k={K_ORTH}) + step every step"
+                               + ("; column-l2 normalisation" if col_l2 else ""),
                    "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
                    "refresh_period": 1},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown_ms": {"full_step_untimed": round(full_ms_untimed, 3), "step_nonrefresh": round(step_ms, 3),
-                         "accumulate": round(acc_ms, 3), "refresh_orth_iter_k1": round(ref_ms, 3),
+                         "accumulate": round(acc_ms, 3), f"refresh_orth_iter_k{K_ORTH}": round(ref_ms, 3),
                          "refresh_exact_cold": round(exact_ms, 1), "refresh_exact_warm": round(warm_ms, 1),
                          "amortized_T10": round(amort(10), 3),
                          "amortized_T9": round(amort(9), 3)},
