@@ -126,11 +126,14 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
         const double sg = x0 >= 0.0 ? 1.0 : -1.0;
         const double tc = alpha == 0.0 ? 0.0 : 1.0 + fabs(x0) / alpha;
         const float inv = alpha == 0.0 ? 1.f : (float)(1.0 / (x0 + sg * alpha));
-        // column c-1 of T: its Gram entries and tau became visible at the barrier above
-        if (c >= 1 && grp == 0 && k < c - 1) {
-            double sum = 0.0;
-            for (int l = k; l < c - 1; ++l) sum += S.Td[k][l] * S.Gs[l][c - 1];
-            S.Td[k][c - 1] = -S.tau[c - 1] * sum;
+        // column c-1 of T: its Gram entries and tau became visible at the barrier above.  Entry
+        // (k, c-1) is a sum over l = k .. c-2, split over the column's 8 threads (l = k + grp + 8 i)
+        if (c >= 2) {   // uniform: every lane takes part in the shuffles
+            double part = 0.0;
+            if (k < c - 1)
+                for (int l = k + grp; l < c - 1; l += 8) part += S.Td[k][l] * S.Gs[l][c - 1];
+            const double sum = col_sum(part);
+            if (grp == 0 && k < c - 1) S.Td[k][c - 1] = -S.tau[c - 1] * sum;
         }
         // v^T P_k = inv (x^T P_k) on this thread's rows, summed over the column's 8 threads
         float x[RPT];
@@ -162,10 +165,12 @@ __device__ __forceinline__ void factor_panel(float (&P)[RPT], int w, int rows, i
         }
     }
     __syncthreads();
-    if (w >= 2 && grp == 0 && k < w - 1) {
-        double sum = 0.0;
-        for (int l = k; l < w - 1; ++l) sum += S.Td[k][l] * S.Gs[l][w - 1];
-        S.Td[k][w - 1] = -S.tau[w - 1] * sum;
+    if (w >= 2) {
+        double part = 0.0;
+        if (k < w - 1)
+            for (int l = k + grp; l < w - 1; l += 8) part += S.Td[k][l] * S.Gs[l][w - 1];
+        const double sum = col_sum(part);
+        if (grp == 0 && k < w - 1) S.Td[k][w - 1] = -S.tau[w - 1] * sum;
     }
 }
 
