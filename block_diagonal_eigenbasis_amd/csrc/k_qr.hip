@@ -72,11 +72,21 @@ __device__ inline PanelPtrs panel_ptrs(unsigned char *dsm, const PanelLds &L) {
                      (double *)(dsm + L.red), (double(*)[kPW])(dsm + L.part), (double *)(dsm + L.tau)};
 }
 
-// sum over the 8 lanes of a column (lanes 8 k .. 8 k + 7 of a wave)
+// v from lane l's partner under a DPP lane pattern (both 32-bit halves moved)
+template <int CTRL>
+__device__ __forceinline__ double dpp_double(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// sum over the 8 lanes of a column (lanes 8 k .. 8 k + 7 of a wave), in registers: the quad's
+// partners by quad_perm [1,0,3,2] and [2,3,0,1], then the other quad of the 8 by row_half_mirror
+// (lane i of a half-row of 8 takes lane 7 - i)
 __device__ __forceinline__ double col_sum(double v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
+    v += dpp_double<0xB1>(v);
+    v += dpp_double<0x4E>(v);
+    v += dpp_double<0x141>(v);
     return v;
 }
 
