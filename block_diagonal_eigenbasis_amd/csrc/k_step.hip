@@ -9,7 +9,7 @@
 // Kernels (one launch each per group of equally shaped matrices):
 //   k_momentum     M <- mu M + G                           HBM-bound elementwise pass
 //   k_project      C_b = P_b Q_b, S = sign(C) as int8     fp32 MFMA 32x32x2, K = nb
-//   k_colnorm      colscale_j = 1/||C[:, j]||             (column-l2 variant only)
+//   k_colnorm      colscale_j = 1/||C[:, j]||             (column-l2 variant only; 16 row groups per column)
 //   k_reconstruct  U_b = S_b Q_b^T, W <- W - lr (s U + wd W)   fp32 MFMA, K = nb
 #include "dobb_internal.h"
 
@@ -132,18 +132,30 @@ struct ColTable {
     float *cs[kMaxMats];
 };
 
-// colscale_j = 1 / ||C[:, j]||_2 (0 for a zero column), summed in fp64 in row order
-__global__ void __launch_bounds__(256) k_colnorm(int64_t m, int64_t n, ColTable t) {
+// colscale_j = 1 / ||C[:, j]||_2 (0 for a zero column), summed in fp64.  grid = (ceil(n / 64), matrices),
+// block 1024: thread (g, c) sums column 64 blockIdx.x + c over rows g, g + 16, ... (64 consecutive
+// columns per row: 256-byte reads), then the 16 partial sums are added in g order (deterministic).
+constexpr int kCnCols = 64, kCnGroups = 16;
+__global__ void __launch_bounds__(kCnCols * kCnGroups) k_colnorm(int64_t m, int64_t n, ColTable t) {
+    __shared__ double part[kCnGroups][kCnCols];
     const int mat = blockIdx.y;
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= n) return;
+    const int c = threadIdx.x % kCnCols, g = threadIdx.x / kCnCols;
+    const int64_t j = (int64_t)blockIdx.x * kCnCols + c;
     const float *C = t.C[mat];
     double s = 0.0;
-    for (int64_t r = 0; r < m; ++r) {
-        double v = C[r * n + j];
-        s += v * v;
+    if (j < n)
+        for (int64_t r = g; r < m; r += kCnGroups) {
+            const double v = C[r * n + j];
+            s += v * v;
+        }
+    part[g][c] = s;
+    __syncthreads();
+    if (g == 0 && j < n) {
+        double tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kCnGroups; ++q) tot += part[q][c];
+        t.cs[mat][j] = tot > 0.0 ? (float)(1.0 / sqrt(tot)) : 0.f;
     }
-    t.cs[mat][j] = s > 0.0 ? (float)(1.0 / sqrt(s)) : 0.f;
 }
 
 struct ReconTable {
@@ -315,8 +327,8 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
         if (norm == DOBB_NORM_COL_L2) {
             ColTable t{};
             for (int i = 0; i < cnt; ++i) { t.C[i] = a.C[c0 + i]; t.cs[i] = a.colscale[c0 + i]; }
-            dim3 grid((unsigned)((n + 255) / 256), cnt);
-            DOBB_LAUNCH("colnorm", s, k_colnorm, grid, dim3(256), 0, m, n, t);
+            dim3 grid((unsigned)((n + kCnCols - 1) / kCnCols), cnt);
+            DOBB_LAUNCH("colnorm", s, k_colnorm, grid, dim3(kCnCols * kCnGroups), 0, m, n, t);
         }
         // reconstruction + parameter update
         {
