@@ -111,6 +111,7 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
       colnorm               C read: 4 m n bytes
       reconstruct           C read, W read + written: (4 + 2 w) m n bytes; 2 m n nb fp32 MFMA flops
+      reconstruct_l2_f16x3  the same for nb <= 128 (nb % 4 == 0), issued as three fp16 products
     The refresh kernels run orth_iters times per refresh.
     """
     w = {}
@@ -138,7 +139,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
             add("momentum", (8.0 + g_bytes) * mn)
             add("project", 8.0 * mn, 2.0 * mn * nb)
             add("colnorm", 4.0 * mn)
-            add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
+            if nb <= STEP_ROWS_MAX_NB and nb % 4 == 0 and s.n % 4 == 0:
+                add("reconstruct_l2_f16x3", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+            else:
+                add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
             continue
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)

@@ -178,6 +178,9 @@ hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s);
 // nb <= 128: the same arithmetic with each block's basis resident in LDS and row tiles staged
 // through LDS (k_step_rows.hip)
 bool step_rows_eligible(const dobb_shape &sh);
+// column-l2 reconstruction for nb <= 128 (nb % 4 == 0) from C and the column scales, split fp16 products
+bool recon_l2_rows_eligible(const dobb_shape &sh);
+hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s);
 // 128 < nb <= 512: basis streamed in k-slices from slice-major planes, row tiles staged in LDS
 bool step_wide_eligible(const dobb_shape &sh);
 size_t step_wide_planes_bytes(const dobb_shape &sh);

@@ -330,8 +330,11 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
             dim3 grid((unsigned)((n + kCnCols - 1) / kCnCols), cnt);
             DOBB_LAUNCH("colnorm", s, k_colnorm, grid, dim3(kCnCols * kCnGroups), 0, m, n, t);
         }
-        // reconstruction + parameter update
-        {
+        // reconstruction + parameter update (column-l2 with nb <= 128: the split-fp16 rows kernel)
+        if (norm == DOBB_NORM_COL_L2 && recon_l2_rows_eligible(a.sh)) {
+            const hipError_t e = launch_recon_l2_rows(a, c0, cnt, s);
+            if (e != hipSuccess) return e;
+        } else {
             ReconTable t{};
             bool vec = (n % 4 == 0) && (nb % 4 == 0);
             for (int i = 0; i < cnt; ++i) {

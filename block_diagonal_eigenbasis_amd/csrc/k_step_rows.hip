@@ -255,6 +255,8 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
 // ---- reconstruction ------------------------------------------------------------------------------
 struct ReconRowsTable {
     const uint8_t *S[kMaxMats];
+    const float *C[kMaxMats];    // column-l2: the coefficients C (m x n fp32) and the column scales
+    const float *cs[kMaxMats];
     const float *Q[kMaxMats];
     void *W[kMaxMats];
     float *U[kMaxMats];
@@ -264,13 +266,22 @@ struct ReconRowsTable {
 // banks).  The tile holds every k the products read, zero past nb (zero times the basis' zero
 // padding: a stale byte there could decode to an infinite fp16 value and give NaN).
 __host__ __device__ inline int rows_spitch(int nb) { return rows_geo(nb).kpad + 8; }
-__host__ __device__ inline size_t recon_rows_lds(int nb, int TR, int ldp) {
+// column-l2: the tile of scaled coefficients, fp32 with pitch kpad + 4 ((pitch / 4) odd), then the
+// block's kpad column scales (zero past nb)
+__host__ __device__ inline int rows_cpitch(int nb) { return rows_geo(nb).kpad + 4; }
+__host__ __device__ inline size_t recon_rows_tile(int nb, int TR, bool l2) {
+    return l2 ? a16((size_t)TR * rows_cpitch(nb) * 4 + (size_t)rows_geo(nb).kpad * 4) : a16((size_t)TR * rows_spitch(nb));
+}
+__host__ __device__ inline size_t recon_rows_lds(int nb, int TR, int ldp, bool l2 = false) {
     const RowsGeo g = rows_geo(nb);
     (void)ldp;
-    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * rows_spitch(nb)) + a16((size_t)TR * g.uld * 4);
+    return a16((size_t)2 * nb * g.qld * 2) + recon_rows_tile(nb, TR, l2) + a16((size_t)TR * g.uld * 4);
 }
 
-template <int NCH, int TR, bool WBF16>
+// L2: column-l2 normalisation (Dobb-l2): the tile holds C~ = C diag(colscale) in fp32 instead of the
+// sign bytes; |C~| <= 1, so it splits into two fp16 parts without a scale and U = C~ Q^T takes three
+// products (hi hi, lo(Q) hi, hi lo(C~)).
+template <int NCH, int TR, bool WBF16, bool L2 = false>
 __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
                                                     int ldp, ReconRowsTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -279,7 +290,10 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
     const int spitch = rows_spitch(nb);
     uint8_t *ssb = lds + a16((size_t)2 * nb * qld * 2);                      // [TR][spitch]
-    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * spitch));   // [TR][uld]
+    const int cpitch = rows_cpitch(nb);
+    float *ct = (float *)ssb;                                                // L2: [TR][cpitch]
+    float *csl = ct + TR * cpitch;                                           // L2: [kpad]
+    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + recon_rows_tile(nb, TR, L2));   // [TR][uld]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -315,7 +329,17 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
         }
     }
 
+    if constexpr (L2) {
+        // the block's column scales, and zero tile columns [nb, kpad) (the staging writes c < nb only)
+        for (int c = tid; c < kpad; c += kRT) csl[c] = c < nb ? t.cs[mat][(int64_t)b * nb + c] : 0.f;
+        for (int e = tid; e < TR * (kpad - nb); e += kRT) {
+            const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
+            ct[r * cpitch + c] = 0.f;
+        }
+        __syncthreads();
+    }
     const uint8_t *S = t.S[mat] + (int64_t)b * ldp;
+    const float *Cm = L2 ? t.C[mat] : nullptr;
     const int64_t sld = (int64_t)nblk * ldp;
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
     void *const Wv = t.W[mat];
@@ -325,9 +349,21 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     constexpr int kSPT = (TR * 16 + kRT - 1) / kRT;   // sign pieces per thread (kpad <= 128)
     constexpr int kWPT = (TR * 32 + kRT - 1) / kRT;   // W pieces per thread (nb <= 128)
     using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
-    uint2 sr[kSPT];
+    uint2 sr[L2 ? 1 : kSPT];
+    f32x4 cr[L2 ? kWPT : 1];
     WVec wr[kWPT];
     auto load_tile = [&](int64_t tile) {
+        if constexpr (L2) {
+#pragma unroll
+            for (int i = 0; i < kWPT; ++i) {
+                const int e = tid + kRT * i;
+                const int r = e / q, c = 4 * (e - r * q);
+                const int64_t row = tile * TR + r;
+                cr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (tile < t_end && e < TR * q && row < m)
+                    cr[i] = *(const f32x4 *)(Cm + row * n + (int64_t)b * nb + c);
+            }
+        } else {
 #pragma unroll
         for (int i = 0; i < kSPT; ++i) {
             const int e = tid + kRT * i;
@@ -340,6 +376,7 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
                 sr[i] = *(const uint2 *)(S + row * sld + c);
                 if (c + 4 >= nb) sr[i].y = 0u;
             }
+        }
         }
 #pragma unroll
         for (int i = 0; i < kWPT; ++i) {
@@ -360,11 +397,24 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     load_tile(t_begin);
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
         uint8_t *sc_ = ssb;
+        if constexpr (L2) {
+#pragma unroll
+            for (int i = 0; i < kWPT; ++i) {
+                const int e = tid + kRT * i;
+                const int r = e / q, c = 4 * (e - r * q);
+                if (e < TR * q) {
+                    const f32x4 sv = *(const f32x4 *)(csl + c);
+                    *(f32x4 *)(ct + r * cpitch + c) =
+                        f32x4{cr[i][0] * sv[0], cr[i][1] * sv[1], cr[i][2] * sv[2], cr[i][3] * sv[3]};
+                }
+            }
+        } else {
 #pragma unroll
         for (int i = 0; i < kSPT; ++i) {
             const int e = tid + kRT * i;
             const int r = e / q8, c = 8 * (e - r * q8);
             if (e < TR * q8) *(uint2 *)(sc_ + r * spitch + c) = sr[i];
+        }
         }
         WVec wcur[kWPT];
 #pragma unroll
@@ -376,9 +426,23 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
 #pragma unroll
         for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
         for (int ks = 0; ks < KS; ++ks) {
-            const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * spitch + ks * kKS + kh);
-            const uint4 av = {signs_f16x2<0>(sv.x), signs_f16x2<1>(sv.x), signs_f16x2<0>(sv.y), signs_f16x2<1>(sv.y)};
-            const f16x8 as = __builtin_bit_cast(f16x8, av);
+            f16x8 as, al;
+            if constexpr (L2) {
+                const float *cp = ct + (32 * rt + (lane & 31)) * cpitch + ks * kKS + kh;
+                const f32x4 c0 = *(const f32x4 *)cp, c1 = *(const f32x4 *)(cp + 4);
+                uint16_t hh[8], hl[8];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    split2h(c0[cc], hh[cc], hl[cc]);
+                    split2h(c1[cc], hh[cc + 4], hl[cc + 4]);
+                }
+                as = __builtin_bit_cast(f16x8, uint4{pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])});
+                al = __builtin_bit_cast(f16x8, uint4{pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])});
+            } else {
+                const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * spitch + ks * kKS + kh);
+                const uint4 av = {signs_f16x2<0>(sv.x), signs_f16x2<1>(sv.x), signs_f16x2<0>(sv.y), signs_f16x2<1>(sv.y)};
+                as = __builtin_bit_cast(f16x8, av);
+            }
             f16x8 Bh[kCPG], Bl[kCPG];
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) {
@@ -396,6 +460,10 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], as, acc[j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bl[j], as, acc[j], 0, 0, 0);
+            if constexpr (L2) {
+#pragma unroll
+                for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], al, acc[j], 0, 0, 0);
+            }
         }
         // U tile -> LDS: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t
 #pragma unroll
@@ -496,6 +564,39 @@ hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream
     return hipGetLastError();
 }
 
+// Column-l2 reconstruction (C and the column scales already in the workspace), 64-row tiles.
+template <int NCH>
+hipError_t launch_recon_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    constexpr int TR = 64;
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const int64_t ntile = (m + TR - 1) / TR;
+    const int64_t blocks = (int64_t)nblk * cnt;
+    int64_t tpg = (ntile * blocks + 1023) / 1024;
+    if (tpg < 4) tpg = 4;
+    if (tpg > ntile) tpg = ntile;
+    const int ngroups = (int)((ntile + tpg - 1) / tpg);
+    const dim3 grid((unsigned)(ngroups * blocks));
+    ReconRowsTable t{};
+    for (int i = 0; i < cnt; ++i) {
+        const dobb_hparams &h = a.hp[c0 + i];
+        t.C[i] = a.C[c0 + i]; t.cs[i] = a.colscale[c0 + i]; t.Q[i] = a.Q[c0 + i]; t.W[i] = a.W[c0 + i];
+        t.U[i] = a.U ? a.U[c0 + i] : nullptr;
+        t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
+    }
+    const size_t sh = recon_rows_lds(nb, TR, 0, true);
+#define DOBB_RL2(WB)                                                                                             \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_recon_rows<NCH, TR, WB, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("reconstruct_l2_f16x3", s, (k_recon_rows<NCH, TR, WB, true>), grid, dim3(kRT), sh, m, n, nb, nblk,  \
+                    ngroups, (int)tpg, 0, t);                                                                    \
+    } while (0)
+    if (a.w_dtype == DOBB_BF16) DOBB_RL2(true); else DOBB_RL2(false);
+#undef DOBB_RL2
+    return hipGetLastError();
+}
+
 template <int NCH>
 hipError_t launch_rows(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
     const int nb = (int)a.sh.nb;
@@ -507,6 +608,19 @@ hipError_t launch_rows(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t 
 }  // namespace
 
 bool step_rows_eligible(const dobb_shape &sh) { return sh.nb <= 128; }
+
+bool recon_l2_rows_eligible(const dobb_shape &sh) {
+    return sh.nb <= 128 && sh.nb % 4 == 0 && sh.n % 4 == 0 &&
+           (int64_t)recon_rows_lds((int)sh.nb, 64, 0, true) <= max_lds_bytes();
+}
+
+hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    const int nct = (int)((a.sh.nb + 31) / 32);
+    if (nct <= 1) return launch_recon_l2_cfg<1>(a, c0, cnt, s);
+    if (nct <= 2) return launch_recon_l2_cfg<2>(a, c0, cnt, s);
+    if (nct <= 3) return launch_recon_l2_cfg<3>(a, c0, cnt, s);
+    return launch_recon_l2_cfg<4>(a, c0, cnt, s);
+}
 
 hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s) {
     const int nct = (int)((a.sh.nb + 31) / 32);

@@ -324,6 +324,24 @@ def test_step_nesterov_and_column_l2():
     np.testing.assert_allclose(host(W_l), W_r, rtol=1e-6, atol=1e-9)
 
 
+@pytest.mark.parametrize("m,n,nb,wdt", [(300, 400, 100, torch.float32), (130, 96, 48, torch.float32),
+                                        (200, 256, 128, torch.bfloat16), (70, 60, 20, torch.float32),
+                                        (64, 90, 30, torch.float32), (100, 800, 400, torch.float32)])
+def test_step_column_l2(m, n, nb, wdt):
+    """Column-l2 normalisation (Tables 11-12): U_b = C_b diag(1/||c_j||) Q_b^T with the column norms
+    over all m rows.  nb <= 128 with nb % 4 == 0 reconstructs with split fp16 products (|C~| <= 1),
+    the others with fp32 products; both to 1e-5 relative Frobenius of U and one fp32 update of W."""
+    print(f"step column-l2 m={m} n={n} nb={nb} {wdt}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=m + 3 * nb, w_dtype=wdt)
+    W_l, M_l, U_l = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_COL_L2)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"], norm=oracle.NORM_COL_L2)
+    _check_momentum(M_l, M, G, hp["momentum"], M_r)
+    U_g = host(U_l)
+    assert np.linalg.norm(U_g - U_r) <= 1e-5 * np.linalg.norm(U_r)
+    check_w(host(W_l), host(W), U_g, hp, bf16=wdt == torch.bfloat16)
+
+
 @pytest.mark.parametrize("m,n,nb", [(96, 128, 64), (140, 400, 200)])
 def test_step_sign_nesterov(m, n, nb):
     """Nesterov (Table 19) through the sign path: P = G + mu (mu M + G) is what gets projected."""
