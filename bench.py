@@ -111,7 +111,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
       colnorm               C read: 4 m n bytes
       reconstruct           C read, W read + written: (4 + 2 w) m n bytes; 2 m n nb fp32 MFMA flops
-      reconstruct_l2_f16x3  the same for nb <= 128 (nb % 4 == 0), issued as three fp16 products
+      for nb <= 128 (nb % 4 == 0) the split-fp16 rows kernels instead:
+      project_l2_f16x3      M read + written, G read, C written: (12 + g) m n bytes; three fp16 products
+      colscale              the tiles' column sums of squares read: 8 ceil(m / 128) n bytes
+      reconstruct_l2_f16x3  C read, W read + written: (4 + 2 w) m n bytes; three fp16 products
     The refresh kernels run orth_iters times per refresh.
     """
     w = {}
@@ -136,12 +139,14 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
             add("qr_form", 0.0, k * 4.0 / 3.0 * nb ** 3 * B)
             add("qr_panel", 0.0, k * QR_PANEL * nb * nb * B, PEAK_FP32_VALU, compute="alu")
         if norm == "col_l2":
-            add("momentum", (8.0 + g_bytes) * mn)
-            add("project", 8.0 * mn, 2.0 * mn * nb)
-            add("colnorm", 4.0 * mn)
             if nb <= STEP_ROWS_MAX_NB and nb % 4 == 0 and s.n % 4 == 0:
+                add("project_l2_f16x3", (12.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+                add("colscale", 8.0 * -(-s.m // 128) * s.n)
                 add("reconstruct_l2_f16x3", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
             else:
+                add("momentum", (8.0 + g_bytes) * mn)
+                add("project", 8.0 * mn, 2.0 * mn * nb)
+                add("colnorm", 4.0 * mn)
                 add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
             continue
         if nb > STEP_ROWS_MAX_NB:

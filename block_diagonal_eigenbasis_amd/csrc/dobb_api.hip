@@ -119,7 +119,10 @@ size_t step_ws_one(const dobb_shape &sh, int norm) {
     if (step_bf16_eligible(sh, norm)) return step_bf16_ws_one(sh);
     const size_t mn = (size_t)sh.m * (size_t)sh.n;
     if (norm == DOBB_NORM_SIGN) return al256(mn);                 // int8 sign codes
-    return al256(mn * 4) + al256((size_t)sh.n * 4);               // fp32 coefficients + column scales
+    size_t b = al256(mn * 4) + al256((size_t)sh.n * 4);           // fp32 coefficients + column scales
+    if (norm == DOBB_NORM_COL_L2)                                 // column sums of squares per 128-row tile
+        b += al256((size_t)((sh.m + 127) / 128) * (size_t)sh.n * 8);
+    return b;
 }
 
 size_t group_ws(dobb_op op, const dobb_shape &sh, int cnt, int64_t N, int variant) {
@@ -298,6 +301,7 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
         const size_t per = step_ws_one(sh, norm);
         std::vector<const void *> gs;
         std::vector<float *> ms, us, cs, ps;
+        std::vector<double *> cps;
         std::vector<void *> ws_;
         std::vector<const float *> qs;
         std::vector<int8_t *> ss;
@@ -314,6 +318,9 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
             ss.push_back((int8_t *)reg);
             cs.push_back((float *)reg);
             ps.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + al256((size_t)sh.m * sh.n * 4)));
+            cps.push_back(norm == DOBB_NORM_COL_L2
+                              ? (double *)(reg + al256((size_t)sh.m * sh.n * 4) + al256((size_t)sh.n * 4))
+                              : nullptr);
             const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
             pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
             aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
@@ -333,6 +340,7 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
         a.S = ss.data();
         a.C = cs.data();
         a.colscale = ps.data();
+        a.colpart = cps.data();
         a.planes = pls.data();
         if (bf16 && aligned) {
             st = hip_status(launch_step_bf16(a, (hipStream_t)stream));

@@ -167,6 +167,7 @@ struct StepArgs {
     int8_t *const *S;                 // sign codes m x n
     float *const *C;                  // fp32 coefficients m x n (identity / column-l2 norms)
     float *const *colscale;           // n column scales (column-l2)
+    double *const *colpart;           // column-l2, nb <= 128: per 128-row tile, column sums of squares
     uint16_t *const *planes;          // bf16 planes of Q (bf16 path)
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
@@ -181,6 +182,9 @@ bool step_rows_eligible(const dobb_shape &sh);
 // column-l2 reconstruction for nb <= 128 (nb % 4 == 0) from C and the column scales, split fp16 products
 bool recon_l2_rows_eligible(const dobb_shape &sh);
 hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s);
+// column-l2 projection for the same shapes: momentum, C, the tiles' column sums of squares, the scales
+bool proj_l2_rows_eligible(const dobb_shape &sh);
+hipError_t launch_proj_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s);
 // 128 < nb <= 512: basis streamed in k-slices from slice-major planes, row tiles staged in LDS
 bool step_wide_eligible(const dobb_shape &sh);
 size_t step_wide_planes_bytes(const dobb_shape &sh);

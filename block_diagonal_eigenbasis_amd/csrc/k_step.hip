@@ -279,6 +279,21 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     for (int c0 = 0; c0 < a.count;) {
         // chunk: at most kMaxMats matrices, and blocks * matrices within grid.x limits
         int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
+        // column-l2 with nb <= 128: the split-fp16 rows kernels do momentum, projection, column norms
+        // and reconstruction
+        if (a.hp[c0].norm == DOBB_NORM_COL_L2 && a.colpart && proj_l2_rows_eligible(a.sh)) {
+            bool al = true;
+            for (int i = 0; i < cnt; ++i)
+                al = al && aligned16(a.M[c0 + i]) &&
+                     ((uintptr_t)a.G[c0 + i] & (a.g_dtype == DOBB_BF16 ? 7u : 15u)) == 0;
+            if (al) {
+                hipError_t e = launch_proj_l2_rows(a, c0, cnt, s);
+                if (e == hipSuccess) e = launch_recon_l2_rows(a, c0, cnt, s);
+                if (e != hipSuccess) return e;
+                c0 += cnt;
+                continue;
+            }
+        }
         // momentum
         {
             MomTable t{};

@@ -55,6 +55,8 @@ struct ProjRowsTable {
     const void *G[kMaxMats];
     const float *Q[kMaxMats];
     uint8_t *S[kMaxMats];
+    float *C[kMaxMats];        // column-l2: the coefficients (m x n fp32)
+    double *part[kMaxMats];    // column-l2: per row tile, the column sums of squares ([tiles][n])
     float mu[kMaxMats];
 };
 // LDS: Q_b^T (two fp16 planes), the P tile (fp32) and the sign tile
@@ -65,7 +67,9 @@ __host__ __device__ inline size_t proj_rows_lds(int nb, int TR, int ldp) {
 
 // grid.x = tile groups x blocks x matrices (block fastest, renumbered per XCD), block 512.
 // TR = 128 or 64 rows per tile; the 8 waves take (32-row tile rt, group cg of column chunks).
-template <int NCH, int TR, int NEST, bool GBF16>
+// L2: column-l2 normalisation (Dobb-l2): the epilogue writes C (unscaled by the row's power of two)
+// along the rows through the P tile's LDS, and each tile's column sums of squares in fp64.
+template <int NCH, int TR, int NEST, bool GBF16, bool L2 = false>
 __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
                                                    int ldp, ProjRowsTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -226,6 +230,43 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql[j], ah, acc[j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], al, acc[j], 0, 0, 0);
+        }
+        if constexpr (L2) {
+            // C tile -> the P tile's LDS (every wave is past its products), then rows out and the
+            // tile's column sums of squares (rows past m are zero)
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kCPG; ++j) {
+                const int ch = cg * kCPG + j;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;
+                    if (ch < NCH && col < nb)
+                        *(f32x4 *)(pc + (32 * rt + (lane & 31)) * pld + col) =
+                            f32x4{__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sexp),
+                                  __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sexp),
+                                  __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sexp),
+                                  __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sexp)};
+                }
+            }
+            __syncthreads();
+            float *Cb = t.C[mat] + (int64_t)b * nb;
+            for (int e = tid; e < TR * q; e += kRT) {
+                const int r = e / q, c = 4 * (e - r * q);
+                const int64_t row = tile * TR + r;
+                if (row < m) *(f32x4 *)(Cb + row * n + c) = *(const f32x4 *)(pc + r * pld + c);
+            }
+            if (tid < nb) {
+                double sq = 0.0;
+                const int rows = m - tile * TR < TR ? (int)(m - tile * TR) : TR;
+                for (int r = 0; r < rows; ++r) {
+                    const double v = pc[r * pld + tid];
+                    sq += v * v;
+                }
+                t.part[mat][tile * n + (int64_t)b * nb + tid] = sq;
+            }
+            __syncthreads();   // the next tile's staging overwrites the P tile
+            continue;
         }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t -> LDS
 #pragma unroll
@@ -564,6 +605,60 @@ hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream
     return hipGetLastError();
 }
 
+// column scales from the row tiles' sums of squares, added in tile order: cs_j = 1 / ||C[:, j]||
+// (0 for a zero column).  grid = (ceil(n / 256), matrices), block 256.
+struct ColScaleTable {
+    const double *part[kMaxMats];
+    float *cs[kMaxMats];
+};
+__global__ void __launch_bounds__(256) k_colscale(int64_t n, int64_t ntile, ColScaleTable t) {
+    const int mat = blockIdx.y;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    double s = 0.0;
+    for (int64_t tl = 0; tl < ntile; ++tl) s += t.part[mat][tl * n + j];
+    t.cs[mat][j] = s > 0.0 ? (float)(1.0 / sqrt(s)) : 0.f;
+}
+
+// Column-l2 projection: momentum, C = P Q (split fp16 products), C to the workspace with the tiles'
+// column sums of squares, then the column scales.  128-row tiles, one tile group per block.
+template <int NCH>
+hipError_t launch_proj_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    constexpr int TR = 128;
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const int64_t ntile = (m + TR - 1) / TR;
+    const int64_t blocks = (int64_t)nblk * cnt;
+    int64_t tpg = (ntile * blocks + 1023) / 1024;
+    if (tpg < 4) tpg = 4;
+    if (tpg > ntile) tpg = ntile;
+    const int ngroups = (int)((ntile + tpg - 1) / tpg);
+    const dim3 grid((unsigned)(ngroups * blocks));
+    ProjRowsTable t{};
+    for (int i = 0; i < cnt; ++i) {
+        t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
+        t.C[i] = a.C[c0 + i]; t.part[i] = a.colpart[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+    }
+    const int ldp = step_bf16_ldp(nb);
+    const size_t sh = proj_rows_lds(nb, TR, ldp);
+    const bool gbf = a.g_dtype == DOBB_BF16;
+    const bool nest = a.hp[c0].nesterov != 0;
+#define DOBB_PL2(NE, GB)                                                                                         \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_l2_f16x3", s, (k_proj_rows<NCH, TR, NE, GB, true>), grid, dim3(kRT), sh, m, n, nb, nblk,   \
+                    ngroups, (int)tpg, ldp, t);                                                                  \
+    } while (0)
+    if (!nest) { if (gbf) DOBB_PL2(0, true); else DOBB_PL2(0, false); }
+    else { if (gbf) DOBB_PL2(1, true); else DOBB_PL2(1, false); }
+#undef DOBB_PL2
+    ColScaleTable ct{};
+    for (int i = 0; i < cnt; ++i) { ct.part[i] = a.colpart[c0 + i]; ct.cs[i] = a.colscale[c0 + i]; }
+    DOBB_LAUNCH("colscale", s, k_colscale, dim3((unsigned)((n + 255) / 256), (unsigned)cnt), dim3(256), 0, n, ntile, ct);
+    return hipGetLastError();
+}
+
 // Column-l2 reconstruction (C and the column scales already in the workspace), 64-row tiles.
 template <int NCH>
 hipError_t launch_recon_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s) {
@@ -612,6 +707,19 @@ bool step_rows_eligible(const dobb_shape &sh) { return sh.nb <= 128; }
 bool recon_l2_rows_eligible(const dobb_shape &sh) {
     return sh.nb <= 128 && sh.nb % 4 == 0 && sh.n % 4 == 0 &&
            (int64_t)recon_rows_lds((int)sh.nb, 64, 0, true) <= max_lds_bytes();
+}
+
+bool proj_l2_rows_eligible(const dobb_shape &sh) {
+    return recon_l2_rows_eligible(sh) &&
+           (int64_t)proj_rows_lds((int)sh.nb, 128, step_bf16_ldp(sh.nb)) <= max_lds_bytes();
+}
+
+hipError_t launch_proj_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    const int nct = (int)((a.sh.nb + 31) / 32);
+    if (nct <= 1) return launch_proj_l2_cfg<1>(a, c0, cnt, s);
+    if (nct <= 2) return launch_proj_l2_cfg<2>(a, c0, cnt, s);
+    if (nct <= 3) return launch_proj_l2_cfg<3>(a, c0, cnt, s);
+    return launch_proj_l2_cfg<4>(a, c0, cnt, s);
 }
 
 hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s) {
