@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--norm", choices=["sign", "col_l2"], default="sign",
                     help="normalisation of the coefficients: sign (Dobb) or column-l2 (Dobb-l2, Tables 11-12)")
     ap.add_argument("--orth-iters", type=int, default=1, help="orthogonal-iteration steps per refresh (Table 15)")
+    ap.add_argument("--streams", type=int, choices=[1, 2], default=1,
+                    help="2: the weights with blocks of at most 128 columns and the wider ones on two streams in "
+                         "the timed region (kernels then share the GPU, so per-launch times are not each "
+                         "kernel's own)")
     ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
                     help="per-kernel MFMA utilisation and issued MFMA flops from a rocprofv3 --pmc run of "
                          "MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 MfmaFlopsF32")
@@ -382,7 +386,7 @@ def main():
     scales = [0.2 * (max(s.m, s.n) / (1.0 if col_l2 else s.m)) ** 0.5 for s in specs]
     group = DobbGroup(Ws, [s.nb for s in specs], grads=Gs, n_tokens=n_tokens, lr=wl["lr"], weight_decay=0.1,
                       momentum=0.9, norm=dobb.DOBB_NORM_COL_L2 if col_l2 else dobb.DOBB_NORM_SIGN,
-                      update_scales=scales)
+                      update_scales=scales, streams=args.streams)
     K_ORTH = args.orth_iters
     beta = 0.9
     # setup: first capture and the exact refresh (untimed, but measured once)
@@ -397,9 +401,7 @@ def main():
           file=sys.stderr, flush=True)
 
     def full_step():
-        group.accumulate(xs, beta)
-        group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH)
-        group.step()
+        group.refresh_step(xs, beta, dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH)
 
     for _ in range(args.warmup):
         full_step()
@@ -439,6 +441,11 @@ def main():
     ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH), reps)
     # the exact refresh warm-started from the current basis (the exact mode's steady state)
     warm_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=True), 1)
+    # the other schedule: one stream, or the narrow and the wide blocks on two overlapping streams
+    other = 3 - args.streams
+    group.set_streams(other)
+    other_ms = timed(full_step, reps)
+    group.set_streams(args.streams)
 
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
@@ -479,10 +486,12 @@ def main():
                                f"refresh (k={K_ORTH}) + step every step"
                                + ("; column-l2 normalisation" if col_l2 else ""),
                    "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
-                   "refresh_period": 1},
+                   "refresh_period": 1, "streams": args.streams},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "breakdown_ms": {"full_step_untimed": round(full_ms_untimed, 3), "step_nonrefresh": round(step_ms, 3),
+        "breakdown_ms": {"full_step_untimed": round(full_ms_untimed, 3),
+                         f"full_step_{other}_stream{'s' if other > 1 else ''}": round(other_ms, 3),
+                         "step_nonrefresh": round(step_ms, 3),
                          "accumulate": round(acc_ms, 3), f"refresh_orth_iter_k{K_ORTH}": round(ref_ms, 3),
                          "refresh_exact_cold": round(exact_ms, 1), "refresh_exact_warm": round(warm_ms, 1),
                          "amortized_T10": round(amort(10), 3),

@@ -1,0 +1,139 @@
+"""The optimizer layer over libdobb.so against the entry points it drives (MI355X only).
+
+* DobbGroup with streams=2 runs the weights whose blocks have at most 128 columns and the wider ones
+  on two streams; its fused refresh_step must leave W, M, A and Q bit for bit where the one-stream
+  accumulate -> refresh -> step sequence leaves them (every kernel is deterministic, and the grouped
+  forms equal the single calls, test_gpu_parity.py).
+* The torch.optim wrapper follows the cadence of the Dobb paper (Tables 14, 15 and 17: capture on
+  refresh iterations only, from the first micro-batch; an exact first refresh, warm-started orthogonal
+  iteration with k = 1 afterwards; the moment EMA starting from the first capture). The test replays
+  that cadence with the single-matrix entry points and compares bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workload
+
+pytestmark = pytest.mark.gpu
+dobb = pytest.importorskip("block_diagonal_eigenbasis_amd")
+from block_diagonal_eigenbasis_amd.optimizer import Dobb, DobbGroup, default_update_scale  # noqa: E402
+
+DEV = "cuda"
+RNG = np.random.default_rng
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def t32(x):
+    return torch.as_tensor(np.ascontiguousarray(x), dtype=torch.float32, device=DEV)
+
+
+SHAPES = [(96, 256, 64), (64, 512, 256), (128, 256, 128), (80, 400, 200), (48, 96, 48)]
+
+
+def test_two_streams_match_one_stream():
+    rng = RNG(91)
+    N = 512
+    Ws = [t32(0.02 * rng.standard_normal((m, n))) for m, n, _ in SHAPES]
+    Gs = [t32(rng.standard_normal((m, n))) for m, n, _ in SHAPES]
+    xs = [t32(workload.activations(N, n, 0.15, rng)).to(torch.bfloat16) for _, n, _ in SHAPES]
+    g1, g2 = [DobbGroup([w.clone() for w in Ws], [nb for _, _, nb in SHAPES], grads=Gs, n_tokens=N,
+                        weight_decay=0.1, momentum=0.9, streams=s) for s in (1, 2)]
+    assert len(g1._parts) == 1 and len(g2._parts) == 2
+    assert sorted(g2._parts[0].idx + g2._parts[1].idx) == list(range(len(SHAPES)))
+    for g in (g1, g2):
+        g.accumulate(xs, 0.0)
+        g.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=False)
+        g.step()
+    for it in range(3):
+        print(f"two streams: iteration {it}", flush=True)
+        g1.accumulate(xs, 0.9)
+        g1.refresh(dobb.DOBB_REFRESH_ORTH_ITER, 1)
+        g1.step()
+        g2.refresh_step(xs, 0.9, dobb.DOBB_REFRESH_ORTH_ITER, 1)
+    g2.set_streams(1)                                        # back to one part, the state kept
+    assert len(g2._parts) == 1
+    g1.step()
+    g2.step()
+    torch.cuda.synchronize()
+    for name in ("W", "M", "A", "Q"):
+        for i, (a, b) in enumerate(zip(getattr(g1, name), getattr(g2, name))):
+            assert torch.equal(a, b), f"{name}[{i}] differs"
+
+
+def test_refresh_step_grows_the_workspace_for_more_tokens():
+    rng = RNG(92)
+    shapes = SHAPES[:2]
+    Ws = [t32(0.02 * rng.standard_normal((m, n))) for m, n, _ in shapes]
+    Gs = [t32(rng.standard_normal((m, n))) for m, n, _ in shapes]
+    g = DobbGroup(Ws, [nb for _, _, nb in shapes], grads=Gs, n_tokens=16, streams=2)
+    As = [torch.zeros_like(a) for a in g.A]
+    xs = [t32(workload.activations(3000, n, 0.15, rng)) for _, n, _ in shapes]
+    g.refresh_step(xs, 0.0, dobb.DOBB_REFRESH_EXACT, 0, warm_start=False)
+    for x, A, (_, _, nb) in zip(xs, As, shapes):
+        dobb.dobb_accumulate_moment(x, A, nb)
+    torch.cuda.synchronize()
+    assert g.n_tokens == 3000
+    for a, b in zip(g.A, As):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("streams", [1, 2])
+def test_optimizer_cadence_matches_entry_points(streams):
+    rng = RNG(93)
+    dims = [(96, 256), (64, 512), (48, 128)]          # blocks=2: nb = 128, 256, 64
+    mods = [torch.nn.Linear(n, m, bias=False).to(DEV) for m, n in dims]
+    params = [mod.weight for mod in mods]
+    with torch.no_grad():
+        for p in params:
+            p.copy_(t32(0.02 * rng.standard_normal(tuple(p.shape))))
+    lr, wd, mu, T, beta = 2.5e-3, 0.1, 0.9, 2, 0.9
+    opt = Dobb(params, lr=lr, weight_decay=wd, momentum=mu, blocks=2, refresh_period=T, orth_iters=1, beta=beta,
+               streams=streams)
+    hooks = opt.attach_capture_hooks(mods)
+    nbs = [n // 2 for _, n in dims]
+    W_ref = [p.detach().clone() for p in params]
+    M_ref = [torch.zeros(m, n, device=DEV) for m, n in dims]
+    A_ref = [torch.zeros(n // nb, nb, nb, device=DEV) for (_, n), nb in zip(dims, nbs)]
+    Q_ref = [torch.eye(nb, device=DEV).expand(n // nb, nb, nb).contiguous() for (_, n), nb in zip(dims, nbs)]
+    hps = [dobb.make_hparams(lr, wd, mu, default_update_scale(m, n)) for m, n in dims]
+    refreshed = False
+    for t in range(5):
+        print(f"optimizer cadence: streams={streams} t={t}", flush=True)
+        captures = opt.wants_capture()
+        assert captures == (t % T == 0)
+        xs = [t32(workload.activations(256, n, 0.15, rng)) for _, n in dims]
+        with torch.no_grad():
+            for mod, x in zip(mods, xs):
+                mod(x)
+                mod(t32(rng.standard_normal(tuple(x.shape))))   # a second micro-batch: not captured
+        grads = [t32(rng.standard_normal((m, n))) for m, n in dims]
+        for p, g in zip(params, grads):
+            p.grad = g
+        opt.step()
+        if captures:
+            for i, nb in enumerate(nbs):
+                dobb.dobb_accumulate_moment(xs[i], A_ref[i], nb, beta if refreshed else 0.0)
+                if refreshed:
+                    dobb.dobb_refresh_basis(A_ref[i], Q_ref[i], dobb.DOBB_REFRESH_ORTH_ITER, iters=1, warm_start=True)
+                else:
+                    dobb.dobb_refresh_basis(A_ref[i], Q_ref[i], dobb.DOBB_REFRESH_EXACT, warm_start=False)
+            refreshed = True
+        for i, nb in enumerate(nbs):
+            dobb.dobb_step(W_ref[i], grads[i], M_ref[i], Q_ref[i], nb, hps[i])
+    torch.cuda.synchronize()
+    for h in hooks:
+        h.remove()
+    g = opt._group
+    for i in range(len(dims)):
+        assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
+        assert torch.equal(g.M[i], M_ref[i]), f"M[{i}]"
+        assert torch.equal(g.A[i], A_ref[i]), f"A[{i}]"
+        assert torch.equal(g.Q[i], Q_ref[i]), f"Q[{i}]"
