@@ -41,6 +41,8 @@ PEAK_HBM = 8.0e12            # B/s
 PEAK_BF16_MFMA = 2.5e15      # flop/s, bf16 and fp16
 PEAK_FP32_MFMA = 157.3e12    # flop/s
 PEAK_FP32_VALU = 157.3e12    # flop/s
+PEAK_FP64_VALU = 78.6e12     # flop/s
+JACOBI_KERNELS = ("jacobi_sweep", "jacobi_sweep_fp64", "jacobi_rotate_v")
 BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
@@ -161,6 +163,24 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
             add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
         add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
     return w
+
+
+def jacobi_entry(kernels, infos, nbs, total_ms):
+    """The exact refresh's rotation work against the fp64 vector peak (both Jacobi stages compute in
+    fp64; the first only stores its working matrix in fp32).  A rotation of the pair (p, q) combines
+    rows p, q and columns p, q of A (4 nb entries, 3 flops each) and columns p, q of V (2 nb entries):
+    18 nb flops; a sweep is nb (nb - 1) / 2 rotations, so 9 nb^2 (nb - 1) flops per block and sweep,
+    counted over the sweeps each block reports in info (those that rotated)."""
+    sweeps = [i.clamp(min=0).double() for i in infos]
+    flops = sum(9.0 * nb * nb * (nb - 1) * float(sw.sum()) for sw, nb in zip(sweeps, nbs))
+    jac_ms = sum(kernels.get(k, (0, 0.0))[1] for k in JACOBI_KERNELS)
+    rate = flops / (jac_ms / 1e3) if jac_ms > 0 else 0.0
+    n_blocks = sum(sw.numel() for sw in sweeps)
+    return {"ms": round(total_ms, 1), "jacobi_kernels_ms": round(jac_ms, 1),
+            "sweeps_mean": round(sum(float(sw.sum()) for sw in sweeps) / n_blocks, 2),
+            "sweeps_max": int(max(float(sw.max()) for sw in sweeps)),
+            "bound": "alu", "achieved": round(rate / 1e12, 4), "peak": PEAK_FP64_VALU / 1e12, "unit": "TFLOP/s",
+            "frac": round(rate / PEAK_FP64_VALU, 5), "flops": flops}
 
 
 def roofline_entry(work, seconds):
@@ -392,10 +412,16 @@ def main():
     # setup: first capture and the exact refresh (untimed, but measured once)
     group.accumulate(xs, 0.0)
     torch.cuda.synchronize()
+    nbs = [s.nb for s in specs]
+    dobb.dobb_profile_reset()
+    dobb.dobb_profile_enable(True)
     t0 = time.perf_counter()
     group.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=False)
     torch.cuda.synchronize()
     exact_ms = (time.perf_counter() - t0) * 1e3
+    dobb.dobb_profile_enable(False)
+    jac_cold = jacobi_entry(dobb.dobb_profile_read(), [i.cpu() for i in group.info], nbs, exact_ms)
+    dobb.dobb_profile_reset()
     info = torch.cat([i for i in group.info]).cpu()
     print(f"[bench] exact refresh {exact_ms:.1f} ms, sweeps min/max {int(info.min())}/{int(info.max())}",
           file=sys.stderr, flush=True)
@@ -440,7 +466,12 @@ def main():
     acc_ms = timed(lambda: group.accumulate(xs, beta), reps)
     ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH), reps)
     # the exact refresh warm-started from the current basis (the exact mode's steady state)
+    dobb.dobb_profile_reset()
+    dobb.dobb_profile_enable(True)
     warm_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=True), 1)
+    dobb.dobb_profile_enable(False)
+    jac_warm = jacobi_entry(dobb.dobb_profile_read(), [i.cpu() for i in group.info], nbs, warm_ms)
+    dobb.dobb_profile_reset()
     # the other schedule: one stream, or the narrow and the wide blocks on two overlapping streams
     other = 3 - args.streams
     group.set_streams(other)
@@ -497,6 +528,9 @@ def main():
                          "amortized_T10": round(amort(10), 3),
                          "amortized_T9": round(amort(9), 3)},
         "kernels": per_kernel,
+        # the exact refresh (setup from the identity, and warm-started from the current basis): the
+        # Jacobi kernels' rotation work against the fp64 vector peak
+        "refresh_exact": {"cold": jac_cold, "warm": jac_warm},
     }
     print(json.dumps(out))
 

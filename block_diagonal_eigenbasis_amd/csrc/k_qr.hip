@@ -580,6 +580,43 @@ __host__ __device__ inline ApplyLds form_lds(int nb) {
     L.total = o;
     return L;
 }
+// stage_v in two halves, so that a panel's V rows can be loaded while the previous panel's products
+// run: load_v_regs reads the rows (zeros past `rows` and past the panel width) into registers,
+// store_v_regs writes them to Vs (rows up to the next multiple of 32).  2 CH passes of NT / 8 rows.
+template <int CH, int NT>
+__device__ __forceinline__ void load_v_regs(f32x4 (&v)[2 * CH], const float *Z, int nb, int j0, int w, int rows,
+                                            int tid) {
+    const int c4 = 4 * (tid & 7), r0 = tid >> 3;
+    const bool vec = (nb & 3) == 0 && c4 + 4 <= w;
+    const float *Zp = Z + (int64_t)j0 * nb + j0;
+#pragma unroll
+    for (int i = 0; i < 2 * CH; ++i) {
+        const int r = r0 + (NT / 8) * i;
+        const bool ok = r < rows;
+        const float *src = Zp + (ok ? r : 0) * nb + c4;
+        if (vec) {
+            v[i] = *(const f32x4 *)src;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[i][q] = c4 + q < w ? src[q] : 0.f;
+        }
+        if (!ok) v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+template <int CH, int NT>
+__device__ __forceinline__ void store_v_regs(float (*Vs)[kPW + 1], const f32x4 (&v)[2 * CH], int rows, int tid) {
+    const int c4 = 4 * (tid & 7), r0 = tid >> 3;
+    const int rpad = (rows + 31) & ~31;
+#pragma unroll
+    for (int i = 0; i < 2 * CH; ++i) {
+        const int r = r0 + (NT / 8) * i;
+        if (r < rpad) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Vs[r][c4 + q] = v[i][q];
+        }
+    }
+}
+
 template <int CH>
 __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *Z_all, const float *Tq_all,
                                                  const int8_t *neg_all, QrBlockOut t, int info_value) {
@@ -613,18 +650,25 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
             x[ch][r] = (colok && row < re && row == ccl) ? 1.f : 0.f;
         }
     const int plast = (blockIdx.x * 64 + 63) / kPW < npanel - 1 ? (blockIdx.x * 64 + 63) / kPW : npanel - 1;
+    // panel p's V rows and T, loaded one panel ahead into registers
+    static_assert(2 * CH * (kFT / 8) >= 32 * kFP * CH, "the V passes cover the row parts");
+    f32x4 vpre[2 * CH];
+    float tpre[kPW * kPW / kFT];
+    auto fetch = [&](int p) {
+        const int j0 = p * kPW;
+        load_v_regs<CH, kFT>(vpre, Z, nb, j0, min(kPW, nb - j0), nb - j0, tid);
+        const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
+#pragma unroll
+        for (int i = 0; i < kPW * kPW / kFT; ++i) tpre[i] = Tq[tid + kFT * i];
+    };
+    fetch(plast);
     for (int p = plast; p >= 0; --p) {
-        const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
+        const int j0 = p * kPW, rows = nb - j0;
         __syncthreads();   // the last panel's readers of Vs, Ts and Wp are done
-        stage_v<CH, kFT>(Vs, Z, nb, j0, w, rows, tid);
-        {
-            const float *Tq = Tq_all + ((int64_t)g * npanel + p) * kPW * kPW;
-            float tv[kPW * kPW / kFT];
+        store_v_regs<CH, kFT>(Vs, vpre, rows, tid);
 #pragma unroll
-            for (int i = 0; i < kPW * kPW / kFT; ++i) tv[i] = Tq[tid + kFT * i];
-#pragma unroll
-            for (int i = 0; i < kPW * kPW / kFT; ++i) Ts[(tid + kFT * i) / kPW][(tid + kFT * i) % kPW] = tv[i];
-        }
+        for (int i = 0; i < kPW * kPW / kFT; ++i) Ts[(tid + kFT * i) / kPW][(tid + kFT * i) % kPW] = tpre[i];
+        if (p > 0) fetch(p - 1);
         __syncthreads();
         // W partial = V^T X over this wave's chunks at rows >= j0 (chunks are 32-aligned, as is j0)
         f32x16 acc = {};
