@@ -81,6 +81,9 @@ def parse():
                     help="2: the weights with blocks of at most 128 columns and the wider ones on two streams in "
                          "the timed region (kernels then share the GPU, so per-launch times are not each "
                          "kernel's own)")
+    ap.add_argument("--compare-streams", action="store_true",
+                    help="also time the full step with the other stream schedule (breakdown_ms); off by default, "
+                         "so that a profiled run's kernel durations are those of the timed schedule only")
     ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
                     help="per-kernel MFMA utilisation and issued MFMA flops from a rocprofv3 --pmc run of "
                          "MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 MfmaFlopsF32")
@@ -474,9 +477,11 @@ def main():
     dobb.dobb_profile_reset()
     # the other schedule: one stream, or the narrow and the wide blocks on two overlapping streams
     other = 3 - args.streams
-    group.set_streams(other)
-    other_ms = timed(full_step, reps)
-    group.set_streams(args.streams)
+    other_ms = None
+    if args.compare_streams:
+        group.set_streams(other)
+        other_ms = timed(full_step, reps)
+        group.set_streams(args.streams)
 
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
@@ -521,7 +526,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown_ms": {"full_step_untimed": round(full_ms_untimed, 3),
-                         f"full_step_{other}_stream{'s' if other > 1 else ''}": round(other_ms, 3),
+                         f"full_step_{other}_stream{'s' if other > 1 else ''}":
+                             None if other_ms is None else round(other_ms, 3),
                          "step_nonrefresh": round(step_ms, 3),
                          "accumulate": round(acc_ms, 3), f"refresh_orth_iter_k{K_ORTH}": round(ref_ms, 3),
                          "refresh_exact_cold": round(exact_ms, 1), "refresh_exact_warm": round(warm_ms, 1),
