@@ -87,6 +87,8 @@ def parse():
     ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
                     help="per-kernel MFMA utilisation and issued MFMA flops from a rocprofv3 --pmc run of "
                          "MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 MfmaFlopsF32")
+    ap.add_argument("--counter-summary", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-kernel stall and cache ratios from rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-kernel HBM traffic table from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -311,6 +313,53 @@ def mfma_summary(counter_csv):
               f"{avg('MfmaFlopsBF16'):.4g} | {avg('MfmaFlopsF16'):.4g} | {avg('MfmaFlopsF32'):.4g} |")
 
 
+def counter_summary(counter_csvs):
+    """Per-kernel stall and cache figures from rocprofv3 --pmc runs (one CSV per pass), by kernel
+    function (the narrow and wide instances of a bench.py kernel apart): each counter averaged over
+    the kernel's dispatches in its pass, then the ratios below where their counters were taken.
+      dependency wait   SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting for an operand or a
+                        counter, e.g. a load in flight)
+      any wait          SQ_WAIT_ANY / SQ_WAVE_CYCLES (also barriers)
+      issuing           SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES
+      LDS conflicts     SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS
+      L2 read latency   TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum (cycles, as seen by L1)
+      L2 hit rate       TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"""
+    import csv
+    import collections
+    csv.field_size_limit(1 << 30)
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    counts = collections.defaultdict(lambda: collections.defaultdict(set))
+    for path in counter_csvs:
+        for r in csv.DictReader(open(path)):
+            mt = re.search(r"\b(k_[a-z0-9_]+)", r["Kernel_Name"])
+            if not mt or "dobb" not in r["Kernel_Name"]:
+                continue
+            k, c = mt.group(1), r["Counter_Name"]
+            sums[k][c] += float(r["Counter_Value"])
+            counts[k][c].add((path, r["Dispatch_Id"]))
+    avg = lambda k, c: sums[k][c] / len(counts[k][c]) if counts[k].get(c) else None
+
+    def ratio(k, a, b, scale=100.0):
+        x, y = avg(k, a), avg(k, b)
+        return None if x is None or not y else scale * x / y
+
+    def hit(k):
+        h, m_ = avg(k, "TCC_HIT_sum"), avg(k, "TCC_MISS_sum")
+        return None if h is None or m_ is None or h + m_ == 0 else 100.0 * h / (h + m_)
+    cols = [("dependency wait %", lambda k: ratio(k, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("any wait %", lambda k: ratio(k, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+            ("issuing %", lambda k: ratio(k, "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("LDS conflict %", lambda k: ratio(k, "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")),
+            ("L2 read latency (cycles)", lambda k: ratio(k, "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", 1.0)),
+            ("L2 hit %", hit)]
+    print("| kernel function | launches | " + " | ".join(c for c, _ in cols) + " |")
+    print("|---|---|" + "---|" * len(cols))
+    for k in sorted(sums, key=lambda k: -(avg(k, "SQ_WAVE_CYCLES") or 0.0)):
+        n = max(len(v) for v in counts[k].values())   # dispatches in a pass
+        vals = [f(k) for _, f in cols]
+        print(f"| `{k}` | {n} | " + " | ".join("–" if v is None else f"{v:.0f}" for v in vals) + " |")
+
+
 def cpu_baseline(group, xs, specs, wl, layers, col_l2=False, k_orth=1):
     """Time the oracle (one thread) on layer 0's weights: the step on 1/cpu_rows of each weight's rows,
     the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on 8 blocks of each
@@ -355,6 +404,9 @@ def main():
         return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the Dobb step here is the single-GPU kernel path "

@@ -57,7 +57,7 @@ __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 // Column index swizzled by row (gemm_swz): the two rows read by the half-waves of an MFMA operand
 // load fall in opposite bank halves, and the four rows a loader wave writes in one instruction
 // spread over all 64 banks.
-struct GemmSmem2 {
+struct __align__(16) GemmSmem2 {
     float a[2][kBK][kBM];
     float b[2][kBK][kBN];
 };
@@ -141,10 +141,11 @@ struct LoadColsK {
             }
         }
     }
+    // the swizzle flips column bits 4 and 5 only, so the four columns stay contiguous: one 16-byte
+    // store per lane (four 4-byte stores at stride 4 put a wave's 64 lanes on 16 banks)
     __device__ __forceinline__ void put(const float (&v)[4], float (*dst)[kBN]) const {
         const int t = threadIdx.x, kk = t >> 4, j = 4 * (t & 15);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[kk][(j + c) ^ gemm_swz(kk)] = v[c];
+        *(f32x4 *)&dst[kk][j ^ gemm_swz(kk)] = f32x4{v[0], v[1], v[2], v[3]};
     }
 };
 
