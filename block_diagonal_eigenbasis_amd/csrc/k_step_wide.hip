@@ -79,9 +79,20 @@ __global__ void __launch_bounds__(256) k_split_wide(int nb, int nblk, SplitWideT
     const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
     uint16_t *Pb = t.planes[mat] + (int64_t)b * PE;
     const int tid = threadIdx.x, k0 = kKSD * ks;
-    for (int e = tid; e < kKSD * R; e += 256) {
-        const int kk = e / R, j = e - kk * R;
-        tile[kk * (R + 1) + j] = (k0 + kk < nb && j < nb) ? Q[(int64_t)(k0 + kk) * nb + j] : 0.f;
+    if (((uintptr_t)Q & 15u) == 0) {   // nb % 4 == 0: rows start 16-byte aligned, 16-byte loads
+        const int R4 = R / 4;
+        for (int e = tid; e < kKSD * R4; e += 256) {
+            const int kk = e / R4, j = 4 * (e - kk * R4);
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (k0 + kk < nb && j < nb) v = *(const f32x4 *)(Q + (int64_t)(k0 + kk) * nb + j);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) tile[kk * (R + 1) + j + c] = v[c];
+        }
+    } else {
+        for (int e = tid; e < kKSD * R; e += 256) {
+            const int kk = e / R, j = e - kk * R;
+            tile[kk * (R + 1) + j] = (k0 + kk < nb && j < nb) ? Q[(int64_t)(k0 + kk) * nb + j] : 0.f;
+        }
     }
     __syncthreads();
     // Q^T slice ks: row j, k: Q[k0 + k][j]
