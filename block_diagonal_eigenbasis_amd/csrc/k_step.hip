@@ -196,12 +196,27 @@ struct LoadSignT {
     }
 };
 
-// a[k][i] = C * colscale (column-l2) or C (identity)
-template <bool SCALED>
+// a[k][i] = C * colscale (column-l2) or C (identity).  VEC: nb and n multiples of 4, and C and the
+// scales in the 256-byte-aligned workspace, so a row's four k sit in one 16-byte piece
+template <bool SCALED, bool VEC>
 struct LoadCoefT {
     const float *src; const float *cs; int64_t ld; int rows; int K;
     __device__ __forceinline__ void fetch(int k0, float (&v)[4]) const {
         const int t = threadIdx.x, i = t >> 2, k = k0 + 4 * (t & 3);
+        if (VEC) {
+            f32x4 q = {0.f, 0.f, 0.f, 0.f};
+            if (i < rows && k < K) {
+                q = *(const f32x4 *)(src + (int64_t)i * ld + k);
+                if (SCALED) {
+                    const f32x4 c4 = *(const f32x4 *)(cs + k);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) q[c] *= c4[c];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = q[c];
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             v[c] = 0.f;
@@ -236,7 +251,7 @@ __global__ void __launch_bounds__(256) k_reconstruct(int64_t m, int64_t n, int n
         LoadSignT<VEC> la{t.S[mat] + off, n, rows, nb};
         acc = gemm_tile(nb, la, lb, sm);
     } else {
-        LoadCoefT<AMODE == 2> la{t.C[mat] + off, t.cs[mat] + (int64_t)b * nb, n, rows, nb};
+        LoadCoefT<AMODE == 2, VEC> la{t.C[mat] + off, t.cs[mat] + (int64_t)b * nb, n, rows, nb};
         acc = gemm_tile(nb, la, lb, sm);
     }
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
