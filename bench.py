@@ -17,7 +17,7 @@ The default workload is the GPT-2 XL set.  ``--workload gpt2small`` runs the GPT
 for it, so a capture here is 4096 tokens).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--layers L] [--copy-mib C]
-                       [--workload gpt2xl|gpt2small|llama7b]
+                       [--workload gpt2xl|gpt2small|llama7b|single768_b4|single768_b1]
        python bench.py --pmc-summary FETCH_CSV WRITE_CSV [--copy-mib C]
        python bench.py --mfma-summary COUNTER_CSV
        python bench.py --counter-summary COUNTER_CSV [COUNTER_CSV ...]
@@ -65,6 +65,13 @@ WORKLOADS = {
                     config=5, lr=2.5e-3, cpu_rows=16, cpu_tokens=512,
                     text="Llama-7B-style stack ({L} layers x q,k,v,o 4096x4096, gate/up 11008x4096, down "
                          "4096x11008; nb=128), bf16 W/G, fp32 M/A/Q, bf16 activations {N} tokens"),
+    # single 768x768 weights: launch-latency bound, reported for completeness
+    "single768_b4": dict(specs="single_768_set", arg=4, layers=1, per_layer=1, tokens=4096, w_dtype="float32",
+                         x_dtype="float32", config=1, lr=2.5e-3, cpu_rows=1, cpu_tokens=4096,
+                         text="single 768x768 weight (B=4, nb=192), fp32 W/G/M/A/Q, fp32 activations {N} tokens"),
+    "single768_b1": dict(specs="single_768_set", arg=1, layers=1, per_layer=1, tokens=4096, w_dtype="float32",
+                         x_dtype="float32", config=2, lr=2.5e-3, cpu_rows=1, cpu_tokens=4096,
+                         text="single 768x768 weight (B=1, nb=768), fp32 W/G/M/A/Q, fp32 activations {N} tokens"),
 }
 
 
@@ -99,14 +106,15 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1):
+def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1, x_bytes=2):
     """Per-step work of each kernel of the path, summed over the matrix set.
 
     Per kernel: algorithmic HBM bytes (each operand read or written once), algorithmic flops with the
     peak of the precision they stand for, and the matrix-core flops the kernel actually issues with
     that dtype's peak.  Units (per weight m x n with B = n / nb blocks):
       accumulate_syrk_*     X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b);
-                            "wide" for bf16 blocks 128 < nb <= 512, nb % 8 == 0
+                            "wide" for bf16 blocks 128 < nb <= 512, nb % 8 == 0; fp32 activations
+                            (x_bytes = 4): accumulate_syrk, 4 N n bytes, fp32 MFMA
       accumulate_reduce     A read + written: 8 nb^2 B bytes
       refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
       qr_block              nb <= 128, the whole Householder QR in one launch: 8/3 nb^3 B flops
@@ -140,8 +148,11 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
 
     for s in specs:
         B, nb, mn = s.n // s.nb, s.nb, s.m * s.n
-        syrk = "accumulate_syrk_wide" if 128 < nb <= 512 and nb % 8 == 0 else "accumulate_syrk_bf16"
-        add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
+        if x_bytes == 4:
+            add("accumulate_syrk", 4.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_FP32_MFMA)
+        else:
+            syrk = "accumulate_syrk_wide" if 128 < nb <= 512 and nb % 8 == 0 else "accumulate_syrk_bf16"
+            add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
         add("accumulate_reduce", 8.0 * nb * nb * B)
         k = orth_iters
         add("refresh_gemm", k * 12.0 * nb * nb * B, k * 2.0 * nb ** 3 * B)
@@ -450,7 +461,8 @@ def main():
         X, basis = workload.activations_torch(n_tokens, s.n, 0.15,
                                               seed=workload.seed_for(wl["config"], li // wl["per_layer"],
                                                                      li % wl["per_layer"]),
-                                              device=dev, dtype=torch.bfloat16, basis=bases.get(s.n))
+                                              device=dev, dtype=getattr(torch, wl.get("x_dtype", "bfloat16")),
+                                              basis=bases.get(s.n))
         bases[s.n] = basis
         xs.append(X)
     del bases
@@ -540,7 +552,7 @@ def main():
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
     w_bytes = Ws[0].element_size()
-    work = kernel_work(specs, n_tokens, g_bytes, w_bytes, args.norm, K_ORTH)
+    work = kernel_work(specs, n_tokens, g_bytes, w_bytes, args.norm, K_ORTH, xs[0].element_size())
     per_kernel = {}
     for name, (launches, total_ms) in kernels.items():
         ent = {"launches_per_step": launches / args.steps, "ms_per_step": round(total_ms / args.steps, 4),

@@ -127,6 +127,12 @@ def llama7b_set(nb: int = 128) -> list[MatrixSpec]:
     return _set(32, shapes, lambda n: nb)
 
 
+def single_768_set(B: int = 4) -> list[MatrixSpec]:
+    """One 768x768 weight with B blocks (the single-matrix configurations: B = 4, and B = 1, 4, 16 for
+    the Table 1(b) gradients)."""
+    return [MatrixSpec("w", 768, 768, 768 // B)]
+
+
 def seed_for(config: int, layer: int, index: int) -> int:
     return 1000 * config + 10 * layer + index
 
@@ -136,5 +142,5 @@ def param_count(specs) -> int:
 
 
 __all__ = ["power_law_alpha", "power_law", "haar", "table1_matrix", "activations",
-           "activations_torch", "MatrixSpec", "gpt2_small_set", "gpt2_xl_set", "llama7b_set",
+           "activations_torch", "MatrixSpec", "gpt2_small_set", "gpt2_xl_set", "llama7b_set", "single_768_set",
            "seed_for", "param_count"]
