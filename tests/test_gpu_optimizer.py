@@ -38,14 +38,17 @@ def t32(x):
 SHAPES = [(96, 256, 64), (64, 512, 256), (128, 256, 128), (80, 400, 200), (48, 96, 48)]
 
 
-def test_two_streams_match_one_stream():
+@pytest.mark.parametrize("norm,wdt", [("sign", torch.float32), ("col_l2", torch.float32), ("sign", torch.bfloat16)])
+def test_two_streams_match_one_stream(norm, wdt):
+    print(f"two streams: norm={norm} W={wdt}", flush=True)
     rng = RNG(91)
     N = 512
-    Ws = [t32(0.02 * rng.standard_normal((m, n))) for m, n, _ in SHAPES]
-    Gs = [t32(rng.standard_normal((m, n))) for m, n, _ in SHAPES]
+    Ws = [t32(0.02 * rng.standard_normal((m, n))).to(wdt) for m, n, _ in SHAPES]
+    Gs = [t32(rng.standard_normal((m, n))).to(wdt) for m, n, _ in SHAPES]
     xs = [t32(workload.activations(N, n, 0.15, rng)).to(torch.bfloat16) for _, n, _ in SHAPES]
+    nm = dobb.DOBB_NORM_COL_L2 if norm == "col_l2" else dobb.DOBB_NORM_SIGN
     g1, g2 = [DobbGroup([w.clone() for w in Ws], [nb for _, _, nb in SHAPES], grads=Gs, n_tokens=N,
-                        weight_decay=0.1, momentum=0.9, streams=s) for s in (1, 2)]
+                        weight_decay=0.1, momentum=0.9, norm=nm, streams=s) for s in (1, 2)]
     assert len(g1._parts) == 1 and len(g2._parts) == 2
     assert sorted(g2._parts[0].idx + g2._parts[1].idx) == list(range(len(SHAPES)))
     for g in (g1, g2):
