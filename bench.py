@@ -7,8 +7,10 @@ for fc-proj).  W, G, M, A and Q are fp32; activations are bf16, 16384 tokens per
 15 % effective-rank power-law spectrum.  One benchmark step is the whole hot path with a refresh
 every step: capture (accumulate + EMA) -> basis refresh (warm-started orthogonal iteration, k = 1,
 Householder) -> the Dobb step (momentum, projection, sign, reconstruction, weight update).  The
-first refresh (setup, untimed) is exact.  Times come from events around the timed steps; the
-library's kernel timer attributes them to kernels.  The CPU oracle is timed on a bounded sample.
+first refresh (setup, untimed) is exact.  The headline comes from events around K timed steps with
+the library's kernel timer off; a second pass over K more steps with the timer on (an event pair
+around every launch, on its stream) attributes the time to kernels.  The CPU oracle is timed on a
+bounded sample, threaded over the host's cores.
 
 The default workload is the GPT-2 XL set.  ``--workload gpt2small`` runs the GPT-2 Small set (12 layers x
 {qkv 2304x768, proj 768x768, fc 3072x768, fc-proj 768x3072}, B = 16, fp32 state, bf16 activations of
@@ -86,6 +88,8 @@ def parse():
     ap.add_argument("--norm", choices=["sign", "col_l2"], default="sign",
                     help="normalisation of the coefficients: sign (Dobb) or column-l2 (Dobb-l2, Tables 11-12)")
     ap.add_argument("--orth-iters", type=int, default=1, help="orthogonal-iteration steps per refresh (Table 15)")
+    ap.add_argument("--basis", choices=["fp32", "bf16"], default="fp32",
+                    help="storage of the block bases (Table 18: bf16 is the pages' principal setting)")
     ap.add_argument("--streams", type=int, choices=[1, 2], default=1,
                     help="2: the weights with blocks of at most 128 columns and the wider ones on two streams in "
                          "the timed region (kernels then share the GPU, so per-launch times are not each "
@@ -122,11 +126,14 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                             all panels): 4/3 nb^3 B flops each (fp32)
       qr_panel              nb > 128, panel factorisation: about QR_PANEL nb^2 B flops (fp32 vector ALU)
       split_q               nb > 128 only, Q read, five 2-byte planes written: (4 + 10) nb^2 B bytes
-      project_f16x3         nb <= 416: M read + written, G read, sign bytes written: (9 + g) m n bytes;
+      project_f16x3         nb <= 416: M read + written, G read: (8 + g) m n bytes of the method (the
+                            projection's share of the step's G + M + W traffic); the sign byte it
+                            writes per entry is traffic of this implementation ("impl_bytes");
                             2 m n nb flops (fp32 contraction), issued as three fp16 products
       project_bf16x6        nb > 416 (staged kernels): same bytes and flops, issued as six bf16 products
-      reconstruct_f16x2     sign bytes read, W read + written: (1 + 2 w) m n bytes;
-                            2 m n nb flops (fp32 contraction), issued as two fp16 products
+      reconstruct_f16x2     W read + written: 2 w m n bytes of the method, plus the sign byte read
+                            (implementation); 2 m n nb flops (fp32 contraction), issued as two fp16
+                            products
     Column-l2 normalisation (norm="col_l2") takes the plain fp32 kernels instead of the last four:
       momentum              G read, M read + written: (8 + g) m n bytes
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
@@ -141,10 +148,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
     w = {}
 
     def add(name, nbytes=0.0, flops=0.0, flops_peak=PEAK_FP32_MFMA, issued=0.0, issued_peak=PEAK_BF16_MFMA,
-            compute="mfma"):
+            compute="mfma", impl=0.0):
         e = w.setdefault(name, dict(bytes=0.0, flops=0.0, flops_peak=flops_peak, issued=0.0,
-                                    issued_peak=issued_peak, compute=compute))
-        e["bytes"] += nbytes; e["flops"] += flops; e["issued"] += issued
+                                    issued_peak=issued_peak, compute=compute, impl_bytes=0.0))
+        e["bytes"] += nbytes; e["flops"] += flops; e["issued"] += issued; e["impl_bytes"] += impl
 
     for s in specs:
         B, nb, mn = s.n // s.nb, s.nb, s.m * s.n
@@ -176,10 +183,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)
         if nb <= 416:
-            add("project_f16x3", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+            add("project_f16x3", (8.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb, impl=mn)
         else:
-            add("project_bf16x6", (9.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb)
-        add("reconstruct_f16x2", (1.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb)
+            add("project_bf16x6", (8.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 6 * 2.0 * mn * nb, impl=mn)
+        add("reconstruct_f16x2", 2.0 * w_bytes * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 2 * 2.0 * mn * nb, impl=mn)
     return w
 
 
@@ -219,6 +226,8 @@ def roofline_entry(work, seconds):
         ent = {"bound": work["compute"], "achieved": rate / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s"}
     ent["frac"] = ent["achieved"] / ent["peak"]
     ent["hbm_frac"] = work["bytes"] / seconds / PEAK_HBM
+    if work.get("impl_bytes"):
+        ent["impl_bytes_per_step"] = work["impl_bytes"]
     if work["issued"]:
         ent["mfma_issued_frac"] = work["issued"] / seconds / work["issued_peak"]
         ent["fp32_equiv_tflops"] = work["flops"] / seconds / 1e12
@@ -373,41 +382,70 @@ def counter_summary(counter_csvs):
         print(f"| `{k}` | {n} | " + " | ".join("–" if v is None else f"{v:.0f}" for v in vals) + " |")
 
 
+def host_cores():
+    """Threads for the CPU baseline: the CPUs this process may run on, at most 16 (the host share of
+    one GPU), and the facts reported with them."""
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = list(range(os.cpu_count() or 1))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    ranges, start = [], None
+    for i, c in enumerate(aff):
+        if start is None:
+            start = c
+        if i + 1 == len(aff) or aff[i + 1] != c + 1:
+            ranges.append(f"{start}-{c}" if c > start else f"{start}")
+            start = None
+    return min(len(aff), 16), {"nproc": os.cpu_count(), "affinity": ",".join(ranges), "cpu_model": model}
+
+
 def cpu_baseline(group, xs, specs, wl, layers, col_l2=False, k_orth=1):
-    """Time the oracle (one thread) on layer 0's weights: the step on 1/cpu_rows of each weight's rows,
-    the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on 8 blocks of each
-    weight; scale linearly to the full set (every term is linear in rows, tokens, blocks and layers)."""
+    """Time the oracle, threaded over the host's cores (row chunks of the step, blocks of the capture
+    and of the refresh), on the weights of the first and the last layer: the step on 1/cpu_rows of
+    each weight's rows, the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on
+    every block; scale linearly to the full set (every term is linear in rows, tokens and layers)."""
     import oracle
-    rows_frac, tok, nblk_s = wl["cpu_rows"], wl["cpu_tokens"], 8
+    cores, facts = host_cores()
+    rows_frac, tok = wl["cpu_rows"], wl["cpu_tokens"]
     n_tokens = wl["tokens"]
-    t_step = t_acc = t_ref = 0.0
-    s_step = s_acc = s_ref = 0.0
-    for i in range(wl["per_layer"]):
+    per = wl["per_layer"]
+    sample = list(range(per)) + (list(range(len(specs) - per, len(specs))) if len(specs) > per else [])
+    t_meas = 0.0
+    s_total = 0.0
+    for i in sample:
         s = specs[i]
-        B = s.n // s.nb
         r = s.m // rows_frac
         W = group.W[i][:r].cpu(); G = group.G[i][:r].cpu(); M = group.M[i][:r].cpu()
         Q = group.Q[i].cpu()
         X = xs[i][:tok].cpu()
-        A = group.A[i][:nblk_s].cpu()
-        Qp = group.Q[i][:nblk_s].cpu()
+        A = group.A[i].cpu()
         t0 = time.perf_counter()
-        oracle.step(W, G, M, Q, s.nb, 2.5e-3, 0.1, 0.9, 0.2, norm=oracle.NORM_COL_L2 if col_l2 else oracle.NORM_SIGN)
+        oracle.step(W, G, M, Q, s.nb, 2.5e-3, 0.1, 0.9, 0.2, norm=oracle.NORM_COL_L2 if col_l2 else oracle.NORM_SIGN,
+                    cores=cores)
         t1 = time.perf_counter()
-        oracle.accumulate(X, s.nb)
+        oracle.accumulate(X, s.nb, cores=cores)
         t2 = time.perf_counter()
-        oracle.orth_iter(A, Qp, k=k_orth, cores=1)
+        oracle.orth_iter(A, Q, k=k_orth, cores=cores)
         t3 = time.perf_counter()
-        t_step += t1 - t0; t_acc += t2 - t1; t_ref += t3 - t2
-        s_step += (t1 - t0) * (s.m / r)
-        s_acc += (t2 - t1) * (n_tokens / tok)
-        s_ref += (t3 - t2) * (B / min(nblk_s, B))
-    total_s = (s_step + s_acc + s_ref) * layers
-    return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
-            "sample": (f"layer 0 of {layers}: step on 1/{rows_frac} of each weight's rows, capture on {tok} of "
-                       f"{n_tokens} tokens, orthogonal-iteration refresh on {nblk_s} blocks of each weight; "
-                       f"measured {t_step + t_acc + t_ref:.1f} s, scaled linearly (rows, tokens, blocks, layers)"),
-            "seconds_measured": round(t_step + t_acc + t_ref, 2)}
+        t_meas += t3 - t0
+        s_total += (t1 - t0) * (s.m / r) + (t2 - t1) * (n_tokens / tok) + (t3 - t2)
+    total_s = s_total * layers / (len(sample) / per)
+    nl = len(sample) // per
+    return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": (f"the {len(sample)} weights of {'layers 0 and ' + str(layers - 1) if nl > 1 else 'layer 0'} "
+                       f"of {layers}: step on 1/{rows_frac} of each weight's rows, capture on {tok} of {n_tokens} "
+                       f"tokens, orthogonal-iteration refresh (k={k_orth}) on every block; measured "
+                       f"{t_meas:.1f} s on {cores} threads, scaled linearly (rows, tokens, layers)"),
+            "seconds_measured": round(t_meas, 2), **facts}
 
 
 def main():
@@ -475,7 +513,8 @@ def main():
     scales = [0.2 * (max(s.m, s.n) / (1.0 if col_l2 else s.m)) ** 0.5 for s in specs]
     group = DobbGroup(Ws, [s.nb for s in specs], grads=Gs, n_tokens=n_tokens, lr=wl["lr"], weight_decay=0.1,
                       momentum=0.9, norm=dobb.DOBB_NORM_COL_L2 if col_l2 else dobb.DOBB_NORM_SIGN,
-                      update_scales=scales, streams=args.streams)
+                      update_scales=scales, streams=args.streams,
+                      basis_dtype=torch.bfloat16 if args.basis == "bf16" else torch.float32)
     K_ORTH = args.orth_iters
     beta = 0.9
     # setup: first capture and the exact refresh (untimed, but measured once)
@@ -502,9 +541,7 @@ def main():
         full_step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K whole steps, kernel timer on ----------------------------------------
-    dobb.dobb_profile_reset()
-    dobb.dobb_profile_enable(True)
+    # ---- timed region: K whole steps, kernel timer off -------------------------------------------
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -513,11 +550,24 @@ def main():
         full_step()
     ev1.record(stream)
     torch.cuda.synchronize()
-    dobb.dobb_profile_enable(False)
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {ms_per_step:.3f} ms per step", file=sys.stderr, flush=True)
+    # ---- the same K steps again with the kernel timer on: per-launch durations from event pairs on
+    # each kernel's own stream
+    dobb.dobb_profile_reset()
+    dobb.dobb_profile_enable(True)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev2.record(stream)
+    for _ in range(args.steps):
+        full_step()
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    dobb.dobb_profile_enable(False)
+    ms_per_step_timer = ev2.elapsed_time(ev3) / args.steps
     kernels = dobb.dobb_profile_read()
     dobb.dobb_profile_reset()
-    print(f"[bench] {ms_per_step:.3f} ms per step", file=sys.stderr, flush=True)
+    print(f"[bench] {ms_per_step_timer:.3f} ms per step with the kernel timer on", file=sys.stderr, flush=True)
 
     # ---- the same pieces without the timer: non-refresh step, capture, refresh ----------------
     def timed(fn, reps):
@@ -572,6 +622,7 @@ def main():
                             and args.norm == "sign" and K_ORTH == 1 else None),
                 "work_per_launch": unit_work / launches,
                 "work_unit": "bytes" if d["bound"] == "hbm" else "flop",
+                "impl_bytes_per_launch": work[dom].get("impl_bytes", 0.0) / launches,
                 "avg_launch_ms": d["avg_launch_ms"], "launches_per_step": launches}
 
     cpu = None
@@ -579,19 +630,21 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(group, xs, specs, wl, layers, col_l2, K_ORTH)
 
-    amort = lambda T: (full_ms_untimed + (T - 1) * step_ms) / T
+    amort = lambda T: (ms_per_step + (T - 1) * step_ms) / T
     out = {
         "metric": METRIC, "value": round(ms_per_step, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl["text"].format(L=layers, N=n_tokens) + f"; capture + orthogonal-iteration "
                                f"refresh (k={K_ORTH}) + step every step"
-                               + ("; column-l2 normalisation" if col_l2 else ""),
+                               + ("; column-l2 normalisation" if col_l2 else "")
+                               + ("; bf16 basis" if args.basis == "bf16" else ""),
                    "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
-                   "refresh_period": 1, "streams": args.streams},
+                   "refresh_period": 1, "streams": args.streams, "basis": args.basis},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "breakdown_ms": {"full_step_untimed": round(full_ms_untimed, 3),
+        "breakdown_ms": {"full_step_kernel_timer_on": round(ms_per_step_timer, 3),
+                         "full_step_again": round(full_ms_untimed, 3),
                          f"full_step_{other}_stream{'s' if other > 1 else ''}":
                              None if other_ms is None else round(other_ms, 3),
                          "step_nonrefresh": round(step_ms, 3),

@@ -1,9 +1,11 @@
 """ctypes binding of libdobb.so (include/dobb.h), with the C names.
 
 Argument marshalling only: every computation runs in the HIP kernels of libdobb.so.  Tensors must be
-torch tensors on a ROCm device; the binding checks dtype, device, shape and contiguity, allocates the
-workspace as a torch uint8 tensor (the caching allocator returns 256-byte aligned blocks) and passes
-torch's current stream.  There is no fallback: if the library is missing, loading raises.
+torch tensors on a ROCm device; the binding checks the dtype, device, shape and contiguity of every
+tensor (the grouped forms take one dtype per argument, so every tensor of a list must share it),
+allocates the workspace as a torch uint8 tensor (the caching allocator returns 256-byte aligned
+blocks) and passes torch's current stream.  There is no fallback: if the library is missing, loading
+raises.
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ DOBB_F32, DOBB_BF16 = 0, 1
 DOBB_REFRESH_EXACT, DOBB_REFRESH_ORTH_ITER = 0, 1
 DOBB_NORM_SIGN, DOBB_NORM_IDENTITY, DOBB_NORM_COL_L2 = 0, 1, 2
 DOBB_OP_ACCUMULATE, DOBB_OP_REFRESH, DOBB_OP_STEP = 0, 1, 2
+DOBB_WS_BF16_BASIS = 16
 
 
 class DobbError(RuntimeError):
@@ -54,14 +57,16 @@ def lib() -> ctypes.CDLL:
         L.dobb_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, PS, i64, i32]
         L.dobb_workspace_size.restype = sz
         L.dobb_accumulate_moment.argtypes = [PS, vp, ctypes.c_int, i64, i64, f32, vp, vp, sz, vp]
-        L.dobb_refresh_basis.argtypes = [PS, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, f32, vp, vp, sz, vp]
-        L.dobb_step.argtypes = [PS, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.POINTER(HParams), vp, vp, sz, vp]
+        L.dobb_refresh_basis.argtypes = [PS, vp, vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, f32,
+                                         vp, vp, sz, vp]
+        L.dobb_step.argtypes = [PS, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.POINTER(HParams),
+                                vp, vp, vp, sz, vp]
         L.dobb_accumulate_moment_grouped.argtypes = [ctypes.c_int, PS, PP, ctypes.c_int, i64,
                                                      ctypes.POINTER(ctypes.c_int64), f32, PP, vp, sz, vp]
-        L.dobb_refresh_basis_grouped.argtypes = [ctypes.c_int, PS, PP, PP, PP, ctypes.c_int, ctypes.c_int,
-                                                 ctypes.c_int, f32, PP, vp, sz, vp]
-        L.dobb_step_grouped.argtypes = [ctypes.c_int, PS, PP, ctypes.c_int, PP, ctypes.c_int, PP, PP,
-                                        ctypes.POINTER(HParams), PP, vp, sz, vp]
+        L.dobb_refresh_basis_grouped.argtypes = [ctypes.c_int, PS, PP, PP, ctypes.c_int, PP, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, f32, PP, vp, sz, vp]
+        L.dobb_step_grouped.argtypes = [ctypes.c_int, PS, PP, ctypes.c_int, PP, ctypes.c_int, PP, PP, ctypes.c_int,
+                                        ctypes.POINTER(HParams), PP, PP, vp, sz, vp]
         for name in ("dobb_accumulate_moment", "dobb_refresh_basis", "dobb_step", "dobb_accumulate_moment_grouped",
                      "dobb_refresh_basis_grouped", "dobb_step_grouped"):
             getattr(L, name).restype = ctypes.c_int
@@ -95,6 +100,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return DOBB_BF16
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _common_dtype(ts, name: str) -> int:
+    """The dtype code shared by every tensor of a grouped argument; a mixed list is rejected (the C
+    ABI takes one dtype per argument, and a wrong element size would read or write past a buffer)."""
+    dts = {t.dtype for t in ts}
+    if len(dts) != 1:
+        raise TypeError(f"{name}: every tensor of a grouped call needs the same dtype, got {sorted(map(str, dts))}")
+    return _dtype_code(ts[0])
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
@@ -148,16 +162,17 @@ def dobb_accumulate_moment(X: torch.Tensor, A: torch.Tensor, nb: int, beta: floa
 def dobb_refresh_basis(A: torch.Tensor, Q: torch.Tensor, mode: int = DOBB_REFRESH_EXACT, iters: int = 0,
                        warm_start: bool = False, tol: float = 0.0, lam: torch.Tensor | None = None,
                        info: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
-    """Refresh Q (B x nb x nb fp32, in/out) from A; see include/dobb.h."""
+    """Refresh Q (B x nb x nb, fp32 or bf16 storage, in/out) from A; see include/dobb.h."""
     B, nb, _ = A.shape
     shape = Shape(1, B * nb, nb)
     ap = _dev(A, "A", torch.float32)
-    qp = _dev(Q, "Q", torch.float32, A.shape)
+    qp = _dev(Q, "Q", None, A.shape)
+    qdt = _dtype_code(Q)
     lp = _dev(lam, "lambda", torch.float32, (B, nb)) if lam is not None else None
     ip = _dev(info, "info", torch.int32, (B,)) if info is not None else None
-    need = dobb_workspace_size(DOBB_OP_REFRESH, [(1, B * nb, nb)])
+    need = dobb_workspace_size(DOBB_OP_REFRESH, [(1, B * nb, nb)], 0, DOBB_WS_BF16_BASIS if qdt == DOBB_BF16 else 0)
     ws, wsb = _workspace(need, A.device, ws)
-    _check(lib().dobb_refresh_basis(ctypes.byref(shape), ap, qp, lp, int(mode), int(iters), int(bool(warm_start)),
+    _check(lib().dobb_refresh_basis(ctypes.byref(shape), ap, qp, qdt, lp, int(mode), int(iters), int(bool(warm_start)),
                                     float(tol), ip, None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
            "dobb_refresh_basis")
     return Q
@@ -169,20 +184,28 @@ def make_hparams(lr: float, weight_decay: float, momentum: float, update_scale: 
                    int(norm))
 
 
+def _step_variant(norm: int, q_dtype: int) -> int:
+    return int(norm) | (DOBB_WS_BF16_BASIS if q_dtype == DOBB_BF16 else 0)
+
+
 def dobb_step(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor, nb: int, hp: HParams,
-              U_out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
-    """One Dobb step on W (m x n, fp32/bf16) in place; M (fp32) in place; U_out optional (fp32)."""
+              U_out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
+              C_out: torch.Tensor | None = None):
+    """One Dobb step on W (m x n, fp32/bf16) in place; M (fp32) in place; Q fp32 or bf16; U_out and
+    C_out optional (fp32 m x n: the update before scaling, and the coefficients C_b = P_b Q_b)."""
     m, n = W.shape
     shape = Shape(m, n, nb)
     wp = _dev(W, "W")
     gp = _dev(G, "G", None, (m, n))
     mp = _dev(M, "M", torch.float32, (m, n))
-    qp = _dev(Q, "Q", torch.float32, (n // nb, nb, nb))
+    qp = _dev(Q, "Q", None, (n // nb, nb, nb))
+    qdt = _dtype_code(Q)
     up = _dev(U_out, "U_out", torch.float32, (m, n)) if U_out is not None else None
-    need = dobb_workspace_size(DOBB_OP_STEP, [(m, n, nb)], 0, hp.norm)
+    cp = _dev(C_out, "C_out", torch.float32, (m, n)) if C_out is not None else None
+    need = dobb_workspace_size(DOBB_OP_STEP, [(m, n, nb)], 0, _step_variant(hp.norm, qdt))
     ws, wsb = _workspace(need, W.device, ws)
-    _check(lib().dobb_step(ctypes.byref(shape), wp, _dtype_code(W), gp, _dtype_code(G), mp, qp, ctypes.byref(hp), up,
-                           None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step")
+    _check(lib().dobb_step(ctypes.byref(shape), wp, _dtype_code(W), gp, _dtype_code(G), mp, qp, qdt, ctypes.byref(hp),
+                           up, cp, None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step")
     return W
 
 
@@ -200,7 +223,7 @@ def dobb_accumulate_moment_grouped(Xs, As, nbs, beta: float = 0.0, ws: torch.Ten
             raise ValueError("all X of a group need the same token count")
         _dev(X, "X")
         _dev(A, "A", torch.float32, (n // nb, nb, nb))
-    dt = _dtype_code(Xs[0])
+    dt = _common_dtype(Xs, "X")
     sarr = (Shape * count)(*[Shape(*s) for s in shapes])
     ldx = (ctypes.c_int64 * count)(*[X.shape[1] for X in Xs])
     need = dobb_workspace_size(DOBB_OP_ACCUMULATE, shapes, N)
@@ -216,11 +239,12 @@ def dobb_refresh_basis_grouped(As, Qs, mode: int, iters: int, warm_start: bool =
     shapes = [(1, A.shape[0] * A.shape[1], A.shape[1]) for A in As]
     for A, Q in zip(As, Qs):
         _dev(A, "A", torch.float32)
-        _dev(Q, "Q", torch.float32, A.shape)
+        _dev(Q, "Q", None, A.shape)
+    qdt = _common_dtype(Qs, "Q")
     sarr = (Shape * count)(*[Shape(*s) for s in shapes])
-    need = dobb_workspace_size(DOBB_OP_REFRESH, shapes)
+    need = dobb_workspace_size(DOBB_OP_REFRESH, shapes, 0, DOBB_WS_BF16_BASIS if qdt == DOBB_BF16 else 0)
     ws, wsb = _workspace(need, As[0].device, ws)
-    _check(lib().dobb_refresh_basis_grouped(count, sarr, _ptrs(As), _ptrs(Qs),
+    _check(lib().dobb_refresh_basis_grouped(count, sarr, _ptrs(As), _ptrs(Qs), qdt,
                                             _ptrs(lams) if lams is not None else None, int(mode), int(iters),
                                             int(bool(warm_start)), float(tol),
                                             _ptrs(infos) if infos is not None else None,
@@ -228,18 +252,25 @@ def dobb_refresh_basis_grouped(As, Qs, mode: int, iters: int, warm_start: bool =
            "dobb_refresh_basis_grouped")
 
 
-def dobb_step_grouped(Ws, Gs, Ms, Qs, nbs, hps, U_outs=None, ws: torch.Tensor | None = None, stream=None):
+def dobb_step_grouped(Ws, Gs, Ms, Qs, nbs, hps, U_outs=None, ws: torch.Tensor | None = None, stream=None,
+                      C_outs=None):
     count = len(Ws)
     shapes = [(W.shape[0], W.shape[1], nb) for W, nb in zip(Ws, nbs)]
     for W, G, M, Q, (m, n, nb) in zip(Ws, Gs, Ms, Qs, shapes):
         _dev(W, "W"); _dev(G, "G", None, (m, n)); _dev(M, "M", torch.float32, (m, n))
-        _dev(Q, "Q", torch.float32, (n // nb, nb, nb))
+        _dev(Q, "Q", None, (n // nb, nb, nb))
+    wdt, gdt, qdt = _common_dtype(Ws, "W"), _common_dtype(Gs, "G"), _common_dtype(Qs, "Q")
+    for name, outs in (("U_out", U_outs), ("C_out", C_outs)):
+        for o, (m, n, _) in zip(outs or [], shapes):
+            if o is not None:
+                _dev(o, name, torch.float32, (m, n))
     sarr = (Shape * count)(*[Shape(*s) for s in shapes])
     harr = (HParams * count)(*hps)
-    need = dobb_workspace_size(DOBB_OP_STEP, shapes, 0, hps[0].norm)
+    need = dobb_workspace_size(DOBB_OP_STEP, shapes, 0, _step_variant(hps[0].norm, qdt))
     ws, wsb = _workspace(need, Ws[0].device, ws)
-    _check(lib().dobb_step_grouped(count, sarr, _ptrs(Ws), _dtype_code(Ws[0]), _ptrs(Gs), _dtype_code(Gs[0]),
-                                   _ptrs(Ms), _ptrs(Qs), harr, _ptrs(U_outs) if U_outs is not None else None,
+    _check(lib().dobb_step_grouped(count, sarr, _ptrs(Ws), wdt, _ptrs(Gs), gdt, _ptrs(Ms), _ptrs(Qs), qdt, harr,
+                                   _ptrs(U_outs) if U_outs is not None else None,
+                                   _ptrs(C_outs) if C_outs is not None else None,
                                    None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step_grouped")
 
 

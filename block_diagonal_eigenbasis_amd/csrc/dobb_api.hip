@@ -125,12 +125,21 @@ size_t step_ws_one(const dobb_shape &sh, int norm) {
     return b;
 }
 
+// the fp32 copy of a bf16 basis, per matrix
+size_t basis_copy_one(const dobb_shape &sh) { return al256((size_t)sh.n * (size_t)sh.nb * 4); }
+
+size_t step_region_one(const dobb_shape &sh, int variant) {
+    const bool qbf = (variant & DOBB_WS_BF16_BASIS) != 0;
+    return step_ws_one(sh, variant & ~DOBB_WS_BF16_BASIS) + (qbf ? basis_copy_one(sh) : 0);
+}
+
 size_t group_ws(dobb_op op, const dobb_shape &sh, int cnt, int64_t N, int variant) {
     const int c = cnt < kMaxMats ? cnt : kMaxMats;
+    const bool qbf = (variant & DOBB_WS_BF16_BASIS) != 0;
     switch (op) {
         case DOBB_OP_ACCUMULATE: return al256(accumulate_ws(sh, N, cnt));
-        case DOBB_OP_REFRESH: return al256(refresh_ws(sh, cnt));
-        case DOBB_OP_STEP: return step_ws_one(sh, variant) * c;
+        case DOBB_OP_REFRESH: return al256(refresh_ws(sh, c)) + (qbf ? basis_copy_one(sh) * c : 0);
+        case DOBB_OP_STEP: return step_region_one(sh, variant) * c;
     }
     return 0;
 }
@@ -169,7 +178,9 @@ size_t dobb_workspace_size(dobb_op op, int count, const dobb_shape *shapes, int6
     if (count < 1 || !shapes) return 0;
     if (op != DOBB_OP_ACCUMULATE && op != DOBB_OP_REFRESH && op != DOBB_OP_STEP) return 0;
     if (op == DOBB_OP_ACCUMULATE && N < 1) return 0;
-    if (op == DOBB_OP_STEP && (variant < 0 || variant > 2)) return 0;
+    if (op == DOBB_OP_STEP && ((variant & ~DOBB_WS_BF16_BASIS) < 0 || (variant & ~DOBB_WS_BF16_BASIS) > 2)) return 0;
+    if (op == DOBB_OP_ACCUMULATE) variant = 0;
+    if (op == DOBB_OP_REFRESH) variant &= DOBB_WS_BF16_BASIS;
     for (int i = 0; i < count; ++i)
         if (check_shape(&shapes[i]) != DOBB_OK) return 0;
     size_t need = 0;
@@ -225,10 +236,12 @@ dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtyp
     return dobb_accumulate_moment_grouped(1, s, &X, x_dtype, N, &ldx, beta, &A, ws, ws_bytes, stream);
 }
 
-dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, const float *const *A, float *const *Q,
-                                       float *const *lambda, dobb_refresh_mode mode, int iters, int warm_start, float tol,
-                                       int32_t *const *info, void *ws, size_t ws_bytes, dobb_stream_t stream) {
+dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, const float *const *A, void *const *Q,
+                                       dobb_dtype q_dtype, float *const *lambda, dobb_refresh_mode mode, int iters,
+                                       int warm_start, float tol, int32_t *const *info, void *ws, size_t ws_bytes,
+                                       dobb_stream_t stream) {
     if (count < 1 || !shapes || !A || !Q) return DOBB_ERR_INVALID_ARG;
+    if (q_dtype != DOBB_F32 && q_dtype != DOBB_BF16) return DOBB_ERR_DTYPE;
     if (mode != DOBB_REFRESH_EXACT && mode != DOBB_REFRESH_ORTH_ITER) return DOBB_ERR_INVALID_ARG;
     if (mode == DOBB_REFRESH_ORTH_ITER && iters < 1) return DOBB_ERR_INVALID_ARG;
     if (iters < 0 || iters > 1000) return DOBB_ERR_INVALID_ARG;
@@ -238,50 +251,82 @@ dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, cons
         if (st != DOBB_OK) return st;
         if (!A[i] || !Q[i]) return DOBB_ERR_INVALID_ARG;
     }
+    const bool qbf = q_dtype == DOBB_BF16;
+    const int variant = qbf ? DOBB_WS_BF16_BASIS : 0;
     const auto groups = group_by_shape(count, shapes);
     size_t need = 0;
-    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_REFRESH, shapes[g[0]], (int)g.size(), 0, 0); if (w > need) need = w; }
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_REFRESH, shapes[g[0]], (int)g.size(), 0, variant); if (w > need) need = w; }
     dobb_status st = check_ws(ws, ws_bytes, need);
     if (st != DOBB_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
     for (const auto &g : groups) {
-        std::vector<const float *> as;
-        std::vector<float *> qs, ls;
-        std::vector<int32_t *> is;
-        for (int i : g) {
-            as.push_back(A[i]); qs.push_back(Q[i]);
-            ls.push_back(lambda ? lambda[i] : nullptr);
-            is.push_back(info ? info[i] : nullptr);
+        const dobb_shape sh = shapes[g[0]];
+        const int64_t elems = sh.n * sh.nb;
+        for (size_t c0 = 0; c0 < g.size(); c0 += kMaxMats) {
+            const int cnt = (int)(g.size() - c0 < (size_t)kMaxMats ? g.size() - c0 : (size_t)kMaxMats);
+            // a bf16 basis is refreshed in an fp32 copy placed after the refresh regions
+            char *copies = (char *)ws + al256(refresh_ws(sh, cnt));
+            std::vector<const float *> as;
+            std::vector<float *> qs, ls;
+            std::vector<int32_t *> is;
+            std::vector<const void *> qsrc;
+            std::vector<void *> qdst;
+            for (int k = 0; k < cnt; ++k) {
+                const int i = g[c0 + k];
+                as.push_back(A[i]);
+                float *qf = qbf ? (float *)(copies + basis_copy_one(sh) * k) : (float *)Q[i];
+                qs.push_back(qf);
+                qsrc.push_back(Q[i]);
+                qdst.push_back(qf);
+                ls.push_back(lambda ? lambda[i] : nullptr);
+                is.push_back(info ? info[i] : nullptr);
+            }
+            // warm starts and orthogonal iteration read the basis; a cold exact refresh does not
+            if (qbf && (mode != DOBB_REFRESH_EXACT || warm_start)) {
+                st = hip_status(launch_basis_convert(cnt, qsrc.data(), qdst.data(), elems, true, hs));
+                if (st != DOBB_OK) return st;
+            }
+            RefreshArgs a{};
+            a.count = cnt;
+            a.sh = sh;
+            a.A = as.data();
+            a.Q = qs.data();
+            a.lambda = ls.data();
+            a.info = is.data();
+            a.mode = mode;
+            a.iters = mode == DOBB_REFRESH_EXACT ? (iters > 0 ? iters : 30) : iters;
+            a.warm = warm_start ? 1 : 0;
+            a.tol = tol > 0.f ? tol : 1e-7f;
+            a.ws = ws;
+            st = hip_status(launch_refresh(a, hs));
+            if (st != DOBB_OK) return st;
+            if (qbf) {
+                std::vector<const void *> fsrc(qs.begin(), qs.end());
+                std::vector<void *> bdst;
+                for (int k = 0; k < cnt; ++k) bdst.push_back(Q[g[c0 + k]]);
+                st = hip_status(launch_basis_convert(cnt, fsrc.data(), bdst.data(), elems, false, hs));
+                if (st != DOBB_OK) return st;
+            }
         }
-        RefreshArgs a{};
-        a.count = (int)g.size();
-        a.sh = shapes[g[0]];
-        a.A = as.data();
-        a.Q = qs.data();
-        a.lambda = ls.data();
-        a.info = is.data();
-        a.mode = mode;
-        a.iters = mode == DOBB_REFRESH_EXACT ? (iters > 0 ? iters : 30) : iters;
-        a.warm = warm_start ? 1 : 0;
-        a.tol = tol > 0.f ? tol : 1e-7f;
-        a.ws = ws;
-        st = hip_status(launch_refresh(a, (hipStream_t)stream));
-        if (st != DOBB_OK) return st;
     }
     return DOBB_OK;
 }
 
-dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, float *Q, float *lambda, dobb_refresh_mode mode,
-                               int iters, int warm_start, float tol, int32_t *info, void *ws, size_t ws_bytes,
-                               dobb_stream_t stream) {
+dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, void *Q, dobb_dtype q_dtype, float *lambda,
+                               dobb_refresh_mode mode, int iters, int warm_start, float tol, int32_t *info, void *ws,
+                               size_t ws_bytes, dobb_stream_t stream) {
     if (!s) return DOBB_ERR_INVALID_ARG;
-    return dobb_refresh_basis_grouped(1, s, &A, &Q, &lambda, mode, iters, warm_start, tol, &info, ws, ws_bytes, stream);
+    return dobb_refresh_basis_grouped(1, s, &A, &Q, q_dtype, &lambda, mode, iters, warm_start, tol, &info, ws, ws_bytes,
+                                      stream);
 }
 
 dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype, const void *const *G,
-                              dobb_dtype g_dtype, float *const *M, const float *const *Q, const dobb_hparams *hp,
-                              float *const *U_out, void *ws, size_t ws_bytes, dobb_stream_t stream) {
+                              dobb_dtype g_dtype, float *const *M, const void *const *Q, dobb_dtype q_dtype,
+                              const dobb_hparams *hp, float *const *U_out, float *const *C_out, void *ws, size_t ws_bytes,
+                              dobb_stream_t stream) {
     if (count < 1 || !shapes || !W || !G || !M || !Q || !hp) return DOBB_ERR_INVALID_ARG;
-    if ((w_dtype != DOBB_F32 && w_dtype != DOBB_BF16) || (g_dtype != DOBB_F32 && g_dtype != DOBB_BF16))
+    if ((w_dtype != DOBB_F32 && w_dtype != DOBB_BF16) || (g_dtype != DOBB_F32 && g_dtype != DOBB_BF16) ||
+        (q_dtype != DOBB_F32 && q_dtype != DOBB_BF16))
         return DOBB_ERR_DTYPE;
     for (int i = 0; i < count; ++i) {
         dobb_status st = check_shape(&shapes[i]);
@@ -291,73 +336,85 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
         if (hp[i].norm != hp[0].norm || (hp[i].nesterov != 0) != (hp[0].nesterov != 0)) return DOBB_ERR_INVALID_ARG;
     }
     const int norm = hp[0].norm;
+    const bool qbf = q_dtype == DOBB_BF16;
+    const int variant = norm | (qbf ? DOBB_WS_BF16_BASIS : 0);
     const auto groups = group_by_shape(count, shapes);
     size_t need = 0;
-    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_STEP, shapes[g[0]], (int)g.size(), 0, norm); if (w > need) need = w; }
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_STEP, shapes[g[0]], (int)g.size(), 0, variant); if (w > need) need = w; }
     dobb_status st = check_ws(ws, ws_bytes, need);
     if (st != DOBB_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
     for (const auto &g : groups) {
         const dobb_shape sh = shapes[g[0]];
-        const size_t per = step_ws_one(sh, norm);
-        std::vector<const void *> gs;
-        std::vector<float *> ms, us, cs, ps;
-        std::vector<double *> cps;
-        std::vector<void *> ws_;
-        std::vector<const float *> qs;
-        std::vector<int8_t *> ss;
-        std::vector<uint16_t *> pls;
-        std::vector<dobb_hparams> hs;
+        const size_t per = step_region_one(sh, variant);
+        const size_t own = step_ws_one(sh, norm);       // the step's regions; a basis copy follows them
         const bool bf16 = step_bf16_eligible(sh, norm);
-        bool aligned = true;
-        for (size_t k = 0; k < g.size(); ++k) {
-            const int i = g[k];
-            gs.push_back(G[i]); ms.push_back(M[i]); ws_.push_back(W[i]); qs.push_back(Q[i]);
-            us.push_back(U_out ? U_out[i] : nullptr);
-            hs.push_back(hp[i]);
-            char *reg = (char *)ws + per * (k % kMaxMats);  // a chunk of kMaxMats shares the workspace
-            ss.push_back((int8_t *)reg);
-            cs.push_back((float *)reg);
-            ps.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + al256((size_t)sh.m * sh.n * 4)));
-            cps.push_back(norm == DOBB_NORM_COL_L2
-                              ? (double *)(reg + al256((size_t)sh.m * sh.n * 4) + al256((size_t)sh.n * 4))
-                              : nullptr);
-            const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
-            pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
-            aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
-                      ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0;
-        }
-        StepArgs a{};
-        a.count = (int)g.size();
-        a.sh = sh;
-        a.w_dtype = w_dtype;
-        a.g_dtype = g_dtype;
-        a.hp = hs.data();
-        a.G = gs.data();
-        a.M = ms.data();
-        a.W = ws_.data();
-        a.U = us.data();
-        a.Q = qs.data();
-        a.S = ss.data();
-        a.C = cs.data();
-        a.colscale = ps.data();
-        a.colpart = cps.data();
-        a.planes = pls.data();
-        if (bf16 && aligned) {
-            st = hip_status(launch_step_bf16(a, (hipStream_t)stream));
+        for (size_t c0 = 0; c0 < g.size(); c0 += kMaxMats) {
+            const int cnt = (int)(g.size() - c0 < (size_t)kMaxMats ? g.size() - c0 : (size_t)kMaxMats);
+            std::vector<const void *> gs, qsrc;
+            std::vector<float *> ms, us, co, cs, ps;
+            std::vector<double *> cps;
+            std::vector<void *> ws_, qdst;
+            std::vector<const float *> qs;
+            std::vector<int8_t *> ss;
+            std::vector<uint16_t *> pls;
+            std::vector<dobb_hparams> hs_;
+            bool aligned = true;
+            for (int k = 0; k < cnt; ++k) {
+                const int i = g[c0 + k];
+                char *reg = (char *)ws + per * k;
+                gs.push_back(G[i]); ms.push_back(M[i]); ws_.push_back(W[i]);
+                us.push_back(U_out ? U_out[i] : nullptr);
+                co.push_back(C_out ? C_out[i] : nullptr);
+                hs_.push_back(hp[i]);
+                float *qf = qbf ? (float *)(reg + own) : (float *)Q[i];
+                qs.push_back(qf);
+                qsrc.push_back(Q[i]);
+                qdst.push_back(qf);
+                ss.push_back((int8_t *)reg);
+                cs.push_back((float *)reg);
+                ps.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + al256((size_t)sh.m * sh.n * 4)));
+                cps.push_back(norm == DOBB_NORM_COL_L2
+                                  ? (double *)(reg + al256((size_t)sh.m * sh.n * 4) + al256((size_t)sh.n * 4))
+                                  : nullptr);
+                const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
+                pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
+                aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
+                          ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0;
+            }
+            if (qbf) {
+                st = hip_status(launch_basis_convert(cnt, qsrc.data(), qdst.data(), sh.n * sh.nb, true, hs));
+                if (st != DOBB_OK) return st;
+            }
+            StepArgs a{};
+            a.count = cnt;
+            a.sh = sh;
+            a.w_dtype = w_dtype;
+            a.g_dtype = g_dtype;
+            a.hp = hs_.data();
+            a.G = gs.data();
+            a.M = ms.data();
+            a.W = ws_.data();
+            a.U = us.data();
+            a.Cout = co.data();
+            a.Q = qs.data();
+            a.S = ss.data();
+            a.C = cs.data();
+            a.colscale = ps.data();
+            a.colpart = cps.data();
+            a.planes = pls.data();
+            st = hip_status(bf16 && aligned ? launch_step_bf16(a, hs) : launch_step(a, hs));
             if (st != DOBB_OK) return st;
-            continue;
         }
-        st = hip_status(launch_step(a, (hipStream_t)stream));
-        if (st != DOBB_OK) return st;
     }
     return DOBB_OK;
 }
 
 dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype, float *M,
-                      const float *Q, const dobb_hparams *hp, float *U_out, void *ws, size_t ws_bytes,
-                      dobb_stream_t stream) {
+                      const void *Q, dobb_dtype q_dtype, const dobb_hparams *hp, float *U_out, float *C_out, void *ws,
+                      size_t ws_bytes, dobb_stream_t stream) {
     if (!s) return DOBB_ERR_INVALID_ARG;
-    return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, hp, &U_out, ws, ws_bytes, stream);
+    return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, q_dtype, hp, &U_out, &C_out, ws, ws_bytes, stream);
 }
 
 void dobb_profile_enable(int on) {

@@ -163,6 +163,7 @@ struct StepArgs {
     float *const *M;
     void *const *W;
     float *const *U;                  // entries may be NULL
+    float *const *Cout;               // coefficients C = P Q before normalisation; entries may be NULL
     const float *const *Q;
     // workspace regions per matrix
     int8_t *const *S;                 // sign codes m x n
@@ -172,6 +173,9 @@ struct StepArgs {
     uint16_t *const *planes;          // bf16 planes of Q (bf16 path)
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+// bf16 basis <-> fp32 copy (k_basis.hip): cnt <= kMaxMats matrices of `elems` entries each
+hipError_t launch_basis_convert(int cnt, const void *const *src, void *const *dst, int64_t elems, bool to_f32,
+                                hipStream_t s);
 // fp32-accurate bf16-split path for the sign norm (nb <= 512, nb % 4 == 0)
 bool step_bf16_eligible(const dobb_shape &sh, int norm);
 size_t step_bf16_ws_one(const dobb_shape &sh);

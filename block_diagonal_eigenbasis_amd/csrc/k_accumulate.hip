@@ -4,10 +4,9 @@
 // diagonal blocks; Figure 2 caption: second moments are averaged over accumulated mini-batches.
 //   A_b <- beta A_b + (1 - beta) (1/N) X_b^T X_b      (X_b = the nb columns of block b, N tokens)
 //
-// k_syrk: one workgroup per (upper-triangle 64x64 tile pair, block, matrix, token split).  The
-// products are formed by v_mfma_f32_32x32x2_f32 (exact for bf16 inputs), summed in fp32 over 64
-// tokens and folded into fp64 registers, so the sum over N tokens is close to correctly rounded.
-// Without a token split the EMA is fused into the epilogue; with one, fp64 partials go to the
+// k_syrk (fp32 activations): one workgroup per (upper-triangle 64x64 tile pair, block, matrix, token
+// split).  The products are exact in fp64 and summed in fp64, so A is correctly rounded but for near
+// ties.  Without a token split the EMA is fused into the epilogue; with one, fp64 partials go to the
 // workspace and k_syrk_reduce adds them in split order (deterministic, no atomics).  Each result is
 // written at (i, j) and (j, i) from the same value, so A is exactly symmetric.
 // k_syrk_bf16 takes bf16 activations in 128 x 128 tile pairs; k_syrk_wide takes bf16 blocks wider
@@ -65,13 +64,15 @@ __device__ __forceinline__ void tile_pair(int p, int T, int &ti, int &tj) {
     tj = ti + p;
 }
 
-constexpr int kFoldChunks = 4;  // fold the fp32 accumulator into fp64 every 4 x 16 = 64 tokens
-
-// grid.x = npairs * nblk * count, grid.y = token splits
-template <bool XBF16, bool VEC>
+// fp32 activations: grid.x = npairs * nblk * count, grid.y = token splits.  Products of fp32 values
+// are exact in fp64 and the sums run in fp64 (v_fma_f64), so the sum over a split is within a few
+// units of 2^-53 of the exact one and A comes out correctly rounded to fp32 but for near ties.
+// Thread t owns the 4 x 4 outputs at rows 4 (t / 16) .., columns 4 (t % 16) .. of the 64 x 64 tile;
+// each 16-token chunk is staged in LDS as fp32, token-major.
+template <bool VEC>
 __global__ void __launch_bounds__(256) k_syrk(int64_t N, int nb, int T, int npairs, int nblk, int64_t tok_per_split,
                                               int nsplit, float beta, AccTable t, double *partial) {
-    __shared__ GemmSmem sm;
+    __shared__ __align__(16) GemmSmem sm;
     const int pair = blockIdx.x % npairs;
     const int rest = blockIdx.x / npairs;
     const int b = rest % nblk, mat = rest / nblk;
@@ -82,55 +83,54 @@ __global__ void __launch_bounds__(256) k_syrk(int64_t N, int nb, int T, int npai
     const int64_t te = min<int64_t>(N, tb + tok_per_split);
     const int K = (int)(te - tb);
     const int64_t ld = t.ldx[mat];
-    const size_t esz = XBF16 ? 2 : 4;
-    const char *base = (const char *)t.X[mat] + (size_t)(tb * ld + (int64_t)b * nb) * esz;
-    LoadTokens<XBF16, VEC> la{base + (size_t)i0 * esz, ld, nb - i0, K};
-    LoadTokens<XBF16, VEC> lb{base + (size_t)j0 * esz, ld, nb - j0, K};
+    const char *base = (const char *)t.X[mat] + (size_t)(tb * ld + (int64_t)b * nb) * 4;
+    LoadTokens<false, VEC> la{base + (size_t)i0 * 4, ld, nb - i0, K};
+    LoadTokens<false, VEC> lb{base + (size_t)j0 * 4, ld, nb - j0, K};
 
-    f32x16 acc = {};
-    double accd[16];
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    double acc[4][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) accd[r] = 0.0;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wr = 32 * (w >> 1), wc = 32 * (w & 1);
-    int chunk = 0;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
     for (int k0 = 0; k0 < K; k0 += kBK) {
         la(k0, sm.a);
         lb(k0, sm.b);
         __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kBK; ++kk) {
+            const f32x4 av = *(const f32x4 *)&sm.a[kk][4 * ty];
+            const f32x4 bv = *(const f32x4 *)&sm.b[kk][4 * tx];
+            double ad[4], bd[4];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 2) {
-            float a = sm.a[kk + (lane >> 5)][wr + (lane & 31)];
-            float bb = sm.b[kk + (lane >> 5)][wc + (lane & 31)];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
+            for (int c = 0; c < 4; ++c) { ad[c] = (double)av[c]; bd[c] = (double)bv[c]; }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fma(ad[r], bd[c], acc[r][c]);
         }
         __syncthreads();
-        if (++chunk == kFoldChunks) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { accd[r] += (double)acc[r]; acc[r] = 0.f; }
-            chunk = 0;
-        }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) accd[r] += (double)acc[r];
 
-    const int gj = j0 + wc + acc_col(lane);
     const double invN = 1.0 / (double)N;
     const double bd = (double)beta;
     float *Ab = t.A[mat] + (int64_t)b * nb * nb;
     const int64_t tot_blocks = gridDim.x / npairs;  // nblk * matrices in this launch
     double *Pb = partial ? partial + ((int64_t)blockIdx.y * tot_blocks + rest) * nb * nb : nullptr;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int gi = i0 + wr + acc_row(r, lane);
-        if (gi >= nb || gj >= nb || gi > gj) continue;  // only the upper triangle (gi <= gj)
-        if (nsplit == 1) {
-            const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
-            const float v = (float)(bd * old + (1.0 - bd) * (accd[r] * invN));
-            Ab[(int64_t)gi * nb + gj] = v;
-            Ab[(int64_t)gj * nb + gi] = v;
-        } else {
-            Pb[(int64_t)gi * nb + gj] = accd[r];
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int gi = i0 + 4 * ty + r, gj = j0 + 4 * tx + c;
+            if (gi >= nb || gj >= nb || gi > gj) continue;  // only the upper triangle (gi <= gj)
+            if (nsplit == 1) {
+                const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
+                const float v = (float)(bd * old + (1.0 - bd) * (acc[r][c] * invN));
+                Ab[(int64_t)gi * nb + gj] = v;
+                Ab[(int64_t)gj * nb + gi] = v;
+            } else {
+                Pb[(int64_t)gi * nb + gj] = acc[r][c];
+            }
         }
     }
 }
@@ -598,7 +598,7 @@ hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
             if (vec8) DOBB_SYRKB(8); else if (vec4) DOBB_SYRKB(4); else DOBB_SYRKB(1);
 #undef DOBB_SYRKB
         } else {
-#define DOBB_SYRK(V) DOBB_LAUNCH("accumulate_syrk", s, (k_syrk<false, V>), grid, dim3(256), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
+#define DOBB_SYRK(V) DOBB_LAUNCH("accumulate_syrk_f64", s, (k_syrk<V>), grid, dim3(256), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
             if (vec4) DOBB_SYRK(true); else DOBB_SYRK(false);
 #undef DOBB_SYRK
         }

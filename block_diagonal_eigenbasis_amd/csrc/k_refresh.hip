@@ -341,244 +341,18 @@ __global__ void __launch_bounds__(256) k_jacobi_finalize(int nb, int nbp, int nb
 // Z <- Z - V T^T (V^T Z) with three fp32 MFMA 32x32x2 products per 32-column tile (one tile per
 // wave).  V and T of every panel are kept (V in Z's panel columns, T in the workspace); Q is then
 // formed from the identity by applying the block reflectors last to first, Q <- Q - V T (V^T Q), and
-// the columns with R_cc < 0 are negated.  Z lives in LDS when it fits, in the workspace otherwise.
+// the columns with R_cc < 0 are negated.  Z lives in the workspace.
 constexpr int kQP = 32;
-constexpr int kQrLdsMaxNb = 64;  // blocks up to this width use the single-workgroup LDS kernel
 
-struct QrLayout {
-    size_t red, tau, gsh, tsd, part, wk, ts, wsh, neg, vs, zs, total;
-};
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) / 16 * 16; }
-__host__ __device__ inline QrLayout qr_layout(int nb, bool zlds) {
-    QrLayout L;
-    size_t o = 0;
-    L.red = o;  o += al16(8 * 8);
-    L.tau = o;  o += al16(kQP * 8);
-    L.gsh = o;  o += al16(kQP * kQP * 8);
-    L.tsd = o;  o += al16(kQP * kQP * 8);
-    L.part = o; o += al16(8 * kQP * 8);
-    L.wk = o;   o += al16(kQP * 8);
-    L.ts = o;   o += al16(kQP * (kQP + 1) * 4);
-    L.wsh = o;  o += al16(4 * 32 * 33 * 4);
-    L.neg = o;  o += al16((size_t)nb);
-    L.vs = o;   o += al16((size_t)nb * (kQP + 1) * 4);
-    L.zs = o;   o += zlds ? al16((size_t)nb * (nb + 1) * 4) : 0;
-    L.total = o;
-    return L;
-}
-
 // acc (32x32, MFMA layout) -> S[32][33]
 __device__ __forceinline__ void acc_to_lds(const f32x16 &acc, float (*S)[33], int lane) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[acc_row(r, lane)][acc_col(lane)] = acc[r];
 }
 
-// One 32-column tile update, run by one wave:  X[rows, c0:c0+32] -= V op(T) (V^T X[rows, c0:c0+32])
-// X rows are offset by j0 (row r of the tile is X row j0 + r).  op(T) = T^T (factorisation) or T.
-template <bool TRANS_T>
-__device__ __forceinline__ void wy_tile(float *X, int ldx, int ncols_total, int j0, int rows, int c0,
-                                        const float (*Vs)[kQP + 1], const float (*Ts)[kQP + 1], float (*W)[33],
-                                        int lane, bool active) {
-    f32x16 acc = {};
-    if (active) {
-        const int kr = lane >> 5, cc = lane & 31;
-        const bool colok = c0 + cc < ncols_total;
-#pragma unroll 8
-        for (int k = 0; k < rows; k += 2) {
-            const int r = k + kr;
-            const float a = r < rows ? Vs[r][cc] : 0.f;
-            const float bz = (r < rows && colok) ? X[(int64_t)(j0 + r) * ldx + c0 + cc] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bz, acc, 0, 0, 0);
-        }
-        acc_to_lds(acc, W, lane);
-    }
-    __syncthreads();
-    f32x16 y = {};
-    if (active) {
-#pragma unroll
-        for (int kk = 0; kk < kQP; kk += 2) {
-            const int k = kk + (lane >> 5), i = lane & 31;
-            const float a = TRANS_T ? Ts[k][i] : Ts[i][k];
-            y = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][i], y, 0, 0, 0);
-        }
-    }
-    __syncthreads();
-    if (active) acc_to_lds(y, W, lane);
-    __syncthreads();
-    if (active) {
-        for (int r0 = 0; r0 < rows; r0 += 32) {
-            f32x16 u = {};
-#pragma unroll
-            for (int kk = 0; kk < kQP; kk += 2) {
-                const int k = kk + (lane >> 5), rr = r0 + (lane & 31);
-                const float a = rr < rows ? Vs[rr][k] : 0.f;
-                u = __builtin_amdgcn_mfma_f32_32x32x2f32(a, W[k][lane & 31], u, 0, 0, 0);
-            }
-            const int col = c0 + acc_col(lane);
-            if (col < ncols_total) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = r0 + acc_row(r, lane);
-                    if (row < rows) X[(int64_t)(j0 + row) * ldx + col] -= u[r];
-                }
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// grid.x = blocks, block 256 (4 waves)
-template <bool ZLDS>
-__global__ void __launch_bounds__(256) k_householder(int nb, int nblk, float *Z_all, float *Tq_all, OutTable t,
-                                                     int info_value) {
-    extern __shared__ __align__(16) unsigned char dsm[];
-    const QrLayout L = qr_layout(nb, ZLDS);
-    double *red = (double *)(dsm + L.red);
-    double *tau = (double *)(dsm + L.tau);
-    double *gsh = (double *)(dsm + L.gsh);
-    double *tsd = (double *)(dsm + L.tsd);
-    double *part = (double *)(dsm + L.part);
-    double *wk = (double *)(dsm + L.wk);
-    float(*Ts)[kQP + 1] = (float(*)[kQP + 1])(dsm + L.ts);
-    float(*Wsh)[32][33] = (float(*)[32][33])(dsm + L.wsh);
-    int8_t *neg = (int8_t *)(dsm + L.neg);
-    float(*Vs)[kQP + 1] = (float(*)[kQP + 1])(dsm + L.vs);
-
-    const int g = blockIdx.x;
-    const int b = g % nblk, mat = g / nblk;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int npanel = (nb + kQP - 1) / kQP;
-    float *Zg = Z_all + (int64_t)g * nb * nb;
-    float *Tq = Tq_all + (int64_t)g * npanel * kQP * kQP;
-    const int ldz = ZLDS ? nb + 1 : nb;
-    float *Z = ZLDS ? (float *)(dsm + L.zs) : Zg;
-    if (ZLDS) for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) Z[(e / nb) * ldz + e % nb] = Zg[e];
-    __syncthreads();
-
-    for (int p = 0; p < npanel; ++p) {
-        const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
-        for (int e = tid; e < rows * kQP; e += 256) {
-            const int r = e / kQP, c = e % kQP;
-            Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
-        }
-        __syncthreads();
-        // factor the panel
-        for (int c = 0; c < w; ++c) {
-            double ps = 0.0;
-            for (int r = c + tid; r < rows; r += 256) { const double x = Vs[r][c]; ps += x * x; }
-            for (int o = 32; o > 0; o >>= 1) ps += __shfl_down(ps, o, 64);
-            if (lane == 0) red[wv] = ps;
-            __syncthreads();
-            if (tid == 0) {
-                const double alpha = sqrt(red[0] + red[1] + red[2] + red[3]);
-                const double x0 = Vs[c][c];
-                const double sg = x0 >= 0.0 ? 1.0 : -1.0;
-                if (alpha == 0.0) { tau[c] = 0.0; red[4] = 1.0; red[5] = 0.0; }
-                else { tau[c] = 1.0 + fabs(x0) / alpha; red[4] = x0 + sg * alpha; red[5] = -sg * alpha; }
-                neg[j0 + c] = red[5] < 0.0;
-            }
-            __syncthreads();
-            const double u0 = red[4], tc = tau[c];
-            for (int r = c + 1 + tid; r < rows; r += 256) Vs[r][c] = (float)((double)Vs[r][c] / u0);
-            __syncthreads();
-            {   // s_k = v^T panel[:, k] for k in (c, w): 8 row groups x 32 columns
-                const int k = tid & 31, grp = tid >> 5;
-                double sk = 0.0;
-                if (k > c && k < w) {
-                    for (int r = c + grp; r < rows; r += 8) {
-                        const double v = r == c ? 1.0 : (double)Vs[r][c];
-                        sk += v * (double)Vs[r][k];
-                    }
-                }
-                part[grp * kQP + k] = sk;
-            }
-            __syncthreads();
-            if (tid < kQP) {
-                double sk = 0.0;
-                for (int q = 0; q < 8; ++q) sk += part[q * kQP + tid];
-                wk[tid] = tc * sk;
-            }
-            __syncthreads();
-            for (int e = tid; e < (rows - c) * kQP; e += 256) {
-                const int r = c + e / kQP, k = e % kQP;
-                if (k > c && k < w) {
-                    const double v = r == c ? 1.0 : (double)Vs[r][c];
-                    Vs[r][k] = (float)((double)Vs[r][k] - v * wk[k]);
-                }
-            }
-            __syncthreads();
-        }
-        // explicit V: unit diagonal, zeros above
-        for (int e = tid; e < rows * kQP; e += 256) {
-            const int r = e / kQP, c = e % kQP;
-            if (c < w) { if (r == c) Vs[r][c] = 1.f; else if (r < c) Vs[r][c] = 0.f; }
-        }
-        __syncthreads();
-        // G = V^T V (upper part) in fp64
-        for (int e = tid; e < kQP * kQP; e += 256) {
-            const int i = e / kQP, j = e % kQP;
-            double sgv = 0.0;
-            if (i < j && j < w)
-                for (int r = i; r < rows; ++r) sgv += (double)Vs[r][i] * (double)Vs[r][j];
-            gsh[e] = sgv;
-            tsd[e] = 0.0;
-        }
-        __syncthreads();
-        // T: T_jj = tau_j, T[0:j, j] = -tau_j T[0:j, 0:j] G[0:j, j]
-        for (int j = 0; j < w; ++j) {
-            if (tid < j) {
-                double sum = 0.0;
-                for (int k = tid; k < j; ++k) sum += tsd[tid * kQP + k] * gsh[k * kQP + j];
-                tsd[tid * kQP + j] = -tau[j] * sum;
-            }
-            if (tid == j) tsd[j * kQP + j] = tau[j];
-            __syncthreads();
-        }
-        for (int e = tid; e < kQP * kQP; e += 256) {
-            const int i = e / kQP, j = e % kQP;
-            Ts[i][j] = (float)tsd[e];
-            Tq[(int64_t)p * kQP * kQP + e] = (float)tsd[e];
-        }
-        // keep V in Z's panel columns for the formation of Q
-        for (int e = tid; e < rows * w; e += 256) {
-            const int r = e / w, c = e % w;
-            Z[(int64_t)(j0 + r) * ldz + j0 + c] = Vs[r][c];
-        }
-        __syncthreads();
-        // trailing update, one 32-column tile per wave per round
-        const int first = j0 + w;
-        const int ntiles = (nb - first + 31) / 32;
-        for (int it = 0; it < (ntiles + 3) / 4; ++it) {
-            const int tile = it * 4 + wv;
-            wy_tile<true>(Z, ldz, nb, j0, rows, first + tile * 32, Vs, Ts, Wsh[wv], lane, tile < ntiles);
-        }
-    }
-
-    // form Q = H_1 ... H_nb from the identity, block reflectors applied last to first
-    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
-    for (int64_t e = tid; e < (int64_t)nb * nb; e += 256) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
-    __syncthreads();
-    for (int p = npanel - 1; p >= 0; --p) {
-        const int j0 = p * kQP, w = min(kQP, nb - j0), rows = nb - j0;
-        for (int e = tid; e < rows * kQP; e += 256) {
-            const int r = e / kQP, c = e % kQP;
-            Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
-        }
-        for (int e = tid; e < kQP * kQP; e += 256) Ts[e / kQP][e % kQP] = Tq[(int64_t)p * kQP * kQP + e];
-        __syncthreads();
-        const int ntiles = (nb - j0 + 31) / 32;
-        for (int it = 0; it < (ntiles + 3) / 4; ++it) {
-            const int tile = it * 4 + wv;
-            wy_tile<false>(Q, nb, nb, j0, rows, j0 + tile * 32, Vs, Ts, Wsh[wv], lane, tile < ntiles);
-        }
-    }
-    for (int64_t e = tid; e < (int64_t)nb * nb; e += 256)
-        if (neg[e % nb]) Q[e] = -Q[e];
-    if (tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
-}
-
 // ---- Householder QR, blocked, one launch per panel step (large blocks) ------------------------
-// The same algorithm as k_householder, split so the trailing updates spread over the whole GPU:
+// Panels of 32 columns, split over launches so the trailing updates spread over the whole GPU:
 //   k_qr_panel   one workgroup per block factors panel p (32 columns) in LDS, writes V into Z's
 //                panel columns, T into the workspace and the signs of R's diagonal;
 //   k_qr_update  one workgroup per (block, 64-column tile) applies the panel's block reflector:
@@ -948,12 +722,9 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
                             nbp, nblk, (const double *)Aw64, (const double *)V, (const int32_t *)state, ot);
             }
         } else {
-            // small blocks: one workgroup per block with Z in LDS; larger ones: one launch per panel step
-            const size_t hl = qr_layout(nb, true).total;
-            const bool lds = nb <= kQrLdsMaxNb && (int64_t)hl <= lds_max;
+            // blocks up to 512 wide: k_qr.hip's kernels; wider ones: one launch per panel step
             const size_t pl = qr_panel_layout(nb).total;
-            if (lds) (void)hipFuncSetAttribute((const void *)k_householder<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hl);
-            else (void)hipFuncSetAttribute((const void *)k_qr_panel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl);
+            (void)hipFuncSetAttribute((const void *)k_qr_panel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl);
             const int npanel = (nb + kQP - 1) / kQP;
             for (int it = 0; it < a.iters; ++it) {
                 DOBB_BGEMM(false, opA, opQ, outT);
@@ -961,11 +732,6 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
                 if (qr_block_supported(nb)) {
                     const hipError_t e = launch_qr_block(nb, nblk, cnt, Tm, tq, negs, ot.Q, ot.info, infov, s);
                     if (e != hipSuccess) return e;
-                    continue;
-                }
-                if (lds) {
-                    DOBB_LAUNCH("householder_qr_lds", s, k_householder<true>, dim3((unsigned)nblocks), dim3(256), hl, nb, nblk,
-                                Tm, tq, ot, infov);
                     continue;
                 }
                 for (int p = 0; p < npanel; ++p) {

@@ -63,6 +63,7 @@ struct ProjTable {
     const float *Q[kMaxMats];
     int8_t *S[kMaxMats];
     float *C[kMaxMats];
+    float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
     float mu[kMaxMats];
 };
 
@@ -122,6 +123,7 @@ __global__ void __launch_bounds__(256) k_project(int64_t m, int64_t n, int nb, i
                 const int64_t e = off + (int64_t)row * n + c0 + col;
                 if (SIGN) t.S[mat][e] = sign_code(acc[r]);
                 else t.C[mat][e] = acc[r];
+                if (t.Cout[mat]) t.Cout[mat][e] = acc[r];
             }
         }
     }
@@ -338,6 +340,7 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
             for (int i = 0; i < cnt; ++i) {
                 t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
                 t.S[i] = a.S[c0 + i]; t.C[i] = a.C[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+                t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
                 vec = vec && aligned16(t.M[i]) && aligned16(t.Q[i]);
             }
             dim3 grid((unsigned)(col_tiles * nblk * cnt), (unsigned)row_tiles);

@@ -152,6 +152,7 @@ struct ProjTable16 {
     const void *G[kMaxMats];
     const uint16_t *planes[kMaxMats];
     uint8_t *S[kMaxMats];
+    float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
     float mu[kMaxMats];
 };
 
@@ -276,6 +277,7 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
     // sign bytes, stored with row stride nblk * ldp (block b at column offset b * ldp)
     uint8_t *const __restrict__ S = t.S[mat] + (int64_t)b * ldp;
     const int64_t lds_ = (int64_t)nblk * ldp;
+    float *const Cout = t.Cout[mat];
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
         const int col = 32 * (cg + CW * c) + acc_col(lane);
@@ -285,7 +287,10 @@ __global__ void __launch_bounds__(512) k_proj_bf16(int64_t m, int64_t n, int nb,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t rr = r0 + (rg * C::RT + i) * 32 + acc_row(r, lane);
-                if (rr < m) S[rr * lds_ + col] = sign_f16_hi(acc[i][c][r]);
+                if (rr < m) {
+                    S[rr * lds_ + col] = sign_f16_hi(acc[i][c][r]);
+                    if (Cout) Cout[rr * n + (int64_t)b * nb + col] = acc[i][c][r];
+                }
             }
     }
 }
@@ -458,6 +463,7 @@ hipError_t launch_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s
         for (int i = 0; i < cnt; ++i) {
             t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i];
             t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+            t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
         }
         const bool gbf = a.g_dtype == DOBB_BF16;
         const bool nest = a.hp[c0].nesterov != 0;

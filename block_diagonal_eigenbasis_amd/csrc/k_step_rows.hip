@@ -57,6 +57,7 @@ struct ProjRowsTable {
     uint8_t *S[kMaxMats];
     float *C[kMaxMats];        // column-l2: the coefficients (m x n fp32)
     double *part[kMaxMats];    // column-l2: per row tile, the column sums of squares ([tiles][n])
+    float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
     float mu[kMaxMats];
 };
 // LDS: Q_b^T (two fp16 planes), the P tile (fp32) and the sign tile
@@ -251,10 +252,15 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             }
             __syncthreads();
             float *Cb = t.C[mat] + (int64_t)b * nb;
+            float *Co = t.Cout[mat] ? t.Cout[mat] + (int64_t)b * nb : nullptr;
             for (int e = tid; e < TR * q; e += kRT) {
                 const int r = e / q, c = 4 * (e - r * q);
                 const int64_t row = tile * TR + r;
-                if (row < m) *(f32x4 *)(Cb + row * n + c) = *(const f32x4 *)(pc + r * pld + c);
+                if (row < m) {
+                    const f32x4 cv = *(const f32x4 *)(pc + r * pld + c);
+                    *(f32x4 *)(Cb + row * n + c) = cv;
+                    if (Co) *(f32x4 *)(Co + row * n + c) = cv;
+                }
             }
             if (tid < nb) {
                 double sq = 0.0;
@@ -269,6 +275,8 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
             continue;
         }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t -> LDS
+        float *const Co = t.Cout[mat];
+        const int64_t crow = tile * TR + 32 * rt + (lane & 31);
 #pragma unroll
         for (int j = 0; j < kCPG; ++j) {
             const int ch = cg * kCPG + j;
@@ -278,6 +286,10 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
                 const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
                                     (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
                 if (ch < NCH && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
+                if (Co && ch < NCH && col < nb && crow < m)
+                    *(f32x4 *)(Co + crow * n + (int64_t)b * nb + col) =
+                        f32x4{__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sexp), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sexp),
+                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sexp), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sexp)};
             }
         }
         __syncthreads();
@@ -570,6 +582,7 @@ hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream
         for (int i = 0; i < cnt; ++i) {
             t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
             t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+            t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
         }
         const size_t sh = proj_rows_lds(nb, TR, ldp);
         const bool gbf = a.g_dtype == DOBB_BF16;
@@ -639,6 +652,7 @@ hipError_t launch_proj_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s)
     for (int i = 0; i < cnt; ++i) {
         t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
         t.C[i] = a.C[c0 + i]; t.part[i] = a.colpart[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+        t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
     }
     const int ldp = step_bf16_ldp(nb);
     const size_t sh = proj_rows_lds(nb, TR, ldp);

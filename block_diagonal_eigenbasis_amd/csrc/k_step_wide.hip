@@ -135,6 +135,7 @@ struct ProjWideTable {
     const void *G[kMaxMats];
     const uint16_t *planes[kMaxMats];
     uint8_t *S[kMaxMats];
+    float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
     float mu[kMaxMats];
 };
 // LDS: two Q^T slices (2 planes each; the sign tile overlays them after the products), the P chunk
@@ -338,6 +339,8 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
         }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 8 qq + 4 (l / 32) + 0..3 -> LDS
         __syncthreads();   // every wave is done with the Q slices that the sign tile overlays
+        float *const Co = t.Cout[mat];
+        const int64_t crow = tile * kTR + prow;
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const int ch = cg + 2 * j;
@@ -347,6 +350,10 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                 const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
                                     (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
                 if (ch < nct && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
+                if (Co && ch < nct && col < nb && crow < m)
+                    *(f32x4 *)(Co + crow * n + (int64_t)b * nb + col) =
+                        f32x4{__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sreg), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sreg),
+                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sreg), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sreg)};
             }
         }
         __syncthreads();
@@ -599,6 +606,7 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
         for (int i = 0; i < cnt; ++i) {
             t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i];
             t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+            t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
         }
         const size_t sh = proj_wide_lds(nb, ldp);
         const bool gbf = a.g_dtype == DOBB_BF16;

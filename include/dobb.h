@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DOBB_ABI_VERSION 1
+#define DOBB_ABI_VERSION 2
 
 struct ihipStream_t;
 typedef struct ihipStream_t *dobb_stream_t; /* the same type as hipStream_t */
@@ -86,9 +86,12 @@ typedef struct {
 } dobb_hparams;
 
 /* Bytes of workspace the op needs for `count` matrices of the given shapes.  N (tokens per capture)
- * is used by DOBB_OP_ACCUMULATE only; variant is the dobb_norm for DOBB_OP_STEP (sign needs 1 byte
- * per weight entry, the other norms 4) and is ignored otherwise.  The refresh figure covers both
- * modes.  Returns 0 for bad arguments and for an op that needs no scratch. */
+ * is used by DOBB_OP_ACCUMULATE only.  For DOBB_OP_STEP, variant is the dobb_norm (sign needs about
+ * 1 byte per weight entry, the other norms 4); for DOBB_OP_STEP and DOBB_OP_REFRESH, adding
+ * DOBB_WS_BF16_BASIS to variant sizes the call for a bf16 basis (an fp32 copy of each basis in the
+ * workspace).  The refresh figure covers every mode.  Returns 0 for bad arguments and for an op that
+ * needs no scratch. */
+#define DOBB_WS_BF16_BASIS 16
 size_t dobb_workspace_size(dobb_op op, int count, const dobb_shape *shapes, int64_t N, int32_t variant);
 
 /* ------------------------------------------------------------------------------------------------
@@ -115,12 +118,14 @@ dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtyp
  *   ORTH_ITER: iters = k >= 1 steps of  Q_b <- qr(A_b Q_b).Q  (Householder, diag(R) > 0) from the
  *              Q passed in (which must hold a basis); lambda_b receives the Rayleigh quotients
  *              q_j^T A_b q_j.  warm_start and tol are ignored.
- * A: device fp32 B x nb x nb (symmetric; only read).  Q: device fp32 B x nb x nb, in/out.
- * lambda: device fp32 B x nb or NULL.  info: device int32 [B] or NULL; receives the sweeps used
- * (EXACT, -1 if iters sweeps did not converge) or k (ORTH_ITER).
+ * A: device fp32 B x nb x nb (symmetric; only read).  Q: device B x nb x nb, in/out, stored as
+ * q_dtype: DOBB_F32, or DOBB_BF16 (Table 18's principal setting, fp32 moments with a bf16 basis: the
+ * refresh reads the bf16 basis exactly, computes in fp32/fp64 as above and rounds the result to
+ * nearest even once).  lambda: device fp32 B x nb or NULL.  info: device int32 [B] or NULL;
+ * receives the sweeps used (EXACT, -1 if iters sweeps did not converge) or k (ORTH_ITER).
  * -------------------------------------------------------------------------------------------------*/
-dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, float *Q, float *lambda,
-                               dobb_refresh_mode mode, int iters, int warm_start, float tol,
+dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, void *Q, dobb_dtype q_dtype,
+                               float *lambda, dobb_refresh_mode mode, int iters, int warm_start, float tol,
                                int32_t *info, void *ws, size_t ws_bytes, dobb_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
@@ -129,31 +134,37 @@ dobb_status dobb_refresh_basis(const dobb_shape *s, const float *A, float *Q, fl
  *   M <- mu M + G;   P = M (or G + mu M with nesterov);   C_b = P_b Q_b;
  *   U_b = sign(C_b) Q_b^T   (sign(0) = 0);   W <- W - lr (update_scale U + weight_decay W).
  * W: device m x n, fp32 or bf16 (bf16 is updated in fp32 and rounded to nearest even).
- * G: device m x n, fp32 or bf16.  M: device fp32 m x n, in/out.  Q: device fp32 B x nb x nb.
+ * G: device m x n, fp32 or bf16.  M: device fp32 m x n, in/out.  Q: device B x nb x nb in q_dtype
+ * (fp32, or bf16 as stored by dobb_refresh_basis; bf16 entries are used exactly).
  * hp: host pointer.  U_out: device fp32 m x n or NULL (receives U before scaling).
+ * C_out: device fp32 m x n or NULL; receives the coefficients C_b = P_b Q_b of every block in block
+ * b's columns, as the projection computed them before normalisation (for verification; writing
+ * them adds 4 bytes per entry of traffic).
  * -------------------------------------------------------------------------------------------------*/
 dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,
-                      float *M, const float *Q, const dobb_hparams *hp, float *U_out, void *ws,
-                      size_t ws_bytes, dobb_stream_t stream);
+                      float *M, const void *Q, dobb_dtype q_dtype, const dobb_hparams *hp, float *U_out,
+                      float *C_out, void *ws, size_t ws_bytes, dobb_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Grouped forms over a matrix set: the same semantics for `count` matrices, enqueued together.
  * shapes, the pointer arrays and hp are HOST arrays of length count whose entries are device
- * pointers (U_out may be NULL, or an array with NULL entries; ldx may be NULL for ldx = n).  The
- * workspace is sized by dobb_workspace_size(op, count, shapes, N, variant) and shared by the whole
- * group.  All hp entries of one dobb_step_grouped call must share norm and nesterov.
+ * pointers (U_out and C_out may be NULL, or arrays with NULL entries; ldx may be NULL for ldx = n).
+ * The workspace is sized by dobb_workspace_size(op, count, shapes, N, variant) and shared by the whole
+ * group.  All hp entries of one dobb_step_grouped call must share norm and nesterov; all matrices of
+ * a call share the dtypes given.
  * -------------------------------------------------------------------------------------------------*/
 dobb_status dobb_accumulate_moment_grouped(int count, const dobb_shape *shapes, const void *const *X,
                                            dobb_dtype x_dtype, int64_t N, const int64_t *ldx, float beta,
                                            float *const *A, void *ws, size_t ws_bytes, dobb_stream_t stream);
 dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, const float *const *A,
-                                       float *const *Q, float *const *lambda, dobb_refresh_mode mode,
-                                       int iters, int warm_start, float tol, int32_t *const *info,
-                                       void *ws, size_t ws_bytes, dobb_stream_t stream);
+                                       void *const *Q, dobb_dtype q_dtype, float *const *lambda,
+                                       dobb_refresh_mode mode, int iters, int warm_start, float tol,
+                                       int32_t *const *info, void *ws, size_t ws_bytes, dobb_stream_t stream);
 dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype,
                               const void *const *G, dobb_dtype g_dtype, float *const *M,
-                              const float *const *Q, const dobb_hparams *hp, float *const *U_out,
-                              void *ws, size_t ws_bytes, dobb_stream_t stream);
+                              const void *const *Q, dobb_dtype q_dtype, const dobb_hparams *hp,
+                              float *const *U_out, float *const *C_out, void *ws, size_t ws_bytes,
+                              dobb_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Kernel timer (tracing).  While enabled, every kernel the library enqueues is bracketed by a pair

@@ -77,14 +77,31 @@ def _pool(cores: int | None):
     return ThreadPoolExecutor(max_workers=max(1, cores or os.cpu_count() or 1))
 
 
-def accumulate(X, nb: int, A=None, beta: float = 0.0) -> np.ndarray:
-    """A_b <- beta A_b + (1-beta)/N sum_t x_{t,b} x_{t,b}^T for every block b (X is N x n)."""
+def accumulate(X, nb: int, A=None, beta: float = 0.0, cores: int | None = 1) -> np.ndarray:
+    """A_b <- beta A_b + (1-beta)/N sum_t x_{t,b} x_{t,b}^T for every block b (X is N x n).
+
+    The blocks are independent; with cores > 1 they are shared among threads (each block's sum is
+    the same single loop over the tokens)."""
     X = _f64(X)
     N, n = X.shape
     assert n % nb == 0
     B = n // nb
     A = np.zeros((B, nb, nb)) if A is None else _f64(A).copy()
-    _load().oracle_accumulate(N, n, nb, n, _ptr(X), float(beta), _ptr(A))
+    lib = _load()
+    if not cores or cores == 1:
+        lib.oracle_accumulate(N, n, nb, n, _ptr(X), float(beta), _ptr(A))
+        return A
+    dp = ctypes.POINTER(ctypes.c_double)
+    base = X.ctypes.data
+
+    def one(b):
+        xb = ctypes.cast(base + 8 * b * nb, dp)      # block b's columns, leading dimension n
+        ab = np.ascontiguousarray(A[b])
+        lib.oracle_accumulate(N, nb, nb, n, xb, float(beta), _ptr(ab))
+        A[b] = ab
+
+    with _pool(cores) as ex:
+        list(ex.map(one, range(B)))
     return A
 
 
@@ -145,14 +162,32 @@ def orth_iter(A, Qprev, k: int = 1, cores: int | None = None):
 
 
 def step(W, G, M, Q, nb: int, lr: float, weight_decay: float, momentum: float, update_scale: float,
-         nesterov: bool = False, norm: int = NORM_SIGN):
-    """One Dobb step on an m x n weight.  Returns (W_new, M_new, U), all float64 (m, n)."""
+         nesterov: bool = False, norm: int = NORM_SIGN, cores: int | None = 1):
+    """One Dobb step on an m x n weight.  Returns (W_new, M_new, U), all float64 (m, n).
+
+    With the sign and identity norms every row is independent, so with cores > 1 row chunks are
+    shared among threads; column-l2 couples the rows and runs whole."""
     W, G, M, Q = _f64(W).copy(), _f64(G), _f64(M).copy(), _f64(Q)
     m, n = W.shape
     assert n % nb == 0 and Q.shape == (n // nb, nb, nb)
     U = np.zeros((m, n))
-    _load().oracle_step(m, n, nb, _ptr(W), _ptr(G), _ptr(M), _ptr(Q), float(lr), float(weight_decay),
-                        float(momentum), float(update_scale), int(bool(nesterov)), int(norm), _ptr(U))
+    lib = _load()
+    args = (float(lr), float(weight_decay), float(momentum), float(update_scale), int(bool(nesterov)), int(norm))
+    if not cores or cores == 1 or norm == NORM_COL_L2 or m < 2:
+        lib.oracle_step(m, n, nb, _ptr(W), _ptr(G), _ptr(M), _ptr(Q), *args, _ptr(U))
+        return W, M, U
+    nchunk = min(m, 4 * cores)
+    bounds = np.linspace(0, m, nchunk + 1).astype(int)
+
+    def one(c):
+        r0, r1 = bounds[c], bounds[c + 1]
+        if r1 > r0:
+            w, mm, u = W[r0:r1], M[r0:r1], U[r0:r1]          # contiguous row slices, written in place
+            g = np.ascontiguousarray(G[r0:r1])
+            lib.oracle_step(r1 - r0, n, nb, _ptr(w), _ptr(g), _ptr(mm), _ptr(Q), *args, _ptr(u))
+
+    with _pool(cores) as ex:
+        list(ex.map(one, range(nchunk)))
     return W, M, U
 
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert _abi.dobb_abi_version() == 1
+    assert _abi.dobb_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert _abi.status_string(st)
     assert "unknown" in _abi.status_string(42)
@@ -47,7 +47,7 @@ def _shape(m, n, nb):
 def test_step_shape_errors(m, n, nb, status):
     s = _shape(m, n, nb)
     hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
-    st = _abi.lib().dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None)
+    st = _abi.lib().dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 1 << 30, None)
     assert st == status
 
 
@@ -55,17 +55,17 @@ def test_step_argument_errors():
     L = _abi.lib()
     s = _shape(64, 64, 16)
     hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
-    assert L.dobb_step(None, FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -1
-    assert L.dobb_step(ctypes.byref(s), None, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -1
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -1
-    assert L.dobb_step(ctypes.byref(s), FAKE, 7, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -3
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 5, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 1 << 30, None) == -3
+    assert L.dobb_step(None, FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), None, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, None, None, None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), FAKE, 7, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 1 << 30, None) == -3
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 5, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 1 << 30, None) == -3
     bad = _abi.make_hparams(0.1, 0.0, 0.9, 0.2, norm=9)
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(bad), None, FAKE, 1 << 30, None) == -1
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(bad), None, None, FAKE, 1 << 30, None) == -1
     # workspace: missing, too small, misaligned
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, None, 0, None) == -4
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None, FAKE, 16, None) == -4
-    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, ctypes.byref(hp), None,
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, None, 0, None) == -4
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE, 16, None) == -4
+    assert L.dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None,
                        ctypes.c_void_p(0x10010), 1 << 30, None) == -4
 
 
@@ -95,14 +95,15 @@ def test_refresh_argument_errors():
     L = _abi.lib()
     s = _shape(1, 64, 16)
 
-    def call(A=FAKE, Q=FAKE, mode=0, iters=0, tol=0.0, ws=None, wsb=0):
-        return L.dobb_refresh_basis(ctypes.byref(s), A, Q, None, mode, iters, 0, tol, None, ws, wsb, None)
+    def call(A=FAKE, Q=FAKE, mode=0, iters=0, tol=0.0, ws=None, wsb=0, qdt=0):
+        return L.dobb_refresh_basis(ctypes.byref(s), A, Q, qdt, None, mode, iters, 0, tol, None, ws, wsb, None)
     assert call(A=None) == -1
     assert call(Q=None) == -1
     assert call(mode=4) == -1
     assert call(mode=1, iters=0) == -1      # orthogonal iteration needs k >= 1
     assert call(iters=-2) == -1
     assert call(tol=-1.0) == -1
+    assert call(qdt=2) == -3                # basis dtype fp32 or bf16
     assert call() == -4                     # the refresh always needs a workspace
 
 
@@ -119,6 +120,11 @@ def test_workspace_sizes():
     big = ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 60, 0, 0)
     assert big == ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 48, 0, 0)
     assert big > ws(_abi.DOBB_OP_STEP, [(64, 64, 16)] * 16, 0, 0)
+    # a bf16 basis adds an fp32 copy of every basis of a launch chunk
+    bf = _abi.DOBB_WS_BF16_BASIS
+    assert ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, bf) >= ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, 0) + 4 * 768 * 192
+    assert ws(_abi.DOBB_OP_REFRESH, [(1, 768, 192)] * 3, 0, bf) >= ws(_abi.DOBB_OP_REFRESH, [(1, 768, 192)] * 3) + 3 * 4 * 768 * 192
+    assert ws(_abi.DOBB_OP_STEP, [(768, 768, 192)], 0, bf | 7) == 0
 
 
 def test_grouped_rejects_mixed_norms():
@@ -126,8 +132,26 @@ def test_grouped_rejects_mixed_norms():
     shapes = (_abi.Shape * 2)(_shape(64, 64, 16), _shape(64, 64, 16))
     hps = (_abi.HParams * 2)(_abi.make_hparams(0.1, 0, 0.9, 0.2), _abi.make_hparams(0.1, 0, 0.9, 0.2, norm=2))
     P = (ctypes.c_void_p * 2)(0x10000, 0x20000)
-    st = L.dobb_step_grouped(2, shapes, P, 0, P, 0, P, P, hps, None, FAKE, 1 << 30, None)
+    st = L.dobb_step_grouped(2, shapes, P, 0, P, 0, P, P, 0, hps, None, None, FAKE, 1 << 30, None)
     assert st == -1
+
+
+def test_step_rejects_bad_basis_dtype():
+    s = _shape(64, 64, 16)
+    hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
+    st = _abi.lib().dobb_step(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 3, ctypes.byref(hp), None, None, FAKE,
+                              1 << 30, None)
+    assert st == _abi.DOBB_ERR_DTYPE
+
+
+def test_grouped_binding_rejects_mixed_dtypes():
+    """The C ABI takes one dtype per argument of a grouped call; a list mixing fp32 and bf16 tensors
+    is refused before any pointer is passed (an element-size mismatch would run past a buffer)."""
+    import torch
+    xs = [torch.zeros(4, 8), torch.zeros(4, 8, dtype=torch.bfloat16)]
+    with pytest.raises(TypeError, match="same dtype"):
+        _abi._common_dtype(xs, "X")
+    assert _abi._common_dtype([torch.zeros(2), torch.zeros(3)], "X") == _abi.DOBB_F32
 
 
 def test_binding_rejects_cpu_tensors():

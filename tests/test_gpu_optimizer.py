@@ -140,3 +140,123 @@ def test_optimizer_cadence_matches_entry_points(streams):
         assert torch.equal(g.M[i], M_ref[i]), f"M[{i}]"
         assert torch.equal(g.A[i], A_ref[i]), f"A[{i}]"
         assert torch.equal(g.Q[i], Q_ref[i]), f"Q[{i}]"
+
+
+def test_lr_scheduler_and_param_groups_take_effect():
+    """lr, weight decay and momentum are read from param_groups at every step: a StepLR schedule
+    halving lr each step, and a second group with its own weight decay, match the entry points
+    called with those values, bit for bit."""
+    rng = RNG(94)
+    dims = [(96, 256), (64, 128)]
+    params = [torch.nn.Parameter(t32(0.02 * rng.standard_normal((m, n)))) for m, n in dims]
+    opt = Dobb([{"params": [params[0]]}, {"params": [params[1]], "weight_decay": 0.3}], lr=4e-3,
+               weight_decay=0.1, momentum=0.9, blocks=2, refresh_period=1000)
+    sched = torch.optim.lr_scheduler.StepLR(opt, step_size=1, gamma=0.5)
+    W_ref = [p.detach().clone() for p in params]
+    M_ref = [torch.zeros(m, n, device=DEV) for m, n in dims]
+    Q_ref = [torch.eye(n // 2, device=DEV).expand(2, n // 2, n // 2).contiguous() for _, n in dims]
+    lr = 4e-3
+    for t in range(4):
+        grads = [t32(rng.standard_normal((m, n))) for m, n in dims]
+        for p, g in zip(params, grads):
+            p.grad = g
+        if t == 2:
+            opt.param_groups[1]["momentum"] = 0.5
+        opt.step()
+        sched.step()
+        for i, (m, n) in enumerate(dims):
+            wd = 0.1 if i == 0 else 0.3
+            mu = 0.5 if (i == 1 and t >= 2) else 0.9
+            hp = dobb.make_hparams(lr, wd, mu, default_update_scale(m, n))
+            dobb.dobb_step(W_ref[i], grads[i], M_ref[i], Q_ref[i], n // 2, hp)
+        lr *= 0.5
+    torch.cuda.synchronize()
+    for i in range(len(dims)):
+        assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
+
+
+def test_mixed_dtypes_are_split_per_call():
+    """A set mixing fp32 and bf16 weights, activations and gradients (as under autocast): every
+    grouped call is issued per dtype, and each weight ends bit for bit where the single-matrix entry
+    points leave it."""
+    rng = RNG(95)
+    shapes = [(96, 256, 64), (64, 128, 64), (80, 256, 128), (48, 128, 32)]
+    wdts = [torch.float32, torch.bfloat16, torch.float32, torch.bfloat16]
+    xdts = [torch.bfloat16, torch.float32, torch.float32, torch.bfloat16]
+    gdts = [torch.float32, torch.float32, torch.bfloat16, torch.bfloat16]
+    Ws = [t32(0.02 * rng.standard_normal((m, n))).to(d) for (m, n, _), d in zip(shapes, wdts)]
+    Gs = [t32(rng.standard_normal((m, n))).to(d) for (m, n, _), d in zip(shapes, gdts)]
+    xs = [t32(workload.activations(300 + 50 * i, n, 0.15, rng)).to(d)
+          for i, ((_, n, _), d) in enumerate(zip(shapes, xdts))]
+    g = DobbGroup([w.clone() for w in Ws], [nb for _, _, nb in shapes], grads=Gs, weight_decay=0.1, momentum=0.9)
+    assert len(g._parts) == 2
+    g.accumulate(xs, 0.0)
+    g.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=False)
+    g.step()
+    g.refresh_step(xs, 0.9, dobb.DOBB_REFRESH_ORTH_ITER, 1)
+    for i, (m, n, nb) in enumerate(shapes):
+        W = Ws[i].clone()
+        M = torch.zeros(m, n, device=DEV)
+        A = torch.zeros(n // nb, nb, nb, device=DEV)
+        Q = torch.empty_like(A)
+        hp = dobb.make_hparams(2.5e-3, 0.1, 0.9, default_update_scale(m, n))
+        dobb.dobb_accumulate_moment(xs[i], A, nb, 0.0)
+        dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_EXACT)
+        dobb.dobb_step(W, Gs[i], M, Q, nb, hp)
+        dobb.dobb_accumulate_moment(xs[i], A, nb, 0.9)
+        dobb.dobb_refresh_basis(A, Q, dobb.DOBB_REFRESH_ORTH_ITER, iters=1, warm_start=True)
+        dobb.dobb_step(W, Gs[i], M, Q, nb, hp)
+        torch.cuda.synchronize()
+        assert torch.equal(g.W[i], W), f"W[{i}]"
+        assert torch.equal(g.A[i], A) and torch.equal(g.Q[i], Q) and torch.equal(g.M[i], M), f"state {i}"
+
+
+def test_capture_all_micro_batches_and_bf16_basis():
+    """capture="all" (Table 17) pools every micro-batch of a refresh iteration into one capture;
+    basis_dtype=bf16 (Table 18) keeps Q in bf16.  Both match the entry points bit for bit."""
+    rng = RNG(96)
+    dims = [(96, 256), (64, 512)]
+    mods = [torch.nn.Linear(n, m, bias=False).to(DEV) for m, n in dims]
+    params = [mod.weight for mod in mods]
+    with torch.no_grad():
+        for p in params:
+            p.copy_(t32(0.02 * rng.standard_normal(tuple(p.shape))))
+    opt = Dobb(params, lr=2.5e-3, weight_decay=0.1, momentum=0.9, blocks=2, refresh_period=2, capture="all",
+               basis_dtype=torch.bfloat16)
+    hooks = opt.attach_capture_hooks(mods)
+    nbs = [n // 2 for _, n in dims]
+    W_ref = [p.detach().clone() for p in params]
+    M_ref = [torch.zeros(m, n, device=DEV) for m, n in dims]
+    A_ref = [torch.zeros(n // nb, nb, nb, device=DEV) for (_, n), nb in zip(dims, nbs)]
+    Q_ref = [torch.eye(nb, device=DEV, dtype=torch.bfloat16).expand(n // nb, nb, nb).contiguous()
+             for (_, n), nb in zip(dims, nbs)]
+    refreshed = False
+    for t in range(4):
+        captures = opt.wants_capture()
+        mbs = [[t32(workload.activations(128, n, 0.15, rng)) for _, n in dims] for _ in range(3)]
+        with torch.no_grad():
+            for mb in mbs:
+                for mod, x in zip(mods, mb):
+                    mod(x)
+        grads = [t32(rng.standard_normal((m, n))) for m, n in dims]
+        for p, gr in zip(params, grads):
+            p.grad = gr
+        opt.step()
+        for i, nb in enumerate(nbs):
+            if captures:
+                x_all = torch.cat([mb[i] for mb in mbs], 0)
+                dobb.dobb_accumulate_moment(x_all, A_ref[i], nb, 0.9 if refreshed else 0.0)
+                mode = dobb.DOBB_REFRESH_ORTH_ITER if refreshed else dobb.DOBB_REFRESH_EXACT
+                dobb.dobb_refresh_basis(A_ref[i], Q_ref[i], mode, iters=1 if refreshed else 0, warm_start=refreshed)
+            m, n = dims[i]
+            dobb.dobb_step(W_ref[i], grads[i], M_ref[i], Q_ref[i], nb,
+                           dobb.make_hparams(2.5e-3, 0.1, 0.9, default_update_scale(m, n)))
+        refreshed = refreshed or captures
+    torch.cuda.synchronize()
+    for h in hooks:
+        h.remove()
+    g = opt._group
+    for i in range(len(dims)):
+        assert g.Q[i].dtype == torch.bfloat16
+        assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
+        assert torch.equal(g.A[i], A_ref[i]) and torch.equal(g.Q[i], Q_ref[i]), f"state {i}"

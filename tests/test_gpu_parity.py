@@ -65,6 +65,8 @@ def random_basis(B, nb, rng):
     (1000, 800, 400, torch.bfloat16),    # wide bf16 blocks: 13 tile rows, 3 token splits, ragged N
     (4500, 512, 512, torch.bfloat16),    # widest wide block: 3 workgroups per block, 2 splits
     (333, 272, 136, torch.bfloat16),     # wide, nb % 32 != 0, one split (EMA fused in the kernel)
+    (1000, 512, 128, torch.bfloat16),    # the 7B-style block width: a full 128-wide bf16 tile, ragged N
+    (777, 384, 128, torch.float32),      # nb = 128 with fp32 activations, ragged N
 ])
 def test_accumulate_matches_oracle(N, n, nb, dtype):
     print(f"accumulate N={N} n={n} nb={nb} {dtype}", flush=True)
@@ -111,7 +113,7 @@ def _check_eig(A32, lam, Q, lam_ref, Q_ref):
 
 
 @pytest.mark.parametrize("N,n,nb", [(4096, 768, 192), (2048, 96, 48), (2048, 75, 25), (4096, 200, 100),
-                                    (4096, 400, 400)])
+                                    (4096, 400, 400), (8192, 256, 128)])
 def test_refresh_exact_matches_oracle(N, n, nb):
     print(f"refresh exact n={n} nb={nb}", flush=True)
     rng = RNG(7 * n + nb)
@@ -129,9 +131,9 @@ def test_refresh_exact_matches_oracle(N, n, nb):
     _check_eig(A32, host(lam), host(Q), lam_ref, Q_ref)
 
 
-def test_refresh_exact_warm_start():
-    rng = RNG(11)
-    n, nb = 384, 96
+@pytest.mark.parametrize("n,nb", [(384, 96), (384, 128)])
+def test_refresh_exact_warm_start(n, nb):
+    rng = RNG(11 + nb)
     A1 = t32(oracle.accumulate(workload.activations(4096, n, 0.15, rng), nb))
     Q = torch.empty(n // nb, nb, nb, device=DEV)
     dobb.dobb_refresh_basis(A1, Q, dobb.DOBB_REFRESH_EXACT)
@@ -160,7 +162,8 @@ def test_refresh_exact_reports_non_convergence():
 # ------------------------------------------------------------------------------------------------
 # orthogonal-iteration refresh
 
-@pytest.mark.parametrize("n,nb,k", [(768, 192, 1), (200, 100, 2), (75, 25, 1), (400, 400, 1), (260, 130, 1), (10, 5, 3)])
+@pytest.mark.parametrize("n,nb,k", [(768, 192, 1), (200, 100, 2), (75, 25, 1), (400, 400, 1), (260, 130, 1), (10, 5, 3),
+                                    (384, 128, 1)])
 def test_refresh_orth_iter_matches_oracle(n, nb, k):
     print(f"refresh orth_iter n={n} nb={nb} k={k}", flush=True)
     rng = RNG(13 * n + k)
@@ -221,11 +224,12 @@ def _check_momentum(M_gpu, M0, G, mu, M_ref):
     assert np.all(err <= 6e-8 * np.abs(M_ref) + 1e-30)
 
 
-def _run_step(W, G, M, Q, nb, hp, norm):
+def _run_step(W, G, M, Q, nb, hp, norm, want_c=False):
     W, M = W.clone(), M.clone()
     U = torch.empty(W.shape, device=DEV)
-    dobb.dobb_step(W, G, M, Q, nb, dobb.make_hparams(norm=norm, **hp), U_out=U)
-    return W, M, U
+    C = torch.full(W.shape, float("nan"), device=DEV) if want_c else None
+    dobb.dobb_step(W, G, M, Q, nb, dobb.make_hparams(norm=norm, **hp), U_out=U, C_out=C)
+    return (W, M, U, C) if want_c else (W, M, U)
 
 
 @pytest.mark.parametrize("m,n,nb", [(768, 768, 192), (130, 96, 48), (70, 75, 25), (200, 800, 400), (64, 256, 128),
@@ -235,16 +239,18 @@ def _run_step(W, G, M, Q, nb, hp, norm):
 def test_step_matches_oracle(m, n, nb):
     print(f"step m={m} n={n} nb={nb}", flush=True)
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=m + n + nb)
-    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    W_s, M_s, U_s, C_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN, want_c=True)
     _, _, U_id = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_IDENTITY)
     W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
                                 hp["update_scale"])
     _check_momentum(M_s, M, G, hp["momentum"], M_r)
     B = n // nb
-    U_sh, U_idh, W_sh, W0 = host(U_s), host(U_id), host(W_s), host(W)
+    U_sh, U_idh, W_sh, W0, C_sh = host(U_s), host(U_id), host(W_s), host(W), host(C_s)
     for b in range(B):
         sl = slice(b * nb, (b + 1) * nb)
         C_ref = M_r[:, sl] @ Qh[b]
+        # the coefficients of the sign path's own projection kernel
+        assert np.linalg.norm(C_sh[:, sl] - C_ref) <= 1e-5 * np.linalg.norm(C_ref), "projection C"
         C_gpu = U_idh[:, sl] @ Qh[b]                        # identity mode: U = C Q^T
         assert np.linalg.norm(C_gpu - C_ref) <= 1e-5 * np.linalg.norm(C_ref)
         S_gpu = np.rint(U_sh[:, sl] @ Qh[b])                # recover the sign codes
@@ -272,14 +278,17 @@ def test_step_rows_across_the_fp32_range(m, n, nb):
     ramp[::3, :] = np.float32(10.0 ** (6.0 * (np.arange(n) % nb) / nb))   # within each block
     M = t32(host(M) * rs * ramp)
     G = t32(host(G) * rs * ramp)
-    W_s, M_s, U_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    W_s, M_s, U_s, C_s = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN, want_c=True)
     W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
                                 hp["update_scale"])
     _check_momentum(M_s, M, G, hp["momentum"], M_r)
-    U_sh = host(U_s)
+    U_sh, C_sh = host(U_s), host(C_s)
     for b in range(n // nb):
         sl = slice(b * nb, (b + 1) * nb)
         C_ref = M_r[:, sl] @ Qh[b]
+        # each row's coefficients to 1e-5 of that row's norm, whatever its scale
+        rn = np.linalg.norm(C_ref, axis=1)
+        assert np.all(np.linalg.norm(C_sh[:, sl] - C_ref, axis=1) <= 1e-5 * rn), "projection C per row"
         S_gpu = np.rint(U_sh[:, sl] @ Qh[b])
         live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref), axis=1, keepdims=True)
         assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the row's dead zone"
@@ -294,6 +303,76 @@ def test_step_identity_round_trip():
     G.zero_()
     _, M1, U = _run_step(W, G, M, Q, 64, hp, dobb.DOBB_NORM_IDENTITY)
     np.testing.assert_allclose(host(U), host(M), atol=2e-6 * float(M.abs().max()))
+
+
+@pytest.mark.parametrize("m,n,nb", [(300, 400, 100), (200, 800, 400), (64, 256, 128), (100, 960, 480), (70, 75, 25)])
+def test_step_bf16_basis_matches_oracle(m, n, nb):
+    """bf16 basis storage (Table 18's principal setting): the step uses the stored bf16 entries
+    exactly, so the oracle fed the same values (widened to fp64) is held to the fp32 bars: the
+    coefficients to 1e-5, no sign mismatch outside the dead zone, U = sign(C) Q^T to 1e-5."""
+    print(f"step bf16 basis m={m} n={n} nb={nb}", flush=True)
+    Q, _, W, G, M, hp = _step_case(m, n, nb, seed=83 + nb)
+    Qb = Q.to(torch.bfloat16)
+    Qh = host(Qb)                      # the bf16 values both sides use
+    W_s, M_s, U_s, C_s = _run_step(W, G, M, Qb, nb, hp, dobb.DOBB_NORM_SIGN, want_c=True)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"])
+    _check_momentum(M_s, M, G, hp["momentum"], M_r)
+    U_sh, C_sh = host(U_s), host(C_s)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = M_r[:, sl] @ Qh[b]
+        assert np.linalg.norm(C_sh[:, sl] - C_ref) <= 1e-5 * np.linalg.norm(C_ref)
+        S_gpu = np.rint(U_sh[:, sl] @ np.linalg.inv(Qh[b]).T)   # the bf16 basis is orthonormal only to ~1e-3
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref))
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the dead zone"
+        R = S_gpu @ Qh[b].T
+        assert np.linalg.norm(U_sh[:, sl] - R) <= 1e-5 * np.linalg.norm(R)
+    assert np.mean(np.abs(U_sh - U_r) > 1e-3) <= 1e-3
+    check_w(host(W_s), host(W), U_sh, hp)
+    # column-l2 with the bf16 basis through its own kernels
+    W_l, _, U_l = _run_step(W, G, M, Qb, nb, hp, dobb.DOBB_NORM_COL_L2)
+    _, _, U_lr = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                             hp["update_scale"], norm=oracle.NORM_COL_L2)
+    assert np.linalg.norm(host(U_l) - U_lr) <= 1e-5 * np.linalg.norm(U_lr)
+
+
+@pytest.mark.parametrize("n,nb,mode", [(400, 100, "orth_iter"), (800, 400, "orth_iter"), (384, 128, "orth_iter"),
+                                       (384, 96, "exact_warm"), (400, 100, "exact_cold")])
+def test_refresh_bf16_basis_matches_oracle(n, nb, mode):
+    """A bf16 basis is read exactly, refreshed as an fp32 one and rounded to nearest even once: the
+    result is within the fp32 bound of the oracle's fed the same bf16 basis, plus half a bf16 ulp."""
+    print(f"refresh bf16 basis n={n} nb={nb} {mode}", flush=True)
+    rng = RNG(101 * nb + len(mode))
+    A32 = np.float64(np.float32(oracle.accumulate(workload.activations(4096, n, 0.15, rng), nb)))
+    A = t32(A32)
+    B = n // nb
+    lam0, Q0, _ = oracle.eig(A32)
+    # a nearby previous basis: the exact one of a perturbed moment, stored in bf16
+    Qp = torch.as_tensor(random_basis(B, nb, rng) if mode == "exact_cold" else Q0, dtype=torch.float32)
+    Qb = Qp.to(torch.bfloat16).to(DEV)
+    Qprev = host(Qb)
+    info = torch.empty(B, dtype=torch.int32, device=DEV)
+    if mode == "orth_iter":
+        dobb.dobb_refresh_basis(A, Qb, dobb.DOBB_REFRESH_ORTH_ITER, iters=1, info=info)
+        Q_ref, _ = oracle.orth_iter(A32, Qprev, k=1)
+    else:
+        warm = mode == "exact_warm"
+        dobb.dobb_refresh_basis(A, Qb, dobb.DOBB_REFRESH_EXACT, warm_start=warm, info=info)
+        _, Q_ref, _ = oracle.eig(A32, V0=Qprev if warm else None)
+    got = host(Qb)
+    assert Qb.dtype == torch.bfloat16
+    for b in range(B):
+        if mode == "orth_iter":
+            cond = np.linalg.cond(A32[b] @ Qprev[b])
+            bound = 4 * 6e-8 * cond + 1e-6
+        else:
+            lr_ = lam0[b]
+            gap = np.full(nb, np.inf)
+            gap[:-1] = np.minimum(gap[:-1], lr_[:-1] - lr_[1:])
+            gap[1:] = np.minimum(gap[1:], lr_[:-1] - lr_[1:])
+            bound = (8 * 6e-8 * np.linalg.norm(A32[b]) / np.maximum(gap, 1e-300) + 1e-6)[None, :]
+        assert np.all(np.abs(got[b] - Q_ref[b]) <= bound + 2.0 ** -8 * np.abs(Q_ref[b]) + 1e-30)
 
 
 @pytest.mark.parametrize("m,n,nb", [(256, 512, 128), (150, 400, 200)])

@@ -8,14 +8,14 @@ B = 1, 4 and 16 blocks (nb = 768, 192, 48): one accumulate (fp32 activations), o
 one step with mu = 0 (so the projected momentum is the gradient).  The pages' own Table 1(b) values
 are missing from the listing, so the orthogonality figures are compared GPU against oracle only.
 
-Bars: the end-to-end bar (<= 0.1 % of U's entries differ by more than 1e-3 RMS(U)) and the
-orthogonality of the GPU's update within 1e-3 of the oracle's, for sign and for column-l2
-normalisation in the same eigenbasis.  The end-to-end bar holds for inputs with distinct eigenvalues;
-at B = 1 the 768 eigenvalues of this spectrum include pairs 1.6e-7 max(lambda) apart, and storing A in
-fp32 (as the library does) moves those eigenvectors by itself: the oracle's own basis of its A
-correctly rounded to fp32 already changes 2.6e-3 of U's entries.  So each case measures that floor
-with the oracle alone (its update from the fp32-rounded A against its update from the fp64 A) and the
-bars are max(0.1 %, 2 x floor) for sign and max(1e-4, 2 x floor) relative Frobenius for column-l2.
+Bars: the end-to-end bar (<= 0.1 % of U's entries differ by more than 1e-3 RMS(U)) for sign and
+1e-5 relative Frobenius for column-l2, against the oracle fed A correctly rounded to fp32 (the
+precision in which the library stores A; its capture of fp32 activations sums exact products in
+fp64, so its A is that same rounding but for near ties), and the orthogonality of the GPU's update
+within 1e-3 of the oracle's.  At B = 1 the 768 eigenvalues of this spectrum include pairs
+1.6e-7 max(lambda) apart, and the fp32 rounding of A moves those eigenvectors by itself: the oracle's
+update from its A rounded to fp32 differs from its update from the fp64 A in 0.13-0.64 % of the
+entries.  That floor is printed for every case; it is a property of fp32 storage, not of the kernels.
 
 The oracle's Jacobi eigensolver at nb = 768 is warm-started from LAPACK's eigenvectors (a library
 routine used as the starting basis only, to keep the case within seconds): the oracle checks that
@@ -110,17 +110,21 @@ def test_table1b_gradients(rank, B):
         _, _, U_ref32 = oracle.step(zeros, Gh, zeros, Q_ref32, nb, 0.0, 0.0, 0.0, 1.0, norm=onorm)
         Ug = host(U)
         if name == "sign":
-            rms = np.sqrt(np.mean(U_ref ** 2))
+            rms = np.sqrt(np.mean(U_ref32 ** 2))
             floor = np.mean(np.abs(U_ref32 - U_ref) > 1e-3 * rms)
-            frac = np.mean(np.abs(Ug - U_ref) > 1e-3 * rms)
-            print(f"  sign: {frac:.2e} of U's entries differ (fp32-storage floor {floor:.2e})", flush=True)
-            assert frac <= max(1e-3, 2 * floor), f"{frac:.2e} of U's entries differ"
+            frac64 = np.mean(np.abs(Ug - U_ref) > 1e-3 * rms)
+            frac = np.mean(np.abs(Ug - U_ref32) > 1e-3 * rms)
+            print(f"  sign: {frac:.2e} of U's entries differ from the oracle on fp32 A "
+                  f"({frac64:.2e} from the oracle on fp64 A; fp32-storage floor {floor:.2e})", flush=True)
+            assert frac <= 1e-3, f"{frac:.2e} of U's entries differ"
         else:
             floor = np.linalg.norm(U_ref32 - U_ref) / np.linalg.norm(U_ref)
-            err = np.linalg.norm(Ug - U_ref) / np.linalg.norm(U_ref)
-            print(f"  column-l2: relative error {err:.2e} (fp32-storage floor {floor:.2e})", flush=True)
-            assert err <= max(1e-4, 2 * floor)
-        o_gpu, o_ref = metrics.orthogonality(Ug), metrics.orthogonality(U_ref)
+            err64 = np.linalg.norm(Ug - U_ref) / np.linalg.norm(U_ref)
+            err = np.linalg.norm(Ug - U_ref32) / np.linalg.norm(U_ref32)
+            print(f"  column-l2: relative error {err:.2e} against the oracle on fp32 A "
+                  f"({err64:.2e} on fp64 A; fp32-storage floor {floor:.2e})", flush=True)
+            assert err <= 1e-5
+        o_gpu, o_ref = metrics.orthogonality(Ug), metrics.orthogonality(U_ref32)
         assert abs(o_gpu - o_ref) <= 1e-3
         out[name] = (o_gpu, o_ref)
     print(f"  rank {rank:.0%} B={B}: orthogonality of G {metrics.orthogonality(Gh):.3f}; "
