@@ -23,6 +23,7 @@ DOBB_REFRESH_EXACT, DOBB_REFRESH_ORTH_ITER = 0, 1
 DOBB_NORM_SIGN, DOBB_NORM_IDENTITY, DOBB_NORM_COL_L2 = 0, 1, 2
 DOBB_OP_ACCUMULATE, DOBB_OP_REFRESH, DOBB_OP_STEP = 0, 1, 2
 DOBB_WS_BF16_BASIS = 16
+DOBB_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class DobbError(RuntimeError):
@@ -67,8 +68,10 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_int, ctypes.c_int, f32, PP, vp, sz, vp]
         L.dobb_step_grouped.argtypes = [ctypes.c_int, PS, PP, ctypes.c_int, PP, ctypes.c_int, PP, PP, ctypes.c_int,
                                         ctypes.POINTER(HParams), PP, PP, vp, sz, vp]
+        L.dobb_step_noalloc.argtypes = [PS, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int,
+                                        ctypes.POINTER(HParams), vp, vp, vp]
         for name in ("dobb_accumulate_moment", "dobb_refresh_basis", "dobb_step", "dobb_accumulate_moment_grouped",
-                     "dobb_refresh_basis_grouped", "dobb_step_grouped"):
+                     "dobb_refresh_basis_grouped", "dobb_step_grouped", "dobb_step_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         L.dobb_status_string.argtypes = [ctypes.c_int]
         L.dobb_status_string.restype = ctypes.c_char_p
@@ -206,6 +209,24 @@ def dobb_step(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor
     ws, wsb = _workspace(need, W.device, ws)
     _check(lib().dobb_step(ctypes.byref(shape), wp, _dtype_code(W), gp, _dtype_code(G), mp, qp, qdt, ctypes.byref(hp),
                            up, cp, None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step")
+    return W
+
+
+def dobb_step_noalloc(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor, nb: int, hp: HParams,
+                      U_out: torch.Tensor | None = None, C_out: torch.Tensor | None = None, stream=None):
+    """dobb_step with the library's static per-GPU scratch instead of a workspace: allocates nothing
+    (for callers that cannot, e.g. under graph capture).  Shapes whose workspace exceeds
+    DOBB_NOALLOC_SCRATCH_BYTES are refused (DOBB_ERR_WORKSPACE)."""
+    m, n = W.shape
+    shape = Shape(m, n, nb)
+    wp = _dev(W, "W")
+    gp = _dev(G, "G", None, (m, n))
+    mp = _dev(M, "M", torch.float32, (m, n))
+    qp = _dev(Q, "Q", None, (n // nb, nb, nb))
+    up = _dev(U_out, "U_out", torch.float32, (m, n)) if U_out is not None else None
+    cp = _dev(C_out, "C_out", torch.float32, (m, n)) if C_out is not None else None
+    _check(lib().dobb_step_noalloc(ctypes.byref(shape), wp, _dtype_code(W), gp, _dtype_code(G), mp, qp, _dtype_code(Q),
+                                   ctypes.byref(hp), up, cp, _stream(stream)), "dobb_step_noalloc")
     return W
 
 

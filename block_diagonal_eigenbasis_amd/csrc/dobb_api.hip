@@ -1,6 +1,7 @@
 // C ABI of libdobb: host-side validation, workspace sizing, grouping of matrix sets by shape, and
 // the optional kernel timer.  Every computation is done by the kernels in k_*.hip.
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -152,6 +153,33 @@ dobb_status check_ws(void *ws, size_t ws_bytes, size_t need) {
 
 dobb_status hip_status(hipError_t e) { return e == hipSuccess ? DOBB_OK : DOBB_ERR_HIP; }
 
+}  // namespace
+
+// ---- scratch of the allocation-free step ---------------------------------------------------------
+// A file-scope device array: every GPU the library is loaded on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and kept in scratch_ptr.  Calls on one
+// GPU share the array, so calls that overlap on one GPU race.  No step kernel reads a workspace byte
+// it has not written in the same call, so the array needs no clearing between calls.
+static __device__ __align__(256) unsigned char scratch[DOBB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+dobb_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DOBB_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DOBB_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return DOBB_OK;
+}
 }  // namespace
 }  // namespace dobb
 
@@ -415,6 +443,26 @@ dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const vo
                       size_t ws_bytes, dobb_stream_t stream) {
     if (!s) return DOBB_ERR_INVALID_ARG;
     return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, q_dtype, hp, &U_out, &C_out, ws, ws_bytes, stream);
+}
+
+dobb_status dobb_step_noalloc(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,
+                              float *M, const void *Q, dobb_dtype q_dtype, const dobb_hparams *hp, float *U_out,
+                              float *C_out, dobb_stream_t stream) {
+    // everything that can be refused is refused before the first HIP call
+    if (!s || !hp || !W || !G || !M || !Q) return DOBB_ERR_INVALID_ARG;
+    dobb_status st = check_shape(s);
+    if (st != DOBB_OK) return st;
+    if ((w_dtype != DOBB_F32 && w_dtype != DOBB_BF16) || (g_dtype != DOBB_F32 && g_dtype != DOBB_BF16) ||
+        (q_dtype != DOBB_F32 && q_dtype != DOBB_BF16))
+        return DOBB_ERR_DTYPE;
+    if (hp->norm < 0 || hp->norm > 2) return DOBB_ERR_INVALID_ARG;
+    const size_t need = group_ws(DOBB_OP_STEP, *s, 1, 0, hp->norm | (q_dtype == DOBB_BF16 ? DOBB_WS_BF16_BASIS : 0));
+    if (need > (size_t)DOBB_NOALLOC_SCRATCH_BYTES) return DOBB_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != DOBB_OK) return st;
+    return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, q_dtype, hp, &U_out, &C_out, ws,
+                             (size_t)DOBB_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 void dobb_profile_enable(int on) {

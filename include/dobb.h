@@ -26,8 +26,9 @@
  *             the eigensolver is reported per block in the device array `info`, never as a status.
  *             NaN/Inf inputs are not checked; they propagate (sign(NaN) = NaN).
  *   Threads   The library keeps no mutable global state except the optional kernel timer
- *             (dobb_profile_*), which is not thread-safe.  Calls that share a workspace or outputs
- *             must be ordered by the caller.
+ *             (dobb_profile_*), which is not thread-safe, and the per-GPU scratch array of
+ *             dobb_step_noalloc.  Calls that share a workspace or outputs must be ordered by the
+ *             caller.
  */
 #ifndef DOBB_H
 #define DOBB_H
@@ -165,6 +166,23 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
                               const void *const *Q, dobb_dtype q_dtype, const dobb_hparams *hp,
                               float *const *U_out, float *const *C_out, void *ws, size_t ws_bytes,
                               dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * The step without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same semantics and
+ * kernels as dobb_step; the scratch is a static device array of DOBB_NOALLOC_SCRATCH_BYTES held by
+ * the library on each GPU it runs on until the process ends (every matrix of the GPT-2 and 7B-style
+ * sets fits with sign normalisation; column-l2 needs 4 bytes per weight entry).  A shape whose
+ * workspace (dobb_workspace_size for this op and variant) exceeds it returns DOBB_ERR_WORKSPACE
+ * before anything is enqueued.  The call allocates and frees nothing.  The device is the caller's
+ * current HIP device, which must be the stream's.  Calls on one GPU share the array: calls that can
+ * overlap on one GPU (different streams, different host threads) race and must be ordered by the
+ * caller; calls in one stream are ordered by it.
+ * -------------------------------------------------------------------------------------------------*/
+#define DOBB_NOALLOC_SCRATCH_BYTES (64u << 20)
+dobb_status dobb_step_noalloc(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,
+                              float *M, const void *Q, dobb_dtype q_dtype, const dobb_hparams *hp, float *U_out,
+                              float *C_out, dobb_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Kernel timer (tracing).  While enabled, every kernel the library enqueues is bracketed by a pair

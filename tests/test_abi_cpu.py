@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _abi.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
 
@@ -159,3 +159,26 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         _abi.dobb_step(torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(4, 4), torch.zeros(1, 4, 4), 4,
                        _abi.make_hparams(0.1, 0, 0.9, 0.2))
+
+
+def test_step_noalloc_refuses_before_any_launch():
+    """The allocation-free step checks its arguments and that the shape's workspace fits the static
+    scratch before it touches a device: a column-l2 step of an 11008 x 4096 weight needs 4 bytes per
+    entry, more than DOBB_NOALLOC_SCRATCH_BYTES."""
+    L = _abi.lib()
+    big = _shape(11008, 4096, 128)
+    l2 = _abi.make_hparams(0.1, 0.0, 0.9, 0.2, norm=_abi.DOBB_NORM_COL_L2)
+    assert _abi.dobb_workspace_size(_abi.DOBB_OP_STEP, [(11008, 4096, 128)], 0, 2) > _abi.DOBB_NOALLOC_SCRATCH_BYTES
+    assert L.dobb_step_noalloc(ctypes.byref(big), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(l2), None, None,
+                               None) == _abi.DOBB_ERR_WORKSPACE
+    hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
+    s = _shape(64, 64, 16)
+    assert L.dobb_step_noalloc(ctypes.byref(s), None, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None,
+                               None) == -1
+    assert L.dobb_step_noalloc(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 5, ctypes.byref(hp), None, None,
+                               None) == -3
+    assert L.dobb_step_noalloc(ctypes.byref(_shape(64, 65, 16)), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp),
+                               None, None, None) == -2
+    # every single weight of the GPT-2 XL and 7B-style sets fits with sign normalisation
+    for shp in [(4800, 1600, 100), (6400, 1600, 100), (1600, 6400, 400), (11008, 4096, 128), (4096, 11008, 128)]:
+        assert 0 < _abi.dobb_workspace_size(_abi.DOBB_OP_STEP, [shp], 0, 0) <= _abi.DOBB_NOALLOC_SCRATCH_BYTES
