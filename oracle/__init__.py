@@ -57,6 +57,8 @@ def _load():
         lib.oracle_orth_iter.restype = None
         lib.oracle_step.argtypes = [L, L, L, P, P, P, P, D, D, D, D, I, I, P]
         lib.oracle_step.restype = None
+        lib.oracle_step_g.argtypes = [L, L, L, P, P, P, P, D, D, D, D, I, I, P]
+        lib.oracle_step_g.restype = None
         _lib = lib
     return _lib
 
@@ -189,6 +191,42 @@ def step(W, G, M, Q, nb: int, lr: float, weight_decay: float, momentum: float, u
     with _pool(cores) as ex:
         list(ex.map(one, range(nchunk)))
     return W, M, U
+
+
+def step_g(W, G, M, P, nb: int, lr: float, weight_decay: float, momentum: float, update_scale: float,
+           nesterov: bool = False, norm: int = NORM_SIGN, cores: int | None = 1):
+    """One Dobb-G step on an m x n weight: blocks of nb rows, bases P (m/nb, nb, nb) of the
+    output-gradient second moment.  Returns (W_new, M_new, U), all float64 (m, n).
+
+    With the sign and identity norms every column is independent within a block, but a block spans
+    all columns, so with cores > 1 whole blocks of rows are shared among threads; Dobb-G-l2 (norm 2)
+    normalises within a block too, so blocks stay independent for every norm."""
+    W, G, M, P = _f64(W).copy(), _f64(G), _f64(M).copy(), _f64(P)
+    m, n = W.shape
+    assert m % nb == 0 and P.shape == (m // nb, nb, nb)
+    U = np.zeros((m, n))
+    lib = _load()
+    args = (float(lr), float(weight_decay), float(momentum), float(update_scale), int(bool(nesterov)), int(norm))
+    B = m // nb
+    if not cores or cores == 1 or B == 1:
+        lib.oracle_step_g(m, n, nb, _ptr(W), _ptr(G), _ptr(M), _ptr(P), *args, _ptr(U))
+        return W, M, U
+
+    def one(b):
+        r = slice(b * nb, (b + 1) * nb)
+        w, mm, u = W[r], M[r], U[r]                        # contiguous row blocks, written in place
+        g, p = np.ascontiguousarray(G[r]), np.ascontiguousarray(P[b:b + 1])
+        lib.oracle_step_g(nb, n, nb, _ptr(w), _ptr(g), _ptr(mm), _ptr(p), *args, _ptr(u))
+
+    with _pool(cores) as ex:
+        list(ex.map(one, range(B)))
+    return W, M, U
+
+
+def default_update_scale_g(m: int, n: int, tau: float = 0.2) -> float:
+    """Applied scale of the Dobb-G sign update: Table 9's Dobb-G row gives ||O||_F^2 = m and
+    RMS tau sqrt(max(m,n)/n), i.e. tau sqrt(max(m,n)/n) on U (whose ||U||_F^2 = m n)."""
+    return tau * float(np.sqrt(max(m, n) / n))
 
 
 def default_update_scale(m: int, n: int, tau: float = 0.2) -> float:

@@ -319,3 +319,67 @@ void oracle_step(long m, long n, long nb, double *W, const double *G, double *M,
     if (U) memcpy(U, Uall, sizeof(double) * m * n);
     free(Meff); free(Uall); free(C);
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * The Dobb-G step (Tables 12-13: the basis comes from the output-gradient second moment instead of
+ * the input-activation one; Figure 2 caption: that moment is m x m; Table 7: with each block inside
+ * one shard, Dobb-G needs no cross-shard payload, and Dobb-G-l2's normalisation reduces along the
+ * input axis, O(m) scalars when that axis is sharded).  Blocks are nb consecutive ROWS of the weight
+ * (output units); P holds B = m / nb consecutive nb x nb bases, eigenvectors as columns.
+ *   M <- mu M + G;  M_eff = M, or G + mu M with Nesterov (as in oracle_step)
+ *   for each block b (rows [b nb, (b+1) nb)):
+ *       C_b = P_b^T M_eff[rows of b, :]             (nb x n: coefficients of every column)
+ *       S_b = sign(C_b)                              (norm 0; sign(0) = 0, NaN stays NaN)
+ *           = C_b                                    (norm 1: identity -- U = P P^T M = M)
+ *           = diag(1/||c_i||) C_b                    (norm 2: each row of C_b over the n columns,
+ *                                                     Dobb-G-l2)
+ *       U[rows of b, :] = P_b S_b                    (reconstruct)
+ *   W <- W - lr (s_eff U + wd W)
+ * Table 9's Dobb-G row: raw ||O||_F^2 = m and RMS(s O) = tau sqrt(max(m,n)/n), so for sign (whose
+ * ||U||_F^2 = m n) O = U / sqrt(n) and s_eff = tau sqrt(max(m,n)/n); the caller passes s_eff.
+ * ---------------------------------------------------------------------------------------------- */
+void oracle_step_g(long m, long n, long nb, double *W, const double *G, double *M, const double *P,
+                   double lr, double wd, double mu, double s_eff, int nesterov, int norm, double *U)
+{
+    long B = m / nb;
+    double *Meff = (double *)malloc(sizeof(double) * m * n);
+    double *Uall = (double *)malloc(sizeof(double) * m * n);
+    double *C = (double *)malloc(sizeof(double) * nb * n);
+    for (long i = 0; i < m * n; ++i) {
+        M[i] = mu * M[i] + G[i];
+        Meff[i] = nesterov ? G[i] + mu * M[i] : M[i];
+    }
+    for (long b = 0; b < B; ++b) {
+        const double *Pb = P + b * nb * nb;
+        const double *Mb = Meff + b * nb * n;
+        for (long i = 0; i < nb; ++i)
+            for (long c = 0; c < n; ++c) {
+                double s = 0.0;
+                for (long p = 0; p < nb; ++p) s += Pb[p * nb + i] * Mb[p * n + c];
+                C[i * n + c] = s;
+            }
+        if (norm == 0) {
+            for (long e = 0; e < nb * n; ++e) {
+                double c = C[e];
+                C[e] = (c > 0.0) ? 1.0 : (c < 0.0) ? -1.0 : (c == 0.0) ? 0.0 : c; /* NaN stays */
+            }
+        } else if (norm == 2) {
+            for (long i = 0; i < nb; ++i) {
+                double s = 0.0;
+                for (long c = 0; c < n; ++c) s += C[i * n + c] * C[i * n + c];
+                double inv = (s > 0.0) ? 1.0 / sqrt(s) : 0.0;
+                for (long c = 0; c < n; ++c) C[i * n + c] *= inv;
+            }
+        }
+        for (long p = 0; p < nb; ++p)
+            for (long c = 0; c < n; ++c) {
+                double s = 0.0;
+                for (long i = 0; i < nb; ++i) s += Pb[p * nb + i] * C[i * n + c];
+                Uall[(b * nb + p) * n + c] = s;
+            }
+    }
+    for (long i = 0; i < m * n; ++i)
+        W[i] = W[i] - lr * (s_eff * Uall[i] + wd * W[i]);
+    if (U) memcpy(U, Uall, sizeof(double) * m * n);
+    free(Meff); free(Uall); free(C);
+}

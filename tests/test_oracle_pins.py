@@ -477,3 +477,98 @@ def test_threaded_oracle_equals_single_thread_bitwise():
     np.testing.assert_array_equal(A0, oracle.accumulate(X, nb, cores=3))
     np.testing.assert_array_equal(oracle.accumulate(X, nb, A=A0, beta=0.9),
                                   oracle.accumulate(X, nb, A=A0, beta=0.9, cores=4))
+
+
+# ------------------------------------------------------------------------------------------------
+# Dobb-G: the basis of the output-gradient second moment, blocks on the output axis (Tables 12-13)
+
+def test_dobb_g_is_dobb_on_the_transposed_weight():
+    """Dobb-G on W (blocks of rows, C_b = P_b^T M_b, U_b = P_b S_b) is Dobb on W^T (blocks of columns,
+    C = M^T P, U^T = S^T P^T): the two oracle functions agree on every norm and with Nesterov."""
+    rng = RNG(201)
+    m, n, nb = 24, 10, 6
+    W, G, M = rng.standard_normal((3, m, n))
+    P = _random_basis(m // nb, nb, rng)
+    for norm in (oracle.NORM_SIGN, oracle.NORM_IDENTITY, oracle.NORM_COL_L2):
+        for nest in (False, True):
+            Wg, Mg, Ug = oracle.step_g(W, G, M, P, nb, 0.01, 0.1, 0.9, 0.3, nesterov=nest, norm=norm)
+            Wt, Mt, Ut = oracle.step(W.T, G.T, M.T, P, nb, 0.01, 0.1, 0.9, 0.3, nesterov=nest, norm=norm)
+            np.testing.assert_allclose(Ug, Ut.T, rtol=1e-14, atol=1e-15)
+            np.testing.assert_allclose(Wg, Wt.T, rtol=1e-14, atol=1e-15)
+            np.testing.assert_allclose(Mg, Mt.T, rtol=1e-15)
+
+
+def test_dobb_g_sign_structure_and_table9_scale(golden_dir):
+    for m, n, rms in _golden(golden_dir, "table9_dobb_g_rms.txt"):
+        assert oracle.default_update_scale_g(int(m), int(n)) == pytest.approx(rms, rel=1e-12)
+    rng = RNG(202)
+    m, n, nb = 36, 20, 12
+    W, G, M = rng.standard_normal((3, m, n))
+    P = _random_basis(m // nb, nb, rng)
+    s = oracle.default_update_scale_g(m, n)
+    W1, M1, U = oracle.step_g(W, G, M, P, nb, 0.01, 0.1, 0.9, s)
+    for b in range(m // nb):
+        r = slice(b * nb, (b + 1) * nb)
+        S = P[b].T @ U[r]                                   # the sign matrix: entries +-1
+        np.testing.assert_allclose(np.abs(S), 1.0, atol=1e-13)
+        np.testing.assert_allclose(np.linalg.norm(U[r], axis=0), np.sqrt(nb), rtol=1e-13)
+    assert np.sum(U * U) == pytest.approx(m * n, rel=1e-12)
+    # RMS of the applied update: tau sqrt(max(m, n) / n)
+    assert np.sqrt(np.mean((s * U) ** 2)) == pytest.approx(0.2 * np.sqrt(max(m, n) / n), rel=1e-12)
+    np.testing.assert_allclose(W1, W - 0.01 * (s * U + 0.1 * W), rtol=1e-14, atol=1e-15)
+
+
+def test_dobb_g_brute_force_steepest_direction_8x8():
+    """Each column of U_b maximises <m_c, P_b v> over all 2^8 sign vectors v: the l_inf-steepest
+    direction in the output-side eigenbasis."""
+    rng = RNG(203)
+    nb = 8
+    P = _random_basis(1, nb, rng)
+    M = rng.standard_normal((nb, 8))
+    _, _, U = oracle.step_g(np.zeros((nb, 8)), np.zeros((nb, 8)), M, P, nb, 0.0, 0.0, 1.0, 1.0)
+    cands = P[0] @ np.array(list(itertools.product([-1.0, 1.0], repeat=nb))).T   # nb x 256
+    for c in range(8):
+        scores = M[:, c] @ cands
+        np.testing.assert_allclose(U[:, c], cands[:, np.argmax(scores)], atol=1e-13)
+
+
+def test_dobb_g_round_trip_block_one_and_sign_flips():
+    rng = RNG(204)
+    m, n, nb = 20, 7, 5
+    W, G, M = rng.standard_normal((3, m, n))
+    P = _random_basis(m // nb, nb, rng)
+    # identity normalisation: U = P P^T M = M
+    _, _, U = oracle.step_g(W, np.zeros_like(G), M, P, nb, 0.0, 0.0, 1.0, 1.0, norm=oracle.NORM_IDENTITY)
+    np.testing.assert_allclose(U, M, atol=1e-14)
+    # one-row blocks: every basis is [+-1], the step is sign descent
+    P1 = rng.choice([-1.0, 1.0], size=(m, 1, 1))
+    _, _, U1 = oracle.step_g(W, G, M, P1, 1, 0.0, 0.0, 0.9, 1.0)
+    np.testing.assert_array_equal(U1, np.sign(0.9 * M + G))
+    # flipping basis vectors leaves U bitwise unchanged
+    flips = rng.choice([-1.0, 1.0], size=(m // nb, 1, nb))
+    _, _, Ua = oracle.step_g(W, G, M, P, nb, 0.0, 0.0, 0.9, 1.0)
+    _, _, Ub = oracle.step_g(W, G, M, P * flips, nb, 0.0, 0.0, 0.9, 1.0)
+    np.testing.assert_array_equal(Ua, Ub)
+
+
+def test_dobb_g_l2_rows_have_unit_norm():
+    """Dobb-G-l2: each row of the coefficient block (over the n columns) is normalised, so
+    P_b^T U_b has unit rows and ||U||_F^2 = m, Table 9's ||O||_F^2 for Dobb-G-l2 with O = U."""
+    rng = RNG(205)
+    m, n, nb = 18, 11, 6
+    W, G, M = rng.standard_normal((3, m, n))
+    P = _random_basis(m // nb, nb, rng)
+    _, _, U = oracle.step_g(W, G, M, P, nb, 0.0, 0.0, 0.9, 1.0, norm=oracle.NORM_COL_L2)
+    for b in range(m // nb):
+        r = slice(b * nb, (b + 1) * nb)
+        Ct = P[b].T @ U[r]
+        np.testing.assert_allclose(np.linalg.norm(Ct, axis=1), 1.0, rtol=1e-13)
+        C = P[b].T @ (0.9 * M[r] + G[r])
+        np.testing.assert_allclose(Ct * np.linalg.norm(C, axis=1, keepdims=True), C, rtol=1e-12, atol=1e-13)
+    assert np.sum(U * U) == pytest.approx(m, rel=1e-12)
+    # threaded over blocks: bitwise the same
+    for norm in (oracle.NORM_SIGN, oracle.NORM_COL_L2):
+        a = oracle.step_g(W, G, M, P, nb, 0.01, 0.1, 0.9, 0.5, norm=norm)
+        b_ = oracle.step_g(W, G, M, P, nb, 0.01, 0.1, 0.9, 0.5, norm=norm, cores=3)
+        for x, y in zip(a, b_):
+            np.testing.assert_array_equal(x, y)
