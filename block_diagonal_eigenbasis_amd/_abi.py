@@ -21,7 +21,7 @@ DOBB_ERR_WORKSPACE, DOBB_ERR_HIP, DOBB_ERR_NOT_CONVERGED = -4, -5, -6
 DOBB_F32, DOBB_BF16 = 0, 1
 DOBB_REFRESH_EXACT, DOBB_REFRESH_ORTH_ITER = 0, 1
 DOBB_NORM_SIGN, DOBB_NORM_IDENTITY, DOBB_NORM_COL_L2 = 0, 1, 2
-DOBB_OP_ACCUMULATE, DOBB_OP_REFRESH, DOBB_OP_STEP = 0, 1, 2
+DOBB_OP_ACCUMULATE, DOBB_OP_REFRESH, DOBB_OP_STEP, DOBB_OP_STEP_G = 0, 1, 2, 3
 DOBB_WS_BF16_BASIS = 16
 DOBB_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -68,10 +68,13 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_int, ctypes.c_int, f32, PP, vp, sz, vp]
         L.dobb_step_grouped.argtypes = [ctypes.c_int, PS, PP, ctypes.c_int, PP, ctypes.c_int, PP, PP, ctypes.c_int,
                                         ctypes.POINTER(HParams), PP, PP, vp, sz, vp]
+        L.dobb_step_g.argtypes = list(L.dobb_step.argtypes)
+        L.dobb_step_g_grouped.argtypes = list(L.dobb_step_grouped.argtypes)
         L.dobb_step_noalloc.argtypes = [PS, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, ctypes.c_int,
                                         ctypes.POINTER(HParams), vp, vp, vp]
         for name in ("dobb_accumulate_moment", "dobb_refresh_basis", "dobb_step", "dobb_accumulate_moment_grouped",
-                     "dobb_refresh_basis_grouped", "dobb_step_grouped", "dobb_step_noalloc"):
+                     "dobb_refresh_basis_grouped", "dobb_step_grouped", "dobb_step_noalloc", "dobb_step_g",
+                     "dobb_step_g_grouped"):
             getattr(L, name).restype = ctypes.c_int
         L.dobb_status_string.argtypes = [ctypes.c_int]
         L.dobb_status_string.restype = ctypes.c_char_p
@@ -212,6 +215,28 @@ def dobb_step(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor
     return W
 
 
+def dobb_step_g(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, P: torch.Tensor, nb: int, hp: HParams,
+                U_out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None,
+                C_out: torch.Tensor | None = None):
+    """One Dobb-G step on W (m x n) in place: blocks of nb rows, P (m/nb x nb x nb, fp32 or bf16) the
+    bases of the output-gradient second moment; M (fp32) in place; U_out, C_out optional (fp32)."""
+    m, n = W.shape
+    shape = Shape(m, n, nb)
+    wp = _dev(W, "W")
+    gp = _dev(G, "G", None, (m, n))
+    mp = _dev(M, "M", torch.float32, (m, n))
+    pp = _dev(P, "P", None, (m // nb, nb, nb))
+    pdt = _dtype_code(P)
+    up = _dev(U_out, "U_out", torch.float32, (m, n)) if U_out is not None else None
+    cp = _dev(C_out, "C_out", torch.float32, (m, n)) if C_out is not None else None
+    need = dobb_workspace_size(DOBB_OP_STEP_G, [(m, n, nb)], 0, _step_variant(hp.norm, pdt))
+    ws, wsb = _workspace(need, W.device, ws)
+    _check(lib().dobb_step_g(ctypes.byref(shape), wp, _dtype_code(W), gp, _dtype_code(G), mp, pp, pdt,
+                             ctypes.byref(hp), up, cp, None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
+           "dobb_step_g")
+    return W
+
+
 def dobb_step_noalloc(W: torch.Tensor, G: torch.Tensor, M: torch.Tensor, Q: torch.Tensor, nb: int, hp: HParams,
                       U_out: torch.Tensor | None = None, C_out: torch.Tensor | None = None, stream=None):
     """dobb_step with the library's static per-GPU scratch instead of a workspace: allocates nothing
@@ -293,6 +318,28 @@ def dobb_step_grouped(Ws, Gs, Ms, Qs, nbs, hps, U_outs=None, ws: torch.Tensor | 
                                    _ptrs(U_outs) if U_outs is not None else None,
                                    _ptrs(C_outs) if C_outs is not None else None,
                                    None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step_grouped")
+
+
+def dobb_step_g_grouped(Ws, Gs, Ms, Ps, nbs, hps, U_outs=None, ws: torch.Tensor | None = None, stream=None,
+                        C_outs=None):
+    count = len(Ws)
+    shapes = [(W.shape[0], W.shape[1], nb) for W, nb in zip(Ws, nbs)]
+    for W, G, M, P, (m, n, nb) in zip(Ws, Gs, Ms, Ps, shapes):
+        _dev(W, "W"); _dev(G, "G", None, (m, n)); _dev(M, "M", torch.float32, (m, n))
+        _dev(P, "P", None, (m // nb, nb, nb))
+    wdt, gdt, pdt = _common_dtype(Ws, "W"), _common_dtype(Gs, "G"), _common_dtype(Ps, "P")
+    for name, outs in (("U_out", U_outs), ("C_out", C_outs)):
+        for o, (m, n, _) in zip(outs or [], shapes):
+            if o is not None:
+                _dev(o, name, torch.float32, (m, n))
+    sarr = (Shape * count)(*[Shape(*s) for s in shapes])
+    harr = (HParams * count)(*hps)
+    need = dobb_workspace_size(DOBB_OP_STEP_G, shapes, 0, _step_variant(hps[0].norm, pdt))
+    ws, wsb = _workspace(need, Ws[0].device, ws)
+    _check(lib().dobb_step_g_grouped(count, sarr, _ptrs(Ws), wdt, _ptrs(Gs), gdt, _ptrs(Ms), _ptrs(Ps), pdt, harr,
+                                     _ptrs(U_outs) if U_outs is not None else None,
+                                     _ptrs(C_outs) if C_outs is not None else None,
+                                     None if ws is None else ws.data_ptr(), wsb, _stream(stream)), "dobb_step_g_grouped")
 
 
 # ------------------------------------------------------------------------------------------------

@@ -102,6 +102,22 @@ dobb_status check_shape(const dobb_shape *s) {
     return DOBB_OK;
 }
 
+// Dobb-G: blocks of nb rows (m % nb == 0); the launch grid holds ceil(nb / 64) x (m / nb) tiles per
+// matrix in its y dimension
+dobb_status check_shape_g(const dobb_shape *s) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    if (s->m < 1 || s->n < 1 || s->nb < 1 || s->nb > kMaxNb || s->m % s->nb != 0) return DOBB_ERR_SHAPE;
+    if ((s->nb + kBM - 1) / kBM * (s->m / s->nb) > 65535 || (s->n + kBN - 1) / kBN > 0x7fffffff) return DOBB_ERR_SHAPE;
+    return DOBB_OK;
+}
+
+// matrices per Dobb-G launch
+int step_g_chunk(const dobb_shape &sh) {
+    const int64_t per = (sh.nb + kBM - 1) / kBM * (sh.m / sh.nb);
+    const int64_t c = 65535 / per;
+    return (int)(c < kMaxMats ? c : kMaxMats);
+}
+
 bool same_shape(const dobb_shape &a, const dobb_shape &b) { return a.m == b.m && a.n == b.n && a.nb == b.nb; }
 
 // indices of matrices grouped by identical shape, first-seen order
@@ -134,10 +150,20 @@ size_t step_region_one(const dobb_shape &sh, int variant) {
     return step_ws_one(sh, variant & ~DOBB_WS_BF16_BASIS) + (qbf ? basis_copy_one(sh) : 0);
 }
 
+// Dobb-G: the step's regions, then the fp32 copy of a bf16 basis (m x nb entries)
+size_t step_g_region_one(const dobb_shape &sh, int variant) {
+    const bool qbf = (variant & DOBB_WS_BF16_BASIS) != 0;
+    return step_g_ws_one(sh, variant & ~DOBB_WS_BF16_BASIS) + (qbf ? al256((size_t)sh.m * (size_t)sh.nb * 4) : 0);
+}
+
 size_t group_ws(dobb_op op, const dobb_shape &sh, int cnt, int64_t N, int variant) {
     const int c = cnt < kMaxMats ? cnt : kMaxMats;
     const bool qbf = (variant & DOBB_WS_BF16_BASIS) != 0;
     switch (op) {
+        case DOBB_OP_STEP_G: {
+            const int cg = step_g_chunk(sh);
+            return step_g_region_one(sh, variant) * (cnt < cg ? cnt : cg);
+        }
         case DOBB_OP_ACCUMULATE: return al256(accumulate_ws(sh, N, cnt));
         case DOBB_OP_REFRESH: return al256(refresh_ws(sh, c)) + (qbf ? basis_copy_one(sh) * c : 0);
         case DOBB_OP_STEP: return step_region_one(sh, variant) * c;
@@ -204,13 +230,15 @@ const char *dobb_status_string(dobb_status st) {
 
 size_t dobb_workspace_size(dobb_op op, int count, const dobb_shape *shapes, int64_t N, int32_t variant) {
     if (count < 1 || !shapes) return 0;
-    if (op != DOBB_OP_ACCUMULATE && op != DOBB_OP_REFRESH && op != DOBB_OP_STEP) return 0;
+    if (op != DOBB_OP_ACCUMULATE && op != DOBB_OP_REFRESH && op != DOBB_OP_STEP && op != DOBB_OP_STEP_G) return 0;
     if (op == DOBB_OP_ACCUMULATE && N < 1) return 0;
-    if (op == DOBB_OP_STEP && ((variant & ~DOBB_WS_BF16_BASIS) < 0 || (variant & ~DOBB_WS_BF16_BASIS) > 2)) return 0;
+    if ((op == DOBB_OP_STEP || op == DOBB_OP_STEP_G) &&
+        ((variant & ~DOBB_WS_BF16_BASIS) < 0 || (variant & ~DOBB_WS_BF16_BASIS) > 2))
+        return 0;
     if (op == DOBB_OP_ACCUMULATE) variant = 0;
     if (op == DOBB_OP_REFRESH) variant &= DOBB_WS_BF16_BASIS;
     for (int i = 0; i < count; ++i)
-        if (check_shape(&shapes[i]) != DOBB_OK) return 0;
+        if ((op == DOBB_OP_STEP_G ? check_shape_g(&shapes[i]) : check_shape(&shapes[i])) != DOBB_OK) return 0;
     size_t need = 0;
     for (const auto &g : group_by_shape(count, shapes)) {
         size_t w = group_ws(op, shapes[g[0]], (int)g.size(), N, variant);
@@ -443,6 +471,92 @@ dobb_status dobb_step(const dobb_shape *s, void *W, dobb_dtype w_dtype, const vo
                       size_t ws_bytes, dobb_stream_t stream) {
     if (!s) return DOBB_ERR_INVALID_ARG;
     return dobb_step_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &Q, q_dtype, hp, &U_out, &C_out, ws, ws_bytes, stream);
+}
+
+dobb_status dobb_step_g_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype,
+                                const void *const *G, dobb_dtype g_dtype, float *const *M, const void *const *P,
+                                dobb_dtype p_dtype, const dobb_hparams *hp, float *const *U_out, float *const *C_out,
+                                void *ws, size_t ws_bytes, dobb_stream_t stream) {
+    if (count < 1 || !shapes || !W || !G || !M || !P || !hp) return DOBB_ERR_INVALID_ARG;
+    if ((w_dtype != DOBB_F32 && w_dtype != DOBB_BF16) || (g_dtype != DOBB_F32 && g_dtype != DOBB_BF16) ||
+        (p_dtype != DOBB_F32 && p_dtype != DOBB_BF16))
+        return DOBB_ERR_DTYPE;
+    for (int i = 0; i < count; ++i) {
+        dobb_status st = check_shape_g(&shapes[i]);
+        if (st != DOBB_OK) return st;
+        if (!W[i] || !G[i] || !M[i] || !P[i]) return DOBB_ERR_INVALID_ARG;
+        if (hp[i].norm < 0 || hp[i].norm > 2) return DOBB_ERR_INVALID_ARG;
+        if (hp[i].norm != hp[0].norm || (hp[i].nesterov != 0) != (hp[0].nesterov != 0)) return DOBB_ERR_INVALID_ARG;
+    }
+    const int norm = hp[0].norm;
+    const bool qbf = p_dtype == DOBB_BF16;
+    const int variant = norm | (qbf ? DOBB_WS_BF16_BASIS : 0);
+    const auto groups = group_by_shape(count, shapes);
+    size_t need = 0;
+    for (const auto &g : groups) { size_t w = group_ws(DOBB_OP_STEP_G, shapes[g[0]], (int)g.size(), 0, variant); if (w > need) need = w; }
+    dobb_status st = check_ws(ws, ws_bytes, need);
+    if (st != DOBB_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    for (const auto &g : groups) {
+        const dobb_shape sh = shapes[g[0]];
+        const size_t per = step_g_region_one(sh, variant);
+        const size_t own = step_g_ws_one(sh, norm);
+        const size_t mn4 = al256((size_t)sh.m * (size_t)sh.n * 4);
+        const size_t chunk = (size_t)step_g_chunk(sh);
+        for (size_t c0 = 0; c0 < g.size(); c0 += chunk) {
+            const int cnt = (int)(g.size() - c0 < chunk ? g.size() - c0 : chunk);
+            std::vector<const void *> gs, qsrc;
+            std::vector<float *> ms, us, co, cs, rsc;
+            std::vector<void *> ws_, qdst;
+            std::vector<const float *> ps;
+            std::vector<int8_t *> ss;
+            std::vector<dobb_hparams> hs_;
+            for (int k = 0; k < cnt; ++k) {
+                const int i = g[c0 + k];
+                char *reg = (char *)ws + per * k;
+                gs.push_back(G[i]); ms.push_back(M[i]); ws_.push_back(W[i]);
+                us.push_back(U_out ? U_out[i] : nullptr);
+                co.push_back(C_out ? C_out[i] : nullptr);
+                hs_.push_back(hp[i]);
+                float *pf = qbf ? (float *)(reg + own) : (float *)P[i];
+                ps.push_back(pf);
+                qsrc.push_back(P[i]);
+                qdst.push_back(pf);
+                ss.push_back((int8_t *)reg);
+                cs.push_back((float *)reg);
+                rsc.push_back(norm == DOBB_NORM_SIGN ? nullptr : (float *)(reg + mn4));
+            }
+            if (qbf) {
+                st = hip_status(launch_basis_convert(cnt, qsrc.data(), qdst.data(), sh.m * sh.nb, true, hs));
+                if (st != DOBB_OK) return st;
+            }
+            StepArgs a{};
+            a.count = cnt;
+            a.sh = sh;
+            a.w_dtype = w_dtype;
+            a.g_dtype = g_dtype;
+            a.hp = hs_.data();
+            a.G = gs.data();
+            a.M = ms.data();
+            a.W = ws_.data();
+            a.U = us.data();
+            a.Cout = co.data();
+            a.Q = ps.data();
+            a.S = ss.data();
+            a.C = cs.data();
+            a.colscale = rsc.data();
+            st = hip_status(launch_step_g(a, hs));
+            if (st != DOBB_OK) return st;
+        }
+    }
+    return DOBB_OK;
+}
+
+dobb_status dobb_step_g(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype, float *M,
+                        const void *P, dobb_dtype p_dtype, const dobb_hparams *hp, float *U_out, float *C_out, void *ws,
+                        size_t ws_bytes, dobb_stream_t stream) {
+    if (!s) return DOBB_ERR_INVALID_ARG;
+    return dobb_step_g_grouped(1, s, &W, w_dtype, &G, g_dtype, &M, &P, p_dtype, hp, &U_out, &C_out, ws, ws_bytes, stream);
 }
 
 dobb_status dobb_step_noalloc(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,

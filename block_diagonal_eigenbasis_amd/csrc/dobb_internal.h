@@ -173,6 +173,12 @@ struct StepArgs {
     uint16_t *const *planes;          // bf16 planes of Q (bf16 path)
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+// M <- mu M + G for matrices c0 .. c0 + cnt - 1 of a (k_step.hip)
+hipError_t launch_momentum(const StepArgs &a, int c0, int cnt, hipStream_t s);
+// The Dobb-G step (k_step_g.hip): blocks of sh.nb rows, bases a.Q = P (m / nb blocks); cnt <= kMaxMats.
+// Workspace per matrix: sign codes (m x n bytes), or fp32 coefficients (m x n) and row scales (m).
+size_t step_g_ws_one(const dobb_shape &sh, int norm);
+hipError_t launch_step_g(const StepArgs &a, hipStream_t s);
 // bf16 basis <-> fp32 copy (k_basis.hip): cnt <= kMaxMats matrices of `elems` entries each
 hipError_t launch_basis_convert(int cnt, const void *const *src, void *const *dst, int64_t elems, bool to_f32,
                                 hipStream_t s);

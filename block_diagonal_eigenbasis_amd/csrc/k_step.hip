@@ -287,6 +287,27 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+hipError_t launch_momentum(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    const int64_t numel = a.sh.m * a.sh.n;
+    MomTable t{};
+    bool vec = numel % 4 == 0;
+    for (int i = 0; i < cnt; ++i) {
+        t.G[i] = a.G[c0 + i]; t.M[i] = a.M[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+        vec = vec && aligned16(t.G[i]) && aligned16(t.M[i]);
+    }
+    const int64_t want = (numel / 4 + 255) / 256;
+    const int gx = (int)(want < 2048 ? (want > 0 ? want : 1) : 2048);
+    const dim3 grid(gx, cnt);
+    if (a.g_dtype == DOBB_BF16) {
+        if (vec) DOBB_LAUNCH("momentum", s, (k_momentum<true, true>), grid, dim3(256), 0, numel, t);
+        else DOBB_LAUNCH("momentum", s, (k_momentum<true, false>), grid, dim3(256), 0, numel, t);
+    } else {
+        if (vec) DOBB_LAUNCH("momentum", s, (k_momentum<false, true>), grid, dim3(256), 0, numel, t);
+        else DOBB_LAUNCH("momentum", s, (k_momentum<false, false>), grid, dim3(256), 0, numel, t);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t m = a.sh.m, n = a.sh.n;
     const int nb = (int)a.sh.nb;
@@ -313,23 +334,8 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
         }
         // momentum
         {
-            MomTable t{};
-            bool vec = (m * n) % 4 == 0;
-            for (int i = 0; i < cnt; ++i) {
-                t.G[i] = a.G[c0 + i]; t.M[i] = a.M[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
-                vec = vec && aligned16(t.G[i]) && aligned16(t.M[i]);
-            }
-            const int64_t numel = m * n;
-            int64_t want = (numel / 4 + 255) / 256;
-            int gx = (int)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-            dim3 grid(gx, cnt);
-            if (a.g_dtype == DOBB_BF16) {
-                if (vec) DOBB_LAUNCH("momentum", s, (k_momentum<true, true>), grid, dim3(256), 0, numel, t);
-                else DOBB_LAUNCH("momentum", s, (k_momentum<true, false>), grid, dim3(256), 0, numel, t);
-            } else {
-                if (vec) DOBB_LAUNCH("momentum", s, (k_momentum<false, true>), grid, dim3(256), 0, numel, t);
-                else DOBB_LAUNCH("momentum", s, (k_momentum<false, false>), grid, dim3(256), 0, numel, t);
-            }
+            const hipError_t e = launch_momentum(a, c0, cnt, s);
+            if (e != hipSuccess) return e;
         }
         const int norm = a.hp[c0].norm;
         const int nest = a.hp[c0].nesterov ? (a.g_dtype == DOBB_BF16 ? 2 : 1) : 0;

@@ -5,7 +5,8 @@ iterations only (Table 17: from the first micro-batch by default, or from all of
 refreshed every T steps (Table 14; T = 9 in the principal runs), the first refresh is an exact
 eigendecomposition and later ones warm-started orthogonal iteration with k = 1 (Table 15), the basis
 may be stored in bf16 (Table 18's principal setting), and the update scale is tau sqrt(max(m, n)/m)
-with tau = 0.2 (Table 9).
+with tau = 0.2 (Table 9).  Dobb-G (Tables 12-13) takes the basis from the output-gradient second
+moment instead, with blocks of rows: side="output" (update scale tau sqrt(max(m, n)/n), Table 9).
 
 ``DobbGroup`` keeps the optimizer state (M, A, Q) of a matrix set as device tensors, marshals the
 per-matrix pointer tables once and owns its workspace, so a step is a handful of ctypes calls.  The
@@ -24,6 +25,11 @@ from . import _abi
 
 def default_update_scale(m: int, n: int, tau: float = 0.2) -> float:
     return tau * math.sqrt(max(m, n) / m)
+
+
+def default_update_scale_g(m: int, n: int, tau: float = 0.2) -> float:
+    """Dobb-G (Table 9): RMS tau sqrt(max(m, n)/n) for the sign update."""
+    return tau * math.sqrt(max(m, n) / n)
 
 
 def _arr(ptrs):
@@ -49,7 +55,9 @@ class _Part:
         shapes = [g.shapes[i] for i in self.idx]
         self.shapes = shapes
         self.sh = (_abi.Shape * self.count)(*[_abi.Shape(*s) for s in shapes])
-        self.ash = (_abi.Shape * self.count)(*[_abi.Shape(1, n, nb) for (_, n, nb) in shapes])
+        # the moments and bases live on the captured axis: inputs (n) for Dobb, outputs (m) for Dobb-G
+        self.cshapes = [(1, g.cap_dim(i), g.nb[i]) for i in self.idx]
+        self.ash = (_abi.Shape * self.count)(*[_abi.Shape(*c) for c in self.cshapes])
         self.w_dtype = _abi._dtype_code(g.W[self.idx[0]])
         self.W = _arr([g.W[i].data_ptr() for i in self.idx])
         self.M = _arr([g.M[i].data_ptr() for i in self.idx])
@@ -57,7 +65,7 @@ class _Part:
         self.Q = _arr([g.Q[i].data_ptr() for i in self.idx])
         self.lam = _arr([g.lam[i].data_ptr() for i in self.idx])
         self.info = _arr([g.info[i].data_ptr() for i in self.idx])
-        self.ldx = (ctypes.c_int64 * self.count)(*[n for (_, n, _) in shapes])
+        self.ldx = (ctypes.c_int64 * self.count)(*[c[1] for c in self.cshapes])
         self.hp = (_abi.HParams * self.count)(*[g.hp[i] for i in self.idx])
         self.ws = None
         self.device = g.device
@@ -65,8 +73,8 @@ class _Part:
 
     def need(self, g, n_tokens):
         qv = _abi.DOBB_WS_BF16_BASIS if g.q_dtype == _abi.DOBB_BF16 else 0
-        ash = [(1, n, nb) for (_, n, nb) in self.shapes]
-        return max(_abi.dobb_workspace_size(_abi.DOBB_OP_STEP, self.shapes, 0, g.norm | qv),
+        ash = self.cshapes
+        return max(_abi.dobb_workspace_size(g.step_op, self.shapes, 0, g.norm | qv),
                    _abi.dobb_workspace_size(_abi.DOBB_OP_REFRESH, ash, 0, qv),
                    _abi.dobb_workspace_size(_abi.DOBB_OP_ACCUMULATE, ash, max(n_tokens, 1)))
 
@@ -90,12 +98,18 @@ class DobbGroup:
     streams=2 splits the set into the weights with blocks of at most 128 columns and the wider ones
     and runs the two on separate streams (each with its own workspace), joined back into the
     caller's stream: the two kernel families then overlap (the wide blocks' refresh is a chain of
-    latency-bound panel launches).  basis_dtype=torch.bfloat16 stores every Q_b in bf16."""
+    latency-bound panel launches).  basis_dtype=torch.bfloat16 stores every Q_b in bf16.
+    side="output" runs Dobb-G: block_sizes divide the output dimensions, the moments are captured from
+    output gradients (accumulate takes N x m tensors) and the step is dobb_step_g."""
 
     def __init__(self, weights, block_sizes, grads=None, n_tokens: int = 0, lr: float = 2.5e-3,
                  weight_decay: float = 0.0, momentum: float = 0.9, tau: float = 0.2, nesterov: bool = False,
                  norm: int = _abi.DOBB_NORM_SIGN, update_scales=None, streams: int = 1,
-                 basis_dtype: torch.dtype = torch.float32):
+                 basis_dtype: torch.dtype = torch.float32, side: str = "input"):
+        if side not in ("input", "output"):
+            raise ValueError('side must be "input" (Dobb) or "output" (Dobb-G)')
+        self.side = side
+        self.step_op = _abi.DOBB_OP_STEP if side == "input" else _abi.DOBB_OP_STEP_G
         self.W = list(weights)
         self.nb = [int(b) for b in block_sizes]
         if len(self.nb) != len(self.W):
@@ -108,27 +122,33 @@ class DobbGroup:
             if w.dim() != 2 or not w.is_contiguous() or w.device != dev:
                 raise ValueError("weights must be contiguous 2-D tensors on one device")
         self.shapes = [(w.shape[0], w.shape[1], nb) for w, nb in zip(self.W, self.nb)]
-        for (m, n, nb) in self.shapes:
-            if n % nb:
-                raise ValueError(f"block size {nb} does not divide {n}")
+        for i, nb in enumerate(self.nb):
+            if self.cap_dim(i) % nb:
+                raise ValueError(f"block size {nb} does not divide {self.cap_dim(i)}")
         if basis_dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("basis_dtype must be torch.float32 or torch.bfloat16")
         self.q_dtype = _abi.DOBB_BF16 if basis_dtype == torch.bfloat16 else _abi.DOBB_F32
         self.M = [torch.zeros(w.shape, dtype=torch.float32, device=dev) for w in self.W]
-        self.A = [torch.zeros(n // nb, nb, nb, dtype=torch.float32, device=dev) for (_, n, nb) in self.shapes]
+        nblk = [self.cap_dim(i) // nb for i, nb in enumerate(self.nb)]
+        self.A = [torch.zeros(B, nb, nb, dtype=torch.float32, device=dev) for B, nb in zip(nblk, self.nb)]
         # Q = I before the first refresh (the step is then sign(M)); the identity is exact in bf16
-        self.Q = [torch.eye(nb, dtype=basis_dtype, device=dev).expand(n // nb, nb, nb).contiguous()
-                  for (_, n, nb) in self.shapes]
-        self.lam = [torch.zeros(n // nb, nb, dtype=torch.float32, device=dev) for (_, n, nb) in self.shapes]
-        self.info = [torch.zeros(n // nb, dtype=torch.int32, device=dev) for (_, n, nb) in self.shapes]
+        self.Q = [torch.eye(nb, dtype=basis_dtype, device=dev).expand(B, nb, nb).contiguous()
+                  for B, nb in zip(nblk, self.nb)]
+        self.lam = [torch.zeros(B, nb, dtype=torch.float32, device=dev) for B, nb in zip(nblk, self.nb)]
+        self.info = [torch.zeros(B, dtype=torch.int32, device=dev) for B in nblk]
         self.G = list(grads) if grads is not None else None
-        scales = update_scales or [default_update_scale(m, n, tau) for (m, n, _) in self.shapes]
+        scale_fn = default_update_scale if side == "input" else default_update_scale_g
+        scales = update_scales or [scale_fn(m, n, tau) for (m, n, _) in self.shapes]
         self.hp = [_abi.make_hparams(lr, weight_decay, momentum, s, nesterov, norm) for s in scales]
         self.norm = norm
         self.n_tokens = n_tokens
         self._parts = []
         self.set_streams(streams)
         self.refreshes = 0
+
+    def cap_dim(self, i: int) -> int:
+        """The dimension the moments of weight i are captured on: n (inputs) or m (outputs, Dobb-G)."""
+        return self.W[i].shape[1] if self.side == "input" else self.W[i].shape[0]
 
     def set_streams(self, streams: int) -> None:
         """Partition the weights for `streams` streams (1 or 2), and by weight dtype; the state
@@ -182,16 +202,16 @@ class DobbGroup:
             if len(sub) == part.count:
                 ash, A, ldx = part.ash, part.A, part.ldx
             else:
-                ash = (_abi.Shape * len(sub))(*[_abi.Shape(1, self.shapes[i][1], self.nb[i]) for i in sub])
+                ash = (_abi.Shape * len(sub))(*[_abi.Shape(1, self.cap_dim(i), self.nb[i]) for i in sub])
                 A = _arr([self.A[i].data_ptr() for i in sub])
-                ldx = (ctypes.c_int64 * len(sub))(*[self.shapes[i][1] for i in sub])
+                ldx = (ctypes.c_int64 * len(sub))(*[self.cap_dim(i) for i in sub])
             for i in sub:
                 x = xs[i]
-                if x.dim() != 2 or x.shape[1] != self.shapes[i][1] or not x.is_contiguous() or x.device != self.device:
-                    raise ValueError(f"activation {i} must be a contiguous (tokens x {self.shapes[i][1]}) tensor")
+                if x.dim() != 2 or x.shape[1] != self.cap_dim(i) or not x.is_contiguous() or x.device != self.device:
+                    raise ValueError(f"capture {i} must be a contiguous (tokens x {self.cap_dim(i)}) tensor")
             N = xs[sub[0]].shape[0]
             part.ensure(_abi.dobb_workspace_size(_abi.DOBB_OP_ACCUMULATE,
-                                                 [(1, self.shapes[i][1], self.nb[i]) for i in sub], N))
+                                                 [(1, self.cap_dim(i), self.nb[i]) for i in sub], N))
             _abi._check(_abi.lib().dobb_accumulate_moment_grouped(
                 len(sub), ash, _arr([xs[i].data_ptr() for i in sub]), _abi._dtype_code(xs[sub[0]]), N, ldx,
                 float(beta), A, part.ws.data_ptr(), part.ws.numel(), sh), "dobb_accumulate_moment_grouped")
@@ -218,12 +238,14 @@ class DobbGroup:
                 Mp = _arr([self.M[i].data_ptr() for i in sub])
                 Qp = _arr([self.Q[i].data_ptr() for i in sub])
                 hp = (_abi.HParams * len(sub))(*[part.hp[pos[i]] for i in sub])
-            _abi._check(_abi.lib().dobb_step_grouped(
-                len(sub), shp, Wp, part.w_dtype, _arr([G[i].data_ptr() for i in sub]), _abi._dtype_code(G[sub[0]]),
-                Mp, Qp, self.q_dtype, hp, None, None, part.ws.data_ptr(), part.ws.numel(), sh), "dobb_step_grouped")
+            fn = _abi.lib().dobb_step_grouped if self.side == "input" else _abi.lib().dobb_step_g_grouped
+            _abi._check(fn(len(sub), shp, Wp, part.w_dtype, _arr([G[i].data_ptr() for i in sub]),
+                           _abi._dtype_code(G[sub[0]]), Mp, Qp, self.q_dtype, hp, None, None, part.ws.data_ptr(),
+                           part.ws.numel(), sh), "dobb_step_grouped" if self.side == "input" else "dobb_step_g_grouped")
 
     def accumulate(self, xs, beta: float, stream=None) -> None:
-        """Capture: A_b <- beta A_b + (1-beta)/N X_b^T X_b for every weight (xs[i] is N_i x n_i)."""
+        """Capture: A_b <- beta A_b + (1-beta)/N X_b^T X_b for every weight (xs[i] is N_i x n_i, or the
+        N_i x m_i output gradients for Dobb-G)."""
         self._grow(max(x.shape[0] for x in xs))
         self._run(stream, lambda part, sh: self._accumulate(part, sh, xs, beta))
 
@@ -265,24 +287,31 @@ class Dobb(torch.optim.Optimizer):
     ``step()`` on refresh iterations; ``wants_capture()`` says whether the coming step refreshes.
     capture="first" keeps a weight's first micro-batch of a refresh iteration (the principal policy
     of Table 17), capture="all" every micro-batch (their tokens are pooled into one capture).
+    basis="output_gradient" runs Dobb-G (Tables 12-13): blocks of rows (m // blocks, or block_size),
+    bases of the output-gradient second moment, captured by the backward hooks of
+    ``attach_capture_hooks`` (or ``capture(param, grad_output)``).
     """
 
     def __init__(self, params, lr: float = 2.5e-3, weight_decay: float = 0.0, momentum: float = 0.9,
                  blocks: int = 16, block_size: int | None = None, refresh_period: int = 9, orth_iters: int = 1,
                  beta: float = 0.9, tau: float = 0.2, nesterov: bool = False, streams: int = 1,
-                 capture: str = "first", basis_dtype: torch.dtype = torch.float32):
+                 capture: str = "first", basis_dtype: torch.dtype = torch.float32, basis: str = "activation"):
         super().__init__(params, dict(lr=lr, weight_decay=weight_decay, momentum=momentum))
         if capture not in ("first", "all"):
             raise ValueError('capture must be "first" or "all"')
+        if basis not in ("activation", "output_gradient"):
+            raise ValueError('basis must be "activation" (Dobb) or "output_gradient" (Dobb-G)')
         params = [p for grp in self.param_groups for p in grp["params"]]
         for p in params:
             if p.dim() != 2:
                 raise ValueError("Dobb handles 2-D weights; use another optimizer for the rest")
-        nbs = [block_size or p.shape[1] // blocks for p in params]
+        self.side = "input" if basis == "activation" else "output"
+        axis = 1 if self.side == "input" else 0
+        nbs = [block_size or p.shape[axis] // blocks for p in params]
         self._params = params
         self._group = DobbGroup([p.data for p in params], nbs, lr=lr, weight_decay=weight_decay,
                                 momentum=momentum, tau=tau, nesterov=nesterov, streams=streams,
-                                basis_dtype=basis_dtype)
+                                basis_dtype=basis_dtype, side=self.side)
         self._slots = []                      # per param group: the weight indices
         k = 0
         for grp in self.param_groups:
@@ -300,27 +329,34 @@ class Dobb(torch.optim.Optimizer):
         return self.t % self.T == 0
 
     def capture(self, param, x: torch.Tensor) -> None:
-        """Record (tokens x n) input activations of `param` for the next refresh: the first call per
-        refresh iteration, or every call with capture="all"."""
+        """Record (tokens x n) input activations of `param` (Dobb), or (tokens x m) output gradients
+        (Dobb-G), for the next refresh: the first call per refresh iteration, or every call with
+        capture="all"."""
         x = x.detach().reshape(-1, x.shape[-1])
         got = self._captured.setdefault(id(param), [])
         if self.capture_policy == "all" or not got:
             got.append(x.contiguous())
 
     def attach_capture_hooks(self, modules):
-        """Forward pre-hooks on nn.Linear modules whose weights this optimizer owns: on refresh
-        iterations their inputs are captured (the first micro-batch, or all with capture="all")."""
+        """Hooks on nn.Linear modules whose weights this optimizer owns: on refresh iterations their
+        inputs (forward pre-hooks; Dobb) or output gradients (backward hooks; Dobb-G) are captured,
+        from the first micro-batch, or all of them with capture="all"."""
         handles = []
         owned = {id(p) for p in self._params}
         for mod in modules:
             w = getattr(mod, "weight", None)
             if w is None or id(w) not in owned:
                 continue
-
-            def hook(module, inputs, w=w):
-                if self.wants_capture():
-                    self.capture(w, inputs[0])
-            handles.append(mod.register_forward_pre_hook(hook))
+            if self.side == "input":
+                def hook(module, inputs, w=w):
+                    if self.wants_capture():
+                        self.capture(w, inputs[0])
+                handles.append(mod.register_forward_pre_hook(hook))
+            else:
+                def bhook(module, grad_input, grad_output, w=w):
+                    if self.wants_capture() and grad_output[0] is not None:
+                        self.capture(w, grad_output[0])
+                handles.append(mod.register_full_backward_hook(bhook))
         return handles
 
     def _sync_hparams(self) -> None:

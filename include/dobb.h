@@ -68,7 +68,7 @@ typedef enum {
     DOBB_NORM_COL_L2 = 2         /* Tables 11-12 "Dobb-l2": unit l2 norm per column of C_b */
 } dobb_norm;
 
-typedef enum { DOBB_OP_ACCUMULATE = 0, DOBB_OP_REFRESH = 1, DOBB_OP_STEP = 2 } dobb_op;
+typedef enum { DOBB_OP_ACCUMULATE = 0, DOBB_OP_REFRESH = 1, DOBB_OP_STEP = 2, DOBB_OP_STEP_G = 3 } dobb_op;
 
 typedef struct {
     int64_t m;   /* output dimension (rows of W) */
@@ -166,6 +166,29 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
                               const void *const *Q, dobb_dtype q_dtype, const dobb_hparams *hp,
                               float *const *U_out, float *const *C_out, void *ws, size_t ws_bytes,
                               dobb_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * The Dobb-G step (Tables 12-13: the basis of the output-gradient second moment; Figure 2 caption:
+ * that moment is m x m; Table 7: blocks along the output axis, and Dobb-G-l2 normalises along the
+ * input axis; Table 9: its update scale).  Blocks are nb consecutive ROWS: s = {m, n, nb} with
+ * m % nb == 0 and B = m / nb.  P: device B x nb x nb in p_dtype (fp32 or bf16), the bases of the
+ * blocks of the output-gradient moment: capture it with dobb_accumulate_moment on the output
+ * gradients (N x m, shape {1, m, nb}) and refresh it with dobb_refresh_basis, unchanged.
+ *   M <- mu M + G;  P_eff = M (or G + mu M);  C_b = P_b^T P_eff[rows of b, :]  (nb x n);
+ *   U[rows of b, :] = P_b sign(C_b)   (IDENTITY: P_b C_b = M;  COL_L2: P_b diag(1/||c_i||) C_b with
+ *   each row c_i of C_b normalised over the n columns: Dobb-G-l2);
+ *   W <- W - lr (update_scale U + weight_decay W).
+ * Table 9's Dobb-G row gives RMS tau sqrt(max(m,n)/n) for sign (update_scale = tau sqrt(max(m,n)/n))
+ * and tau sqrt(max(m,n)) for Dobb-G-l2.  Other arguments, layouts and errors as dobb_step (C_out
+ * receives C_b in the rows of block b); the workspace is dobb_workspace_size(DOBB_OP_STEP_G, ...).
+ * -------------------------------------------------------------------------------------------------*/
+dobb_status dobb_step_g(const dobb_shape *s, void *W, dobb_dtype w_dtype, const void *G, dobb_dtype g_dtype,
+                        float *M, const void *P, dobb_dtype p_dtype, const dobb_hparams *hp, float *U_out,
+                        float *C_out, void *ws, size_t ws_bytes, dobb_stream_t stream);
+dobb_status dobb_step_g_grouped(int count, const dobb_shape *shapes, void *const *W, dobb_dtype w_dtype,
+                                const void *const *G, dobb_dtype g_dtype, float *const *M, const void *const *P,
+                                dobb_dtype p_dtype, const dobb_hparams *hp, float *const *U_out,
+                                float *const *C_out, void *ws, size_t ws_bytes, dobb_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------------
  * The step without a workspace argument, for callers that cannot allocate device memory (code under

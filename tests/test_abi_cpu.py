@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _abi.lib()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
 
@@ -182,3 +182,21 @@ def test_step_noalloc_refuses_before_any_launch():
     # every single weight of the GPT-2 XL and 7B-style sets fits with sign normalisation
     for shp in [(4800, 1600, 100), (6400, 1600, 100), (1600, 6400, 400), (11008, 4096, 128), (4096, 11008, 128)]:
         assert 0 < _abi.dobb_workspace_size(_abi.DOBB_OP_STEP, [shp], 0, 0) <= _abi.DOBB_NOALLOC_SCRATCH_BYTES
+
+
+def test_step_g_shape_errors_and_workspace():
+    """Dobb-G's blocks are rows: m % nb == 0 is required and n is free."""
+    L = _abi.lib()
+    hp = _abi.make_hparams(0.1, 0.0, 0.9, 0.2)
+    for (m, n, nb), want in [((10, 8, 4), -2), ((0, 8, 4), -2), ((8, 0, 4), -2), ((8, 6, 0), -2)]:
+        s = _shape(m, n, nb)
+        st = L.dobb_step_g(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, FAKE,
+                           1 << 30, None)
+        assert st == want, (m, n, nb)
+    s = _shape(8, 6, 4)   # n % nb != 0 is fine for row blocks: fails only on the missing workspace
+    assert L.dobb_step_g(ctypes.byref(s), FAKE, 0, FAKE, 0, FAKE, FAKE, 0, ctypes.byref(hp), None, None, None, 0,
+                         None) == -4
+    ws = _abi.dobb_workspace_size
+    assert ws(_abi.DOBB_OP_STEP_G, [(768, 770, 192)], 0, 0) >= 768 * 770
+    assert ws(_abi.DOBB_OP_STEP_G, [(768, 770, 192)], 0, 2) >= 4 * 768 * 770 + 4 * 768
+    assert ws(_abi.DOBB_OP_STEP_G, [(770, 768, 192)], 0, 0) == 0

@@ -260,3 +260,52 @@ def test_capture_all_micro_batches_and_bf16_basis():
         assert g.Q[i].dtype == torch.bfloat16
         assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
         assert torch.equal(g.A[i], A_ref[i]) and torch.equal(g.Q[i], Q_ref[i]), f"state {i}"
+
+
+def test_dobb_g_optimizer_captures_output_gradients():
+    """basis="output_gradient" (Dobb-G, Tables 12-13): backward hooks capture each weight's output
+    gradient on refresh iterations, the moments and bases live on the output axis (blocks of rows),
+    and the step is dobb_step_g; bit for bit equal to those entry points called in turn."""
+    rng = RNG(97)
+    dims = [(128, 96), (64, 256)]           # (m, n); blocks=2: nb = 64, 32 rows
+    mods = [torch.nn.Linear(n, m, bias=False).to(DEV) for m, n in dims]
+    params = [mod.weight for mod in mods]
+    with torch.no_grad():
+        for p in params:
+            p.copy_(t32(0.02 * rng.standard_normal(tuple(p.shape))))
+    opt = Dobb(params, lr=2.5e-3, weight_decay=0.1, momentum=0.9, blocks=2, refresh_period=2,
+               basis="output_gradient")
+    hooks = opt.attach_capture_hooks(mods)
+    nbs = [m // 2 for m, _ in dims]
+    W_ref = [p.detach().clone() for p in params]
+    M_ref = [torch.zeros(m, n, device=DEV) for m, n in dims]
+    A_ref = [torch.zeros(2, nb, nb, device=DEV) for nb in nbs]
+    P_ref = [torch.eye(nb, device=DEV).expand(2, nb, nb).contiguous() for nb in nbs]
+    refreshed = False
+    for t in range(4):
+        captures = opt.wants_capture()
+        xs = [t32(workload.activations(200, n, 0.15, rng)) for _, n in dims]
+        dys = [t32(workload.activations(200, m, 0.15, rng)) for m, _ in dims]
+        for p in params:
+            p.grad = None
+        for mod, x, dy in zip(mods, xs, dys):
+            (mod(x) * dy).sum().backward()            # the output gradient is dy
+        grads = [p.grad.detach().clone() for p in params]
+        opt.step()
+        for i, nb in enumerate(nbs):
+            m, n = dims[i]
+            if captures:
+                dobb.dobb_accumulate_moment(dys[i], A_ref[i], nb, 0.9 if refreshed else 0.0)
+                mode = dobb.DOBB_REFRESH_ORTH_ITER if refreshed else dobb.DOBB_REFRESH_EXACT
+                dobb.dobb_refresh_basis(A_ref[i], P_ref[i], mode, iters=1 if refreshed else 0, warm_start=refreshed)
+            dobb.dobb_step_g(W_ref[i], grads[i], M_ref[i], P_ref[i], nb,
+                             dobb.make_hparams(2.5e-3, 0.1, 0.9, 0.2 * (max(m, n) / n) ** 0.5))
+        refreshed = refreshed or captures
+    torch.cuda.synchronize()
+    for h in hooks:
+        h.remove()
+    g = opt._group
+    for i in range(len(dims)):
+        assert g.A[i].shape == (2, nbs[i], nbs[i])
+        assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
+        assert torch.equal(g.A[i], A_ref[i]) and torch.equal(g.Q[i], P_ref[i]), f"state {i}"
