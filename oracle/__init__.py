@@ -59,6 +59,10 @@ def _load():
         lib.oracle_step.restype = None
         lib.oracle_step_g.argtypes = [L, L, L, P, P, P, P, D, D, D, D, I, I, P]
         lib.oracle_step_g.restype = None
+        lib.oracle_cholesky_qr2.argtypes = [L, P, P]
+        lib.oracle_cholesky_qr2.restype = I
+        lib.oracle_orth_iter_cholqr2.argtypes = [L, P, P, I, P, P]
+        lib.oracle_orth_iter_cholqr2.restype = I
         _lib = lib
     return _lib
 
@@ -142,10 +146,23 @@ def householder_qr(Z) -> np.ndarray:
     return Q
 
 
-def orth_iter(A, Qprev, k: int = 1, cores: int | None = None):
-    """k steps of warm-started orthogonal iteration per block: Q <- qr(A_b Q).Q (Householder).
+def cholesky_qr2(Z) -> np.ndarray:
+    """Orthonormal factor of a square matrix by Cholesky QR, two passes (diag(R) > 0)."""
+    Z = _f64(Z)
+    n = Z.shape[0]
+    Q = np.zeros((n, n))
+    if _load().oracle_cholesky_qr2(n, _ptr(Z), _ptr(Q)) != 0:
+        raise np.linalg.LinAlgError("Cholesky QR: a pivot was not positive")
+    return Q
+
+
+def orth_iter(A, Qprev, k: int = 1, cores: int | None = None, qr: str = "householder"):
+    """k steps of warm-started orthogonal iteration per block: Q <- qr(A_b Q).Q, with the
+    Householder QR (Table 16's principal) or qr="cholesky" (Table 16's Cholesky QR, two passes).
 
     Returns (Q (B, nb, nb), Rayleigh quotients (B, nb))."""
+    if qr not in ("householder", "cholesky"):
+        raise ValueError(qr)
     A, Qprev = _f64(A), _f64(Qprev)
     B, nb, _ = A.shape
     Q = np.zeros((B, nb, nb))
@@ -154,8 +171,11 @@ def orth_iter(A, Qprev, k: int = 1, cores: int | None = None):
 
     def one(b):
         qb, lb = np.zeros((nb, nb)), np.zeros(nb)
-        lib.oracle_orth_iter(nb, _ptr(np.ascontiguousarray(A[b])), _ptr(np.ascontiguousarray(Qprev[b])),
-                             int(k), _ptr(qb), _ptr(lb))
+        a, qp = _ptr(np.ascontiguousarray(A[b])), _ptr(np.ascontiguousarray(Qprev[b]))
+        if qr == "householder":
+            lib.oracle_orth_iter(nb, a, qp, int(k), _ptr(qb), _ptr(lb))
+        elif lib.oracle_orth_iter_cholqr2(nb, a, qp, int(k), _ptr(qb), _ptr(lb)) != 0:
+            raise np.linalg.LinAlgError(f"Cholesky QR failed in block {b}")
         Q[b], lam[b] = qb, lb
 
     with _pool(cores) as ex:

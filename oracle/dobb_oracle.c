@@ -383,3 +383,87 @@ void oracle_step_g(long m, long n, long nb, double *W, const double *G, double *
     if (U) memcpy(U, Uall, sizeof(double) * m * n);
     free(Meff); free(Uall); free(C);
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Cholesky QR of a square n x n matrix Z (Table 16: "Cholesky" is the faster QR routine of the
+ * orthogonal-iteration refresh, next to the principal Householder).  Reading: CholeskyQR2, i.e. two
+ * passes of
+ *     G = Z^T Z,   G = R^T R (Cholesky, R upper triangular with a positive diagonal),   Z <- Z R^{-1};
+ * in exact arithmetic the second pass has R = I, in floating point it restores the orthogonality
+ * the first one loses (about cond(Z)^2 u).  The result is the orthonormal factor of the QR with
+ * diag(R) > 0 (R = R_2 R_1): the same factor as oracle_householder_qr.  Returns 0, or -1 if a pivot
+ * was not positive (Z numerically rank deficient), in which case Q is left undefined.
+ * ---------------------------------------------------------------------------------------------- */
+int oracle_cholesky_qr2(long n, const double *Z, double *Q)
+{
+    double *X = (double *)malloc(sizeof(double) * n * n);
+    double *G = (double *)malloc(sizeof(double) * n * n);
+    int status = 0;
+    memcpy(X, Z, sizeof(double) * n * n);
+    for (int pass = 0; pass < 2 && status == 0; ++pass) {
+        /* G = X^T X */
+        for (long i = 0; i < n; ++i)
+            for (long j = 0; j < n; ++j) {
+                double s = 0.0;
+                for (long k = 0; k < n; ++k) s += X[k * n + i] * X[k * n + j];
+                G[i * n + j] = s;
+            }
+        /* Cholesky, row by row: R[i][i] = sqrt(G_ii - sum_k R_ki^2), R[i][j] = (G_ij - sum_k R_ki R_kj) / R_ii;
+           R overwrites the upper triangle of G */
+        for (long i = 0; i < n && status == 0; ++i) {
+            double d = G[i * n + i];
+            for (long k = 0; k < i; ++k) d -= G[k * n + i] * G[k * n + i];
+            if (!(d > 0.0)) { status = -1; break; }
+            double rii = sqrt(d);
+            G[i * n + i] = rii;
+            for (long j = i + 1; j < n; ++j) {
+                double s = G[i * n + j];
+                for (long k = 0; k < i; ++k) s -= G[k * n + i] * G[k * n + j];
+                G[i * n + j] = s / rii;
+            }
+        }
+        if (status) break;
+        /* X <- X R^{-1}: each row x solves y R = x by forward substitution along the columns */
+        for (long r = 0; r < n; ++r) {
+            double *x = X + r * n;
+            for (long j = 0; j < n; ++j) {
+                double s = x[j];
+                for (long k = 0; k < j; ++k) s -= x[k] * G[k * n + j];
+                x[j] = s / G[j * n + j];
+            }
+        }
+    }
+    memcpy(Q, X, sizeof(double) * n * n);
+    free(X); free(G);
+    return status;
+}
+
+/* Orthogonal-iteration refresh with the Cholesky QR routine (Table 16): as oracle_orth_iter, with
+ * Q <- CholeskyQR2(A_b Q).  Returns 0, or -1 if a Cholesky pivot failed. */
+int oracle_orth_iter_cholqr2(long n, const double *A, const double *Qprev, int k, double *Q, double *lam_out)
+{
+    double *Z = (double *)malloc(sizeof(double) * n * n);
+    int status = 0;
+    memcpy(Q, Qprev, sizeof(double) * n * n);
+    for (int it = 0; it < k && status == 0; ++it) {
+        memset(Z, 0, sizeof(double) * n * n);
+        for (long i = 0; i < n; ++i)
+            for (long l = 0; l < n; ++l)
+                for (long j = 0; j < n; ++j)
+                    Z[i * n + j] += A[i * n + l] * Q[l * n + j];
+        status = oracle_cholesky_qr2(n, Z, Q);
+    }
+    if (lam_out && status == 0) {
+        for (long j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (long p = 0; p < n; ++p) {
+                double aq = 0.0;
+                for (long q = 0; q < n; ++q) aq += A[p * n + q] * Q[q * n + j];
+                s += Q[p * n + j] * aq;
+            }
+            lam_out[j] = s;
+        }
+    }
+    free(Z);
+    return status;
+}

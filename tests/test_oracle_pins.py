@@ -572,3 +572,50 @@ def test_dobb_g_l2_rows_have_unit_norm():
         b_ = oracle.step_g(W, G, M, P, nb, 0.01, 0.1, 0.9, 0.5, norm=norm, cores=3)
         for x, y in zip(a, b_):
             np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------------------------------------------------------
+# Cholesky QR (Table 16's faster QR routine of the refresh)
+
+@pytest.mark.parametrize("n,cond", [(8, 10.0), (40, 1e3), (100, 1e6)])
+def test_cholesky_qr2_is_the_unique_qr_factor(n, cond):
+    """QR with diag(R) > 0 is unique: Cholesky QR equals LAPACK's sign-fixed Householder factor and
+    the oracle's own Householder QR to cond * 1e-13, is orthonormal to 1e-14 even at cond 1e6 (one
+    pass alone loses about cond^2 u = 1e-4 there), and Q^T Z is upper triangular with a positive
+    diagonal."""
+    rng = RNG(600 + n)
+    U, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    Z = (U * np.geomspace(1.0, 1.0 / cond, n)) @ V.T
+    Q = oracle.cholesky_qr2(Z)
+    q, r = np.linalg.qr(Z)
+    ref = q * np.sign(np.diag(r))
+    np.testing.assert_allclose(Q, ref, atol=1e-13 * cond)
+    np.testing.assert_allclose(Q, oracle.householder_qr(Z), atol=1e-13 * cond)
+    assert np.max(np.abs(Q.T @ Q - np.eye(n))) <= 1e-14 * n
+    R = Q.T @ Z
+    assert np.max(np.abs(np.tril(R, -1))) <= 1e-12 * np.linalg.norm(Z)
+    assert np.all(np.diag(R) > 0)
+
+
+def test_cholesky_qr2_reports_rank_deficiency():
+    Z = np.ones((5, 5))
+    with pytest.raises(np.linalg.LinAlgError):
+        oracle.cholesky_qr2(Z)
+
+
+def test_orth_iter_with_cholesky_qr_equals_householder():
+    """Both QR routines give the same refresh (Table 16 compares them as interchangeable routines);
+    the exact eigenbasis is a fixed point of either."""
+    rng = RNG(610)
+    A = np.stack([_spd(24, rng, spread=300)[0] for _ in range(3)])
+    Qp = _random_basis(3, 24, rng)
+    for k in (1, 2):
+        Qh, lh = oracle.orth_iter(A, Qp, k=k)
+        Qc, lc = oracle.orth_iter(A, Qp, k=k, qr="cholesky")
+        np.testing.assert_allclose(Qc, Qh, atol=1e-11)
+        np.testing.assert_allclose(lc, lh, rtol=1e-12, atol=1e-14)
+    w, V = np.linalg.eigh(A[0])
+    V = V[:, ::-1] * np.sign(V[:, ::-1][0])
+    Q1, _ = oracle.orth_iter(A[:1], V[None], k=1, qr="cholesky")
+    np.testing.assert_allclose(Q1[0], V, atol=1e-12)
