@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--norm", choices=["sign", "col_l2"], default="sign",
                     help="normalisation of the coefficients: sign (Dobb) or column-l2 (Dobb-l2, Tables 11-12)")
     ap.add_argument("--orth-iters", type=int, default=1, help="orthogonal-iteration steps per refresh (Table 15)")
+    ap.add_argument("--qr", choices=["householder", "cholesky"], default="householder",
+                    help="QR routine of the orthogonal-iteration refresh (Table 16: Householder is the principal)")
     ap.add_argument("--basis", choices=["fp32", "bf16"], default="fp32",
                     help="storage of the block bases (Table 18: bf16 is the pages' principal setting)")
     ap.add_argument("--streams", type=int, choices=[1, 2], default=1,
@@ -110,7 +112,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1, x_bytes=2):
+def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1, x_bytes=2, qr="householder"):
     """Per-step work of each kernel of the path, summed over the matrix set.
 
     Per kernel: algorithmic HBM bytes (each operand read or written once), algorithmic flops with the
@@ -143,7 +145,11 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       project_l2_f16x3      M read + written, G read, C written: (12 + g) m n bytes; three fp16 products
       colscale              the tiles' column sums of squares read: 8 ceil(m / 128) n bytes
       reconstruct_l2_f16x3  C read, W read + written: (4 + 2 w) m n bytes; three fp16 products
-    The refresh kernels run orth_iters times per refresh.
+    The refresh kernels run orth_iters times per refresh.  With qr="cholesky" (Table 16) the refresh is
+    Z = A Q and two Cholesky QR passes, each a Gram product Z^T Z, the factor R with its inverse and
+    the product Z R^{-1}:
+      refresh_gemm          five nb^3 products: 10 nb^3 B flops (fp32)
+      cholqr_factor         R (nb^3 / 3) and R^{-1} (nb^3 / 3) twice: 4/3 nb^3 B flops
     """
     w = {}
 
@@ -162,8 +168,14 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
             add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
         add("accumulate_reduce", 8.0 * nb * nb * B)
         k = orth_iters
-        add("refresh_gemm", k * 12.0 * nb * nb * B, k * 2.0 * nb ** 3 * B)
-        if nb <= QR_SINGLE_LAUNCH_MAX_NB:
+        if qr == "cholesky":
+            add("refresh_gemm", k * 5 * 12.0 * nb * nb * B, k * 10.0 * nb ** 3 * B)
+            add("cholqr_factor", 0.0, k * 4.0 / 3.0 * nb ** 3 * B)
+        else:
+            add("refresh_gemm", k * 12.0 * nb * nb * B, k * 2.0 * nb ** 3 * B)
+        if qr == "cholesky":
+            pass
+        elif nb <= QR_SINGLE_LAUNCH_MAX_NB:
             add("qr_block", 0.0, k * 8.0 / 3.0 * nb ** 3 * B)
         else:
             add("qr_update", 0.0, k * 4.0 / 3.0 * nb ** 3 * B)
@@ -516,6 +528,7 @@ def main():
                       update_scales=scales, streams=args.streams,
                       basis_dtype=torch.bfloat16 if args.basis == "bf16" else torch.float32)
     K_ORTH = args.orth_iters
+    REFRESH_MODE = dobb.DOBB_REFRESH_ORTH_ITER_CHOLQR if args.qr == "cholesky" else dobb.DOBB_REFRESH_ORTH_ITER
     beta = 0.9
     # setup: first capture and the exact refresh (untimed, but measured once)
     group.accumulate(xs, 0.0)
@@ -535,7 +548,7 @@ def main():
           file=sys.stderr, flush=True)
 
     def full_step():
-        group.refresh_step(xs, beta, dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH)
+        group.refresh_step(xs, beta, REFRESH_MODE, K_ORTH)
 
     for _ in range(args.warmup):
         full_step()
@@ -583,7 +596,7 @@ def main():
     full_ms_untimed = timed(full_step, reps)
     step_ms = timed(group.step, reps)
     acc_ms = timed(lambda: group.accumulate(xs, beta), reps)
-    ref_ms = timed(lambda: group.refresh(dobb.DOBB_REFRESH_ORTH_ITER, K_ORTH), reps)
+    ref_ms = timed(lambda: group.refresh(REFRESH_MODE, K_ORTH), reps)
     # the exact refresh warm-started from the current basis (the exact mode's steady state)
     dobb.dobb_profile_reset()
     dobb.dobb_profile_enable(True)
@@ -602,7 +615,7 @@ def main():
     # ---- roofline: every kernel with a work model; the dominant one (most time) is reported --------
     g_bytes = Gs[0].element_size()
     w_bytes = Ws[0].element_size()
-    work = kernel_work(specs, n_tokens, g_bytes, w_bytes, args.norm, K_ORTH, xs[0].element_size())
+    work = kernel_work(specs, n_tokens, g_bytes, w_bytes, args.norm, K_ORTH, xs[0].element_size(), args.qr)
     per_kernel = {}
     for name, (launches, total_ms) in kernels.items():
         ent = {"launches_per_step": launches / args.steps, "ms_per_step": round(total_ms / args.steps, 4),
@@ -619,7 +632,7 @@ def main():
                 "frac": d["frac"],
                 # counters were taken on the full GPT-2 XL set only
                 "traffic": (measured_traffic(dom) if args.workload == "gpt2xl" and layers == 48
-                            and args.norm == "sign" and K_ORTH == 1 else None),
+                            and args.norm == "sign" and K_ORTH == 1 and args.qr == "householder" else None),
                 "work_per_launch": unit_work / launches,
                 "work_unit": "bytes" if d["bound"] == "hbm" else "flop",
                 "impl_bytes_per_launch": work[dom].get("impl_bytes", 0.0) / launches,
@@ -636,11 +649,11 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl["text"].format(L=layers, N=n_tokens) + f"; capture + orthogonal-iteration "
-                               f"refresh (k={K_ORTH}) + step every step"
+                               f"refresh (k={K_ORTH}, {args.qr} QR) + step every step"
                                + ("; column-l2 normalisation" if col_l2 else "")
                                + ("; bf16 basis" if args.basis == "bf16" else ""),
                    "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
-                   "refresh_period": 1, "streams": args.streams, "basis": args.basis},
+                   "refresh_period": 1, "streams": args.streams, "basis": args.basis, "qr": args.qr},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown_ms": {"full_step_kernel_timer_on": round(ms_per_step_timer, 3),

@@ -12,4 +12,4 @@ from ._abi import (DOBB_BF16, DOBB_F32, DOBB_NORM_COL_L2, DOBB_NORM_IDENTITY, DO
                    dobb_profile_read, dobb_profile_reset, dobb_refresh_basis, dobb_refresh_basis_grouped,
                    dobb_step, dobb_step_grouped, dobb_step_noalloc, dobb_workspace_size, lib, make_hparams,
                    status_string, DOBB_ERR_WORKSPACE, DOBB_NOALLOC_SCRATCH_BYTES, DOBB_WS_BF16_BASIS,
-                   DOBB_OP_STEP_G, dobb_step_g, dobb_step_g_grouped)
+                   DOBB_OP_STEP_G, dobb_step_g, dobb_step_g_grouped, DOBB_REFRESH_ORTH_ITER_CHOLQR)

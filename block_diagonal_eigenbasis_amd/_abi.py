@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdobb.so
 DOBB_OK, DOBB_ERR_INVALID_ARG, DOBB_ERR_SHAPE, DOBB_ERR_DTYPE = 0, -1, -2, -3
 DOBB_ERR_WORKSPACE, DOBB_ERR_HIP, DOBB_ERR_NOT_CONVERGED = -4, -5, -6
 DOBB_F32, DOBB_BF16 = 0, 1
-DOBB_REFRESH_EXACT, DOBB_REFRESH_ORTH_ITER = 0, 1
+DOBB_REFRESH_EXACT, DOBB_REFRESH_ORTH_ITER, DOBB_REFRESH_ORTH_ITER_CHOLQR = 0, 1, 2
 DOBB_NORM_SIGN, DOBB_NORM_IDENTITY, DOBB_NORM_COL_L2 = 0, 1, 2
 DOBB_OP_ACCUMULATE, DOBB_OP_REFRESH, DOBB_OP_STEP, DOBB_OP_STEP_G = 0, 1, 2, 3
 DOBB_WS_BF16_BASIS = 16

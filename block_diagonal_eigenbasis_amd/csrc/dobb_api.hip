@@ -298,14 +298,16 @@ dobb_status dobb_refresh_basis_grouped(int count, const dobb_shape *shapes, cons
                                        dobb_stream_t stream) {
     if (count < 1 || !shapes || !A || !Q) return DOBB_ERR_INVALID_ARG;
     if (q_dtype != DOBB_F32 && q_dtype != DOBB_BF16) return DOBB_ERR_DTYPE;
-    if (mode != DOBB_REFRESH_EXACT && mode != DOBB_REFRESH_ORTH_ITER) return DOBB_ERR_INVALID_ARG;
-    if (mode == DOBB_REFRESH_ORTH_ITER && iters < 1) return DOBB_ERR_INVALID_ARG;
+    if (mode != DOBB_REFRESH_EXACT && mode != DOBB_REFRESH_ORTH_ITER && mode != DOBB_REFRESH_ORTH_ITER_CHOLQR)
+        return DOBB_ERR_INVALID_ARG;
+    if (mode != DOBB_REFRESH_EXACT && iters < 1) return DOBB_ERR_INVALID_ARG;
     if (iters < 0 || iters > 1000) return DOBB_ERR_INVALID_ARG;
     if (!(tol >= 0.f) || tol >= 1.f) return DOBB_ERR_INVALID_ARG;
     for (int i = 0; i < count; ++i) {
         dobb_status st = check_shape(&shapes[i]);
         if (st != DOBB_OK) return st;
         if (!A[i] || !Q[i]) return DOBB_ERR_INVALID_ARG;
+        if (mode == DOBB_REFRESH_ORTH_ITER_CHOLQR && !chol_supported(shapes[i].nb)) return DOBB_ERR_SHAPE;
     }
     const bool qbf = q_dtype == DOBB_BF16;
     const int variant = qbf ? DOBB_WS_BF16_BASIS : 0;

@@ -236,6 +236,12 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s);
 // Householder QR of every block of a launch, nb <= 512.  Z: the blocks of the launch, dense nb x nb
 // each (overwritten); tq: npanel x 32 x 32 fp32 per block; negs: nb bytes per block.
 bool qr_block_supported(int64_t nb);
+// Cholesky QR (k_cholqr.hip): per block, R with R^T R = G overwrites G's upper part and X = R^{-1};
+// flag[g] records a non-positive pivot (first: set, else or-ed in)
+bool chol_supported(int64_t nb);
+hipError_t launch_chol_inv(int nb, int nblocks, float *G, float *X, int32_t *flag, int first, hipStream_t s);
+hipError_t launch_chol_info(int nblk, int nblocks, const int32_t *flag, int32_t *const *info, int cnt, int info_value,
+                            hipStream_t s);
 hipError_t launch_qr_block(int nb, int nblk, int cnt, float *Z, float *tq, int8_t *negs, float *const *Q,
                            int32_t *const *info, int info_value, hipStream_t s);
 

@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(256) k_qr_finish(int nb, int nblk, const int8_
     if (threadIdx.x == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
 }
 
-// lambda_j = q_j^T (A q_j), with T = A Q in the workspace.  grid.x = blocks.
+// lambda_j = q_j^T (A q_j), with T = A Q in the workspace; info = k when k >= 0.  grid.x = blocks.
 __global__ void __launch_bounds__(256) k_rayleigh(int nb, int nblk, const float *T_all, OutTable t, int k) {
     const int g = blockIdx.x;
     const int b = g % nblk, mat = g / nblk;
@@ -574,7 +574,7 @@ __global__ void __launch_bounds__(256) k_rayleigh(int nb, int nblk, const float 
         for (int p = 0; p < nb; ++p) s += (double)Q[(int64_t)p * nb + j] * (double)T[(int64_t)p * nb + j];
         if (t.lam[mat]) t.lam[mat][(int64_t)b * nb + j] = (float)s;
     }
-    if (threadIdx.x == 0 && t.info[mat]) t.info[mat][b] = k;
+    if (threadIdx.x == 0 && t.info[mat] && k >= 0) t.info[mat][b] = k;   // k < 0: info is written elsewhere
 }
 
 // ---- workspace layout: five regions, each an array of dense per-block records ----------------
@@ -720,6 +720,41 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
                 }
                 DOBB_LAUNCH("jacobi_finalize", s, k_jacobi_finalize, dim3((unsigned)nblocks), dim3(256), (size_t)nb * 8, nb,
                             nbp, nblk, (const double *)Aw64, (const double *)V, (const int32_t *)state, ot);
+            }
+        } else if (a.mode == DOBB_REFRESH_ORTH_ITER_CHOLQR) {
+            // Z = A Q in the first half of the T region, the first pass's result in its second half;
+            // the Gram matrix (then R) and R^{-1} in the working-matrix region; a flag per block
+            float *Q1 = Tm + t_stride * nblocks;
+            float *Gm = Aw, *Xm = Aw + t_stride * nblocks;
+            Opnd opZ{}, opQ1{}, opX{};
+            OutOpnd outG{}, outQ1{}, outQ{};
+            for (int i = 0; i < cnt; ++i) {
+                const int64_t o = (int64_t)i * nblk * t_stride;
+                opZ.p[i] = Tm + o; opQ1.p[i] = Q1 + o; opX.p[i] = Xm + o;
+                outG.p[i] = Gm + o; outQ1.p[i] = Q1 + o; outQ.p[i] = a.Q[c0 + i];
+            }
+            opZ.blk_stride = opQ1.blk_stride = opX.blk_stride = t_stride;
+            outG.blk_stride = outQ1.blk_stride = outQ.blk_stride = t_stride;
+            opZ.ld = opQ1.ld = opX.ld = outG.ld = outQ1.ld = outQ.ld = nb;
+            for (int it = 0; it < a.iters; ++it) {
+                DOBB_BGEMM(false, opA, opQ, outT);                                        // Z = A Q
+                DOBB_BGEMM(true, opZ, opZ, outG);                                         // Z^T Z
+                hipError_t e = launch_chol_inv(nb, (int)nblocks, Gm, Xm, state, it == 0, s);
+                if (e != hipSuccess) return e;
+                DOBB_BGEMM(false, opZ, opX, outQ1);                                       // Z R^{-1}
+                DOBB_BGEMM(true, opQ1, opQ1, outG);                                       // second pass
+                e = launch_chol_inv(nb, (int)nblocks, Gm, Xm, state, 0, s);
+                if (e != hipSuccess) return e;
+                DOBB_BGEMM(false, opQ1, opX, outQ);
+            }
+            hipError_t e = launch_chol_info(nblk, (int)nblocks, state, ot.info, cnt, a.iters, s);
+            if (e != hipSuccess) return e;
+            bool want_lam = false;
+            for (int i = 0; i < cnt; ++i) want_lam |= ot.lam[i] != nullptr;
+            if (want_lam) {
+                DOBB_BGEMM(false, opA, opQ, outT);
+                DOBB_LAUNCH("rayleigh", s, k_rayleigh, dim3((unsigned)nblocks), dim3(256), 0, nb, nblk, (const float *)Tm, ot,
+                            -1);
             }
         } else {
             // blocks up to 512 wide: k_qr.hip's kernels; wider ones: one launch per panel step

@@ -59,7 +59,8 @@ typedef enum { DOBB_F32 = 0, DOBB_BF16 = 1 } dobb_dtype;
 
 typedef enum {
     DOBB_REFRESH_EXACT = 0,      /* Table 15 "Exact eigendecomposition": cyclic Jacobi to tolerance */
-    DOBB_REFRESH_ORTH_ITER = 1   /* Table 15 "k=1 (principal)": k steps Q <- qr(A_b Q).Q, Householder */
+    DOBB_REFRESH_ORTH_ITER = 1,  /* Table 15 "k=1 (principal)": k steps Q <- qr(A_b Q).Q, Householder */
+    DOBB_REFRESH_ORTH_ITER_CHOLQR = 2  /* Table 16 "Cholesky": the same steps with Cholesky QR */
 } dobb_refresh_mode;
 
 typedef enum {
@@ -119,6 +120,11 @@ dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtyp
  *   ORTH_ITER: iters = k >= 1 steps of  Q_b <- qr(A_b Q_b).Q  (Householder, diag(R) > 0) from the
  *              Q passed in (which must hold a basis); lambda_b receives the Rayleigh quotients
  *              q_j^T A_b q_j.  warm_start and tol are ignored.
+ *   ORTH_ITER_CHOLQR: the same iteration with the QR by Cholesky (Table 16): two passes of
+ *              G = Z^T Z = R^T R, Z <- Z R^{-1} (fp32), the same factor with diag(R) > 0.  A block whose
+ *              Gram matrix is not numerically positive definite (Z rank deficient) gets info = -1 and
+ *              an unspecified basis.  nb is limited by the LDS (32 (nb + 1) + 3k floats per workgroup:
+ *              nb <= 1024 on MI355X); wider blocks return DOBB_ERR_SHAPE.
  * A: device fp32 B x nb x nb (symmetric; only read).  Q: device B x nb x nb, in/out, stored as
  * q_dtype: DOBB_F32, or DOBB_BF16 (Table 18's principal setting, fp32 moments with a bf16 basis: the
  * refresh reads the bf16 basis exactly, computes in fp32/fp64 as above and rounds the result to

@@ -101,6 +101,7 @@ def test_refresh_argument_errors():
     assert call(Q=None) == -1
     assert call(mode=4) == -1
     assert call(mode=1, iters=0) == -1      # orthogonal iteration needs k >= 1
+    assert call(mode=2, iters=0) == -1      # with either QR routine
     assert call(iters=-2) == -1
     assert call(tol=-1.0) == -1
     assert call(qdt=2) == -3                # basis dtype fp32 or bf16
