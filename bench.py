@@ -51,6 +51,7 @@ BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
 STEP_ROWS_MAX_NB = 128        # blocks up to this width keep Q resident in LDS in the step kernels (no split_q)
+STEP_FUSED_MAX_NB = 112       # ... and up to this width both orientations fit: the one-pass step kernel
 
 # Matrix sets.  per_layer: weights per layer; tokens: activations per capture; config: seed namespace;
 # cpu_rows / cpu_tokens: the oracle sample (1/cpu_rows of each weight's rows, cpu_tokens of the tokens).
@@ -136,6 +137,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       reconstruct_f16x2     W read + written: 2 w m n bytes of the method, plus the sign byte read
                             (implementation); 2 m n nb flops (fp32 contraction), issued as two fp16
                             products
+      step_fused_f16        nb <= 112, nb % 4 = 0: the one-pass step kernel: G read, M read + written,
+                            W read + written: (8 + g + 2 w) m n bytes, no sign bytes; 4 m n nb flops
+                            issued as five fp16 products
     Column-l2 normalisation (norm="col_l2") takes the plain fp32 kernels instead of the last four:
       momentum              G read, M read + written: (8 + g) m n bytes
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
@@ -191,6 +195,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                 add("project", 8.0 * mn, 2.0 * mn * nb)
                 add("colnorm", 4.0 * mn)
                 add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
+            continue
+        if nb <= STEP_FUSED_MAX_NB and nb % 4 == 0:
+            add("step_fused_f16", (8.0 + g_bytes + 2 * w_bytes) * mn, 4.0 * mn * nb, PEAK_FP32_MFMA,
+                5 * 2.0 * mn * nb)
             continue
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)
@@ -261,6 +269,7 @@ KERNEL_SYMBOLS = {
     "qr_form": (r"k_qr_form<", "k_qr.hip"),
     "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
     "project_f16x3": (r"k_proj_(rows|wide)<", ("k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
+    "step_fused_f16": (r"k_step_rows_fused<", ("k_step_rows.hip", "step_common.h")),
     "project_bf16x6": (r"k_proj_bf16<", ("k_step_bf16.hip", "step_common.h")),
     "reconstruct_f16x2": (r"k_recon_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
 }

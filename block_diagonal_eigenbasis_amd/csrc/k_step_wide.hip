@@ -151,7 +151,8 @@ __host__ __device__ inline size_t proj_wide_lds(int nb, int ldp) {
 
 // grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
 // NCT = ceil(nb / 32).  Wave w: 32-row tile rt = w % 4, column chunks cg + 2 j (cg = w / 4).
-template <int NCT, int NEST, bool GBF16>
+// CO: also write the coefficients to t.Cout (a verification output; off in the timed path)
+template <int NCT, int NEST, bool GBF16, bool CO = false>
 __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
                                                    int ldp, ProjWideTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -339,7 +340,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
         }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 8 qq + 4 (l / 32) + 0..3 -> LDS
         __syncthreads();   // every wave is done with the Q slices that the sign tile overlays
-        float *const Co = t.Cout[mat];
+        float *const Co = CO ? t.Cout[mat] : nullptr;
         const int64_t crow = tile * kTR + prow;
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
@@ -350,7 +351,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                 const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
                                     (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
                 if (ch < nct && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
-                if (Co && ch < nct && col < nb && crow < m)
+                if (CO && Co && ch < nct && col < nb && crow < m)
                     *(f32x4 *)(Co + crow * n + (int64_t)b * nb + col) =
                         f32x4{__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sreg), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sreg),
                               __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sreg), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sreg)};
@@ -611,14 +612,21 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
         const size_t sh = proj_wide_lds(nb, ldp);
         const bool gbf = a.g_dtype == DOBB_BF16;
         const bool nest = a.hp[c0].nesterov != 0;
-#define DOBB_PWIDE(NE, GB)                                                                                       \
+        bool co = false;
+        for (int i = 0; i < cnt; ++i) co = co || t.Cout[i] != nullptr;
+#define DOBB_PWIDE(NE, GB, CO)                                                                                   \
     do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_proj_wide<NCT, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("project_f16x3", s, (k_proj_wide<NCT, NE, GB>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups,  \
+        (void)hipFuncSetAttribute((const void *)k_proj_wide<NCT, NE, GB, CO>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_f16x3", s, (k_proj_wide<NCT, NE, GB, CO>), grid, dim3(kWT), sh, m, n, nb, nblk, ngroups,  \
                     (int)tpg, ldp, t);                                                                           \
     } while (0)
-        if (!nest) { if (gbf) DOBB_PWIDE(0, true); else DOBB_PWIDE(0, false); }
-        else { if (gbf) DOBB_PWIDE(1, true); else DOBB_PWIDE(1, false); }
+        if (co) {
+            if (!nest) { if (gbf) DOBB_PWIDE(0, true, true); else DOBB_PWIDE(0, false, true); }
+            else { if (gbf) DOBB_PWIDE(1, true, true); else DOBB_PWIDE(1, false, true); }
+        } else {
+            if (!nest) { if (gbf) DOBB_PWIDE(0, true, false); else DOBB_PWIDE(0, false, false); }
+            else { if (gbf) DOBB_PWIDE(1, true, false); else DOBB_PWIDE(1, false, false); }
+        }
 #undef DOBB_PWIDE
     }
     {

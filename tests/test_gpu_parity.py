@@ -569,3 +569,37 @@ def test_end_to_end_768_B4(seed):
     gaps = np.min(np.diff(-lam_ref, axis=1) / lam_ref[:, :1], axis=1)
     print(f"  differing U entries {frac:.2e}  min relative gap per block {gaps}", flush=True)
     assert frac <= 1e-3
+
+
+@pytest.mark.parametrize("m,n,nb,wdt,nest", [(300, 400, 100, torch.float32, False), (130, 96, 48, torch.float32, False),
+                                             (64, 256, 64, torch.bfloat16, False), (1000, 1600, 100, torch.float32, True),
+                                             (70, 60, 20, torch.float32, False), (257, 224, 112, torch.bfloat16, False)])
+def test_step_one_pass_kernel(m, n, nb, wdt, nest):
+    """Without a coefficient output, blocks whose split basis fits the LDS twice take the one-pass
+    step kernel (momentum, projection, signs, reconstruction and update per row tile).  It must meet
+    the step's bars against the oracle, and it computes the same products in the same order as the
+    two-kernel path, so W, M and U are bitwise those of a run with C_out."""
+    print(f"one-pass step m={m} n={n} nb={nb} {wdt} nesterov={nest}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=7 * m + nb, w_dtype=wdt, g_dtype=wdt, nesterov=nest)
+    W1, M1, U1 = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)                 # one pass
+    W2, M2, U2, _ = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN, want_c=True)  # two kernels
+    assert torch.equal(W1, W2) and torch.equal(M1, M2) and torch.equal(U1, U2)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"], nesterov=nest)
+    _check_momentum(M1, M, G, hp["momentum"], M_r)
+    P_r = (G.cpu().double().numpy() + hp["momentum"] * M_r) if nest else M_r
+    U_sh = host(U1)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = P_r[:, sl] @ Qh[b]
+        S_gpu = np.rint(U_sh[:, sl] @ Qh[b])
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref))
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the dead zone"
+        R = S_gpu @ Qh[b].T
+        assert np.linalg.norm(U_sh[:, sl] - R) <= 1e-5 * np.linalg.norm(R)
+    assert np.mean(np.abs(U_sh - U_r) > 1e-3) <= 1e-3
+    check_w(host(W1), host(W), U_sh, hp, bf16=wdt == torch.bfloat16)
+    # without U_out as well (the benchmark's launch)
+    W3, M3 = W.clone(), M.clone()
+    dobb.dobb_step(W3, G, M3, Q, nb, dobb.make_hparams(norm=dobb.DOBB_NORM_SIGN, **hp))
+    assert torch.equal(W3, W1) and torch.equal(M3, M1)
