@@ -51,7 +51,7 @@ BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
 STEP_ROWS_MAX_NB = 128        # blocks up to this width keep Q resident in LDS in the step kernels (no split_q)
-STEP_FUSED_MAX_NB = 112       # ... and up to this width both orientations fit: the one-pass step kernel
+STEP_FUSED_MAX_NB = 128       # ... and up to this width (nb % 4 == 0) the one-pass step kernel
 
 # Matrix sets.  per_layer: weights per layer; tokens: activations per capture; config: seed namespace;
 # cpu_rows / cpu_tokens: the oracle sample (1/cpu_rows of each weight's rows, cpu_tokens of the tokens).
@@ -137,9 +137,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       reconstruct_f16x2     W read + written: 2 w m n bytes of the method, plus the sign byte read
                             (implementation); 2 m n nb flops (fp32 contraction), issued as two fp16
                             products
-      step_fused_f16        nb <= 112, nb % 4 = 0: the one-pass step kernel: G read, M read + written,
+      step_fused_f16        nb <= 128, nb % 4 = 0: the one-pass step kernel: G read, M read + written,
                             W read + written: (8 + g + 2 w) m n bytes, no sign bytes; 4 m n nb flops
-                            issued as five fp16 products
+                            issued as five fp16 products over the padded block (16 ceil(nb / 16) basis
+                            rows, 32 ceil(nb / 32) deep)
     Column-l2 normalisation (norm="col_l2") takes the plain fp32 kernels instead of the last four:
       momentum              G read, M read + written: (8 + g) m n bytes
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
@@ -197,8 +198,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                 add("reconstruct", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb)
             continue
         if nb <= STEP_FUSED_MAX_NB and nb % 4 == 0:
+            rows, kp = 16 * -(-nb // 16), 32 * -(-nb // 32)   # basis rows and contraction depth, padded
             add("step_fused_f16", (8.0 + g_bytes + 2 * w_bytes) * mn, 4.0 * mn * nb, PEAK_FP32_MFMA,
-                5 * 2.0 * mn * nb)
+                5 * 2.0 * s.m * B * rows * kp)
             continue
         if nb > STEP_ROWS_MAX_NB:
             add("split_q", 14.0 * nb * nb * B)

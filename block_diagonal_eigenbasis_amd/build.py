@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdobb.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["dobb_api.hip", "k_basis.hip", "k_cholqr.hip", "k_step.hip", "k_step_g.hip", "k_step_bf16.hip", "k_accumulate.hip", "k_refresh.hip", "k_qr.hip", "k_step_rows.hip", "k_step_wide.hip"]
+SOURCES = ["dobb_api.hip", "k_basis.hip", "k_cholqr.hip", "k_step.hip", "k_step_g.hip", "k_step_bf16.hip", "k_step_fused.hip", "k_accumulate.hip", "k_refresh.hip", "k_qr.hip", "k_step_rows.hip", "k_step_wide.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

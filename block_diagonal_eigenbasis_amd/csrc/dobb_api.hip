@@ -438,7 +438,9 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
                 const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
                 pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
                 aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
-                          ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0;
+                          ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&
+                          ((uintptr_t)W[i] & (w_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&
+                          ((uintptr_t)us.back() & 15u) == 0 && ((uintptr_t)co.back() & 15u) == 0;
             }
             if (qbf) {
                 st = hip_status(launch_basis_convert(cnt, qsrc.data(), qdst.data(), sh.n * sh.nb, true, hs));

@@ -187,9 +187,11 @@ bool step_bf16_eligible(const dobb_shape &sh, int norm);
 size_t step_bf16_ws_one(const dobb_shape &sh);
 int step_bf16_ldp(int64_t nb);
 hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s);
-// nb <= 128: the same arithmetic with each block's basis resident in LDS and row tiles staged
-// through LDS (k_step_rows.hip)
-bool step_rows_eligible(const dobb_shape &sh);
+// nb <= 128 (nb % 4 == 0): the whole sign step in one pass, the block's basis resident in LDS and
+// every wave on its own 16-row tiles (k_step_fused.hip); 16-byte aligned M, G, W, U, C (8 bytes for
+// bf16 G and W)
+bool step_fused_eligible(const dobb_shape &sh);
+hipError_t launch_step_fused(const StepArgs &a, hipStream_t s);
 // column-l2 reconstruction for nb <= 128 (nb % 4 == 0) from C and the column scales, split fp16 products
 bool recon_l2_rows_eligible(const dobb_shape &sh);
 hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s);
@@ -200,7 +202,6 @@ hipError_t launch_proj_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s
 bool step_wide_eligible(const dobb_shape &sh);
 size_t step_wide_planes_bytes(const dobb_shape &sh);
 hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s);
-hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s);
 
 struct AccumulateArgs {
     int count;

@@ -527,7 +527,7 @@ size_t step_bf16_ws_one(const dobb_shape &sh) {
 hipError_t launch_step_bf16(const StepArgs &a, hipStream_t s) {
     const int nb = (int)a.sh.nb;
     const int ldp = step_bf16_ldp(nb);
-    if (step_rows_eligible(a.sh)) return launch_step_rows(a, ldp, s);
+    if (step_fused_eligible(a.sh)) return launch_step_fused(a, s);
     if (step_wide_eligible(a.sh)) return launch_step_wide(a, ldp, s);
     const int nct = (nb + 31) / 32;   // 32-column chunks of a block
     for (int c0 = 0; c0 < a.count;) {

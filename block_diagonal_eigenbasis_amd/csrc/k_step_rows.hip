@@ -1,26 +1,29 @@
-// The Dobb step (sign normalisation) for block widths nb <= 128: row tiles staged through LDS.
+// The Dobb-l2 step (column-l2 normalisation of the coefficients) for block widths nb <= 128,
+// nb % 4 == 0: row tiles staged through LDS.
 //
-// Dobb paper (arXiv 2610.39412): abstract (project momentum into the block bases, sign-normalise,
-// reconstruct), Table 9 (update scale), Table 21 caption (decoupled weight decay), Table 19
-// (Nesterov).
+// Dobb paper (arXiv 2610.39412): Tables 11-12 (Dobb-l2: every column of C_b scaled to unit l2 norm
+// over the rows), abstract (projection and reconstruction in the block bases), Table 9 (update
+// scale), Table 21 caption (decoupled weight decay), Table 19 (Nesterov).  The sign step of these
+// widths runs in one pass (k_step_fused.hip); the column norms need every row's coefficients before
+// any row can be reconstructed, so this step takes two passes with C in the workspace.
 //
 // C = P Q with both operands split into two fp16 parts (three products: hi*hi, hi*lo, lo*hi).  The
 // rows of P are first scaled by a power of two (exact) that puts each row's largest magnitude in
-// [2^13, 2^14), so the fp16 parts neither overflow nor lose the row's scale; the sign of C does not
-// depend on that scale.  U = S Q^T with Q split into two fp16 parts (S is exact in fp16).
-// Signs travel as the high byte of their fp16 value (+1 -> 0x3c, -1 -> 0xbc, 0 -> 0x00, NaN -> 0x7e).
+// [2^13, 2^14), so the fp16 parts neither overflow nor lose the row's scale; C is stored unscaled.
+// U = C~ Q^T with C~ = C diag(colscale), |C~| <= 1, split into two fp16 parts, and Q split into two
+// (three products).
 //
 // Layout of the work: a workgroup (8 waves) owns one block b; it splits Q_b into LDS once and then
 // streams tiles of TR rows.  Every global access walks along rows (consecutive lanes take
-// consecutive 16- or 8-byte pieces of a row's nb-wide slice): an access pattern where each lane
-// takes a different row, as the MFMA operand layout would, reaches well under half of the HBM
-// bandwidth.  The MFMA operands are read from LDS tiles:
+// consecutive 16- or 8-byte pieces of a row's nb-wide slice).  The MFMA operands are read from LDS
+// tiles:
 //   k_proj_rows   M, G rows -> M <- mu M + G (written back), P -> LDS (fp32);
-//                 waves take (32-row tile, column chunks): C^T = Q^T P^T; sign bytes -> LDS -> rows
-//   k_recon_rows  sign bytes rows -> LDS; U^T = Q S^T; U -> LDS -> rows, where
+//                 waves take (32-row tile, column chunks): C^T = Q^T P^T; C -> LDS -> rows, with
+//                 each tile's column sums of squares (fp64)
+//   k_colscale    the column scales 1 / ||C[:, j]|| from the tiles' sums
+//   k_recon_rows  C rows -> C~ in LDS; U^T = Q C~^T; U -> LDS -> rows, where
 //                 W <- W - lr (s U + wd W) is applied to the W rows loaded one tile ahead
-// The next tile's rows are loaded while the current tile's products run (in the reconstruction,
-// from before its products to the end of its W update).
+// The next tile's rows are loaded while the current tile's products run.
 #include "step_common.h"
 
 #include <type_traits>
@@ -54,32 +57,30 @@ struct ProjRowsTable {
     float *M[kMaxMats];
     const void *G[kMaxMats];
     const float *Q[kMaxMats];
-    uint8_t *S[kMaxMats];
-    float *C[kMaxMats];        // column-l2: the coefficients (m x n fp32)
-    double *part[kMaxMats];    // column-l2: per row tile, the column sums of squares ([tiles][n])
+    float *C[kMaxMats];        // the coefficients (m x n fp32)
+    double *part[kMaxMats];    // per row tile, the column sums of squares ([tiles][n])
     float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
     float mu[kMaxMats];
 };
-// LDS: Q_b^T (two fp16 planes), the P tile (fp32) and the sign tile
-__host__ __device__ inline size_t proj_rows_lds(int nb, int TR, int ldp) {
+// LDS: Q_b^T (two fp16 planes) and the P tile (fp32), which later holds the C tile
+__host__ __device__ inline size_t proj_rows_lds(int nb, int TR) {
     const RowsGeo g = rows_geo(nb);
-    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * ldp);
+    return a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4);
 }
 
 // grid.x = tile groups x blocks x matrices (block fastest, renumbered per XCD), block 512.
 // TR = 128 or 64 rows per tile; the 8 waves take (32-row tile rt, group cg of column chunks).
-// L2: column-l2 normalisation (Dobb-l2): the epilogue writes C (unscaled by the row's power of two)
-// along the rows through the P tile's LDS, and each tile's column sums of squares in fp64.
-// CO: also write the coefficients to t.Cout (a verification output; off in the timed path)
-template <int NCH, int TR, int NEST, bool GBF16, bool L2 = false, bool CO = false>
+// The epilogue writes C (unscaled by the row's power of two) along the rows through the P tile's
+// LDS, also to t.Cout when given (a verification output), and each tile's column sums of squares
+// in fp64.
+template <int NCH, int TR, int NEST, bool GBF16>
 __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
-                                                   int ldp, ProjRowsTable t) {
+                                                   ProjRowsTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
     const RowsGeo geo = rows_geo(nb);
     const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, pld = geo.pld;
     uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
     float *ps = (float *)(lds + a16((size_t)2 * nb * qld * 2));              // [TR][pld]
-    uint8_t *ss = lds + a16((size_t)2 * nb * qld * 2) + a16((size_t)TR * pld * 4);   // [TR][ldp]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -152,8 +153,6 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
     constexpr int kCPG = (NCH + kGroups - 1) / kGroups;
     const int rt = wv % kRTiles, cg = wv / kRTiles;
     const int kh = 8 * (lane >> 5);
-    uint8_t *S = t.S[mat] + (int64_t)b * ldp;
-    const int64_t sld = (int64_t)nblk * ldp;
 
     load_tile(t_begin);
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
@@ -233,7 +232,7 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], al, acc[j], 0, 0, 0);
         }
-        if constexpr (L2) {
+        {
             // C tile -> the P tile's LDS (every wave is past its products), then rows out and the
             // tile's column sums of squares (rows past m are zero)
             __syncthreads();
@@ -273,81 +272,43 @@ __global__ void __launch_bounds__(512) k_proj_rows(int64_t m, int64_t n, int nb,
                 t.part[mat][tile * n + (int64_t)b * nb + tid] = sq;
             }
             __syncthreads();   // the next tile's staging overwrites the P tile
-            continue;
-        }
-        // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t -> LDS
-        float *const Co = CO ? t.Cout[mat] : nullptr;
-        const int64_t crow = tile * TR + 32 * rt + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < kCPG; ++j) {
-            const int ch = cg * kCPG + j;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;   // nb % 4 == 0: all 4 valid or none
-                const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
-                                    (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
-                if (ch < NCH && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * ldp + col) = w4;
-                if (CO && Co && ch < NCH && col < nb && crow < m)
-                    *(f32x4 *)(Co + crow * n + (int64_t)b * nb + col) =
-                        f32x4{__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sexp), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sexp),
-                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sexp), __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sexp)};
-            }
-        }
-        __syncthreads();
-        // sign rows out in 8-byte pieces (bytes [nb, ldp) of a row are padding, never read as signs)
-        {
-            const int q8 = ldp / 8;
-            for (int e = tid; e < TR * q8; e += kRT) {
-                const int r = e / q8, c = 8 * (e - r * q8);
-                const int64_t row = tile * TR + r;
-                if (row < m) *(uint2 *)(S + row * sld + c) = *(const uint2 *)(ss + r * ldp + c);
-            }
         }
     }
 }
 
 // ---- reconstruction ------------------------------------------------------------------------------
 struct ReconRowsTable {
-    const uint8_t *S[kMaxMats];
-    const float *C[kMaxMats];    // column-l2: the coefficients C (m x n fp32) and the column scales
+    const float *C[kMaxMats];    // the coefficients C (m x n fp32) and the column scales
     const float *cs[kMaxMats];
     const float *Q[kMaxMats];
     void *W[kMaxMats];
     float *U[kMaxMats];
     float lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
 };
-// sign tile pitch: the k extent kpad plus 8 bytes (an odd number of 8-byte units: rows on distinct
-// banks).  The tile holds every k the products read, zero past nb (zero times the basis' zero
-// padding: a stale byte there could decode to an infinite fp16 value and give NaN).
-__host__ __device__ inline int rows_spitch(int nb) { return rows_geo(nb).kpad + 8; }
-// column-l2: the tile of scaled coefficients, fp32 with pitch kpad + 4 ((pitch / 4) odd), then the
-// block's kpad column scales (zero past nb)
+// the tile of scaled coefficients, fp32 with pitch kpad + 4 ((pitch / 4) odd), then the block's
+// kpad column scales (zero past nb)
 __host__ __device__ inline int rows_cpitch(int nb) { return rows_geo(nb).kpad + 4; }
-__host__ __device__ inline size_t recon_rows_tile(int nb, int TR, bool l2) {
-    return l2 ? a16((size_t)TR * rows_cpitch(nb) * 4 + (size_t)rows_geo(nb).kpad * 4) : a16((size_t)TR * rows_spitch(nb));
+__host__ __device__ inline size_t recon_rows_tile(int nb, int TR) {
+    return a16((size_t)TR * rows_cpitch(nb) * 4 + (size_t)rows_geo(nb).kpad * 4);
 }
-__host__ __device__ inline size_t recon_rows_lds(int nb, int TR, int ldp, bool l2 = false) {
+__host__ __device__ inline size_t recon_rows_lds(int nb, int TR) {
     const RowsGeo g = rows_geo(nb);
-    (void)ldp;
-    return a16((size_t)2 * nb * g.qld * 2) + recon_rows_tile(nb, TR, l2) + a16((size_t)TR * g.uld * 4);
+    return a16((size_t)2 * nb * g.qld * 2) + recon_rows_tile(nb, TR) + a16((size_t)TR * g.uld * 4);
 }
 
-// L2: column-l2 normalisation (Dobb-l2): the tile holds C~ = C diag(colscale) in fp32 instead of the
-// sign bytes; |C~| <= 1, so it splits into two fp16 parts without a scale and U = C~ Q^T takes three
-// products (hi hi, lo(Q) hi, hi lo(C~)).
-template <int NCH, int TR, bool WBF16, bool L2 = false>
+// The tile holds C~ = C diag(colscale) in fp32; |C~| <= 1, so it splits into two fp16 parts without
+// a scale and U = C~ Q^T takes three products (hi hi, lo(Q) hi, hi lo(C~)).
+template <int NCH, int TR, bool WBF16>
 __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
-                                                    int ldp, ReconRowsTable t) {
+                                                    ReconRowsTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
     const RowsGeo geo = rows_geo(nb);
     const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, uld = geo.uld;
     uint16_t *qs = (uint16_t *)lds;                                          // [2][nb][qld]
-    const int spitch = rows_spitch(nb);
-    uint8_t *ssb = lds + a16((size_t)2 * nb * qld * 2);                      // [TR][spitch]
     const int cpitch = rows_cpitch(nb);
-    float *ct = (float *)ssb;                                                // L2: [TR][cpitch]
-    float *csl = ct + TR * cpitch;                                           // L2: [kpad]
-    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + recon_rows_tile(nb, TR, L2));   // [TR][uld]
+    float *ct = (float *)(lds + a16((size_t)2 * nb * qld * 2));              // [TR][cpitch]
+    float *csl = ct + TR * cpitch;                                           // [kpad]
+    float *us = (float *)(lds + a16((size_t)2 * nb * qld * 2) + recon_rows_tile(nb, TR));   // [TR][uld]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int b = x % nblk, rest = x / nblk;
@@ -383,54 +344,32 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
         }
     }
 
-    if constexpr (L2) {
-        // the block's column scales, and zero tile columns [nb, kpad) (the staging writes c < nb only)
-        for (int c = tid; c < kpad; c += kRT) csl[c] = c < nb ? t.cs[mat][(int64_t)b * nb + c] : 0.f;
-        for (int e = tid; e < TR * (kpad - nb); e += kRT) {
-            const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
-            ct[r * cpitch + c] = 0.f;
-        }
-        __syncthreads();
+    // the block's column scales, and zero tile columns [nb, kpad) (the staging writes c < nb only)
+    for (int c = tid; c < kpad; c += kRT) csl[c] = c < nb ? t.cs[mat][(int64_t)b * nb + c] : 0.f;
+    for (int e = tid; e < TR * (kpad - nb); e += kRT) {
+        const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
+        ct[r * cpitch + c] = 0.f;
     }
-    const uint8_t *S = t.S[mat] + (int64_t)b * ldp;
-    const float *Cm = L2 ? t.C[mat] : nullptr;
-    const int64_t sld = (int64_t)nblk * ldp;
+    __syncthreads();
+    const float *Cm = t.C[mat];
     const float lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
     void *const Wv = t.W[mat];
     float *const U = t.U[mat];
-    // sign rows: 8-byte pieces, kpad / 8 per row; W rows: 4-element pieces, nb / 4 per row
-    const int q8 = kpad / 8, q = nb / 4;
-    constexpr int kSPT = (TR * 16 + kRT - 1) / kRT;   // sign pieces per thread (kpad <= 128)
-    constexpr int kWPT = (TR * 32 + kRT - 1) / kRT;   // W pieces per thread (nb <= 128)
+    // C and W rows: 4-element pieces, nb / 4 per row
+    const int q = nb / 4;
+    constexpr int kWPT = (TR * 32 + kRT - 1) / kRT;   // pieces per thread (nb <= 128)
     using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
-    uint2 sr[L2 ? 1 : kSPT];
-    f32x4 cr[L2 ? kWPT : 1];
+    f32x4 cr[kWPT];
     WVec wr[kWPT];
     auto load_tile = [&](int64_t tile) {
-        if constexpr (L2) {
 #pragma unroll
-            for (int i = 0; i < kWPT; ++i) {
-                const int e = tid + kRT * i;
-                const int r = e / q, c = 4 * (e - r * q);
-                const int64_t row = tile * TR + r;
-                cr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (tile < t_end && e < TR * q && row < m)
-                    cr[i] = *(const f32x4 *)(Cm + row * n + (int64_t)b * nb + c);
-            }
-        } else {
-#pragma unroll
-        for (int i = 0; i < kSPT; ++i) {
+        for (int i = 0; i < kWPT; ++i) {
             const int e = tid + kRT * i;
-            const int r = e / q8, c = 8 * (e - r * q8);
+            const int r = e / q, c = 4 * (e - r * q);
             const int64_t row = tile * TR + r;
-            sr[i] = uint2{0u, 0u};
-            // c < nb <= ldp, multiples of 8 (c, ldp) and 4 (nb): the piece lies inside the row;
-            // bytes at or past nb are zero
-            if (tile < t_end && e < TR * q8 && row < m && c < nb) {
-                sr[i] = *(const uint2 *)(S + row * sld + c);
-                if (c + 4 >= nb) sr[i].y = 0u;
-            }
-        }
+            cr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tile < t_end && e < TR * q && row < m)
+                cr[i] = *(const f32x4 *)(Cm + row * n + (int64_t)b * nb + c);
         }
 #pragma unroll
         for (int i = 0; i < kWPT; ++i) {
@@ -450,38 +389,28 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
 
     load_tile(t_begin);
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        uint8_t *sc_ = ssb;
-        if constexpr (L2) {
 #pragma unroll
-            for (int i = 0; i < kWPT; ++i) {
-                const int e = tid + kRT * i;
-                const int r = e / q, c = 4 * (e - r * q);
-                if (e < TR * q) {
-                    const f32x4 sv = *(const f32x4 *)(csl + c);
-                    *(f32x4 *)(ct + r * cpitch + c) =
-                        f32x4{cr[i][0] * sv[0], cr[i][1] * sv[1], cr[i][2] * sv[2], cr[i][3] * sv[3]};
-                }
-            }
-        } else {
-#pragma unroll
-        for (int i = 0; i < kSPT; ++i) {
+        for (int i = 0; i < kWPT; ++i) {
             const int e = tid + kRT * i;
-            const int r = e / q8, c = 8 * (e - r * q8);
-            if (e < TR * q8) *(uint2 *)(sc_ + r * spitch + c) = sr[i];
-        }
+            const int r = e / q, c = 4 * (e - r * q);
+            if (e < TR * q) {
+                const f32x4 sv = *(const f32x4 *)(csl + c);
+                *(f32x4 *)(ct + r * cpitch + c) =
+                    f32x4{cr[i][0] * sv[0], cr[i][1] * sv[1], cr[i][2] * sv[2], cr[i][3] * sv[3]};
+            }
         }
         WVec wcur[kWPT];
 #pragma unroll
         for (int i = 0; i < kWPT; ++i) wcur[i] = wr[i];
         load_tile(tile + 1);
         __syncthreads();
-        // U^T = Q S^T for 32-row tile rt and this wave's column chunks
+        // U^T = Q C~^T for 32-row tile rt and this wave's column chunks
         f32x16 acc[kCPG];
 #pragma unroll
         for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
         for (int ks = 0; ks < KS; ++ks) {
             f16x8 as, al;
-            if constexpr (L2) {
+            {
                 const float *cp = ct + (32 * rt + (lane & 31)) * cpitch + ks * kKS + kh;
                 const f32x4 c0 = *(const f32x4 *)cp, c1 = *(const f32x4 *)(cp + 4);
                 uint16_t hh[8], hl[8];
@@ -492,10 +421,6 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
                 }
                 as = __builtin_bit_cast(f16x8, uint4{pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])});
                 al = __builtin_bit_cast(f16x8, uint4{pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])});
-            } else {
-                const uint2 sv = *(const uint2 *)(sc_ + (32 * rt + (lane & 31)) * spitch + ks * kKS + kh);
-                const uint4 av = {signs_f16x2<0>(sv.x), signs_f16x2<1>(sv.x), signs_f16x2<0>(sv.y), signs_f16x2<1>(sv.y)};
-                as = __builtin_bit_cast(f16x8, av);
             }
             f16x8 Bh[kCPG], Bl[kCPG];
 #pragma unroll
@@ -514,10 +439,8 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], as, acc[j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bl[j], as, acc[j], 0, 0, 0);
-            if constexpr (L2) {
 #pragma unroll
-                for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], al, acc[j], 0, 0, 0);
-            }
+            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], al, acc[j], 0, 0, 0);
         }
         // U tile -> LDS: lane holds row 32 rt + l % 32, columns 32 ch + 4 (l / 32) + 8 qq + t
 #pragma unroll
@@ -565,390 +488,6 @@ __global__ void __launch_bounds__(512) k_recon_rows(int64_t m, int64_t n, int nb
     }
 }
 
-// ---- the whole step in one pass --------------------------------------------------------------------
-// k_step_rows_fused: momentum, projection, signs, reconstruction and the weight update of a row tile
-// in one kernel.  Both orientations of the split basis stay in LDS (Q^T for C^T = Q^T P^T, Q for
-// U^T = Q S^T), the signs go from the projection's accumulators to an LDS tile that the
-// reconstruction reads, U goes through the P tile's LDS (same pitch, so the P tile's zero columns
-// past nb survive) to row-wise W updates.  The next tile's M, G and W rows are loaded while the
-// current tile's products run.  HBM traffic is the method's: G and W read, M read and written, W
-// written (no sign bytes).
-struct FusedRowsTable {
-    float *M[kMaxMats];
-    const void *G[kMaxMats];
-    const float *Q[kMaxMats];
-    void *W[kMaxMats];
-    float *U[kMaxMats];
-    float mu[kMaxMats], lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
-};
-__host__ __device__ inline size_t fused_rows_lds(int nb, int TR) {
-    const RowsGeo g = rows_geo(nb);
-    return 2 * a16((size_t)2 * nb * g.qld * 2) + a16((size_t)TR * g.pld * 4) + a16((size_t)TR * rows_spitch(nb));
-}
-
-template <int NCH, int TR, int NEST, bool GBF16, bool WBF16>
-__global__ void __launch_bounds__(512) k_step_rows_fused(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
-                                                         FusedRowsTable t) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    const RowsGeo geo = rows_geo(nb);
-    const int KS = geo.KS, kpad = geo.kpad, qld = geo.qld, pld = geo.pld;
-    const int spitch = rows_spitch(nb);
-    const size_t qbytes = a16((size_t)2 * nb * qld * 2);
-    uint16_t *qt = (uint16_t *)lds;                                // [2][nb][qld]: Q^T, element (j, p)
-    uint16_t *qn = (uint16_t *)(lds + qbytes);                     // [2][nb][qld]: Q, element (p, c)
-    float *ps = (float *)(lds + 2 * qbytes);                       // [TR][pld]: P, then U
-    uint8_t *ss = lds + 2 * qbytes + a16((size_t)TR * pld * 4);    // [TR][spitch]: sign bytes
-
-    const int x = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = x % nblk, rest = x / nblk;
-    const int tg = rest % ngroups, mat = rest / ngroups;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t ntile = (m + TR - 1) / TR;
-    const int64_t t_begin = (int64_t)tg * tpg;
-    const int64_t t_end = t_begin + tpg < ntile ? t_begin + tpg : ntile;
-
-    // both split planes of Q_b from one read of it; zero past nb in k (Q^T) and in c (Q)
-    {
-        const float *Q = t.Q[mat] + (int64_t)b * nb * nb;
-        const int total = kpad * nb;
-        for (int e0 = 0; e0 < total; e0 += kRT * 8) {
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = e0 + tid + kRT * i;
-                v[i] = (e < total && e < nb * nb) ? Q[e] : 0.f;   // e = p * nb + j
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = e0 + tid + kRT * i;
-                if (e < total) {
-                    const int p = e / nb, j = e - p * nb;
-                    uint16_t h, l;
-                    split2h(v[i], h, l);
-                    qt[(0 * nb + j) * qld + p] = h;
-                    qt[(1 * nb + j) * qld + p] = l;
-                    if (p < nb) {
-                        qn[(0 * nb + p) * qld + j] = h;
-                        qn[(1 * nb + p) * qld + j] = l;
-                    }
-                }
-            }
-        }
-        for (int e = tid; e < nb * (kpad - nb); e += kRT) {
-            const int p = e / (kpad - nb), c = nb + e % (kpad - nb);
-            qn[(0 * nb + p) * qld + c] = 0;
-            qn[(1 * nb + p) * qld + c] = 0;
-        }
-        // the P tile's columns [nb, kpad) and the sign tile's bytes [nb, kpad) stay zero
-        for (int e = tid; e < TR * (kpad - nb); e += kRT) {
-            const int r = e / (kpad - nb), c = nb + e % (kpad - nb);
-            ps[r * pld + c] = 0.f;
-            ss[r * spitch + c] = 0;
-        }
-    }
-
-    const int q = nb / 4;
-    constexpr int kIPT = (TR * 32 + kRT - 1) / kRT;   // row pieces per thread for q <= 32
-    float *M = t.M[mat] + (int64_t)b * nb;
-    const void *Gv = t.G[mat];
-    void *const Wv = t.W[mat];
-    float *const U = t.U[mat];
-    const float mu = t.mu[mat], lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
-    using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
-    f32x4 mr[kIPT], gr[kIPT];
-    WVec wr[kIPT];
-    auto load_tile = [&](int64_t tile) {
-#pragma unroll
-        for (int i = 0; i < kIPT; ++i) {
-            const int e = tid + kRT * i;
-            const int r = e / q, c = 4 * (e - r * q);
-            const int64_t row = tile * TR + r;
-            mr[i] = gr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tile < t_end && e < TR * q && row < m) {
-                const int64_t off = row * n + c;
-                mr[i] = *(const f32x4 *)(M + off);
-                if (GBF16) {
-                    const uint2 hb = *(const uint2 *)((const uint16_t *)Gv + (int64_t)b * nb + off);
-                    gr[i] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
-                                  bf16_to_f32((uint16_t)hb.y), bf16_to_f32((uint16_t)(hb.y >> 16))};
-                } else {
-                    gr[i] = *(const f32x4 *)((const float *)Gv + (int64_t)b * nb + off);
-                }
-                wr[i] = *(const WVec *)((const char *)Wv + ((off + (int64_t)b * nb) * (WBF16 ? 2 : 4)));
-            }
-        }
-    };
-
-    constexpr int kRTiles = TR / 32;
-    constexpr int kGroups = 8 / kRTiles;
-    constexpr int kCPG = (NCH + kGroups - 1) / kGroups;
-    const int rt = wv % kRTiles, cg = wv / kRTiles;
-    const int kh = 8 * (lane >> 5);
-
-    load_tile(t_begin);
-    for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        // momentum (written back along the rows) and P into the LDS tile; this tile's W rows move to
-        // wcur, then the next tile's rows start loading
-        WVec wcur[kIPT];
-#pragma unroll
-        for (int i = 0; i < kIPT; ++i) {
-            const int e = tid + kRT * i;
-            const int r = e / q, c = 4 * (e - r * q);
-            const int64_t row = tile * TR + r;
-            f32x4 mn, pv;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
-                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
-            }
-            if (e < TR * q) {
-                if (row < m) *(f32x4 *)(M + row * n + c) = mn;
-                *(f32x4 *)(ps + r * pld + c) = pv;   // rows past m hold zeros (their loads read zero)
-            }
-            wcur[i] = wr[i];
-        }
-        load_tile(tile + 1);
-        __syncthreads();
-        // the scale of this lane's row (its half, then the other half from lane ^ 32)
-        int sexp;
-        {
-            const float *pr = ps + (32 * rt + (lane & 31)) * pld + kh;
-            uint32_t mx = 0u;
-            for (int ks = 0; ks < KS; ++ks) {
-                const f32x4 p0 = *(const f32x4 *)(pr + ks * kKS), p1 = *(const f32x4 *)(pr + ks * kKS + 4);
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const uint32_t u0 = __float_as_uint(p0[cc]) & 0x7fffffffu;
-                    const uint32_t u1 = __float_as_uint(p1[cc]) & 0x7fffffffu;
-                    mx = u0 > mx ? u0 : mx;
-                    mx = u1 > mx ? u1 : mx;
-                }
-            }
-            const uint32_t o = (uint32_t)__shfl_xor((int)mx, 32);
-            sexp = row_scale_exp(o > mx ? o : mx);
-        }
-        // C^T = Q^T P^T for 32-row tile rt and this wave's column chunks
-        f32x16 acc[kCPG];
-#pragma unroll
-        for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
-        for (int ks = 0; ks < KS; ++ks) {
-            const float *pr = ps + (32 * rt + (lane & 31)) * pld + ks * kKS + kh;
-            const f32x4 p0 = *(const f32x4 *)pr, p1 = *(const f32x4 *)(pr + 4);
-            uint16_t hh[8], hl[8];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                split2s(__builtin_amdgcn_ldexpf(p0[cc], sexp), hh[cc], hl[cc]);
-                split2s(__builtin_amdgcn_ldexpf(p1[cc], sexp), hh[cc + 4], hl[cc + 4]);
-            }
-            const f16x8 ah = __builtin_bit_cast(f16x8, uint4{pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])});
-            const f16x8 al = __builtin_bit_cast(f16x8, uint4{pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])});
-            f16x8 Qh[kCPG], Ql[kCPG];
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) {
-                const int ch = cg * kCPG + j;
-                const int col = 32 * ch + (lane & 31);
-                const bool ok = ch < NCH && col < nb;
-                const int cs = ok ? col : 0;
-                uint4 bh = *(const uint4 *)&qt[(0 * nb + cs) * qld + ks * kKS + kh];
-                uint4 bl = *(const uint4 *)&qt[(1 * nb + cs) * qld + ks * kKS + kh];
-                if (!ok) bh = bl = uint4{0u, 0u, 0u, 0u};
-                Qh[j] = __builtin_bit_cast(f16x8, bh);
-                Ql[j] = __builtin_bit_cast(f16x8, bl);
-            }
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], ah, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql[j], ah, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh[j], al, acc[j], 0, 0, 0);
-        }
-        // sign bytes into the reconstruction's tile: lane holds row 32 rt + l % 32, columns
-        // 32 ch + 4 (l / 32) + 8 qq + t
-#pragma unroll
-        for (int j = 0; j < kCPG; ++j) {
-            const int ch = cg * kCPG + j;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;   // nb % 4 == 0: all 4 valid or none
-                const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
-                                    (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
-                if (ch < NCH && col < nb) *(uint32_t *)(ss + (32 * rt + (lane & 31)) * spitch + col) = w4;
-            }
-        }
-        __syncthreads();   // the signs are in LDS; every wave is done with the P tile
-        // U^T = Q S^T for 32-row tile rt and this wave's column chunks
-#pragma unroll
-        for (int j = 0; j < kCPG; ++j) acc[j] = (f32x16){};
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint2 sv = *(const uint2 *)(ss + (32 * rt + (lane & 31)) * spitch + ks * kKS + kh);
-            const f16x8 as = signs_f16x8(sv);
-            f16x8 Bh[kCPG], Bl[kCPG];
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) {
-                const int ch = cg * kCPG + j;
-                const int p = 32 * ch + (lane & 31);
-                const bool ok = ch < NCH && p < nb;
-                const int pp = ok ? p : 0;
-                uint4 bh = *(const uint4 *)&qn[(0 * nb + pp) * qld + ks * kKS + kh];
-                uint4 bl = *(const uint4 *)&qn[(1 * nb + pp) * qld + ks * kKS + kh];
-                if (!ok) bh = bl = uint4{0u, 0u, 0u, 0u};
-                Bh[j] = __builtin_bit_cast(f16x8, bh);
-                Bl[j] = __builtin_bit_cast(f16x8, bl);
-            }
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bh[j], as, acc[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < kCPG; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Bl[j], as, acc[j], 0, 0, 0);
-        }
-        // U tile -> the P tile's LDS (pitch pld; columns < nb only)
-#pragma unroll
-        for (int j = 0; j < kCPG; ++j) {
-            const int ch = cg * kCPG + j;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int col = 32 * ch + 4 * (lane >> 5) + 8 * qq;
-                if (ch < NCH && col < nb)
-                    *(f32x4 *)(ps + (32 * rt + (lane & 31)) * pld + col) =
-                        f32x4{acc[j][4 * qq], acc[j][4 * qq + 1], acc[j][4 * qq + 2], acc[j][4 * qq + 3]};
-            }
-        }
-        __syncthreads();
-        // W <- W - lr (s U + wd W) along the rows
-#pragma unroll
-        for (int i = 0; i < kIPT; ++i) {
-            const int e = tid + kRT * i;
-            const int r = e / q, c = 4 * (e - r * q);
-            const int64_t row = tile * TR + r;
-            if (e < TR * q && row < m) {
-                const f32x4 u = *(const f32x4 *)(ps + r * pld + c);
-                const int64_t off = row * n + (int64_t)b * nb + c;
-                float w0[4];
-                if constexpr (WBF16) {
-                    const uint2 hb = wcur[i];
-                    w0[0] = bf16_to_f32((uint16_t)hb.x); w0[1] = bf16_to_f32((uint16_t)(hb.x >> 16));
-                    w0[2] = bf16_to_f32((uint16_t)hb.y); w0[3] = bf16_to_f32((uint16_t)(hb.y >> 16));
-                } else {
-                    w0[0] = wcur[i][0]; w0[1] = wcur[i][1]; w0[2] = wcur[i][2]; w0[3] = wcur[i][3];
-                }
-                float nw[4];
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) nw[cc] = w0[cc] - lr * __builtin_fmaf(sc, u[cc], wd * w0[cc]);
-                if (U) *(f32x4 *)(U + off) = u;
-                if constexpr (WBF16) {
-                    *(uint2 *)((uint16_t *)Wv + off) =
-                        uint2{(uint32_t)f32_to_bf16(nw[0]) | ((uint32_t)f32_to_bf16(nw[1]) << 16),
-                              (uint32_t)f32_to_bf16(nw[2]) | ((uint32_t)f32_to_bf16(nw[3]) << 16)};
-                } else {
-                    *(f32x4 *)((float *)Wv + off) = f32x4{nw[0], nw[1], nw[2], nw[3]};
-                }
-            }
-        }
-        __syncthreads();   // every thread is done with U before the next tile's P staging
-    }
-}
-
-template <int NCH, int TR>
-hipError_t launch_fused_tr(const StepArgs &a, int c0, int cnt, hipStream_t s) {
-    const int64_t m = a.sh.m, n = a.sh.n;
-    const int nb = (int)a.sh.nb;
-    const int nblk = (int)(n / nb);
-    const int64_t ntile = (m + TR - 1) / TR;
-    const int64_t blocks = (int64_t)nblk * cnt;
-    int64_t tpg = (ntile * blocks + 1023) / 1024;
-    if (tpg < 4) tpg = 4;
-    if (tpg > ntile) tpg = ntile;
-    const int ngroups = (int)((ntile + tpg - 1) / tpg);
-    const dim3 grid((unsigned)(ngroups * blocks));
-    FusedRowsTable t{};
-    for (int i = 0; i < cnt; ++i) {
-        const dobb_hparams &h = a.hp[c0 + i];
-        t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i]; t.W[i] = a.W[c0 + i];
-        t.U[i] = a.U ? a.U[c0 + i] : nullptr;
-        t.mu[i] = h.momentum; t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
-    }
-    const size_t sh = fused_rows_lds(nb, TR);
-    const bool gbf = a.g_dtype == DOBB_BF16, wbf = a.w_dtype == DOBB_BF16;
-    const bool nest = a.hp[c0].nesterov != 0;
-#define DOBB_FUSED(NE, GB, WB)                                                                                   \
-    do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_step_rows_fused<NCH, TR, NE, GB, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("step_fused_f16", s, (k_step_rows_fused<NCH, TR, NE, GB, WB>), grid, dim3(kRT), sh, m, n, nb, nblk, \
-                    ngroups, (int)tpg, t);                                                                       \
-    } while (0)
-    if (!nest) {
-        if (gbf) { if (wbf) DOBB_FUSED(0, true, true); else DOBB_FUSED(0, true, false); }
-        else { if (wbf) DOBB_FUSED(0, false, true); else DOBB_FUSED(0, false, false); }
-    } else {
-        if (gbf) { if (wbf) DOBB_FUSED(1, true, true); else DOBB_FUSED(1, true, false); }
-        else { if (wbf) DOBB_FUSED(1, false, true); else DOBB_FUSED(1, false, false); }
-    }
-#undef DOBB_FUSED
-    return hipGetLastError();
-}
-
-template <int NCH, int TR>
-hipError_t launch_rows_tr(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
-    const int64_t m = a.sh.m, n = a.sh.n;
-    const int nb = (int)a.sh.nb;
-    const int nblk = (int)(n / nb);
-    const int64_t ntile = (m + TR - 1) / TR;
-    const int64_t blocks = (int64_t)nblk * cnt;
-    // about four workgroups per CU over the launch, at least 4 tiles each
-    int64_t tpg = (ntile * blocks + 1023) / 1024;
-    if (tpg < 4) tpg = 4;
-    if (tpg > ntile) tpg = ntile;
-    const int ngroups = (int)((ntile + tpg - 1) / tpg);
-    const dim3 grid((unsigned)(ngroups * blocks));
-    {
-        ProjRowsTable t{};
-        for (int i = 0; i < cnt; ++i) {
-            t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.Q[i] = a.Q[c0 + i];
-            t.S[i] = (uint8_t *)a.S[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
-            t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
-        }
-        const size_t sh = proj_rows_lds(nb, TR, ldp);
-        const bool gbf = a.g_dtype == DOBB_BF16;
-        const bool nest = a.hp[c0].nesterov != 0;
-        bool co = false;
-        for (int i = 0; i < cnt; ++i) co = co || t.Cout[i] != nullptr;
-#define DOBB_PROWS(NE, GB, CO)                                                                                   \
-    do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB, false, CO>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("project_f16x3", s, (k_proj_rows<NCH, TR, NE, GB, false, CO>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups,  \
-                    (int)tpg, ldp, t);                                                                           \
-    } while (0)
-        if (co) {
-            if (!nest) { if (gbf) DOBB_PROWS(0, true, true); else DOBB_PROWS(0, false, true); }
-            else { if (gbf) DOBB_PROWS(1, true, true); else DOBB_PROWS(1, false, true); }
-        } else {
-            if (!nest) { if (gbf) DOBB_PROWS(0, true, false); else DOBB_PROWS(0, false, false); }
-            else { if (gbf) DOBB_PROWS(1, true, false); else DOBB_PROWS(1, false, false); }
-        }
-#undef DOBB_PROWS
-    }
-    {
-        ReconRowsTable t{};
-        for (int i = 0; i < cnt; ++i) {
-            const dobb_hparams &h = a.hp[c0 + i];
-            t.S[i] = (const uint8_t *)a.S[c0 + i]; t.Q[i] = a.Q[c0 + i]; t.W[i] = a.W[c0 + i];
-            t.U[i] = a.U ? a.U[c0 + i] : nullptr;
-            t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
-        }
-        const size_t sh = recon_rows_lds(nb, TR, ldp);
-#define DOBB_RROWS(WB)                                                                                           \
-    do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_recon_rows<NCH, TR, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("reconstruct_f16x2", s, (k_recon_rows<NCH, TR, WB>), grid, dim3(kRT), sh, m, n, nb, nblk, ngroups, \
-                    (int)tpg, ldp, t);                                                                           \
-    } while (0)
-        if (a.w_dtype == DOBB_BF16) DOBB_RROWS(true); else DOBB_RROWS(false);
-#undef DOBB_RROWS
-    }
-    return hipGetLastError();
-}
-
-// column scales from the row tiles' sums of squares, added in tile order: cs_j = 1 / ||C[:, j]||
-// (0 for a zero column).  grid = (ceil(n / 256), matrices), block 256.
 struct ColScaleTable {
     const double *part[kMaxMats];
     float *cs[kMaxMats];
@@ -983,15 +522,14 @@ hipError_t launch_proj_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s)
         t.C[i] = a.C[c0 + i]; t.part[i] = a.colpart[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
         t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
     }
-    const int ldp = step_bf16_ldp(nb);
-    const size_t sh = proj_rows_lds(nb, TR, ldp);
+    const size_t sh = proj_rows_lds(nb, TR);
     const bool gbf = a.g_dtype == DOBB_BF16;
     const bool nest = a.hp[c0].nesterov != 0;
 #define DOBB_PL2(NE, GB)                                                                                         \
     do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("project_l2_f16x3", s, (k_proj_rows<NCH, TR, NE, GB, true>), grid, dim3(kRT), sh, m, n, nb, nblk,   \
-                    ngroups, (int)tpg, ldp, t);                                                                  \
+        (void)hipFuncSetAttribute((const void *)k_proj_rows<NCH, TR, NE, GB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_l2_f16x3", s, (k_proj_rows<NCH, TR, NE, GB>), grid, dim3(kRT), sh, m, n, nb, nblk,   \
+                    ngroups, (int)tpg, t);                                                                       \
     } while (0)
     if (!nest) { if (gbf) DOBB_PL2(0, true); else DOBB_PL2(0, false); }
     else { if (gbf) DOBB_PL2(1, true); else DOBB_PL2(1, false); }
@@ -1023,43 +561,28 @@ hipError_t launch_recon_l2_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s
         t.U[i] = a.U ? a.U[c0 + i] : nullptr;
         t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
     }
-    const size_t sh = recon_rows_lds(nb, TR, 0, true);
+    const size_t sh = recon_rows_lds(nb, TR);
 #define DOBB_RL2(WB)                                                                                             \
     do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_recon_rows<NCH, TR, WB, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("reconstruct_l2_f16x3", s, (k_recon_rows<NCH, TR, WB, true>), grid, dim3(kRT), sh, m, n, nb, nblk,  \
-                    ngroups, (int)tpg, 0, t);                                                                    \
+        (void)hipFuncSetAttribute((const void *)k_recon_rows<NCH, TR, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("reconstruct_l2_f16x3", s, (k_recon_rows<NCH, TR, WB>), grid, dim3(kRT), sh, m, n, nb, nblk,  \
+                    ngroups, (int)tpg, t);                                                                       \
     } while (0)
     if (a.w_dtype == DOBB_BF16) DOBB_RL2(true); else DOBB_RL2(false);
 #undef DOBB_RL2
     return hipGetLastError();
 }
 
-template <int NCH>
-hipError_t launch_rows(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
-    const int nb = (int)a.sh.nb;
-    // the one-pass kernel when both split planes and a 64-row tile fit the LDS and no coefficient
-    // output is asked for
-    bool co = false;
-    for (int i = 0; i < cnt; ++i) co = co || (a.Cout && a.Cout[c0 + i]);
-    if (!co && (int64_t)fused_rows_lds(nb, 64) <= max_lds_bytes()) return launch_fused_tr<NCH, 64>(a, c0, cnt, s);
-    if ((int64_t)proj_rows_lds(nb, 128, ldp) <= max_lds_bytes() && (int64_t)recon_rows_lds(nb, 128, ldp) <= max_lds_bytes())
-        return launch_rows_tr<NCH, 128>(a, c0, cnt, ldp, s);
-    return launch_rows_tr<NCH, 64>(a, c0, cnt, ldp, s);
-}
-
 }  // namespace
-
-bool step_rows_eligible(const dobb_shape &sh) { return sh.nb <= 128; }
 
 bool recon_l2_rows_eligible(const dobb_shape &sh) {
     return sh.nb <= 128 && sh.nb % 4 == 0 && sh.n % 4 == 0 &&
-           (int64_t)recon_rows_lds((int)sh.nb, 64, 0, true) <= max_lds_bytes();
+           (int64_t)recon_rows_lds((int)sh.nb, 64) <= max_lds_bytes();
 }
 
 bool proj_l2_rows_eligible(const dobb_shape &sh) {
     return recon_l2_rows_eligible(sh) &&
-           (int64_t)proj_rows_lds((int)sh.nb, 128, step_bf16_ldp(sh.nb)) <= max_lds_bytes();
+           (int64_t)proj_rows_lds((int)sh.nb, 128) <= max_lds_bytes();
 }
 
 hipError_t launch_proj_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s) {
@@ -1076,21 +599,6 @@ hipError_t launch_recon_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t 
     if (nct <= 2) return launch_recon_l2_cfg<2>(a, c0, cnt, s);
     if (nct <= 3) return launch_recon_l2_cfg<3>(a, c0, cnt, s);
     return launch_recon_l2_cfg<4>(a, c0, cnt, s);
-}
-
-hipError_t launch_step_rows(const StepArgs &a, int ldp, hipStream_t s) {
-    const int nct = (int)((a.sh.nb + 31) / 32);
-    for (int c0 = 0; c0 < a.count;) {
-        const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
-        hipError_t e;
-        if (nct <= 1) e = launch_rows<1>(a, c0, cnt, ldp, s);
-        else if (nct <= 2) e = launch_rows<2>(a, c0, cnt, ldp, s);
-        else if (nct <= 3) e = launch_rows<3>(a, c0, cnt, ldp, s);
-        else e = launch_rows<4>(a, c0, cnt, ldp, s);
-        if (e != hipSuccess) return e;
-        c0 += cnt;
-    }
-    return hipSuccess;
 }
 
 }  // namespace dobb

@@ -1,4 +1,4 @@
-// Device helpers shared by the step kernels that stage row tiles through LDS (k_step_rows.hip,
+// Device helpers shared by the step kernels (k_step_fused.hip, k_step_rows.hip,
 // k_step_wide.hip): the operand splits, sign codes and buffer-descriptor access.
 #pragma once
 #include "dobb_internal.h"

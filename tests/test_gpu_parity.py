@@ -524,15 +524,18 @@ def test_grouped_equals_single_calls():
         assert torch.equal(a, b)
 
 
-def test_profiler_reports_kernels():
+@pytest.mark.parametrize("nb,names", [(64, ("step_fused",)), (192, ("project", "reconstruct"))])
+def test_profiler_reports_kernels(nb, names):
+    # blocks up to 128 wide take the one-pass kernel; wider ones the projection and reconstruction pair
     dobb.dobb_profile_reset()
     dobb.dobb_profile_enable(True)
-    Q, Qh, W, G, M, hp = _step_case(128, 256, 64, seed=71)
-    _run_step(W, G, M, Q, 64, hp, dobb.DOBB_NORM_SIGN)
+    Q, Qh, W, G, M, hp = _step_case(128, 2 * nb, nb, seed=71)
+    _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
     torch.cuda.synchronize()
     dobb.dobb_profile_enable(False)
     rep = dobb.dobb_profile_read()
-    assert any(k.startswith("project") for k in rep) and any(k.startswith("reconstruct") for k in rep)
+    for name in names:
+        assert any(k.startswith(name) for k in rep), (name, sorted(rep))
     for k, (launches, ms) in rep.items():
         assert launches >= 1 and ms > 0
     dobb.dobb_profile_reset()
@@ -573,12 +576,16 @@ def test_end_to_end_768_B4(seed):
 
 @pytest.mark.parametrize("m,n,nb,wdt,nest", [(300, 400, 100, torch.float32, False), (130, 96, 48, torch.float32, False),
                                              (64, 256, 64, torch.bfloat16, False), (1000, 1600, 100, torch.float32, True),
-                                             (70, 60, 20, torch.float32, False), (257, 224, 112, torch.bfloat16, False)])
+                                             (70, 60, 20, torch.float32, False), (257, 224, 112, torch.bfloat16, False),
+                                             (17, 8, 4, torch.float32, False), (1, 24, 8, torch.float32, True),
+                                             (45, 48, 16, torch.bfloat16, True), (99, 88, 44, torch.float32, False),
+                                             (203, 232, 116, torch.float32, False), (333, 512, 128, torch.float32, False),
+                                             (129, 384, 128, torch.bfloat16, True)])
 def test_step_one_pass_kernel(m, n, nb, wdt, nest):
-    """Without a coefficient output, blocks whose split basis fits the LDS twice take the one-pass
-    step kernel (momentum, projection, signs, reconstruction and update per row tile).  It must meet
-    the step's bars against the oracle, and it computes the same products in the same order as the
-    two-kernel path, so W, M and U are bitwise those of a run with C_out."""
+    """Blocks up to 128 wide (nb % 4 == 0) take the one-pass step kernel (momentum, projection, signs,
+    reconstruction and update per 16-row tile, one instance per 16-column chunk count 1..8 and
+    contraction depth).  It must meet the step's bars against the oracle; asked for C as well, the
+    same kernel only adds the store, so W, M and U are bitwise those of a run without it."""
     print(f"one-pass step m={m} n={n} nb={nb} {wdt} nesterov={nest}", flush=True)
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=7 * m + nb, w_dtype=wdt, g_dtype=wdt, nesterov=nest)
     W1, M1, U1 = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)                 # one pass
