@@ -57,7 +57,7 @@ STEP_FUSED_MAX_NB = 128       # ... and up to this width (nb % 4 == 0) the one-p
 # cpu_rows / cpu_tokens: the oracle sample (1/cpu_rows of each weight's rows, cpu_tokens of the tokens).
 WORKLOADS = {
     "gpt2xl": dict(specs="gpt2_xl_set", arg=BLOCKS, layers=48, per_layer=4, tokens=16384, w_dtype="float32",
-                   config=4, lr=2.5e-3, cpu_rows=1, cpu_tokens=8192,
+                   config=4, lr=2.5e-3, cpu_rows=1, cpu_tokens=16384, cpu_layers=4,
                    text="GPT-2 XL matrix set ({L} layers x qkv 4800x1600, proj 1600x1600, fc 6400x1600, "
                         "fc-proj 1600x6400; B=16, nb=100/400), fp32 W/G/M/A/Q, bf16 activations {N} tokens"),
     "gpt2small": dict(specs="gpt2_small_set", arg=BLOCKS, layers=12, per_layer=4, tokens=8192, w_dtype="float32",
@@ -270,10 +270,13 @@ KERNEL_SYMBOLS = {
     "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),
     "qr_form": (r"k_qr_form<", "k_qr.hip"),
     "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
-    "project_f16x3": (r"k_proj_(rows|wide)<", ("k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
-    "step_fused_f16": (r"k_step_rows_fused<", ("k_step_rows.hip", "step_common.h")),
+    "project_f16x3": (r"k_proj_wide<", ("k_step_wide.hip", "step_common.h")),
+    "step_fused_f16": (r"k_step_fused<", ("k_step_fused.hip", "step_common.h")),
     "project_bf16x6": (r"k_proj_bf16<", ("k_step_bf16.hip", "step_common.h")),
-    "reconstruct_f16x2": (r"k_recon_(bf16|rows|wide)<", ("k_step_bf16.hip", "k_step_rows.hip", "k_step_wide.hip", "step_common.h")),
+    "reconstruct_f16x2": (r"k_recon_(bf16|wide)<", ("k_step_bf16.hip", "k_step_wide.hip", "step_common.h")),
+    "project_l2_f16x3": (r"k_proj_rows<", ("k_step_rows.hip", "step_common.h")),
+    "reconstruct_l2_f16x3": (r"k_recon_rows<", ("k_step_rows.hip", "step_common.h")),
+    "cholqr_factor": (r"k_chol_inv", "k_cholqr.hip"),
 }
 
 
@@ -433,15 +436,18 @@ def host_cores():
 
 def cpu_baseline(group, xs, specs, wl, layers, col_l2=False, k_orth=1):
     """Time the oracle, threaded over the host's cores (row chunks of the step, blocks of the capture
-    and of the refresh), on the weights of the first and the last layer: the step on 1/cpu_rows of
-    each weight's rows, the capture on cpu_tokens of the tokens, the orthogonal-iteration refresh on
-    every block; scale linearly to the full set (every term is linear in rows, tokens and layers)."""
+    and of the refresh), on the weights of cpu_layers evenly spaced layers (the first and the last
+    among them): the step on 1/cpu_rows of each weight's rows, the capture on cpu_tokens of the
+    tokens, the orthogonal-iteration refresh on every block; scale linearly to the full set (every
+    term is linear in rows, tokens and layers)."""
     import oracle
     cores, facts = host_cores()
     rows_frac, tok = wl["cpu_rows"], wl["cpu_tokens"]
     n_tokens = wl["tokens"]
     per = wl["per_layer"]
-    sample = list(range(per)) + (list(range(len(specs) - per, len(specs))) if len(specs) > per else [])
+    k = min(wl.get("cpu_layers", 2), layers)
+    picked = [0] if k <= 1 else sorted({round(i * (layers - 1) / (k - 1)) for i in range(k)})
+    sample = [per * l + j for l in picked for j in range(per)]
     t_meas = 0.0
     s_total = 0.0
     for i in sample:
@@ -461,10 +467,9 @@ def cpu_baseline(group, xs, specs, wl, layers, col_l2=False, k_orth=1):
         t3 = time.perf_counter()
         t_meas += t3 - t0
         s_total += (t1 - t0) * (s.m / r) + (t2 - t1) * (n_tokens / tok) + (t3 - t2)
-    total_s = s_total * layers / (len(sample) / per)
-    nl = len(sample) // per
+    total_s = s_total * layers / len(picked)
     return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
-            "sample": (f"the {len(sample)} weights of {'layers 0 and ' + str(layers - 1) if nl > 1 else 'layer 0'} "
+            "sample": (f"the {len(sample)} weights of layers {', '.join(str(l) for l in picked)} "
                        f"of {layers}: step on 1/{rows_frac} of each weight's rows, capture on {tok} of {n_tokens} "
                        f"tokens, orthogonal-iteration refresh (k={k_orth}) on every block; measured "
                        f"{t_meas:.1f} s on {cores} threads, scaled linearly (rows, tokens, layers)"),
