@@ -141,7 +141,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                             W read + written: (8 + g + 2 w) m n bytes, no sign bytes; 4 m n nb flops
                             issued as five fp16 products over the padded block (16 ceil(nb / 16) basis
                             rows, 32 ceil(nb / 32) deep)
-    Column-l2 normalisation (norm="col_l2") takes the plain fp32 kernels instead of the last four:
+    Column-l2 normalisation (norm="col_l2") takes, for 128 < nb <= 416, split_q, project_l2_f16x3 (M
+    read + written, G read, C written: (12 + g) m n bytes), colnorm and reconstruct_l2_f16x3 (C read,
+    W read + written) on the wide kernels, and otherwise the plain fp32 kernels instead of the last four:
       momentum              G read, M read + written: (8 + g) m n bytes
       project               M read, C written: 8 m n bytes; 2 m n nb fp32 MFMA flops
       colnorm               C read: 4 m n bytes
@@ -190,6 +192,11 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
             if nb <= STEP_ROWS_MAX_NB and nb % 4 == 0 and s.n % 4 == 0:
                 add("project_l2_f16x3", (12.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
                 add("colscale", 8.0 * -(-s.m // 128) * s.n)
+                add("reconstruct_l2_f16x3", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+            elif STEP_ROWS_MAX_NB < nb <= 416 and nb % 4 == 0:
+                add("split_q", 14.0 * nb * nb * B)
+                add("project_l2_f16x3", (12.0 + g_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
+                add("colnorm", 4.0 * mn)
                 add("reconstruct_l2_f16x3", (4.0 + 2 * w_bytes) * mn, 2.0 * mn * nb, PEAK_FP32_MFMA, 3 * 2.0 * mn * nb)
             else:
                 add("momentum", (8.0 + g_bytes) * mn)

@@ -139,6 +139,8 @@ size_t step_ws_one(const dobb_shape &sh, int norm) {
     size_t b = al256(mn * 4) + al256((size_t)sh.n * 4);           // fp32 coefficients + column scales
     if (norm == DOBB_NORM_COL_L2)                                 // column sums of squares per 128-row tile
         b += al256((size_t)((sh.m + 127) / 128) * (size_t)sh.n * 8);
+    if (norm == DOBB_NORM_COL_L2 && step_wide_eligible(sh))       // the wide kernels' basis planes
+        b += al256(step_wide_planes_bytes(sh));
     return b;
 }
 
@@ -436,7 +438,11 @@ dobb_status dobb_step_grouped(int count, const dobb_shape *shapes, void *const *
                                   ? (double *)(reg + al256((size_t)sh.m * sh.n * 4) + al256((size_t)sh.n * 4))
                                   : nullptr);
                 const size_t s_bytes = al256((size_t)sh.m * (sh.n / sh.nb) * step_bf16_ldp(sh.nb));
-                pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes) : nullptr);
+                const size_t l2_planes = al256((size_t)sh.m * sh.n * 4) + al256((size_t)sh.n * 4) +
+                                         al256((size_t)((sh.m + 127) / 128) * (size_t)sh.n * 8);
+                pls.push_back(bf16 ? (uint16_t *)(reg + s_bytes)
+                              : norm == DOBB_NORM_COL_L2 && step_wide_eligible(sh) ? (uint16_t *)(reg + l2_planes)
+                                                                                    : nullptr);
                 aligned = aligned && ((uintptr_t)M[i] & 15u) == 0 &&
                           ((uintptr_t)G[i] & (g_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&
                           ((uintptr_t)W[i] & (w_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&

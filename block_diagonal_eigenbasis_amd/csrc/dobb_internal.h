@@ -202,6 +202,11 @@ hipError_t launch_proj_l2_rows(const StepArgs &a, int c0, int cnt, hipStream_t s
 bool step_wide_eligible(const dobb_shape &sh);
 size_t step_wide_planes_bytes(const dobb_shape &sh);
 hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s);
+// column-l2 for the same widths (k_step_wide.hip): matrices c0 .. c0 + cnt - 1 of a (cnt <= kMaxMats),
+// a.planes the basis planes (step_wide_planes_bytes each), a.C / a.colscale as for the fp32 kernels
+hipError_t launch_step_wide_l2(const StepArgs &a, int c0, int cnt, hipStream_t s);
+// the column scales 1 / ||C[:, j]|| of a.C into a.colscale (k_step.hip)
+hipError_t launch_colnorm(const StepArgs &a, int c0, int cnt, hipStream_t s);
 
 struct AccumulateArgs {
     int count;

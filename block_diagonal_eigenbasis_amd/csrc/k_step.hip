@@ -308,6 +308,14 @@ hipError_t launch_momentum(const StepArgs &a, int c0, int cnt, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_colnorm(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    ColTable t{};
+    for (int i = 0; i < cnt; ++i) { t.C[i] = a.C[c0 + i]; t.cs[i] = a.colscale[c0 + i]; }
+    dim3 grid((unsigned)((a.sh.n + kCnCols - 1) / kCnCols), cnt);
+    DOBB_LAUNCH("colnorm", s, k_colnorm, grid, dim3(kCnCols * kCnGroups), 0, a.sh.m, a.sh.n, t);
+    return hipGetLastError();
+}
+
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t m = a.sh.m, n = a.sh.n;
     const int nb = (int)a.sh.nb;
@@ -327,6 +335,21 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
             if (al) {
                 hipError_t e = launch_proj_l2_rows(a, c0, cnt, s);
                 if (e == hipSuccess) e = launch_recon_l2_rows(a, c0, cnt, s);
+                if (e != hipSuccess) return e;
+                c0 += cnt;
+                continue;
+            }
+        }
+        // column-l2 with 128 < nb <= 416: the split-fp16 wide kernels (basis streamed in k-slices)
+        if (a.hp[c0].norm == DOBB_NORM_COL_L2 && a.planes && a.planes[c0] && step_wide_eligible(a.sh)) {
+            bool al = true;
+            for (int i = 0; i < cnt; ++i)
+                al = al && aligned16(a.M[c0 + i]) &&
+                     ((uintptr_t)a.G[c0 + i] & (a.g_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&
+                     ((uintptr_t)a.W[c0 + i] & (a.w_dtype == DOBB_BF16 ? 7u : 15u)) == 0 &&
+                     (!a.U || aligned16(a.U[c0 + i])) && (!a.Cout || aligned16(a.Cout[c0 + i]));
+            if (al) {
+                const hipError_t e = launch_step_wide_l2(a, c0, cnt, s);
                 if (e != hipSuccess) return e;
                 c0 += cnt;
                 continue;
@@ -364,10 +387,8 @@ hipError_t launch_step(const StepArgs &a, hipStream_t s) {
 #undef DOBB_PROJ
         }
         if (norm == DOBB_NORM_COL_L2) {
-            ColTable t{};
-            for (int i = 0; i < cnt; ++i) { t.C[i] = a.C[c0 + i]; t.cs[i] = a.colscale[c0 + i]; }
-            dim3 grid((unsigned)((n + kCnCols - 1) / kCnCols), cnt);
-            DOBB_LAUNCH("colnorm", s, k_colnorm, grid, dim3(kCnCols * kCnGroups), 0, m, n, t);
+            const hipError_t e = launch_colnorm(a, c0, cnt, s);
+            if (e != hipSuccess) return e;
         }
         // reconstruction + parameter update (column-l2 with nb <= 128: the split-fp16 rows kernel)
         if (norm == DOBB_NORM_COL_L2 && recon_l2_rows_eligible(a.sh)) {

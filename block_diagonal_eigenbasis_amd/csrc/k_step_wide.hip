@@ -18,6 +18,11 @@
 //   k_recon_wide  64-row tiles, two workgroups per CU: sign-byte rows -> LDS once; waves take
 //                 (32-row tile, every fourth chunk): U = S Q^T; U -> LDS (32 rows at a time) -> rows,
 //                 where W <- W - lr (s U + wd W) is applied
+// Column-l2 normalisation (Dobb-l2, Tables 11-12) takes the same two kernels with L2 set: the
+// projection writes C (unscaled by the row's power of two) to the workspace instead of sign bytes,
+// k_colnorm (k_step.hip) turns C into the column scales 1 / ||C[:, j]||, and the reconstruction
+// stages, with each basis slice, the 16 columns of C~ = C diag(colscale) the slice multiplies
+// (|C~| <= 1: two fp16 parts without a scale, three products hi hi, hi lo(Q), lo hi).
 // The workgroups of one block are adjacent in launch order, so they run together on one XCD and
 // read the basis slices from its L2.
 #include "step_common.h"
@@ -136,6 +141,7 @@ struct ProjWideTable {
     const uint16_t *planes[kMaxMats];
     uint8_t *S[kMaxMats];
     float *Cout[kMaxMats];     // NULL or m x n fp32: the coefficients (verification output)
+    float *C[kMaxMats];        // column-l2: the coefficients (m x n fp32 workspace)
     float mu[kMaxMats];
 };
 // LDS: two Q^T slices (2 planes each; the sign tile overlays them after the products), the P chunk
@@ -151,8 +157,9 @@ __host__ __device__ inline size_t proj_wide_lds(int nb, int ldp) {
 
 // grid.x = tile groups (fastest) x blocks x matrices, renumbered per XCD; block 512.
 // NCT = ceil(nb / 32).  Wave w: 32-row tile rt = w % 4, column chunks cg + 2 j (cg = w / 4).
-// CO: also write the coefficients to t.Cout (a verification output; off in the timed path)
-template <int NCT, int NEST, bool GBF16, bool CO = false>
+// CO: also write the coefficients to t.Cout (a verification output; off in the timed path).
+// L2: column-l2 normalisation: C to t.C instead of the sign bytes.
+template <int NCT, int NEST, bool GBF16, bool CO = false, bool L2 = false>
 __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb, int nblk, int ngroups, int tpg,
                                                    int ldp, ProjWideTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -338,10 +345,32 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                 par ^= 1;
             }
         }
+        const int64_t crow = tile * kTR + prow;
+        if constexpr (L2) {
+            // C, unscaled, along the lane's row: columns 32 ch + 8 qq + 4 (l / 32) + 0..3
+            float *const Cw = t.C[mat] + (int64_t)b * nb;
+            float *const Co = t.Cout[mat] ? t.Cout[mat] + (int64_t)b * nb : nullptr;
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                const int ch = cg + 2 * j;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int col = 32 * ch + 8 * qq + 4 * (lane >> 5);
+                    if (ch < nct && col < nb && crow < m) {
+                        const f32x4 cv = {__builtin_amdgcn_ldexpf(acc[j][4 * qq], -sreg),
+                                          __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -sreg),
+                                          __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -sreg),
+                                          __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -sreg)};
+                        *(f32x4 *)(Cw + crow * n + col) = cv;
+                        if (Co) *(f32x4 *)(Co + crow * n + col) = cv;
+                    }
+                }
+            }
+            continue;
+        }
         // sign bytes: lane holds row 32 rt + l % 32, columns 32 ch + 8 qq + 4 (l / 32) + 0..3 -> LDS
         __syncthreads();   // every wave is done with the Q slices that the sign tile overlays
         float *const Co = CO ? t.Cout[mat] : nullptr;
-        const int64_t crow = tile * kTR + prow;
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const int ch = cg + 2 * j;
@@ -371,6 +400,8 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
 // ---- reconstruction ------------------------------------------------------------------------------
 struct ReconWideTable {
     const uint8_t *S[kMaxMats];
+    const float *C[kMaxMats];    // column-l2: the coefficients (m x n fp32) and the column scales
+    const float *cs[kMaxMats];
     const uint16_t *planes[kMaxMats];
     void *W[kMaxMats];
     float *U[kMaxMats];
@@ -384,21 +415,25 @@ __host__ __device__ inline int wide_spitch(int nb) { return kKSD * ((nb + kKSD -
 // the half-waves of one accumulator register fall in opposite bank halves
 __host__ __device__ inline int wide_uld(int nb) { return wide_geo(nb).R + 8; }
 constexpr int kRTR = 64;   // reconstruction: rows per workgroup
+constexpr int kCSP = kKSD + 8;   // column-l2: C~ slice plane pitch in 2-byte elements (3 16-byte units)
 // LDS: region 0 holds two Q slices (2 planes each) during the products, then 32 rows of U at a time;
-// region 1 the tile's sign rows.  At most 81408 bytes (nb <= 416): two workgroups fit on a CU.
+// region 1 the tile's sign rows, or (column-l2) two C~ slices of kRTR rows x 16 columns, each split
+// into two fp16 planes.  At most
+// 81408 bytes (nb <= 416): two workgroups fit on a CU.
 __host__ __device__ inline size_t recon_wide_qregion(int nb) {
     const size_t q = (size_t)2 * 2 * wide_geo(nb).R * kKSD * 2, u = (size_t)32 * wide_uld(nb) * 4;
     return a16(q > u ? q : u);
 }
-__host__ __device__ inline size_t recon_wide_lds(int nb, int ldp) {
+__host__ __device__ inline size_t recon_wide_lds(int nb, int ldp, bool l2 = false) {
     (void)ldp;
-    return recon_wide_qregion(nb) + a16((size_t)kRTR * wide_spitch(nb));
+    return recon_wide_qregion(nb) + (l2 ? a16((size_t)2 * 2 * kRTR * kCSP * 2) : a16((size_t)kRTR * wide_spitch(nb)));
 }
 
 // grid.x = tiles of kRTR rows (fastest) x blocks x matrices, renumbered per XCD; block 512, two
 // workgroups per CU (four waves per SIMD), so that one's products overlap the other's row traffic.
 // NCT = ceil(nb / 32).  Wave w: 32-row tile rt = w / 4, column chunks cg + 4 j (cg = w % 4).
-template <int NCT, bool WBF16>
+// L2: column-l2 normalisation (C~ slices instead of the sign tile, three products).
+template <int NCT, bool WBF16, bool L2 = false>
 __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int nb, int nblk, int ntile, int ldp,
                                                        ReconWideTable t) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -409,6 +444,7 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
     uint16_t *qs = (uint16_t *)lds;                        // [2][2][R][16], then U rows [32][uld] fp32
     float *us = (float *)lds;
     uint8_t *ss = lds + recon_wide_qregion(nb);             // [kRTR][spitch]
+    uint16_t *cbuf = (uint16_t *)(lds + recon_wide_qregion(nb));   // L2: [2 slices][2 planes][kRTR][kCSP]
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = x % ntile, rest = x / ntile;
@@ -424,7 +460,10 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
     float *const U = t.U[mat];
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(U ? (const void *)(U + (int64_t)b * nb) : t.W[mat], U ? mn_el * 4 : 0);
     const int64_t sld = (int64_t)nblk * ldp;
-    const __amdgpu_buffer_rsrc_t rS = make_rsrc(t.S[mat] + (int64_t)b * ldp, m * sld - (int64_t)b * ldp);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(L2 ? (const void *)t.W[mat] : (const void *)(t.S[mat] + (int64_t)b * ldp),
+                                                L2 ? 0 : m * sld - (int64_t)b * ldp);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(L2 ? (const void *)(t.C[mat] + (int64_t)b * nb) : (const void *)t.W[mat],
+                                                L2 ? mn_el * 4 : 0);
     const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
     const uint16_t *QN = t.planes[mat] + (int64_t)b * PE;
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QN, (plane + PE) * 2);
@@ -457,9 +496,39 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
         }
     };
 
+    // column-l2: piece e < 4 kRTR of a C~ slice: row e / 4, columns 4 (e % 4) .. + 3 of the slice,
+    // C times its column scales (zero past m and nb)
+    f32x4 cpc = {0.f, 0.f, 0.f, 0.f};
+    auto load_c = [&](int ks) {
+        if constexpr (L2) {
+            const int e = tid, r = e >> 2, c = kKSD * ks + 4 * (e & 3);
+            const int64_t row = row0 + r;
+            const bool ok = e < 4 * kRTR && row < m && c < nb;
+            cpc = bload4(rC, boff(ok ? (unsigned)(row * n + c) : kOff, 4));
+            if (ok) {
+                const f32x4 sv = *(const f32x4 *)(t.cs[mat] + (int64_t)b * nb + c);
+                cpc = f32x4{cpc[0] * sv[0], cpc[1] * sv[1], cpc[2] * sv[2], cpc[3] * sv[3]};
+            }
+        }
+    };
+    // split once at staging (|C~| <= 1: two fp16 parts, no scale)
+    auto store_c = [&](int buf) {
+        if constexpr (L2) {
+            if (tid < 4 * kRTR) {
+                uint16_t h[4], l[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) split2h(cpc[cc], h[cc], l[cc]);
+                uint16_t *d = cbuf + ((size_t)2 * buf * kRTR + (tid >> 2)) * kCSP + 4 * (tid & 3);
+                *(uint2 *)d = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+                *(uint2 *)(d + kRTR * kCSP) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+            }
+        }
+    };
+
     load_q(0);
+    load_c(0);
     // sign rows of the tile -> LDS in 8-byte pieces, k = 0 .. 16 KS - 1 (zero at and past nb)
-    {
+    if constexpr (!L2) {
         constexpr int kSP = (kRTR * (R / 8) + kWT - 1) / kWT;
         const int q8 = 2 * KS;
         const float inv_q8 = 1.0f / (float)q8;
@@ -489,9 +558,21 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
     int par = 0;
     for (int ks = 0; ks < KS; ++ks) {
         store_q(par);
-        if (ks + 1 < KS) load_q(ks + 1);
+        store_c(par);
+        if (ks + 1 < KS) {
+            load_q(ks + 1);
+            load_c(ks + 1);
+        }
         __syncthreads();
-        const f16x8 as = signs_f16x8(*(const uint2 *)(ss + (32 * rt + (lane & 31)) * spitch + kKSD * ks + kh));
+        f16x8 as, al;
+        if constexpr (L2) {
+            const uint16_t *cp = cbuf + ((size_t)2 * par * kRTR + 32 * rt + (lane & 31)) * kCSP + kh;
+            as = __builtin_bit_cast(f16x8, *(const uint4 *)cp);
+            al = __builtin_bit_cast(f16x8, *(const uint4 *)(cp + kRTR * kCSP));
+        } else {
+            as = signs_f16x8(*(const uint2 *)(ss + (32 * rt + (lane & 31)) * spitch + kKSD * ks + kh));
+            al = as;
+        }
         const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
@@ -503,6 +584,7 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
                 const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
+                if constexpr (L2) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, Bh, acc[j], 0, 0, 0);
             }
             // one chunk's operands at a time (the other waves of the SIMD cover the LDS latency)
             __builtin_amdgcn_sched_barrier(0);
@@ -652,6 +734,71 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
     return hipGetLastError();
 }
 
+// Column-l2: the basis planes, C (with momentum) into the workspace, the column scales, then the
+// reconstruction of C~ with the W update.
+template <int NCT>
+hipError_t launch_wide_l2_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStream_t s) {
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const WideGeo geo = wide_geo(nb);
+    {
+        SplitWideTable t{};
+        for (int i = 0; i < cnt; ++i) { t.Q[i] = a.Q[c0 + i]; t.planes[i] = a.planes[c0 + i]; }
+        DOBB_LAUNCH("split_q", s, k_split_wide, dim3((unsigned)geo.KS, (unsigned)(nblk * cnt)), dim3(256), 0, nb, nblk, t);
+    }
+    const int64_t ntile = (m + kTR - 1) / kTR;
+    const int64_t tpg = wide_tpg(ntile, (int64_t)nblk * cnt);
+    const int ngroups = (int)((ntile + tpg - 1) / tpg);
+    const dim3 grid((unsigned)((int64_t)ngroups * nblk * cnt));
+    {
+        ProjWideTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i];
+            t.C[i] = a.C[c0 + i]; t.mu[i] = a.hp[c0 + i].momentum;
+            t.Cout[i] = a.Cout ? a.Cout[c0 + i] : nullptr;
+        }
+        const size_t sh = proj_wide_lds(nb, ldp);
+        const bool gbf = a.g_dtype == DOBB_BF16;
+        const bool nest = a.hp[c0].nesterov != 0;
+#define DOBB_PWL2(NE, GB)                                                                                        \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_proj_wide<NCT, NE, GB, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("project_l2_f16x3", s, (k_proj_wide<NCT, NE, GB, false, true>), grid, dim3(kWT), sh, m, n, nb, nblk, \
+                    ngroups, (int)tpg, ldp, t);                                                                  \
+    } while (0)
+        if (!nest) { if (gbf) DOBB_PWL2(0, true); else DOBB_PWL2(0, false); }
+        else { if (gbf) DOBB_PWL2(1, true); else DOBB_PWL2(1, false); }
+#undef DOBB_PWL2
+    }
+    {
+        const hipError_t e = launch_colnorm(a, c0, cnt, s);
+        if (e != hipSuccess) return e;
+    }
+    {
+        ReconWideTable t{};
+        for (int i = 0; i < cnt; ++i) {
+            const dobb_hparams &h = a.hp[c0 + i];
+            t.C[i] = a.C[c0 + i]; t.cs[i] = a.colscale[c0 + i];
+            t.planes[i] = a.planes[c0 + i]; t.W[i] = a.W[c0 + i];
+            t.U[i] = a.U ? a.U[c0 + i] : nullptr;
+            t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
+        }
+        const size_t sh = recon_wide_lds(nb, ldp, true);
+        const int rtiles = (int)((m + kRTR - 1) / kRTR);
+        const dim3 rgrid((unsigned)((int64_t)rtiles * nblk * cnt));
+#define DOBB_RWL2(WB)                                                                                            \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_recon_wide<NCT, WB, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("reconstruct_l2_f16x3", s, (k_recon_wide<NCT, WB, true>), rgrid, dim3(kWT), sh, m, n, nb, nblk,  \
+                    rtiles, ldp, t);                                                                             \
+    } while (0)
+        if (a.w_dtype == DOBB_BF16) DOBB_RWL2(true); else DOBB_RWL2(false);
+#undef DOBB_RWL2
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool step_wide_eligible(const dobb_shape &sh) {
@@ -667,6 +814,22 @@ bool step_wide_eligible(const dobb_shape &sh) {
 
 size_t step_wide_planes_bytes(const dobb_shape &sh) {
     return (size_t)4 * (size_t)(sh.n / sh.nb) * (size_t)wide_plane_elems((int)sh.nb) * 2;
+}
+
+hipError_t launch_step_wide_l2(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    const int ldp = step_bf16_ldp(a.sh.nb);
+    switch ((int)((a.sh.nb + 31) / 32)) {
+        case 5: return launch_wide_l2_cfg<5>(a, c0, cnt, ldp, s);
+        case 6: return launch_wide_l2_cfg<6>(a, c0, cnt, ldp, s);
+        case 7: return launch_wide_l2_cfg<7>(a, c0, cnt, ldp, s);
+        case 8: return launch_wide_l2_cfg<8>(a, c0, cnt, ldp, s);
+        case 9: return launch_wide_l2_cfg<9>(a, c0, cnt, ldp, s);
+        case 10: return launch_wide_l2_cfg<10>(a, c0, cnt, ldp, s);
+        case 11: return launch_wide_l2_cfg<11>(a, c0, cnt, ldp, s);
+        case 12: return launch_wide_l2_cfg<12>(a, c0, cnt, ldp, s);
+        case 13: return launch_wide_l2_cfg<13>(a, c0, cnt, ldp, s);
+        default: return hipErrorInvalidValue;   // see step_wide_eligible
+    }
 }
 
 hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {

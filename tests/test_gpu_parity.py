@@ -388,6 +388,36 @@ def test_step_bf16_weights_and_gradients(m, n, nb):
     check_w(host(W_s), host(W), host(U_s), hp, bf16=True)
 
 
+@pytest.mark.parametrize("m,n,nb,wdt,nest", [(257, 800, 400, torch.bfloat16, False), (130, 544, 136, torch.float32, True),
+                                             (203, 832, 416, torch.float32, False), (1, 400, 400, torch.float32, False),
+                                             (129, 1152, 192, torch.bfloat16, True)])
+def test_step_column_l2_wide(m, n, nb, wdt, nest):
+    """Column-l2 for 128 < nb <= 416 runs on the wide split-fp16 kernels: the projection writes C (to
+    the workspace and to C_out), the column scales come from C, and the reconstruction stages slices
+    of C~ = C diag(colscale) beside the basis slices (three fp16 products).  C within 1e-5 of the
+    oracle's per block, U within 1e-5 relative Frobenius, M within one rounding, W within one fp32
+    update (bf16 store when W is bf16)."""
+    print(f"step column-l2 wide m={m} n={n} nb={nb} {wdt} nesterov={nest}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=5 * m + nb, w_dtype=wdt, g_dtype=wdt, nesterov=nest)
+    W_l, M_l, U_l, C_l = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_COL_L2, want_c=True)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"], nesterov=nest, norm=oracle.NORM_COL_L2)
+    _check_momentum(M_l, M, G, hp["momentum"], M_r)
+    P_r = (G.cpu().double().numpy() + hp["momentum"] * M_r) if nest else M_r
+    C_g = host(C_l)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = P_r[:, sl] @ Qh[b]
+        assert np.linalg.norm(C_g[:, sl] - C_ref) <= 1e-5 * np.linalg.norm(C_ref)
+    U_g = host(U_l)
+    assert np.linalg.norm(U_g - U_r) <= 1e-5 * np.linalg.norm(U_r)
+    check_w(host(W_l), host(W), U_g, hp, bf16=wdt == torch.bfloat16)
+    # without C_out and U_out (the timed launch): the same W and M
+    W2, M2 = W.clone(), M.clone()
+    dobb.dobb_step(W2, G, M2, Q, nb, dobb.make_hparams(norm=dobb.DOBB_NORM_COL_L2, **hp))
+    assert torch.equal(W2, W_l) and torch.equal(M2, M_l)
+
+
 def test_step_nesterov_and_column_l2():
     m, n, nb = 96, 128, 64
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=21, nesterov=True)
