@@ -141,6 +141,10 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                             W read + written: (8 + g + 2 w) m n bytes, no sign bytes; 4 m n nb flops
                             issued as five fp16 products over the padded block (16 ceil(nb / 16) basis
                             rows, 32 ceil(nb / 32) deep)
+      step_wide_fused_f16   128 < nb <= 416, nb % 4 = 0: the one-pass wide kernel, same bytes and flops
+                            (after split_q), five fp16 products over 32 ceil(nb / 32) basis rows and a
+                            16 ceil(nb / 16)-deep contraction; project_f16x3 and reconstruct_f16x2 are
+                            the two-kernel path a coefficient output takes
     Column-l2 normalisation (norm="col_l2") takes, for 128 < nb <= 416, split_q, project_l2_f16x3 (M
     read + written, G read, C written: (12 + g) m n bytes), colnorm and reconstruct_l2_f16x3 (C read,
     W read + written) on the wide kernels, and otherwise the plain fp32 kernels instead of the last four:
@@ -207,6 +211,12 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
         if nb <= STEP_FUSED_MAX_NB and nb % 4 == 0:
             rows, kp = 16 * -(-nb // 16), 32 * -(-nb // 32)   # basis rows and contraction depth, padded
             add("step_fused_f16", (8.0 + g_bytes + 2 * w_bytes) * mn, 4.0 * mn * nb, PEAK_FP32_MFMA,
+                5 * 2.0 * s.m * B * rows * kp)
+            continue
+        if STEP_ROWS_MAX_NB < nb <= 416 and nb % 4 == 0:
+            rows, kp = 32 * -(-nb // 32), 16 * -(-nb // 16)   # basis rows and contraction depth, padded
+            add("split_q", 14.0 * nb * nb * B)
+            add("step_wide_fused_f16", (8.0 + g_bytes + 2 * w_bytes) * mn, 4.0 * mn * nb, PEAK_FP32_MFMA,
                 5 * 2.0 * s.m * B * rows * kp)
             continue
         if nb > STEP_ROWS_MAX_NB:
@@ -279,6 +289,7 @@ KERNEL_SYMBOLS = {
     "split_q": (r"k_split_(q|wide)", ("k_step_bf16.hip", "k_step_wide.hip")),
     "project_f16x3": (r"k_proj_wide<", ("k_step_wide.hip", "step_common.h")),
     "step_fused_f16": (r"k_step_fused<", ("k_step_fused.hip", "step_common.h")),
+    "step_wide_fused_f16": (r"k_step_wide_fused<", ("k_step_wide.hip", "step_common.h")),
     "project_bf16x6": (r"k_proj_bf16<", ("k_step_bf16.hip", "step_common.h")),
     "reconstruct_f16x2": (r"k_recon_(bf16|wide)<", ("k_step_bf16.hip", "k_step_wide.hip", "step_common.h")),
     "project_l2_f16x3": (r"k_proj_rows<", ("k_step_rows.hip", "step_common.h")),

@@ -665,6 +665,305 @@ __global__ void __launch_bounds__(512, 4) k_recon_wide(int64_t m, int64_t n, int
     update(1);
 }
 
+// ---- the whole step in one pass --------------------------------------------------------------------
+// k_step_wide_fused: one 128-row tile of one block per workgroup.  Momentum and the projection run as
+// in k_proj_wide (P chunks staged in LDS, Q^T slices streamed); the signs go to an LDS tile that stays
+// for the reconstruction, which runs U = S Q^T over the same 128 rows with the Q slices streamed in
+// turn (wave w: 32-row tile w % 4, every second 32-column chunk from w / 4, the projection's split);
+// W is updated straight from the accumulators.  The sign bytes never reach HBM, and each
+// basis slice serves 128 rows in both products.  Templated on the chunks per wave (NCW = ceil(nct / 2),
+// nct = ceil(nb / 32) at run time) to keep the instances few.
+struct FusedWideTable {
+    float *M[kMaxMats];
+    const void *G[kMaxMats];
+    const uint16_t *planes[kMaxMats];
+    void *W[kMaxMats];
+    float *U[kMaxMats];
+    float mu[kMaxMats], lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
+};
+// LDS: region 0 the two basis slices (2 planes each); the P chunk planes; the tile's row scale
+// exponents; the sign tile (rows of wide_spitch bytes)
+__host__ __device__ inline size_t fused_wide_qregion(int nb) { return a16((size_t)2 * 2 * wide_geo(nb).R * kKSD * 2); }
+__host__ __device__ inline size_t fused_wide_lds(int nb) {
+    return fused_wide_qregion(nb) + (size_t)2 * kTR * kPLD * 2 + a16((size_t)kTR * 4) +
+           a16((size_t)kTR * wide_spitch(nb));
+}
+
+// grid.x = 128-row tiles (fastest) x blocks x matrices, renumbered per XCD; block 512.
+template <int NCW, int NEST, bool GBF16, bool WBF16>
+__global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, int nb, int nblk, int ntile,
+                                                         FusedWideTable t) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const WideGeo geo = wide_geo(nb);
+    const int nct = geo.nct, R = geo.R, KS = geo.KS;
+    const int spitch = wide_spitch(nb);
+    uint16_t *qs = (uint16_t *)lds;                                      // [2][2][R][16]
+    uint16_t *ps = (uint16_t *)(lds + fused_wide_qregion(nb));           // [2][kTR][kPLD]
+    int *rs = (int *)(ps + 2 * kTR * kPLD);                              // [kTR] row scale exponents
+    uint8_t *ss = (uint8_t *)rs + a16((size_t)kTR * 4);                  // [kTR][spitch] sign bytes
+
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = x % ntile, rest = x / ntile;
+    const int b = rest % nblk, mat = rest / nblk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rt = w & 3, cg = w >> 2;
+    const int64_t row0 = (int64_t)tile * kTR;
+
+    constexpr int kGS = GBF16 ? 2 : 4, kWS = WBF16 ? 2 : 4;
+    const int64_t mn_el = m * n - (int64_t)b * nb;
+    const __amdgpu_buffer_rsrc_t rM = make_rsrc(t.M[mat] + (int64_t)b * nb, mn_el * 4);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc((const char *)t.G[mat] + (int64_t)b * nb * kGS, mn_el * kGS);
+    float *const U = t.U[mat];
+    const int64_t PE = wide_plane_elems(nb), plane = (int64_t)nblk * PE;
+    const __amdgpu_buffer_rsrc_t rQN = make_rsrc(t.planes[mat] + (int64_t)b * PE, (plane + PE) * 2);              // Q
+    const __amdgpu_buffer_rsrc_t rQT = make_rsrc(t.planes[mat] + 2 * plane + (int64_t)b * PE, (plane + PE) * 2);  // Q^T
+    const float mu = t.mu[mat], lr = t.lr[mat], wd = t.wd[mat], sc = t.scale[mat];
+
+    // ---- momentum and P: M / G chunk pieces, kTR rows x 16 four-column pieces, 4 per thread ----
+    constexpr int kMP = kTR * (kKC / 4) / kWT;
+    f32x4 mr[kMP], gr[kMP];
+    auto mg_off = [&](int i, int kc0) -> unsigned {
+        const int e = tid + kWT * i;
+        const int r = e / (kKC / 4), c = kc0 + 4 * (e - r * (kKC / 4));
+        const int64_t row = row0 + r;
+        return (row < m && c < nb) ? (unsigned)row * (unsigned)n + (unsigned)c : kOff;
+    };
+    auto load_mg = [&](int kc0) {
+#pragma unroll
+        for (int i = 0; i < kMP; ++i) {
+            const unsigned o = mg_off(i, kc0);
+            mr[i] = bload4(rM, boff(o, 4));
+            if constexpr (GBF16) {
+                const uint2 hb = bload2u(rG, boff(o, 2));
+                gr[i] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
+                              bf16_to_f32((uint16_t)hb.y), bf16_to_f32((uint16_t)(hb.y >> 16))};
+            } else {
+                gr[i] = bload4(rG, boff(o, 4));
+            }
+        }
+    };
+    // momentum written back along the rows; P scaled by its row's power of two and split once into two
+    // fp16 planes of the LDS chunk (as in k_proj_wide)
+    auto stage_p = [&](int kc0, bool first) {
+#pragma unroll
+        for (int i = 0; i < kMP; ++i) {
+            const int e = tid + kWT * i;
+            const int r = e / (kKC / 4), c = 4 * (e - r * (kKC / 4));
+            f32x4 mn, pv;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
+                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
+            }
+            bstore4(mn, rM, boff(mg_off(i, kc0), 4));
+            uint32_t mx = __float_as_uint(pv[0]) & 0x7fffffffu;
+#pragma unroll
+            for (int cc = 1; cc < 4; ++cc) {
+                const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
+                mx = u > mx ? u : mx;
+            }
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)mx, sh, 16);
+                mx = o > mx ? o : mx;
+            }
+            int se = row_scale_exp(mx);
+            if (!first) {
+                const int so = rs[r];
+                se = so < se ? so : se;
+            }
+            if ((tid & 15) == 0) rs[r] = se;
+            uint16_t h[4], l[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) split2s(__builtin_amdgcn_ldexpf(pv[cc], se), h[cc], l[cc]);
+            uint16_t *pp = ps + r * kPLD + c;
+            *(uint2 *)pp = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+            *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+        }
+    };
+    // basis slice pieces: 2 planes x R rows x 2 halves of 16 bytes (R <= 64 NCW)
+    constexpr int kQP = (4 * 64 * NCW + kWT - 1) / kWT;
+    uint4 qr[kQP];
+    auto load_q = [&](__amdgpu_buffer_rsrc_t rq, int ks) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            const int pl = e / (2 * R), rem = e - pl * 2 * R;
+            const unsigned o = e < 4 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
+            qr[i] = bload4u(rq, boff(o, 2));
+        }
+    };
+    auto store_q = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kQP; ++i) {
+            const int e = tid + kWT * i;
+            if (e < 4 * R) *(uint4 *)(qs + (size_t)buf * 2 * R * kKSD + 8 * e) = qr[i];
+        }
+    };
+
+    const int kh = 8 * (lane >> 5);
+    const int prow = 32 * rt + (lane & 31);   // the tile row of this lane's accumulators
+    const int nchunk = (KS + kSPC - 1) / kSPC;
+    int par = 0;
+    load_mg(0);
+    load_q(rQT, 0);
+    f32x16 acc[NCW];
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+
+    // ---- C^T = Q^T P^T ----
+    {
+        const int qrow = 32 * cg + (lane & 31);
+        const int qoff = qrow * kKSD + 8 * ((lane >> 5) ^ qswz(qrow));
+        int sreg = 0;   // the scale exponent acc holds its row at
+        for (int c = 0; c < nchunk; ++c) {
+            const int kc0 = c * kKC;
+            __syncthreads();   // the last chunk's products are done with ps
+            stage_p(kc0, c == 0);
+            if (c + 1 < nchunk) load_mg(kc0 + kKC);
+            const int s_end = KS - kSPC * c < kSPC ? KS - kSPC * c : kSPC;
+            for (int s = 0; s < s_end; ++s) {
+                const int ks = kSPC * c + s;
+                store_q(par);
+                if (ks + 1 < KS) load_q(rQT, ks + 1);
+                else load_q(rQN, 0);   // the reconstruction starts at slice 0 of Q
+                __syncthreads();
+                if (s == 0) {
+                    const int se = rs[prow];
+                    const int d = c == 0 ? 0 : se - sreg;
+                    if (__any(d != 0)) {
+#pragma unroll
+                        for (int j = 0; j < NCW; ++j)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) acc[j][i] = __builtin_amdgcn_ldexpf(acc[j][i], d);
+                    }
+                    sreg = se;
+                }
+                const uint16_t *pr = ps + prow * kPLD + kKSD * s + kh;
+                const f16x8 ah = *(const f16x8 *)pr;
+                const f16x8 al = *(const f16x8 *)(pr + kTR * kPLD);
+                const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD + qoff;
+#pragma unroll
+                for (int j = 0; j < NCW; j += 2) {
+                    const bool two = j + 1 < NCW && cg + 2 * (j + 1) < nct;
+                    if (cg + 2 * j < nct) {
+                        const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
+                        const uint16_t *q1 = q0 + 2 * 32 * kKSD;
+                        const f16x8 Qh0 = *(const f16x8 *)q0, Ql0 = *(const f16x8 *)(q0 + R * kKSD);
+                        if (two) {
+                            const f16x8 Qh1 = *(const f16x8 *)q1, Ql1 = *(const f16x8 *)(q1 + R * kKSD);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql1, ah, acc[j + 1], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, al, acc[j + 1], 0, 0, 0);
+                        } else {
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                        }
+                    }
+                }
+                par ^= 1;
+            }
+        }
+    }
+    // ---- the signs -> the sign tile: lane holds row prow, columns 32 ch + 8 qq + 4 (l / 32) + 0..3;
+    // bytes at and past nb stay zero (written here for the chunks past nb, below for the row tail) ----
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+        const int ch = cg + 2 * j;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int col = 32 * ch + 8 * qq + 4 * (lane >> 5);   // nb % 4 == 0: all 4 valid or none
+            const uint32_t w4 = sign_byte(acc[j][4 * qq]) | (sign_byte(acc[j][4 * qq + 1]) << 8) |
+                                (sign_byte(acc[j][4 * qq + 2]) << 16) | (sign_byte(acc[j][4 * qq + 3]) << 24);
+            if (ch < nct && col < nb) *(uint32_t *)(ss + prow * spitch + col) = w4;
+        }
+    }
+    // zero the row tails [nb, 16 KS) that the products read (nb % 4 == 0: whole 4-byte words)
+    for (int e = tid; e < kTR * ((kKSD * KS - nb) / 4); e += kWT) {
+        const int q4 = (kKSD * KS - nb) / 4;
+        const int r = e / q4, c = nb + 4 * (e - r * q4);
+        *(uint32_t *)(ss + r * spitch + c) = 0u;
+    }
+
+    // ---- U = S Q^T over the same rows ----
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+    for (int ks = 0; ks < KS; ++ks) {
+        store_q(par);
+        if (ks + 1 < KS) load_q(rQN, ks + 1);
+        __syncthreads();   // the slice and (first step) every wave's signs are in LDS
+        const f16x8 as = signs_f16x8(*(const uint2 *)(ss + prow * spitch + kKSD * ks + kh));
+        const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int ch = cg + 2 * j;
+            if (ch < nct) {
+                const int p = 32 * ch + (lane & 31);
+                const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
+                const f16x8 Bh = *(const f16x8 *)(qb + o);
+                const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        par ^= 1;
+    }
+
+    // ---- W <- W - lr (s U + wd W) straight from the accumulators: lane holds column 32 ch + l % 32 of
+    // rows 8 (r / 4) + 4 (l / 32) + r % 4 of its 32-row tile, so one 4-byte access per lane covers two
+    // 128-byte row pieces.  The descriptors start at the tile's first row and end with its last one,
+    // so rows past m are dropped by the hardware; a chunk's W loads are issued one chunk ahead ----
+    const int64_t trows = m - row0 < kTR ? m - row0 : kTR;
+    const int64_t tile_el = (trows - 1) * n + nb;      // elements from (row0, b nb) to the tile's last one
+    const int64_t tbase = row0 * n + (int64_t)b * nb;
+    const __amdgpu_buffer_rsrc_t rWt = make_rsrc((const char *)t.W[mat] + tbase * kWS, tile_el * kWS);
+    const __amdgpu_buffer_rsrc_t rUt = make_rsrc(U ? (const void *)(U + tbase) : t.W[mat], U ? tile_el * 4 : 0);
+    const unsigned rbase = (unsigned)((32 * rt + 4 * (lane >> 5)) * n);   // row offset of r = 0
+    const unsigned r8 = (unsigned)(8 * n);
+    auto col_off = [&](int j) -> unsigned {
+        const int col = 32 * (cg + 2 * j) + (lane & 31);
+        return cg + 2 * j < nct && col < nb ? rbase + (unsigned)col : kOff;
+    };
+    // element offset of register r of a chunk whose row-0 offset is c0 (kOff stays kOff)
+    auto el = [&](unsigned c0, int r) -> unsigned {
+        return c0 == kOff ? kOff : c0 + (unsigned)(r >> 2) * r8 + (unsigned)(r & 3) * (unsigned)n;
+    };
+    using WEl = typename std::conditional<WBF16, uint16_t, float>::type;
+    WEl wv[2][16];
+    auto load_w = [&](int j, WEl (&d)[16]) {
+        const unsigned c0 = col_off(j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (WBF16) d[r] = bload1h(rWt, boff(el(c0, r), 2));
+            else d[r] = bload1(rWt, boff(el(c0, r), 4));
+        }
+    };
+    load_w(0, wv[0]);
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+        if (j + 1 < NCW) load_w(j + 1, wv[(j + 1) & 1]);
+        const unsigned c0 = col_off(j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const unsigned o = el(c0, r);
+            float w0;
+            if constexpr (WBF16) w0 = bf16_to_f32(wv[j & 1][r]);
+            else w0 = wv[j & 1][r];
+            const float u = acc[j][r];
+            const float nw = w0 - lr * __builtin_fmaf(sc, u, wd * w0);
+            if (U) bstore1(u, rUt, boff(o, 4));
+            if constexpr (WBF16) bstore1h(f32_to_bf16(nw), rWt, boff(o, 2));
+            else bstore1(nw, rWt, boff(o, 4));
+        }
+    }
+}
+
 // One 128-row tile per workgroup: the workgroups of a block are then as many as its tiles and run
 // together on one XCD, sharing its basis slices in L2.
 int64_t wide_tpg(int64_t, int64_t) { return 1; }
@@ -731,6 +1030,47 @@ hipError_t launch_wide_cfg(const StepArgs &a, int c0, int cnt, int ldp, hipStrea
         if (a.w_dtype == DOBB_BF16) DOBB_RWIDE(true); else DOBB_RWIDE(false);
 #undef DOBB_RWIDE
     }
+    return hipGetLastError();
+}
+
+// The one-pass sign step: the basis planes, then one workgroup per 128-row tile of every block.
+template <int NCW>
+hipError_t launch_wide_fused_cfg(const StepArgs &a, int c0, int cnt, hipStream_t s) {
+    const int64_t m = a.sh.m, n = a.sh.n;
+    const int nb = (int)a.sh.nb;
+    const int nblk = (int)(n / nb);
+    const WideGeo geo = wide_geo(nb);
+    {
+        SplitWideTable t{};
+        for (int i = 0; i < cnt; ++i) { t.Q[i] = a.Q[c0 + i]; t.planes[i] = a.planes[c0 + i]; }
+        DOBB_LAUNCH("split_q", s, k_split_wide, dim3((unsigned)geo.KS, (unsigned)(nblk * cnt)), dim3(256), 0, nb, nblk, t);
+    }
+    const int ntile = (int)((m + kTR - 1) / kTR);
+    const dim3 grid((unsigned)((int64_t)ntile * nblk * cnt));
+    FusedWideTable t{};
+    for (int i = 0; i < cnt; ++i) {
+        const dobb_hparams &h = a.hp[c0 + i];
+        t.M[i] = a.M[c0 + i]; t.G[i] = a.G[c0 + i]; t.planes[i] = a.planes[c0 + i]; t.W[i] = a.W[c0 + i];
+        t.U[i] = a.U ? a.U[c0 + i] : nullptr;
+        t.mu[i] = h.momentum; t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
+    }
+    const size_t sh = fused_wide_lds(nb);
+    const bool gbf = a.g_dtype == DOBB_BF16, wbf = a.w_dtype == DOBB_BF16;
+    const bool nest = a.hp[c0].nesterov != 0;
+#define DOBB_WF(NE, GB, WB)                                                                                      \
+    do {                                                                                                         \
+        (void)hipFuncSetAttribute((const void *)k_step_wide_fused<NCW, NE, GB, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
+        DOBB_LAUNCH("step_wide_fused_f16", s, (k_step_wide_fused<NCW, NE, GB, WB>), grid, dim3(kWT), sh, m, n, nb, nblk, \
+                    ntile, t);                                                                                   \
+    } while (0)
+    if (!nest) {
+        if (gbf) { if (wbf) DOBB_WF(0, true, true); else DOBB_WF(0, true, false); }
+        else { if (wbf) DOBB_WF(0, false, true); else DOBB_WF(0, false, false); }
+    } else {
+        if (gbf) { if (wbf) DOBB_WF(1, true, true); else DOBB_WF(1, true, false); }
+        else { if (wbf) DOBB_WF(1, false, true); else DOBB_WF(1, false, false); }
+    }
+#undef DOBB_WF
     return hipGetLastError();
 }
 
@@ -837,6 +1177,22 @@ hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {
     for (int c0 = 0; c0 < a.count;) {
         const int cnt = a.count - c0 < kMaxMats ? a.count - c0 : kMaxMats;
         hipError_t e;
+        // the one-pass kernel unless the coefficients are asked for (the two-kernel path writes them)
+        bool co = false;
+        for (int i = 0; i < cnt; ++i) co = co || (a.Cout && a.Cout[c0 + i]);
+        if (!co && (int64_t)fused_wide_lds((int)a.sh.nb) <= max_lds_bytes()) {
+            switch ((nct + 1) / 2) {
+                case 3: e = launch_wide_fused_cfg<3>(a, c0, cnt, s); break;
+                case 4: e = launch_wide_fused_cfg<4>(a, c0, cnt, s); break;
+                case 5: e = launch_wide_fused_cfg<5>(a, c0, cnt, s); break;
+                case 6: e = launch_wide_fused_cfg<6>(a, c0, cnt, s); break;
+                case 7: e = launch_wide_fused_cfg<7>(a, c0, cnt, s); break;
+                default: return hipErrorInvalidValue;   // see step_wide_eligible
+            }
+            if (e != hipSuccess) return e;
+            c0 += cnt;
+            continue;
+        }
         switch (nct) {
             case 5: e = launch_wide_cfg<5>(a, c0, cnt, ldp, s); break;
             case 6: e = launch_wide_cfg<6>(a, c0, cnt, ldp, s); break;

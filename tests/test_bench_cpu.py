@@ -20,24 +20,21 @@ def test_work_model_gpt2xl_totals():
     assert P == 1_474_560_000
     w = bench.kernel_work(specs, 16384)
     # projection and reconstruction: 2 m n nb flops each, 4 m n nb together = 1.180e12 for this set
-    gemm = w["project_f16x3"]["flops"] + w["reconstruct_f16x2"]["flops"] + w["step_fused_f16"]["flops"]
+    gemm = w["step_wide_fused_f16"]["flops"] + w["step_fused_f16"]["flops"]
     assert gemm == pytest.approx(1.17965e12, rel=1e-4)
-    # the split products actually issued: three fp16 products to project, two to reconstruct, five in
-    # the one-pass kernel (the nb = 100 weights), whose blocks are padded to 112 basis rows and a
-    # contraction 128 deep
-    assert w["project_f16x3"]["issued"] == 3 * w["project_f16x3"]["flops"]
-    assert w["reconstruct_f16x2"]["issued"] == 2 * w["reconstruct_f16x2"]["flops"]
+    # the split products actually issued: five fp16 products in each one-pass kernel, the nb = 100
+    # blocks padded to 112 basis rows and a contraction 128 deep, the nb = 400 blocks to 416 rows and
+    # a contraction 400 deep
     assert w["step_fused_f16"]["issued"] == pytest.approx(2.5 * w["step_fused_f16"]["flops"] * 112 * 128 / 100 ** 2)
+    assert w["step_wide_fused_f16"]["issued"] == pytest.approx(2.5 * w["step_wide_fused_f16"]["flops"] * 416 / 400)
     # the method's bytes: M read + written, G read (12 B per parameter with fp32 G); W read + written
-    # (8 B per parameter with fp32 W): together the step's 20 B per parameter.  The sign byte written
-    # by the projection and read by the reconstruction is this implementation's traffic, apart; the
-    # one-pass kernel has none.
+    # (8 B per parameter with fp32 W): together the step's 20 B per parameter, with no sign bytes in
+    # either one-pass kernel
     P_wide = 48 * 1600 * 6400
-    assert w["project_f16x3"]["bytes"] == 12 * P_wide
-    assert w["reconstruct_f16x2"]["bytes"] == 8 * P_wide
+    assert w["step_wide_fused_f16"]["bytes"] == 20 * P_wide
     assert w["step_fused_f16"]["bytes"] == 20 * (P - P_wide)
-    assert w["project_f16x3"]["impl_bytes"] == P_wide and w["reconstruct_f16x2"]["impl_bytes"] == P_wide
-    assert w["step_fused_f16"]["impl_bytes"] == 0
+    assert w["step_fused_f16"]["impl_bytes"] == 0 and w["step_wide_fused_f16"]["impl_bytes"] == 0
+    assert "project_f16x3" not in w and "reconstruct_f16x2" not in w
     # capture: bf16 activations of 16384 tokens for all 192 weights, 17.6 GB read once
     x_bytes = w["accumulate_syrk_bf16"]["bytes"] + w["accumulate_syrk_wide"]["bytes"]
     assert x_bytes == pytest.approx(17.6e9, rel=2e-3)
@@ -48,7 +45,7 @@ def test_work_model_gpt2xl_totals():
     w2 = bench.kernel_work(specs, 16384, orth_iters=2)
     for k in ("refresh_gemm", "qr_block", "qr_update", "qr_form", "qr_panel"):
         assert w2[k]["flops"] == 2 * w[k]["flops"]
-    assert w2["project_f16x3"] == w["project_f16x3"]
+    assert w2["step_wide_fused_f16"] == w["step_wide_fused_f16"]
 
 
 def test_jacobi_flop_count():

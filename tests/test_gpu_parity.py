@@ -418,6 +418,41 @@ def test_step_column_l2_wide(m, n, nb, wdt, nest):
     assert torch.equal(W2, W_l) and torch.equal(M2, M_l)
 
 
+@pytest.mark.parametrize("m,n,nb,wdt,nest", [(200, 800, 400, torch.float32, False), (257, 800, 400, torch.bfloat16, True),
+                                             (130, 272, 136, torch.float32, False), (1, 416, 416, torch.float32, False),
+                                             (300, 1152, 192, torch.bfloat16, False), (129, 960, 320, torch.float32, True)])
+def test_step_wide_one_pass_kernel(m, n, nb, wdt, nest):
+    """Without a coefficient output, blocks of 128 < nb <= 416 take the one-pass wide kernel (the
+    projection, the signs in LDS, the reconstruction and the update per 128-row tile).  It computes
+    the same products in the same order as the two-kernel path that a C_out request takes, so W, M and
+    U are bitwise equal, and it meets the step's bars against the oracle."""
+    print(f"wide one-pass step m={m} n={n} nb={nb} {wdt} nesterov={nest}", flush=True)
+    Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=3 * m + nb, w_dtype=wdt, g_dtype=wdt, nesterov=nest)
+    W1, M1, U1 = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)                 # one pass
+    W2, M2, U2, C2 = _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN, want_c=True)  # two kernels
+    assert torch.equal(W1, W2) and torch.equal(M1, M2) and torch.equal(U1, U2)
+    W_r, M_r, U_r = oracle.step(W.cpu(), G.cpu(), M.cpu(), Qh, nb, hp["lr"], hp["weight_decay"], hp["momentum"],
+                                hp["update_scale"], nesterov=nest)
+    _check_momentum(M1, M, G, hp["momentum"], M_r)
+    P_r = (G.cpu().double().numpy() + hp["momentum"] * M_r) if nest else M_r
+    U_sh, C_sh = host(U1), host(C2)
+    for b in range(n // nb):
+        sl = slice(b * nb, (b + 1) * nb)
+        C_ref = P_r[:, sl] @ Qh[b]
+        assert np.linalg.norm(C_sh[:, sl] - C_ref) <= 1e-5 * np.linalg.norm(C_ref)
+        S_gpu = np.rint(U_sh[:, sl] @ Qh[b])
+        live = np.abs(C_ref) > 1e-5 * np.max(np.abs(C_ref))
+        assert np.all(S_gpu[live] == np.sign(C_ref[live])), "sign mismatch outside the dead zone"
+        R = S_gpu @ Qh[b].T
+        assert np.linalg.norm(U_sh[:, sl] - R) <= 1e-5 * np.linalg.norm(R)
+    assert np.mean(np.abs(U_sh - U_r) > 1e-3) <= 1e-3
+    check_w(host(W1), host(W), U_sh, hp, bf16=wdt == torch.bfloat16)
+    # without U_out as well (the benchmark's launch)
+    W3, M3 = W.clone(), M.clone()
+    dobb.dobb_step(W3, G, M3, Q, nb, dobb.make_hparams(norm=dobb.DOBB_NORM_SIGN, **hp))
+    assert torch.equal(W3, W1) and torch.equal(M3, M1)
+
+
 def test_step_nesterov_and_column_l2():
     m, n, nb = 96, 128, 64
     Q, Qh, W, G, M, hp = _step_case(m, n, nb, seed=21, nesterov=True)
@@ -554,13 +589,15 @@ def test_grouped_equals_single_calls():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("nb,names", [(64, ("step_fused",)), (192, ("project", "reconstruct"))])
-def test_profiler_reports_kernels(nb, names):
-    # blocks up to 128 wide take the one-pass kernel; wider ones the projection and reconstruction pair
+@pytest.mark.parametrize("nb,want_c,names", [(64, False, ("step_fused",)), (192, False, ("split_q", "step_wide_fused")),
+                                              (192, True, ("project", "reconstruct"))])
+def test_profiler_reports_kernels(nb, want_c, names):
+    # without a coefficient output, blocks up to 416 wide take a one-pass kernel; with one, blocks
+    # wider than 128 take the projection and reconstruction pair
     dobb.dobb_profile_reset()
     dobb.dobb_profile_enable(True)
     Q, Qh, W, G, M, hp = _step_case(128, 2 * nb, nb, seed=71)
-    _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN)
+    _run_step(W, G, M, Q, nb, hp, dobb.DOBB_NORM_SIGN, want_c=want_c)
     torch.cuda.synchronize()
     dobb.dobb_profile_enable(False)
     rep = dobb.dobb_profile_read()
