@@ -28,6 +28,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 from __future__ import annotations
 
 import argparse
+import collections
 import json
 import os
 import re
@@ -113,6 +114,30 @@ def parse():
     return ap.parse_args()
 
 
+def capture_splits(n, nb, count, n_tokens, bf16):
+    """Token splits of one capture launch group (count weights of width n, blocks of nb), as the
+    library plans them: bf16 blocks 128 < nb <= 512 (nb % 8 == 0) take the wide kernel, whose splits
+    hold at most 4096 tokens and give about 1024 workgroups of 8 waves (one per 8 groups of 2 x 4
+    tiles of 32 x 32 over the upper triangle); the others split until about 512 (bf16) or 1024 (fp32)
+    tile pairs of 128 or 64 columns, at least 256 tokens each."""
+    cnt = min(count, 48)
+    B = n // nb
+    if bf16 and 128 < nb <= 512 and nb % 8 == 0:
+        t32 = -(-nb // 32)
+        groups = sum(len(range(r, t32, 4)) for r in range(0, t32, 2))
+        wgtot = -(-groups // 8) * B * cnt
+        ns = min(-(-1024 // wgtot), n_tokens // 256)
+        ns = max(ns, -(-n_tokens // 4096), 1)
+        length = -(-(-(-n_tokens // ns)) // 64) * 64
+        return -(-n_tokens // length)
+    tile = 128 if bf16 else 64
+    T = -(-nb // tile)
+    tiles = T * (T + 1) // 2 * B * cnt
+    ns = max(min(-(-(512 if bf16 else 1024) // tiles), n_tokens // 256, 64), 1)
+    length = -(-(-(-n_tokens // ns)) // 64) * 64
+    return -(-n_tokens // length)
+
+
 def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1, x_bytes=2, qr="householder"):
     """Per-step work of each kernel of the path, summed over the matrix set.
 
@@ -122,7 +147,9 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
       accumulate_syrk_*     X read once: 2 N n bytes; N nb (nb + 1) B flops (unique entries of X_b^T X_b);
                             "wide" for bf16 blocks 128 < nb <= 512, nb % 8 == 0; fp32 activations
                             (x_bytes = 4): accumulate_syrk, 4 N n bytes, fp32 MFMA
-      accumulate_reduce     A read + written: 8 nb^2 B bytes
+      accumulate_reduce     A read + written: 8 nb^2 B bytes, where the capture splits its tokens over
+                            workgroups (capture_splits); otherwise the EMA is in the capture kernel
+                            and these bytes are its own
       refresh_gemm          Z = A Q: 2 nb^3 B flops (fp32); A, Q read, Z written: 12 nb^2 B bytes
       qr_block              nb <= 128, the whole Householder QR in one launch: 8/3 nb^3 B flops
       qr_update / qr_form   nb > 128, factor updates (a launch per panel) / formation (one launch for
@@ -170,14 +197,19 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
                                     issued_peak=issued_peak, compute=compute, impl_bytes=0.0))
         e["bytes"] += nbytes; e["flops"] += flops; e["issued"] += issued; e["impl_bytes"] += impl
 
+    shapes = collections.Counter((s.n, s.nb) for s in specs)
     for s in specs:
         B, nb, mn = s.n // s.nb, s.nb, s.m * s.n
+        split = capture_splits(s.n, nb, shapes[(s.n, s.nb)], n_tokens, x_bytes == 2) > 1
         if x_bytes == 4:
-            add("accumulate_syrk", 4.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_FP32_MFMA)
+            add("accumulate_syrk", 4.0 * n_tokens * s.n + (0.0 if split else 8.0 * nb * nb * B),
+                n_tokens * nb * (nb + 1) * B, PEAK_FP32_MFMA)
         else:
             syrk = "accumulate_syrk_wide" if 128 < nb <= 512 and nb % 8 == 0 else "accumulate_syrk_bf16"
-            add(syrk, 2.0 * n_tokens * s.n, n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
-        add("accumulate_reduce", 8.0 * nb * nb * B)
+            add(syrk, 2.0 * n_tokens * s.n + (0.0 if split else 8.0 * nb * nb * B),
+                n_tokens * nb * (nb + 1) * B, PEAK_BF16_MFMA)
+        if split:
+            add("accumulate_reduce", 8.0 * nb * nb * B)
         k = orth_iters
         if qr == "cholesky":
             add("refresh_gemm", k * 5 * 12.0 * nb * nb * B, k * 10.0 * nb ** 3 * B)

@@ -303,11 +303,15 @@ __global__ void __launch_bounds__(512) k_syrk_bf16(int64_t N, int nb, int T, int
 // A chunk is loaded into registers (8 tokens x 8 columns per thread), transposed 8 x 8 on the way
 // into LDS ([column][token], 16-byte slots swizzled against bank conflicts), double buffered.
 // The sums stay fp32 over a split of at most 4096 tokens (256 MFMA steps); splits are added in fp64
-// by k_syrk_reduce<float> in split order.
+// by k_syrk_reduce<float> in split order.  The diagonal entries are sums of squares, every term
+// positive, and would collect the largest fp32 rounding error that way (about 5e-7 of max|A_b| at
+// 4096 tokens): the waves whose group holds the two diagonal tiles move them into fp64 registers
+// every kWFold chunks (fp32 runs of 16 MFMA steps), one entry per lane and tile.
 constexpr int kWK = 64;          // tokens per LDS chunk
 constexpr int kWMaxGroups = 32;  // 2 x 4 tile groups for up to 16 tile rows (20 needed)
 constexpr int64_t kWSplitMax = 4096;
 constexpr unsigned kWOff = 0xffffffffu;   // buffer offset past the end: the load returns zeros
+constexpr int kWFold = 4;        // chunks between moves of the diagonal entries into fp64
 
 struct WideGroups {
     uint8_t r0[kWMaxGroups], c0[kWMaxGroups];
@@ -374,8 +378,29 @@ __global__ void __launch_bounds__(512) k_syrk_wide(int64_t N, int nb, int T32, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) bcol[j] = 32 * (C0 + j < T32 ? C0 + j : 0) + (lane & 31);
 
+    // a diagonal group (C0 == R0) holds tiles (R0, R0) and (R0 + 1, R0 + 1) at acc[0][0] and acc[1][1];
+    // lane l has the diagonal entry of each in register rd (when 8 (rd / 4) + rd % 4 =
+    // l % 32 - 4 (l / 32) has a solution), and keeps its fp64 sums in dg[]
+    const bool dgroup = active && C0 == R0;
+    const int dt = (lane & 31) - 4 * (lane >> 5);
+    const int rd = (dt >= 0 && (dt & 7) < 4) ? 4 * (dt >> 3) + (dt & 7) : -1;
+    double dg[2] = {0.0, 0.0};
+    auto fold_diag = [&]() {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                v = r == rd ? acc[k][k][r] : v;
+                acc[k][k][r] = r == rd ? 0.f : acc[k][k][r];
+            }
+            dg[k] += (double)v;
+        }
+    };
+
     if (tb < te) gload(tb);
     int cur = 0;
+    int chunk = 0;
     for (int64_t t0 = tb; t0 < te; t0 += kWK) {
         uint16_t *xs = xw + (size_t)cur * nbp * kWK;
         if (loader) {
@@ -409,8 +434,13 @@ __global__ void __launch_bounds__(512) k_syrk_wide(int64_t N, int nb, int T32, i
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
             }
         }
+        if (dgroup && ++chunk == kWFold) {
+            fold_diag();
+            chunk = 0;
+        }
         cur ^= 1;
     }
+    if (dgroup) fold_diag();
     if (!active) return;
 
     const int64_t tot_blocks = (int64_t)nblk * (gridDim.x / (wgs * nblk));
@@ -427,11 +457,13 @@ __global__ void __launch_bounds__(512) k_syrk_wide(int64_t N, int nb, int T32, i
             for (int r = 0; r < 16; ++r) {
                 const int gi = 32 * (R0 + i) + acc_row(r, lane);
                 if (gi >= nb || gj >= nb || gi > gj) continue;
+                // the diagonal entries of a diagonal group are all in dg (acc holds 0 there)
+                const double sum = (dgroup && i == j && r == rd) ? dg[i] : (double)acc[i][j][r];
                 if (Pb) {
-                    Pb[(int64_t)gi * nb + gj] = acc[i][j][r];
+                    Pb[(int64_t)gi * nb + gj] = (float)sum;
                 } else {
                     const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
-                    const float v = (float)(bd * old + (1.0 - bd) * ((double)acc[i][j][r] * invN));
+                    const float v = (float)(bd * old + (1.0 - bd) * (sum * invN));
                     Ab[(int64_t)gi * nb + gj] = v;
                     Ab[(int64_t)gj * nb + gi] = v;
                 }
@@ -519,7 +551,9 @@ int accumulate_plan(const dobb_shape &sh, int64_t N, int count, int64_t *tps, bo
     const int tile = bf16 ? kST : kBM;
     const int T = (nb + tile - 1) / tile;
     const int64_t tiles = (int64_t)T * (T + 1) / 2 * (sh.n / nb) * (count < kMaxMats ? count : kMaxMats);
-    int64_t nsplit = (1024 + tiles - 1) / tiles;
+    // bf16: 512 tile pairs already fill the chip (the fp64 fold makes a split unnecessary for accuracy)
+    const int64_t target = bf16 ? 512 : 1024;
+    int64_t nsplit = (target + tiles - 1) / tiles;
     const int64_t cap = N / 256;
     if (nsplit > cap) nsplit = cap;
     if (nsplit < 1) nsplit = 1;

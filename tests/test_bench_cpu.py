@@ -35,9 +35,16 @@ def test_work_model_gpt2xl_totals():
     assert w["step_fused_f16"]["bytes"] == 20 * (P - P_wide)
     assert w["step_fused_f16"]["impl_bytes"] == 0 and w["step_wide_fused_f16"]["impl_bytes"] == 0
     assert "project_f16x3" not in w and "reconstruct_f16x2" not in w
-    # capture: bf16 activations of 16384 tokens for all 192 weights, 17.6 GB read once
-    x_bytes = w["accumulate_syrk_bf16"]["bytes"] + w["accumulate_syrk_wide"]["bytes"]
+    # capture: bf16 activations of 16384 tokens for all 192 weights, 17.6 GB read once.  The nb = 100
+    # launches (768 tile pairs each) run unsplit, so the EMA's A read + write is theirs; the wide
+    # nb = 400 launch splits its tokens four ways (fp32 sums of at most 4096 tokens), and the reduce
+    # kernel reads and writes A for it
+    A_100 = 8.0 * 100 * 100 * 16 * 144
+    x_bytes = w["accumulate_syrk_bf16"]["bytes"] - A_100 + w["accumulate_syrk_wide"]["bytes"]
     assert x_bytes == pytest.approx(17.6e9, rel=2e-3)
+    assert bench.capture_splits(1600, 100, 48, 16384, True) == 1
+    assert bench.capture_splits(6400, 400, 48, 16384, True) == 4
+    assert w["accumulate_reduce"]["bytes"] == 8.0 * 400 * 400 * 16 * 48
     # only the nb = 400 weights (fc-proj) take the wide capture kernel and the split basis planes
     assert w["accumulate_syrk_wide"]["bytes"] == 2 * 16384 * 6400 * 48
     assert w["split_q"]["bytes"] == 14 * 400 * 400 * 16 * 48
