@@ -294,7 +294,8 @@ __global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float 
     const int npanel = (nb + kPW - 1) / kPW;
     const float *Zg = Z_all + (int64_t)g * nb * nb;
     float *Tq = Tq_all + (int64_t)g * npanel * kPW * kPW;
-    for (int64_t e = tid; e < (int64_t)nb * nb; e += kQT) Z[(e / nb) * ldz + e % nb] = Zg[e];
+    for (int r = wv; r < nb; r += kQT / 64)
+        for (int c = lane; c < nb; c += 64) Z[r * ldz + c] = Zg[(int64_t)r * nb + c];
     __syncthreads();
 
     for (int p = 0; p < npanel; ++p) {
@@ -329,8 +330,12 @@ __global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float 
         __syncthreads();
     }
 
-    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
-    for (int64_t e = tid; e < (int64_t)nb * nb; e += kQT) Q[e] = (e / nb == e % nb) ? 1.f : 0.f;
+    // Q formed in place over Z (as LAPACK's orgqr does): panels last to first.  When panel p comes,
+    // columns >= j0 + w already hold Q's columns as the later panels left them (their rows < j0 + w
+    // untouched so far), columns j0 .. j0 + w - 1 still hold V_p, and columns < j0 the earlier V.
+    // V_p goes to Vs, its columns restart as identity columns, the R entries in rows j0 .. j0 + w - 1
+    // right of the panel become the zeros Q has there before H_p, and H_p = I - V_p T_p V_p^T is
+    // applied to rows and columns >= j0.
     for (int p = npanel - 1; p >= 0; --p) {
         const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
         for (int e = tid; e < rows * kPW; e += kQT) {
@@ -338,14 +343,26 @@ __global__ void __launch_bounds__(256) k_qr_block(int nb, int nblk, const float 
             Vs[r][c] = c < w ? Z[(int64_t)(j0 + r) * ldz + j0 + c] : 0.f;
         }
         for (int e = tid; e < kPW * kPW; e += kQT) Ts[e / kPW][e % kPW] = Tq[(int64_t)p * kPW * kPW + e];
+        __syncthreads();   // V_p staged: its columns can be overwritten
+        for (int e = tid; e < nb * w; e += kQT) {   // the panel's columns: identity columns
+            const int r = e / w, c = e - r * w;
+            Z[r * ldz + j0 + c] = r == j0 + c ? 1.f : 0.f;
+        }
+        for (int e = tid; e < w * (nb - j0 - w); e += kQT) {   // its rows right of the panel: zero
+            const int r = e / (nb - j0 - w), c = e - r * (nb - j0 - w);
+            Z[(j0 + r) * ldz + j0 + w + c] = 0.f;
+        }
         __syncthreads();
         const int ntiles = (nb - j0 + 31) / 32;
         for (int tile = wv; tile < ntiles; tile += 4) {
-            if (p == 0) wy_wave<false, true>(Q, nb, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
-            else wy_wave<false, false>(Q, nb, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
+            if (p == 0) wy_wave<false, true>(Z, ldz, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
+            else wy_wave<false, false>(Z, ldz, nb, j0, rows, j0 + 32 * tile, Vs, Ts, Wsc[wv], neg, lane);
         }
         __syncthreads();
     }
+    float *Q = t.Q[mat] + (int64_t)b * nb * nb;
+    for (int r = wv; r < nb; r += kQT / 64)
+        for (int c = lane; c < nb; c += 64) Q[(int64_t)r * nb + c] = Z[r * ldz + c];
     if (tid == 0 && info_value > 0 && t.info[mat]) t.info[mat][b] = info_value;
 }
 
