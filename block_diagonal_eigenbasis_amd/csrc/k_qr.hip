@@ -578,14 +578,14 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
 // ---- nb > 128: formation of Q in one launch ---------------------------------------------------------
 // A workgroup owns a 64-column tile of Q_b over all nb rows and keeps it in registers (accumulator
 // layout, as in k_qr_apply) from the identity to the final store.  Its 8 waves split the tile into
-// two column halves by four row parts, so a wave holds at most 4 x 32 rows and two waves share each
+// two column halves by four row sets, so a wave holds at most 4 x 32 rows and two waves share each
 // SIMD.  It applies the block reflectors
 // I - V_p T_p V_p^T for p = min(npanel - 1, last column / 32) down to 0 (panels starting past the
 // tile's last column leave its identity columns unchanged), each with V_p and T_p staged in LDS, and
-// stores the tile once with the columns whose R_cc < 0 negated.  Wave (kp, h): column half h, rows
-// [kp part, (kp + 1) part) with part = 32 ceil(nb / 128); 32-row chunks lying wholly above a panel's
-// first row are skipped (V = 0).
-// grid = (ceil(nb / 64) tiles, blocks), block 512.  CH = part / 32.
+// stores the tile once with the columns whose R_cc < 0 negated.  Wave (kp, h): column half h, the
+// 32-row chunks kp, kp + 4, kp + 8, ... (interleaved, so that the chunks a panel touches stay spread
+// over the waves); chunks lying wholly above a panel's first row are skipped (V = 0).
+// grid = (ceil(nb / 64) tiles, blocks), block 512.  CH = ceil(ceil(nb / 32) / 4).
 constexpr int kFP = 4;                 // formation: row parts
 constexpr int kFT = 2 * 64 * kFP;      // formation: threads per workgroup
 __host__ __device__ inline ApplyLds form_lds(int nb) {
@@ -653,9 +653,10 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
     const int c0 = blockIdx.x * 64 + 32 * h;
     const bool colok = c0 + cc < nb;
     const int ccl = colok ? c0 + cc : 0;
-    const int part = ((nb + 32 * kFP - 1) / (32 * kFP)) * 32;
-    const int rb = kp * part, re = rb + part < nb ? rb + part : nb;
-    const unsigned lo = (unsigned)((rb + 4 * kr) * nb + ccl);
+    // this wave's 32-row chunks: 32 (kp + kFP ch), interleaved over the row sets so that the chunks
+    // at or below a panel's first row stay evenly spread as the panels advance
+    auto chunk_row = [&](int ch) { return 32 * (kp + kFP * ch); };
+    const unsigned lo = (unsigned)((32 * kp + 4 * kr) * nb + ccl);
     const unsigned unb = (unsigned)nb;
     // the identity columns of the tile
     f32x16 x[CH];
@@ -663,8 +664,8 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
     for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = rb + 32 * ch + acc_row(r, lane);
-            x[ch][r] = (colok && row < re && row == ccl) ? 1.f : 0.f;
+            const int row = chunk_row(ch) + acc_row(r, lane);
+            x[ch][r] = (colok && row < nb && row == ccl) ? 1.f : 0.f;
         }
     const int plast = (blockIdx.x * 64 + 63) / kPW < npanel - 1 ? (blockIdx.x * 64 + 63) / kPW : npanel - 1;
     // panel p's V rows and T, loaded one panel ahead into registers
@@ -691,8 +692,8 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
         f32x16 acc = {};
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch) {
-            const int r0 = rb + 32 * ch;
-            if (r0 >= re) break;
+            const int r0 = chunk_row(ch);
+            if (r0 >= nb) break;
             if (r0 < j0) continue;
 #pragma unroll
             for (int s2 = 0; s2 < 16; ++s2) {
@@ -723,8 +724,8 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
         // X -= V Y on this wave's chunks at rows >= j0
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch) {
-            const int r0 = rb + 32 * ch;
-            if (r0 >= re) break;
+            const int r0 = chunk_row(ch);
+            if (r0 >= nb) break;
             if (r0 < j0) continue;
             f32x16 u = {};
 #pragma unroll
@@ -739,15 +740,16 @@ __global__ void __launch_bounds__(kFT) k_qr_form(int nb, int nblk, const float *
         const float sgn = neg_all[(int64_t)g * nb + ccl] ? -1.f : 1.f;
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch) {
-            const int r0 = rb + 32 * ch;
-            if (r0 >= re) break;
-            if (r0 + 32 <= re) {
+            const int r0 = chunk_row(ch);
+            if (r0 >= nb) break;
+            const unsigned cb = lo + (unsigned)(32 * kFP * ch) * unb;
+            if (r0 + 32 <= nb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Q[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
+                for (int r = 0; r < 16; ++r) Q[cb + (unsigned)(8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (r0 + acc_row(r, lane) < re) Q[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
+                    if (r0 + acc_row(r, lane) < nb) Q[cb + (unsigned)(8 * (r >> 2) + (r & 3)) * unb] = sgn * x[ch][r];
             }
         }
     }
@@ -791,7 +793,7 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
             DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
                         as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
     }
-    // formation: four row parts of 32 ceil(nb / 128) rows, i.e. CH / 2 chunks
+    // formation: each wave ceil(ceil(nb / 32) / 4) chunks of 32 rows, i.e. CH / 2
     const size_t fs = form_lds(nb).total;
     (void)hipFuncSetAttribute((const void *)k_qr_form<CH / 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fs);
     DOBB_LAUNCH("qr_form", s, (k_qr_form<CH / 2>), dim3((unsigned)((nb + 63) / 64), (unsigned)nblocks), dim3(kFT), fs,
