@@ -8,8 +8,10 @@ for fc-proj).  W, G, M, A and Q are fp32; activations are bf16, 16384 tokens per
 every step: capture (accumulate + EMA) -> basis refresh (warm-started orthogonal iteration, k = 1,
 Householder) -> the Dobb step (momentum, projection, sign, reconstruction, weight update).  The
 first refresh (setup, untimed) is exact.  The headline comes from events around K timed steps with
-the library's kernel timer off; a second pass over K more steps with the timer on (an event pair
-around every launch, on its stream) attributes the time to kernels.  The CPU oracle is timed on a
+the library's kernel timer off, each step a replay of a HIP graph of the step (``--eager``: launched
+from the host instead; both times are in the breakdown); a second pass over K more steps, launched
+from the host with the timer on (an event pair around every launch, on its stream), attributes the
+time to kernels.  The CPU oracle is timed on a
 bounded sample, threaded over the host's cores.
 
 The default workload is the GPT-2 XL set.  ``--workload gpt2small`` runs the GPT-2 Small set (12 layers x
@@ -18,7 +20,7 @@ The default workload is the GPT-2 XL set.  ``--workload gpt2small`` runs the GPT
 11008x4096, down 4096x11008}, nb = 128, bf16 W and G, fp32 M, A and Q; the pages give no token count
 for it, so a capture here is 4096 tokens).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--layers L] [--copy-mib C]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--layers L] [--copy-mib C] [--eager]
                        [--workload gpt2xl|gpt2small|llama7b|single768_b4|single768_b1]
        python bench.py --pmc-summary FETCH_CSV WRITE_CSV [--copy-mib C]
        python bench.py --mfma-summary COUNTER_CSV
@@ -85,6 +87,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host each step instead of replaying a HIP graph of the step")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2xl")
     ap.add_argument("--layers", type=int, default=0, help="layers of the matrix set (default: all)")
     ap.add_argument("--norm", choices=["sign", "col_l2"], default="sign",
@@ -619,6 +623,19 @@ def main():
     for _ in range(args.warmup):
         full_step()
     torch.cuda.synchronize()
+    # the step as a HIP graph (the same kernels on the same buffers, without the host launch work and
+    # the gaps between launches), and the non-refresh step likewise
+    if args.eager:
+        step_fn, nonrefresh_fn = full_step, group.step
+    else:
+        graph_full = group.capture_refresh_step(xs, beta, REFRESH_MODE, K_ORTH)
+        graph_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_step):
+            group.step()
+        step_fn, nonrefresh_fn = graph_full.replay, graph_step.replay
+        step_fn()
+        nonrefresh_fn()
+        torch.cuda.synchronize()
 
     # ---- timed region: K whole steps, kernel timer off -------------------------------------------
     stream = torch.cuda.current_stream()
@@ -626,7 +643,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        full_step()
+        step_fn()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
@@ -659,8 +676,9 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
     reps = max(3, args.steps)
-    full_ms_untimed = timed(full_step, reps)
-    step_ms = timed(group.step, reps)
+    full_ms_untimed = timed(step_fn, reps)
+    full_ms_eager = timed(full_step, reps)
+    step_ms = timed(nonrefresh_fn, reps)
     acc_ms = timed(lambda: group.accumulate(xs, beta), reps)
     ref_ms = timed(lambda: group.refresh(REFRESH_MODE, K_ORTH), reps)
     # the exact refresh warm-started from the current basis (the exact mode's steady state)
@@ -719,11 +737,13 @@ def main():
                                + ("; column-l2 normalisation" if col_l2 else "")
                                + ("; bf16 basis" if args.basis == "bf16" else ""),
                    "matrices": len(specs), "params": workload.param_count(specs), "tokens": n_tokens,
-                   "refresh_period": 1, "streams": args.streams, "basis": args.basis, "qr": args.qr},
+                   "refresh_period": 1, "streams": args.streams, "basis": args.basis, "qr": args.qr,
+                   "launch": "eager" if args.eager else "hip graph"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown_ms": {"full_step_kernel_timer_on": round(ms_per_step_timer, 3),
                          "full_step_again": round(full_ms_untimed, 3),
+                         "full_step_eager": round(full_ms_eager, 3),
                          f"full_step_{other}_stream{'s' if other > 1 else ''}":
                              None if other_ms is None else round(other_ms, 3),
                          "step_nonrefresh": round(step_ms, 3),

@@ -277,6 +277,23 @@ class DobbGroup:
         self._run(stream, go)
         self.refreshes += 1
 
+    def capture_refresh_step(self, xs, beta: float, mode: int, iters: int, grads=None,
+                             warm_start: bool = True) -> "torch.cuda.CUDAGraph":
+        """A HIP graph of refresh_step(xs, beta, mode, iters, grads): replaying it runs the same
+        kernels on the same buffers without the per-launch host work and gaps.  xs, the gradients and
+        the optimizer state are bound by address, so the caller refills them in place between replays.
+        Capturing runs nothing; the workspaces must already have their size, so call refresh_step once
+        (or accumulate with the same token counts) first.  Each replay counts as one refresh."""
+        N = max(x.shape[0] for x in xs)
+        if N > self.n_tokens:
+            raise RuntimeError("call refresh_step once before capturing it (the workspaces are sized there)")
+        graph = torch.cuda.CUDAGraph()
+        refreshes = self.refreshes
+        with torch.cuda.graph(graph):
+            self.refresh_step(xs, beta, mode, iters, grads=grads, warm_start=warm_start)
+        self.refreshes = refreshes
+        return graph
+
 
 class Dobb(torch.optim.Optimizer):
     """torch.optim interface: 2-D parameters only, each with a block size (default: n // blocks).

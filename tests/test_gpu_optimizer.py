@@ -309,3 +309,35 @@ def test_dobb_g_optimizer_captures_output_gradients():
         assert g.A[i].shape == (2, nbs[i], nbs[i])
         assert torch.equal(params[i].detach(), W_ref[i]), f"W[{i}]"
         assert torch.equal(g.A[i], A_ref[i]) and torch.equal(g.Q[i], P_ref[i]), f"state {i}"
+
+
+@pytest.mark.parametrize("streams", [1, 2])
+def test_graph_replay_matches_eager_steps(streams):
+    """refresh_step captured into a HIP graph: each replay, with eager work and synchronisations
+    between the replays, leaves W, M, A and Q bitwise equal to a twin group stepped eagerly."""
+    print(f"graph replay: streams={streams}", flush=True)
+    rng = RNG(97)
+    N = 512
+    Ws = [t32(0.02 * rng.standard_normal((m, n))) for m, n, _ in SHAPES]
+    Gs = [t32(rng.standard_normal((m, n))) for m, n, _ in SHAPES]
+    xs = [t32(workload.activations(N, n, 0.15, rng)).to(torch.bfloat16) for _, n, _ in SHAPES]
+    eager, graphed = [DobbGroup([w.clone() for w in Ws], [nb for _, _, nb in SHAPES], grads=Gs, n_tokens=N,
+                                weight_decay=0.1, momentum=0.9, streams=streams) for _ in range(2)]
+    for g in (eager, graphed):
+        g.accumulate(xs, 0.0)
+        g.refresh(dobb.DOBB_REFRESH_EXACT, 0, warm_start=False)
+        g.refresh_step(xs, 0.9, dobb.DOBB_REFRESH_ORTH_ITER, 1)
+    graph = graphed.capture_refresh_step(xs, 0.9, dobb.DOBB_REFRESH_ORTH_ITER, 1)
+    torch.cuda.synchronize()
+    for g1, g2 in ((eager.W, graphed.W), (eager.A, graphed.A)):   # capturing ran nothing
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+    for it in range(4):
+        eager.refresh_step(xs, 0.9, dobb.DOBB_REFRESH_ORTH_ITER, 1)
+        graph.replay()
+        noise = torch.randn(4096, device=DEV)          # eager work between the replays
+        assert torch.isfinite(noise.sum()).item()
+        torch.cuda.synchronize()
+        for name in ("W", "M", "A", "Q"):
+            for i, (a, b) in enumerate(zip(getattr(eager, name), getattr(graphed, name))):
+                assert torch.equal(a, b), (it, name, i)
