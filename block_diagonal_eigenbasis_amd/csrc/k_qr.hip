@@ -457,9 +457,14 @@ __host__ __device__ inline ApplyLds apply_lds(int nb) {
     return L;
 }
 
-template <int CH, bool FACTOR, bool FLIP>
+// TWO (factoring only): apply panel p's block reflector and then panel p + 1's to the columns from
+// 32 (p + 2) on, reading and writing the tile once for both; the columns of panel p + 1 get panel
+// p's reflector alone, from a launch limited by cend (columns from cend on are left alone), before
+// panel p + 1 is factored.  Each column sees the same products in the same order either way.
+template <int CH, bool FACTOR, bool FLIP, bool TWO = false>
 __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const float *Z_all, const float *Tq_all,
-                                                  const int8_t *neg_all, QrBlockOut t, int info_value) {
+                                                  const int8_t *neg_all, QrBlockOut t, int info_value,
+                                                  int cend = 1 << 30) {
     extern __shared__ __align__(16) unsigned char dsm[];
     const ApplyLds L = apply_lds(nb);
     float(*Vs)[kPW + 1] = (float(*)[kPW + 1])(dsm + L.vs);
@@ -474,9 +479,9 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
     const int j0 = p * kPW, w = min(kPW, nb - j0), rows = nb - j0;
     const float *Z = Z_all + (int64_t)g * nb * nb;
     float *X = FACTOR ? (float *)Z_all + (int64_t)g * nb * nb : t.Q[mat] + (int64_t)b * nb * nb;
-    const int first = FACTOR ? j0 + w : j0;
+    const int first = FACTOR ? (TWO ? j0 + 2 * kPW : j0 + w) : j0;
     const int c0 = first + blockIdx.x * 64 + 32 * h;
-    const bool colok = c0 + cc < nb;
+    const bool colok = c0 + cc < nb && c0 + cc < cend;
     const int ccl = colok ? c0 + cc : 0;
     // rows of this wave: [rb, re), at most CH chunks of 32
     const int half = ((rows + 63) / 64) * 32;
@@ -545,7 +550,7 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
     float yb[kPW / 2];   // B operands of the V Y products, the same for every chunk
 #pragma unroll
     for (int kk = 0; kk < kPW; kk += 2) yb[kk / 2] = Wp[kp][h][kk + kr][cc];
-    // X -= V Y on this wave's rows
+    // X -= V Y on this wave's rows (kept in registers when panel p + 1 follows)
     const float sgn = (FLIP && colok && neg_all[(int64_t)g * nb + ccl]) ? -1.f : 1.f;
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
@@ -555,19 +560,83 @@ __global__ void __launch_bounds__(256) k_qr_apply(int nb, int nblk, int p, const
 #pragma unroll
         for (int kk = 0; kk < kPW; kk += 2)
             u = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[r0 + cc][kk + kr], yb[kk / 2], u, 0, 0, 0);
-        if (!colok) continue;
-        if (r0 + 32 <= re) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = x[ch][r] - u[r];
-                Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = FLIP ? sgn * v : v;
+        for (int r = 0; r < 16; ++r) x[ch][r] -= u[r];
+    }
+    if constexpr (TWO) {
+        // panel p + 1: its rows start 32 rows down the tile, so it acts on chunks r0 >= 32
+        const int j1 = j0 + kPW, w1 = min(kPW, nb - j1), rows1 = nb - j1;
+        __syncthreads();   // panel p's readers of Vs, Ts and Wp are done
+        stage_v<CH>(Vs, Z, nb, j1, w1, rows1, tid);
+        {
+            const float *Tq1 = Tq_all + ((int64_t)g * npanel + p + 1) * kPW * kPW;
+            float tv[kPW * kPW / kQT];
+#pragma unroll
+            for (int i = 0; i < kPW * kPW / kQT; ++i) tv[i] = Tq1[tid + kQT * i];
+#pragma unroll
+            for (int i = 0; i < kPW * kPW / kQT; ++i) Ts[(tid + kQT * i) / kPW][(tid + kQT * i) % kPW] = tv[i];
+        }
+        __syncthreads();
+        f32x16 acc1 = {};
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 < kPW) continue;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float a = Vs[r0 - kPW + 8 * (s >> 2) + 4 * kr + (s & 3)][cc];
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x[ch][s], acc1, 0, 0, 0);
             }
-        } else {
+        }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (r0 + acc_row(r, lane) < re) {
-                    const float v = x[ch][r] - u[r];
+        for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = acc1[r];
+        __syncthreads();
+        f32x16 y1 = {};
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2) {
+            const int kx = kk + kr;
+            y1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[kx][cc], Wp[0][h][kx][cc] + Wp[1][h][kx][cc], y1, 0, 0, 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Wp[kp][h][acc_row(r, lane)][acc_col(lane)] = y1[r];
+        wave_sync_lds();
+#pragma unroll
+        for (int kk = 0; kk < kPW; kk += 2) yb[kk / 2] = Wp[kp][h][kk + kr][cc];
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 < kPW) continue;
+            f32x16 u = {};
+#pragma unroll
+            for (int kk = 0; kk < kPW; kk += 2) {
+                const int rr = r0 - kPW + cc;
+                u = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[rr][kk + kr], yb[kk / 2], u, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[ch][r] -= u[r];
+        }
+    }
+    if (colok) {
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int r0 = rb + 32 * ch;
+            if (r0 >= re) break;
+            if (r0 + 32 <= re) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = x[ch][r];
                     Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = FLIP ? sgn * v : v;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (r0 + acc_row(r, lane) < re) {
+                        const float v = x[ch][r];
+                        Xr[lo + (unsigned)(32 * ch + 8 * (r >> 2) + (r & 3)) * unb] = FLIP ? sgn * v : v;
+                    }
                 }
             }
         }
@@ -776,8 +845,10 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
     (void)hipFuncSetAttribute((const void *)k_qr_panel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
     (void)hipFuncSetAttribute((const void *)k_qr_panel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ps);
     (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)as);
+    (void)hipFuncSetAttribute((const void *)k_qr_apply<CH, true, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)as);
     const int npanel = (nb + kPW - 1) / kPW;
-    for (int p = 0; p < npanel; ++p) {
+    auto factor = [&](int p) {
         const int rows = nb - p * kPW;   // rows per thread: ceil(rows / 8), rounded up to a template size
         if (rows <= 64 && RPT > 8)
             DOBB_LAUNCH("qr_panel", s, (k_qr_panel<8>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
@@ -787,11 +858,32 @@ hipError_t launch_panels(int nb, int nblk, int nblocks, float *Z, float *tq, int
             DOBB_LAUNCH("qr_panel", s, (k_qr_panel<32>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
         else
             DOBB_LAUNCH("qr_panel", s, (k_qr_panel<RPT>), dim3((unsigned)nblocks), dim3(kQT), ps, nb, p, Z, tq, negs);
-        const int first = p * kPW + (nb - p * kPW < kPW ? nb - p * kPW : kPW);
-        const int ntiles = (nb - first + 63) / 64;
-        if (ntiles > 0)
-            DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks), dim3(kQT),
-                        as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0);
+    };
+    // panels in pairs: panel p's reflector goes to panel p + 1's columns alone, panel p + 1 is
+    // factored, and both reflectors then go to the remaining columns in one pass (the trailing part
+    // of the block is read and written once per two panels); an odd last panel updates alone
+    for (int p = 0; p < npanel;) {
+        factor(p);
+        const int j0 = p * kPW;
+        if (p + 1 < npanel) {
+            DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3(1u, (unsigned)nblocks), dim3(kQT), as, nb, nblk,
+                        p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0, j0 + 2 * kPW);
+            factor(p + 1);
+            const int ntiles = (nb - (j0 + 2 * kPW) + 63) / 64;
+            if (ntiles > 0)
+                DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false, true>), dim3((unsigned)ntiles, (unsigned)nblocks),
+                            dim3(kQT), as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0,
+                            1 << 30);
+            p += 2;
+        } else {
+            const int first = j0 + (nb - j0 < kPW ? nb - j0 : kPW);
+            const int ntiles = (nb - first + 63) / 64;
+            if (ntiles > 0)
+                DOBB_LAUNCH("qr_update", s, (k_qr_apply<CH, true, false>), dim3((unsigned)ntiles, (unsigned)nblocks),
+                            dim3(kQT), as, nb, nblk, p, (const float *)Z, (const float *)tq, (const int8_t *)negs, o, 0,
+                            1 << 30);
+            p += 1;
+        }
     }
     // formation: each wave ceil(ceil(nb / 32) / 4) chunks of 32 rows, i.e. CH / 2
     const size_t fs = form_lds(nb).total;
