@@ -9,8 +9,9 @@
 // ties.  Without a token split the EMA is fused into the epilogue; with one, fp64 partials go to the
 // workspace and k_syrk_reduce adds them in split order (deterministic, no atomics).  Each result is
 // written at (i, j) and (j, i) from the same value, so A is exactly symmetric.
-// k_syrk_bf16 takes bf16 activations in 128 x 128 tile pairs; k_syrk_wide takes bf16 blocks wider
-// than 128 whole, so that their activations are read from HBM once (both described below).
+// k_syrk_bf16 takes bf16 activations in 128 x 128 tile pairs; k_syrk_wide_dma (up to 416 columns)
+// and k_syrk_wide (up to 512) take bf16 blocks wider than 128 whole, so that their activations are
+// read from HBM once (all described below).
 #include "dobb_internal.h"
 
 namespace dobb {
@@ -471,6 +472,208 @@ __global__ void __launch_bounds__(512) k_syrk_wide(int64_t N, int nb, int T32, i
         }
 }
 
+// The same tile groups, with X staged by the memory engine: each wave's buffer loads write their
+// 16 bytes per lane straight into LDS (no registers, no repacking), so three 64-token chunks fit
+// in LDS and two are in flight while the third is multiplied.  LDS keeps X's own layout, rows of
+// PC columns (PC = 32 mod 128, so that the four rows one half-wave reads fall in disjoint banks);
+// columns nb .. PC - 1 and tokens past the split are loaded from an offset past the end of the
+// buffer, i.e. as zeros.  The MFMA operands (8 tokens of one column per lane) come from gfx950's
+// transposing LDS read: ds_read_b64_tr_b16 gives lane i of each 16-lane group, as its element j,
+// element i % 4 of the 8 bytes addressed by lane 4 j + i / 4, so lanes that address 4 tokens x 4
+// four-column pieces receive 4 tokens of one column each; two reads make an operand.
+// The three buffers are separate LDS arrays and the loop is unrolled over them, so that the
+// compiler sees which buffer each load writes and each read reads, and waits before a read only
+// for the loads into that buffer; the barrier is written out (waits on this wave's own loads of
+// the next chunk, then s_barrier) so that it does not wait for the loads still in flight.  Every wave
+// issues the same number of loads in every step (a chunk's 16-byte pieces come in PC / 8 loads of
+// 1 KiB, 4 mod 8 of them: waves 4..7 repeat their previous load, same bytes to the same place),
+// including loads of chunks past the split's end (all lanes out of range: zeros, no memory
+// traffic), so that the compiler's count of loads in flight is exact on every path.
+constexpr int kWDMaxCols = 416;    // 3 x 64 x 416 x 2 B = 156 KiB of LDS
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 *lds_s16x4;
+typedef __attribute__((address_space(3))) void *lds_void;
+
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t *p, int pitch4) {
+    // two transposing reads, 4 tokens apart: the lane's 8 tokens of one column
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p + pitch4));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left alone (N < 16)
+template <int N>
+__device__ __forceinline__ void vm_wait() { __builtin_amdgcn_s_waitcnt(0x0f70 | N); }
+
+template <int PC>
+struct WideDma {
+    static constexpr int kPitch = 2 * PC;            // bytes per token row
+    static constexpr int kBytes = kWK * kPitch;      // one chunk
+    static constexpr int kPpr = PC / 8;              // 16-byte pieces per row = 1 KiB loads per chunk
+    static constexpr int kNld = (kPpr + 7) / 8;      // loads per chunk of waves w < kPpr % 8 (else one fewer)
+};
+
+// grid.x = wgs (fastest) x blocks x matrices, renumbered per XCD; grid.y = token splits; block 512
+template <int PC>
+__global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T32, int ngroups, int wgs, int nblk,
+                                                       int64_t tok_per_split, int nsplit, float beta, AccTable t,
+                                                       WideGroups grp, float *partial) {
+    using D = WideDma<PC>;
+    __shared__ __align__(16) uint8_t xb0[D::kBytes], xb1[D::kBytes], xb2[D::kBytes];
+    const int x = xcd_remap(blockIdx.x, gridDim.x);
+    const int wg = x % wgs, rest = x / wgs;
+    const int b = rest % nblk, mat = rest / nblk;
+    const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t te = min<int64_t>(N, tb + tok_per_split);
+    const int64_t ld = t.ldx[mat];
+    const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // loads: wave w issues loads r = w, w + 8, ... of each chunk (the last one again where that
+    // passes kPpr); load r fills LDS bytes [1 KiB r, 1 KiB (r + 1)) of the buffer, lane l the piece
+    // P = 64 r + l: token P / kPpr, 16-byte piece P % kPpr of that token's row
+    static_assert(D::kPpr % 8 == 4, "PC = 32 mod 128");
+    const __amdgpu_buffer_rsrc_t rX =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Xb), (short)0, (int)((N * ld - (int64_t)b * nb) * 2), 0x00020000);
+    int ldr[D::kNld], tkn[D::kNld];
+    unsigned boff[D::kNld];
+#pragma unroll
+    for (int i = 0; i < D::kNld; ++i) {
+        const int r = w + 8 * i < D::kPpr ? w + 8 * i : w + 8 * (i - 1);
+        const int P = 64 * r + lane;
+        const int tk = P / D::kPpr, pc = P - tk * D::kPpr;
+        ldr[i] = r;
+        tkn[i] = 8 * pc < nb ? tk : kWK;   // padding columns: never in range
+        boff[i] = (unsigned)(((int64_t)tk * ld + 8 * pc) * 2);
+    }
+    auto issue = [&](int64_t t0, uint8_t *buf) {
+        const int lim = (int)max<int64_t>(-1, min<int64_t>(kWK, te - t0));
+        const unsigned base = lim > 0 ? (unsigned)(t0 * ld * 2) : 0u;
+#pragma unroll
+        for (int i = 0; i < D::kNld; ++i) {
+            const unsigned off = tkn[i] < lim ? base + boff[i] : kWOff;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_void)(buf + 1024 * ldr[i]), 16, off, 0, 0, 0);
+        }
+    };
+
+    const int g = wg * 8 + w;
+    const bool active = g < ngroups;
+    const int R0 = active ? grp.r0[g] : 0, C0 = active ? grp.c0[g] : 0;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    // operand addresses: lane (group G = lane / 16, q = lane % 16) points at token 8 (G / 2) + q / 4
+    // and columns 16 (G % 2) + 4 (q % 4) .. + 3 of its tile
+    const int G = lane >> 4, q = lane & 15;
+    const int lofs = (8 * (G >> 1) + (q >> 2)) * D::kPitch + 2 * (16 * (G & 1) + 4 * (q & 3));
+    int aof[2], bof[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) aof[i] = lofs + 64 * (R0 + i < T32 ? R0 + i : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bof[j] = lofs + 64 * (C0 + j < T32 ? C0 + j : 0);
+
+    const bool dgroup = active && C0 == R0;
+    const int dt = (lane & 31) - 4 * (lane >> 5);
+    const int rd = (dt >= 0 && (dt & 7) < 4) ? 4 * (dt >> 3) + (dt & 7) : -1;
+    double dg[2] = {0.0, 0.0};
+    auto fold_diag = [&]() {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                v = r == rd ? acc[k][k][r] : v;
+                acc[k][k][r] = r == rd ? 0.f : acc[k][k][r];
+            }
+            dg[k] += (double)v;
+        }
+    };
+    int chunk = 0;
+    // one chunk: refill `nxt` (the previous chunk's buffer) with the chunk after next, multiply
+    // the chunk in `cur`, wait for this wave's loads of the next chunk (those of the chunk after
+    // it stay in flight), barrier (every wave's loads of the next chunk have landed and every
+    // wave is done with `cur`)
+    auto step = [&](int64_t t0, const uint8_t *cur, uint8_t *nxt) {
+        issue(t0 + 2 * kWK, nxt);
+        if (active) {
+#pragma unroll
+            for (int kk = 0; kk < kWK; kk += 16) {
+                bf16x8 a[2], bv[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) a[i] = tr_operand(cur + aof[i] + kk * D::kPitch, 4 * D::kPitch);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = tr_operand(cur + bof[j] + kk * D::kPitch, 4 * D::kPitch);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (dgroup && ++chunk == kWFold) {
+            fold_diag();
+            chunk = 0;
+        }
+        if (t0 + kWK < te) vm_wait<D::kNld>(); else vm_wait<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    issue(tb, xb0);
+    issue(tb + kWK, xb1);
+    vm_wait<D::kNld>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // unrolled twice over the three buffers: the compiler's count of loads in flight merges less
+    // precisely at the loop head, where its first read waits for the next chunk as well
+    for (int64_t t0 = tb; t0 < te; t0 += 6 * kWK) {
+        step(t0, xb0, xb2);
+        if (t0 + kWK >= te) break;
+        step(t0 + kWK, xb1, xb0);
+        if (t0 + 2 * kWK >= te) break;
+        step(t0 + 2 * kWK, xb2, xb1);
+        if (t0 + 3 * kWK >= te) break;
+        step(t0 + 3 * kWK, xb0, xb2);
+        if (t0 + 4 * kWK >= te) break;
+        step(t0 + 4 * kWK, xb1, xb0);
+        if (t0 + 5 * kWK >= te) break;
+        step(t0 + 5 * kWK, xb2, xb1);
+    }
+    vm_wait<0>();   // the loads past the end: none may land after the workgroup has ended
+    if (dgroup) fold_diag();
+    if (!active) return;
+
+    const int64_t tot_blocks = (int64_t)nblk * (gridDim.x / (wgs * nblk));
+    float *Ab = t.A[mat] + (int64_t)b * nb * nb;
+    float *Pb = partial ? partial + ((int64_t)blockIdx.y * tot_blocks + rest) * nb * nb : nullptr;
+    const double invN = 1.0 / (double)N, bd = (double)beta;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (R0 + i >= T32 || C0 + j >= T32 || C0 + j < R0 + i) continue;
+            const int gj = 32 * (C0 + j) + acc_col(lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gi = 32 * (R0 + i) + acc_row(r, lane);
+                if (gi >= nb || gj >= nb || gi > gj) continue;
+                const double sum = (dgroup && i == j && r == rd) ? dg[i] : (double)acc[i][j][r];
+                if (Pb) {
+                    Pb[(int64_t)gi * nb + gj] = (float)sum;
+                } else {
+                    const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
+                    const float v = (float)(bd * old + (1.0 - bd) * (sum * invN));
+                    Ab[(int64_t)gi * nb + gj] = v;
+                    Ab[(int64_t)gj * nb + gi] = v;
+                }
+            }
+        }
+}
+
 // Sum the token-split partials in split order, apply the EMA, write both triangles.  One
 // workgroup per 32 x 32 tile (I, J), I <= J, of a block: the partials of the upper triangle are
 // read along rows, and the mirrored tile (J, I) goes out through LDS, also along rows.
@@ -526,6 +729,12 @@ static int wide_groups(int T32, WideGroups *g) {
 }
 
 static bool wide_shape(int64_t nb) { return nb > 128 && nb <= 512 && nb % 8 == 0; }
+
+// LDS row width of k_syrk_wide_dma for T32 tiles: the least width >= 32 T32 that is 32 mod 128
+static int dma_cols(int T32) {
+    const int c = 32 * T32;
+    return c + ((32 - c % 128) + 128) % 128;
+}
 
 
 // Split plan of the wide kernel: at most kWSplitMax tokens per split (the fp32 sum length), enough
@@ -608,12 +817,19 @@ hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
             const int wgs = (ngroups + 7) / 8;
             int64_t wtps = a.N;
             const int wsplit = wide_plan(a.sh, a.N, a.count, &wtps);
-            const size_t lds = (size_t)2 * 32 * T32 * kWK * sizeof(uint16_t);
-            (void)hipFuncSetAttribute((const void *)k_syrk_wide, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             float *wpart = wsplit > 1 ? (float *)a.partial : nullptr;
             dim3 grid((unsigned)(wgs * nblk * cnt), (unsigned)wsplit);
-            DOBB_LAUNCH("accumulate_syrk_wide", s, k_syrk_wide, grid, dim3(512), lds, a.N, nb, T32, ngroups, wgs, nblk,
-                        wtps, wsplit, a.beta, t, grp, wpart);
+            const int pcols = dma_cols(T32);
+            if (pcols <= kWDMaxCols) {
+#define DOBB_WDMA(PC) DOBB_LAUNCH("accumulate_syrk_wide", s, k_syrk_wide_dma<PC>, grid, dim3(512), 0, a.N, nb, T32, ngroups, wgs, nblk, wtps, wsplit, a.beta, t, grp, wpart)
+                if (pcols == 160) DOBB_WDMA(160); else if (pcols == 288) DOBB_WDMA(288); else DOBB_WDMA(416);
+#undef DOBB_WDMA
+            } else {
+                const size_t lds = (size_t)2 * 32 * T32 * kWK * sizeof(uint16_t);
+                (void)hipFuncSetAttribute((const void *)k_syrk_wide, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                DOBB_LAUNCH("accumulate_syrk_wide", s, k_syrk_wide, grid, dim3(512), lds, a.N, nb, T32, ngroups, wgs, nblk,
+                            wtps, wsplit, a.beta, t, grp, wpart);
+            }
             if (wsplit > 1) {
                 const int64_t tot = (int64_t)nblk * cnt;
                 dim3 g2((unsigned)(T32 * (T32 + 1) / 2), (unsigned)tot);

@@ -65,6 +65,8 @@ def random_basis(B, nb, rng):
     (1000, 800, 400, torch.bfloat16),    # wide bf16 blocks: 13 tile rows, 3 token splits, ragged N
     (4500, 512, 512, torch.bfloat16),    # widest wide block: 3 workgroups per block, 2 splits
     (333, 272, 136, torch.bfloat16),     # wide, nb % 32 != 0, one split (EMA fused in the kernel)
+    (700, 512, 256, torch.bfloat16),     # wide, LDS rows of 288 columns (32 of them zero padding)
+    (130, 768, 384, torch.bfloat16),     # wide, 13 row tiles with an empty one, last chunk 2 tokens
     (1000, 512, 128, torch.bfloat16),    # the 7B-style block width: a full 128-wide bf16 tile, ragged N
     (777, 384, 128, torch.float32),      # nb = 128 with fp32 activations, ragged N
 ])
