@@ -9,9 +9,9 @@
 // ties.  Without a token split the EMA is fused into the epilogue; with one, fp64 partials go to the
 // workspace and k_syrk_reduce adds them in split order (deterministic, no atomics).  Each result is
 // written at (i, j) and (j, i) from the same value, so A is exactly symmetric.
-// k_syrk_bf16 takes bf16 activations in 128 x 128 tile pairs; k_syrk_wide_dma (up to 416 columns)
-// and k_syrk_wide (up to 512) take bf16 blocks wider than 128 whole, so that their activations are
-// read from HBM once (all described below).
+// bf16 activations: k_syrk_narrow_dma (blocks of 33 .. 128 columns), k_syrk_wide_dma (up to 416)
+// and k_syrk_wide (up to 512) take each block whole, so that its activations are read from HBM
+// once; k_syrk_bf16 (128 x 128 tile pairs) takes the rest (all described below).
 #include "dobb_internal.h"
 
 namespace dobb {
@@ -508,21 +508,98 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint8_t *p, int pitch4) {
 template <int N>
 __device__ __forceinline__ void vm_wait() { __builtin_amdgcn_s_waitcnt(0x0f70 | N); }
 
-template <int PC>
-struct WideDma {
-    static constexpr int kPitch = 2 * PC;            // bytes per token row
-    static constexpr int kBytes = kWK * kPitch;      // one chunk
-    static constexpr int kPpr = PC / 8;              // 16-byte pieces per row = 1 KiB loads per chunk
-    static constexpr int kNld = (kPpr + 7) / 8;      // loads per chunk of waves w < kPpr % 8 (else one fewer)
+// The staging plan of one workgroup of NW waves: a chunk's kWK token rows of PC / 8 16-byte pieces
+// are PC / 8 loads of 1 KiB; wave w issues loads w, w + NW, ... (the last one again where that
+// passes the count, so that every wave issues kNld per chunk); load r fills LDS bytes
+// [1 KiB r, 1 KiB (r + 1)) of the buffer, lane l the piece P = 64 r + l: token P / (PC / 8), piece
+// P % (PC / 8) of that token's row.  Pieces from column nb on, and tokens from the split's end on,
+// load from an offset past the end of the buffer (zeros).  A piece that runs past column nb (nb % 8
+// = 4) brings 4 columns of the next block, which only feed discarded entries.
+template <int PC, int NW>
+struct DmaPlan {
+    static constexpr int kPitch = 2 * PC;                 // bytes per token row
+    static constexpr int kBytes = kWK * kPitch;           // one chunk
+    static constexpr int kPpr = PC / 8;                   // pieces per row = loads per chunk
+    static constexpr int kNld = (kPpr + NW - 1) / NW;     // loads per chunk and wave
+    static_assert(PC % 128 == 32 && kPpr >= NW, "rows of 32 mod 128 columns, one load per wave at least");
+    __amdgpu_buffer_rsrc_t rX;
+    int64_t ld, te;
+    int ldr[kNld], tkn[kNld];
+    unsigned boff[kNld];
+    __device__ __forceinline__ DmaPlan(const uint16_t *Xb, int64_t range, int64_t ld_, int nb, int64_t te_, int w, int lane)
+        : ld(ld_), te(te_) {
+        rX = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Xb), (short)0, (int)(range * 2), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < kNld; ++i) {
+            const int r = w + NW * i < kPpr ? w + NW * i : w + NW * (i - 1);
+            const int P = 64 * r + lane;
+            const int tk = P / kPpr, pc = P - tk * kPpr;
+            ldr[i] = r;
+            tkn[i] = 8 * pc < nb ? tk : kWK;   // padding columns: never in range
+            boff[i] = (unsigned)(((int64_t)tk * ld + 8 * pc) * 2);
+        }
+    }
+    // the chunk of tokens t0 .. t0 + kWK - 1 into buf (all zeros when t0 >= te)
+    __device__ __forceinline__ void issue(int64_t t0, uint8_t *buf) const {
+        const int lim = (int)max<int64_t>(-1, min<int64_t>(kWK, te - t0));
+        const unsigned base = lim > 0 ? (unsigned)(t0 * ld * 2) : 0u;
+#pragma unroll
+        for (int i = 0; i < kNld; ++i) {
+            const unsigned off = tkn[i] < lim ? base + boff[i] : kWOff;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_void)(buf + 1024 * ldr[i]), 16, off, 0, 0, 0);
+        }
+    }
 };
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// body(cur) for the chunks t0 = tb, tb + kWK, .. < te, each in LDS at cur, with NBUF chunk buffers
+// (NBUF - 1 chunks in flight).  A step refills the previous chunk's buffer with the chunk NBUF - 1
+// ahead, runs the body, waits for this wave's loads of the next chunk (those of the chunks after it
+// stay in flight) and meets the barrier (every wave's loads of the next chunk have landed and every
+// wave is done with cur).  Unrolled twice over the buffers: the compiler's count of loads in flight
+// merges less precisely at the loop head, where its first read also waits for the next chunk.  On
+// return no load is in flight.
+template <int NBUF, class Plan, class Body>
+__device__ __forceinline__ void dma_chunks(const Plan &L, int64_t tb, int64_t te, uint8_t *const (&buf)[NBUF],
+                                           Body &&body) {
+    static_assert((NBUF - 2) * Plan::kNld < 16, "vmcnt immediate");
+    auto step = [&](int64_t t0, const uint8_t *cur, uint8_t *nxt) {
+        L.issue(t0 + (NBUF - 1) * kWK, nxt);
+        body(cur);
+        if (t0 + kWK < te) vm_wait<(NBUF - 2) * Plan::kNld>(); else vm_wait<0>();
+        lds_barrier();
+    };
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) L.issue(tb + k * kWK, buf[k]);
+    vm_wait<(NBUF - 2) * Plan::kNld>();
+    lds_barrier();
+    for (int64_t t0 = tb; t0 < te; t0 += 2 * NBUF * kWK) {
+#pragma unroll
+        for (int k = 0; k < 2 * NBUF; ++k) {
+            if (t0 + k * kWK >= te) break;
+            step(t0 + k * kWK, buf[k % NBUF], buf[(k + NBUF - 1) % NBUF]);
+        }
+    }
+    vm_wait<0>();   // the loads past the end: none may land after the workgroup has ended
+}
+
+// operand address within a chunk buffer: lane (group G = lane / 16, q = lane % 16) points at token
+// 8 (G / 2) + q / 4 and columns 16 (G % 2) + 4 (q % 4) .. + 3 of 32-column tile `tile`
+template <int PITCH>
+__device__ __forceinline__ int tr_lane_offset(int lane, int tile) {
+    const int G = lane >> 4, q = lane & 15;
+    return (8 * (G >> 1) + (q >> 2)) * PITCH + 2 * (16 * (G & 1) + 4 * (q & 3)) + 64 * tile;
+}
 
 // grid.x = wgs (fastest) x blocks x matrices, renumbered per XCD; grid.y = token splits; block 512
 template <int PC>
 __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T32, int ngroups, int wgs, int nblk,
                                                        int64_t tok_per_split, int nsplit, float beta, AccTable t,
                                                        WideGroups grp, float *partial) {
-    using D = WideDma<PC>;
+    using D = DmaPlan<PC, 8>;
     __shared__ __align__(16) uint8_t xb0[D::kBytes], xb1[D::kBytes], xb2[D::kBytes];
+    uint8_t *const bufs[3] = {xb0, xb1, xb2};
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int wg = x % wgs, rest = x / wgs;
     const int b = rest % nblk, mat = rest / nblk;
@@ -532,33 +609,7 @@ __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T3
     const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // loads: wave w issues loads r = w, w + 8, ... of each chunk (the last one again where that
-    // passes kPpr); load r fills LDS bytes [1 KiB r, 1 KiB (r + 1)) of the buffer, lane l the piece
-    // P = 64 r + l: token P / kPpr, 16-byte piece P % kPpr of that token's row
-    static_assert(D::kPpr % 8 == 4, "PC = 32 mod 128");
-    const __amdgpu_buffer_rsrc_t rX =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Xb), (short)0, (int)((N * ld - (int64_t)b * nb) * 2), 0x00020000);
-    int ldr[D::kNld], tkn[D::kNld];
-    unsigned boff[D::kNld];
-#pragma unroll
-    for (int i = 0; i < D::kNld; ++i) {
-        const int r = w + 8 * i < D::kPpr ? w + 8 * i : w + 8 * (i - 1);
-        const int P = 64 * r + lane;
-        const int tk = P / D::kPpr, pc = P - tk * D::kPpr;
-        ldr[i] = r;
-        tkn[i] = 8 * pc < nb ? tk : kWK;   // padding columns: never in range
-        boff[i] = (unsigned)(((int64_t)tk * ld + 8 * pc) * 2);
-    }
-    auto issue = [&](int64_t t0, uint8_t *buf) {
-        const int lim = (int)max<int64_t>(-1, min<int64_t>(kWK, te - t0));
-        const unsigned base = lim > 0 ? (unsigned)(t0 * ld * 2) : 0u;
-#pragma unroll
-        for (int i = 0; i < D::kNld; ++i) {
-            const unsigned off = tkn[i] < lim ? base + boff[i] : kWOff;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_void)(buf + 1024 * ldr[i]), 16, off, 0, 0, 0);
-        }
-    };
+    const D L(Xb, N * ld - (int64_t)b * nb, ld, nb, te, w, lane);
 
     const int g = wg * 8 + w;
     const bool active = g < ngroups;
@@ -568,15 +619,11 @@ __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T3
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-    // operand addresses: lane (group G = lane / 16, q = lane % 16) points at token 8 (G / 2) + q / 4
-    // and columns 16 (G % 2) + 4 (q % 4) .. + 3 of its tile
-    const int G = lane >> 4, q = lane & 15;
-    const int lofs = (8 * (G >> 1) + (q >> 2)) * D::kPitch + 2 * (16 * (G & 1) + 4 * (q & 3));
     int aof[2], bof[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) aof[i] = lofs + 64 * (R0 + i < T32 ? R0 + i : 0);
+    for (int i = 0; i < 2; ++i) aof[i] = tr_lane_offset<D::kPitch>(lane, R0 + i < T32 ? R0 + i : 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bof[j] = lofs + 64 * (C0 + j < T32 ? C0 + j : 0);
+    for (int j = 0; j < 4; ++j) bof[j] = tr_lane_offset<D::kPitch>(lane, C0 + j < T32 ? C0 + j : 0);
 
     const bool dgroup = active && C0 == R0;
     const int dt = (lane & 31) - 4 * (lane >> 5);
@@ -595,12 +642,7 @@ __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T3
         }
     };
     int chunk = 0;
-    // one chunk: refill `nxt` (the previous chunk's buffer) with the chunk after next, multiply
-    // the chunk in `cur`, wait for this wave's loads of the next chunk (those of the chunk after
-    // it stay in flight), barrier (every wave's loads of the next chunk have landed and every
-    // wave is done with `cur`)
-    auto step = [&](int64_t t0, const uint8_t *cur, uint8_t *nxt) {
-        issue(t0 + 2 * kWK, nxt);
+    dma_chunks(L, tb, te, bufs, [&](const uint8_t *cur) {
         if (active) {
 #pragma unroll
             for (int kk = 0; kk < kWK; kk += 16) {
@@ -620,30 +662,7 @@ __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T3
             fold_diag();
             chunk = 0;
         }
-        if (t0 + kWK < te) vm_wait<D::kNld>(); else vm_wait<0>();
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
-
-    issue(tb, xb0);
-    issue(tb + kWK, xb1);
-    vm_wait<D::kNld>();
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // unrolled twice over the three buffers: the compiler's count of loads in flight merges less
-    // precisely at the loop head, where its first read waits for the next chunk as well
-    for (int64_t t0 = tb; t0 < te; t0 += 6 * kWK) {
-        step(t0, xb0, xb2);
-        if (t0 + kWK >= te) break;
-        step(t0 + kWK, xb1, xb0);
-        if (t0 + 2 * kWK >= te) break;
-        step(t0 + 2 * kWK, xb2, xb1);
-        if (t0 + 3 * kWK >= te) break;
-        step(t0 + 3 * kWK, xb0, xb2);
-        if (t0 + 4 * kWK >= te) break;
-        step(t0 + 4 * kWK, xb1, xb0);
-        if (t0 + 5 * kWK >= te) break;
-        step(t0 + 5 * kWK, xb2, xb1);
-    }
-    vm_wait<0>();   // the loads past the end: none may land after the workgroup has ended
+    });
     if (dgroup) fold_diag();
     if (!active) return;
 
@@ -672,6 +691,90 @@ __global__ void __launch_bounds__(512) k_syrk_wide_dma(int64_t N, int nb, int T3
                 }
             }
         }
+}
+
+// Blocks of 33 .. 128 columns, bf16 X (nb % 4 == 0), the same staging with four waves: one
+// workgroup per block and token split, two per CU (a fourth chunk buffer, three chunks in flight,
+// measured no faster: 2.05 against 2.03 ms for the GPT-2 XL nb = 100 set).  The upper triangle's T32 (T32 + 1) / 2 tiles
+// of 32 x 32 (at most 10) go to the waves in turn, at most 3 per wave; every 4 chunks (256
+// tokens) the fp32 sums move into fp64 registers, so a split needs no fp32 length limit and the
+// bf16 token-split plan applies (one split for the GPT-2 XL set, the EMA fused in the epilogue).
+constexpr int kNMaxTiles = 3;
+__global__ void __launch_bounds__(256) k_syrk_narrow_dma(int64_t N, int nb, int T32, int nblk, int64_t tok_per_split,
+                                                         int nsplit, float beta, AccTable t, double *partial) {
+    using D = DmaPlan<160, 4>;
+    __shared__ __align__(16) uint8_t xb0[D::kBytes], xb1[D::kBytes], xb2[D::kBytes];
+    uint8_t *const bufs[3] = {xb0, xb1, xb2};
+    const int rest = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = rest % nblk, mat = rest / nblk;
+    const int64_t tb = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t te = min<int64_t>(N, tb + tok_per_split);
+    const int64_t ld = t.ldx[mat];
+    const uint16_t *Xb = (const uint16_t *)t.X[mat] + (int64_t)b * nb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const D L(Xb, N * ld - (int64_t)b * nb, ld, nb, te, w, lane);
+
+    // tiles w, w + 4, w + 8 of the row-major upper triangle
+    const int ntiles = T32 * (T32 + 1) / 2;
+    int ti[kNMaxTiles], tj[kNMaxTiles], aof[kNMaxTiles], bof[kNMaxTiles];
+    bool has[kNMaxTiles];
+    f32x16 acc[kNMaxTiles];
+    double accd[kNMaxTiles][16];
+#pragma unroll
+    for (int k = 0; k < kNMaxTiles; ++k) {
+        has[k] = w + 4 * k < ntiles;
+        tile_pair(has[k] ? w + 4 * k : 0, T32, ti[k], tj[k]);
+        aof[k] = tr_lane_offset<D::kPitch>(lane, ti[k]);
+        bof[k] = tr_lane_offset<D::kPitch>(lane, tj[k]);
+        acc[k] = (f32x16){};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accd[k][r] = 0.0;
+    }
+    int chunk = 0;
+    dma_chunks(L, tb, te, bufs, [&](const uint8_t *cur) {
+#pragma unroll
+        for (int kk = 0; kk < kWK; kk += 16) {
+#pragma unroll
+            for (int k = 0; k < kNMaxTiles; ++k) {
+                if (!has[k]) continue;
+                const bf16x8 a = tr_operand(cur + aof[k] + kk * D::kPitch, 4 * D::kPitch);
+                const bf16x8 bv = tr_operand(cur + bof[k] + kk * D::kPitch, 4 * D::kPitch);
+                acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[k], 0, 0, 0);
+            }
+        }
+        if (++chunk == 4) {
+            chunk = 0;
+#pragma unroll
+            for (int k = 0; k < kNMaxTiles; ++k)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { accd[k][r] += (double)acc[k][r]; acc[k][r] = 0.f; }
+        }
+    });
+
+    const double invN = 1.0 / (double)N, bd = (double)beta;
+    float *Ab = t.A[mat] + (int64_t)b * nb * nb;
+    const int64_t tot_blocks = gridDim.x;
+    double *Pb = partial ? partial + ((int64_t)blockIdx.y * tot_blocks + rest) * nb * nb : nullptr;
+#pragma unroll
+    for (int k = 0; k < kNMaxTiles; ++k) {
+        if (!has[k]) continue;
+        const int gj = 32 * tj[k] + acc_col(lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int gi = 32 * ti[k] + acc_row(r, lane);
+            if (gi >= nb || gj >= nb || gi > gj) continue;
+            const double sum = accd[k][r] + (double)acc[k][r];
+            if (nsplit == 1) {
+                const double old = beta > 0.f ? (double)Ab[(int64_t)gi * nb + gj] : 0.0;
+                const float v = (float)(bd * old + (1.0 - bd) * (sum * invN));
+                Ab[(int64_t)gi * nb + gj] = v;
+                Ab[(int64_t)gj * nb + gi] = v;
+            } else {
+                Pb[(int64_t)gi * nb + gj] = sum;
+            }
+        }
+    }
 }
 
 // Sum the token-split partials in split order, apply the EMA, write both triangles.  One
@@ -843,7 +946,10 @@ hipError_t launch_accumulate(const AccumulateArgs &a, hipStream_t s) {
         }
         dim3 grid((unsigned)(npairs * nblk * cnt), (unsigned)nsplit);
         double *part = nsplit > 1 ? a.partial : nullptr;
-        if (xbf) {
+        if (xbf && vec4 && wide_ok && nb > 32 && nb <= 128) {
+            DOBB_LAUNCH("accumulate_syrk_bf16", s, k_syrk_narrow_dma, grid, dim3(256), 0, a.N, nb, (nb + 31) / 32, nblk,
+                        tps, nsplit, a.beta, t, part);
+        } else if (xbf) {
 #define DOBB_SYRKB(V) DOBB_LAUNCH("accumulate_syrk_bf16", s, (k_syrk_bf16<V>), grid, dim3(512), 0, a.N, nb, T, npairs, nblk, tps, nsplit, a.beta, t, part)
             if (vec8) DOBB_SYRKB(8); else if (vec4) DOBB_SYRKB(4); else DOBB_SYRKB(1);
 #undef DOBB_SYRKB
