@@ -12,6 +12,8 @@
 //           accumulator by k_jacobi_rotate_v, spread over many workgroups (rows of V are
 //           independent).  k_jacobi_finalize sorts by descending eigenvalue, makes the largest entry
 //           of every eigenvector positive and writes fp32 Q, lambda and info.
+//           When even the fp32 working matrix exceeds the LDS, block Jacobi in fp64 instead
+//           (k_bj_sub / k_bj_apply below): a round touches A and V once instead of nbp - 1 times.
 // ORTH_ITER k times: Z = A_b Q_b (MFMA), Q_b <- qr(Z).Q by Householder (k_qr.hip: one launch with
 //           Z in LDS for nb <= 128, panel / update / formation launches above), diag(R) > 0.
 //           Rayleigh quotients go to lambda when requested.
@@ -281,6 +283,302 @@ __global__ void __launch_bounds__(256) k_jacobi_rotate_v(int nb, int nbp, double
     for (int e = threadIdx.x; e < rows * nb; e += 256) {
         const int r = e / nb, c = e % nb;
         V[(int64_t)r * nb + c] = Vs[r * nbp + c];
+    }
+}
+
+// ---- block Jacobi: working matrices that do not fit the LDS ------------------------------------
+// The indices are cut into m (even) index blocks of b (the last ones padded past nb: zero rows and
+// columns, never rotated).  A round pairs the index blocks by the circle method, so a sweep is
+// m - 1 rounds and meets every pair of index blocks once; in a round the m / 2 pair sets
+// S_k = I_k u J_k (2b indices each) are disjoint.  k_bj_sub gives each S_k one cyclic sweep of its
+// 2b x 2b sub-problem in LDS, by the rotation rule of k_jacobi_sweep, and keeps the product R_k of
+// those rotations (fp64); the swept sub-matrix is A's diagonal tile R_k^T A_{S_k S_k} R_k.
+// k_bj_apply carries the round to the rest: A_{S_p S_q} <- R_p^T A_{S_p S_q} R_q for p < q (and its
+// transpose), V_{:, S_q} <- V_{:, S_q} R_q.  A round so reads and writes A and V once, where the
+// element-wise sweep does so for every one of its nbp - 1 rounds.  All in fp64; the rotation rule
+// and threshold are those of the refinement stage, so the result meets the same 1e-14 criterion.
+struct BjGeo {
+    int m, b;   // index blocks (even), indices per block (a multiple of 4, at most 40)
+};
+__host__ __device__ inline BjGeo bj_geo(int nb) {
+    BjGeo G;
+    G.m = 2 * ((nb + 79) / 80);
+    const int b = (nb + G.m - 1) / G.m;
+    G.b = (b + 3) / 4 * 4;
+    return G;
+}
+// index of local row l (0 .. 2b - 1) of the pair set (I, J)
+__device__ __forceinline__ int bj_idx(int l, int I, int J, int b) { return l < b ? I * b + l : J * b + (l - b); }
+
+__host__ __device__ inline size_t bj_sub_lds(int nb) {
+    const int b2 = 2 * bj_geo(nb).b;
+    return (size_t)2 * b2 * (b2 + 1) * 8 + (size_t)(b2 / 2) * (5 * 8 + 4 + 4) + 16;
+}
+constexpr int kBjK = 16;   // rows of R per LDS chunk in k_bj_apply
+__host__ __device__ inline size_t bj_apply_lds(int nb) {
+    const int b2 = 2 * bj_geo(nb).b;
+    return (size_t)(b2 + kBjK) * (b2 + 1) * 8;
+}
+
+// grid = (m / 2 pair sets, blocks), block 512.  R_all: per block m / 2 matrices 2b x 2b; nrot_all:
+// per block and pair set, the rotations of this round (0: R is the identity and was not written).
+// B2 = 2b.  One step of the inner sweep is three passes over LDS: the rotations (tangent, cosine
+// and sine, computed once by the thread that chooses the pair, with the pair's new diagonal);
+// A <- A J and R <- R J; A <- J^T A, which writes the pair's own 2 x 2 block exactly (a_pq = a_qp =
+// 0, a_pp - t a_pq, a_qq + t a_pq).  In the two update passes a thread keeps one row (one column)
+// index and takes every kBjThreads / B2-th pair, so a wave's lanes touch consecutive rows (columns)
+// of the same two columns (rows); the row pitch, B2 + 1 doubles, spreads a column over the banks.
+// The two orders of rounding leave A symmetric to rounding only; the angles read the upper entry
+// and the swept tile is written back symmetric.
+constexpr int kBjThreads = 512;
+template <int B2>
+__global__ void __launch_bounds__(kBjThreads) k_bj_sub(int nb, int nbp, int round, float tol, double *Aw_all,
+                                                       double *R_all, int32_t *nrot_all, int32_t *state_all) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    constexpr int b = B2 / 2, np = b, ld = B2 + 1;
+    constexpr int kPT = kBjThreads / B2;             // threads per row (column) index
+    constexpr int kKP = (np + kPT - 1) / kPT;        // pairs per thread and pass
+    const BjGeo G = bj_geo(nb);
+    const int k = blockIdx.x, g = blockIdx.y;
+    int32_t *st = state_all + 4 * g;
+    if (st[1]) return;   // converged
+    double *As = (double *)dsm;
+    double *Rs = As + B2 * ld;
+    double *tsh = Rs + B2 * ld;
+    double *csh = tsh + np;
+    double *ssh = csh + np;
+    double *dp = ssh + np;    // new a_pp
+    double *dq = dp + np;     // new a_qq
+    int *psh = (int *)(dq + np);
+    int *qsh = psh + np;
+    int *nrot_sh = qsh + np;
+    int I, J;
+    rr_pair(G.m, round, k, I, J);
+    double *Aw = Aw_all + (int64_t)g * nbp * nbp;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < B2 * B2; e += kBjThreads) {
+        const int r = e / B2, c = e - r * B2;
+        const int gi = bj_idx(r, I, J, b), gj = bj_idx(c, I, J, b);
+        As[r * ld + c] = (gi < nb && gj < nb) ? Aw[(int64_t)gi * nbp + gj] : 0.0;
+        Rs[r * ld + c] = r == c ? 1.0 : 0.0;
+    }
+    if (tid == 0) *nrot_sh = 0;
+    __syncthreads();
+    int myrot = 0;
+    const double dtol = (double)tol;
+    const int ix = tid % B2, kk0 = tid / B2;         // this thread's row (column) and first pair
+    const bool worker = kk0 < kPT;
+    for (int s = 0; s < B2 - 1; ++s) {
+        if (tid < np) {
+            int p, q;
+            rr_pair(B2, s, tid, p, q);
+            double t = 0.0;
+            const double app = As[p * ld + p], aqq = As[q * ld + q], apq = As[p * ld + q];
+            if (apq != 0.0 && fabs(apq) > dtol * sqrt(fabs(app * aqq))) {
+                const double theta = (aqq - app) / (2.0 * apq);
+                if (fabs(theta) > 1e150) t = 0.5 / theta;
+                else t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(1.0 + theta * theta));
+                ++myrot;
+            }
+            const double c = 1.0 / sqrt(1.0 + t * t);
+            tsh[tid] = t; csh[tid] = c; ssh[tid] = t * c; psh[tid] = p; qsh[tid] = q;
+            dp[tid] = app - t * apq;
+            dq[tid] = aqq + t * apq;
+        }
+        __syncthreads();
+        // columns p, q of A and of R, in row ix
+        if (worker) {
+#pragma unroll
+            for (int i = 0; i < kKP; ++i) {
+                const int kk = kk0 + kPT * i;
+                if (kk < np && tsh[kk] != 0.0) {
+                    const int p = psh[kk], q = qsh[kk];
+                    const double c = csh[kk], sn = ssh[kk];
+                    const double ap = As[ix * ld + p], aq = As[ix * ld + q];
+                    const double rp = Rs[ix * ld + p], rq = Rs[ix * ld + q];
+                    As[ix * ld + p] = c * ap - sn * aq;
+                    As[ix * ld + q] = sn * ap + c * aq;
+                    Rs[ix * ld + p] = c * rp - sn * rq;
+                    Rs[ix * ld + q] = sn * rp + c * rq;
+                }
+            }
+        }
+        __syncthreads();
+        // rows p, q of A, in column ix; the pair's own columns get the exact block
+        if (worker) {
+#pragma unroll
+            for (int i = 0; i < kKP; ++i) {
+                const int kk = kk0 + kPT * i;
+                if (kk < np && tsh[kk] != 0.0) {
+                    const int p = psh[kk], q = qsh[kk];
+                    double vp, vq;
+                    if (ix == p) { vp = dp[kk]; vq = 0.0; }
+                    else if (ix == q) { vp = 0.0; vq = dq[kk]; }
+                    else {
+                        const double c = csh[kk], sn = ssh[kk];
+                        const double yp = As[p * ld + ix], yq = As[q * ld + ix];
+                        vp = c * yp - sn * yq;
+                        vq = sn * yp + c * yq;
+                    }
+                    As[p * ld + ix] = vp;
+                    As[q * ld + ix] = vq;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (myrot) atomicAdd(nrot_sh, myrot);   // integer counts: order-independent
+    __syncthreads();
+    const int rot = *nrot_sh;
+    if (rot) {
+        double *R = R_all + ((int64_t)g * (G.m / 2) + k) * B2 * B2;
+        for (int e = tid; e < B2 * B2; e += kBjThreads) {
+            const int r = e / B2, c = e - r * B2;
+            const int gi = bj_idx(r, I, J, b), gj = bj_idx(c, I, J, b);
+            // the swept tile, symmetric: the upper entry for both
+            const double v = r <= c ? As[r * ld + c] : As[c * ld + r];
+            if (gi < nb && gj < nb) Aw[(int64_t)gi * nbp + gj] = v;
+            R[e] = Rs[r * ld + c];
+        }
+    }
+    if (tid == 0) {
+        nrot_all[(int64_t)g * (G.m / 2) + k] = rot;
+        if (rot) atomicAdd(&st[2], rot);
+    }
+}
+
+// grid = (tiles, blocks), block 256: tiles [0, m/2 (m/2 - 1) / 2) are the pairs p < q of pair sets
+// (A_{S_p S_q} <- R_p^T A_{S_p S_q} R_q, written with its transpose), the rest (pair set q, B2-row
+// tile) V_{rows, S_q} <- V_{rows, S_q} R_q.  Each thread owns a kT x kT piece of the B2 x B2 result
+// (rows ty + 16 i, columns tx + 16 j); the operand X sits in LDS, R comes in kBjK-row chunks.  A pair
+// set whose sub-problem rotated nothing has R = I (not read).
+template <int B2>
+__global__ void __launch_bounds__(256) k_bj_apply(int nb, int nbp, int round, double *Aw_all, double *V_all,
+                                                  const double *R_all, const int32_t *nrot_all, const int32_t *state_all) {
+    extern __shared__ __align__(16) unsigned char dsm[];
+    constexpr int b = B2 / 2, ld = B2 + 1, kT = (B2 + 15) / 16;
+    const BjGeo G = bj_geo(nb);
+    const int np2 = G.m / 2;
+    const int g = blockIdx.y;
+    if (state_all[4 * g + 1]) return;
+    const int na = np2 * (np2 - 1) / 2;
+    const int tile = blockIdx.x;
+    int p = 0, q = 0, rt = 0;
+    const bool isA = tile < na;
+    if (isA) {
+        int rem = tile;
+        while (rem >= np2 - 1 - p) { rem -= np2 - 1 - p; ++p; }
+        q = p + 1 + rem;
+    } else {
+        const int v = tile - na, nrt = (nb + B2 - 1) / B2;
+        q = v / nrt;
+        rt = v - q * nrt;
+    }
+    const int32_t *nr = nrot_all + (int64_t)g * np2;
+    const bool rq_id = nr[q] == 0, rp_id = !isA || nr[p] == 0;
+    if (rq_id && rp_id) return;
+    int Ip = 0, Jp = 0, Iq, Jq;
+    rr_pair(G.m, round, q, Iq, Jq);
+    if (isA) rr_pair(G.m, round, p, Ip, Jp);
+    double *X = (double *)dsm;            // [B2][ld]
+    double *Rc = X + B2 * ld;             // [kBjK][ld]
+    double *Aw = Aw_all + (int64_t)g * nbp * nbp;
+    double *V = V_all + (int64_t)g * nb * nb;
+    const double *Rq = R_all + ((int64_t)g * np2 + q) * B2 * B2;
+    const double *Rp = isA ? R_all + ((int64_t)g * np2 + p) * B2 * B2 : nullptr;
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    // the operand: A_{S_p S_q} or rows rt B2 .. of V's columns S_q (zero outside)
+    for (int e = tid; e < B2 * B2; e += 256) {
+        const int r = e / B2, c = e - r * B2;
+        const int gj = bj_idx(c, Iq, Jq, b);
+        double v = 0.0;
+        if (isA) {
+            const int gi = bj_idx(r, Ip, Jp, b);
+            if (gi < nb && gj < nb) v = Aw[(int64_t)gi * nbp + gj];
+        } else {
+            const int gi = rt * B2 + r;
+            if (gi < nb && gj < nb) v = V[(int64_t)gi * nb + gj];
+        }
+        X[r * ld + c] = v;
+    }
+    double acc[kT][kT];
+    // acc = X R, or (trans_lhs) R^T X; R = I when ident
+    auto product = [&](const double *R, bool ident, bool trans_lhs) {
+#pragma unroll
+        for (int i = 0; i < kT; ++i)
+#pragma unroll
+            for (int j = 0; j < kT; ++j) acc[i][j] = 0.0;
+        for (int k0 = 0; k0 < B2; k0 += kBjK) {
+            __syncthreads();   // X complete (first chunk) / the previous chunk's readers are done
+            for (int e = tid; e < kBjK * B2; e += 256) {
+                const int kr = e / B2, c = e - kr * B2, kk = k0 + kr;
+                Rc[kr * ld + c] = kk < B2 ? (ident ? (kk == c ? 1.0 : 0.0) : R[(int64_t)kk * B2 + c]) : 0.0;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int kr = 0; kr < kBjK; ++kr) {
+                if (k0 + kr >= B2) break;
+                double xv[kT], rv[kT];
+#pragma unroll
+                for (int i = 0; i < kT; ++i) {
+                    const int r = ty + 16 * i;
+                    xv[i] = r < B2 ? (trans_lhs ? Rc[kr * ld + r] : X[r * ld + k0 + kr]) : 0.0;
+                }
+#pragma unroll
+                for (int j = 0; j < kT; ++j) {
+                    const int c = tx + 16 * j;
+                    rv[j] = c < B2 ? (trans_lhs ? X[(k0 + kr) * ld + c] : Rc[kr * ld + c]) : 0.0;
+                }
+#pragma unroll
+                for (int i = 0; i < kT; ++i)
+#pragma unroll
+                    for (int j = 0; j < kT; ++j) acc[i][j] = __builtin_fma(xv[i], rv[j], acc[i][j]);
+            }
+        }
+    };
+    product(Rq, rq_id, false);
+    if (isA) {
+        // the partial product X R_q back into X, then R_p^T (X R_q)
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kT; ++i)
+#pragma unroll
+            for (int j = 0; j < kT; ++j) {
+                const int r = ty + 16 * i, c = tx + 16 * j;
+                if (r < B2 && c < B2) X[r * ld + c] = acc[i][j];
+            }
+        product(Rp, rp_id, true);
+    }
+#pragma unroll
+    for (int i = 0; i < kT; ++i)
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+            const int r = ty + 16 * i, c = tx + 16 * j;
+            if (r >= B2 || c >= B2) continue;
+            const int gj = bj_idx(c, Iq, Jq, b);
+            if (gj >= nb) continue;
+            if (isA) {
+                const int gi = bj_idx(r, Ip, Jp, b);
+                if (gi >= nb) continue;
+                Aw[(int64_t)gi * nbp + gj] = acc[i][j];
+                Aw[(int64_t)gj * nbp + gi] = acc[i][j];
+            } else {
+                const int gi = rt * B2 + r;
+                if (gi < nb) V[(int64_t)gi * nb + gj] = acc[i][j];
+            }
+        }
+}
+
+// state: [0] sweeps that rotated, [1] converged, [2] rotations in this sweep, [3] = 1 (one stage)
+__global__ void k_bj_begin(int32_t *state_all) {
+    if (threadIdx.x == 0) state_all[4 * blockIdx.x + 3] = 1;
+}
+__global__ void k_bj_sweep_end(int32_t *state_all) {
+    int32_t *st = state_all + 4 * blockIdx.x;
+    if (threadIdx.x == 0 && !st[1]) {
+        if (st[2] == 0) st[1] = 1;
+        else st[0] += 1;
+        st[2] = 0;
     }
 }
 
@@ -587,7 +885,8 @@ Regions regions(int64_t nb, int64_t nblocks) {
     Regions R;
     R.aw = al256((size_t)nbp * nbp * 8 * nblocks);  // Aw: nbp x nbp, fp32 (first stage) then fp64
     R.v = al256((size_t)nb * nb * 8 * nblocks);     // V: nb x nb fp64
-    R.t = al256((size_t)nb * nb * 8 * nblocks);     // T: nb x nb, fp32 (A Q products) or fp64 (refinement)
+    R.t = al256((size_t)nb * nb * 8 * nblocks);     // T: nb x nb, fp32 (A Q products) or fp64 (refinement),
+                                                    // or the block-Jacobi rotations (fewer than nb^2 per block)
     R.tlog = al256((size_t)(nbp - 1) * (nbp / 2) * 8 * nblocks);   // tangents of one sweep
     R.state = al256((size_t)16 * nblocks);                         // 4 ints
     R.tq = al256((size_t)((nb + kQP - 1) / kQP) * kQP * kQP * 4 * nblocks);  // QR panel T factors
@@ -614,6 +913,24 @@ __global__ void k_stage_flag(int32_t *state_all) {
 size_t refresh_ws(const dobb_shape &sh, int count) {
     const int cnt = count < kMaxMats ? count : kMaxMats;
     return regions(sh.nb, (sh.n / sh.nb) * cnt).total;
+}
+
+// the block-Jacobi sweeps: per sweep m - 1 rounds of k_bj_sub and k_bj_apply, then the bookkeeping
+template <int B2>
+hipError_t launch_bj(int nb, int nbp, int m, int sweeps, dim3 gs, dim3 ga, size_t ls, size_t la, double *Aw64,
+                     double *V, double *Rw, int32_t *nrot, int32_t *state, hipStream_t s) {
+    (void)hipFuncSetAttribute((const void *)k_bj_sub<B2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ls);
+    (void)hipFuncSetAttribute((const void *)k_bj_apply<B2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)la);
+    for (int sw = 0; sw < sweeps; ++sw) {
+        for (int r = 0; r < m - 1; ++r) {
+            DOBB_LAUNCH("jacobi_block_sub", s, k_bj_sub<B2>, gs, dim3(kBjThreads), ls, nb, nbp, r, kTolFp64, Aw64, Rw, nrot,
+                        state);
+            DOBB_LAUNCH("jacobi_block_apply", s, k_bj_apply<B2>, ga, dim3(256), la, nb, nbp, r, Aw64, V, (const double *)Rw,
+                        (const int32_t *)nrot, (const int32_t *)state);
+        }
+        DOBB_LAUNCH("jacobi_sweep_end", s, k_bj_sweep_end, dim3(gs.y), dim3(64), 0, state);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
@@ -658,7 +975,43 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
         else DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, false>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC);         \
     } while (0)
 
-        if (a.mode == DOBB_REFRESH_EXACT) {
+        const bool block_jacobi = a.mode == DOBB_REFRESH_EXACT && (int64_t)jacobi_lds_bytes(nbp, 4) > lds_max;
+        if (block_jacobi) {
+            // one fp64 stage: Aw64 = V^T A V (V = I or Q_prev, widened), block-Jacobi sweeps to the
+            // refinement threshold, then the common finalisation
+            JacTable jt{};
+            for (int i = 0; i < cnt; ++i) { jt.A[i] = a.A[c0 + i]; jt.Qp[i] = a.Q[c0 + i]; }
+            DOBB_LAUNCH("jacobi_init", s, k_jacobi_init, dim3((unsigned)nblocks), dim3(256), 0, nb, nbp, nblk, a.warm, jt,
+                        Aw, V, state);
+            double *Aw64 = (double *)Aw;
+            double *T64 = (double *)Tm;
+            const int tiles = (nb + 15) / 16;
+            const dim3 gr((unsigned)(tiles * tiles), (unsigned)nblocks);
+            DOBB_LAUNCH("jacobi_refine_gemm", s, k_refine_gemm, gr, dim3(256), 0, nb, nbp, nblk, 0, jt, (const double *)V,
+                        T64, Aw64, state);
+            DOBB_LAUNCH("jacobi_refine_gemm", s, k_refine_gemm, gr, dim3(256), 0, nb, nbp, nblk, 1, jt, (const double *)V,
+                        T64, Aw64, state);
+            DOBB_LAUNCH("jacobi_symmetrize", s, k_symmetrize64, dim3((unsigned)nblocks), dim3(256), 0, nbp, Aw64);
+            DOBB_LAUNCH("jacobi_stage_flag", s, k_bj_begin, dim3((unsigned)nblocks), dim3(64), 0, state);
+            const BjGeo G = bj_geo(nb);
+            const int b2 = 2 * G.b, np2 = G.m / 2, nrt = (nb + b2 - 1) / b2;
+            double *Rw = T64;                        // the rotations of a round: np2 x b2 x b2 per block
+            int32_t *nrot = (int32_t *)tlog;         // their counts: np2 per block
+            const size_t ls = bj_sub_lds(nb), la = bj_apply_lds(nb);
+            const dim3 gs((unsigned)np2, (unsigned)nblocks), ga((unsigned)(np2 * (np2 - 1) / 2 + np2 * nrt), (unsigned)nblocks);
+            const int sweeps = a.iters > 0 ? a.iters : 30;
+            hipError_t eb = hipSuccess;
+            switch (b2) {
+#define DOBB_BJ(B2) case B2: eb = launch_bj<B2>(nb, nbp, G.m, sweeps, gs, ga, ls, la, Aw64, V, Rw, nrot, state, s); break;
+                DOBB_BJ(8) DOBB_BJ(16) DOBB_BJ(24) DOBB_BJ(32) DOBB_BJ(40) DOBB_BJ(48) DOBB_BJ(56) DOBB_BJ(64)
+                DOBB_BJ(72) DOBB_BJ(80)
+#undef DOBB_BJ
+                default: return hipErrorInvalidValue;
+            }
+            if (eb != hipSuccess) return eb;
+            DOBB_LAUNCH("jacobi_finalize", s, k_jacobi_finalize, dim3((unsigned)nblocks), dim3(256), (size_t)nb * 8, nb, nbp,
+                        nblk, (const double *)Aw64, (const double *)V, (const int32_t *)state, ot);
+        } else if (a.mode == DOBB_REFRESH_EXACT) {
             if (a.warm) {
                 DOBB_BGEMM(false, opA, opQ, outT);
                 Opnd opT{};

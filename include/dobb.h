@@ -111,12 +111,17 @@ dobb_status dobb_accumulate_moment(const dobb_shape *s, const void *X, dobb_dtyp
 
 /* ------------------------------------------------------------------------------------------------
  * Basis refresh (abstract: a complete basis is tracked within each block; Tables 14-16).
- *   EXACT:     Q_b, lambda_b = eig(A_b) by parallel-order cyclic Jacobi in fp32.  warm_start = 0
- *              starts from the identity; warm_start = 1 diagonalises Q_prev^T A_b Q_prev and
- *              accumulates the rotations onto Q_prev.  iters = maximum sweeps (<= 0: 30).  tol is
- *              the relative threshold: a pair (p,q) is rotated while |a_pq| > tol sqrt(|a_pp a_qq|)
- *              (<= 0: 1e-7); the block has converged after a sweep with no rotation.  Output is
- *              sorted by descending eigenvalue, each eigenvector with its largest entry positive.
+ *   EXACT:     Q_b, lambda_b = eig(A_b) by parallel-order cyclic Jacobi: sweeps on an fp32 working
+ *              matrix, then fp64 sweeps on V^T A_b V to |a_pq| <= 1e-14 sqrt(|a_pp a_qq|).  Blocks
+ *              whose fp32 working matrix exceeds the LDS (nb above about 200) run block Jacobi in
+ *              fp64 from the start (index blocks of up to 40 paired by the circle method, one sweep
+ *              of each pair's sub-problem per round) to that same threshold.  warm_start = 0 starts
+ *              from the identity; warm_start = 1 diagonalises Q_prev^T A_b Q_prev and accumulates
+ *              the rotations onto Q_prev.  iters = maximum sweeps of the first stage (<= 0: 30).
+ *              tol is the first stage's relative threshold: a pair (p,q) is rotated while
+ *              |a_pq| > tol sqrt(|a_pp a_qq|) (<= 0: 1e-7); a stage has converged after a sweep with
+ *              no rotation, and info is -1 unless both have.  Output is sorted by descending
+ *              eigenvalue, each eigenvector with its largest entry positive.
  *   ORTH_ITER: iters = k >= 1 steps of  Q_b <- qr(A_b Q_b).Q  (Householder, diag(R) > 0) from the
  *              Q passed in (which must hold a basis); lambda_b receives the Rayleigh quotients
  *              q_j^T A_b q_j.  warm_start and tol are ignored.

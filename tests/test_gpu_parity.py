@@ -149,7 +149,10 @@ def _check_eig(A32, lam, Q, lam_ref, Q_ref):
 
 
 @pytest.mark.parametrize("N,n,nb", [(4096, 768, 192), (2048, 96, 48), (2048, 75, 25), (4096, 200, 100),
-                                    (4096, 400, 400), (8192, 256, 128)])
+                                    (4096, 400, 400), (8192, 256, 128),
+                                    # block Jacobi (working matrix past the LDS): index blocks padded
+                                    # past nb (300: 8 blocks of 40), an odd width
+                                    (4096, 600, 300), (3000, 301, 301)])
 def test_refresh_exact_matches_oracle(N, n, nb):
     print(f"refresh exact n={n} nb={nb}", flush=True)
     rng = RNG(7 * n + nb)
@@ -167,7 +170,7 @@ def test_refresh_exact_matches_oracle(N, n, nb):
     _check_eig(A32, host(lam), host(Q), lam_ref, Q_ref)
 
 
-@pytest.mark.parametrize("n,nb", [(384, 96), (384, 128)])
+@pytest.mark.parametrize("n,nb", [(384, 96), (384, 128), (800, 400)])
 def test_refresh_exact_warm_start(n, nb):
     rng = RNG(11 + nb)
     A1 = t32(oracle.accumulate(workload.activations(4096, n, 0.15, rng), nb))
