@@ -49,7 +49,34 @@ PEAK_BF16_MFMA = 2.5e15      # flop/s, bf16 and fp16
 PEAK_FP32_MFMA = 157.3e12    # flop/s
 PEAK_FP32_VALU = 157.3e12    # flop/s
 PEAK_FP64_VALU = 78.6e12     # flop/s
-JACOBI_KERNELS = ("jacobi_sweep", "jacobi_sweep_fp64", "jacobi_rotate_v")
+JACOBI_KERNELS = ("jacobi_sweep", "jacobi_sweep_fp64", "jacobi_rotate_v", "jacobi_block_sub", "jacobi_block_apply")
+LDS_BYTES = 160 * 1024
+
+
+def block_jacobi(nb):
+    """Whether the library runs block Jacobi for nb (its fp32 element-wise working matrix exceeds the
+    LDS), and then its geometry (m index blocks of b), as the library chooses them."""
+    nbp = (nb + 1) // 2 * 2
+    if ((nbp // 2) * 16 + 4 + 15) // 16 * 16 + nbp * nbp * 4 <= LDS_BYTES:
+        return None
+    m = 2 * ((nb + 79) // 80)
+    b = (-(-nb // m) + 3) // 4 * 4
+    return m, b
+
+
+def jacobi_sweep_flops(nb):
+    """fp64 flops of one sweep on one block.  Element-wise: nb (nb - 1) / 2 rotations, each combining
+    rows p, q and columns p, q of A (4 nb entries, 3 flops each) and columns p, q of V (2 nb entries):
+    9 nb^2 (nb - 1).  Block Jacobi: m - 1 rounds, each with m / 2 sub-problem sweeps of size 2b (the
+    same count at 2b) and the tile products R_p^T A R_q for the (m/2)(m/2 - 1)/2 off-diagonal pairs
+    (2 (2b)^3 twice) and V R_q for the m / 2 pair sets (2 nb (2b)^2)."""
+    g = block_jacobi(nb)
+    if g is None:
+        return 9.0 * nb * nb * (nb - 1)
+    m, b = g
+    b2, h = 2 * b, m // 2
+    per_round = h * 9.0 * b2 * b2 * (b2 - 1) + h * (h - 1) / 2 * 4.0 * b2 ** 3 + h * 2.0 * nb * b2 * b2
+    return (m - 1) * per_round
 BLOCKS = 16
 QR_PANEL = 32                # Householder panel width of the refresh
 QR_SINGLE_LAUNCH_MAX_NB = 128  # blocks up to this width are factored in one launch (Z in LDS)
@@ -266,13 +293,11 @@ def kernel_work(specs, n_tokens, g_bytes=4, w_bytes=4, norm="sign", orth_iters=1
 
 
 def jacobi_entry(kernels, infos, nbs, total_ms):
-    """The exact refresh's rotation work against the fp64 vector peak (both Jacobi stages compute in
-    fp64; the first only stores its working matrix in fp32).  A rotation of the pair (p, q) combines
-    rows p, q and columns p, q of A (4 nb entries, 3 flops each) and columns p, q of V (2 nb entries):
-    18 nb flops; a sweep is nb (nb - 1) / 2 rotations, so 9 nb^2 (nb - 1) flops per block and sweep,
-    counted over the sweeps each block reports in info (those that rotated)."""
+    """The exact refresh's work against the fp64 vector peak (every Jacobi stage computes in fp64; the
+    element-wise first stage only stores its working matrix in fp32): jacobi_sweep_flops per block and
+    sweep, counted over the sweeps each block reports in info (those that rotated)."""
     sweeps = [i.clamp(min=0).double() for i in infos]
-    flops = sum(9.0 * nb * nb * (nb - 1) * float(sw.sum()) for sw, nb in zip(sweeps, nbs))
+    flops = sum(jacobi_sweep_flops(nb) * float(sw.sum()) for sw, nb in zip(sweeps, nbs))
     jac_ms = sum(kernels.get(k, (0, 0.0))[1] for k in JACOBI_KERNELS)
     rate = flops / (jac_ms / 1e3) if jac_ms > 0 else 0.0
     n_blocks = sum(sw.numel() for sw in sweeps)

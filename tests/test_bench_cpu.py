@@ -70,6 +70,16 @@ def test_jacobi_flop_count():
     assert e["flops"] == 9 * 100 * 100 * 99
     assert e["achieved"] == pytest.approx(9 * 100 * 100 * 99 / 1e-6 / 1e12, rel=1e-3)   # TFLOP/s
     assert e["frac"] == pytest.approx(e["achieved"] / 78.6, rel=1e-3) and e["bound"] == "alu"
+    # nb = 400 runs block Jacobi (its fp32 working matrix, 640 KB, exceeds the LDS): 10 index blocks
+    # of 40, 9 rounds of 5 sub-problem sweeps at 80 (9 80^2 79 each), 10 tile pairs (4 80^3 each) and
+    # 5 V updates (2 400 80^2 each); its kernels' time is counted
+    assert bench.block_jacobi(192) is None and bench.block_jacobi(400) == (10, 40)
+    assert bench.block_jacobi(300) == (8, 40) and bench.block_jacobi(301) == (8, 40)
+    per_round = 5 * 9 * 80 * 80 * 79 + 10 * 4 * 80 ** 3 + 5 * 2 * 400 * 80 * 80
+    kern = {"jacobi_block_sub": (9, 20.0), "jacobi_block_apply": (9, 10.0), "jacobi_init": (1, 5.0)}
+    e = bench.jacobi_entry(kern, [torch.tensor([10, 9], dtype=torch.int32)], [400], 40.0)
+    assert e["flops"] == pytest.approx(9 * per_round * 19)
+    assert e["jacobi_kernels_ms"] == pytest.approx(30.0)
 
 
 def _write_csv(path, rows):
