@@ -339,7 +339,7 @@ CSRC = os.path.join(ROOT, "block_diagonal_eigenbasis_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gpt2xl_step.md")
 # library kernel name -> (regular expression on the device symbol, source file)
 KERNEL_SYMBOLS = {
-    "accumulate_syrk_bf16": (r"k_syrk_bf16<", "k_accumulate.hip"),
+    "accumulate_syrk_bf16": (r"k_syrk_(bf16<|narrow_dma)", "k_accumulate.hip"),
     "accumulate_syrk_wide": (r"k_syrk_wide", "k_accumulate.hip"),
     "accumulate_reduce": (r"k_syrk_reduce", "k_accumulate.hip"),
     "refresh_gemm": (r"k_bgemm<", "k_refresh.hip"),
