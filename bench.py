@@ -342,7 +342,7 @@ KERNEL_SYMBOLS = {
     "accumulate_syrk_bf16": (r"k_syrk_(bf16<|narrow_dma)", "k_accumulate.hip"),
     "accumulate_syrk_wide": (r"k_syrk_wide", "k_accumulate.hip"),
     "accumulate_reduce": (r"k_syrk_reduce", "k_accumulate.hip"),
-    "refresh_gemm": (r"k_bgemm<", "k_refresh.hip"),
+    "refresh_gemm": (r"k_bgemm(_t)?<", "k_refresh.hip"),
     "qr_block": (r"k_qr_block<", "k_qr.hip"),
     "qr_panel": (r"k_qr_panel<", "k_qr.hip"),
     "qr_update": (r"k_qr_apply<\d+, true,", "k_qr.hip"),

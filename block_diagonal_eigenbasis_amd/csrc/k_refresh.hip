@@ -70,6 +70,118 @@ __global__ void __launch_bounds__(256) k_bgemm(int nb, int T, int nblk, Opnd A, 
     }
 }
 
+// The same product on 16 x 16 x 4 fp32 MFMA tiles, for widths that a tile of 16 NT fits without
+// much padding (NT = 5: 80-wide tiles, 25 per nb = 400 block; nb <= 16 NT: one tile per block, so
+// nb = 100 runs as 112 x 112 instead of 128 x 128 with a 112-deep K).  NT waves, wave w computing rows
+// 16 w .. 16 w + 15 of the tile against its NT column tiles (the row operand read once per k-step
+// for NT products); K in 16-deep chunks, double buffered in LDS with one barrier per chunk, both
+// operands k-major there (a[k][i] = op(A)[i][k], b[k][j] = B[k][j]).  The 16 x 16 x 4 lane layout
+// (checked on gfx950): A[l % 16][l / 16], B[l / 16][l % 16], D[4 (l / 16) + i][l % 16].
+constexpr int kTK = 16;
+template <int NT>
+struct TileSmem {
+    // row pitch 16 or 48 words modulo the 64 banks, so a k-step's four rows of 16 meet no conflict
+    static constexpr int P = (16 * NT) % 32 == 0 ? 16 * NT + 16 : 16 * NT;
+    float a[2][kTK][P];
+    float b[2][kTK][P];
+};
+// grid.x = tiles * tiles * nblk * count (T = ceil(nb / 16 NT)), block 64 NT
+template <int NT, bool TRANS_A, bool VEC>
+__global__ void __launch_bounds__(64 * NT) k_bgemm_t(int nb, int T, int nblk, Opnd A, Opnd B, OutOpnd C) {
+    constexpr int TILE = 16 * NT, NTH = 64 * NT, Q4 = TILE / 4, K4 = kTK / 4, R = kTK / 16;
+    __shared__ __align__(16) TileSmem<NT> sm;
+    const int x = xcd_remap(blockIdx.x, gridDim.x);   // the tiles of a block share one XCD's L2
+    const int tile = x % (T * T);
+    const int rest = x / (T * T);
+    const int b = rest % nblk, mat = rest / nblk;
+    const int i0 = (tile / T) * TILE, j0 = (tile % T) * TILE;
+    const float *Ab = A.p[mat] + (int64_t)b * A.blk_stride;
+    const float *Bb = B.p[mat] + (int64_t)b * B.blk_stride;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // one chunk is TILE x kTK floats of each operand, R float4 pieces of each per thread
+    f32x4 va[R], vb[R];
+    auto load4 = [&](const float *p, int lim) -> f32x4 {   // p[0..3] that lie below lim, zeros past it
+        f32x4 q = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (VEC) {
+            if (lim > 0) q = *(const f32x4 *)p;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) if (c < lim) q[c] = p[c];
+        }
+        return q;
+    };
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = t + r * NTH;
+            {   // B[k][j]: k = e / Q4, j = 4 (e % Q4) ..
+                const int kk = e / Q4, jj = 4 * (e - kk * Q4), k = k0 + kk, j = j0 + jj;
+                vb[r] = k < nb ? load4(Bb + (int64_t)k * B.ld + j, nb - j) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if (TRANS_A) {   // op(A)[i][k] = A[k][i]
+                const int kk = e / Q4, ii = 4 * (e - kk * Q4), k = k0 + kk, i = i0 + ii;
+                va[r] = k < nb ? load4(Ab + (int64_t)k * A.ld + i, nb - i) : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {         // op(A)[i][k] = A[i][k]: i = e / K4, k = 4 (e % K4) ..
+                const int ii = e / K4, kk = 4 * (e % K4), i = i0 + ii, k = k0 + kk;
+                va[r] = i < nb ? load4(Ab + (int64_t)i * A.ld + k, nb - k) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = t + r * NTH;
+            {
+                const int kk = e / Q4, jj = 4 * (e - kk * Q4);
+                *(f32x4 *)&sm.b[buf][kk][jj] = vb[r];
+            }
+            if (TRANS_A) {
+                const int kk = e / Q4, ii = 4 * (e - kk * Q4);
+                *(f32x4 *)&sm.a[buf][kk][ii] = va[r];
+            } else {
+                const int ii = e / K4, kk = 4 * (e % K4);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sm.a[buf][kk + c][ii] = va[r][c];
+            }
+        }
+    };
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    put(0);
+    __syncthreads();
+    int cur = 0;
+    const int r16 = lane & 15, k4 = lane >> 4;
+    for (int k0 = 0; k0 < nb; k0 += kTK) {
+        const bool more = k0 + kTK < nb;
+        if (more) fetch(k0 + kTK);
+#pragma unroll
+        for (int ks = 0; ks < kTK; ks += 4) {
+            const float av = sm.a[cur][ks + k4][16 * w + r16];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const float bv = sm.b[cur][ks + k4][16 * j + r16];
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
+            }
+        }
+        if (more) put(cur ^ 1);   // the other buffer's readers finished before the last barrier
+        __syncthreads();
+        cur ^= 1;
+    }
+    float *Cb = C.p[mat] + (int64_t)b * C.blk_stride;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int col = j0 + 16 * j + r16;
+        if (col >= nb) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = i0 + 16 * w + 4 * k4 + i;
+            if (row < nb) Cb[(int64_t)row * C.ld + col] = acc[j][i];
+        }
+    }
+}
+
 // ---- Jacobi ------------------------------------------------------------------------------------
 // Round-robin (circle method) pairing of nbp (even) indices: step s, pair k.  Index nbp-1 is fixed;
 // over nbp-1 steps every pair (p, q) meets exactly once and the pairs of one step are disjoint.
@@ -969,10 +1081,28 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
         outT.blk_stride = t_stride;
         outT.ld = nb;
         const dim3 ggemm((unsigned)(T * T * nblocks));
+        // the 16 x 16 MFMA tiles where 16 NT fits the width: 80 for multiples of 80, one tile per
+        // block up to 128 (the 32 x 32 tiles' 64 x 64 workgroup tiles otherwise)
+        const int tnt = nb % 80 == 0 ? 5 : nb <= 48 ? 3 : nb <= 96 ? 6 : nb <= 112 ? 7 : nb <= 128 ? 8 : 0;
+        const int tT = tnt ? (nb + 16 * tnt - 1) / (16 * tnt) : 0;
+        const dim3 gtile((unsigned)(tT * tT * nblocks));
+#define DOBB_BGEMM_T(NT, TR, OA, OB, OC)                                                                          \
+    do {                                                                                                          \
+        if (nb % 4 == 0) DOBB_LAUNCH("refresh_gemm", s, (k_bgemm_t<NT, TR, true>), gtile, dim3(64 * NT), 0, nb, tT, nblk, OA, OB, OC); \
+        else DOBB_LAUNCH("refresh_gemm", s, (k_bgemm_t<NT, TR, false>), gtile, dim3(64 * NT), 0, nb, tT, nblk, OA, OB, OC);         \
+    } while (0)
 #define DOBB_BGEMM(TR, OA, OB, OC)                                                                               \
     do {                                                                                                         \
-        if (nb % 4 == 0) DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, true>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC); \
-        else DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, false>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC);         \
+        switch (tnt) {                                                                                           \
+        case 3: DOBB_BGEMM_T(3, TR, OA, OB, OC); break;                                                         \
+        case 5: DOBB_BGEMM_T(5, TR, OA, OB, OC); break;                                                         \
+        case 6: DOBB_BGEMM_T(6, TR, OA, OB, OC); break;                                                         \
+        case 7: DOBB_BGEMM_T(7, TR, OA, OB, OC); break;                                                         \
+        case 8: DOBB_BGEMM_T(8, TR, OA, OB, OC); break;                                                         \
+        default:                                                                                                 \
+            if (nb % 4 == 0) DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, true>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC); \
+            else DOBB_LAUNCH("refresh_gemm", s, (k_bgemm<TR, false>), ggemm, dim3(256), 0, nb, T, nblk, OA, OB, OC);         \
+        }                                                                                                        \
     } while (0)
 
         const bool block_jacobi = a.mode == DOBB_REFRESH_EXACT && (int64_t)jacobi_lds_bytes(nbp, 4) > lds_max;
@@ -1148,6 +1278,7 @@ hipError_t launch_refresh(const RefreshArgs &a, hipStream_t s) {
             }
         }
         #undef DOBB_BGEMM
+        #undef DOBB_BGEMM_T
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         c0 += cnt;
