@@ -681,26 +681,57 @@ struct FusedWideTable {
     float *U[kMaxMats];
     float mu[kMaxMats], lr[kMaxMats], wd[kMaxMats], scale[kMaxMats];
 };
-// LDS: region 0 the two basis slices (2 planes each); the P chunk planes; the tile's row scale
-// exponents; the sign tile (rows of wide_spitch bytes)
-__host__ __device__ inline size_t fused_wide_qregion(int nb) { return a16((size_t)2 * 2 * wide_geo(nb).R * kKSD * 2); }
-__host__ __device__ inline size_t fused_wide_lds(int nb) {
-    return fused_wide_qregion(nb) + (size_t)2 * kTR * kPLD * 2 + a16((size_t)kTR * 4) +
-           a16((size_t)kTR * wide_spitch(nb));
+// LDS, static per instance (nb <= RM): a ring of four basis-slice stages (2 planes each), one region
+// that holds the P chunk planes during the projection and the sign tile (rows of wide_spitch bytes)
+// after it, and the tile's row scale exponents.  At RM = 416: 4 x 26624 + 54272 + 512 = 161280 bytes.
+template <int NCW>
+struct RingGeo {
+    static constexpr int RM = 64 * NCW < 416 ? 64 * NCW : 416;   // staged rows at most
+    static constexpr int KSM = (RM + kKSD - 1) / kKSD;           // k-steps at most
+    static constexpr int kStage = 2 * RM * kKSD;                 // 2-byte elements of one stage
+    static constexpr int kP = 2 * kTR * kPLD * 2, kS = kTR * (kKSD * KSM + 8);
+    static constexpr int kPS = kP > kS ? kP : kS;                // bytes of the P / sign region
+    static constexpr int kND = (2 * (RM / 32) + 7) / 8;          // slice loads per wave and stage
+};
+// s_waitcnt vmcnt(N) (this wave's memory operations older than the last N are done), then lgkmcnt(0)
+// and the workgroup barrier, in one asm block so that no memory operation moves across it
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+typedef __attribute__((address_space(3))) void *lds_void;
+// one 16-byte piece per lane from buffer offset off into LDS at dst + 16 lane (zeros past the range);
+// a function of its own: the builtin written inside the kernel's lambdas kept the host pass from
+// emitting the kernel's launch stub
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void *dst, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)dst, 16, off, 0, 0, 0);
 }
 
 // grid.x = 128-row tiles (fastest) x blocks x matrices, renumbered per XCD; block 512.
+// The basis slices reach LDS by loads that write it directly: the projection's KS slices of Q^T and
+// the reconstruction's KS slices of Q form one sequence of slots, each phase padded to 4 nchunk slots
+// (empty ones load zeros and skip the products), slot t in stage t % 4; the loads of slot t + 3 are
+// issued once every wave has passed the barrier of slot t (so stage (t + 3) % 4 = (t - 1) % 4 is free),
+// three slices in flight.  Each wave issues kND 1 KiB loads per slot (piece w + 8 i of the stage's
+// 2 nct pieces, piece w again past the count), and a chunk start adds 12 buffer operations (the
+// momentum stores and the next chunk's M and G loads, issued for every chunk so that the count is
+// fixed): before the barrier of slot t a wave waits until its operations older than the last
+// 2 kND (+ 12 where a chunk start lies between) are done, which covers its loads of slot t.
 template <int NCW, int NEST, bool GBF16, bool WBF16>
 __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, int nb, int nblk, int ntile,
                                                          FusedWideTable t) {
-    extern __shared__ __align__(16) unsigned char lds[];
+    using L = RingGeo<NCW>;
+    __shared__ __align__(16) uint16_t qst0[L::kStage], qst1[L::kStage], qst2[L::kStage], qst3[L::kStage];
+    __shared__ __align__(16) uint8_t pss[L::kPS];
+    __shared__ int rs[kTR];   // row scale exponents
+    uint16_t *const qst[4] = {qst0, qst1, qst2, qst3};
     const WideGeo geo = wide_geo(nb);
     const int nct = geo.nct, R = geo.R, KS = geo.KS;
     const int spitch = wide_spitch(nb);
-    uint16_t *qs = (uint16_t *)lds;                                      // [2][2][R][16]
-    uint16_t *ps = (uint16_t *)(lds + fused_wide_qregion(nb));           // [2][kTR][kPLD]
-    int *rs = (int *)(ps + 2 * kTR * kPLD);                              // [kTR] row scale exponents
-    uint8_t *ss = (uint8_t *)rs + a16((size_t)kTR * 4);                  // [kTR][spitch] sign bytes
+    uint16_t *const ps = (uint16_t *)pss;   // [2][kTR][kPLD] during the projection
+    uint8_t *const ss = pss;                // [kTR][spitch] sign bytes after it
 
     const int x = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = x % ntile, rest = x / ntile;
@@ -722,6 +753,7 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
 
     // ---- momentum and P: M / G chunk pieces, kTR rows x 16 four-column pieces, 4 per thread ----
     constexpr int kMP = kTR * (kKC / 4) / kWT;
+    static_assert(kMP == 4, "a chunk start issues 3 kMP = 12 buffer operations");
     f32x4 mr[kMP], gr[kMP];
     auto mg_off = [&](int i, int kc0) -> unsigned {
         const int e = tid + kWT * i;
@@ -782,32 +814,37 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
             *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
         }
     };
-    // basis slice pieces: 2 planes x R rows x 2 halves of 16 bytes (R <= 64 NCW)
-    constexpr int kQP = (4 * 64 * NCW + kWT - 1) / kWT;
-    uint4 qr[kQP];
-    auto load_q = [&](__amdgpu_buffer_rsrc_t rq, int ks) {
+    // ---- the slice loads: this wave's pieces (stage bytes 1024 p .. + 1023; plane p / nct) ----
+    const int nchunk = (KS + kSPC - 1) / kSPC;
+    const int PS = kSPC * nchunk;   // slots per phase
+    unsigned dof[L::kND];
+    int dlds[L::kND];
 #pragma unroll
-        for (int i = 0; i < kQP; ++i) {
-            const int e = tid + kWT * i;
-            const int pl = e / (2 * R), rem = e - pl * 2 * R;
-            const unsigned o = e < 4 * R ? (unsigned)(pl * plane + (int64_t)ks * R * kKSD + 8 * rem) : kOff;
-            qr[i] = bload4u(rq, boff(o, 2));
-        }
-    };
-    auto store_q = [&](int buf) {
+    for (int i = 0; i < L::kND; ++i) {
+        const int p = w + 8 * i < 2 * nct ? w + 8 * i : w;
+        const int pl = p >= nct;
+        dof[i] = (unsigned)(pl * plane * 2) + 1024u * (unsigned)(p - pl * nct) + 16u * (unsigned)lane;
+        dlds[i] = 1024 * p;
+    }
+    // the loads of slot tl into stage st: Q^T slice tl (projection), Q slice tl - PS (reconstruction),
+    // zeros for the padding slots and past the end
+    auto issue = [&](int tl, uint16_t *st) {
+        const bool proj = tl < PS;
+        const int ks = proj ? tl : tl - PS;
+        const bool real = ks < KS && tl < 2 * PS;
+        const __amdgpu_buffer_rsrc_t rq = proj ? rQT : rQN;
+        const unsigned sb = (unsigned)ks * (unsigned)(R * kKSD * 2);
 #pragma unroll
-        for (int i = 0; i < kQP; ++i) {
-            const int e = tid + kWT * i;
-            if (e < 4 * R) *(uint4 *)(qs + (size_t)buf * 2 * R * kKSD + 8 * e) = qr[i];
-        }
+        for (int i = 0; i < L::kND; ++i)
+            lds_load16(rq, (uint8_t *)st + dlds[i], real ? sb + dof[i] : kOff);
     };
 
     const int kh = 8 * (lane >> 5);
     const int prow = 32 * rt + (lane & 31);   // the tile row of this lane's accumulators
-    const int nchunk = (KS + kSPC - 1) / kSPC;
-    int par = 0;
     load_mg(0);
-    load_q(rQT, 0);
+    issue(0, qst[0]);
+    issue(1, qst[1]);
+    issue(2, qst[2]);
     f32x16 acc[NCW];
 #pragma unroll
     for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
@@ -819,57 +856,60 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
         int sreg = 0;   // the scale exponent acc holds its row at
         for (int c = 0; c < nchunk; ++c) {
             const int kc0 = c * kKC;
-            __syncthreads();   // the last chunk's products are done with ps
-            stage_p(kc0, c == 0);
-            if (c + 1 < nchunk) load_mg(kc0 + kKC);
-            const int s_end = KS - kSPC * c < kSPC ? KS - kSPC * c : kSPC;
-            for (int s = 0; s < s_end; ++s) {
+#pragma unroll
+            for (int s = 0; s < kSPC; ++s) {
                 const int ks = kSPC * c + s;
-                store_q(par);
-                if (ks + 1 < KS) load_q(rQT, ks + 1);
-                else load_q(rQN, 0);   // the reconstruction starts at slice 0 of Q
-                __syncthreads();
+                if (s == 1 || s == 2) vm_wait_barrier<2 * L::kND + 3 * kMP>();
+                else vm_wait_barrier<2 * L::kND>();   // slot ks in LDS; every wave done with slot ks - 1
                 if (s == 0) {
-                    const int se = rs[prow];
-                    const int d = c == 0 ? 0 : se - sreg;
-                    if (__any(d != 0)) {
-#pragma unroll
-                        for (int j = 0; j < NCW; ++j)
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) acc[j][i] = __builtin_amdgcn_ldexpf(acc[j][i], d);
-                    }
-                    sreg = se;
+                    stage_p(kc0, c == 0);
+                    load_mg(kc0 + kKC);   // past nb on the last chunk: zeros, no memory traffic
+                    lds_barrier();
                 }
-                const uint16_t *pr = ps + prow * kPLD + kKSD * s + kh;
-                const f16x8 ah = *(const f16x8 *)pr;
-                const f16x8 al = *(const f16x8 *)(pr + kTR * kPLD);
-                const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD + qoff;
+                issue(ks + 3, qst[(s + 3) % 4]);
+                if (ks < KS) {
+                    if (s == 0) {
+                        const int se = rs[prow];
+                        const int d = c == 0 ? 0 : se - sreg;
+                        if (__any(d != 0)) {
 #pragma unroll
-                for (int j = 0; j < NCW; j += 2) {
-                    const bool two = j + 1 < NCW && cg + 2 * (j + 1) < nct;
-                    if (cg + 2 * j < nct) {
-                        const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
-                        const uint16_t *q1 = q0 + 2 * 32 * kKSD;
-                        const f16x8 Qh0 = *(const f16x8 *)q0, Ql0 = *(const f16x8 *)(q0 + R * kKSD);
-                        if (two) {
-                            const f16x8 Qh1 = *(const f16x8 *)q1, Ql1 = *(const f16x8 *)(q1 + R * kKSD);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, ah, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql1, ah, acc[j + 1], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
-                            acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, al, acc[j + 1], 0, 0, 0);
-                        } else {
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
-                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                            for (int j = 0; j < NCW; ++j)
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) acc[j][i] = __builtin_amdgcn_ldexpf(acc[j][i], d);
+                        }
+                        sreg = se;
+                    }
+                    const uint16_t *pr = ps + prow * kPLD + kKSD * s + kh;
+                    const f16x8 ah = *(const f16x8 *)pr;
+                    const f16x8 al = *(const f16x8 *)(pr + kTR * kPLD);
+                    const uint16_t *qb = qst[s] + qoff;
+#pragma unroll
+                    for (int j = 0; j < NCW; j += 2) {
+                        const bool two = j + 1 < NCW && cg + 2 * (j + 1) < nct;
+                        if (cg + 2 * j < nct) {
+                            const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
+                            const uint16_t *q1 = q0 + 2 * 32 * kKSD;
+                            const f16x8 Qh0 = *(const f16x8 *)q0, Ql0 = *(const f16x8 *)(q0 + R * kKSD);
+                            if (two) {
+                                const f16x8 Qh1 = *(const f16x8 *)q1, Ql1 = *(const f16x8 *)(q1 + R * kKSD);
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                                acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, ah, acc[j + 1], 0, 0, 0);
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                                acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql1, ah, acc[j + 1], 0, 0, 0);
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                                acc[j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh1, al, acc[j + 1], 0, 0, 0);
+                            } else {
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, ah, acc[j], 0, 0, 0);
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ql0, ah, acc[j], 0, 0, 0);
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Qh0, al, acc[j], 0, 0, 0);
+                            }
                         }
                     }
                 }
-                par ^= 1;
             }
         }
     }
+    lds_barrier();   // every wave is done with the P planes the sign tile overwrites
     // ---- the signs -> the sign tile: lane holds row prow, columns 32 ch + 8 qq + 4 (l / 32) + 0..3;
     // bytes at and past nb stay zero (written here for the chunks past nb, below for the row tail) ----
 #pragma unroll
@@ -890,35 +930,11 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
         *(uint32_t *)(ss + r * spitch + c) = 0u;
     }
 
-    // ---- U = S Q^T over the same rows ----
-#pragma unroll
-    for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
-    for (int ks = 0; ks < KS; ++ks) {
-        store_q(par);
-        if (ks + 1 < KS) load_q(rQN, ks + 1);
-        __syncthreads();   // the slice and (first step) every wave's signs are in LDS
-        const f16x8 as = signs_f16x8(*(const uint2 *)(ss + prow * spitch + kKSD * ks + kh));
-        const uint16_t *qb = qs + (size_t)par * 2 * R * kKSD;
-#pragma unroll
-        for (int j = 0; j < NCW; ++j) {
-            const int ch = cg + 2 * j;
-            if (ch < nct) {
-                const int p = 32 * ch + (lane & 31);
-                const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
-                const f16x8 Bh = *(const f16x8 *)(qb + o);
-                const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        par ^= 1;
-    }
-
     // ---- W <- W - lr (s U + wd W) straight from the accumulators: lane holds column 32 ch + l % 32 of
     // rows 8 (r / 4) + 4 (l / 32) + r % 4 of its 32-row tile, so one 4-byte access per lane covers two
     // 128-byte row pieces.  The descriptors start at the tile's first row and end with its last one,
-    // so rows past m are dropped by the hardware; a chunk's W loads are issued one chunk ahead ----
+    // so rows past m are dropped by the hardware; a chunk's W loads are issued two chunks ahead (the
+    // first two during the last reconstruction slots) ----
     const int64_t trows = m - row0 < kTR ? m - row0 : kTR;
     const int64_t tile_el = (trows - 1) * n + nb;      // elements from (row0, b nb) to the tile's last one
     const int64_t tbase = row0 * n + (int64_t)b * nb;
@@ -935,7 +951,7 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
         return c0 == kOff ? kOff : c0 + (unsigned)(r >> 2) * r8 + (unsigned)(r & 3) * (unsigned)n;
     };
     using WEl = typename std::conditional<WBF16, uint16_t, float>::type;
-    WEl wv[2][16];
+    WEl wv[3][16];
     auto load_w = [&](int j, WEl (&d)[16]) {
         const unsigned c0 = col_off(j);
 #pragma unroll
@@ -944,17 +960,64 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
             else d[r] = bload1(rWt, boff(el(c0, r), 4));
         }
     };
-    load_w(0, wv[0]);
+    // ---- U = S Q^T over the same rows ----
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) acc[j] = (f32x16){};
+    auto recon_slice = [&](int ks, const uint16_t *qb) {
+        const f16x8 as = signs_f16x8(*(const uint2 *)(ss + prow * spitch + kKSD * ks + kh));
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int ch = cg + 2 * j;
+            if (ch < nct) {
+                const int p = 32 * ch + (lane & 31);
+                const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
+                const f16x8 Bh = *(const f16x8 *)(qb + o);
+                const f16x8 Bl = *(const f16x8 *)(qb + R * kKSD + o);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int g = 0; g < nchunk - 1; ++g) {
+#pragma unroll
+        for (int s = 0; s < kSPC; ++s) {
+            const int ks = kSPC * g + s;
+            vm_wait_barrier<2 * L::kND>();   // the slice and (first slot) every wave's signs are in LDS
+            issue(PS + ks + 3, qst[(s + 3) % 4]);
+            if (ks < KS) recon_slice(ks, qst[s]);
+        }
+    }
+    // the last group of four slots: only its first slot has a slice left to load (the last one); after
+    // it come the W loads of the update's first two chunks (2 x 16 per lane), which stay in flight
+    // through the remaining products
+    {
+        const int k0 = kSPC * (nchunk - 1);
+        vm_wait_barrier<2 * L::kND>();
+        issue(PS + k0 + 3, qst[3]);
+        asm volatile("" ::: "memory");   // the W loads stay behind the slice loads: the waits below count on it
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(0, wv[0]);
+        load_w(1, wv[1]);
+        if (k0 < KS) recon_slice(k0, qst[0]);
+        vm_wait_barrier<2 * L::kND + 32>();
+        if (k0 + 1 < KS) recon_slice(k0 + 1, qst[1]);
+        vm_wait_barrier<L::kND + 32>();
+        if (k0 + 2 < KS) recon_slice(k0 + 2, qst[2]);
+        vm_wait_barrier<32>();   // the last slice loads of this wave: none lands after the workgroup ends
+        if (k0 + 3 < KS) recon_slice(k0 + 3, qst[3]);
+    }
+
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
-        if (j + 1 < NCW) load_w(j + 1, wv[(j + 1) & 1]);
+        if (j + 2 < NCW) load_w(j + 2, wv[(j + 2) % 3]);
         const unsigned c0 = col_off(j);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const unsigned o = el(c0, r);
             float w0;
-            if constexpr (WBF16) w0 = bf16_to_f32(wv[j & 1][r]);
-            else w0 = wv[j & 1][r];
+            if constexpr (WBF16) w0 = bf16_to_f32(wv[j % 3][r]);
+            else w0 = wv[j % 3][r];
             const float u = acc[j][r];
             const float nw = w0 - lr * __builtin_fmaf(sc, u, wd * w0);
             if (U) bstore1(u, rUt, boff(o, 4));
@@ -1054,15 +1117,10 @@ hipError_t launch_wide_fused_cfg(const StepArgs &a, int c0, int cnt, hipStream_t
         t.U[i] = a.U ? a.U[c0 + i] : nullptr;
         t.mu[i] = h.momentum; t.lr[i] = h.lr; t.wd[i] = h.weight_decay; t.scale[i] = h.update_scale;
     }
-    const size_t sh = fused_wide_lds(nb);
     const bool gbf = a.g_dtype == DOBB_BF16, wbf = a.w_dtype == DOBB_BF16;
     const bool nest = a.hp[c0].nesterov != 0;
 #define DOBB_WF(NE, GB, WB)                                                                                      \
-    do {                                                                                                         \
-        (void)hipFuncSetAttribute((const void *)k_step_wide_fused<NCW, NE, GB, WB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh); \
-        DOBB_LAUNCH("step_wide_fused_f16", s, (k_step_wide_fused<NCW, NE, GB, WB>), grid, dim3(kWT), sh, m, n, nb, nblk, \
-                    ntile, t);                                                                                   \
-    } while (0)
+    DOBB_LAUNCH("step_wide_fused_f16", s, (k_step_wide_fused<NCW, NE, GB, WB>), grid, dim3(kWT), 0, m, n, nb, nblk, ntile, t)
     if (!nest) {
         if (gbf) { if (wbf) DOBB_WF(0, true, true); else DOBB_WF(0, true, false); }
         else { if (wbf) DOBB_WF(0, false, true); else DOBB_WF(0, false, false); }
@@ -1180,7 +1238,7 @@ hipError_t launch_step_wide(const StepArgs &a, int ldp, hipStream_t s) {
         // the one-pass kernel unless the coefficients are asked for (the two-kernel path writes them)
         bool co = false;
         for (int i = 0; i < cnt; ++i) co = co || (a.Cout && a.Cout[c0 + i]);
-        if (!co && (int64_t)fused_wide_lds((int)a.sh.nb) <= max_lds_bytes()) {
+        if (!co) {   // the one-pass kernel's static LDS fits every nb <= 416
             switch ((nct + 1) / 2) {
                 case 3: e = launch_wide_fused_cfg<3>(a, c0, cnt, s); break;
                 case 4: e = launch_wide_fused_cfg<4>(a, c0, cnt, s); break;
