@@ -59,6 +59,19 @@ __host__ __device__ inline int64_t wide_plane_elems(int nb) {
 // alternate, so 8 or 16 consecutive rows read the same logical half from distinct banks
 __host__ __device__ inline int qswz(int j) { return ((j >> 2) ^ (j >> 3)) & 1; }
 __host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+// the largest of v over the 16 lanes of a DPP row, in every lane of it: the partners within a quad
+// (quad_perm [1,0,3,2], [2,3,0,1]), the other quad of the half-row (row_half_mirror) and the other
+// half (row_mirror), register to register
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    return max(v, dpp_u32<0x140>(v));
+}
 
 // ---- basis planes --------------------------------------------------------------------------------
 // planes (4 per matrix, each nblk x KS x R x 16 two-byte elements, slice-major):
@@ -236,11 +249,7 @@ __global__ void __launch_bounds__(512) k_proj_wide(int64_t m, int64_t n, int nb,
                 const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
                 mx = u > mx ? u : mx;
             }
-#pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) {
-                const uint32_t o = (uint32_t)__shfl_xor((int)mx, sh, 16);
-                mx = o > mx ? o : mx;
-            }
+            mx = row16_max(mx);
             int se = row_scale_exp(mx);
             if (!first) {
                 const int so = rs[r];
@@ -777,38 +786,43 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
     };
     // momentum written back along the rows; P scaled by its row's power of two and split once into two
     // fp16 planes of the LDS chunk (as in k_proj_wide)
+    // (the kMP pieces are rows 32 i + tid / 16, one 16-lane group each: their row maxima, the reads of
+    // the rows' previous exponents and the writes go as independent batches, not one chain per piece)
     auto stage_p = [&](int kc0, bool first) {
+        f32x4 pv[kMP];
+        int se[kMP];
 #pragma unroll
         for (int i = 0; i < kMP; ++i) {
-            const int e = tid + kWT * i;
-            const int r = e / (kKC / 4), c = 4 * (e - r * (kKC / 4));
-            f32x4 mn, pv;
+            f32x4 mn;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 mn[cc] = __builtin_fmaf(mu, mr[i][cc], gr[i][cc]);
-                pv[cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
+                pv[i][cc] = NEST ? __builtin_fmaf(mu, mn[cc], gr[i][cc]) : mn[cc];
             }
             bstore4(mn, rM, boff(mg_off(i, kc0), 4));
-            uint32_t mx = __float_as_uint(pv[0]) & 0x7fffffffu;
+            uint32_t mx = __float_as_uint(pv[i][0]) & 0x7fffffffu;
 #pragma unroll
             for (int cc = 1; cc < 4; ++cc) {
-                const uint32_t u = __float_as_uint(pv[cc]) & 0x7fffffffu;
+                const uint32_t u = __float_as_uint(pv[i][cc]) & 0x7fffffffu;
                 mx = u > mx ? u : mx;
             }
+            se[i] = row_scale_exp(row16_max(mx));
+        }
+        const int r0 = tid / (kKC / 4), c = 4 * (tid - r0 * (kKC / 4));   // row r0 + 32 i, columns c ..
+        if (!first) {
+            int so[kMP];
 #pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) {
-                const uint32_t o = (uint32_t)__shfl_xor((int)mx, sh, 16);
-                mx = o > mx ? o : mx;
-            }
-            int se = row_scale_exp(mx);
-            if (!first) {
-                const int so = rs[r];
-                se = so < se ? so : se;
-            }
-            if ((tid & 15) == 0) rs[r] = se;
+            for (int i = 0; i < kMP; ++i) so[i] = rs[r0 + 32 * i];
+#pragma unroll
+            for (int i = 0; i < kMP; ++i) se[i] = so[i] < se[i] ? so[i] : se[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kMP; ++i) {
+            const int r = r0 + 32 * i;
+            if ((tid & 15) == 0) rs[r] = se[i];
             uint16_t h[4], l[4];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) split2s(__builtin_amdgcn_ldexpf(pv[cc], se), h[cc], l[cc]);
+            for (int cc = 0; cc < 4; ++cc) split2s(__builtin_amdgcn_ldexpf(pv[i][cc], se[i]), h[cc], l[cc]);
             uint16_t *pp = ps + r * kPLD + c;
             *(uint2 *)pp = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
             *(uint2 *)(pp + kTR * kPLD) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
@@ -885,8 +899,9 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
                     const uint16_t *qb = qst[s] + qoff;
 #pragma unroll
                     for (int j = 0; j < NCW; j += 2) {
-                        const bool two = j + 1 < NCW && cg + 2 * (j + 1) < nct;
-                        if (cg + 2 * j < nct) {
+                        // nct is 2 NCW - 1 or 2 NCW: only the last chunk of a wave can lie past it
+                        const bool two = j + 1 < NCW && (j + 1 < NCW - 1 || cg + 2 * (j + 1) < nct);
+                        if (j < NCW - 1 || cg + 2 * j < nct) {
                             const uint16_t *q0 = qb + 2 * j * 32 * kKSD;
                             const uint16_t *q1 = q0 + 2 * 32 * kKSD;
                             const f16x8 Qh0 = *(const f16x8 *)q0, Ql0 = *(const f16x8 *)(q0 + R * kKSD);
@@ -968,7 +983,7 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const int ch = cg + 2 * j;
-            if (ch < nct) {
+            if (j < NCW - 1 || ch < nct) {
                 const int p = 32 * ch + (lane & 31);
                 const int o = p * kKSD + 8 * ((lane >> 5) ^ qswz(p));
                 const f16x8 Bh = *(const f16x8 *)(qb + o);
@@ -976,7 +991,6 @@ __global__ void __launch_bounds__(512) k_step_wide_fused(int64_t m, int64_t n, i
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bh, acc[j], 0, 0, 0);
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, Bl, acc[j], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
     for (int g = 0; g < nchunk - 1; ++g) {
