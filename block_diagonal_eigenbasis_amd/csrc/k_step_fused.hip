@@ -195,11 +195,13 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
                 }
                 bstore4(mn, rm, boff(eo[s][h], 4));
             }
+        // the row's largest magnitude over the wave's four 16-lane rows: the lane swaps between rows
+        // (whichever way a swap goes, the two results of a lane are its own value and its partner's)
         {
-            uint32_t o = (uint32_t)__shfl_xor((int)mx, 16);
-            mx = o > mx ? o : mx;
-            o = (uint32_t)__shfl_xor((int)mx, 32);
-            mx = o > mx ? o : mx;
+            const auto a = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+            mx = max(a[0], a[1]);
+            const auto b = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+            mx = max(b[0], b[1]);
         }
         const int sexp = row_scale_exp(mx);
 #pragma unroll
