@@ -202,7 +202,7 @@ def test_refresh_exact_reports_non_convergence():
 # orthogonal-iteration refresh
 
 @pytest.mark.parametrize("n,nb,k", [(768, 192, 1), (200, 100, 2), (75, 25, 1), (400, 400, 1), (260, 130, 1), (10, 5, 3),
-                                    (384, 128, 1)])
+                                    (384, 128, 1), (240, 60, 1), (320, 160, 2)])
 def test_refresh_orth_iter_matches_oracle(n, nb, k):
     print(f"refresh orth_iter n={n} nb={nb} k={k}", flush=True)
     rng = RNG(13 * n + k)
