@@ -1122,6 +1122,7 @@ hipError_t launch_wide_fused_cfg(const StepArgs &a, int c0, int cnt, hipStream_t
         for (int i = 0; i < cnt; ++i) { t.Q[i] = a.Q[c0 + i]; t.planes[i] = a.planes[c0 + i]; }
         DOBB_LAUNCH("split_q", s, k_split_wide, dim3((unsigned)geo.KS, (unsigned)(nblk * cnt)), dim3(256), 0, nb, nblk, t);
     }
+    if (geo.R > RingGeo<NCW>::RM) return hipErrorInvalidValue;   // the static stages hold RM rows (nb <= 416)
     const int ntile = (int)((m + kTR - 1) / kTR);
     const dim3 grid((unsigned)((int64_t)ntile * nblk * cnt));
     FusedWideTable t{};
