@@ -143,15 +143,19 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
         return r < 16 ? r : 16;
     };
 
-    f32x4 pm[KS][2], pg[KS][2];
-    auto load_mg = [&](int64_t tl) {
+    // M and G of two tiles in flight where the registers allow it (up to 112 basis rows; 248 VGPRs at
+    // 128 rows, where one tile ahead is kept): buffer BUF (a compile-time index) holds tile tl
+    constexpr bool kTwo = NC <= 7;
+    f32x4 pm[kTwo ? 2 : 1][KS][2], pg[kTwo ? 2 : 1][KS][2];
+    auto load_mg = [&](int64_t tl, auto BUF) {
+        constexpr int B_ = decltype(BUF)::value;
         const int64_t rows = tile_rows(tl), r0 = tl * 16;
         const __amdgpu_buffer_rsrc_t rm = make_rsrc(M + r0 * n, rows * n * 4);
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gv + r0 * n * GS, rows * n * GS);
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) pm[s][h] = bload4(rm, boff(eo[s][h], 4));
+            for (int h = 0; h < 2; ++h) pm[B_][s][h] = bload4(rm, boff(eo[s][h], 4));
         __builtin_amdgcn_sched_barrier(0);   // all of the tile's M rows, then its G rows (2 % faster
                                              // on the GPT-2 XL shapes than interleaving the two)
 #pragma unroll
@@ -160,20 +164,16 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
             for (int h = 0; h < 2; ++h) {
                 if constexpr (GBF16) {
                     const uint2 hb = bload2u(rg, boff(eo[s][h], 2));
-                    pg[s][h] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
+                    pg[B_][s][h] = f32x4{bf16_to_f32((uint16_t)hb.x), bf16_to_f32((uint16_t)(hb.x >> 16)),
                                      bf16_to_f32((uint16_t)hb.y), bf16_to_f32((uint16_t)(hb.y >> 16))};
                 } else {
-                    pg[s][h] = bload4(rg, boff(eo[s][h], 4));
+                    pg[B_][s][h] = bload4(rg, boff(eo[s][h], 4));
                 }
             }
     };
 
-    int64_t tile = t_begin + wv;
-    load_mg(tile);
-    // the first tile's rows, waited for here: the loop head then has no loads of its own to wait for
-    // and does not wait for the previous tile's stores
-    __builtin_amdgcn_s_waitcnt(0);
-    for (; tile < t_end; tile += 8) {
+    auto do_tile = [&](int64_t tile, auto BUF) {
+        constexpr int B_ = decltype(BUF)::value;
         const int64_t rows = tile_rows(tile), r0 = tile * 16;
         const __amdgpu_buffer_rsrc_t rm = make_rsrc(M + r0 * n, rows * n * 4);
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wv + r0 * n * WS, rows * n * WS);
@@ -188,8 +188,8 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
                 f32x4 mn;
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
-                    mn[cc] = __builtin_fmaf(mu, pm[s][h][cc], pg[s][h][cc]);
-                    pv[s][h][cc] = NEST ? __builtin_fmaf(mu, mn[cc], pg[s][h][cc]) : mn[cc];
+                    mn[cc] = __builtin_fmaf(mu, pm[B_][s][h][cc], pg[B_][s][h][cc]);
+                    pv[s][h][cc] = NEST ? __builtin_fmaf(mu, mn[cc], pg[B_][s][h][cc]) : mn[cc];
                     const uint32_t u = __float_as_uint(pv[s][h][cc]) & 0x7fffffffu;
                     mx = u > mx ? u : mx;
                 }
@@ -212,8 +212,8 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
             ph[s] = __builtin_bit_cast(f16x8, uint4{pack2(hh[0], hh[1]), pack2(hh[2], hh[3]), pack2(hh[4], hh[5]), pack2(hh[6], hh[7])});
             pl[s] = __builtin_bit_cast(f16x8, uint4{pack2(hl[0], hl[1]), pack2(hl[2], hl[3]), pack2(hl[4], hl[5]), pack2(hl[6], hl[7])});
         }
-        // the next tile's M and G, this tile's W
-        load_mg(tile + 8);
+        // the M and G of this buffer's next tile (two tiles on, or the next one), this tile's W
+        load_mg(tile + (kTwo ? 16 : 8), BUF);
         using WVec = typename std::conditional<WBF16, uint2, f32x4>::type;
         WVec wcur[NC];
 #pragma unroll
@@ -306,7 +306,24 @@ __global__ void __launch_bounds__(kFT) k_step_fused(int64_t m, int64_t n, int nb
                 bstore4(f32x4{nw[0], nw[1], nw[2], nw[3]}, rw, boff(wo[ch], 4));
             }
         }
+        };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int64_t tile = t_begin + wv;
+    load_mg(tile, I0{});
+    if constexpr (kTwo) load_mg(tile + 8, I1{});
+    // the first tile's rows, waited for here: the loop head then has no loads of its own to wait for
+    // and does not wait for the previous tile's stores
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (kTwo) {
+        for (; tile < t_end; tile += 16) {
+            do_tile(tile, I0{});
+            if (tile + 8 < t_end) do_tile(tile + 8, I1{});
+        }
+    } else {
+        for (; tile < t_end; tile += 8) do_tile(tile, I0{});
     }
+
 }
 
 template <int NC, int KS>
